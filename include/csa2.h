@@ -1,0 +1,181 @@
+/*
+ * csa2.h -- C ABI of the CSA2 (Compressed Sparse Attention 2) global-attention
+ * hot path on AMD Instinct MI355X (gfx950).
+ *
+ * The calls follow how the pages on DeepSeek-V4.1-Flash state the problem:
+ *   - eogee.com report "DeepSeek V4.1-Flash 技术报告深度解析", 3.2: a light
+ *     indexer scores main-KV entries with an indexer Q and an indexer K (32
+ *     heads x 128 dims), each query keeps its Top-K (512) entries and attends
+ *     to them plus its layer's sliding-window (SWA, 128 tokens) KV with 64
+ *     query heads of dim 512 sharing one KV head. Layers run in Full (score
+ *     every visible entry), Reindex (own indexer Q over the shared indexer K)
+ *     or Reuse (inherit the indices) mode.
+ *   - same report, 3.3: the decoder's first Full layer also keeps the 2048 best
+ *     blocks of 8 positions (block score = best position score) as a candidate
+ *     pool of 16384 positions; later Reindex layers score only that pool.
+ *   - same report, 3.4, and the nxbn.cn walkthrough 2.3: the main KV is stored
+ *     as FP4 E2M1 with one E4M3 scale per 16 channels and dequantized before the
+ *     attention math.
+ * Details the pages leave open are fixed as: score = sum_h w_h * max(q_h.k, 0);
+ * block score = max of its positions; each main-KV entry is both key and
+ * value; RoPE is already applied; softmax scale is an argument (1/sqrt(512));
+ * ties go to the lower position.
+ *
+ * Conventions for every call:
+ *   - Pointers are DEVICE pointers owned by the caller, unless stated.
+ *   - bf16 values travel as uint16_t bit patterns; sizes are int64_t/int32_t.
+ *   - Work is enqueued on `stream` (0 = the null stream); the call returns
+ *     without synchronizing. Faults inside kernels surface at the caller's
+ *     next synchronization.
+ *   - The library never allocates device memory and keeps no state between
+ *     calls: calls on different streams may run concurrently if their outputs
+ *     do not overlap.
+ *   - Return value: CSA2_OK, or a negative code. CSA2_EINVAL: an argument
+ *     check failed, nothing was launched and no output was touched.
+ *     CSA2_ELAUNCH: the HIP runtime refused a launch (outputs unspecified).
+ *     CSA2_EWORKSPACE: the workspace passed is smaller than the matching
+ *     *_workspace_bytes() result. csa2_last_error() gives a message for the
+ *     calling thread's last failure.
+ *   - Geometry is fixed: 512-channel main entries in 288-byte records, 32 x 128
+ *     indexer heads, 64 x 512 attention heads, sliding windows of at most 128.
+ */
+#ifndef CSA2_H
+#define CSA2_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#include <hip/hip_runtime_api.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define CSA2_OK 0
+#define CSA2_EINVAL (-1)
+#define CSA2_ELAUNCH (-2)
+#define CSA2_EWORKSPACE (-3)
+
+#define CSA2_DIM 512        /* attention head dim = main-KV entry channels */
+#define CSA2_HEADS 64       /* query heads sharing the single KV head */
+#define CSA2_IDX_HEADS 32   /* indexer heads */
+#define CSA2_IDX_DIM 128    /* indexer head dim */
+#define CSA2_GROUP 16       /* channels per E4M3 scale */
+#define CSA2_RECORD 288     /* bytes per FP4 main-KV entry: 256 code bytes + 32 scale bytes */
+#define CSA2_MAX_WINDOW 128 /* sliding-window length limit */
+#define CSA2_MAX_TOPK 4096  /* largest k accepted by csa2_topk */
+
+/* Layout version of the 288-byte record (below); bumps if the layout changes. */
+int csa2_format_version(void);
+
+/* Message describing the calling thread's last non-OK return (static storage). */
+const char* csa2_last_error(void);
+
+/*
+ * fp4_kv_pack -- write FP4 main-KV records (eogee.com report 3.4; nxbn.cn 2.3).
+ *   x_bf16 [n][512] bf16 row-major, values after RoPE.
+ *   out    [n][288] bytes. Record: byte j (0..255) holds channel 2j in bits 3:0
+ *          and channel 2j+1 in bits 7:4 as E2M1 codes (bit 3 sign); byte 256+g
+ *          (g = 0..31) holds the E4M3 scale of channels 16g..16g+15.
+ *   Per 16-channel group: S = E4M3(amax/6) (amax/6 in fp32, rounded to nearest
+ *   even, saturating at 448); each channel takes the E2M1 code whose value
+ *   times S is nearest to x (ties to the even code, beyond 6S -> 6S; zero
+ *   magnitude -> +0 code); S == 0 gives all-zero codes. Inputs must be finite.
+ *   n >= 0 (n == 0 launches nothing). Records are independent, so a caller may
+ *   pack one new token's entry at a time.
+ */
+int fp4_kv_pack(const uint16_t* x_bf16, int64_t n, uint8_t* out, hipStream_t stream);
+
+/*
+ * fp4_kv_unpack -- decode FP4 records to bf16: y = E2M1(code) * E4M3(scale),
+ * exact in bf16. in [n][288] -> y_bf16 [n][512]. Test and inspection export;
+ * the attention kernel decodes records on the fly and never calls it.
+ */
+int fp4_kv_unpack(const uint8_t* in, int64_t n, uint16_t* y_bf16, hipStream_t stream);
+
+/*
+ * csa2_index_full -- Full-mode indexer scoring (eogee.com report 3.2, 3.3).
+ *   q_idx     [nq][32][128] bf16: the layer's indexer query heads.
+ *   w         [nq][32] fp32: per-head weights.
+ *   k_idx     [nseq][N][128] bf16: shared indexer-K cache, nseq = nq/q_per_seq.
+ *   N         entries per sequence (1 .. 2^31-1).
+ *   q_per_seq queries per sequence; query q reads sequence q / q_per_seq
+ *             (decode: 1, prefill chunk on one sequence: nq). Must divide nq.
+ *   n_visible [nq] int32 or NULL (= N): entries [0, n_visible[q]) are visible
+ *             (0 <= n_visible <= N); the rest score -inf.
+ *   scores    [nq][N] fp32 out: sum_h w[q][h] * max(q_idx[q][h] . k, 0).
+ *   block_size 0 (no block scores) or 8.
+ *   block_scores [nq][ceil(N/8)] fp32 out (when block_size == 8): max of the
+ *             block's scores (-inf if none visible). NULL when block_size == 0.
+ */
+int csa2_index_full(const uint16_t* q_idx, const float* w, const uint16_t* k_idx, int64_t N, int32_t nq,
+                    int32_t q_per_seq, const int32_t* n_visible, float* scores, int32_t block_size,
+                    float* block_scores, hipStream_t stream);
+
+/*
+ * csa2_index_reindex -- Reindex-mode scoring restricted to the candidate pool
+ * (eogee.com report 3.3: later indexers score only inside the pool).
+ *   q_idx, w, k_idx, N, nq, q_per_seq, n_visible: as csa2_index_full, with the
+ *             Reindex layer's own q_idx and w.
+ *   cand_blocks [nq][nb] int32: block ids chosen by the Full layer (ascending
+ *             for lower-position tie-breaks downstream; -1 = padding).
+ *   nb        blocks per query (1 .. 65536); block_size must be 8.
+ *   pool_scores [nq][nb*8] fp32 out: score of entry cand_blocks[q][j]*8 + t at
+ *             position j*8 + t; -inf for padding, invisible or >= N entries.
+ *   pool_ids  [nq][nb*8] int32 out or NULL: the entry id at each position
+ *             (-1 where the score is -inf because of padding or range).
+ */
+int csa2_index_reindex(const uint16_t* q_idx, const float* w, const uint16_t* k_idx, int64_t N, int32_t nq,
+                       int32_t q_per_seq, const int32_t* n_visible, const int32_t* cand_blocks, int32_t nb,
+                       int32_t block_size, float* pool_scores, int32_t* pool_ids, hipStream_t stream);
+
+/*
+ * csa2_topk -- per-row Top-K selection (titansim blog, CSA2 modes: Top-512;
+ * eogee.com report 3.3: Top-2048 blocks).
+ *   scores  [rows][ld] fp32, columns [0, ncols) are candidates.
+ *   row_len [rows] int32 or NULL: only columns [0, row_len[r]) of row r compete.
+ *   k       1 .. CSA2_MAX_TOPK.
+ *   id_map  [rows][ld] int32 or NULL: output column c of row r as id_map[r][c]
+ *           (used to turn pool positions into entry ids).
+ *   out_idx [rows][k] int32 out: the chosen columns (mapped), ascending by
+ *           column, then -1 padding. Order of merit: higher score first, equal
+ *           scores (-0 == +0) by lower column. -inf and NaN are never chosen;
+ *           a row with fewer than k candidates returns all of them.
+ *   workspace / ws_bytes: device scratch of at least
+ *           csa2_topk_workspace_bytes(rows, ncols, k) bytes (may be NULL when
+ *           that is 0). Contents on entry do not matter.
+ */
+size_t csa2_topk_workspace_bytes(int32_t rows, int64_t ncols, int32_t k);
+int csa2_topk(const float* scores, int32_t rows, int64_t ncols, int64_t ld, const int32_t* row_len, int32_t k,
+              const int32_t* id_map, int32_t* out_idx, void* workspace, size_t ws_bytes, hipStream_t stream);
+
+/*
+ * csa2_sparse_attn -- sparse MQA attention over selected FP4 entries plus the
+ * sliding window (eogee.com report 3.2 and 3.4).
+ *   q       [nq][64][512] bf16: query heads (RoPE applied).
+ *   kv      [nseq][N][288] FP4 records (layout of fp4_kv_pack); entry = key = value.
+ *   idx     [nq][k] int32: selected entry ids of query q (in sequence q/q_per_seq);
+ *           -1 = empty slot; other values must lie in [0, N). k 0 .. 4096.
+ *   swa     [nseq][T][512] bf16: the layer's window KV rows (key = value).
+ *   swa_start, swa_len [nq] int32: query q also attends to rows
+ *           [swa_start[q], swa_start[q]+swa_len[q]) of its sequence's window
+ *           buffer; 0 <= swa_len <= 128 and the range must lie inside [0, T).
+ *           Both may be NULL (no window keys).
+ *   softmax_scale: multiplies q.k before the softmax (1/sqrt(512)).
+ *   out     [nq][64][512] bf16 out: softmax over all of the query's keys jointly.
+ *   lse     [nq][64] fp32 out or NULL: natural-log sum of exp of the scaled logits.
+ *           A query with no keys gets out = 0 and lse = -inf.
+ *   workspace / ws_bytes: at least csa2_sparse_attn_workspace_bytes(nq, k) bytes
+ *           (partial results when a query's keys are split across workgroups).
+ */
+size_t csa2_sparse_attn_workspace_bytes(int32_t nq, int32_t k);
+int csa2_sparse_attn(const uint16_t* q, const uint8_t* kv, int64_t N, int32_t nq, int32_t q_per_seq,
+                     const int32_t* idx, int32_t k, const uint16_t* swa, int64_t T, const int32_t* swa_start,
+                     const int32_t* swa_len, float softmax_scale, uint16_t* out, float* lse, void* workspace,
+                     size_t ws_bytes, hipStream_t stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* CSA2_H */

@@ -1,0 +1,198 @@
+"""ctypes binding of libcsa2.so (the C ABI in include/csa2.h).
+
+Argument marshalling only: tensors are passed as raw device pointers, the
+stream is torch's current stream; every step runs in the HIP kernels. Loading
+fails loudly when the built library is missing -- there is no fallback.
+"""
+import ctypes
+import os
+
+import torch
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "libcsa2.so")
+
+CSA2_OK, CSA2_EINVAL, CSA2_ELAUNCH, CSA2_EWORKSPACE = 0, -1, -2, -3
+DIM, HEADS, IDX_HEADS, IDX_DIM, RECORD = 512, 64, 32, 128, 288
+
+_lib = None
+
+
+class Csa2Error(RuntimeError):
+    def __init__(self, code, msg):
+        super().__init__("%s (code %d)" % (msg, code))
+        self.code = code
+
+
+def load():
+    """Load libcsa2.so (built by kv_cache_compression_csa2_amd.build)."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(LIB_PATH):
+        raise ImportError("libcsa2.so is not built: run `python -m kv_cache_compression_csa2_amd.build` "
+                          "(or __graft_entry__.build())")
+    L = ctypes.CDLL(LIB_PATH)
+    vp, i64, i32, f32, sz = ctypes.c_void_p, ctypes.c_int64, ctypes.c_int32, ctypes.c_float, ctypes.c_size_t
+    L.csa2_format_version.restype = ctypes.c_int
+    L.csa2_last_error.restype = ctypes.c_char_p
+    L.fp4_kv_pack.argtypes = [vp, i64, vp, vp]
+    L.fp4_kv_unpack.argtypes = [vp, i64, vp, vp]
+    L.csa2_index_full.argtypes = [vp, vp, vp, i64, i32, i32, vp, vp, i32, vp, vp]
+    L.csa2_index_reindex.argtypes = [vp, vp, vp, i64, i32, i32, vp, vp, i32, i32, vp, vp, vp]
+    L.csa2_topk_workspace_bytes.argtypes = [i32, i64, i32]
+    L.csa2_topk_workspace_bytes.restype = sz
+    L.csa2_topk.argtypes = [vp, i32, i64, i64, vp, i32, vp, vp, vp, sz, vp]
+    L.csa2_sparse_attn_workspace_bytes.argtypes = [i32, i32]
+    L.csa2_sparse_attn_workspace_bytes.restype = sz
+    L.csa2_sparse_attn.argtypes = [vp, vp, i64, i32, i32, vp, i32, vp, i64, vp, vp, f32, vp, vp, vp, sz, vp]
+    for name in ["fp4_kv_pack", "fp4_kv_unpack", "csa2_index_full", "csa2_index_reindex", "csa2_topk",
+                 "csa2_sparse_attn"]:
+        getattr(L, name).restype = ctypes.c_int
+    _lib = L
+    return L
+
+
+EXPORTS = ["csa2_format_version", "csa2_last_error", "fp4_kv_pack", "fp4_kv_unpack", "csa2_index_full",
+           "csa2_index_reindex", "csa2_topk_workspace_bytes", "csa2_topk", "csa2_sparse_attn_workspace_bytes",
+           "csa2_sparse_attn"]
+
+
+def _ptr(t):
+    return None if t is None else ctypes.c_void_p(t.data_ptr())
+
+
+def _stream(stream):
+    if stream is None:
+        stream = torch.cuda.current_stream()
+    return ctypes.c_void_p(stream.cuda_stream)
+
+
+def _check(rc, name):
+    if rc != CSA2_OK:
+        msg = load().csa2_last_error().decode()
+        raise Csa2Error(rc, msg or name)
+
+
+def _need(t, dtype, name, cuda=True):
+    if t is None:
+        return
+    if t.dtype != dtype:
+        raise TypeError("%s must be %s, got %s" % (name, dtype, t.dtype))
+    if not t.is_contiguous():
+        raise ValueError("%s must be contiguous" % name)
+    if cuda and not t.is_cuda:
+        raise ValueError("%s must be a device tensor" % name)
+
+
+def format_version():
+    return load().csa2_format_version()
+
+
+def fp4_kv_pack(x, out=None, stream=None):
+    """bf16 [n,512] -> uint8 [n,288] FP4 records."""
+    _need(x, torch.bfloat16, "x")
+    n = x.numel() // DIM
+    if out is None:
+        out = torch.empty((n, RECORD), dtype=torch.uint8, device=x.device)
+    _need(out, torch.uint8, "out")
+    _check(load().fp4_kv_pack(_ptr(x), n, _ptr(out), _stream(stream)), "fp4_kv_pack")
+    return out
+
+
+def fp4_kv_unpack(rec, out=None, stream=None):
+    """uint8 [n,288] FP4 records -> bf16 [n,512]."""
+    _need(rec, torch.uint8, "rec")
+    n = rec.numel() // RECORD
+    if out is None:
+        out = torch.empty((n, DIM), dtype=torch.bfloat16, device=rec.device)
+    _need(out, torch.bfloat16, "out")
+    _check(load().fp4_kv_unpack(_ptr(rec), n, _ptr(out), _stream(stream)), "fp4_kv_unpack")
+    return out
+
+
+def csa2_index_full(q_idx, w, k_idx, N, q_per_seq, n_visible=None, block_size=0, scores=None, block_scores=None,
+                    stream=None):
+    """Full-mode indexer scores [nq,N] fp32 (and block maxima [nq,ceil(N/8)] when block_size == 8)."""
+    for t, dt, nm in [(q_idx, torch.bfloat16, "q_idx"), (w, torch.float32, "w"), (k_idx, torch.bfloat16, "k_idx"),
+                      (n_visible, torch.int32, "n_visible")]:
+        _need(t, dt, nm)
+    nq = q_idx.shape[0]
+    dev = q_idx.device
+    if scores is None:
+        scores = torch.empty((nq, N), dtype=torch.float32, device=dev)
+    if block_size and block_scores is None:
+        block_scores = torch.empty((nq, (N + 7) // 8), dtype=torch.float32, device=dev)
+    _check(load().csa2_index_full(_ptr(q_idx), _ptr(w), _ptr(k_idx), N, nq, q_per_seq, _ptr(n_visible),
+                                  _ptr(scores), block_size, _ptr(block_scores) if block_size else None,
+                                  _stream(stream)), "csa2_index_full")
+    return (scores, block_scores) if block_size else scores
+
+
+def csa2_index_reindex(q_idx, w, k_idx, N, q_per_seq, cand_blocks, n_visible=None, block_size=8, pool_scores=None,
+                       pool_ids=None, want_ids=True, stream=None):
+    """Reindex-mode scores over the pool [nq, nb*8] fp32 (+ entry ids [nq, nb*8] int32)."""
+    for t, dt, nm in [(q_idx, torch.bfloat16, "q_idx"), (w, torch.float32, "w"), (k_idx, torch.bfloat16, "k_idx"),
+                      (cand_blocks, torch.int32, "cand_blocks"), (n_visible, torch.int32, "n_visible")]:
+        _need(t, dt, nm)
+    nq, nb = cand_blocks.shape
+    dev = q_idx.device
+    if pool_scores is None:
+        pool_scores = torch.empty((nq, nb * block_size), dtype=torch.float32, device=dev)
+    if want_ids and pool_ids is None:
+        pool_ids = torch.empty((nq, nb * block_size), dtype=torch.int32, device=dev)
+    _check(load().csa2_index_reindex(_ptr(q_idx), _ptr(w), _ptr(k_idx), N, nq, q_per_seq, _ptr(n_visible),
+                                     _ptr(cand_blocks), nb, block_size, _ptr(pool_scores), _ptr(pool_ids),
+                                     _stream(stream)), "csa2_index_reindex")
+    return pool_scores, pool_ids
+
+
+def csa2_topk_workspace_bytes(rows, ncols, k):
+    return load().csa2_topk_workspace_bytes(rows, ncols, k)
+
+
+def csa2_topk(scores, k, row_len=None, id_map=None, out=None, workspace=None, stream=None):
+    """Per-row Top-K columns ascending, -1 padded: int32 [rows, k]."""
+    _need(scores, torch.float32, "scores")
+    _need(row_len, torch.int32, "row_len")
+    _need(id_map, torch.int32, "id_map")
+    rows, ncols = scores.shape
+    if out is None:
+        out = torch.empty((rows, k), dtype=torch.int32, device=scores.device)
+    need = csa2_topk_workspace_bytes(rows, ncols, k)
+    if workspace is None and need:
+        workspace = torch.empty((need,), dtype=torch.uint8, device=scores.device)
+    wsb = workspace.numel() * workspace.element_size() if workspace is not None else 0
+    _check(load().csa2_topk(_ptr(scores), rows, ncols, ncols, _ptr(row_len), k, _ptr(id_map), _ptr(out),
+                            _ptr(workspace), wsb, _stream(stream)), "csa2_topk")
+    return out
+
+
+def csa2_sparse_attn_workspace_bytes(nq, k):
+    return load().csa2_sparse_attn_workspace_bytes(nq, k)
+
+
+def csa2_sparse_attn(q, kv, N, q_per_seq, idx, swa=None, swa_start=None, swa_len=None, softmax_scale=None,
+                     out=None, lse=None, want_lse=True, workspace=None, stream=None):
+    """Sparse MQA attention: bf16 out [nq,64,512] (and lse [nq,64] fp32)."""
+    for t, dt, nm in [(q, torch.bfloat16, "q"), (kv, torch.uint8, "kv"), (idx, torch.int32, "idx"),
+                      (swa, torch.bfloat16, "swa"), (swa_start, torch.int32, "swa_start"),
+                      (swa_len, torch.int32, "swa_len")]:
+        _need(t, dt, nm)
+    nq = q.shape[0]
+    k = idx.shape[1]
+    T = swa.shape[-2] if swa is not None else 0
+    if softmax_scale is None:
+        softmax_scale = DIM ** -0.5
+    if out is None:
+        out = torch.empty((nq, HEADS, DIM), dtype=torch.bfloat16, device=q.device)
+    if want_lse and lse is None:
+        lse = torch.empty((nq, HEADS), dtype=torch.float32, device=q.device)
+    need = csa2_sparse_attn_workspace_bytes(nq, k)
+    if workspace is None and need:
+        workspace = torch.empty((need,), dtype=torch.uint8, device=q.device)
+    wsb = workspace.numel() * workspace.element_size() if workspace is not None else 0
+    _check(load().csa2_sparse_attn(_ptr(q), _ptr(kv), N, nq, q_per_seq, _ptr(idx), k, _ptr(swa), T,
+                                   _ptr(swa_start), _ptr(swa_len), float(softmax_scale), _ptr(out), _ptr(lse),
+                                   _ptr(workspace), wsb, _stream(stream)), "csa2_sparse_attn")
+    return out, lse

@@ -1,0 +1,140 @@
+// C ABI of the CSA2 hot path (declared in include/csa2.h): argument checks on
+// the host, then kernel launches on the caller's stream. No allocation, no
+// state besides the calling thread's last error message.
+#include <stdarg.h>
+#include <stdio.h>
+
+#include "../../include/csa2.h"
+#include "launch.h"
+
+namespace {
+
+thread_local char g_err[256] = "";
+
+int fail(int code, const char* fmt, ...) {
+    va_list ap;
+    va_start(ap, fmt);
+    vsnprintf(g_err, sizeof(g_err), fmt, ap);
+    va_end(ap);
+    return code;
+}
+
+int launched(const char* what) {
+    const hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return fail(CSA2_ELAUNCH, "%s: launch failed: %s", what, hipGetErrorString(e));
+    return CSA2_OK;
+}
+
+constexpr int64_t kMaxN = 2147483647LL;
+
+}  // namespace
+
+extern "C" {
+
+int csa2_format_version(void) { return 1; }
+
+const char* csa2_last_error(void) { return g_err; }
+
+int fp4_kv_pack(const uint16_t* x_bf16, int64_t n, uint8_t* out, hipStream_t stream) {
+    if (n < 0) return fail(CSA2_EINVAL, "fp4_kv_pack: n < 0");
+    if (n > 0 && (!x_bf16 || !out)) return fail(CSA2_EINVAL, "fp4_kv_pack: null pointer");
+    (void)hipGetLastError();
+    csa2::launch_fp4_pack(x_bf16, n, out, stream);
+    return launched("fp4_kv_pack");
+}
+
+int fp4_kv_unpack(const uint8_t* in, int64_t n, uint16_t* y_bf16, hipStream_t stream) {
+    if (n < 0) return fail(CSA2_EINVAL, "fp4_kv_unpack: n < 0");
+    if (n > 0 && (!in || !y_bf16)) return fail(CSA2_EINVAL, "fp4_kv_unpack: null pointer");
+    (void)hipGetLastError();
+    csa2::launch_fp4_unpack(in, n, y_bf16, stream);
+    return launched("fp4_kv_unpack");
+}
+
+static int check_index_common(const char* who, const uint16_t* q_idx, const float* w, const uint16_t* k_idx,
+                              int64_t N, int32_t nq, int32_t q_per_seq) {
+    if (nq < 0) return fail(CSA2_EINVAL, "%s: nq < 0", who);
+    if (N < 1 || N > kMaxN) return fail(CSA2_EINVAL, "%s: N must be in [1, 2^31-1]", who);
+    if (q_per_seq < 1) return fail(CSA2_EINVAL, "%s: q_per_seq < 1", who);
+    if (nq % q_per_seq != 0) return fail(CSA2_EINVAL, "%s: q_per_seq must divide nq", who);
+    if (nq > 0 && (!q_idx || !w || !k_idx)) return fail(CSA2_EINVAL, "%s: null pointer", who);
+    return CSA2_OK;
+}
+
+int csa2_index_full(const uint16_t* q_idx, const float* w, const uint16_t* k_idx, int64_t N, int32_t nq,
+                    int32_t q_per_seq, const int32_t* n_visible, float* scores, int32_t block_size,
+                    float* block_scores, hipStream_t stream) {
+    int rc = check_index_common("csa2_index_full", q_idx, w, k_idx, N, nq, q_per_seq);
+    if (rc) return rc;
+    if (nq > 0 && !scores) return fail(CSA2_EINVAL, "csa2_index_full: null scores");
+    if (block_size != 0 && block_size != 8) return fail(CSA2_EINVAL, "csa2_index_full: block_size must be 0 or 8");
+    if (block_size == 8 && nq > 0 && !block_scores)
+        return fail(CSA2_EINVAL, "csa2_index_full: block_scores required when block_size == 8");
+    (void)hipGetLastError();
+    csa2::launch_index_full(q_idx, w, k_idx, N, nq, q_per_seq, n_visible, scores, block_size, block_scores, stream);
+    return launched("csa2_index_full");
+}
+
+int csa2_index_reindex(const uint16_t* q_idx, const float* w, const uint16_t* k_idx, int64_t N, int32_t nq,
+                       int32_t q_per_seq, const int32_t* n_visible, const int32_t* cand_blocks, int32_t nb,
+                       int32_t block_size, float* pool_scores, int32_t* pool_ids, hipStream_t stream) {
+    int rc = check_index_common("csa2_index_reindex", q_idx, w, k_idx, N, nq, q_per_seq);
+    if (rc) return rc;
+    if (block_size != 8) return fail(CSA2_EINVAL, "csa2_index_reindex: block_size must be 8");
+    if (nb < 1 || nb > 65536) return fail(CSA2_EINVAL, "csa2_index_reindex: nb must be in [1, 65536]");
+    if (nq > 0 && (!cand_blocks || !pool_scores)) return fail(CSA2_EINVAL, "csa2_index_reindex: null pointer");
+    (void)hipGetLastError();
+    csa2::launch_index_reindex(q_idx, w, k_idx, N, nq, q_per_seq, n_visible, cand_blocks, nb, pool_scores, pool_ids,
+                               stream);
+    return launched("csa2_index_reindex");
+}
+
+size_t csa2_topk_workspace_bytes(int32_t rows, int64_t ncols, int32_t k) {
+    if (rows <= 0 || ncols <= 0 || k < 1 || k > CSA2_MAX_TOPK) return 0;
+    return csa2::topk_workspace_bytes(rows, ncols, k);
+}
+
+int csa2_topk(const float* scores, int32_t rows, int64_t ncols, int64_t ld, const int32_t* row_len, int32_t k,
+              const int32_t* id_map, int32_t* out_idx, void* workspace, size_t ws_bytes, hipStream_t stream) {
+    if (rows < 0) return fail(CSA2_EINVAL, "csa2_topk: rows < 0");
+    if (ncols < 1 || ncols > kMaxN) return fail(CSA2_EINVAL, "csa2_topk: ncols must be in [1, 2^31-1]");
+    if (ld < ncols) return fail(CSA2_EINVAL, "csa2_topk: ld < ncols");
+    if (k < 1 || k > CSA2_MAX_TOPK) return fail(CSA2_EINVAL, "csa2_topk: k must be in [1, %d]", CSA2_MAX_TOPK);
+    if (rows > 0 && (!scores || !out_idx)) return fail(CSA2_EINVAL, "csa2_topk: null pointer");
+    const size_t need = csa2_topk_workspace_bytes(rows, ncols, k);
+    if (rows > 0 && need > 0 && (!workspace || ws_bytes < need))
+        return fail(CSA2_EWORKSPACE, "csa2_topk: workspace needs %zu bytes", need);
+    (void)hipGetLastError();
+    csa2::launch_topk(scores, rows, ncols, ld, row_len, k, id_map, out_idx, workspace, stream);
+    return launched("csa2_topk");
+}
+
+size_t csa2_sparse_attn_workspace_bytes(int32_t nq, int32_t k) {
+    if (nq <= 0 || k < 0 || k > CSA2_MAX_TOPK) return 0;
+    return csa2::attn_workspace_bytes(nq, k);
+}
+
+int csa2_sparse_attn(const uint16_t* q, const uint8_t* kv, int64_t N, int32_t nq, int32_t q_per_seq,
+                     const int32_t* idx, int32_t k, const uint16_t* swa, int64_t T, const int32_t* swa_start,
+                     const int32_t* swa_len, float softmax_scale, uint16_t* out, float* lse, void* workspace,
+                     size_t ws_bytes, hipStream_t stream) {
+    if (nq < 0) return fail(CSA2_EINVAL, "csa2_sparse_attn: nq < 0");
+    if (N < 1 || N > kMaxN) return fail(CSA2_EINVAL, "csa2_sparse_attn: N must be in [1, 2^31-1]");
+    if (q_per_seq < 1 || nq % q_per_seq != 0)
+        return fail(CSA2_EINVAL, "csa2_sparse_attn: q_per_seq must be >= 1 and divide nq");
+    if (k < 0 || k > CSA2_MAX_TOPK) return fail(CSA2_EINVAL, "csa2_sparse_attn: k must be in [0, %d]", CSA2_MAX_TOPK);
+    if (nq > 0 && (!q || !kv || !out)) return fail(CSA2_EINVAL, "csa2_sparse_attn: null pointer");
+    if (nq > 0 && k > 0 && !idx) return fail(CSA2_EINVAL, "csa2_sparse_attn: null idx");
+    if (swa && (T < 1 || !swa_start || !swa_len))
+        return fail(CSA2_EINVAL, "csa2_sparse_attn: a window needs T >= 1, swa_start and swa_len");
+    if (!(softmax_scale == softmax_scale)) return fail(CSA2_EINVAL, "csa2_sparse_attn: softmax_scale is NaN");
+    const size_t need = csa2_sparse_attn_workspace_bytes(nq, k);
+    if (nq > 0 && need > 0 && (!workspace || ws_bytes < need))
+        return fail(CSA2_EWORKSPACE, "csa2_sparse_attn: workspace needs %zu bytes", need);
+    (void)hipGetLastError();
+    csa2::launch_sparse_attn(q, kv, N, nq, q_per_seq, idx, k, swa, swa ? T : 0, swa ? swa_start : nullptr,
+                             swa ? swa_len : nullptr, softmax_scale, out, lse, workspace, stream);
+    return launched("csa2_sparse_attn");
+}
+
+}  // extern "C"

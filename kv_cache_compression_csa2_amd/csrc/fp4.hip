@@ -1,0 +1,88 @@
+// FP4 main-KV records: pack (bf16 -> E2M1 codes + E4M3 scales) and unpack.
+// Format: eogee.com report on DeepSeek-V4.1-Flash, 3.4 (E2M1 elements, one
+// E4M3 scale per 16 channels, no second-level scale); nxbn.cn walkthrough 2.3.
+#include "device_common.h"
+#include "launch.h"
+
+namespace csa2 {
+
+// One thread per 16-channel group: 32 threads per 512-channel row, so a wave
+// covers two rows; loads are 32 contiguous bytes per thread.
+__global__ __launch_bounds__(256) void fp4_pack_kernel(const uint16_t* __restrict__ x, int64_t n,
+                                                       uint8_t* __restrict__ out) {
+    const int64_t t = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+    const int64_t row = t >> 5;
+    const int g = (int)(t & 31);
+    if (row >= n) return;
+    const uint4* src = reinterpret_cast<const uint4*>(x + row * kDim + g * kGroup);
+    const uint4 v0 = src[0], v1 = src[1];
+    const uint32_t wv[8] = {v0.x, v0.y, v0.z, v0.w, v1.x, v1.y, v1.z, v1.w};
+    float xs[16];
+    float amax = 0.0f;
+#pragma unroll
+    for (int i = 0; i < 8; i++) {
+        xs[2 * i] = bf16_bits_to_float(wv[i] & 0xFFFFu);
+        xs[2 * i + 1] = bf16_bits_to_float(wv[i] >> 16);
+    }
+#pragma unroll
+    for (int i = 0; i < 16; i++) amax = fmaxf(amax, fabsf(xs[i]));
+    const uint32_t sb = e4m3_encode_rne_sat(amax / 6.0f);
+    const float S = e4m3_to_float(sb);
+    // Midpoints of the E2M1 grid times S (exact in fp32): an exact tie goes to
+    // the neighbour with the even code, so the comparison is >= where the upper
+    // neighbour is even (0.75, 1.75, 3.5) and > otherwise.
+    const float t025 = 0.25f * S, t075 = 0.75f * S, t125 = 1.25f * S, t175 = 1.75f * S;
+    const float t250 = 2.5f * S, t350 = 3.5f * S, t500 = 5.0f * S;
+    uint32_t lo = 0, hi = 0;
+#pragma unroll
+    for (int i = 0; i < 16; i++) {
+        const float a = fabsf(xs[i]);
+        uint32_t c = (uint32_t)(a > t025) + (uint32_t)(a >= t075) + (uint32_t)(a > t125) + (uint32_t)(a >= t175) +
+                     (uint32_t)(a > t250) + (uint32_t)(a >= t350) + (uint32_t)(a > t500);
+        if (S == 0.0f) c = 0;
+        if (c != 0 && xs[i] < 0.0f) c |= 8u;
+        if (i < 8)
+            lo |= c << (4 * i);
+        else
+            hi |= c << (4 * (i - 8));
+    }
+    uint8_t* rec = out + row * kRecord;
+    *reinterpret_cast<uint2*>(rec + g * 8) = make_uint2(lo, hi);
+    rec[kCodeBytes + g] = (uint8_t)sb;
+}
+
+// One thread per 16-channel group: 8 code bytes + 1 scale byte -> 32 bytes.
+__global__ __launch_bounds__(256) void fp4_unpack_kernel(const uint8_t* __restrict__ in, int64_t n,
+                                                         uint16_t* __restrict__ y) {
+    const int64_t t = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+    const int64_t row = t >> 5;
+    const int g = (int)(t & 31);
+    if (row >= n) return;
+    const uint8_t* rec = in + row * kRecord;
+    const uint2 c = *reinterpret_cast<const uint2*>(rec + g * 8);
+    const float hs = 0.5f * e4m3_to_float(rec[kCodeBytes + g]);
+    uint32_t o[8];
+    dequant8(c.x, hs, o);
+    dequant8(c.y, hs, o + 4);
+    uint4* dst = reinterpret_cast<uint4*>(y + row * kDim + g * kGroup);
+    dst[0] = make_uint4(o[0], o[1], o[2], o[3]);
+    dst[1] = make_uint4(o[4], o[5], o[6], o[7]);
+}
+
+int launch_fp4_pack(const uint16_t* x, int64_t n, uint8_t* out, hipStream_t s) {
+    if (n == 0) return 0;
+    const int64_t threads = n * 32;
+    const int64_t blocks = (threads + 255) / 256;
+    hipLaunchKernelGGL(fp4_pack_kernel, dim3((unsigned)blocks), dim3(256), 0, s, x, n, out);
+    return 0;
+}
+
+int launch_fp4_unpack(const uint8_t* in, int64_t n, uint16_t* y, hipStream_t s) {
+    if (n == 0) return 0;
+    const int64_t threads = n * 32;
+    const int64_t blocks = (threads + 255) / 256;
+    hipLaunchKernelGGL(fp4_unpack_kernel, dim3((unsigned)blocks), dim3(256), 0, s, in, n, y);
+    return 0;
+}
+
+}  // namespace csa2

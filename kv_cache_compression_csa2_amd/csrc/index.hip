@@ -1,0 +1,287 @@
+// Indexer scoring: score(q, i) = sum_h w[q][h] * max(q_idx[q][h] . k_idx[i], 0)
+// over 32 heads x 128 dims (eogee.com report on DeepSeek-V4.1-Flash, 3.2 and
+// 3.3; nxbn.cn walkthrough 3.3 for the 32 x 128 geometry), plus the 8-position
+// block maximum of the hierarchical indexer (eogee.com report 3.3).
+//
+// The head contraction runs on 32x32x16 bf16 MFMA: M = the 32 heads of one
+// query, N = 32 entries, K = 128 channels in 8 steps. Each lane of the result
+// holds 16 heads of one entry; the ReLU-weighted head sum runs in fp32 on the
+// lane, then one cross-half exchange adds the other 16 heads.
+//
+// Two kernels:
+//  * index_stream_kernel -- one query per workgroup slice; each wave streams
+//    32-entry tiles of the indexer K straight from HBM into MFMA operand
+//    registers (2 tiles in flight). Bound by HBM (256 B per entry per query).
+//    Serves decode (a sequence per query) and the Reindex pool gather.
+//  * index_prefill_kernel -- many queries over one sequence: a workgroup holds
+//    8 queries' operands in registers and stages 64-entry K tiles in LDS, so
+//    each K byte read from L2 feeds 8 queries. Bound by MFMA.
+#include <math.h>
+
+#include "device_common.h"
+#include "launch.h"
+
+namespace csa2 {
+
+namespace {
+
+constexpr int kStreamThreads = 256;
+constexpr int kStreamWaves = kStreamThreads / 64;
+
+struct StreamTile {
+    bf16x8 b[8];
+    int64_t ent;
+    bool valid;
+};
+
+// Row of the accumulator held in register r by a lane of half `half` (32x32 layout).
+CSA2_DEVINL int acc_row(int r, int half) { return (r >> 2) * 8 + half * 4 + (r & 3); }
+
+template <bool kReindex>
+__global__ __launch_bounds__(kStreamThreads) void index_stream_kernel(
+    const uint16_t* __restrict__ q_idx, const float* __restrict__ w, const uint16_t* __restrict__ k_idx, int64_t N,
+    int32_t q_per_seq, const int32_t* __restrict__ n_visible, const int32_t* __restrict__ cand_blocks, int32_t nb,
+    float* __restrict__ scores, float* __restrict__ block_scores, int32_t* __restrict__ pool_ids, int64_t ncols,
+    int64_t ntiles, int32_t wgs_per_q, int32_t tiles_per_wg) {
+    const int64_t q = blockIdx.x / wgs_per_q;
+    const int64_t chunk = blockIdx.x % wgs_per_q;
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    const int half = lane >> 5, col_in_tile = lane & 31;
+    const int64_t seq = q / q_per_seq;
+    int64_t nv = n_visible ? (int64_t)n_visible[q] : N;
+    nv = nv < N ? nv : N;
+
+    // A operand: head = lane % 32, channels 16j + 8*half .. +8 for step j.
+    const uint4* qsrc = reinterpret_cast<const uint4*>(q_idx + (q * kIdxHeads + col_in_tile) * kIdxDim) + half;
+    bf16x8 a[8];
+#pragma unroll
+    for (int j = 0; j < 8; j++) a[j] = as_bf16x8(qsrc[2 * j]);
+    float wr[16];
+#pragma unroll
+    for (int r = 0; r < 16; r++) wr[r] = w[q * kIdxHeads + acc_row(r, half)];
+
+    const uint16_t* kseq = k_idx + seq * N * kIdxDim;
+    const int64_t t_begin = chunk * tiles_per_wg;
+    const int64_t t_end = (t_begin + tiles_per_wg < ntiles) ? t_begin + tiles_per_wg : ntiles;
+    const int64_t nblk = (N + 7) >> 3;
+
+    auto load = [&](int64_t t, StreamTile& st) {
+        const int64_t col = t * 32 + col_in_tile;
+        int64_t ent;
+        bool valid;
+        if (kReindex) {
+            const int32_t blk = (col < ncols) ? cand_blocks[q * nb + (col >> 3)] : -1;
+            ent = (int64_t)blk * 8 + (col & 7);
+            valid = blk >= 0 && ent < nv;
+        } else {
+            ent = col;
+            valid = col < nv;
+        }
+        st.ent = ent;
+        st.valid = valid;
+        const u32x4* src = reinterpret_cast<const u32x4*>(kseq + (valid ? ent : 0) * kIdxDim) + half;
+#pragma unroll
+        for (int j = 0; j < 8; j++) st.b[j] = as_bf16x8(__builtin_nontemporal_load(src + 2 * j));
+    };
+
+    auto finish = [&](int64_t t, const StreamTile& st) {
+        f32x16 acc = {};
+#pragma unroll
+        for (int j = 0; j < 8; j++) acc = mfma32x32x16(a[j], st.b[j], acc);
+        float s = 0.0f;
+#pragma unroll
+        for (int r = 0; r < 16; r++) s = fmaf(wr[r], fmaxf(acc[r], 0.0f), s);
+        s += __shfl_xor(s, 32);
+        if (!st.valid) s = -INFINITY;
+        const int64_t col = t * 32 + col_in_tile;
+        if (half == 0 && col < ncols) scores[q * ncols + col] = s;
+        if (kReindex) {
+            if (pool_ids && half == 0 && col < ncols) pool_ids[q * ncols + col] = st.valid ? (int32_t)st.ent : -1;
+        } else if (block_scores) {
+            float m = s;
+            m = fmaxf(m, __shfl_xor(m, 1));
+            m = fmaxf(m, __shfl_xor(m, 2));
+            m = fmaxf(m, __shfl_xor(m, 4));
+            if (half == 0 && (lane & 7) == 0 && col < ncols) block_scores[q * nblk + (col >> 3)] = m;
+        }
+    };
+
+    int64_t t = t_begin + wave;
+    if (t >= t_end) return;
+    StreamTile s0, s1;
+    load(t, s0);
+    while (true) {
+        const int64_t t1 = t + kStreamWaves;
+        if (t1 < t_end) load(t1, s1);
+        finish(t, s0);
+        if (t1 >= t_end) break;
+        const int64_t t2 = t1 + kStreamWaves;
+        if (t2 < t_end) load(t2, s0);
+        finish(t1, s1);
+        if (t2 >= t_end) break;
+        t = t2;
+    }
+}
+
+constexpr int kPfQueries = 8;          // queries per workgroup (2 per wave)
+constexpr int kPfSub = 64;             // entries per LDS tile
+constexpr int kPfRow = 256 + 16;       // padded LDS row bytes
+constexpr int kPfChunk = 4096;         // entries per workgroup
+
+__global__ __launch_bounds__(256, 2) void index_prefill_kernel(
+    const uint16_t* __restrict__ q_idx, const float* __restrict__ w, const uint16_t* __restrict__ k_idx, int64_t N,
+    int32_t q_per_seq, const int32_t* __restrict__ n_visible, float* __restrict__ scores,
+    float* __restrict__ block_scores, int32_t nchunks) {
+    __shared__ __attribute__((aligned(16))) uint8_t lds[2][kPfSub * kPfRow];
+    const int b = blockIdx.x;
+    int chunk, qg;
+    if ((nchunks & 7) == 0) {
+        // Consecutive workgroups land on different XCDs (round-robin); give each
+        // XCD a fixed slice of entry chunks so its L2 keeps serving the same K.
+        const int per = nchunks >> 3;
+        chunk = (b & 7) * per + (b >> 3) % per;
+        qg = b / nchunks;
+    } else {
+        chunk = b % nchunks;
+        qg = b / nchunks;
+    }
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const int half = lane >> 5, col_in_tile = lane & 31;
+    const int64_t qa = (int64_t)qg * kPfQueries + 2 * wave, qb = qa + 1;
+    const int64_t seq = ((int64_t)qg * kPfQueries) / q_per_seq;
+    int64_t nva = n_visible ? (int64_t)n_visible[qa] : N, nvb = n_visible ? (int64_t)n_visible[qb] : N;
+    nva = nva < N ? nva : N;
+    nvb = nvb < N ? nvb : N;
+
+    bf16x8 aa[8], ab[8];
+    {
+        const uint4* sa = reinterpret_cast<const uint4*>(q_idx + (qa * kIdxHeads + col_in_tile) * kIdxDim) + half;
+        const uint4* sb = reinterpret_cast<const uint4*>(q_idx + (qb * kIdxHeads + col_in_tile) * kIdxDim) + half;
+#pragma unroll
+        for (int j = 0; j < 8; j++) {
+            aa[j] = as_bf16x8(sa[2 * j]);
+            ab[j] = as_bf16x8(sb[2 * j]);
+        }
+    }
+    float wa[16], wb[16];
+#pragma unroll
+    for (int r = 0; r < 16; r++) {
+        wa[r] = w[qa * kIdxHeads + acc_row(r, half)];
+        wb[r] = w[qb * kIdxHeads + acc_row(r, half)];
+    }
+
+    const uint16_t* kseq = k_idx + seq * N * kIdxDim;
+    const int64_t e_begin = (int64_t)chunk * kPfChunk;
+    const int64_t e_end = (e_begin + kPfChunk < N) ? e_begin + kPfChunk : N;
+    const int nsub = (int)((e_end - e_begin + kPfSub - 1) / kPfSub);
+    const int64_t nblk = (N + 7) >> 3;
+
+    struct Pre {
+        uint4 v[4];
+    };
+    auto gload = [&](int st) {
+        Pre p;
+#pragma unroll
+        for (int i = 0; i < 4; i++) {
+            const int u = i * 256 + tid;  // 16-byte unit within the 64 x 256 B tile
+            const int row = u >> 4, c16 = u & 15;
+            int64_t e = e_begin + (int64_t)st * kPfSub + row;
+            e = e < N ? e : 0;
+            p.v[i] = reinterpret_cast<const uint4*>(kseq + e * kIdxDim)[c16];
+        }
+        return p;
+    };
+    auto lstore = [&](int buf, const Pre& p) {
+#pragma unroll
+        for (int i = 0; i < 4; i++) {
+            const int u = i * 256 + tid;
+            const int row = u >> 4, c16 = u & 15;
+            *reinterpret_cast<uint4*>(&lds[buf][row * kPfRow + c16 * 16]) = p.v[i];
+        }
+    };
+    auto epilogue = [&](const f32x16& acc, const float (&wr)[16], int64_t q, int64_t nv, int64_t col) {
+        float s = 0.0f;
+#pragma unroll
+        for (int r = 0; r < 16; r++) s = fmaf(wr[r], fmaxf(acc[r], 0.0f), s);
+        s += __shfl_xor(s, 32);
+        if (col >= nv) s = -INFINITY;
+        if (half == 0 && col < N) scores[q * N + col] = s;
+        if (block_scores) {
+            float m = s;
+            m = fmaxf(m, __shfl_xor(m, 1));
+            m = fmaxf(m, __shfl_xor(m, 2));
+            m = fmaxf(m, __shfl_xor(m, 4));
+            if (half == 0 && (lane & 7) == 0 && col < N) block_scores[q * nblk + (col >> 3)] = m;
+        }
+    };
+
+    lstore(0, gload(0));
+    __syncthreads();
+    for (int st = 0; st < nsub; st++) {
+        const bool more = st + 1 < nsub;
+        // the last iteration re-reads tile 0 (in bounds) and discards it
+        const Pre nxt = gload(more ? st + 1 : 0);
+        const uint8_t* tile = lds[st & 1];
+#pragma unroll
+        for (int h2 = 0; h2 < 2; h2++) {
+            const uint8_t* rowp = tile + (h2 * 32 + col_in_tile) * kPfRow + half * 16;
+            f32x16 acca = {}, accb = {};
+#pragma unroll
+            for (int j = 0; j < 8; j++) {
+                const bf16x8 bj = as_bf16x8(*reinterpret_cast<const uint4*>(rowp + j * 32));
+                acca = mfma32x32x16(aa[j], bj, acca);
+                accb = mfma32x32x16(ab[j], bj, accb);
+            }
+            const int64_t col = e_begin + (int64_t)st * kPfSub + h2 * 32 + col_in_tile;
+            epilogue(acca, wa, qa, nva, col);
+            epilogue(accb, wb, qb, nvb, col);
+        }
+        if (more) lstore((st + 1) & 1, nxt);
+        __syncthreads();
+    }
+}
+
+}  // namespace
+
+int launch_index_full(const uint16_t* q_idx, const float* w, const uint16_t* k_idx, int64_t N, int32_t nq,
+                      int32_t q_per_seq, const int32_t* n_visible, float* scores, int32_t block_size,
+                      float* block_scores, hipStream_t s) {
+    if (nq == 0) return 0;
+    float* bs = block_size > 0 ? block_scores : nullptr;
+    if (q_per_seq % kPfQueries == 0) {
+        const int32_t nchunks = (int32_t)((N + kPfChunk - 1) / kPfChunk);
+        const int64_t grid = (int64_t)(nq / kPfQueries) * nchunks;
+        hipLaunchKernelGGL(index_prefill_kernel, dim3((unsigned)grid), dim3(256), 0, s, q_idx, w, k_idx, N,
+                           q_per_seq, n_visible, scores, bs, nchunks);
+        return 0;
+    }
+    const int64_t ntiles = (N + 31) / 32;
+    const int64_t total = ntiles * nq;
+    int64_t tpw = (total + 2047) / 2048;
+    tpw = ((tpw + kStreamWaves - 1) / kStreamWaves) * kStreamWaves;
+    if (tpw < kStreamWaves) tpw = kStreamWaves;
+    const int64_t wgs_per_q = (ntiles + tpw - 1) / tpw;
+    hipLaunchKernelGGL(index_stream_kernel<false>, dim3((unsigned)(wgs_per_q * nq)), dim3(kStreamThreads), 0, s,
+                       q_idx, w, k_idx, N, q_per_seq, n_visible, (const int32_t*)nullptr, 0, scores, bs,
+                       (int32_t*)nullptr, N, ntiles, (int32_t)wgs_per_q, (int32_t)tpw);
+    return 0;
+}
+
+int launch_index_reindex(const uint16_t* q_idx, const float* w, const uint16_t* k_idx, int64_t N, int32_t nq,
+                         int32_t q_per_seq, const int32_t* n_visible, const int32_t* cand_blocks, int32_t nb,
+                         float* pool_scores, int32_t* pool_ids, hipStream_t s) {
+    if (nq == 0) return 0;
+    const int64_t ncols = (int64_t)nb * 8;
+    const int64_t ntiles = (ncols + 31) / 32;
+    const int64_t total = ntiles * nq;
+    int64_t tpw = (total + 2047) / 2048;
+    tpw = ((tpw + kStreamWaves - 1) / kStreamWaves) * kStreamWaves;
+    if (tpw < kStreamWaves) tpw = kStreamWaves;
+    const int64_t wgs_per_q = (ntiles + tpw - 1) / tpw;
+    hipLaunchKernelGGL(index_stream_kernel<true>, dim3((unsigned)(wgs_per_q * nq)), dim3(kStreamThreads), 0, s,
+                       q_idx, w, k_idx, N, q_per_seq, n_visible, cand_blocks, nb, pool_scores, (float*)nullptr,
+                       pool_ids, ncols, ntiles, (int32_t)wgs_per_q, (int32_t)tpw);
+    return 0;
+}
+
+}  // namespace csa2

@@ -1,0 +1,97 @@
+"""One step of the CSA2 hot path, composed from the C-ABI calls.
+
+Layer modes (titansim blog, CSA2 paragraph; eogee.com report 3.2 and 3.3):
+  Full     score every visible entry, keep its own Top-512 (and, in the
+           hierarchical decoder, the 2048 best 8-position blocks as the pool);
+  Reindex  the layer's own indexer Q over the shared indexer K, inside the pool,
+           keeps its own Top-512;
+  Reuse    attends with the indices of the previous layer, no scoring.
+Every layer attends with its own Q and its own window KV.
+
+Buffers are allocated once per Step object, so a timed loop allocates nothing.
+"""
+import torch
+
+from . import _lib as L
+from .workloads import BLOCK, POOL_BLOCKS, TOPK
+
+
+class Step:
+    """Pre-allocated outputs for one workload; call run(...) per step."""
+
+    def __init__(self, wl, device):
+        self.wl = wl
+        nq, N = wl.nq, wl.N
+        f32, i32, bf16 = torch.float32, torch.int32, torch.bfloat16
+        self.scores = torch.empty((nq, N), dtype=f32, device=device)
+        self.blocks = torch.empty((nq, (N + 7) // 8), dtype=f32, device=device) if wl.hier else None
+        self.top = [torch.empty((nq, TOPK), dtype=i32, device=device) for _ in range(wl.n_index_layers)]
+        self.cand = torch.empty((nq, POOL_BLOCKS), dtype=i32, device=device) if wl.hier else None
+        pool = POOL_BLOCKS * BLOCK
+        self.pool_scores = torch.empty((nq, pool), dtype=f32, device=device) if wl.hier else None
+        self.pool_ids = torch.empty((nq, pool), dtype=i32, device=device) if wl.hier else None
+        self.out = [torch.empty((nq, L.HEADS, L.DIM), dtype=bf16, device=device) for _ in range(wl.n_attn_layers)]
+        self.lse = [torch.empty((nq, L.HEADS), dtype=f32, device=device) for _ in range(wl.n_attn_layers)]
+
+        def ws(nbytes):
+            return torch.empty((max(nbytes, 1),), dtype=torch.uint8, device=device)
+
+        self.ws_topk = ws(max(L.csa2_topk_workspace_bytes(nq, N, TOPK),
+                              L.csa2_topk_workspace_bytes(nq, (N + 7) // 8, POOL_BLOCKS) if wl.hier else 0,
+                              L.csa2_topk_workspace_bytes(nq, pool, TOPK) if wl.hier else 0))
+        self.ws_attn = ws(L.csa2_sparse_attn_workspace_bytes(nq, TOPK))
+
+    def index_full(self, k_idx):
+        wl = self.wl
+        if wl.hier:
+            L.csa2_index_full(wl.q_idx[0], wl.w[0], k_idx, wl.N, wl.q_per_seq, wl.n_visible, 8, self.scores,
+                              self.blocks)
+        else:
+            L.csa2_index_full(wl.q_idx[0], wl.w[0], k_idx, wl.N, wl.q_per_seq, wl.n_visible, 0, self.scores)
+
+    def topk_full(self):
+        wl = self.wl
+        L.csa2_topk(self.scores, TOPK, row_len=wl.n_visible, out=self.top[0], workspace=self.ws_topk)
+        if wl.hier:
+            L.csa2_topk(self.blocks, POOL_BLOCKS, out=self.cand, workspace=self.ws_topk)
+
+    def reindex(self, layer, k_idx):
+        wl = self.wl
+        L.csa2_index_reindex(wl.q_idx[layer], wl.w[layer], k_idx, wl.N, wl.q_per_seq, self.cand, wl.n_visible,
+                             pool_scores=self.pool_scores, pool_ids=self.pool_ids)
+        L.csa2_topk(self.pool_scores, TOPK, id_map=self.pool_ids, out=self.top[layer], workspace=self.ws_topk)
+
+    def attend(self, layer, kv, idx):
+        wl = self.wl
+        L.csa2_sparse_attn(wl.q[layer], kv, wl.N, wl.q_per_seq, idx, wl.swa[layer], wl.swa_start, wl.swa_len,
+                           out=self.out[layer], lse=self.lse[layer], workspace=self.ws_attn)
+
+    def run(self, k_idx, kv):
+        """The whole hot path once: Full (+ Reindex x3 + Reuse when hierarchical)."""
+        self.index_full(k_idx)
+        self.topk_full()
+        self.attend(0, kv, self.top[0])
+        if self.wl.hier:
+            for layer in (1, 2, 3):
+                self.reindex(layer, k_idx)
+                self.attend(layer, kv, self.top[layer])
+            self.attend(4, kv, self.top[3])  # Reuse: inherits the last Reindex layer's indices
+        return self.out
+
+
+def pack_workload_kv(wl, device):
+    """Main-KV cache of a workload, packed on the GPU where rows come as bf16."""
+    from .workloads import RECORD, clustered_kv_rows
+    if wl.kv is None:
+        kv = torch.empty((wl.nseq, wl.N, RECORD), dtype=torch.uint8, device=device)
+        for s in range(wl.nseq):
+            for r0 in range(0, wl.N, 262144):
+                n = min(262144, wl.N - r0)
+                rows = clustered_kv_rows(wl.clustered_seed, s, wl.N, device, r0, n)
+                L.fp4_kv_pack(rows.contiguous(), out=kv[s, r0:r0 + n])
+    else:
+        kv = wl.kv.clone()
+    if wl.kv_prepack is not None:
+        packed = L.fp4_kv_pack(wl.kv_prepack)
+        kv.view(-1, RECORD)[wl.kv_prepack_rows] = packed
+    return kv

@@ -1,0 +1,128 @@
+"""The C-ABI library loads, exports every declared call, and rejects bad
+arguments on the host before touching the GPU. CPU only (no kernel launches)."""
+import ctypes
+import os
+import re
+
+import pytest
+
+import kv_cache_compression_csa2_amd as K
+from kv_cache_compression_csa2_amd import _lib as L
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+
+def _declared():
+    src = open(os.path.join(ROOT, "include", "csa2.h")).read()
+    src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
+    return sorted(set(re.findall(r"^\s*(?:const\s+)?\w+\*?\s+\*?(\w+)\s*\(", src, flags=re.M)))
+
+
+def test_header_declares_the_boundary():
+    names = _declared()
+    for n in ["fp4_kv_pack", "fp4_kv_unpack", "csa2_index_full", "csa2_index_reindex", "csa2_topk",
+              "csa2_topk_workspace_bytes", "csa2_sparse_attn", "csa2_sparse_attn_workspace_bytes",
+              "csa2_format_version", "csa2_last_error"]:
+        assert n in names
+    assert sorted(L.EXPORTS) == names
+
+
+def test_library_exports_every_declared_symbol():
+    lib = K.load()
+    for n in _declared():
+        assert hasattr(lib, n), n
+    assert K.format_version() == 1
+
+
+P = ctypes.c_void_p(16)  # never dereferenced: every call below fails validation first
+S = ctypes.c_void_p(0)
+
+
+def _err(rc):
+    return rc, K.load().csa2_last_error().decode()
+
+
+@pytest.mark.parametrize("args,frag", [
+    ((P, -1, P, S), "n < 0"),
+    ((None, 5, P, S), "null"),
+])
+def test_pack_rejects(args, frag):
+    rc, msg = _err(K.load().fp4_kv_pack(*args))
+    assert rc == L.CSA2_EINVAL and frag in msg
+
+
+@pytest.mark.parametrize("kw,frag", [
+    (dict(N=0), "N must be"),
+    (dict(nq=-1), "nq < 0"),
+    (dict(q_per_seq=0), "q_per_seq < 1"),
+    (dict(nq=6, q_per_seq=4), "divide"),
+    (dict(block_size=4), "block_size"),
+    (dict(block_size=8, block=None), "block_scores"),
+    (dict(scores=None), "null scores"),
+    (dict(q=None), "null pointer"),
+])
+def test_index_full_rejects(kw, frag):
+    a = dict(q=P, w=P, k=P, N=100, nq=2, q_per_seq=1, nv=None, scores=P, block_size=0, block=P)
+    a.update(kw)
+    rc, msg = _err(K.load().csa2_index_full(a["q"], a["w"], a["k"], a["N"], a["nq"], a["q_per_seq"], a["nv"],
+                                            a["scores"], a["block_size"], a["block"], S))
+    assert rc == L.CSA2_EINVAL and frag in msg, msg
+
+
+@pytest.mark.parametrize("kw,frag", [
+    (dict(block_size=16), "block_size"),
+    (dict(nb=0), "nb must be"),
+    (dict(nb=70000), "nb must be"),
+    (dict(cand=None), "null pointer"),
+])
+def test_reindex_rejects(kw, frag):
+    a = dict(nb=2048, block_size=8, cand=P)
+    a.update(kw)
+    rc, msg = _err(K.load().csa2_index_reindex(P, P, P, 1000, 2, 1, None, a["cand"], a["nb"], a["block_size"], P,
+                                               None, S))
+    assert rc == L.CSA2_EINVAL and frag in msg, msg
+
+
+@pytest.mark.parametrize("kw,frag,code", [
+    (dict(k=0), "k must be", L.CSA2_EINVAL),
+    (dict(k=4097), "k must be", L.CSA2_EINVAL),
+    (dict(ncols=0), "ncols", L.CSA2_EINVAL),
+    (dict(ld=10), "ld < ncols", L.CSA2_EINVAL),
+    (dict(rows=-2), "rows < 0", L.CSA2_EINVAL),
+    (dict(ncols=1 << 20, ld=1 << 20, ws=None), "workspace", L.CSA2_EWORKSPACE),
+    (dict(ncols=1 << 20, ld=1 << 20, wsb=8), "workspace", L.CSA2_EWORKSPACE),
+])
+def test_topk_rejects(kw, frag, code):
+    a = dict(rows=8, ncols=1000, ld=1000, k=512, ws=P, wsb=1 << 40)
+    a.update(kw)
+    rc, msg = _err(K.load().csa2_topk(P, a["rows"], a["ncols"], a["ld"], None, a["k"], None, P, a["ws"], a["wsb"],
+                                      S))
+    assert rc == code and frag in msg, msg
+
+
+def test_workspace_sizes():
+    assert K.csa2_topk_workspace_bytes(4096, 65536, 512) == 0  # many rows: one chunk per row
+    big = K.csa2_topk_workspace_bytes(8, 1 << 20, 512)
+    assert big > 0 and big % 8 == 0
+    assert K.csa2_topk_workspace_bytes(1, 1000, 512) == 0
+    assert K.csa2_sparse_attn_workspace_bytes(4096, 512) == 0
+    assert K.csa2_sparse_attn_workspace_bytes(8, 512) > 0
+
+
+@pytest.mark.parametrize("kw,frag,code", [
+    (dict(k=-1), "k must be", L.CSA2_EINVAL),
+    (dict(N=0), "N must be", L.CSA2_EINVAL),
+    (dict(q_per_seq=3), "q_per_seq", L.CSA2_EINVAL),
+    (dict(idx=None), "null idx", L.CSA2_EINVAL),
+    (dict(T=0), "window", L.CSA2_EINVAL),
+    (dict(start=None), "window", L.CSA2_EINVAL),
+    (dict(scale=float("nan")), "NaN", L.CSA2_EINVAL),
+    (dict(ws=None), "workspace", L.CSA2_EWORKSPACE),
+])
+def test_attn_rejects(kw, frag, code):
+    a = dict(N=1000, nq=8, q_per_seq=1, idx=P, k=512, swa=P, T=128, start=P, len_=P, scale=0.04, ws=P, wsb=1 << 40)
+    a.update(kw)
+    rc, msg = _err(K.load().csa2_sparse_attn(P, P, a["N"], a["nq"], a["q_per_seq"], a["idx"], a["k"], a["swa"],
+                                             a["T"], a["start"], a["len_"], a["scale"], P, None, a["ws"], a["wsb"],
+                                             S))
+    assert rc == code and frag in msg, msg

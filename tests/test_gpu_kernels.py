@@ -1,0 +1,271 @@
+"""GPU parity of each C-ABI call against the CPU oracle on seeded inputs, at
+sizes the oracle finishes in seconds that still span several tiles and a
+ragged tail, plus the degenerate cases. Bars: bit-exact for FP4 records,
+decoded values and Top-K indices; indexer scores within 1e-3 relative (floor
+1e-5 * max|ref|); attention within 1e-2 * max|ref|."""
+import math
+
+import numpy as np
+import pytest
+import torch
+
+from oracle import oracle as O
+from tests._conv import bf16_bits_to_f64, dev_i32, np_, rel_close, u16
+
+pytestmark = pytest.mark.gpu
+DEV = "cuda"
+SCALE = 1.0 / math.sqrt(512.0)
+
+
+def K():
+    import kv_cache_compression_csa2_amd as k
+    return k
+
+
+def _g(seed):
+    g = torch.Generator(device=DEV)
+    g.manual_seed(seed)
+    return g
+
+
+def _bf16(shape, seed, scale=1.0):
+    return (torch.randn(shape, generator=_g(seed), device=DEV) * scale).to(torch.bfloat16)
+
+
+def _records(n, seed):
+    from kv_cache_compression_csa2_amd.workloads import random_records
+    return random_records(n, _g(seed), DEV)
+
+
+# ------------------------------------------------------------------ FP4
+
+def test_pack_bit_exact_random_scales():
+    print("case: pack random", flush=True)
+    x = _bf16((3000, 512), 1) * torch.exp2(torch.randint(-20, 12, (3000, 1), generator=_g(2), device=DEV)).to(
+        torch.bfloat16)
+    x[0] = 0
+    x[1, :16] = -0.0
+    x[2, :16] = 1e-30
+    x[3, :32] = 3e4  # saturating group
+    rec = K().fp4_kv_pack(x.contiguous())
+    torch.cuda.synchronize()
+    ref = O.fp4_pack(u16(x))
+    assert np.array_equal(np_(rec), ref)
+
+
+def test_pack_bit_exact_ties():
+    """Inputs exactly on the E2M1 midpoints of their group's scale."""
+    print("case: pack ties", flush=True)
+    rng = np.random.default_rng(3)
+    S = torch.tensor(np.exp2(rng.integers(-9, 8, (512, 32, 1))).astype(np.float32))
+    mids = torch.tensor([0.25, 0.75, 1.25, 1.75, 2.5, 3.5, 5.0, 6.0], dtype=torch.float32)
+    pick = torch.tensor(rng.integers(0, 8, (512, 32, 16)))
+    sign = torch.tensor(rng.choice([-1.0, 1.0], (512, 32, 16)).astype(np.float32))
+    v = (mids[pick] * sign * S)
+    v[:, :, 0] = 6.0 * S[:, :, 0]  # amax = 6S so the scale is exactly S
+    x = v.reshape(512, 512).to(torch.bfloat16).to(DEV)
+    rec = K().fp4_kv_pack(x)
+    torch.cuda.synchronize()
+    assert np.array_equal(np_(rec), O.fp4_pack(u16(x)))
+
+
+def test_unpack_exhaustive_and_roundtrip():
+    print("case: unpack exhaustive", flush=True)
+    # every (code, scale byte) pair: record r, group g uses scale byte (r*32+g) % 256
+    n = 64
+    rec = np.zeros((n, 288), np.uint8)
+    for r in range(n):
+        rec[r, :256] = np.arange(256, dtype=np.uint8)  # each byte = two codes: all 16x16 pairs
+    for r in range(n):
+        sc = (r * 32 + np.arange(32)) % 256
+        sc[(sc == 0x7F) | (sc == 0xFF)] = 0x7E
+        rec[r, 256:] = sc
+        rec[r, :256] = np.arange(256, dtype=np.uint8)
+    y = K().fp4_kv_unpack(torch.tensor(rec, device=DEV))
+    torch.cuda.synchronize()
+    got = bf16_bits_to_f64(u16(y))
+    ref = O.fp4_unpack(rec)
+    assert np.array_equal(got, ref)
+    assert np.array_equal(np.signbit(got), np.signbit(ref))
+    # pack(unpack(x)) keeps values (grid points with any scale)
+    x = _bf16((256, 512), 5)
+    r1 = K().fp4_kv_pack(x)
+    back = K().fp4_kv_unpack(r1)
+    r2 = K().fp4_kv_pack(back)
+    torch.cuda.synchronize()
+    assert np.array_equal(bf16_bits_to_f64(u16(K().fp4_kv_unpack(r2))), bf16_bits_to_f64(u16(back)))
+
+
+def test_pack_empty():
+    out = torch.empty((0, 288), dtype=torch.uint8, device=DEV)
+    K().fp4_kv_pack(torch.empty((0, 512), dtype=torch.bfloat16, device=DEV), out=out)
+    torch.cuda.synchronize()
+
+
+# ------------------------------------------------------------------ indexer
+
+def _idx_inputs(nq, N, nseq, seed):
+    q = _bf16((nq, 32, 128), seed)
+    w = torch.rand((nq, 32), generator=_g(seed + 1), device=DEV)
+    k = _bf16((nseq, N, 128), seed + 2)
+    return q, w, k
+
+
+@pytest.mark.parametrize("nq,N,qps", [(1, 1024, 1), (3, 1000, 1), (5, 77, 1), (2, 40000, 1), (4, 1, 1),
+                                      (16, 5003, 16), (24, 4096 * 2 + 100, 8)])
+def test_index_full_matches_oracle(nq, N, qps):
+    print("case: index_full", nq, N, qps, flush=True)
+    q, w, k = _idx_inputs(nq, N, nq // qps, 10 + N)
+    rng = np.random.default_rng(N)
+    nv = rng.integers(0, N + 1, nq).astype(np.int32)
+    nv[0] = N
+    s, b = K().csa2_index_full(q, w, k, N, qps, n_visible=dev_i32(nv, DEV), block_size=8)
+    torch.cuda.synchronize()
+    rs, rb = O.index_full(u16(q), np_(w), u16(k), N, qps, n_visible=nv, block_size=8)
+    ok, msg = rel_close(np_(s), rs)
+    assert ok, msg
+    ok, msg = rel_close(np_(b), rb)
+    assert ok, msg
+    s2 = K().csa2_index_full(q, w, k, N, qps)  # no visibility limit, no blocks
+    torch.cuda.synchronize()
+    ok, msg = rel_close(np_(s2), O.index_full(u16(q), np_(w), u16(k), N, qps))
+    assert ok, msg
+
+
+def test_index_reindex_matches_oracle():
+    print("case: reindex", flush=True)
+    nq, N, nb = 3, 9000, 300
+    q, w, k = _idx_inputs(nq, N, nq, 77)
+    rng = np.random.default_rng(7)
+    blocks = np.sort(np.stack([rng.choice((N + 7) // 8, nb, replace=False) for _ in range(nq)]), 1).astype(np.int32)
+    blocks[1, -5:] = -1
+    nv = np.array([N, 5000, 8999], np.int32)
+    ps, pid = K().csa2_index_reindex(q, w, k, N, 1, dev_i32(blocks, DEV), n_visible=dev_i32(nv, DEV))
+    torch.cuda.synchronize()
+    pool = O.pool_ids(blocks, 8)
+    pool_vis = np.where((pool >= 0) & (pool < nv[:, None]), pool, -1)
+    ref = O.index_reindex(u16(q), np_(w), u16(k), N, 1, pool, n_visible=nv)
+    ok, msg = rel_close(np_(ps), ref)
+    assert ok, msg
+    assert np.array_equal(np_(pid), pool_vis)
+
+
+# ------------------------------------------------------------------ Top-K
+
+def _topk_check(scores_np, k, row_len=None, id_map=None):
+    s = torch.tensor(scores_np, device=DEV)
+    got = K().csa2_topk(s, k, row_len=None if row_len is None else dev_i32(row_len, DEV),
+                        id_map=None if id_map is None else dev_i32(id_map, DEV))
+    torch.cuda.synchronize()
+    ref = O.topk(scores_np, k, row_len=row_len, id_map=id_map)
+    assert np.array_equal(np_(got), ref)
+
+
+@pytest.mark.parametrize("rows,n,k", [(1, 1024, 512), (3, 1000, 512), (64, 32768, 512), (8, 131072, 2048),
+                                      (4, 300001, 512), (2, 1 << 20, 512), (300, 5000, 512), (2, 100, 4096)])
+def test_topk_bit_exact_on_oracle_scores(rows, n, k):
+    print("case: topk", rows, n, k, flush=True)
+    rng = np.random.default_rng(rows * 7 + n)
+    s = rng.normal(0, 10, (rows, n)).astype(np.float32)
+    _topk_check(s, k)
+
+
+def test_topk_ties_nonfinite_and_lengths():
+    print("case: topk ties", flush=True)
+    rng = np.random.default_rng(1)
+    s = (rng.integers(-50, 50, (6, 70000)) / 4).astype(np.float32)
+    s[0, ::2] = -np.inf
+    s[1, ::3] = np.nan
+    s[2, :30000] = -0.0
+    s[2, 30000:] = 0.0
+    s[3] = 2.5
+    s[4, :] = -np.inf
+    s[5, 10:] = np.inf
+    row_len = np.array([70000, 60000, 70000, 70000, 70000, 311], np.int32)
+    _topk_check(s, 512, row_len=row_len)
+    _topk_check(s, 2048)
+    _topk_check(s[:, :600], 512)  # fewer candidates than k in some rows
+
+
+def test_topk_id_map():
+    print("case: topk id_map", flush=True)
+    rng = np.random.default_rng(2)
+    s = rng.normal(0, 1, (5, 16384)).astype(np.float32)
+    ids = np.sort(rng.choice(1 << 20, (5, 16384), replace=False), 1).astype(np.int32)
+    ids[0, 100:200] = -1
+    s[0, 100:200] = -np.inf
+    _topk_check(s, 512, id_map=ids)
+
+
+# ------------------------------------------------------------------ attention
+
+def _attn_case(nq, N, k, qps, seed, T=128, slen=None, sstart=None, pad=0):
+    q = _bf16((nq, 64, 512), seed)
+    kv = _records((nq // qps) * N, seed + 1).view(nq // qps, N, 288)
+    rng = np.random.default_rng(seed)
+    idx = np.sort(np.stack([rng.choice(N, k, replace=False) for _ in range(nq)]), 1).astype(np.int32)
+    if pad:
+        idx[:, -pad:] = -1
+    swa = _bf16((nq // qps, T, 512), seed + 2)
+    sl = np.full(nq, 128 if slen is None else slen, np.int32) if slen is None or np.isscalar(slen) else slen
+    st = np.zeros(nq, np.int32) if sstart is None else sstart
+    return q, kv, idx, swa, st, sl
+
+
+def _attn_check(q, kv, idx, swa, st, sl, N, qps, T):
+    out, lse = K().csa2_sparse_attn(q, kv, N, qps, dev_i32(idx, DEV), swa, dev_i32(st, DEV), dev_i32(sl, DEV))
+    torch.cuda.synchronize()
+    ro, rl = O.sparse_attn(u16(q), np_(kv), N, qps, idx, u16(swa), T, st, sl, SCALE)
+    got = bf16_bits_to_f64(u16(out))
+    err = np.abs(got - ro).max()
+    assert err <= 1e-2 * np.abs(ro).max(), (err, np.abs(ro).max())
+    glse = np_(lse).astype(np.float64)
+    fin = np.isfinite(rl)
+    assert np.array_equal(fin, np.isfinite(glse))
+    assert np.allclose(glse[fin], rl[fin], rtol=1e-3, atol=2e-3)
+
+
+@pytest.mark.parametrize("nq,N,k,pad", [(1, 1024, 512, 0), (3, 2000, 512, 7), (8, 5000, 512, 0), (2, 700, 100, 0),
+                                        (40, 3000, 512, 3)])
+def test_sparse_attn_decode_matches_oracle(nq, N, k, pad):
+    print("case: attn", nq, N, k, pad, flush=True)
+    q, kv, idx, swa, st, sl = _attn_case(nq, N, k, 1, 100 + nq, pad=pad)
+    _attn_check(q, kv, idx, swa, st, sl, N, 1, 128)
+
+
+def test_sparse_attn_no_split_many_queries():
+    """>= 512 queries: one workgroup per query, output written directly."""
+    print("case: attn 520", flush=True)
+    nq, N = 520, 600
+    q, kv, idx, swa, st, sl = _attn_case(nq, N, 512, nq, 5, T=nq + 127)
+    st = np.arange(nq, dtype=np.int32)
+    sl = np.full(nq, 128, np.int32)
+    sl[:5] = [0, 1, 31, 33, 127]
+    _attn_check(q, kv, idx, swa, st, sl, N, nq, nq + 127)
+
+
+def test_sparse_attn_degenerate():
+    print("case: attn degenerate", flush=True)
+    nq, N = 4, 300
+    q, kv, idx, swa, st, sl = _attn_case(nq, N, 64, 1, 9)
+    idx[0, :] = -1  # window only
+    idx[1, :] = -1
+    sl[1] = 0  # no keys at all -> zeros, -inf
+    sl[2] = 0  # selected entries only
+    _attn_check(q, kv, idx, swa, st, sl, N, 1, 128)
+    out, lse = K().csa2_sparse_attn(q, kv, N, 1, dev_i32(idx, DEV), swa, dev_i32(st, DEV), dev_i32(sl, DEV))
+    torch.cuda.synchronize()
+    assert torch.all(out[1] == 0) and torch.all(torch.isneginf(lse[1]))
+    # k = 0, no window at all
+    out2, lse2 = K().csa2_sparse_attn(q, kv, N, 1, torch.empty((nq, 0), dtype=torch.int32, device=DEV))
+    torch.cuda.synchronize()
+    assert torch.all(out2 == 0) and torch.all(torch.isneginf(lse2))
+
+
+def test_sparse_attn_deterministic():
+    print("case: attn determinism", flush=True)
+    q, kv, idx, swa, st, sl = _attn_case(16, 4000, 512, 1, 11)
+    a = [K().csa2_sparse_attn(q, kv, 4000, 1, dev_i32(idx, DEV), swa, dev_i32(st, DEV), dev_i32(sl, DEV))[0]
+         for _ in range(3)]
+    torch.cuda.synchronize()
+    assert torch.equal(a[0], a[1]) and torch.equal(a[1], a[2])
