@@ -71,8 +71,9 @@ CSA2_DEVINL void dequant8(uint32_t w, float half_scale, uint32_t out[4]) {
     for (int b = 0; b < 4; b++) {
         const float fe = (float)((ilo >> (8 * b)) & 0xFFu) * half_scale;
         const float fo = (float)((ihi >> (8 * b)) & 0xFFu) * half_scale;
-        const uint32_t ue = __float_as_uint(fe) | ((w << (28 - 8 * b)) & 0x80000000u);
-        const uint32_t uo = __float_as_uint(fo) | ((w << (24 - 8 * b)) & 0x80000000u);
+        // sign of the product = sign of the scale XOR the code's sign bit
+        const uint32_t ue = __float_as_uint(fe) ^ ((w << (28 - 8 * b)) & 0x80000000u);
+        const uint32_t uo = __float_as_uint(fo) ^ ((w << (24 - 8 * b)) & 0x80000000u);
         out[b] = __builtin_amdgcn_perm(uo, ue, 0x07060302u);
     }
 }
