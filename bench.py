@@ -1,0 +1,327 @@
+"""Benchmark of the CSA2 hot path on one MI355X.
+
+A step is one pass of the whole hot path over one batch of synthetic input:
+  encoder64k / tiny : Full scoring -> Top-512 -> sparse attention;
+  decoder256k / decode1m : Full scoring (+ 8-position block maxima) -> Top-512
+      and Top-2048 blocks -> attention; 3 x (Reindex over the 16384-entry pool
+      -> Top-512 -> attention); 1 Reuse attention;
+  prefill128k : Full scoring of 4096 queries with causal visibility -> Top-512
+      -> attention with per-query windows.
+The headline is decode queries/s on encoder64k (64 queries, 64K-token context
+at m=2 = 32768 FP4 entries per sequence). Inputs live in HBM before timing and
+two independent input sets alternate between steps, so the 256 MB last-level
+cache cannot hold a step's working set. Per-call times come from HIP events on
+the stream the kernels run on.
+
+    python bench.py [--gpus 1] [--steps 20] [--warmup 3] [--workloads a,b,...]
+"""
+import argparse
+import hashlib
+import json
+import math
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBS = 8000.0       # MI355X HBM3E
+BF16_PEAK_TFLOPS = 2500.0   # MI355X dense bf16 MFMA
+METRIC = "CSA2 decode queries/s + HBM GB/s at 64K/1M ctx; prefill indexer TFLOP/s"
+HEADLINE = "encoder64k"
+
+
+def alg_bytes_index_full(wl):
+    """K_idx rows read once per query (256 B each; prefill: once per sequence),
+    scores written (4 B per entry per query), queries and weights read."""
+    n_vis = wl.N * wl.nq if wl.n_visible is None else int(wl.n_visible.sum().item())
+    kbytes = (wl.N * 256 * wl.nseq) if wl.q_per_seq > 1 else n_vis * 256
+    out = wl.nq * wl.N * 4 + (wl.nq * ((wl.N + 7) // 8) * 4 if wl.hier else 0)
+    return kbytes + out + wl.nq * (32 * 128 * 2 + 32 * 4)
+
+
+def alg_flops_index_full(wl):
+    n_vis = wl.N * wl.nq if wl.n_visible is None else int(wl.n_visible.sum().item())
+    return 2 * 32 * 128 * n_vis
+
+
+def alg_bytes_attn(nq, k=512, window=128):
+    """Per query-layer: k FP4 records (288 B), the window rows (1 KiB each),
+    the query (64 KiB), the output (64 KiB) and k indices."""
+    return nq * (k * 288 + window * 1024 + 64 * 1024 + 64 * 1024 + k * 4)
+
+
+def alg_flops_attn(nq, k=512, window=128):
+    return nq * 2 * 2 * 64 * (k + window) * 512
+
+
+class Timer:
+    """Records HIP events around named calls on the current stream."""
+
+    def __init__(self, torch):
+        self.torch = torch
+        self.rec = []
+
+    def span(self, name):
+        t = self
+
+        class _S:
+            def __enter__(s):
+                s.a = t.torch.cuda.Event(enable_timing=True)
+                s.b = t.torch.cuda.Event(enable_timing=True)
+                s.a.record()
+
+            def __exit__(s, *exc):
+                s.b.record()
+                t.rec.append((name, s.a, s.b))
+        return _S()
+
+    def summary(self):
+        out = {}
+        for name, a, b in self.rec:
+            out.setdefault(name, []).append(a.elapsed_time(b))
+        return {k: (sum(v) / len(v), len(v)) for k, v in out.items()}
+
+
+def run_step(step, k_idx, kv, timer=None):
+    """One pass of the hot path, with optional per-call event spans."""
+    import contextlib
+    sp = timer.span if timer else (lambda n: contextlib.nullcontext())
+    wl = step.wl
+    with sp("index_full"):
+        step.index_full(k_idx)
+    with sp("topk_full"):
+        step.topk_full()
+    with sp("attn"):
+        step.attend(0, kv, step.top[0])
+    if wl.hier:
+        for layer in (1, 2, 3):
+            with sp("reindex+topk"):
+                step.reindex(layer, k_idx)
+            with sp("attn"):
+                step.attend(layer, kv, step.top[layer])
+        with sp("attn"):
+            step.attend(4, kv, step.top[3])
+
+
+def bench_workload(name, steps, warmup, nsets, torch):
+    from kv_cache_compression_csa2_amd.pipeline import Step, pack_workload_kv
+    from kv_cache_compression_csa2_amd.workloads import CONFIGS, make_workload
+    dev = "cuda"
+    sets = []
+    for s in range(nsets):
+        wl = make_workload(name, device=dev, seed=CONFIGS[name]["seed"] + 100 * s)
+        kv = pack_workload_kv(wl, dev)
+        sets.append((Step(wl, dev), wl, kv))
+    torch.cuda.synchronize()
+    for i in range(warmup):
+        st, wl, kv = sets[i % nsets]
+        run_step(st, wl.k_idx, kv)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(steps):
+        st, wl, kv = sets[i % nsets]
+        run_step(st, wl.k_idx, kv)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    # second timed pass with per-call events (same work, separate from the wall clock)
+    timer = Timer(torch)
+    for i in range(steps):
+        st, wl, kv = sets[i % nsets]
+        run_step(st, wl.k_idx, kv, timer)
+    torch.cuda.synchronize()
+    calls = timer.summary()
+    wl = sets[0][1]
+    ms_step = wall * 1e3 / steps
+    res = {"workload": name, "nq": wl.nq, "N": wl.N, "ms_per_step": ms_step,
+           "queries_per_s": wl.nq / (ms_step * 1e-3),
+           "calls_ms": {k: round(v[0], 5) for k, v in calls.items()}}
+    t_idx = calls["index_full"][0] * 1e-3
+    res["index_full_GBps"] = alg_bytes_index_full(wl) / t_idx / 1e9
+    res["index_full_TFLOPs"] = alg_flops_index_full(wl) / t_idx / 1e12
+    t_att = calls["attn"][0] * 1e-3
+    res["attn_GBps"] = alg_bytes_attn(wl.nq) / t_att / 1e9
+    res["attn_TFLOPs"] = alg_flops_attn(wl.nq) / t_att / 1e12
+    res["_alg_bytes_index_full"] = alg_bytes_index_full(wl)
+    res["_alg_flops_index_full"] = alg_flops_index_full(wl)
+    del sets
+    torch.cuda.empty_cache()
+    return res
+
+
+def bench_attn_gather(nq, torch, steps=20, warmup=3, nsets=4):
+    """The FP4 main-KV gather path alone: nq decode queries (one sequence each,
+    4096 entries), 512 random distinct entries + 128 window rows each;
+    `nsets` independent KV caches and index sets rotate between calls."""
+    from kv_cache_compression_csa2_amd import _lib as L
+    from kv_cache_compression_csa2_amd.workloads import bf16_normal, generator, random_records
+    dev = "cuda"
+    N = 4096
+    sets = []
+    for s in range(nsets):
+        g = generator(dev, 77 + s, 1)
+        kv = random_records(nq * N, g, dev).view(nq, N, 288)
+        idx = torch.sort(torch.rand((nq, N), generator=generator(dev, 77 + s, 2), device=dev).argsort(1)[:, :512],
+                         1)[0].to(torch.int32).contiguous()
+        q = bf16_normal((nq, 64, 512), generator(dev, 77 + s, 3), dev)
+        swa = bf16_normal((nq, 128, 512), generator(dev, 77 + s, 4), dev)
+        st = torch.zeros((nq,), dtype=torch.int32, device=dev)
+        sl = torch.full((nq,), 128, dtype=torch.int32, device=dev)
+        out = torch.empty((nq, 64, 512), dtype=torch.bfloat16, device=dev)
+        lse = torch.empty((nq, 64), dtype=torch.float32, device=dev)
+        ws = torch.empty((max(L.csa2_sparse_attn_workspace_bytes(nq, 512), 1),), dtype=torch.uint8, device=dev)
+        sets.append((q, kv, idx, swa, st, sl, out, lse, ws))
+    torch.cuda.synchronize()
+
+    def call(i):
+        q, kv, idx, swa, st, sl, out, lse, ws = sets[i % nsets]
+        L.csa2_sparse_attn(q, kv, N, 1, idx, swa, st, sl, out=out, lse=lse, workspace=ws)
+
+    for i in range(warmup):
+        call(i)
+    timer = Timer(torch)
+    for i in range(steps):
+        with timer.span("attn"):
+            call(i)
+    torch.cuda.synchronize()
+    t = timer.summary()["attn"][0] * 1e-3
+    del sets
+    torch.cuda.empty_cache()
+    return {"nq": nq, "ms": t * 1e3, "GBps": alg_bytes_attn(nq) / t / 1e9, "TFLOPs": alg_flops_attn(nq) / t / 1e12}
+
+
+def cpu_baseline(torch, target_s=15.0):
+    """The CPU oracle, as it stands, on a bounded sample of the headline
+    workload: the first n queries (scoring over all 32768 entries, Top-512,
+    attention), n chosen from a 4-query trial so the run takes ~target_s."""
+    import numpy as np
+    from kv_cache_compression_csa2_amd.workloads import make_workload
+    from oracle import oracle as O
+    O.build(force=False)
+    wl = make_workload(HEADLINE, device="cuda")
+
+    def u16(t):
+        return t.detach().cpu().contiguous().view(torch.int16).numpy().view(np.uint16)
+
+    qi_all, w_all, k_all = u16(wl.q_idx[0]), wl.w[0].cpu().numpy(), u16(wl.k_idx)
+    kv_all = wl.kv.cpu().numpy()
+    flat = wl.kv_prepack_rows.cpu().numpy()
+    pre = u16(wl.kv_prepack)
+    q_all, swa_all = u16(wl.q[0]), u16(wl.swa[0])
+    st_all, sl_all = wl.swa_start.cpu().numpy(), wl.swa_len.cpu().numpy()
+
+    def run(n):
+        kv = kv_all[:n].copy()
+        t0 = time.perf_counter()
+        recs = O.fp4_pack(pre)  # the oracle packs the planted entries itself
+        for j, fid in enumerate(flat):
+            if fid // wl.N < n:
+                kv[fid // wl.N, fid % wl.N] = recs[j]
+        s = O.index_full(qi_all[:n], w_all[:n], k_all[:n], wl.N, 1)
+        top = O.topk(s, 512)
+        O.sparse_attn(q_all[:n], kv, wl.N, 1, top, swa_all[:n], wl.swa_T, st_all[:n], sl_all[:n],
+                      1.0 / math.sqrt(512.0))
+        return time.perf_counter() - t0
+
+    t4 = run(4)
+    n = int(min(wl.nq, max(4, round(4 * target_s / max(t4, 1e-3)))))
+    reps, total, done = 0, 0.0, 0
+    while total < target_s * 0.66 and reps < 64:
+        total += run(n)
+        done += n
+        reps += 1
+    return {"value": round(done / total, 3), "unit": "queries/s", "cores": O.num_threads(), "kind": "oracle",
+            "sample": "%d x %d of the 64 encoder64k queries (whole path: score 32768 entries, Top-512, attention), "
+                      "%.1f s of CPU time" % (reps, n, total)}
+
+
+def traffic_from_profiles(kernel_src):
+    """HBM bytes per launch of the dominant kernel from the committed rocprofv3
+    counter summary, if it was taken on the current kernel source."""
+    path = os.path.join(ROOT, "profiles", "index_stream_encoder64k_pmc.json")
+    if not os.path.exists(path):
+        return None
+    try:
+        d = json.load(open(path))
+    except Exception:
+        return None
+    h = hashlib.sha256(open(kernel_src, "rb").read()).hexdigest()[:16]
+    if d.get("kernel_source_sha256_16") != h:
+        return None
+    return d.get("hbm_bytes_per_launch")
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--workloads", default="encoder64k,decoder256k,decode1m,prefill128k")
+    ap.add_argument("--attn-sweep", default="64,256,1024")
+    ap.add_argument("--no-cpu", action="store_true")
+    ap.add_argument("--calibrate-copy", action="store_true",
+                    help="only run a 1 GiB device copy (counter calibration for rocprofv3 --pmc)")
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print("bench.py: this build runs on one GPU only; --gpus %d is not supported" % args.gpus, file=sys.stderr)
+        sys.exit(2)
+    import torch
+    import kv_cache_compression_csa2_amd as K
+    K.load()
+    if args.calibrate_copy:
+        a = torch.empty((1 << 30,), dtype=torch.uint8, device="cuda")
+        b = torch.empty_like(a)
+        for _ in range(3):
+            b.copy_(a)
+        torch.cuda.synchronize()
+        print(json.dumps({"calibration_copy_bytes": 1 << 30}))
+        return
+    names = [n for n in args.workloads.split(",") if n]
+    if HEADLINE not in names:
+        names.insert(0, HEADLINE)
+    res = {}
+    for n in names:
+        print("bench: %s ..." % n, file=sys.stderr, flush=True)
+        res[n] = bench_workload(n, args.steps, args.warmup, 1 if n in ("prefill128k", "tiny") else 2, torch)
+        print("bench: %s %.4f ms/step" % (n, res[n]["ms_per_step"]), file=sys.stderr, flush=True)
+    sweep = {}
+    for nq in [int(x) for x in args.attn_sweep.split(",") if x]:
+        print("bench: attention gather nq=%d ..." % nq, file=sys.stderr, flush=True)
+        sweep[str(nq)] = bench_attn_gather(nq, torch)
+    h = res[HEADLINE]
+    t_idx_s = h["calls_ms"]["index_full"] * 1e-3
+    achieved = h["_alg_bytes_index_full"] / t_idx_s / 1e9
+    src = os.path.join(ROOT, "kv_cache_compression_csa2_amd", "csrc", "index.hip")
+    roofline = {"kernel": "index_stream_kernel<Full> (csa2_index_full)", "bound": "hbm",
+                "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": traffic_from_profiles(src),
+                "alg_bytes_per_launch": h["_alg_bytes_index_full"]}
+    cpu = None
+    if not args.no_cpu:
+        print("bench: cpu oracle baseline ...", file=sys.stderr, flush=True)
+        cpu = cpu_baseline(torch)
+    extra = {}
+    for n, r in res.items():
+        e = {k: (round(v, 4) if isinstance(v, float) else v) for k, v in r.items() if not k.startswith("_")}
+        extra[n] = e
+    if "prefill128k" in res:
+        p = res["prefill128k"]
+        extra["prefill128k"]["indexer_TFLOPs"] = round(p["index_full_TFLOPs"], 2)
+        extra["prefill128k"]["indexer_frac_of_bf16_peak"] = round(p["index_full_TFLOPs"] / BF16_PEAK_TFLOPS, 4)
+    extra["attn_gather_sweep"] = {k: {kk: round(vv, 4) for kk, vv in v.items()} for k, v in sweep.items()}
+    line = {
+        "metric": METRIC, "value": round(h["queries_per_s"], 1), "unit": "queries/s", "n_gpus": 1,
+        "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(h["ms_per_step"], 5),
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "bf16",
+        "data": "synthetic (seeded; shapes and distributions of the pages' 64K encoder decode)",
+        "config": {"workload": "encoder64k: 64 decode queries, 64K-token context at m=2 = 32768 FP4 entries "
+                               "per sequence, Full mode, Top-512, 64x512 MQA + 128 SWA",
+                   "global_batch": 64, "seq_len": 65536, "entries": 32768, "parallelism": "single GPU"},
+        "roofline": roofline, "cpu_baseline": cpu, "extra": extra,
+    }
+    print(json.dumps(line))
+
+
+if __name__ == "__main__":
+    main()

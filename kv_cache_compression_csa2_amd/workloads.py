@@ -70,7 +70,7 @@ def random_scale_bytes(shape, g, device):
 
 def random_records(n_rows, g, device):
     """Main-KV records with uniformly random E2M1 codes and random scales."""
-    codes = torch.randint(0, 256, (n_rows, DIM // 2), generator=g, device=device, dtype=torch.int32).to(torch.uint8)
+    codes = torch.randint(0, 256, (n_rows, DIM // 2), generator=g, device=device, dtype=torch.uint8)
     scales = random_scale_bytes((n_rows, DIM // 16), g, device)
     return torch.cat([codes, scales], dim=1).contiguous()
 
