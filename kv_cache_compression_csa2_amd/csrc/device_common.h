@@ -78,6 +78,15 @@ CSA2_DEVINL void dequant8(uint32_t w, float half_scale, uint32_t out[4]) {
     }
 }
 
+// Workgroup barrier that orders LDS only. __syncthreads() also drains every
+// outstanding global load (s_waitcnt vmcnt(0)), which would stall prefetches
+// that are meant to stay in flight across the barrier.
+CSA2_DEVINL void lds_barrier() {
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup", "local");
+    __builtin_amdgcn_s_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup", "local");
+}
+
 CSA2_DEVINL float wave_max(float v) {
 #pragma unroll
     for (int o = 32; o > 0; o >>= 1) v = fmaxf(v, __shfl_xor(v, o));

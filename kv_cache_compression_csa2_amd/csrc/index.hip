@@ -79,9 +79,12 @@ __global__ __launch_bounds__(kStreamThreads) void index_stream_kernel(
         }
         st.ent = ent;
         st.valid = valid;
-        const u32x4* src = reinterpret_cast<const u32x4*>(kseq + (valid ? ent : 0) * kIdxDim) + half;
+        // Plain (cache-allocating) loads: a tile reads 32 B of each of 32 rows per
+        // instruction, and the other 7 instructions of the same wave consume the
+        // rest of those lines, so the lines must stay in cache between them.
+        const uint4* src = reinterpret_cast<const uint4*>(kseq + (valid ? ent : 0) * kIdxDim) + half;
 #pragma unroll
-        for (int j = 0; j < 8; j++) st.b[j] = as_bf16x8(__builtin_nontemporal_load(src + 2 * j));
+        for (int j = 0; j < 8; j++) st.b[j] = as_bf16x8(src[2 * j]);
     };
 
     auto finish = [&](int64_t t, const StreamTile& st) {
@@ -216,7 +219,7 @@ __global__ __launch_bounds__(256, 2) void index_prefill_kernel(
     };
 
     lstore(0, gload(0));
-    __syncthreads();
+    lds_barrier();
     for (int st = 0; st < nsub; st++) {
         const bool more = st + 1 < nsub;
         // the last iteration re-reads tile 0 (in bounds) and discards it
@@ -237,7 +240,7 @@ __global__ __launch_bounds__(256, 2) void index_prefill_kernel(
             epilogue(accb, wb, qb, nvb, col);
         }
         if (more) lstore((st + 1) & 1, nxt);
-        __syncthreads();
+        lds_barrier();
     }
 }
 
