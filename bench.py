@@ -238,18 +238,20 @@ def cpu_baseline(torch, target_s=15.0):
 
 def traffic_from_profiles(kernel_src):
     """HBM bytes per launch of the dominant kernel from the committed rocprofv3
-    counter summary, if it was taken on the current kernel source."""
-    path = os.path.join(ROOT, "profiles", "index_stream_encoder64k_pmc.json")
+    counter summary (FETCH_SIZE + WRITE_SIZE, calibrated on a 1 GiB copy), if it
+    was taken on the current kernel source; else None."""
+    path = os.path.join(ROOT, "profiles", "index_stream_encoder64k_traffic.md")
     if not os.path.exists(path):
         return None
-    try:
-        d = json.load(open(path))
-    except Exception:
-        return None
+    fields = {}
+    for line in open(path):
+        if ":" in line and not line.startswith(("|", "#", "`", "rocprof")):
+            k, v = line.split(":", 1)
+            fields[k.strip()] = v.strip()
     h = hashlib.sha256(open(kernel_src, "rb").read()).hexdigest()[:16]
-    if d.get("kernel_source_sha256_16") != h:
+    if fields.get("kernel_source_sha256_16") != h or "hbm_bytes_per_launch" not in fields:
         return None
-    return d.get("hbm_bytes_per_launch")
+    return int(fields["hbm_bytes_per_launch"])
 
 
 def main():
