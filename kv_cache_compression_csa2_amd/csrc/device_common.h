@@ -87,6 +87,30 @@ CSA2_DEVINL void lds_barrier() {
     __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup", "local");
 }
 
+// max(x, 0) for a float that is not NaN, taken on its bit pattern: a float
+// with the sign bit clear compares like its int32 bits, one with the sign bit
+// set is a negative int32. One v_max_i32, where fmaxf(x, 0) on a value the
+// compiler cannot prove canonical costs a canonicalising max as well.
+CSA2_DEVINL float relu_bits(float x) { return __int_as_float(max(__float_as_int(x), 0)); }
+
+// Lanes 0..31 receive x from lane l + 32 (v_permlane32_swap exchanges lanes
+// 32..63 of its first operand with lanes 0..31 of its second; element 1 of the
+// result is the second operand after the swap). Lanes 32..63 get their own x.
+CSA2_DEVINL float from_upper_half(float x) {
+    const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+    return __uint_as_float(r[1]);
+}
+
+// Maximum over the aligned group of 8 lanes, in every lane of the group, with
+// DPP moves (quad_perm [1,0,3,2], quad_perm [2,3,0,1], row_half_mirror)
+// instead of LDS-routed shuffles.
+CSA2_DEVINL float max8_lanes(float v) {
+    v = fmaxf(v, __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), 0xB1, 0xF, 0xF, true)));
+    v = fmaxf(v, __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), 0x4E, 0xF, 0xF, true)));
+    v = fmaxf(v, __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), 0x141, 0xF, 0xF, true)));
+    return v;
+}
+
 CSA2_DEVINL float wave_max(float v) {
 #pragma unroll
     for (int o = 32; o > 0; o >>= 1) v = fmaxf(v, __shfl_xor(v, o));

@@ -93,18 +93,15 @@ __global__ __launch_bounds__(kStreamThreads) void index_stream_kernel(
         for (int j = 0; j < 8; j++) acc = mfma32x32x16(a[j], st.b[j], acc);
         float s = 0.0f;
 #pragma unroll
-        for (int r = 0; r < 16; r++) s = fmaf(wr[r], fmaxf(acc[r], 0.0f), s);
-        s += __shfl_xor(s, 32);
+        for (int r = 0; r < 16; r++) s = fmaf(wr[r], relu_bits(acc[r]), s);
+        s += from_upper_half(s);  // lanes 0..31 hold the sum over all 32 heads
         if (!st.valid) s = -INFINITY;
         const int64_t col = t * 32 + col_in_tile;
         if (half == 0 && col < ncols) scores[q * ncols + col] = s;
         if (kReindex) {
             if (pool_ids && half == 0 && col < ncols) pool_ids[q * ncols + col] = st.valid ? (int32_t)st.ent : -1;
         } else if (block_scores) {
-            float m = s;
-            m = fmaxf(m, __shfl_xor(m, 1));
-            m = fmaxf(m, __shfl_xor(m, 2));
-            m = fmaxf(m, __shfl_xor(m, 4));
+            const float m = max8_lanes(s);
             if (half == 0 && (lane & 7) == 0 && col < ncols) block_scores[q * nblk + (col >> 3)] = m;
         }
     };
@@ -202,45 +199,73 @@ __global__ __launch_bounds__(256, 2) void index_prefill_kernel(
             *reinterpret_cast<uint4*>(&lds[buf][row * kPfRow + c16 * 16]) = p.v[i];
         }
     };
-    auto epilogue = [&](const f32x16& acc, const float (&wr)[16], int64_t q, int64_t nv, int64_t col) {
+    // ReLU-weighted head sum of one query's 32 x 32 block; valid in lanes 0..31.
+    auto head_sum = [&](const f32x16& acc, const float (&wr)[16], int64_t nv, int64_t col) {
         float s = 0.0f;
 #pragma unroll
-        for (int r = 0; r < 16; r++) s = fmaf(wr[r], fmaxf(acc[r], 0.0f), s);
-        s += __shfl_xor(s, 32);
-        if (col >= nv) s = -INFINITY;
-        if (half == 0 && col < N) scores[q * N + col] = s;
-        if (block_scores) {
-            float m = s;
-            m = fmaxf(m, __shfl_xor(m, 1));
-            m = fmaxf(m, __shfl_xor(m, 2));
-            m = fmaxf(m, __shfl_xor(m, 4));
-            if (half == 0 && (lane & 7) == 0 && col < N) block_scores[q * nblk + (col >> 3)] = m;
+        for (int r = 0; r < 16; r++) s = fmaf(wr[r], relu_bits(acc[r]), s);
+        s += from_upper_half(s);
+        return col < nv ? s : -INFINITY;
+    };
+    auto store = [&](float s, float m, int64_t q, int64_t col) {
+        if (half == 0 && col < N) {
+            scores[q * N + col] = s;
+            if (block_scores && (lane & 7) == 0) block_scores[q * nblk + (col >> 3)] = m;
+        }
+    };
+    // One group = 32 entries (rows h2*32.. of an LDS tile) for both queries:
+    // 8 fragment reads, 16 MFMAs. The epilogue of the previous group runs in
+    // the same straight-line block so the scheduler can put its VALU work in
+    // the shadow of these MFMAs.
+    auto group = [&](const uint8_t* tile, int h2, f32x16& acca, f32x16& accb, const f32x16& pa, const f32x16& pb,
+                     int64_t pcol, float (&out)[4]) {
+        const uint8_t* rowp = tile + (h2 * 32 + col_in_tile) * kPfRow + half * 16;
+        bf16x8 bj[8];
+#pragma unroll
+        for (int j = 0; j < 8; j++) bj[j] = as_bf16x8(*reinterpret_cast<const uint4*>(rowp + j * 32));
+        acca = f32x16{};
+        accb = f32x16{};
+#pragma unroll
+        for (int j = 0; j < 8; j++) {
+            acca = mfma32x32x16(aa[j], bj[j], acca);
+            accb = mfma32x32x16(ab[j], bj[j], accb);
+        }
+        out[0] = head_sum(pa, wa, nva, pcol);
+        out[1] = head_sum(pb, wb, nvb, pcol);
+        out[2] = max8_lanes(out[0]);
+        out[3] = max8_lanes(out[1]);
+        __builtin_amdgcn_sched_group_barrier(0x100, 8, 0);  // fragment reads first
+        __builtin_amdgcn_sched_group_barrier(0x002, 8, 0);
+#pragma unroll
+        for (int i = 0; i < 16; i++) {
+            __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+            __builtin_amdgcn_sched_group_barrier(0x002, 5, 0);
         }
     };
 
+    const int64_t tile_base = e_begin;
     lstore(0, gload(0));
     lds_barrier();
+    f32x16 pa, pb, ca, cb;
+    float out[4];
+    {
+        const f32x16 z = {};
+        group(lds[0], 0, pa, pb, z, z, N, out);  // no previous group: its results are discarded
+    }
     for (int st = 0; st < nsub; st++) {
         const bool more = st + 1 < nsub;
         // the last iteration re-reads tile 0 (in bounds) and discards it
         const Pre nxt = gload(more ? st + 1 : 0);
-        const uint8_t* tile = lds[st & 1];
-#pragma unroll
-        for (int h2 = 0; h2 < 2; h2++) {
-            const uint8_t* rowp = tile + (h2 * 32 + col_in_tile) * kPfRow + half * 16;
-            f32x16 acca = {}, accb = {};
-#pragma unroll
-            for (int j = 0; j < 8; j++) {
-                const bf16x8 bj = as_bf16x8(*reinterpret_cast<const uint4*>(rowp + j * 32));
-                acca = mfma32x32x16(aa[j], bj, acca);
-                accb = mfma32x32x16(ab[j], bj, accb);
-            }
-            const int64_t col = e_begin + (int64_t)st * kPfSub + h2 * 32 + col_in_tile;
-            epilogue(acca, wa, qa, nva, col);
-            epilogue(accb, wb, qb, nvb, col);
-        }
+        const int64_t col0 = tile_base + (int64_t)st * kPfSub + col_in_tile;
+        group(lds[st & 1], 1, ca, cb, pa, pb, col0, out);
+        store(out[0], out[2], qa, col0);
+        store(out[1], out[3], qb, col0);
         if (more) lstore((st + 1) & 1, nxt);
         lds_barrier();
+        // After the last tile this reads the stale buffer; those results are never stored.
+        group(lds[(st + 1) & 1], 0, pa, pb, ca, cb, col0 + 32, out);
+        store(out[0], out[2], qa, col0 + 32);
+        store(out[1], out[3], qb, col0 + 32);
     }
 }
 
