@@ -4,23 +4,24 @@
 //
 // Scores map to order-preserving 32-bit keys (larger key = larger score, -0
 // folded onto +0, -inf and NaN to key 0 = never chosen). A workgroup finds the
-// exact k-th largest key T with a 3-pass MSB radix select (11, 11, 10 bits)
+// exact k-th largest key T with a 3-pass MSB radix select (12, 10, 10 bits)
 // over LDS histograms, then emits every key > T plus the lowest-column ties
-// == T, in column order, through a block-wide scan -- so the output is already
-// ascending.
+// == T, in column order -- so the output is already ascending.
 //
 // Long rows are split: stage 1 selects the top-k of each chunk as (key,
 // column) candidates; stage 2 selects the row's top-k among the candidates.
 // A row's top-k entry is in its chunk's top-k (fewer than k chunk entries can
 // beat it), so the two stages give the same set as one pass.
 //
-// Main path: a 1024-thread workgroup stages its chunk (<= 32768 keys) or its
-// candidates (<= 16384 key/column pairs) in LDS, so every radix pass and the
-// compaction read LDS, not memory. The first (most skewed) digit's histogram
-// merges equal bins across a wave before the LDS atomic. The compaction gives
-// each wave a contiguous range and emits in order with ballot prefix counts.
-// Shapes beyond those capacities take the global-memory path (512 threads,
-// every pass re-reads the scores through the caches).
+// Main path: each thread of a 256- or 1024-thread workgroup holds a
+// contiguous run of up to 32 keys (chunks <= 32768 keys, merges <= 16384
+// candidates) in registers, so the radix passes read no memory; wave scans use
+// DPP, and the ordered emission is one packed block scan of per-thread
+// (> T, == T) counts followed by in-order writes. The merge stage starts its
+// first digit at the highest bit where its candidates differ, since they sit
+// in a narrow band at the top of the row. Shapes beyond those capacities take
+// the global-memory path (512 threads, every pass re-reads the scores through
+// the caches).
 #include <math.h>
 
 #include "device_common.h"
@@ -270,175 +271,218 @@ __global__ __launch_bounds__(kTkThreads) void topk_merge_kernel(int64_t ld, int3
     for (int64_t t = (int64_t)kq + threadIdx.x; t < k; t += kTkThreads) out[t] = -1;
 }
 
-// ------------------------------------------------------------------ LDS path
+// ------------------------------------------------------------- register path
 
-constexpr int kLdsThreads = 1024;
-constexpr int kLdsWaves = kLdsThreads / 64;
-constexpr int kLdsMaxKeys = 32768;  // stage-1 chunk capacity (128 KiB of keys)
-constexpr int kLdsMaxCand = 16384;  // merge capacity (keys + columns, 128 KiB)
+constexpr int kRegMaxKpt = 32;        // keys per thread
+constexpr int kRegMaxKeys = 1024 * kRegMaxKpt;  // 32768 per chunk
+constexpr int kRegMaxCand = 16384;    // merge capacity per row
 
-struct LdsTk {
-    uint32_t hist[kHistBins];
-    uint32_t wsum[kLdsWaves];
-    uint32_t wsum2[kLdsWaves];
-    uint32_t wgt[kLdsWaves];
-    uint32_t weq[kLdsWaves];
-    uint32_t sel_bin, sel_above;
+// Histograms of the three radix digits (key bits 31..20, 19..10, 9..0), all
+// cleared once at the start.
+template <int NT>
+struct RegTk {
+    uint32_t h1[4096];
+    uint32_t h2[1024];
+    uint32_t h3[1024];
+    uint32_t wsum[NT / 64];
+    uint32_t sel_bin, sel_above, total;
 };
 
-CSA2_DEVINL uint32_t lane_prefix(uint64_t mask) {
-    return __builtin_amdgcn_mbcnt_hi((uint32_t)(mask >> 32), __builtin_amdgcn_mbcnt_lo((uint32_t)mask, 0u));
+// Inclusive prefix sum over the 64 lanes with DPP: row_shr 1, 2, 4, 8 within
+// each 16-lane row, then row_bcast15 / row_bcast31 carry row totals forward.
+CSA2_DEVINL uint32_t wave_incl_scan(uint32_t x) {
+    x += (uint32_t)__builtin_amdgcn_update_dpp(0, (int)x, 0x111, 0xF, 0xF, false);
+    x += (uint32_t)__builtin_amdgcn_update_dpp(0, (int)x, 0x112, 0xF, 0xF, false);
+    x += (uint32_t)__builtin_amdgcn_update_dpp(0, (int)x, 0x114, 0xF, 0xF, false);
+    x += (uint32_t)__builtin_amdgcn_update_dpp(0, (int)x, 0x118, 0xF, 0xF, false);
+    x += (uint32_t)__builtin_amdgcn_update_dpp(0, (int)x, 0x142, 0xA, 0xF, false);
+    x += (uint32_t)__builtin_amdgcn_update_dpp(0, (int)x, 0x143, 0xC, 0xF, false);
+    return x;
 }
 
-CSA2_DEVINL uint32_t block_excl_scan_lds(uint32_t v, uint32_t* wsum, uint32_t* total) {
+// Exclusive scan over the block in thread order (one barrier); *total = sum.
+// wsum must not be rewritten until every thread has returned (the callers
+// place a barrier in between).
+template <int NT>
+CSA2_DEVINL uint32_t reg_block_scan(uint32_t v, uint32_t* wsum, uint32_t* total) {
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-    uint32_t x = v;
-#pragma unroll
-    for (int o = 1; o < 64; o <<= 1) {
-        const uint32_t y = __shfl_up(x, o);
-        if (lane >= o) x += y;
-    }
+    const uint32_t x = wave_incl_scan(v);
     if (lane == 63) wsum[wave] = x;
     __syncthreads();
     uint32_t before = 0, tot = 0;
 #pragma unroll
-    for (int i = 0; i < kLdsWaves; i++) {
-        const uint32_t s = wsum[i];
-        before += (i < wave) ? s : 0u;
-        tot += s;
+    for (int i = 0; i < NT / 64; i++) {
+        const uint32_t sw = wsum[i];
+        before += (i < wave) ? sw : 0u;
+        tot += sw;
     }
-    __syncthreads();
     *total = tot;
     return before + x - v;
 }
 
-// Adds 1 to hist[bin] for every active lane; lanes of a wave with equal bins
-// are merged into one atomic (the top digit of similar scores is shared).
-CSA2_DEVINL void hist_add_merged(uint32_t* hist, uint32_t bin, bool act) {
-    uint64_t todo = __ballot(act);
-    const int lane = threadIdx.x & 63;
-    while (todo) {
-        const int leader = __ffsll((unsigned long long)todo) - 1;
-        const uint32_t b = __shfl(bin, leader);
-        const uint64_t same = __ballot(act && bin == b);
-        if (lane == leader) atomicAdd(&hist[b], (uint32_t)__popcll(same));
-        todo &= ~same;
-    }
-}
-
-// Finds, from the current histogram, the bin holding the rem-th largest key
-// (counting from the top bin): sets sh.sel_bin and sh.sel_above (keys in
-// higher bins). nbins is 2048 or 1024.
-CSA2_DEVINL void pick_bin(LdsTk& sh, uint32_t nbins, uint32_t rem) {
+// From histogram h of nbins bins, finds the bin holding the rem-th largest
+// counted key, counting from the top bin: sets sh.sel_bin and sh.sel_above
+// (keys in higher bins). rem == 0 means rem = min(k, all counted keys), which
+// is also stored in sh.total. Two barriers; the results are readable after.
+template <int NT>
+CSA2_DEVINL void reg_pick_bin(const uint32_t* h, RegTk<NT>& sh, int nbins, uint32_t rem, uint32_t k) {
+    constexpr int kMaxPer = 4096 / NT;
     const int tid = threadIdx.x;
-    const int per = (int)(nbins / kLdsThreads);  // 2 or 1
-    uint32_t c2[2] = {0u, 0u}, loc = 0;
+    const int per = nbins / NT;
+    uint32_t c[kMaxPer], loc = 0;
 #pragma unroll
-    for (int jx = 0; jx < 2; jx++) {
-        c2[jx] = (jx < per) ? sh.hist[nbins - 1 - (tid * per + jx)] : 0u;
-        loc += c2[jx];
+    for (int j = 0; j < kMaxPer; j++) {
+        c[j] = (j < per) ? h[nbins - 1 - (tid * per + j)] : 0u;
+        loc += c[j];
     }
     uint32_t tot;
-    uint32_t above = block_excl_scan_lds(loc, sh.wsum2, &tot);
+    uint32_t above = reg_block_scan<NT>(loc, sh.wsum, &tot);
+    if (rem == 0) {
+        rem = tot < k ? tot : k;
+        if (tid == 0) sh.total = rem;
+    }
     if (above < rem && rem <= above + loc) {
-        for (int jx = 0; jx < per; jx++) {
-            if (above + c2[jx] >= rem) {
-                sh.sel_bin = nbins - 1 - (tid * per + jx);
+        for (int j = 0; j < per; j++) {
+            if (above + c[j] >= rem) {
+                sh.sel_bin = nbins - 1 - (tid * per + j);
                 sh.sel_above = above;
                 break;
             }
-            above += c2[jx];
+            above += c[j];
         }
     }
     __syncthreads();
 }
 
-// Radix select over n LDS keys whose top-digit histogram and selectable count
-// are already in sh.hist / `total`. Returns T and need (see radix_select).
-CSA2_DEVINL void lds_select(const uint32_t* keys, int n, uint32_t kk, LdsTk& sh, uint32_t* T, uint32_t* need) {
+// Exact selection over the keys held in registers (thread t holds positions
+// t*KPT .. t*KPT+KPT-1 of the segment; key 0 = never selected): a 3-pass MSB
+// radix select (12, 10, 10 bits) over LDS histograms finds the k-th largest
+// key T, then emit(slot, u) is called for every key > T and for the first
+// `need` keys == T, slots ascending with position (one packed block scan of
+// the per-thread counts). Returns the number selected, min(k, #nonzero keys).
+//
+// kNarrow (used for merged candidates, whose values sit in a narrow band at
+// the top of the row): the first digit ends at the highest bit where the
+// largest and smallest key differ -- every key shares the bits above it -- so
+// the first histogram spreads instead of piling into a few bins. The three
+// digits then cover bits [0, s1 + 12); s1 <= 20 always.
+template <int NT, int KPT, bool kNarrow, class Emit>
+CSA2_DEVINL uint32_t reg_select_emit(const uint32_t (&key)[KPT], uint32_t k, RegTk<NT>& sh, Emit emit) {
     const int tid = threadIdx.x;
-    uint32_t prefix = 0, rem = kk;
-    pick_bin(sh, 2048u, rem);
-    prefix = sh.sel_bin;
-    rem -= sh.sel_above;
-    const int shifts[2] = {10, 0};
-    const int bits[2] = {11, 10};
+    for (int i = tid; i < 4096; i += NT) sh.h1[i] = 0;
+    for (int i = tid; i < 1024; i += NT) sh.h2[i] = 0;
+    int s1 = 20;        // digit 1 = key bits [s1, s1 + 12)
+    uint32_t high = 0;  // bits >= s1 + 12, shared by every nonzero key
+    if (kNarrow) {
+        uint32_t mx = 0u, mn = 0xFFFFFFFFu;
 #pragma unroll
-    for (int p = 0; p < 2; p++) {
-        __syncthreads();
-        for (int i = tid; i < kHistBins; i += kLdsThreads) sh.hist[i] = 0;
-        __syncthreads();
-        const int sh_ = shifts[p], hi_shift = shifts[p] + bits[p];
-        const uint32_t mask = (1u << bits[p]) - 1u;
-        for (int i = tid; i < n; i += kLdsThreads) {
-            const uint32_t key = keys[i];
-            if (key && (key >> hi_shift) == prefix) atomicAdd(&sh.hist[(key >> sh_) & mask], 1u);
+        for (int u = 0; u < KPT; u++) {
+            mx = max(mx, key[u]);
+            if (key[u]) mn = min(mn, key[u]);
+        }
+#pragma unroll
+        for (int o = 32; o > 0; o >>= 1) {
+            mx = max(mx, (uint32_t)__shfl_xor((int)mx, o));
+            mn = min(mn, (uint32_t)__shfl_xor((int)mn, o));
+        }
+        if ((tid & 63) == 0) {
+            sh.h3[tid >> 6] = mx;
+            sh.h3[512 + (tid >> 6)] = mn;
         }
         __syncthreads();
-        pick_bin(sh, 1u << bits[p], rem);
-        prefix = (prefix << bits[p]) | sh.sel_bin;
-        rem -= sh.sel_above;
-    }
-    *T = prefix;
-    *need = rem;
-}
-
-// Ordered emission of the selected positions of keys[0, n): wave w owns a
-// contiguous range; emit(slot, i) is called for each selected i, slots in
-// ascending i. Returns the number emitted.
-template <class Emit>
-CSA2_DEVINL uint32_t lds_emit(const uint32_t* keys, int n, uint32_t T, uint32_t need, LdsTk& sh, Emit emit) {
-    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-    int W = (n + kLdsWaves - 1) / kLdsWaves;
-    W = (W + 63) & ~63;
-    const int b0 = wave * W, b1 = (b0 + W < n) ? b0 + W : n;
-    uint32_t gt = 0, eq = 0;
-    for (int i = b0 + lane; i < b1; i += 64) {
-        const uint32_t key = keys[i];
-        gt += key > T;
-        eq += key == T;
-    }
+        uint32_t bmax = 0u, bmin = 0xFFFFFFFFu;
 #pragma unroll
-    for (int o = 32; o > 0; o >>= 1) {
-        gt += __shfl_xor(gt, o);
-        eq += __shfl_xor(eq, o);
+        for (int i = 0; i < NT / 64; i++) {
+            bmax = max(bmax, sh.h3[i]);
+            bmin = min(bmin, sh.h3[512 + i]);
+        }
+        if (bmax != 0u) {
+            const int h = bmax > bmin ? 31 - __builtin_clz(bmax ^ bmin) : 0;  // highest differing bit
+            s1 = h >= 31 ? 20 : (h >= 11 ? h - 11 : 0);
+            high = (s1 + 12 < 32) ? (bmax & ~((1u << (s1 + 12)) - 1u)) : 0u;
+        }
+        __syncthreads();  // every thread has read h3 before it is cleared
     }
-    if (lane == 0) {
-        sh.wgt[wave] = gt;
-        sh.weq[wave] = eq;
-    }
+    for (int i = tid; i < 1024; i += NT) sh.h3[i] = 0;
+    const int s2 = s1 >= 10 ? s1 - 10 : 0;  // digit 2 = bits [s2, s1)
+    const int s3 = s2 >= 10 ? s2 - 10 : 0;  // digit 3 = bits [s3, s2); s3 == 0
+    const uint32_t m2 = (1u << (s1 - s2)) - 1u, m3 = (1u << (s2 - s3)) - 1u;
     __syncthreads();
-    uint32_t gt_before = 0, eq_before = 0, total_gt = 0, total_eq = 0;
 #pragma unroll
-    for (int w = 0; w < kLdsWaves; w++) {
-        gt_before += (w < wave) ? sh.wgt[w] : 0u;
-        eq_before += (w < wave) ? sh.weq[w] : 0u;
-        total_gt += sh.wgt[w];
-        total_eq += sh.weq[w];
+    for (int u = 0; u < KPT; u++)
+        if (key[u]) atomicAdd(&sh.h1[(key[u] >> s1) & 4095u], 1u);
+    __syncthreads();
+    reg_pick_bin<NT>(sh.h1, sh, 4096, 0u, k);
+    const uint32_t kk = sh.total;
+    if (kk == 0) return 0;
+    uint32_t prefix = sh.sel_bin, rem = kk - sh.sel_above;  // T's bits [s1, s1 + 12)
+#pragma unroll
+    for (int u = 0; u < KPT; u++)
+        if (key[u] && ((key[u] >> s1) & 4095u) == prefix) atomicAdd(&sh.h2[(key[u] >> s2) & m2], 1u);
+    __syncthreads();
+    reg_pick_bin<NT>(sh.h2, sh, 1024, rem, k);
+    prefix = (prefix << (s1 - s2)) | sh.sel_bin;  // bits [s2, s1 + 12)
+    rem -= sh.sel_above;
+    const uint32_t m12 = (1u << (12 + s1 - s2)) - 1u;
+#pragma unroll
+    for (int u = 0; u < KPT; u++)
+        if (key[u] && ((key[u] >> s2) & m12) == prefix) atomicAdd(&sh.h3[(key[u] >> s3) & m3], 1u);
+    __syncthreads();
+    reg_pick_bin<NT>(sh.h3, sh, 1024, rem, k);
+    const uint32_t T = high | (((prefix << (s2 - s3)) | sh.sel_bin) << s3);
+    const uint32_t need = rem - sh.sel_above;
+
+    uint32_t gt = 0, eq = 0;
+#pragma unroll
+    for (int u = 0; u < KPT; u++) {
+        gt += key[u] > T;
+        eq += key[u] == T;
     }
+    uint32_t tot;
+    const uint32_t before = reg_block_scan<NT>((gt << 16) | eq, sh.wsum, &tot);
+    const uint32_t gt_before = before >> 16, eq_before = before & 0xFFFFu;
     uint32_t slot = gt_before + (eq_before < need ? eq_before : need);
     uint32_t eq_run = eq_before;
-    for (int base = b0; base < b1; base += 64) {
-        const int i = base + lane;
-        const uint32_t key = (i < b1) ? keys[i] : 0u;
-        const bool isgt = (i < b1) && key > T, iseq = (i < b1) && key == T;
-        const uint64_t eqm = __ballot(iseq);
-        const bool sel = isgt || (iseq && eq_run + lane_prefix(eqm) < need);
-        const uint64_t selm = __ballot(sel);
-        if (sel) emit(slot + lane_prefix(selm), i);
-        eq_run += (uint32_t)__popcll(eqm);
-        slot += (uint32_t)__popcll(selm);
+#pragma unroll
+    for (int u = 0; u < KPT; u++) {
+        const bool is_eq = key[u] == T;
+        const bool sel = key[u] > T || (is_eq && eq_run < need);
+        eq_run += is_eq;
+        if (sel && slot < kk) emit(slot, u);  // slot < kk always holds; the check keeps stores in bounds regardless
+        slot += sel;
     }
-    return total_gt + (total_eq < need ? total_eq : need);
+    return kk;
 }
 
-// Stage 1 (or the only stage) on LDS: one 1024-thread workgroup per (row, chunk).
-__global__ __launch_bounds__(kLdsThreads) void topk_lds_chunk_kernel(
+// Loads KPT consecutive scores of this thread (positions tid*KPT..) as keys;
+// positions >= n give key 0.
+template <int KPT>
+CSA2_DEVINL void load_keys(const float* src, int n, uint32_t (&key)[KPT]) {
+    const int p0 = threadIdx.x * KPT;
+    if ((KPT % 4) == 0 && (reinterpret_cast<uintptr_t>(src) & 15u) == 0 && p0 + KPT <= n) {
+        const float4* v = reinterpret_cast<const float4*>(src + p0);
+#pragma unroll
+        for (int u = 0; u < KPT / 4; u++) {
+            const float4 f = v[u];
+            key[4 * u + 0] = score_key(f.x);
+            key[4 * u + 1] = score_key(f.y);
+            key[4 * u + 2] = score_key(f.z);
+            key[4 * u + 3] = score_key(f.w);
+        }
+    } else {
+#pragma unroll
+        for (int u = 0; u < KPT; u++) key[u] = (p0 + u < n) ? score_key(src[p0 + u]) : 0u;
+    }
+}
+
+// Stage 1 (or the only stage): one NT-thread workgroup per (row, chunk), the
+// chunk's keys in registers.
+template <int NT, int KPT>
+__global__ __launch_bounds__(NT) void topk_reg_chunk_kernel(
     const float* __restrict__ scores, int64_t ncols, int64_t ld, const int32_t* __restrict__ row_len, int32_t k,
     int32_t nchunks, int64_t chunk_len, const int32_t* __restrict__ id_map, int32_t* __restrict__ out_idx,
     uint32_t* __restrict__ cand_key, int32_t* __restrict__ cand_col) {
-    __shared__ uint32_t keys[kLdsMaxKeys];
-    __shared__ LdsTk sh;
+    __shared__ RegTk<NT> sh;
     const int tid = threadIdx.x;
     const int64_t row = blockIdx.x / nchunks;
     const int64_t chunk = blockIdx.x % nchunks;
@@ -449,132 +493,120 @@ __global__ __launch_bounds__(kLdsThreads) void topk_lds_chunk_kernel(
     int64_t nn = len - c0;
     nn = nn < chunk_len ? nn : chunk_len;
     const int n = nn > 0 ? (int)nn : 0;
-    for (int i = tid; i < kHistBins; i += kLdsThreads) sh.hist[i] = 0;
-    __syncthreads();
-    const float* src = scores + row * ld + c0;
-    // Stage the chunk: 8 independent loads in flight per thread, then the
-    // top-digit histogram from LDS (its merge loop would otherwise serialize
-    // the loads).
-    for (int i0 = 0; i0 < n; i0 += 8 * kLdsThreads) {
-        float v[8];
-#pragma unroll
-        for (int u = 0; u < 8; u++) {
-            const int i = i0 + u * kLdsThreads + tid;
-            v[u] = (i < n) ? src[i] : 0.0f;
-        }
-#pragma unroll
-        for (int u = 0; u < 8; u++) {
-            const int i = i0 + u * kLdsThreads + tid;
-            if (i < n) keys[i] = score_key(v[u]);
-        }
-    }
-    __syncthreads();
-    uint32_t cnt = 0;
-    for (int i = tid; i < n; i += kLdsThreads) {
-        const uint32_t key = keys[i];
-        cnt += key != 0u;
-        if (key) atomicAdd(&sh.hist[key >> 21], 1u);
-    }
-    uint32_t total;
-    block_excl_scan_lds(cnt, sh.wsum, &total);  // also orders the key stores above
-    const uint32_t kk = total < (uint32_t)k ? total : (uint32_t)k;
-    uint32_t emitted = 0;
-    if (kk > 0) {
-        uint32_t T, need;
-        lds_select(keys, n, kk, sh, &T, &need);
-        if (nchunks == 1) {
-            int32_t* out = out_idx + row * k;
-            const int32_t* map = id_map ? id_map + row * ld : nullptr;
-            emitted = lds_emit(keys, n, T, need, sh, [&](uint32_t slot, int i) {
-                out[slot] = map ? map[c0 + i] : (int32_t)(c0 + i);
-            });
-        } else {
-            uint32_t* ck = cand_key + (row * nchunks + chunk) * k;
-            int32_t* cc = cand_col + (row * nchunks + chunk) * k;
-            emitted = lds_emit(keys, n, T, need, sh, [&](uint32_t slot, int i) {
-                ck[slot] = keys[i];
-                cc[slot] = (int32_t)(c0 + i);
-            });
-        }
-    }
+    uint32_t key[KPT];
+    load_keys<KPT>(scores + row * ld + c0, n, key);
+    const int p0 = tid * KPT;
+    uint32_t emitted;
     if (nchunks == 1) {
         int32_t* out = out_idx + row * k;
-        for (int t = (int)emitted + tid; t < k; t += kLdsThreads) out[t] = -1;
+        const int32_t* map = id_map ? id_map + row * ld : nullptr;
+        emitted = reg_select_emit<NT, KPT, false>(key, (uint32_t)k, sh, [&](uint32_t slot, int u) {
+            const int64_t col = c0 + p0 + u;
+            out[slot] = map ? map[col] : (int32_t)col;
+        });
+        for (int t = (int)emitted + tid; t < k; t += NT) out[t] = -1;
     } else {
         uint32_t* ck = cand_key + (row * nchunks + chunk) * k;
         int32_t* cc = cand_col + (row * nchunks + chunk) * k;
-        for (int t = (int)emitted + tid; t < k; t += kLdsThreads) {
+        emitted = reg_select_emit<NT, KPT, false>(key, (uint32_t)k, sh, [&](uint32_t slot, int u) {
+            ck[slot] = key[u];
+            cc[slot] = (int32_t)(c0 + p0 + u);
+        });
+        for (int t = (int)emitted + tid; t < k; t += NT) {
             ck[t] = 0u;
             cc[t] = -1;
         }
     }
 }
 
-// Stage 2 on LDS: one workgroup per row over its nchunks * k candidates.
-__global__ __launch_bounds__(kLdsThreads) void topk_lds_merge_kernel(int64_t ld, int32_t k, int32_t nchunks,
-                                                                      const int32_t* __restrict__ id_map,
-                                                                      const uint32_t* __restrict__ cand_key,
-                                                                      const int32_t* __restrict__ cand_col,
-                                                                      int32_t* __restrict__ out_idx) {
-    __shared__ uint32_t keys[kLdsMaxCand];
-    __shared__ int32_t cols[kLdsMaxCand];
-    __shared__ LdsTk sh;
+// Stage 2: one workgroup per row over its nchunks * k candidates, which are
+// in column order (chunk by chunk, each chunk's selection ascending; unused
+// slots hold key 0).
+template <int NT, int KPT>
+__global__ __launch_bounds__(NT) void topk_reg_merge_kernel(int64_t ld, int32_t k, int32_t nchunks,
+                                                             const int32_t* __restrict__ id_map,
+                                                             const uint32_t* __restrict__ cand_key,
+                                                             const int32_t* __restrict__ cand_col,
+                                                             int32_t* __restrict__ out_idx) {
+    __shared__ RegTk<NT> sh;
     const int tid = threadIdx.x;
     const int64_t row = blockIdx.x;
     const int n = nchunks * k;
-    for (int i = tid; i < kHistBins; i += kLdsThreads) sh.hist[i] = 0;
-    __syncthreads();
-    const uint32_t* ckr = cand_key + row * n;
-    const int32_t* ccr = cand_col + row * n;
-    for (int i0 = 0; i0 < n; i0 += 4 * kLdsThreads) {
-        uint32_t kv_[4];
-        int32_t cv[4];
+    const uint32_t* ckr = cand_key + row * (int64_t)n;
+    const int32_t* ccr = cand_col + row * (int64_t)n;
+    const int p0 = tid * KPT;
+    uint32_t key[KPT];
+    int32_t col[KPT];
+    const bool aligned = ((reinterpret_cast<uintptr_t>(ckr) | reinterpret_cast<uintptr_t>(ccr)) & 15u) == 0;
+    if ((KPT % 4) == 0 && aligned && p0 + KPT <= n) {
 #pragma unroll
-        for (int u = 0; u < 4; u++) {
-            const int i = i0 + u * kLdsThreads + tid;
-            kv_[u] = (i < n) ? ckr[i] : 0u;
-            cv[u] = (i < n) ? ccr[i] : -1;
+        for (int u = 0; u < KPT / 4; u++) {
+            const uint4 kv4 = reinterpret_cast<const uint4*>(ckr + p0)[u];
+            const int4 cv4 = reinterpret_cast<const int4*>(ccr + p0)[u];
+            key[4 * u + 0] = kv4.x;
+            key[4 * u + 1] = kv4.y;
+            key[4 * u + 2] = kv4.z;
+            key[4 * u + 3] = kv4.w;
+            col[4 * u + 0] = cv4.x;
+            col[4 * u + 1] = cv4.y;
+            col[4 * u + 2] = cv4.z;
+            col[4 * u + 3] = cv4.w;
         }
+    } else {
 #pragma unroll
-        for (int u = 0; u < 4; u++) {
-            const int i = i0 + u * kLdsThreads + tid;
-            if (i < n) {
-                keys[i] = kv_[u];
-                cols[i] = cv[u];
-            }
+        for (int u = 0; u < KPT; u++) {
+            key[u] = (p0 + u < n) ? ckr[p0 + u] : 0u;
+            col[u] = (p0 + u < n) ? ccr[p0 + u] : -1;
         }
     }
-    __syncthreads();
-    uint32_t cnt = 0;
-    for (int i = tid; i < n; i += kLdsThreads) {
-        const uint32_t key = keys[i];
-        cnt += key != 0u;
-        if (key) atomicAdd(&sh.hist[key >> 21], 1u);
-    }
-    uint32_t total;
-    block_excl_scan_lds(cnt, sh.wsum, &total);
-    const uint32_t kk = total < (uint32_t)k ? total : (uint32_t)k;
     int32_t* out = out_idx + row * k;
-    uint32_t emitted = 0;
-    if (kk > 0) {
-        uint32_t T, need;
-        lds_select(keys, n, kk, sh, &T, &need);
-        const int32_t* map = id_map ? id_map + row * ld : nullptr;
-        emitted = lds_emit(keys, n, T, need, sh, [&](uint32_t slot, int i) {
-            const int32_t col = cols[i];
-            out[slot] = map ? map[col] : col;
-        });
-    }
-    for (int t = (int)emitted + tid; t < k; t += kLdsThreads) out[t] = -1;
+    const int32_t* map = id_map ? id_map + row * ld : nullptr;
+    const uint32_t emitted = reg_select_emit<NT, KPT, true>(key, (uint32_t)k, sh, [&](uint32_t slot, int u) {
+        out[slot] = map ? map[col[u]] : col[u];
+    });
+    for (int t = (int)emitted + tid; t < k; t += NT) out[t] = -1;
 }
 
-// Chunks per row on the LDS path; 0 = the shape needs the global-memory path.
-int32_t topk_lds_chunks(int32_t rows, int64_t ncols, int32_t k) {
-    int64_t c = (ncols + kLdsMaxKeys - 1) / kLdsMaxKeys;
-    // few rows: split further so more workgroups share the row (chunks >= 4096)
-    while (rows * c < 128 && ncols / (c * 2) >= 4096 && (c * 2) * k <= kLdsMaxCand) c *= 2;
-    if (c > 1 && c * k > kLdsMaxCand) return 0;
+// Chunks per row on the register path; 0 = the shape needs the global-memory path.
+int32_t topk_reg_chunks(int32_t rows, int64_t ncols, int32_t k) {
+    // chunks of <= 16384 keys (16 per thread: two workgroups fit a CU) unless
+    // the merge capacity needs the larger ones
+    int64_t c = (ncols + kRegMaxKeys / 2 - 1) / (kRegMaxKeys / 2);
+    if (c > 1 && c * k > kRegMaxCand) c = (ncols + kRegMaxKeys - 1) / kRegMaxKeys;
+    // few rows: split further so the chunks of all rows cover the GPU (chunks >= 2048)
+    while (rows * c < 256 && ncols / (c * 2) >= 2048 && (c * 2) * k <= kRegMaxCand) c *= 2;
+    if (c > 1 && c * k > kRegMaxCand) return 0;
     return (int32_t)c;
+}
+
+// Workgroup size and keys per thread for a segment of n keys: 256 threads up
+// to 8 keys each, else 1024 threads with the smallest power of two covering n.
+struct RegShape {
+    int nt, kpt;
+};
+RegShape reg_shape(int64_t n) {
+    if (n <= 256 * 8) {
+        int kpt = 1;
+        while ((int64_t)kpt * 256 < n) kpt *= 2;
+        return {256, kpt};
+    }
+    int kpt = 1;
+    while ((int64_t)kpt * 1024 < n) kpt *= 2;
+    return {1024, kpt};
+}
+
+template <int NT, int KPT>
+void launch_reg_chunk(dim3 grid, hipStream_t s, const float* scores, int64_t ncols, int64_t ld, const int32_t* row_len,
+                      int32_t k, int32_t c, int64_t chunk_len, const int32_t* id_map, int32_t* out_idx, uint32_t* ck,
+                      int32_t* cc) {
+    hipLaunchKernelGGL((topk_reg_chunk_kernel<NT, KPT>), grid, dim3(NT), 0, s, scores, ncols, ld, row_len, k, c,
+                       chunk_len, id_map, out_idx, ck, cc);
+}
+
+template <int NT, int KPT>
+void launch_reg_merge(dim3 grid, hipStream_t s, int64_t ld, int32_t k, int32_t c, const int32_t* id_map,
+                      const uint32_t* ck, const int32_t* cc, int32_t* out_idx) {
+    hipLaunchKernelGGL((topk_reg_merge_kernel<NT, KPT>), grid, dim3(NT), 0, s, ld, k, c, id_map, ck, cc, out_idx);
 }
 
 int32_t topk_chunks(int32_t rows, int64_t ncols, int32_t k) {
@@ -588,7 +620,7 @@ int32_t topk_chunks(int32_t rows, int64_t ncols, int32_t k) {
 }  // namespace
 
 size_t topk_workspace_bytes(int32_t rows, int64_t ncols, int32_t k) {
-    int32_t c = topk_lds_chunks(rows, ncols, k);
+    int32_t c = topk_reg_chunks(rows, ncols, k);
     if (c == 0) c = topk_chunks(rows, ncols, k);
     if (c == 1) return 0;
     return (size_t)rows * c * k * (sizeof(uint32_t) + sizeof(int32_t));
@@ -597,7 +629,7 @@ size_t topk_workspace_bytes(int32_t rows, int64_t ncols, int32_t k) {
 int launch_topk(const float* scores, int32_t rows, int64_t ncols, int64_t ld, const int32_t* row_len, int32_t k,
                 const int32_t* id_map, int32_t* out_idx, void* ws, hipStream_t s) {
     if (rows == 0) return 0;
-    const int32_t cl = topk_lds_chunks(rows, ncols, k);
+    const int32_t cl = topk_reg_chunks(rows, ncols, k);
     const int32_t c = cl ? cl : topk_chunks(rows, ncols, k);
     const int64_t chunk_len = (ncols + c - 1) / c;
     uint32_t* ck = nullptr;
@@ -607,11 +639,45 @@ int launch_topk(const float* scores, int32_t rows, int64_t ncols, int64_t ld, co
         cc = reinterpret_cast<int32_t*>(ck + (size_t)rows * c * k);
     }
     if (cl) {
-        hipLaunchKernelGGL(topk_lds_chunk_kernel, dim3((unsigned)((int64_t)rows * c)), dim3(kLdsThreads), 0, s, scores,
-                           ncols, ld, row_len, k, c, chunk_len, id_map, out_idx, ck, cc);
-        if (c > 1)
-            hipLaunchKernelGGL(topk_lds_merge_kernel, dim3((unsigned)rows), dim3(kLdsThreads), 0, s, ld, k, c, id_map,
-                               ck, cc, out_idx);
+        const dim3 g1((unsigned)((int64_t)rows * c));
+        const RegShape a = reg_shape(chunk_len);
+#define CSA2_CHUNK(NT, KPT) launch_reg_chunk<NT, KPT>(g1, s, scores, ncols, ld, row_len, k, c, chunk_len, id_map, out_idx, ck, cc)
+        if (a.nt == 256) {
+            switch (a.kpt) {
+                case 1: CSA2_CHUNK(256, 1); break;
+                case 2: CSA2_CHUNK(256, 2); break;
+                case 4: CSA2_CHUNK(256, 4); break;
+                default: CSA2_CHUNK(256, 8); break;
+            }
+        } else {
+            switch (a.kpt) {
+                case 1: case 2: case 4: CSA2_CHUNK(1024, 4); break;
+                case 8: CSA2_CHUNK(1024, 8); break;
+                case 16: CSA2_CHUNK(1024, 16); break;
+                default: CSA2_CHUNK(1024, 32); break;
+            }
+        }
+#undef CSA2_CHUNK
+        if (c > 1) {
+            const dim3 g2((unsigned)rows);
+            const RegShape m = reg_shape((int64_t)c * k);
+#define CSA2_MERGE(NT, KPT) launch_reg_merge<NT, KPT>(g2, s, ld, k, c, id_map, ck, cc, out_idx)
+            if (m.nt == 256) {
+                switch (m.kpt) {
+                    case 1: CSA2_MERGE(256, 1); break;
+                    case 2: CSA2_MERGE(256, 2); break;
+                    case 4: CSA2_MERGE(256, 4); break;
+                    default: CSA2_MERGE(256, 8); break;
+                }
+            } else {
+                switch (m.kpt) {
+                    case 1: case 2: case 4: CSA2_MERGE(1024, 4); break;
+                    case 8: CSA2_MERGE(1024, 8); break;
+                    default: CSA2_MERGE(1024, 16); break;
+                }
+            }
+#undef CSA2_MERGE
+        }
         return 0;
     }
     hipLaunchKernelGGL(topk_chunk_kernel, dim3((unsigned)((int64_t)rows * c)), dim3(kTkThreads), 0, s, scores, ncols,

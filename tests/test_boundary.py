@@ -101,9 +101,12 @@ def test_topk_rejects(kw, frag, code):
 
 
 def test_workspace_sizes():
-    assert K.csa2_topk_workspace_bytes(4096, 32768, 512) == 0  # many rows, chunk fits: one pass per row
-    # rows longer than one 32768-key chunk: candidates of every chunk (key + column)
-    assert K.csa2_topk_workspace_bytes(4096, 65536, 512) == 4096 * 2 * 512 * 8
+    assert K.csa2_topk_workspace_bytes(4096, 16384, 512) == 0  # many rows, one 16384-key chunk: one pass per row
+    # longer rows: chunks of <= 16384 keys, candidates of every chunk (key + column)
+    assert K.csa2_topk_workspace_bytes(4096, 32768, 512) == 4096 * 2 * 512 * 8
+    assert K.csa2_topk_workspace_bytes(4096, 65536, 512) == 4096 * 4 * 512 * 8
+    # 1M-entry rows need 32768-key chunks to keep the merge within 16384 candidates
+    assert K.csa2_topk_workspace_bytes(8, 1 << 20, 512) == 8 * 32 * 512 * 8
     big = K.csa2_topk_workspace_bytes(8, 1 << 20, 512)
     assert big > 0 and big % 8 == 0
     assert K.csa2_topk_workspace_bytes(1, 1000, 512) == 0

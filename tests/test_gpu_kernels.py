@@ -188,6 +188,18 @@ def test_topk_ties_nonfinite_and_lengths():
     _topk_check(s[:, :600], 512)  # fewer candidates than k in some rows
 
 
+@pytest.mark.parametrize("rows,n,k", [(4, 1 << 20, 512), (8, 131072, 2048), (64, 32768, 512)])
+def test_topk_narrow_band(rows, n, k):
+    """Scores packed in a narrow band (shared sign, exponent and leading
+    mantissa bits), plus exact ties: the merge stage sees candidates that
+    differ only in low bits."""
+    print("case: topk narrow", rows, n, k, flush=True)
+    rng = np.random.default_rng(rows + n + k)
+    s = (100.0 + rng.normal(0, 0.01, (rows, n))).astype(np.float32)
+    s[:, ::7] = np.float32(100.0)  # many keys equal to one value inside the band
+    _topk_check(s, k)
+
+
 def test_topk_id_map():
     print("case: topk id_map", flush=True)
     rng = np.random.default_rng(2)
