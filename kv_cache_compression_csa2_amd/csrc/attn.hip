@@ -90,8 +90,11 @@ static inline int attn_total_tiles(int32_t k) { return (k + kTile - 1) / kTile +
 
 static inline int attn_splits(int32_t nq, int32_t k) {
     const int tiles = attn_total_tiles(k);
-    int want = (512 + nq - 1) / (nq > 0 ? nq : 1);
-    if (want < 1) want = 1;
+    // Workgroups per query: more splits fill the GPU at small batch but add
+    // partial (O, max, sum) traffic and merge work. Measured on MI355X for
+    // Top-512 + 128 window (20 tiles): best at 10 / 7 / 4 / 2 / 2 / 1 splits
+    // for 8 / 16-32 / 64 / 128 / 256 / 512 queries.
+    int want = nq >= 512 ? 1 : nq >= 128 ? 2 : nq >= 64 ? 4 : nq >= 16 ? 7 : 10;
     if (want > tiles) want = tiles;
     const int per = (tiles + want - 1) / want;
     return (tiles + per - 1) / per;
@@ -126,15 +129,6 @@ __global__ __launch_bounds__(kAttThreads, 2) void sparse_attn_kernel(
     const int t_begin = split * tiles_per_split;
     int t_end = t_begin + tiles_per_split;
     t_end = t_end < total_tiles ? t_end : total_tiles;
-
-    // Q^T operand of k-step s: head `head`, the logical dims of physical unit 4s + G.
-    bf16x8 qf[16];
-    {
-        const uint16_t* qh = q + (qi * kHeads + head) * kDim;
-#pragma unroll
-        for (int s = 0; s < 16; s++)
-            qf[s] = as_bf16x8(*reinterpret_cast<const uint4*>(qh + 8 * unit_logical(4 * s + G)));
-    }
 
     f32x4 o[32];
 #pragma unroll
@@ -221,6 +215,16 @@ __global__ __launch_bounds__(kAttThreads, 2) void sparse_attn_kernel(
         load_raw(id_b, raw_b);
     }
     if (prefetchable(t_begin + 2)) row_ids(t_begin + 2, id_n);
+    // Q after the index and record loads: memory counters retire in order, so
+    // loads issued first are the ones the first decode can wait for alone.
+    // Q^T operand of k-step s: head `head`, the logical dims of physical unit 4s + G.
+    bf16x8 qf[16];
+    {
+        const uint16_t* qh = q + (qi * kHeads + head) * kDim;
+#pragma unroll
+        for (int s = 0; s < 16; s++)
+            qf[s] = as_bf16x8(*reinterpret_cast<const uint4*>(qh + 8 * unit_logical(4 * s + G)));
+    }
 
     const int pr_a = perm16(j), pr_t = perm16(4 * G + (j >> 2));
     auto tile = [&](int t, RawRec& rw, int32_t (&id)[2]) -> bool {
@@ -285,11 +289,9 @@ __global__ __launch_bounds__(kAttThreads, 2) void sparse_attn_kernel(
             const float p0 = (m_run == -INFINITY) ? 0.0f : exp2f(x[i] - m_run);
             const float p1 = (m_run == -INFINITY) ? 0.0f : exp2f(x[i + 1] - m_run);
             // round to bf16 (nearest even); the denominator sums the rounded values
-            const uint32_t u0 = __float_as_uint(p0), u1 = __float_as_uint(p1);
-            const uint32_t b0 = (u0 + 0x7FFFu + ((u0 >> 16) & 1u)) >> 16;
-            const uint32_t b1 = (u1 + 0x7FFFu + ((u1 >> 16) & 1u)) >> 16;
-            l_run += bf16_bits_to_float(b0) + bf16_bits_to_float(b1);
-            pk[i >> 1] = b0 | (b1 << 16);
+            const uint32_t b = pack_bf16x2(p0, p1);
+            l_run += bf16_bits_to_float(b & 0xFFFFu) + bf16_bits_to_float(b >> 16);
+            pk[i >> 1] = b;
         }
         const bf16x8 pf = as_bf16x8(make_uint4(pk[0], pk[1], pk[2], pk[3]));
 
@@ -321,16 +323,9 @@ __global__ __launch_bounds__(kAttThreads, 2) void sparse_attn_kernel(
         const float inv = l_tot > 0.0f ? 1.0f / l_tot : 0.0f;
         uint16_t* orow = out + (qi * kHeads + head) * kDim + 4 * (G & 1);
 #pragma unroll
-        for (int mt = 0; mt < 32; mt++) {
-            uint32_t b[4];
-#pragma unroll
-            for (int r = 0; r < 4; r++) {
-                const uint32_t u = __float_as_uint(o[mt][r] * inv);
-                b[r] = (u + 0x7FFFu + ((u >> 16) & 1u)) >> 16;
-            }
+        for (int mt = 0; mt < 32; mt++)
             *reinterpret_cast<uint2*>(orow + 8 * unit_logical(2 * mt + (G >> 1))) =
-                make_uint2(b[0] | (b[1] << 16), b[2] | (b[3] << 16));
-        }
+                make_uint2(pack_bf16x2(o[mt][0] * inv, o[mt][1] * inv), pack_bf16x2(o[mt][2] * inv, o[mt][3] * inv));
         if (lse && G == 0)
             lse[qi * kHeads + head] = l_tot > 0.0f ? (m_run + log2f(l_tot)) * 0.69314718055994531f : -INFINITY;
     } else {
@@ -366,13 +361,8 @@ __global__ __launch_bounds__(128) void attn_merge_kernel(const float* __restrict
         acc += *reinterpret_cast<const f32x4*>(part_o + pidx * kDim + d) * f;
     }
     const float inv = L > 0.0f ? 1.0f / L : 0.0f;
-    uint32_t b[4];
-#pragma unroll
-    for (int r = 0; r < 4; r++) {
-        const uint32_t u = __float_as_uint(acc[r] * inv);
-        b[r] = (u + 0x7FFFu + ((u >> 16) & 1u)) >> 16;
-    }
-    *reinterpret_cast<uint2*>(out + qh * kDim + d) = make_uint2(b[0] | (b[1] << 16), b[2] | (b[3] << 16));
+    *reinterpret_cast<uint2*>(out + qh * kDim + d) =
+        make_uint2(pack_bf16x2(acc[0] * inv, acc[1] * inv), pack_bf16x2(acc[2] * inv, acc[3] * inv));
     if (lse && threadIdx.x == 0) lse[qh] = L > 0.0f ? (M + log2f(L)) * 0.69314718055994531f : -INFINITY;
 }
 

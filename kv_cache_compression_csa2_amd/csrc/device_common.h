@@ -27,6 +27,14 @@ CSA2_DEVINL bf16x8 as_bf16x8(u32x4 v) { return __builtin_bit_cast(bf16x8, v); }
 
 CSA2_DEVINL float bf16_bits_to_float(uint32_t b) { return __uint_as_float(b << 16); }
 
+// Two floats -> packed bf16 pair (lo in bits 0..15), round to nearest even:
+// one v_cvt_pk_bf16_f32 on gfx950.
+CSA2_DEVINL uint32_t pack_bf16x2(float lo, float hi) {
+    typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+    const bf16x2_t v = {(__bf16)lo, (__bf16)hi};
+    return __builtin_bit_cast(uint32_t, v);
+}
+
 // 32x32x16 bf16 MFMA: A 32x16 (lane l: row l%32, k (l/32)*8..+8), B 16x32
 // (lane l: col l%32, same k), C/D 32x32 (lane l, reg r: col l%32,
 // row (r/4)*8 + (l/32)*4 + r%4).
