@@ -6,7 +6,12 @@ A step is one pass of the whole hot path over one batch of synthetic input:
       and Top-2048 blocks -> attention; 3 x (Reindex over the 16384-entry pool
       -> Top-512 -> attention); 1 Reuse attention;
   prefill128k : Full scoring of 4096 queries with causal visibility -> Top-512
-      -> attention with per-query windows.
+      -> attention with per-query windows;
+  encoder_group64k : the 64K shapes as a layer group sharing one cache: Full
+      -> Top-512 -> 6 attention layers (the Full layer's and 5 Reuse layers');
+  decoder_group256k : the 256K shapes as a decoder group: Reindex over a pool
+      built once beforehand (untimed) -> Top-512 -> 4 attention layers (the
+      Reindex layer's and 3 Reuse layers').
 The headline is decode queries/s on encoder64k (64 queries, 64K-token context
 at m=2 = 32768 FP4 entries per sequence). Inputs live in HBM before timing and
 two independent input sets alternate between steps, so the 256 MB last-level
@@ -86,23 +91,7 @@ class Timer:
 
 def run_step(step, k_idx, kv, timer=None):
     """One pass of the hot path, with optional per-call event spans."""
-    import contextlib
-    sp = timer.span if timer else (lambda n: contextlib.nullcontext())
-    wl = step.wl
-    with sp("index_full"):
-        step.index_full(k_idx)
-    with sp("topk_full"):
-        step.topk_full()
-    with sp("attn"):
-        step.attend(0, kv, step.top[0])
-    if wl.hier:
-        for layer in (1, 2, 3):
-            with sp("reindex+topk"):
-                step.reindex(layer, k_idx)
-            with sp("attn"):
-                step.attend(layer, kv, step.top[layer])
-        with sp("attn"):
-            step.attend(4, kv, step.top[3])
+    step.run(k_idx, kv, timer.span if timer else None)
 
 
 def bench_workload(name, steps, warmup, nsets, torch):
@@ -113,7 +102,9 @@ def bench_workload(name, steps, warmup, nsets, torch):
     for s in range(nsets):
         wl = make_workload(name, device=dev, seed=CONFIGS[name]["seed"] + 100 * s)
         kv = pack_workload_kv(wl, dev)
-        sets.append((Step(wl, dev), wl, kv))
+        st = Step(wl, dev)
+        st.prepare(wl.k_idx)
+        sets.append((st, wl, kv))
     torch.cuda.synchronize()
     for i in range(warmup):
         st, wl, kv = sets[i % nsets]
@@ -137,9 +128,10 @@ def bench_workload(name, steps, warmup, nsets, torch):
     res = {"workload": name, "nq": wl.nq, "N": wl.N, "ms_per_step": ms_step,
            "queries_per_s": wl.nq / (ms_step * 1e-3),
            "calls_ms": {k: round(v[0], 5) for k, v in calls.items()}}
-    t_idx = calls["index_full"][0] * 1e-3
-    res["index_full_GBps"] = alg_bytes_index_full(wl) / t_idx / 1e9
-    res["index_full_TFLOPs"] = alg_flops_index_full(wl) / t_idx / 1e12
+    if "index_full" in calls:
+        t_idx = calls["index_full"][0] * 1e-3
+        res["index_full_GBps"] = alg_bytes_index_full(wl) / t_idx / 1e9
+        res["index_full_TFLOPs"] = alg_flops_index_full(wl) / t_idx / 1e12
     t_att = calls["attn"][0] * 1e-3
     res["attn_GBps"] = alg_bytes_attn(wl.nq) / t_att / 1e9
     res["attn_TFLOPs"] = alg_flops_attn(wl.nq) / t_att / 1e12
@@ -259,7 +251,8 @@ def main():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=3)
-    ap.add_argument("--workloads", default="encoder64k,decoder256k,decode1m,prefill128k")
+    ap.add_argument("--workloads",
+                    default="encoder64k,decoder256k,decode1m,prefill128k,encoder_group64k,decoder_group256k")
     ap.add_argument("--attn-sweep", default="64,256,1024")
     ap.add_argument("--no-cpu", action="store_true")
     ap.add_argument("--calibrate-copy", action="store_true",

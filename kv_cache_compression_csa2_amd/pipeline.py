@@ -66,16 +66,34 @@ class Step:
         L.csa2_sparse_attn(wl.q[layer], kv, wl.N, wl.q_per_seq, idx, wl.swa[layer], wl.swa_start, wl.swa_len,
                            out=self.out[layer], lse=self.lse[layer], workspace=self.ws_attn)
 
-    def run(self, k_idx, kv):
-        """The whole hot path once: Full (+ Reindex x3 + Reuse when hierarchical)."""
-        self.index_full(k_idx)
-        self.topk_full()
-        self.attend(0, kv, self.top[0])
-        if self.wl.hier:
-            for layer in (1, 2, 3):
-                self.reindex(layer, k_idx)
-                self.attend(layer, kv, self.top[layer])
-            self.attend(4, kv, self.top[3])  # Reuse: inherits the last Reindex layer's indices
+    def prepare(self, k_idx):
+        """Set-up outside a timed step: the decoder group's pool comes from a
+        Full layer of another group."""
+        if self.wl.group == "decoder":
+            self.index_full(k_idx)
+            self.topk_full()
+
+    def run(self, k_idx, kv, span=None):
+        """The whole hot path once, layer by layer: the Full layer (not for the
+        decoder group, whose pool prepare() built), each Reindex layer, and
+        every attention layer on the Top-512 it inherits. `span(name)` gives
+        an optional timing context per call."""
+        import contextlib
+        sp = span or (lambda n: contextlib.nullcontext())
+        wl = self.wl
+        if wl.group != "decoder":
+            with sp("index_full"):
+                self.index_full(k_idx)
+            with sp("topk_full"):
+                self.topk_full()
+        done = {0} if wl.group != "decoder" else set()
+        for layer, src in enumerate(wl.attn_src):
+            if src not in done:
+                with sp("reindex+topk"):
+                    self.reindex(src, k_idx)
+                done.add(src)
+            with sp("attn"):
+                self.attend(layer, kv, self.top[src])
         return self.out
 
 

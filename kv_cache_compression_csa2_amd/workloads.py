@@ -20,6 +20,16 @@ m=1 decoder compression -- eogee.com report 3.2-3.4, nxbn.cn walkthrough 3.3):
                131072-token context), 65536 entries at m=2, causal visibility.
   decode1m     8 queries, 1048576 entries (m=1), clustered keys (16 centroids,
                sigma 0.3); Full + 3 Reindex + 1 Reuse.
+
+Layer groups that share one cache (eogee.com report 3.2: an encoder cache
+serves a Full layer and the Reuse layers after it; a decoder cache serves a
+Reindex layer and Reuse layers), timed as layer sequences:
+
+  encoder_group64k   the 64K shapes; Full + 5 Reuse (6 attention layers on
+                     one Top-512).
+  decoder_group256k  the 256K shapes; a Full layer builds the 2048-block pool
+                     once (set-up, untimed), then Reindex + 3 Reuse (4
+                     attention layers on the Reindex layer's Top-512).
 """
 import math
 from dataclasses import dataclass, field
@@ -41,6 +51,10 @@ CONFIGS = {
                         planted=0, prefill=True),
     "decode1m": dict(nq=8, N=1048576, q_per_seq=1, hier=True, seed=4, kv="clustered", kidx="clustered", planted=0,
                      prefill=False),
+    "encoder_group64k": dict(nq=64, N=32768, q_per_seq=1, hier=False, seed=5, kv="random", kidx="normal",
+                             planted=8, prefill=False, group="encoder"),
+    "decoder_group256k": dict(nq=32, N=262144, q_per_seq=1, hier=True, seed=6, kv="random", kidx="normal",
+                              planted=0, prefill=False, group="decoder"),
 }
 
 # Norm given to a planted main-KV row before packing: about twice the RMS norm
@@ -84,6 +98,7 @@ class Workload:
     nseq: int
     hier: bool
     swa_T: int
+    group: str = None  # None, "encoder" (Full + 5 Reuse) or "decoder" (Reindex + 3 Reuse)
     q_idx: list = field(default_factory=list)  # per indexer layer: bf16 [nq,32,128]
     w: list = field(default_factory=list)  # per indexer layer: f32 [nq,32]
     k_idx: torch.Tensor = None  # bf16 [nseq,N,128]
@@ -100,11 +115,28 @@ class Workload:
 
     @property
     def n_index_layers(self):
+        """Scoring layers: the Full layer, then Reindex layers."""
+        if self.group == "decoder":
+            return 2
         return 4 if self.hier else 1
 
     @property
+    def reindex_layers(self):
+        return list(range(1, self.n_index_layers))
+
+    @property
+    def attn_src(self):
+        """For each attention layer, the scoring layer whose Top-512 it uses
+        (a Reuse layer repeats the previous layer's)."""
+        if self.group == "encoder":
+            return [0] * 6
+        if self.group == "decoder":
+            return [1] * 4
+        return [0, 1, 2, 3, 3] if self.hier else [0]
+
+    @property
     def n_attn_layers(self):
-        return 5 if self.hier else 1
+        return len(self.attn_src)
 
 
 def clustered_kv_rows(seed, seq, N, device, row0=0, nrows=None):
@@ -138,7 +170,7 @@ def make_workload(name, device="cpu", seed=None, nq=None, N=None):
     q_per_seq = nq if c["prefill"] else c["q_per_seq"]
     nseq = nq // q_per_seq
     swa_T = (nq + WINDOW - 1) if c["prefill"] else WINDOW
-    wl = Workload(name, nq, N, q_per_seq, nseq, c["hier"], swa_T)
+    wl = Workload(name, nq, N, q_per_seq, nseq, c["hier"], swa_T, c.get("group"))
     s = 0
 
     def nxt():

@@ -27,7 +27,7 @@ SCALE = 1.0 / math.sqrt(512.0)
 
 
 def _sample(wl):
-    if wl.name in ("tiny", "encoder64k"):
+    if wl.name in ("tiny", "encoder64k", "encoder_group64k"):
         return list(range(wl.nq))
     if wl.name == "prefill128k":
         return list(range(0, wl.nq, wl.nq // 64))
@@ -77,7 +77,8 @@ def _kv_for(qsub_seq, kvrows, N):
     return kv
 
 
-@pytest.mark.parametrize("name", ["tiny", "encoder64k", "decoder256k", "prefill128k", "decode1m"])
+@pytest.mark.parametrize("name", ["tiny", "encoder64k", "decoder256k", "prefill128k", "decode1m",
+                                  "encoder_group64k", "decoder_group256k"])
 def test_workload_parity(name):
     import kv_cache_compression_csa2_amd as K
     from kv_cache_compression_csa2_amd.pipeline import Step, pack_workload_kv
@@ -86,6 +87,7 @@ def test_workload_parity(name):
     wl = make_workload(name, device=DEV)
     kv = pack_workload_kv(wl, DEV)
     step = Step(wl, DEV)
+    step.prepare(wl.k_idx)
     step.run(wl.k_idx, kv)
     torch.cuda.synchronize()
     print("  gpu step done", flush=True)
@@ -134,7 +136,7 @@ def test_workload_parity(name):
         assert ovc.mean() >= 0.995
         pool = O.pool_ids(cand_o, 8)
         assert all(set(top_o[j].tolist()) <= set(pool[j].tolist()) for j in range(len(Qs)))
-        for layer in (1, 2, 3):
+        for layer in wl.reindex_layers:
             ps_o = O.index_reindex(u16(wl.q_idx[layer][qt]), np_(wl.w[layer][qt]), k_sub, wl.N, 1, pool,
                                    n_visible=nv)
             ps_g, pid_g = K.csa2_index_reindex(wl.q_idx[layer][qt].contiguous(), wl.w[layer][qt].contiguous(),
@@ -152,11 +154,13 @@ def test_workload_parity(name):
             print("  reindex %d overlap mean %.5f min %.5f" % (layer, ovr.mean(), ovr.min()), flush=True)
             assert ovr.mean() >= 0.995
             idx_layers.append(t_o)
-        idx_layers.append(idx_layers[-1])  # Reuse layer
+    # every attention layer attends with the Top-512 of the scoring layer it
+    # follows (Reuse layers repeat it)
+    attn_idx = [idx_layers[src] for src in wl.attn_src]
 
     # 4. attention on the oracle's indices, every layer
     ids_per_seq = {s: [] for s in seqs}
-    for li in idx_layers:
+    for li in attn_idx:
         for j, q in enumerate(Qs):
             ids_per_seq[q // wl.q_per_seq].append(li[j])
     kvrows = _oracle_kv_rows(wl, seqs, ids_per_seq)
@@ -167,7 +171,7 @@ def test_workload_parity(name):
     kv_o = _kv_for(seqs, kvrows, wl.N)
     kv_g = kv[torch.tensor(seqs, device=DEV, dtype=torch.long)].contiguous()
     swa_rows = None
-    for layer, li in enumerate(idx_layers):
+    for layer, li in enumerate(attn_idx):
         swa_l = wl.swa[layer][torch.tensor(seqs, device=DEV, dtype=torch.long)].contiguous()
         st, sl = np_(wl.swa_start[qt]), np_(wl.swa_len[qt])
         ro, rl = O.sparse_attn(u16(wl.q[layer][qt]), kv_o, wl.N, qps_sub, li, u16(swa_l), swa_l.shape[1], st, sl,
@@ -179,8 +183,8 @@ def test_workload_parity(name):
         assert err <= 1e-2 * np.abs(ro).max(), (layer, err, np.abs(ro).max())
         assert np.allclose(np_(gl), rl, rtol=1e-3, atol=2e-3)
         # the pipeline's own output where its selection equals the oracle's
-        same = [j for j, q in enumerate(Qs) if set(np_(step.top[min(layer, len(step.top) - 1)][q]).tolist())
-                == set(li[j].tolist())]
+        src = wl.attn_src[layer]
+        same = [j for j, q in enumerate(Qs) if set(np_(step.top[src][q]).tolist()) == set(li[j].tolist())]
         if same:
             pe = np.abs(bf16_bits_to_f64(u16(step.out[layer][qt][same])) - ro[same]).max()
             assert pe <= 1e-2 * np.abs(ro[same]).max()
