@@ -26,6 +26,10 @@
  *   positions; key == value; softmax scale 1/sqrt(512); ties -> lower index;
  *   scale = E4M3(amax / 6) rounded to nearest even, saturating at 448;
  *   elements rounded to the nearest E2M1 grid value, ties to the even code.
+ *   FP4 indexer K (the pages' storage precision, implied by the 890 B/token
+ *   accounting of [TIT] and [EOG] 5.3: 2.5 entries/token x (288 B main KV +
+ *   68 B indexer K)): 128 E2M1 codes (64 B) + one binary32 scale (4 B) per
+ *   entry, scale = amax / 6 in float, codes by the same nearest-grid rule.
  *
  * Precision: bf16 / E4M3 / E2M1 inputs are decoded exactly into double; dot
  * products, weighted sums and the softmax accumulate in double. The scale
@@ -48,6 +52,7 @@
 #define ORC_DIM 512
 #define ORC_GROUP 16
 #define ORC_RECORD (ORC_DIM / 2 + ORC_DIM / ORC_GROUP) /* 256 code bytes + 32 scale bytes */
+#define ORC_KREC (ORC_IDX_DIM / 2 + 4)                  /* 64 code bytes + binary32 scale */
 
 int orc_num_threads(void) {
 #ifdef _OPENMP
@@ -58,6 +63,7 @@ int orc_num_threads(void) {
 }
 
 int orc_record_bytes(void) { return ORC_RECORD; }
+int orc_kidx_record_bytes(void) { return ORC_KREC; }
 
 /* bf16 -> double: the bf16 bits are the high half of an IEEE binary32. */
 static double bf16_value(uint16_t b) {
@@ -175,14 +181,71 @@ void orc_fp4_unpack(const uint8_t* in, int64_t n, double* out) {
         for (int c = 0; c < ORC_DIM; c++) out[r * ORC_DIM + c] = record_value(in + r * ORC_RECORD, c);
 }
 
+/* FP4 indexer-K entry (reading of the pages' byte accounting: 128-dim FP4 +
+ * a 4-byte scale = 68 B): bytes [0,64) hold channel 2j in the low nibble and
+ * 2j+1 in the high nibble of byte j; bytes [64,68) hold the scale as an IEEE
+ * binary32, least significant byte first. Scale = amax / 6 computed in float;
+ * each channel takes the nearest E2M1 grid value times the scale, ties to the
+ * even code, as for the main KV. */
+void orc_kidx_fp4_pack(const uint16_t* x, int64_t n, uint8_t* out) {
+#pragma omp parallel for schedule(static)
+    for (int64_t r = 0; r < n; r++) {
+        const uint16_t* xr = x + r * ORC_IDX_DIM;
+        uint8_t* o = out + r * ORC_KREC;
+        memset(o, 0, ORC_KREC);
+        float amax = 0.0f;
+        for (int c = 0; c < ORC_IDX_DIM; c++) {
+            float a = fabsf((float)bf16_value(xr[c]));
+            if (a > amax) amax = a;
+        }
+        float s = amax / 6.0f;
+        uint32_t sb;
+        memcpy(&sb, &s, 4);
+        for (int b = 0; b < 4; b++) o[ORC_IDX_DIM / 2 + b] = (uint8_t)(sb >> (8 * b));
+        for (int c = 0; c < ORC_IDX_DIM; c++) {
+            uint8_t code = (s == 0.0f) ? 0 : orc_e2m1_encode(bf16_value(xr[c]), (double)s);
+            o[c / 2] |= (uint8_t)(code << (4 * (c & 1)));
+        }
+    }
+}
+
+static double kidx_fp4_scale(const uint8_t* rec) {
+    uint32_t sb = 0;
+    for (int b = 0; b < 4; b++) sb |= (uint32_t)rec[ORC_IDX_DIM / 2 + b] << (8 * b);
+    float s;
+    memcpy(&s, &sb, 4);
+    return (double)s;
+}
+
+/* Channel c of an FP4 indexer-K entry: E2M1(code) * scale, exact in double. */
+static double kidx_fp4_value(const uint8_t* rec, int c) {
+    return orc_e2m1_value((rec[c / 2] >> (4 * (c & 1))) & 15) * kidx_fp4_scale(rec);
+}
+
+void orc_kidx_fp4_unpack(const uint8_t* in, int64_t n, double* out) {
+#pragma omp parallel for schedule(static)
+    for (int64_t r = 0; r < n; r++)
+        for (int c = 0; c < ORC_IDX_DIM; c++) out[r * ORC_IDX_DIM + c] = kidx_fp4_value(in + r * ORC_KREC, c);
+}
+
+/* Indexer K of entry `row` decoded to double: bf16 (kfmt 0, [.][128] uint16)
+ * or the FP4 entry above (kfmt 1, [.][68] bytes). */
+static void load_key(const void* k, int kfmt, int64_t row, double* kd) {
+    if (kfmt == 0) {
+        const uint16_t* kr = (const uint16_t*)k + row * ORC_IDX_DIM;
+        for (int c = 0; c < ORC_IDX_DIM; c++) kd[c] = bf16_value(kr[c]);
+    } else {
+        const uint8_t* kr = (const uint8_t*)k + row * ORC_KREC;
+        for (int c = 0; c < ORC_IDX_DIM; c++) kd[c] = kidx_fp4_value(kr, c);
+    }
+}
+
 /* Indexer score of one entry ([EOG] 3.2: the indexer Q and indexer K score a
  * main-KV entry; 32 heads x 128 dims per [NXB] 3.3):
  *   score = sum_h w_h * max(q_h . k, 0).
- * qd holds the query's 32 x 128 values already decoded to double. */
-static double index_score(const double* qd /*[32][128]*/, const float* w /*[32]*/, const uint16_t* k /*[128]*/) {
-    double kd[ORC_IDX_DIM];
+ * qd holds the query's 32 x 128 values already decoded to double, kd the key. */
+static double index_score(const double* qd /*[32][128]*/, const float* w /*[32]*/, const double* kd /*[128]*/) {
     double s = 0.0;
-    for (int c = 0; c < ORC_IDX_DIM; c++) kd[c] = bf16_value(k[c]);
     for (int h = 0; h < ORC_IDX_HEADS; h++) {
         double d = 0.0;
         for (int c = 0; c < ORC_IDX_DIM; c++) d += qd[h * ORC_IDX_DIM + c] * kd[c];
@@ -200,9 +263,9 @@ static void decode_query(const uint16_t* q, double* qd) {
  * n_visible[q] (or N when n_visible is NULL) score -inf. Scores are stored as
  * float. When block_size > 0, block j's score is the max over its positions
  * [j*bs, j*bs+bs) ([EOG] 3.3: each block takes its highest index score). */
-void orc_index_full(const uint16_t* q_idx, const float* w, const uint16_t* k_idx, int64_t N, int32_t nq,
-                    int32_t q_per_seq, const int32_t* n_visible, float* scores, int32_t block_size,
-                    float* block_scores) {
+static void index_full_any(const uint16_t* q_idx, const float* w, const void* k_idx, int kfmt, int64_t N,
+                           int32_t nq, int32_t q_per_seq, const int32_t* n_visible, float* scores,
+                           int32_t block_size, float* block_scores) {
     const int64_t CH = 4096; /* entries per parallel work item */
     int64_t nch = (N + CH - 1) / CH;
     double* qd = (double*)malloc(sizeof(double) * (size_t)(nq > 0 ? nq : 1) * ORC_IDX_HEADS * ORC_IDX_DIM);
@@ -217,8 +280,15 @@ void orc_index_full(const uint16_t* q_idx, const float* w, const uint16_t* k_idx
         const double* qq = qd + (int64_t)q * ORC_IDX_HEADS * ORC_IDX_DIM;
         const float* ww = w + (int64_t)q * ORC_IDX_HEADS;
         float* srow = scores + (int64_t)q * N;
-        for (int64_t i = i0; i < i0 + CH && i < N; i++)
-            srow[i] = (i < nv) ? (float)index_score(qq, ww, k_idx + (seq * N + i) * ORC_IDX_DIM) : -INFINITY;
+        double kd[ORC_IDX_DIM];
+        for (int64_t i = i0; i < i0 + CH && i < N; i++) {
+            if (i < nv) {
+                load_key(k_idx, kfmt, seq * N + i, kd);
+                srow[i] = (float)index_score(qq, ww, kd);
+            } else {
+                srow[i] = -INFINITY;
+            }
+        }
     }
     free(qd);
     if (block_size > 0) {
@@ -235,6 +305,19 @@ void orc_index_full(const uint16_t* q_idx, const float* w, const uint16_t* k_idx
     }
 }
 
+void orc_index_full(const uint16_t* q_idx, const float* w, const uint16_t* k_idx, int64_t N, int32_t nq,
+                    int32_t q_per_seq, const int32_t* n_visible, float* scores, int32_t block_size,
+                    float* block_scores) {
+    index_full_any(q_idx, w, k_idx, 0, N, nq, q_per_seq, n_visible, scores, block_size, block_scores);
+}
+
+/* Full-mode scoring over the FP4 indexer-K cache ([N][68] entries). */
+void orc_index_full_fp4k(const uint16_t* q_idx, const float* w, const uint8_t* k_fp4, int64_t N, int32_t nq,
+                         int32_t q_per_seq, const int32_t* n_visible, float* scores, int32_t block_size,
+                         float* block_scores) {
+    index_full_any(q_idx, w, k_fp4, 1, N, nq, q_per_seq, n_visible, scores, block_size, block_scores);
+}
+
 /* Candidate pool ([EOG] 3.3): the chosen blocks' positions, in block order.
  * A block id < 0 (padding) gives id -1 for its positions. */
 void orc_pool_ids(const int32_t* blocks, int32_t nq, int32_t nb, int32_t block_size, int32_t* pool) {
@@ -249,9 +332,9 @@ void orc_pool_ids(const int32_t* blocks, int32_t nq, int32_t nb, int32_t block_s
 /* Reindex-mode scoring ([TIT] Reindex mode; [EOG] 3.3 later indexers score only
  * inside the pool): the layer's own (Q_idx, w) over the shared indexer K, for
  * the pool positions only. Positions whose id is -1 or not visible score -inf. */
-void orc_index_reindex(const uint16_t* q_idx, const float* w, const uint16_t* k_idx, int64_t N, int32_t nq,
-                       int32_t q_per_seq, const int32_t* n_visible, const int32_t* pool, int64_t pool_len,
-                       float* pool_scores) {
+static void index_reindex_any(const uint16_t* q_idx, const float* w, const void* k_idx, int kfmt, int64_t N,
+                              int32_t nq, int32_t q_per_seq, const int32_t* n_visible, const int32_t* pool,
+                              int64_t pool_len, float* pool_scores) {
 #pragma omp parallel for schedule(dynamic, 1)
     for (int32_t q = 0; q < nq; q++) {
         double qd[ORC_IDX_HEADS * ORC_IDX_DIM];
@@ -260,12 +343,30 @@ void orc_index_reindex(const uint16_t* q_idx, const float* w, const uint16_t* k_
         if (nv > N) nv = N;
         decode_query(q_idx + (int64_t)q * ORC_IDX_HEADS * ORC_IDX_DIM, qd);
         const float* ww = w + (int64_t)q * ORC_IDX_HEADS;
+        double kd[ORC_IDX_DIM];
         for (int64_t p = 0; p < pool_len; p++) {
             int64_t id = pool[(int64_t)q * pool_len + p];
-            pool_scores[(int64_t)q * pool_len + p] =
-                (id >= 0 && id < nv) ? (float)index_score(qd, ww, k_idx + (seq * N + id) * ORC_IDX_DIM) : -INFINITY;
+            if (id >= 0 && id < nv) {
+                load_key(k_idx, kfmt, seq * N + id, kd);
+                pool_scores[(int64_t)q * pool_len + p] = (float)index_score(qd, ww, kd);
+            } else {
+                pool_scores[(int64_t)q * pool_len + p] = -INFINITY;
+            }
         }
     }
+}
+
+void orc_index_reindex(const uint16_t* q_idx, const float* w, const uint16_t* k_idx, int64_t N, int32_t nq,
+                       int32_t q_per_seq, const int32_t* n_visible, const int32_t* pool, int64_t pool_len,
+                       float* pool_scores) {
+    index_reindex_any(q_idx, w, k_idx, 0, N, nq, q_per_seq, n_visible, pool, pool_len, pool_scores);
+}
+
+/* Reindex-mode scoring over the FP4 indexer-K cache. */
+void orc_index_reindex_fp4k(const uint16_t* q_idx, const float* w, const uint8_t* k_fp4, int64_t N, int32_t nq,
+                            int32_t q_per_seq, const int32_t* n_visible, const int32_t* pool, int64_t pool_len,
+                            float* pool_scores) {
+    index_reindex_any(q_idx, w, k_fp4, 1, N, nq, q_per_seq, n_visible, pool, pool_len, pool_scores);
 }
 
 typedef struct {

@@ -20,6 +20,7 @@ _LIB_PATH = os.path.join(_HERE, "libcsa2_oracle.so")
 _lib = None
 
 RECORD_BYTES = 288
+KIDX_RECORD_BYTES = 68  # FP4 indexer-K entry: 64 code bytes + binary32 scale
 IDX_HEADS, IDX_DIM, HEADS, DIM = 32, 128, 64, 512
 
 
@@ -56,6 +57,10 @@ def lib():
         L.orc_fp4_pack.argtypes = [vp, i64, vp]
         L.orc_fp4_unpack.argtypes = [vp, i64, vp]
         L.orc_index_full.argtypes = [vp, vp, vp, i64, i32, i32, vp, vp, i32, vp]
+        L.orc_index_full_fp4k.argtypes = [vp, vp, vp, i64, i32, i32, vp, vp, i32, vp]
+        L.orc_kidx_fp4_pack.argtypes = [vp, i64, vp]
+        L.orc_kidx_fp4_unpack.argtypes = [vp, i64, vp]
+        L.orc_index_reindex_fp4k.argtypes = [vp, vp, vp, i64, i32, i32, vp, vp, i64, vp]
         L.orc_pool_ids.argtypes = [vp, i32, i32, i32, vp]
         L.orc_index_reindex.argtypes = [vp, vp, vp, i64, i32, i32, vp, vp, i64, vp]
         L.orc_topk.argtypes = [vp, i32, i64, i64, vp, i32, vp, vp]
@@ -109,17 +114,41 @@ def fp4_unpack(rec):
     return out
 
 
-def index_full(q_idx, w, k_idx, N, q_per_seq, n_visible=None, block_size=0):
-    """Full-mode indexer scores [nq, N] float32 (+ block maxima when block_size>0)."""
+def kidx_fp4_pack(x_bf16):
+    """FP4 indexer-K entry of each 128-channel bf16 row [n, 68] uint8 (the
+    pages' byte accounting: 128-dim FP4 + a 4-byte scale)."""
+    x = _c(x_bf16, np.uint16).reshape(-1, IDX_DIM)
+    out = np.zeros((x.shape[0], KIDX_RECORD_BYTES), np.uint8)
+    lib().orc_kidx_fp4_pack(_p(x), x.shape[0], _p(out))
+    return out
+
+
+def kidx_fp4_unpack(rec):
+    """Exact values of FP4 indexer-K entries, float64 [n, 128]."""
+    r = _c(rec, np.uint8).reshape(-1, KIDX_RECORD_BYTES)
+    out = np.zeros((r.shape[0], IDX_DIM), np.float64)
+    lib().orc_kidx_fp4_unpack(_p(r), r.shape[0], _p(out))
+    return out
+
+
+def index_full(q_idx, w, k_idx, N, q_per_seq, n_visible=None, block_size=0, k_fp4=None):
+    """Full-mode indexer scores [nq, N] float32 (+ block maxima when block_size>0).
+    The indexer K is bf16 `k_idx` [nseq, N, 128], or FP4 entries `k_fp4`
+    [nseq, N, 68] when given (then k_idx is ignored)."""
     q = _c(q_idx, np.uint16)
     nq = q.shape[0]
     ww = _c(w, np.float32)
-    k = _c(k_idx, np.uint16)
     nv = _c(n_visible, np.int32)
     scores = np.zeros((nq, N), np.float32)
     nb = (N + block_size - 1) // block_size if block_size > 0 else 0
     blocks = np.zeros((nq, nb), np.float32) if block_size > 0 else None
-    lib().orc_index_full(_p(q), _p(ww), _p(k), N, nq, q_per_seq, _p(nv), _p(scores), block_size, _p(blocks))
+    if k_fp4 is not None:
+        k = _c(k_fp4, np.uint8)
+        lib().orc_index_full_fp4k(_p(q), _p(ww), _p(k), N, nq, q_per_seq, _p(nv), _p(scores), block_size,
+                                  _p(blocks))
+    else:
+        k = _c(k_idx, np.uint16)
+        lib().orc_index_full(_p(q), _p(ww), _p(k), N, nq, q_per_seq, _p(nv), _p(scores), block_size, _p(blocks))
     return (scores, blocks) if block_size > 0 else scores
 
 
@@ -132,14 +161,19 @@ def pool_ids(blocks, block_size):
     return out
 
 
-def index_reindex(q_idx, w, k_idx, N, q_per_seq, pool, n_visible=None):
-    """Reindex-mode scores over pool positions [nq, pool_len] float32."""
+def index_reindex(q_idx, w, k_idx, N, q_per_seq, pool, n_visible=None, k_fp4=None):
+    """Reindex-mode scores over pool positions [nq, pool_len] float32 (FP4
+    indexer K from `k_fp4` when given)."""
     q = _c(q_idx, np.uint16)
     nq = q.shape[0]
     pl = _c(pool, np.int32)
     out = np.zeros(pl.shape, np.float32)
-    lib().orc_index_reindex(_p(q), _p(_c(w, np.float32)), _p(_c(k_idx, np.uint16)), N, nq, q_per_seq,
-                            _p(_c(n_visible, np.int32)), _p(pl), pl.shape[1], _p(out))
+    if k_fp4 is not None:
+        lib().orc_index_reindex_fp4k(_p(q), _p(_c(w, np.float32)), _p(_c(k_fp4, np.uint8)), N, nq, q_per_seq,
+                                     _p(_c(n_visible, np.int32)), _p(pl), pl.shape[1], _p(out))
+    else:
+        lib().orc_index_reindex(_p(q), _p(_c(w, np.float32)), _p(_c(k_idx, np.uint16)), N, nq, q_per_seq,
+                                _p(_c(n_visible, np.int32)), _p(pl), pl.shape[1], _p(out))
     return out
 
 

@@ -490,3 +490,117 @@ def test_planted_entries_are_recalled():
     top = O.topk(s, 512)
     for r in range(4):
         assert set(wl.planted[r].tolist()) <= set(top[r].tolist())
+
+
+# ------------------------------------------------------ FP4 indexer K (NEXT row)
+
+def _kidx_deq_independent(rec):
+    """Decode FP4 indexer-K entries with the OCP E2M1 table and numpy's view of
+    the little-endian binary32 scale."""
+    rec = np.asarray(rec, np.uint8).reshape(-1, 68)
+    codes = rec[:, :64]
+    nib = np.stack([codes & 15, codes >> 4], -1).reshape(rec.shape[0], 128)
+    sc = np.ascontiguousarray(rec[:, 64:68]).view("<f4").astype(np.float64)  # [n, 1]
+    return _e2m1_table()[nib] * sc
+
+
+def _nearest_grid_code(x, s):
+    """Brute force over the 8 magnitudes: nearest v*s to |x| (exact in float64
+    for a binary32 s), ties to the even code, +0 for magnitude 0."""
+    mags = np.array([0, 0.5, 1, 1.5, 2, 3, 4, 6], np.float64) * s
+    d = np.abs(np.abs(x) - mags)
+    best = 0
+    for c in range(8):
+        if d[c] < d[best] or (d[c] == d[best] and c % 2 == 0 and best % 2 == 1):
+            best = c
+    if best and x < 0:
+        best |= 8
+    return best
+
+
+def test_kidx_fp4_entry_layout_matches_68_byte_accounting():
+    g = _golden("byte_accounting.txt")
+    assert O.KIDX_RECORD_BYTES == int(g["indexer_key_bytes_read"]) == 128 // 2 + 4
+    x = np.zeros((2, 128), np.float32)
+    x[0, :6] = [6, -6, 3, 0.5, 0, -1.25]  # amax 6 -> scale 1; -1.25 is a tie -> 1 (even code 2)
+    x[1, 127] = -0.75 * 2.0 ** -20        # the amax: scale = it / 6, code 7 (6s) with the sign bit
+    rec = O.kidx_fp4_pack(_bf16(x))
+    assert rec.shape == (2, 68)
+    assert list(rec[0, :3]) == [0xF7, 0x15, 0xA0] and not rec[0, 3:64].any()
+    assert rec[0, 64:].tobytes() == np.float32(1.0).tobytes()  # little-endian binary32
+    s1 = np.float32(np.float32(0.75 * 2.0 ** -20) / np.float32(6.0))
+    assert rec[1, 64:].tobytes() == s1.tobytes()
+    assert rec[1, 63] == (0x8 | 7) << 4 and not rec[1, :63].any()
+
+
+def test_kidx_fp4_codes_brute_force_and_scale_definition():
+    rng = np.random.default_rng(21)
+    rows = np.concatenate([rng.normal(0, 1, (40, 128)), rng.normal(0, 1, (20, 128)) * np.exp2(
+        rng.integers(-30, 30, (20, 1))), rng.uniform(-6, 6, (10, 128))]).astype(np.float32)
+    xb = _bf16(rows)
+    xf = _bf16_to_f64(xb)
+    rec = O.kidx_fp4_pack(xb)
+    for r in range(rows.shape[0]):
+        amax = np.float32(np.abs(xf[r]).max())
+        s = np.float32(amax / np.float32(6.0))
+        assert rec[r, 64:].tobytes() == s.tobytes()
+        nib = np.stack([rec[r, :64] & 15, rec[r, :64] >> 4], -1).reshape(128)
+        want = [_nearest_grid_code(xf[r, c], float(s)) for c in range(128)]
+        assert list(nib) == want, r
+
+
+def test_kidx_fp4_unpack_is_table_times_scale_and_ties_go_even():
+    rng = np.random.default_rng(22)
+    xb = _rand_bf16(rng, (64, 128), 3.0)
+    rec = O.kidx_fp4_pack(xb)
+    assert np.array_equal(O.kidx_fp4_unpack(rec), _kidx_deq_independent(rec))
+    # every midpoint between neighbours of the grid, times scale 1 (amax 6)
+    mids = np.array([0.25, 0.75, 1.25, 1.75, 2.5, 3.5, 5.0])
+    even = np.array([0, 2, 2, 4, 4, 6, 6])  # the even neighbour's code
+    x = np.zeros((1, 128), np.float32)
+    x[0, 0] = 6.0
+    x[0, 1:8] = mids
+    x[0, 8:15] = -mids
+    rec = O.kidx_fp4_pack(_bf16(x))
+    nib = np.stack([rec[0, :64] & 15, rec[0, :64] >> 4], -1).reshape(128)
+    assert list(nib[1:8]) == list(even)
+    assert list(nib[8:15]) == [c | 8 if c else 0 for c in even]
+    # an all-zero row: zero scale, zero codes
+    assert not O.kidx_fp4_pack(np.zeros((1, 128), np.uint16)).any()
+
+
+def test_kidx_fp4_pack_is_scale_equivariant():
+    rng = np.random.default_rng(23)
+    xb = _rand_bf16(rng, (32, 128))
+    rec = O.kidx_fp4_pack(xb)
+    for m in (-7, 5):
+        rec2 = O.kidx_fp4_pack(_bf16(_bf16_to_f64(xb) * 2.0 ** m))
+        assert np.array_equal(rec2[:, :64], rec[:, :64])
+        assert np.array_equal(rec2[:, 64:].copy().view("<f4"), rec[:, 64:].copy().view("<f4") * np.float32(2.0 ** m))
+
+
+def test_index_fp4k_is_the_score_formula_on_decoded_keys():
+    rng = np.random.default_rng(24)
+    nq, N = 3, 150
+    q = _rand_bf16(rng, (nq, 32, 128))
+    w = rng.uniform(0, 1, (nq, 32)).astype(np.float32)
+    kf = O.kidx_fp4_pack(_rand_bf16(rng, (nq * N, 128))).reshape(nq, N, 68)
+    nv = np.array([150, 61, 0], np.int32)
+    s, b = O.index_full(q, w, None, N, 1, n_visible=nv, block_size=8, k_fp4=kf)
+    kd = _kidx_deq_independent(kf.reshape(-1, 68)).reshape(nq, N, 128)
+    d = np.einsum("qhc,qnc->qhn", _bf16_to_f64(q), kd)
+    ref = np.einsum("qh,qhn->qn", w.astype(np.float64), np.maximum(d, 0.0))
+    for r in range(nq):
+        assert np.allclose(s[r, :nv[r]], ref[r, :nv[r]], rtol=1e-6, atol=1e-6)
+        assert np.all(np.isneginf(s[r, nv[r]:]))
+    pad = np.concatenate([s[0], np.full(152 - N, -np.inf, np.float32)])
+    assert np.array_equal(b[0], pad.reshape(19, 8).max(1))
+    # Reindex over a pool scores the same entries identically
+    pool = np.stack([np.arange(0, 2048, 8) % N for _ in range(nq)]).astype(np.int32)
+    pool[1, 5] = -1
+    ps = O.index_reindex(q, w, None, N, 1, pool, n_visible=nv, k_fp4=kf)
+    for r in range(nq):
+        for j in range(pool.shape[1]):
+            i = pool[r, j]
+            exp = s[r, i] if i >= 0 else -np.inf
+            assert ps[r, j] == exp or (np.isneginf(ps[r, j]) and np.isneginf(exp))
