@@ -11,7 +11,10 @@ A step is one pass of the whole hot path over one batch of synthetic input:
       -> Top-512 -> 6 attention layers (the Full layer's and 5 Reuse layers');
   decoder_group256k : the 256K shapes as a decoder group: Reindex over a pool
       built once beforehand (untimed) -> Top-512 -> 4 attention layers (the
-      Reindex layer's and 3 Reuse layers').
+      Reindex layer's and 3 Reuse layers');
+  encoder64k_fp4k / decode1m_fp4k : the 64K and 1M steps reading the indexer
+      K as FP4 entries (68 B) packed from the same kind of bf16 keys before
+      timing.
 The headline is decode queries/s on encoder64k (64 queries, 64K-token context
 at m=2 = 32768 FP4 entries per sequence). Inputs live in HBM before timing and
 two independent input sets alternate between steps, so the 256 MB last-level
@@ -38,10 +41,12 @@ HEADLINE = "encoder64k"
 
 
 def alg_bytes_index_full(wl):
-    """K_idx rows read once per query (256 B each; prefill: once per sequence),
-    scores written (4 B per entry per query), queries and weights read."""
+    """K_idx rows read once per query (256 B bf16 or 68 B FP4 entries; prefill:
+    once per sequence), scores written (4 B per entry per query), queries and
+    weights read."""
     n_vis = wl.N * wl.nq if wl.n_visible is None else int(wl.n_visible.sum().item())
-    kbytes = (wl.N * 256 * wl.nseq) if wl.q_per_seq > 1 else n_vis * 256
+    row = 68 if wl.kfmt == "fp4" else 256
+    kbytes = (wl.N * row * wl.nseq) if wl.q_per_seq > 1 else n_vis * row
     out = wl.nq * wl.N * 4 + (wl.nq * ((wl.N + 7) // 8) * 4 if wl.hier else 0)
     return kbytes + out + wl.nq * (32 * 128 * 2 + 32 * 4)
 
@@ -95,32 +100,35 @@ def run_step(step, k_idx, kv, timer=None):
 
 
 def bench_workload(name, steps, warmup, nsets, torch):
-    from kv_cache_compression_csa2_amd.pipeline import Step, pack_workload_kv
+    from kv_cache_compression_csa2_amd.pipeline import Step, pack_workload_kv, workload_kidx
     from kv_cache_compression_csa2_amd.workloads import CONFIGS, make_workload
     dev = "cuda"
     sets = []
     for s in range(nsets):
         wl = make_workload(name, device=dev, seed=CONFIGS[name]["seed"] + 100 * s)
         kv = pack_workload_kv(wl, dev)
+        kk = workload_kidx(wl)
+        if kk is not wl.k_idx:
+            wl.k_idx = None  # the step reads the FP4 entries only
         st = Step(wl, dev)
-        st.prepare(wl.k_idx)
-        sets.append((st, wl, kv))
+        st.prepare(kk)
+        sets.append((st, wl, kv, kk))
     torch.cuda.synchronize()
     for i in range(warmup):
-        st, wl, kv = sets[i % nsets]
-        run_step(st, wl.k_idx, kv)
+        st, wl, kv, kk = sets[i % nsets]
+        run_step(st, kk, kv)
     torch.cuda.synchronize()
     t0 = time.perf_counter()
     for i in range(steps):
-        st, wl, kv = sets[i % nsets]
-        run_step(st, wl.k_idx, kv)
+        st, wl, kv, kk = sets[i % nsets]
+        run_step(st, kk, kv)
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
     # second timed pass with per-call events (same work, separate from the wall clock)
     timer = Timer(torch)
     for i in range(steps):
-        st, wl, kv = sets[i % nsets]
-        run_step(st, wl.k_idx, kv, timer)
+        st, wl, kv, kk = sets[i % nsets]
+        run_step(st, kk, kv, timer)
     torch.cuda.synchronize()
     calls = timer.summary()
     wl = sets[0][1]
@@ -252,7 +260,8 @@ def main():
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--workloads",
-                    default="encoder64k,decoder256k,decode1m,prefill128k,encoder_group64k,decoder_group256k")
+                    default="encoder64k,decoder256k,decode1m,prefill128k,encoder_group64k,decoder_group256k,"
+                            "encoder64k_fp4k,decode1m_fp4k")
     ap.add_argument("--attn-sweep", default="64,256,1024")
     ap.add_argument("--no-cpu", action="store_true")
     ap.add_argument("--calibrate-copy", action="store_true",

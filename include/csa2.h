@@ -62,6 +62,7 @@ extern "C" {
 #define CSA2_IDX_DIM 128    /* indexer head dim */
 #define CSA2_GROUP 16       /* channels per E4M3 scale */
 #define CSA2_RECORD 288     /* bytes per FP4 main-KV entry: 256 code bytes + 32 scale bytes */
+#define CSA2_KIDX_RECORD 68 /* bytes per FP4 indexer-K entry: 64 code bytes + binary32 scale */
 #define CSA2_MAX_WINDOW 128 /* sliding-window length limit */
 #define CSA2_MAX_TOPK 4096  /* largest k accepted by csa2_topk */
 
@@ -128,6 +129,38 @@ int csa2_index_full(const uint16_t* q_idx, const float* w, const uint16_t* k_idx
 int csa2_index_reindex(const uint16_t* q_idx, const float* w, const uint16_t* k_idx, int64_t N, int32_t nq,
                        int32_t q_per_seq, const int32_t* n_visible, const int32_t* cand_blocks, int32_t nb,
                        int32_t block_size, float* pool_scores, int32_t* pool_ids, hipStream_t stream);
+
+/*
+ * kidx_fp4_pack -- FP4 indexer-K entries, the storage precision the pages'
+ * byte accounting implies (890 B/token = 2.5 entries x (288 B main KV + 68 B
+ * indexer K): titansim blog, eogee.com report 5.3; eogee.com 3.4 notes FP4
+ * indexer Q/K in the predecessor).
+ *   x_bf16 [n][128] bf16 row-major.
+ *   out    [n][68] bytes. Entry: byte j (0..63) holds channel 2j in bits 3:0
+ *          and channel 2j+1 in bits 7:4 as E2M1 codes (bit 3 sign); bytes
+ *          64..67 hold the scale s as an IEEE binary32, least significant byte
+ *          first. s = amax / 6 (fp32, round to nearest); each channel takes the
+ *          E2M1 code whose value times s is nearest to x (ties to the even
+ *          code, beyond 6s -> 6s, zero magnitude -> +0); s == 0 gives zero
+ *          codes. Inputs must be finite. n >= 0; entries are independent.
+ *   value(channel c) = E2M1(code_c) * s.
+ */
+int kidx_fp4_pack(const uint16_t* x_bf16, int64_t n, uint8_t* out, hipStream_t stream);
+
+/*
+ * csa2_index_full_fp4k / csa2_index_reindex_fp4k -- csa2_index_full and
+ * csa2_index_reindex over the FP4 indexer-K cache k_fp4 [nseq][N][68] (entries
+ * of kidx_fp4_pack) instead of bf16 k_idx; every other argument, output and
+ * error rule is the same. The score uses the decoded key E2M1(code) * s; the
+ * kernels apply s once per entry after the head sum, since ReLU(s x) = s ReLU(x)
+ * for s >= 0.
+ */
+int csa2_index_full_fp4k(const uint16_t* q_idx, const float* w, const uint8_t* k_fp4, int64_t N, int32_t nq,
+                         int32_t q_per_seq, const int32_t* n_visible, float* scores, int32_t block_size,
+                         float* block_scores, hipStream_t stream);
+int csa2_index_reindex_fp4k(const uint16_t* q_idx, const float* w, const uint8_t* k_fp4, int64_t N, int32_t nq,
+                            int32_t q_per_seq, const int32_t* n_visible, const int32_t* cand_blocks, int32_t nb,
+                            int32_t block_size, float* pool_scores, int32_t* pool_ids, hipStream_t stream);
 
 /*
  * csa2_topk -- per-row Top-K selection (titansim blog, CSA2 modes: Top-512;

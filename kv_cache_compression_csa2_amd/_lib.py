@@ -14,6 +14,7 @@ LIB_PATH = os.path.join(_HERE, "libcsa2.so")
 
 CSA2_OK, CSA2_EINVAL, CSA2_ELAUNCH, CSA2_EWORKSPACE = 0, -1, -2, -3
 DIM, HEADS, IDX_HEADS, IDX_DIM, RECORD = 512, 64, 32, 128, 288
+KIDX_RECORD = 68  # FP4 indexer-K entry: 64 code bytes + binary32 scale
 
 _lib = None
 
@@ -40,6 +41,9 @@ def load():
     L.fp4_kv_unpack.argtypes = [vp, i64, vp, vp]
     L.csa2_index_full.argtypes = [vp, vp, vp, i64, i32, i32, vp, vp, i32, vp, vp]
     L.csa2_index_reindex.argtypes = [vp, vp, vp, i64, i32, i32, vp, vp, i32, i32, vp, vp, vp]
+    L.kidx_fp4_pack.argtypes = [vp, i64, vp, vp]
+    L.csa2_index_full_fp4k.argtypes = [vp, vp, vp, i64, i32, i32, vp, vp, i32, vp, vp]
+    L.csa2_index_reindex_fp4k.argtypes = [vp, vp, vp, i64, i32, i32, vp, vp, i32, i32, vp, vp, vp]
     L.csa2_topk_workspace_bytes.argtypes = [i32, i64, i32]
     L.csa2_topk_workspace_bytes.restype = sz
     L.csa2_topk.argtypes = [vp, i32, i64, i64, vp, i32, vp, vp, vp, sz, vp]
@@ -47,7 +51,7 @@ def load():
     L.csa2_sparse_attn_workspace_bytes.restype = sz
     L.csa2_sparse_attn.argtypes = [vp, vp, i64, i32, i32, vp, i32, vp, i64, vp, vp, f32, vp, vp, vp, sz, vp]
     for name in ["fp4_kv_pack", "fp4_kv_unpack", "csa2_index_full", "csa2_index_reindex", "csa2_topk",
-                 "csa2_sparse_attn"]:
+                 "csa2_sparse_attn", "kidx_fp4_pack", "csa2_index_full_fp4k", "csa2_index_reindex_fp4k"]:
         getattr(L, name).restype = ctypes.c_int
     _lib = L
     return L
@@ -55,7 +59,7 @@ def load():
 
 EXPORTS = ["csa2_format_version", "csa2_last_error", "fp4_kv_pack", "fp4_kv_unpack", "csa2_index_full",
            "csa2_index_reindex", "csa2_topk_workspace_bytes", "csa2_topk", "csa2_sparse_attn_workspace_bytes",
-           "csa2_sparse_attn"]
+           "csa2_sparse_attn", "kidx_fp4_pack", "csa2_index_full_fp4k", "csa2_index_reindex_fp4k"]
 
 
 def _ptr(t):
@@ -111,39 +115,64 @@ def fp4_kv_unpack(rec, out=None, stream=None):
     return out
 
 
+def _k_args(k_idx, k_fp4):
+    """(pointer, call suffix) of the indexer-K operand: bf16 k_idx or FP4 k_fp4."""
+    if (k_idx is None) == (k_fp4 is None):
+        raise ValueError("pass exactly one of k_idx (bf16) and k_fp4 (uint8 [.., 68])")
+    if k_fp4 is not None:
+        _need(k_fp4, torch.uint8, "k_fp4")
+        return _ptr(k_fp4), "_fp4k"
+    _need(k_idx, torch.bfloat16, "k_idx")
+    return _ptr(k_idx), ""
+
+
+def kidx_fp4_pack(x, out=None, stream=None):
+    """bf16 [n,128] indexer keys -> uint8 [n,68] FP4 entries (64 code bytes + binary32 scale)."""
+    _need(x, torch.bfloat16, "x")
+    n = x.numel() // IDX_DIM
+    if out is None:
+        out = torch.empty((n, KIDX_RECORD), dtype=torch.uint8, device=x.device)
+    _need(out, torch.uint8, "out")
+    _check(load().kidx_fp4_pack(_ptr(x), n, _ptr(out), _stream(stream)), "kidx_fp4_pack")
+    return out
+
+
 def csa2_index_full(q_idx, w, k_idx, N, q_per_seq, n_visible=None, block_size=0, scores=None, block_scores=None,
-                    stream=None):
-    """Full-mode indexer scores [nq,N] fp32 (and block maxima [nq,ceil(N/8)] when block_size == 8)."""
-    for t, dt, nm in [(q_idx, torch.bfloat16, "q_idx"), (w, torch.float32, "w"), (k_idx, torch.bfloat16, "k_idx"),
-                      (n_visible, torch.int32, "n_visible")]:
+                    stream=None, k_fp4=None):
+    """Full-mode indexer scores [nq,N] fp32 (and block maxima [nq,ceil(N/8)] when block_size == 8).
+    The indexer K is bf16 `k_idx` [nseq,N,128], or FP4 entries `k_fp4` [nseq,N,68] (pass k_idx=None)."""
+    for t, dt, nm in [(q_idx, torch.bfloat16, "q_idx"), (w, torch.float32, "w"), (n_visible, torch.int32, "n_visible")]:
         _need(t, dt, nm)
+    kp, suffix = _k_args(k_idx, k_fp4)
     nq = q_idx.shape[0]
     dev = q_idx.device
     if scores is None:
         scores = torch.empty((nq, N), dtype=torch.float32, device=dev)
     if block_size and block_scores is None:
         block_scores = torch.empty((nq, (N + 7) // 8), dtype=torch.float32, device=dev)
-    _check(load().csa2_index_full(_ptr(q_idx), _ptr(w), _ptr(k_idx), N, nq, q_per_seq, _ptr(n_visible),
-                                  _ptr(scores), block_size, _ptr(block_scores) if block_size else None,
-                                  _stream(stream)), "csa2_index_full")
+    fn = getattr(load(), "csa2_index_full" + suffix)
+    _check(fn(_ptr(q_idx), _ptr(w), kp, N, nq, q_per_seq, _ptr(n_visible), _ptr(scores), block_size,
+              _ptr(block_scores) if block_size else None, _stream(stream)), "csa2_index_full" + suffix)
     return (scores, block_scores) if block_size else scores
 
 
 def csa2_index_reindex(q_idx, w, k_idx, N, q_per_seq, cand_blocks, n_visible=None, block_size=8, pool_scores=None,
-                       pool_ids=None, want_ids=True, stream=None):
-    """Reindex-mode scores over the pool [nq, nb*8] fp32 (+ entry ids [nq, nb*8] int32)."""
-    for t, dt, nm in [(q_idx, torch.bfloat16, "q_idx"), (w, torch.float32, "w"), (k_idx, torch.bfloat16, "k_idx"),
+                       pool_ids=None, want_ids=True, stream=None, k_fp4=None):
+    """Reindex-mode scores over the pool [nq, nb*8] fp32 (+ entry ids [nq, nb*8] int32).
+    The indexer K is bf16 `k_idx`, or FP4 entries `k_fp4` (pass k_idx=None)."""
+    for t, dt, nm in [(q_idx, torch.bfloat16, "q_idx"), (w, torch.float32, "w"),
                       (cand_blocks, torch.int32, "cand_blocks"), (n_visible, torch.int32, "n_visible")]:
         _need(t, dt, nm)
+    kp, suffix = _k_args(k_idx, k_fp4)
     nq, nb = cand_blocks.shape
     dev = q_idx.device
     if pool_scores is None:
         pool_scores = torch.empty((nq, nb * block_size), dtype=torch.float32, device=dev)
     if want_ids and pool_ids is None:
         pool_ids = torch.empty((nq, nb * block_size), dtype=torch.int32, device=dev)
-    _check(load().csa2_index_reindex(_ptr(q_idx), _ptr(w), _ptr(k_idx), N, nq, q_per_seq, _ptr(n_visible),
-                                     _ptr(cand_blocks), nb, block_size, _ptr(pool_scores), _ptr(pool_ids),
-                                     _stream(stream)), "csa2_index_reindex")
+    fn = getattr(load(), "csa2_index_reindex" + suffix)
+    _check(fn(_ptr(q_idx), _ptr(w), kp, N, nq, q_per_seq, _ptr(n_visible), _ptr(cand_blocks), nb, block_size,
+              _ptr(pool_scores), _ptr(pool_ids), _stream(stream)), "csa2_index_reindex" + suffix)
     return pool_scores, pool_ids
 
 

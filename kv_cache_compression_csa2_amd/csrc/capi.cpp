@@ -51,7 +51,7 @@ int fp4_kv_unpack(const uint8_t* in, int64_t n, uint16_t* y_bf16, hipStream_t st
     return launched("fp4_kv_unpack");
 }
 
-static int check_index_common(const char* who, const uint16_t* q_idx, const float* w, const uint16_t* k_idx,
+static int check_index_common(const char* who, const uint16_t* q_idx, const float* w, const void* k_idx,
                               int64_t N, int32_t nq, int32_t q_per_seq) {
     if (nq < 0) return fail(CSA2_EINVAL, "%s: nq < 0", who);
     if (N < 1 || N > kMaxN) return fail(CSA2_EINVAL, "%s: N must be in [1, 2^31-1]", who);
@@ -61,32 +61,70 @@ static int check_index_common(const char* who, const uint16_t* q_idx, const floa
     return CSA2_OK;
 }
 
+// Full scoring over bf16 (kfp4 == false) or FP4 (kfp4 == true) indexer K.
+static int index_full_impl(const char* who, const uint16_t* q_idx, const float* w, const void* k, bool kfp4,
+                           int64_t N, int32_t nq, int32_t q_per_seq, const int32_t* n_visible, float* scores,
+                           int32_t block_size, float* block_scores, hipStream_t stream) {
+    int rc = check_index_common(who, q_idx, w, k, N, nq, q_per_seq);
+    if (rc) return rc;
+    if (nq > 0 && !scores) return fail(CSA2_EINVAL, "%s: null scores", who);
+    if (block_size != 0 && block_size != 8) return fail(CSA2_EINVAL, "%s: block_size must be 0 or 8", who);
+    if (block_size == 8 && nq > 0 && !block_scores)
+        return fail(CSA2_EINVAL, "%s: block_scores required when block_size == 8", who);
+    (void)hipGetLastError();
+    csa2::launch_index_full(q_idx, w, k, kfp4, N, nq, q_per_seq, n_visible, scores, block_size, block_scores, stream);
+    return launched(who);
+}
+
+static int index_reindex_impl(const char* who, const uint16_t* q_idx, const float* w, const void* k, bool kfp4,
+                              int64_t N, int32_t nq, int32_t q_per_seq, const int32_t* n_visible,
+                              const int32_t* cand_blocks, int32_t nb, int32_t block_size, float* pool_scores,
+                              int32_t* pool_ids, hipStream_t stream) {
+    int rc = check_index_common(who, q_idx, w, k, N, nq, q_per_seq);
+    if (rc) return rc;
+    if (block_size != 8) return fail(CSA2_EINVAL, "%s: block_size must be 8", who);
+    if (nb < 1 || nb > 65536) return fail(CSA2_EINVAL, "%s: nb must be in [1, 65536]", who);
+    if (nq > 0 && (!cand_blocks || !pool_scores)) return fail(CSA2_EINVAL, "%s: null pointer", who);
+    (void)hipGetLastError();
+    csa2::launch_index_reindex(q_idx, w, k, kfp4, N, nq, q_per_seq, n_visible, cand_blocks, nb, pool_scores, pool_ids,
+                               stream);
+    return launched(who);
+}
+
 int csa2_index_full(const uint16_t* q_idx, const float* w, const uint16_t* k_idx, int64_t N, int32_t nq,
                     int32_t q_per_seq, const int32_t* n_visible, float* scores, int32_t block_size,
                     float* block_scores, hipStream_t stream) {
-    int rc = check_index_common("csa2_index_full", q_idx, w, k_idx, N, nq, q_per_seq);
-    if (rc) return rc;
-    if (nq > 0 && !scores) return fail(CSA2_EINVAL, "csa2_index_full: null scores");
-    if (block_size != 0 && block_size != 8) return fail(CSA2_EINVAL, "csa2_index_full: block_size must be 0 or 8");
-    if (block_size == 8 && nq > 0 && !block_scores)
-        return fail(CSA2_EINVAL, "csa2_index_full: block_scores required when block_size == 8");
-    (void)hipGetLastError();
-    csa2::launch_index_full(q_idx, w, k_idx, N, nq, q_per_seq, n_visible, scores, block_size, block_scores, stream);
-    return launched("csa2_index_full");
+    return index_full_impl("csa2_index_full", q_idx, w, k_idx, false, N, nq, q_per_seq, n_visible, scores,
+                           block_size, block_scores, stream);
+}
+
+int csa2_index_full_fp4k(const uint16_t* q_idx, const float* w, const uint8_t* k_fp4, int64_t N, int32_t nq,
+                         int32_t q_per_seq, const int32_t* n_visible, float* scores, int32_t block_size,
+                         float* block_scores, hipStream_t stream) {
+    return index_full_impl("csa2_index_full_fp4k", q_idx, w, k_fp4, true, N, nq, q_per_seq, n_visible, scores,
+                           block_size, block_scores, stream);
 }
 
 int csa2_index_reindex(const uint16_t* q_idx, const float* w, const uint16_t* k_idx, int64_t N, int32_t nq,
                        int32_t q_per_seq, const int32_t* n_visible, const int32_t* cand_blocks, int32_t nb,
                        int32_t block_size, float* pool_scores, int32_t* pool_ids, hipStream_t stream) {
-    int rc = check_index_common("csa2_index_reindex", q_idx, w, k_idx, N, nq, q_per_seq);
-    if (rc) return rc;
-    if (block_size != 8) return fail(CSA2_EINVAL, "csa2_index_reindex: block_size must be 8");
-    if (nb < 1 || nb > 65536) return fail(CSA2_EINVAL, "csa2_index_reindex: nb must be in [1, 65536]");
-    if (nq > 0 && (!cand_blocks || !pool_scores)) return fail(CSA2_EINVAL, "csa2_index_reindex: null pointer");
+    return index_reindex_impl("csa2_index_reindex", q_idx, w, k_idx, false, N, nq, q_per_seq, n_visible, cand_blocks,
+                              nb, block_size, pool_scores, pool_ids, stream);
+}
+
+int csa2_index_reindex_fp4k(const uint16_t* q_idx, const float* w, const uint8_t* k_fp4, int64_t N, int32_t nq,
+                            int32_t q_per_seq, const int32_t* n_visible, const int32_t* cand_blocks, int32_t nb,
+                            int32_t block_size, float* pool_scores, int32_t* pool_ids, hipStream_t stream) {
+    return index_reindex_impl("csa2_index_reindex_fp4k", q_idx, w, k_fp4, true, N, nq, q_per_seq, n_visible,
+                              cand_blocks, nb, block_size, pool_scores, pool_ids, stream);
+}
+
+int kidx_fp4_pack(const uint16_t* x_bf16, int64_t n, uint8_t* out, hipStream_t stream) {
+    if (n < 0) return fail(CSA2_EINVAL, "kidx_fp4_pack: n < 0");
+    if (n > 0 && (!x_bf16 || !out)) return fail(CSA2_EINVAL, "kidx_fp4_pack: null pointer");
     (void)hipGetLastError();
-    csa2::launch_index_reindex(q_idx, w, k_idx, N, nq, q_per_seq, n_visible, cand_blocks, nb, pool_scores, pool_ids,
-                               stream);
-    return launched("csa2_index_reindex");
+    csa2::launch_kidx_fp4_pack(x_bf16, n, out, stream);
+    return launched("kidx_fp4_pack");
 }
 
 size_t csa2_topk_workspace_bytes(int32_t rows, int64_t ncols, int32_t k) {

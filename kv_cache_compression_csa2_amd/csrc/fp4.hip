@@ -69,6 +69,59 @@ __global__ __launch_bounds__(256) void fp4_unpack_kernel(const uint8_t* __restri
     dst[1] = make_uint4(o[4], o[5], o[6], o[7]);
 }
 
+// FP4 indexer-K entries (68 bytes: 64 code bytes, binary32 scale), the
+// storage precision implied by the pages' 890 B/token accounting (titansim
+// blog; eogee.com report 5.3). 16 threads per 128-channel row, 8 channels
+// each; the row's 16 threads are 16 aligned lanes of one wave. The scale is
+// amax / 6 rounded to nearest; the midpoints of the E2M1 grid times that
+// binary32 scale are exact in double, so the nearest-code decision (ties to
+// the even code) is made there.
+__global__ __launch_bounds__(256) void kidx_fp4_pack_kernel(const uint16_t* __restrict__ x, int64_t n,
+                                                            uint8_t* __restrict__ out) {
+    const int64_t t = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+    const int64_t row = t >> 4;
+    const int sl = (int)(t & 15);
+    const bool ok = row < n;
+    const uint4 v = ok ? reinterpret_cast<const uint4*>(x + row * kIdxDim)[sl] : make_uint4(0u, 0u, 0u, 0u);
+    const uint32_t wv[4] = {v.x, v.y, v.z, v.w};
+    float xs[8];
+    float amax = 0.0f;
+#pragma unroll
+    for (int i = 0; i < 4; i++) {
+        xs[2 * i] = bf16_bits_to_float(wv[i] & 0xFFFFu);
+        xs[2 * i + 1] = bf16_bits_to_float(wv[i] >> 16);
+    }
+#pragma unroll
+    for (int i = 0; i < 8; i++) amax = fmaxf(amax, fabsf(xs[i]));
+#pragma unroll
+    for (int o = 1; o < 16; o <<= 1) amax = fmaxf(amax, __shfl_xor(amax, o));
+    if (!ok) return;
+    const float s = __fdiv_rn(amax, 6.0f);
+    const double sd = (double)s;
+    const double mid[7] = {0.25 * sd, 0.75 * sd, 1.25 * sd, 1.75 * sd, 2.5 * sd, 3.5 * sd, 5.0 * sd};
+    uint32_t codes = 0;
+#pragma unroll
+    for (int i = 0; i < 8; i++) {
+        const double a = fabs((double)xs[i]);
+        uint32_t c = 0;
+#pragma unroll
+        for (int m = 0; m < 7; m++) c += (uint32_t)(a > mid[m]);
+        if (c < 7 && (c & 1u) && a == mid[c]) c++;  // exact tie: the even neighbour
+        if (c != 0 && xs[i] < 0.0f) c |= 8u;
+        codes |= c << (4 * i);
+    }
+    uint8_t* dst = out + row * 68;
+    reinterpret_cast<uint32_t*>(dst)[sl] = codes;
+    if (sl == 0) reinterpret_cast<uint32_t*>(dst)[16] = __float_as_uint(s);
+}
+
+int launch_kidx_fp4_pack(const uint16_t* x, int64_t n, uint8_t* out, hipStream_t s) {
+    if (n == 0) return 0;
+    const int64_t blocks = (n * 16 + 255) / 256;
+    hipLaunchKernelGGL(kidx_fp4_pack_kernel, dim3((unsigned)blocks), dim3(256), 0, s, x, n, out);
+    return 0;
+}
+
 int launch_fp4_pack(const uint16_t* x, int64_t n, uint8_t* out, hipStream_t s) {
     if (n == 0) return 0;
     const int64_t threads = n * 32;

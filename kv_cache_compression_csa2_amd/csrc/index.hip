@@ -8,6 +8,11 @@
 // holds 16 heads of one entry; the ReLU-weighted head sum runs in fp32 on the
 // lane, then one cross-half exchange adds the other 16 heads.
 //
+// The indexer K is either bf16 [N][128] or FP4 entries [N][68] (128 E2M1
+// codes + one binary32 scale s, the storage precision implied by the pages'
+// byte accounting). FP4 codes decode exactly to bf16 and feed the same MFMA;
+// s multiplies the entry's head sum once (ReLU(s x) = s ReLU(x), s >= 0).
+//
 // Two kernels:
 //  * index_stream_kernel -- one query per workgroup slice; each wave streams
 //    32-entry tiles of the indexer K straight from HBM into MFMA operand
@@ -28,18 +33,43 @@ namespace {
 constexpr int kStreamThreads = 256;
 constexpr int kStreamWaves = kStreamThreads / 64;
 
-struct StreamTile {
+template <bool kFp4>
+struct StreamTile;
+template <>
+struct StreamTile<false> {
     bf16x8 b[8];
     int64_t ent;
     bool valid;
 };
+template <>
+struct StreamTile<true> {
+    uint32_t code[8];  // 64 channels of the entry, 8 per dword
+    float scale;
+    int64_t ent;
+    bool valid;
+};
+
+constexpr int kKRec = 68;  // bytes per FP4 indexer-K entry
+
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+
+// Eight E2M1 codes (channel 2b in bits 8b..8b+3, 2b+1 above) -> their exact
+// bf16 values, in channel order.
+CSA2_DEVINL bf16x8 fp4x8_to_bf16(uint32_t w) {
+    const bf16x2 p0 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(w, 1.0f, 0);
+    const bf16x2 p1 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(w, 1.0f, 1);
+    const bf16x2 p2 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(w, 1.0f, 2);
+    const bf16x2 p3 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(w, 1.0f, 3);
+    return as_bf16x8(make_uint4(__builtin_bit_cast(uint32_t, p0), __builtin_bit_cast(uint32_t, p1),
+                                __builtin_bit_cast(uint32_t, p2), __builtin_bit_cast(uint32_t, p3)));
+}
 
 // Row of the accumulator held in register r by a lane of half `half` (32x32 layout).
 CSA2_DEVINL int acc_row(int r, int half) { return (r >> 2) * 8 + half * 4 + (r & 3); }
 
-template <bool kReindex>
+template <bool kReindex, bool kFp4>
 __global__ __launch_bounds__(kStreamThreads) void index_stream_kernel(
-    const uint16_t* __restrict__ q_idx, const float* __restrict__ w, const uint16_t* __restrict__ k_idx, int64_t N,
+    const uint16_t* __restrict__ q_idx, const float* __restrict__ w, const void* __restrict__ k_idx, int64_t N,
     int32_t q_per_seq, const int32_t* __restrict__ n_visible, const int32_t* __restrict__ cand_blocks, int32_t nb,
     float* __restrict__ scores, float* __restrict__ block_scores, int32_t* __restrict__ pool_ids, int64_t ncols,
     int64_t ntiles, int32_t wgs_per_q, int32_t tiles_per_wg) {
@@ -51,21 +81,26 @@ __global__ __launch_bounds__(kStreamThreads) void index_stream_kernel(
     int64_t nv = n_visible ? (int64_t)n_visible[q] : N;
     nv = nv < N ? nv : N;
 
-    // A operand: head = lane % 32, channels 16j + 8*half .. +8 for step j.
-    const uint4* qsrc = reinterpret_cast<const uint4*>(q_idx + (q * kIdxHeads + col_in_tile) * kIdxDim) + half;
+    // A operand: head = lane % 32; step j covers channels 16j + 8*half .. +8
+    // (bf16 K), or 64*half + 8j .. +8 for FP4 K so that a lane's 8 steps read
+    // 32 contiguous code bytes of its entry (the same re-ordering on both
+    // operands leaves the dot product unchanged).
+    const uint16_t* qrow = q_idx + (q * kIdxHeads + col_in_tile) * kIdxDim;
     bf16x8 a[8];
 #pragma unroll
-    for (int j = 0; j < 8; j++) a[j] = as_bf16x8(qsrc[2 * j]);
+    for (int j = 0; j < 8; j++)
+        a[j] = as_bf16x8(reinterpret_cast<const uint4*>(qrow)[kFp4 ? 8 * half + j : 2 * j + half]);
     float wr[16];
 #pragma unroll
     for (int r = 0; r < 16; r++) wr[r] = w[q * kIdxHeads + acc_row(r, half)];
 
-    const uint16_t* kseq = k_idx + seq * N * kIdxDim;
+    const uint16_t* kseq = static_cast<const uint16_t*>(k_idx) + (kFp4 ? 0 : seq * N * kIdxDim);
+    const uint8_t* kfseq = static_cast<const uint8_t*>(k_idx) + (kFp4 ? seq * N * kKRec : 0);
     const int64_t t_begin = chunk * tiles_per_wg;
     const int64_t t_end = (t_begin + tiles_per_wg < ntiles) ? t_begin + tiles_per_wg : ntiles;
     const int64_t nblk = (N + 7) >> 3;
 
-    auto load = [&](int64_t t, StreamTile& st) {
+    auto load = [&](int64_t t, StreamTile<kFp4>& st) {
         const int64_t col = t * 32 + col_in_tile;
         int64_t ent;
         bool valid;
@@ -82,19 +117,34 @@ __global__ __launch_bounds__(kStreamThreads) void index_stream_kernel(
         // Plain (cache-allocating) loads: a tile reads 32 B of each of 32 rows per
         // instruction, and the other 7 instructions of the same wave consume the
         // rest of those lines, so the lines must stay in cache between them.
-        const uint4* src = reinterpret_cast<const uint4*>(kseq + (valid ? ent : 0) * kIdxDim) + half;
+        if constexpr (kFp4) {
+            // 68-byte entries are only 4-byte aligned: dword loads
+            const uint8_t* e = kfseq + (valid ? ent : 0) * kKRec;
+            const uint32_t* src = reinterpret_cast<const uint32_t*>(e + 32 * half);
 #pragma unroll
-        for (int j = 0; j < 8; j++) st.b[j] = as_bf16x8(src[2 * j]);
+            for (int j = 0; j < 8; j++) st.code[j] = src[j];
+            st.scale = *reinterpret_cast<const float*>(e + 64);
+        } else {
+            const uint4* src = reinterpret_cast<const uint4*>(kseq + (valid ? ent : 0) * kIdxDim) + half;
+#pragma unroll
+            for (int j = 0; j < 8; j++) st.b[j] = as_bf16x8(src[2 * j]);
+        }
     };
 
-    auto finish = [&](int64_t t, const StreamTile& st) {
+    auto finish = [&](int64_t t, const StreamTile<kFp4>& st) {
         f32x16 acc = {};
 #pragma unroll
-        for (int j = 0; j < 8; j++) acc = mfma32x32x16(a[j], st.b[j], acc);
+        for (int j = 0; j < 8; j++) {
+            if constexpr (kFp4)
+                acc = mfma32x32x16(a[j], fp4x8_to_bf16(st.code[j]), acc);
+            else
+                acc = mfma32x32x16(a[j], st.b[j], acc);
+        }
         float s = 0.0f;
 #pragma unroll
         for (int r = 0; r < 16; r++) s = fmaf(wr[r], relu_bits(acc[r]), s);
         s += from_upper_half(s);  // lanes 0..31 hold the sum over all 32 heads
+        if constexpr (kFp4) s *= st.scale;
         if (!st.valid) s = -INFINITY;
         const int64_t col = t * 32 + col_in_tile;
         if (half == 0 && col < ncols) scores[q * ncols + col] = s;
@@ -108,7 +158,7 @@ __global__ __launch_bounds__(kStreamThreads) void index_stream_kernel(
 
     int64_t t = t_begin + wave;
     if (t >= t_end) return;
-    StreamTile s0, s1;
+    StreamTile<kFp4> s0, s1;
     load(t, s0);
     while (true) {
         const int64_t t1 = t + kStreamWaves;
@@ -128,11 +178,27 @@ constexpr int kPfSub = 64;             // entries per LDS tile
 constexpr int kPfRow = 256 + 16;       // padded LDS row bytes
 constexpr int kPfChunk = 4096;         // entries per workgroup
 
+// Registers of one prefill tile load: bf16 K 4 units of 16 bytes per thread;
+// FP4 K 16 code bytes and the entry scale per thread.
+template <bool kFp4>
+struct PfPre;
+template <>
+struct PfPre<false> {
+    uint4 v[4];
+};
+template <>
+struct PfPre<true> {
+    uint4 v;
+    float scale;
+};
+
+template <bool kFp4>
 __global__ __launch_bounds__(256, 2) void index_prefill_kernel(
-    const uint16_t* __restrict__ q_idx, const float* __restrict__ w, const uint16_t* __restrict__ k_idx, int64_t N,
+    const uint16_t* __restrict__ q_idx, const float* __restrict__ w, const void* __restrict__ k_idx, int64_t N,
     int32_t q_per_seq, const int32_t* __restrict__ n_visible, float* __restrict__ scores,
     float* __restrict__ block_scores, int32_t nchunks) {
     __shared__ __attribute__((aligned(16))) uint8_t lds[2][kPfSub * kPfRow];
+    __shared__ float kscale[2][kPfSub];  // FP4 K: the entries' scales
     const int b = blockIdx.x;
     int chunk, qg;
     if ((nchunks & 7) == 0) {
@@ -170,41 +236,63 @@ __global__ __launch_bounds__(256, 2) void index_prefill_kernel(
         wb[r] = w[qb * kIdxHeads + acc_row(r, half)];
     }
 
-    const uint16_t* kseq = k_idx + seq * N * kIdxDim;
+    const uint16_t* kseq = static_cast<const uint16_t*>(k_idx) + (kFp4 ? 0 : seq * N * kIdxDim);
+    const uint8_t* kfseq = static_cast<const uint8_t*>(k_idx) + (kFp4 ? seq * N * kKRec : 0);
     const int64_t e_begin = (int64_t)chunk * kPfChunk;
     const int64_t e_end = (e_begin + kPfChunk < N) ? e_begin + kPfChunk : N;
     const int nsub = (int)((e_end - e_begin + kPfSub - 1) / kPfSub);
     const int64_t nblk = (N + 7) >> 3;
 
-    struct Pre {
-        uint4 v[4];
-    };
+    // Tile loads into registers. bf16 K: 4 16-byte units per thread of the
+    // 64 x 256 B tile. FP4 K: thread (entry tid/4, quarter tid%4) takes 16 code
+    // bytes (32 channels) and the entry's scale.
+    using Pre = PfPre<kFp4>;
     auto gload = [&](int st) {
         Pre p;
-#pragma unroll
-        for (int i = 0; i < 4; i++) {
-            const int u = i * 256 + tid;  // 16-byte unit within the 64 x 256 B tile
-            const int row = u >> 4, c16 = u & 15;
+        if constexpr (kFp4) {
+            const int row = tid >> 2, qq = tid & 3;
             int64_t e = e_begin + (int64_t)st * kPfSub + row;
             e = e < N ? e : 0;
-            p.v[i] = reinterpret_cast<const uint4*>(kseq + e * kIdxDim)[c16];
+            const uint32_t* src = reinterpret_cast<const uint32_t*>(kfseq + e * kKRec) + 4 * qq;
+            p.v = make_uint4(src[0], src[1], src[2], src[3]);
+            p.scale = *reinterpret_cast<const float*>(kfseq + e * kKRec + 64);
+        } else {
+#pragma unroll
+            for (int i = 0; i < 4; i++) {
+                const int u = i * 256 + tid;  // 16-byte unit within the 64 x 256 B tile
+                const int row = u >> 4, c16 = u & 15;
+                int64_t e = e_begin + (int64_t)st * kPfSub + row;
+                e = e < N ? e : 0;
+                p.v[i] = reinterpret_cast<const uint4*>(kseq + e * kIdxDim)[c16];
+            }
         }
         return p;
     };
     auto lstore = [&](int buf, const Pre& p) {
+        if constexpr (kFp4) {
+            const int row = tid >> 2, qq = tid & 3;
+            uint8_t* dst = &lds[buf][row * kPfRow + qq * 64];
+            const uint32_t c[4] = {p.v.x, p.v.y, p.v.z, p.v.w};
 #pragma unroll
-        for (int i = 0; i < 4; i++) {
-            const int u = i * 256 + tid;
-            const int row = u >> 4, c16 = u & 15;
-            *reinterpret_cast<uint4*>(&lds[buf][row * kPfRow + c16 * 16]) = p.v[i];
+            for (int i = 0; i < 4; i++) *reinterpret_cast<bf16x8*>(dst + 16 * i) = fp4x8_to_bf16(c[i]);
+            if (qq == 0) kscale[buf][row] = p.scale;
+        } else {
+#pragma unroll
+            for (int i = 0; i < 4; i++) {
+                const int u = i * 256 + tid;
+                const int row = u >> 4, c16 = u & 15;
+                *reinterpret_cast<uint4*>(&lds[buf][row * kPfRow + c16 * 16]) = p.v[i];
+            }
         }
     };
-    // ReLU-weighted head sum of one query's 32 x 32 block; valid in lanes 0..31.
-    auto head_sum = [&](const f32x16& acc, const float (&wr)[16], int64_t nv, int64_t col) {
+    // ReLU-weighted head sum of one query's 32 x 32 block (times the entry's
+    // scale for FP4 K); valid in lanes 0..31.
+    auto head_sum = [&](const f32x16& acc, const float (&wr)[16], int64_t nv, int64_t col, float esc) {
         float s = 0.0f;
 #pragma unroll
         for (int r = 0; r < 16; r++) s = fmaf(wr[r], relu_bits(acc[r]), s);
         s += from_upper_half(s);
+        if constexpr (kFp4) s *= esc;
         return col < nv ? s : -INFINITY;
     };
     auto store = [&](float s, float m, int64_t q, int64_t col) {
@@ -216,13 +304,15 @@ __global__ __launch_bounds__(256, 2) void index_prefill_kernel(
     // One group = 32 entries (rows h2*32.. of an LDS tile) for both queries:
     // 8 fragment reads, 16 MFMAs. The epilogue of the previous group runs in
     // the same straight-line block so the scheduler can put its VALU work in
-    // the shadow of these MFMAs.
-    auto group = [&](const uint8_t* tile, int h2, f32x16& acca, f32x16& accb, const f32x16& pa, const f32x16& pb,
-                     int64_t pcol, float (&out)[4]) {
-        const uint8_t* rowp = tile + (h2 * 32 + col_in_tile) * kPfRow + half * 16;
+    // the shadow of these MFMAs. The group's entry scale (FP4 K) is read here,
+    // while its tile is still in LDS, and travels with the accumulators.
+    auto group = [&](int buf, int h2, f32x16& acca, f32x16& accb, float& esc, const f32x16& pa, const f32x16& pb,
+                     float pesc, int64_t pcol, float (&out)[4]) {
+        const uint8_t* rowp = lds[buf] + (h2 * 32 + col_in_tile) * kPfRow + half * 16;
         bf16x8 bj[8];
 #pragma unroll
         for (int j = 0; j < 8; j++) bj[j] = as_bf16x8(*reinterpret_cast<const uint4*>(rowp + j * 32));
+        if constexpr (kFp4) esc = kscale[buf][h2 * 32 + col_in_tile];
         acca = f32x16{};
         accb = f32x16{};
 #pragma unroll
@@ -230,11 +320,11 @@ __global__ __launch_bounds__(256, 2) void index_prefill_kernel(
             acca = mfma32x32x16(aa[j], bj[j], acca);
             accb = mfma32x32x16(ab[j], bj[j], accb);
         }
-        out[0] = head_sum(pa, wa, nva, pcol);
-        out[1] = head_sum(pb, wb, nvb, pcol);
+        out[0] = head_sum(pa, wa, nva, pcol, pesc);
+        out[1] = head_sum(pb, wb, nvb, pcol, pesc);
         out[2] = max8_lanes(out[0]);
         out[3] = max8_lanes(out[1]);
-        __builtin_amdgcn_sched_group_barrier(0x100, 8, 0);  // fragment reads first
+        __builtin_amdgcn_sched_group_barrier(0x100, kFp4 ? 9 : 8, 0);  // fragment reads first
         __builtin_amdgcn_sched_group_barrier(0x002, 8, 0);
 #pragma unroll
         for (int i = 0; i < 16; i++) {
@@ -247,23 +337,24 @@ __global__ __launch_bounds__(256, 2) void index_prefill_kernel(
     lstore(0, gload(0));
     lds_barrier();
     f32x16 pa, pb, ca, cb;
+    float pesc = 1.0f, cesc = 1.0f;
     float out[4];
     {
         const f32x16 z = {};
-        group(lds[0], 0, pa, pb, z, z, N, out);  // no previous group: its results are discarded
+        group(0, 0, pa, pb, pesc, z, z, 1.0f, N, out);  // no previous group: its results are discarded
     }
     for (int st = 0; st < nsub; st++) {
         const bool more = st + 1 < nsub;
         // the last iteration re-reads tile 0 (in bounds) and discards it
         const Pre nxt = gload(more ? st + 1 : 0);
         const int64_t col0 = tile_base + (int64_t)st * kPfSub + col_in_tile;
-        group(lds[st & 1], 1, ca, cb, pa, pb, col0, out);
+        group(st & 1, 1, ca, cb, cesc, pa, pb, pesc, col0, out);
         store(out[0], out[2], qa, col0);
         store(out[1], out[3], qb, col0);
         if (more) lstore((st + 1) & 1, nxt);
         lds_barrier();
         // After the last tile this reads the stale buffer; those results are never stored.
-        group(lds[(st + 1) & 1], 0, pa, pb, ca, cb, col0 + 32, out);
+        group((st + 1) & 1, 0, pa, pb, pesc, ca, cb, cesc, col0 + 32, out);
         store(out[0], out[2], qa, col0 + 32);
         store(out[1], out[3], qb, col0 + 32);
     }
@@ -271,7 +362,7 @@ __global__ __launch_bounds__(256, 2) void index_prefill_kernel(
 
 }  // namespace
 
-int launch_index_full(const uint16_t* q_idx, const float* w, const uint16_t* k_idx, int64_t N, int32_t nq,
+int launch_index_full(const uint16_t* q_idx, const float* w, const void* k, bool kfp4, int64_t N, int32_t nq,
                       int32_t q_per_seq, const int32_t* n_visible, float* scores, int32_t block_size,
                       float* block_scores, hipStream_t s) {
     if (nq == 0) return 0;
@@ -279,8 +370,12 @@ int launch_index_full(const uint16_t* q_idx, const float* w, const uint16_t* k_i
     if (q_per_seq % kPfQueries == 0) {
         const int32_t nchunks = (int32_t)((N + kPfChunk - 1) / kPfChunk);
         const int64_t grid = (int64_t)(nq / kPfQueries) * nchunks;
-        hipLaunchKernelGGL(index_prefill_kernel, dim3((unsigned)grid), dim3(256), 0, s, q_idx, w, k_idx, N,
-                           q_per_seq, n_visible, scores, bs, nchunks);
+        if (kfp4)
+            hipLaunchKernelGGL(index_prefill_kernel<true>, dim3((unsigned)grid), dim3(256), 0, s, q_idx, w, k, N,
+                               q_per_seq, n_visible, scores, bs, nchunks);
+        else
+            hipLaunchKernelGGL(index_prefill_kernel<false>, dim3((unsigned)grid), dim3(256), 0, s, q_idx, w, k, N,
+                               q_per_seq, n_visible, scores, bs, nchunks);
         return 0;
     }
     const int64_t ntiles = (N + 31) / 32;
@@ -289,13 +384,19 @@ int launch_index_full(const uint16_t* q_idx, const float* w, const uint16_t* k_i
     tpw = ((tpw + kStreamWaves - 1) / kStreamWaves) * kStreamWaves;
     if (tpw < kStreamWaves) tpw = kStreamWaves;
     const int64_t wgs_per_q = (ntiles + tpw - 1) / tpw;
-    hipLaunchKernelGGL(index_stream_kernel<false>, dim3((unsigned)(wgs_per_q * nq)), dim3(kStreamThreads), 0, s,
-                       q_idx, w, k_idx, N, q_per_seq, n_visible, (const int32_t*)nullptr, 0, scores, bs,
-                       (int32_t*)nullptr, N, ntiles, (int32_t)wgs_per_q, (int32_t)tpw);
+    const dim3 grid((unsigned)(wgs_per_q * nq));
+    if (kfp4)
+        hipLaunchKernelGGL((index_stream_kernel<false, true>), grid, dim3(kStreamThreads), 0, s, q_idx, w, k, N,
+                           q_per_seq, n_visible, (const int32_t*)nullptr, 0, scores, bs, (int32_t*)nullptr, N, ntiles,
+                           (int32_t)wgs_per_q, (int32_t)tpw);
+    else
+        hipLaunchKernelGGL((index_stream_kernel<false, false>), grid, dim3(kStreamThreads), 0, s, q_idx, w, k, N,
+                           q_per_seq, n_visible, (const int32_t*)nullptr, 0, scores, bs, (int32_t*)nullptr, N, ntiles,
+                           (int32_t)wgs_per_q, (int32_t)tpw);
     return 0;
 }
 
-int launch_index_reindex(const uint16_t* q_idx, const float* w, const uint16_t* k_idx, int64_t N, int32_t nq,
+int launch_index_reindex(const uint16_t* q_idx, const float* w, const void* k, bool kfp4, int64_t N, int32_t nq,
                          int32_t q_per_seq, const int32_t* n_visible, const int32_t* cand_blocks, int32_t nb,
                          float* pool_scores, int32_t* pool_ids, hipStream_t s) {
     if (nq == 0) return 0;
@@ -306,9 +407,15 @@ int launch_index_reindex(const uint16_t* q_idx, const float* w, const uint16_t* 
     tpw = ((tpw + kStreamWaves - 1) / kStreamWaves) * kStreamWaves;
     if (tpw < kStreamWaves) tpw = kStreamWaves;
     const int64_t wgs_per_q = (ntiles + tpw - 1) / tpw;
-    hipLaunchKernelGGL(index_stream_kernel<true>, dim3((unsigned)(wgs_per_q * nq)), dim3(kStreamThreads), 0, s,
-                       q_idx, w, k_idx, N, q_per_seq, n_visible, cand_blocks, nb, pool_scores, (float*)nullptr,
-                       pool_ids, ncols, ntiles, (int32_t)wgs_per_q, (int32_t)tpw);
+    const dim3 grid((unsigned)(wgs_per_q * nq));
+    if (kfp4)
+        hipLaunchKernelGGL((index_stream_kernel<true, true>), grid, dim3(kStreamThreads), 0, s, q_idx, w, k, N,
+                           q_per_seq, n_visible, cand_blocks, nb, pool_scores, (float*)nullptr, pool_ids, ncols,
+                           ntiles, (int32_t)wgs_per_q, (int32_t)tpw);
+    else
+        hipLaunchKernelGGL((index_stream_kernel<true, false>), grid, dim3(kStreamThreads), 0, s, q_idx, w, k, N,
+                           q_per_seq, n_visible, cand_blocks, nb, pool_scores, (float*)nullptr, pool_ids, ncols,
+                           ntiles, (int32_t)wgs_per_q, (int32_t)tpw);
     return 0;
 }
 

@@ -11,10 +11,14 @@ namespace csa2 {
 int launch_fp4_pack(const uint16_t* x, int64_t n, uint8_t* out, hipStream_t s);
 int launch_fp4_unpack(const uint8_t* in, int64_t n, uint16_t* y, hipStream_t s);
 
-int launch_index_full(const uint16_t* q_idx, const float* w, const uint16_t* k_idx, int64_t N, int32_t nq,
+int launch_kidx_fp4_pack(const uint16_t* x, int64_t n, uint8_t* out, hipStream_t s);
+
+// Indexer scoring; k is bf16 [nseq][N][128] (kfp4 false) or FP4 entries
+// [nseq][N][68] (kfp4 true).
+int launch_index_full(const uint16_t* q_idx, const float* w, const void* k, bool kfp4, int64_t N, int32_t nq,
                       int32_t q_per_seq, const int32_t* n_visible, float* scores, int32_t block_size,
                       float* block_scores, hipStream_t s);
-int launch_index_reindex(const uint16_t* q_idx, const float* w, const uint16_t* k_idx, int64_t N, int32_t nq,
+int launch_index_reindex(const uint16_t* q_idx, const float* w, const void* k, bool kfp4, int64_t N, int32_t nq,
                          int32_t q_per_seq, const int32_t* n_visible, const int32_t* cand_blocks, int32_t nb,
                          float* pool_scores, int32_t* pool_ids, hipStream_t s);
 

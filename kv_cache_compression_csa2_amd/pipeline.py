@@ -41,13 +41,20 @@ class Step:
                               L.csa2_topk_workspace_bytes(nq, pool, TOPK) if wl.hier else 0))
         self.ws_attn = ws(L.csa2_sparse_attn_workspace_bytes(nq, TOPK))
 
-    def index_full(self, k_idx):
+    @staticmethod
+    def _k(k):
+        """(k_idx, k_fp4) keyword pair for an indexer-K operand: bf16 keys or
+        FP4 entries (uint8 [.., 68])."""
+        return (None, k) if k.dtype == torch.uint8 else (k, None)
+
+    def index_full(self, k):
         wl = self.wl
+        kb, kf = self._k(k)
         if wl.hier:
-            L.csa2_index_full(wl.q_idx[0], wl.w[0], k_idx, wl.N, wl.q_per_seq, wl.n_visible, 8, self.scores,
-                              self.blocks)
+            L.csa2_index_full(wl.q_idx[0], wl.w[0], kb, wl.N, wl.q_per_seq, wl.n_visible, 8, self.scores,
+                              self.blocks, k_fp4=kf)
         else:
-            L.csa2_index_full(wl.q_idx[0], wl.w[0], k_idx, wl.N, wl.q_per_seq, wl.n_visible, 0, self.scores)
+            L.csa2_index_full(wl.q_idx[0], wl.w[0], kb, wl.N, wl.q_per_seq, wl.n_visible, 0, self.scores, k_fp4=kf)
 
     def topk_full(self):
         wl = self.wl
@@ -55,10 +62,11 @@ class Step:
         if wl.hier:
             L.csa2_topk(self.blocks, POOL_BLOCKS, out=self.cand, workspace=self.ws_topk)
 
-    def reindex(self, layer, k_idx):
+    def reindex(self, layer, k):
         wl = self.wl
-        L.csa2_index_reindex(wl.q_idx[layer], wl.w[layer], k_idx, wl.N, wl.q_per_seq, self.cand, wl.n_visible,
-                             pool_scores=self.pool_scores, pool_ids=self.pool_ids)
+        kb, kf = self._k(k)
+        L.csa2_index_reindex(wl.q_idx[layer], wl.w[layer], kb, wl.N, wl.q_per_seq, self.cand, wl.n_visible,
+                             pool_scores=self.pool_scores, pool_ids=self.pool_ids, k_fp4=kf)
         L.csa2_topk(self.pool_scores, TOPK, id_map=self.pool_ids, out=self.top[layer], workspace=self.ws_topk)
 
     def attend(self, layer, kv, idx):
@@ -95,6 +103,14 @@ class Step:
             with sp("attn"):
                 self.attend(layer, kv, self.top[src])
         return self.out
+
+
+def workload_kidx(wl):
+    """The indexer-K operand a workload's step reads: the bf16 keys, or their
+    FP4 entries packed on the GPU (kidx_fp4_pack) for kfmt == "fp4"."""
+    if wl.kfmt != "fp4":
+        return wl.k_idx
+    return L.kidx_fp4_pack(wl.k_idx.reshape(-1, L.IDX_DIM)).view(wl.nseq, wl.N, L.KIDX_RECORD)
 
 
 def pack_workload_kv(wl, device):

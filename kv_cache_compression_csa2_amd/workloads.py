@@ -21,6 +21,12 @@ m=1 decoder compression -- eogee.com report 3.2-3.4, nxbn.cn walkthrough 3.3):
   decode1m     8 queries, 1048576 entries (m=1), clustered keys (16 centroids,
                sigma 0.3); Full + 3 Reindex + 1 Reuse.
 
+With the pages' storage precision for the indexer K (FP4, 68 B per entry),
+packed from the same bf16 keys on the GPU before timing:
+
+  encoder64k_fp4k    the 64K shapes.
+  decode1m_fp4k      the 1M shapes, Full + 3 Reindex + 1 Reuse.
+
 Layer groups that share one cache (eogee.com report 3.2: an encoder cache
 serves a Full layer and the Reuse layers after it; a decoder cache serves a
 Reindex layer and Reuse layers), timed as layer sequences:
@@ -55,6 +61,10 @@ CONFIGS = {
                              planted=8, prefill=False, group="encoder"),
     "decoder_group256k": dict(nq=32, N=262144, q_per_seq=1, hier=True, seed=6, kv="random", kidx="normal",
                               planted=0, prefill=False, group="decoder"),
+    "encoder64k_fp4k": dict(nq=64, N=32768, q_per_seq=1, hier=False, seed=7, kv="random", kidx="normal",
+                            planted=8, prefill=False, kfmt="fp4"),
+    "decode1m_fp4k": dict(nq=8, N=1048576, q_per_seq=1, hier=True, seed=8, kv="clustered", kidx="clustered",
+                          planted=0, prefill=False, kfmt="fp4"),
 }
 
 # Norm given to a planted main-KV row before packing: about twice the RMS norm
@@ -99,6 +109,7 @@ class Workload:
     hier: bool
     swa_T: int
     group: str = None  # None, "encoder" (Full + 5 Reuse) or "decoder" (Reindex + 3 Reuse)
+    kfmt: str = "bf16"  # indexer-K cache precision the step reads: "bf16" or "fp4" (68 B entries)
     q_idx: list = field(default_factory=list)  # per indexer layer: bf16 [nq,32,128]
     w: list = field(default_factory=list)  # per indexer layer: f32 [nq,32]
     k_idx: torch.Tensor = None  # bf16 [nseq,N,128]
@@ -170,7 +181,7 @@ def make_workload(name, device="cpu", seed=None, nq=None, N=None):
     q_per_seq = nq if c["prefill"] else c["q_per_seq"]
     nseq = nq // q_per_seq
     swa_T = (nq + WINDOW - 1) if c["prefill"] else WINDOW
-    wl = Workload(name, nq, N, q_per_seq, nseq, c["hier"], swa_T, c.get("group"))
+    wl = Workload(name, nq, N, q_per_seq, nseq, c["hier"], swa_T, c.get("group"), c.get("kfmt", "bf16"))
     s = 0
 
     def nxt():

@@ -22,7 +22,8 @@ def test_header_declares_the_boundary():
     names = _declared()
     for n in ["fp4_kv_pack", "fp4_kv_unpack", "csa2_index_full", "csa2_index_reindex", "csa2_topk",
               "csa2_topk_workspace_bytes", "csa2_sparse_attn", "csa2_sparse_attn_workspace_bytes",
-              "csa2_format_version", "csa2_last_error"]:
+              "csa2_format_version", "csa2_last_error", "kidx_fp4_pack", "csa2_index_full_fp4k",
+              "csa2_index_reindex_fp4k"]:
         assert n in names
     assert sorted(L.EXPORTS) == names
 
@@ -67,6 +68,27 @@ def test_index_full_rejects(kw, frag):
     rc, msg = _err(K.load().csa2_index_full(a["q"], a["w"], a["k"], a["N"], a["nq"], a["q_per_seq"], a["nv"],
                                             a["scores"], a["block_size"], a["block"], S))
     assert rc == L.CSA2_EINVAL and frag in msg, msg
+
+
+@pytest.mark.parametrize("kw,frag", [
+    (dict(N=0), "N must be"),
+    (dict(q_per_seq=4), "divide"),
+    (dict(block_size=8, block=None), "block_scores"),
+    (dict(k=None), "null pointer"),
+])
+def test_index_fp4k_rejects(kw, frag):
+    a = dict(q=P, w=P, k=P, N=100, nq=6, q_per_seq=1, scores=P, block_size=0, block=P)
+    a.update(kw)
+    L_ = K.load()
+    rc, msg = _err(L_.csa2_index_full_fp4k(a["q"], a["w"], a["k"], a["N"], a["nq"], a["q_per_seq"], None,
+                                          a["scores"], a["block_size"], a["block"], S))
+    assert rc == L.CSA2_EINVAL and frag in msg and "fp4k" in msg, msg
+    rc, msg = _err(L_.csa2_index_reindex_fp4k(a["q"], a["w"], a["k"], a["N"], a["nq"], a["q_per_seq"], None, P, 4,
+                                             8, P, None, S))
+    if kw.get("block_size") is None:
+        assert rc == L.CSA2_EINVAL and frag in msg, msg
+    rc, msg = _err(L_.kidx_fp4_pack(None, 3, P, S))
+    assert rc == L.CSA2_EINVAL and "null" in msg
 
 
 @pytest.mark.parametrize("kw,frag", [

@@ -10,7 +10,10 @@ Protocol per workload:
   4. attention of every layer: GPU attention on the oracle's indices within
      1e-2 * max|ref| of the oracle's.
 Samples: every query of the tiny and 64K workloads, the queries of 2
-sequences at 256K and 1M, 64 strided queries of the prefill chunk.
+sequences at 256K and 1M, 64 strided queries of the prefill chunk. The FP4
+indexer-K workloads also check the GPU's packed entries of the sampled
+sequences against the oracle's packing byte for byte, and score with the
+oracle's own entries.
 """
 import math
 
@@ -27,11 +30,11 @@ SCALE = 1.0 / math.sqrt(512.0)
 
 
 def _sample(wl):
-    if wl.name in ("tiny", "encoder64k", "encoder_group64k"):
+    if wl.name in ("tiny", "encoder64k", "encoder_group64k", "encoder64k_fp4k"):
         return list(range(wl.nq))
     if wl.name == "prefill128k":
         return list(range(0, wl.nq, wl.nq // 64))
-    return [0, wl.nq - 1] if wl.name == "decode1m" else [0, 17]
+    return [0, wl.nq - 1] if wl.name in ("decode1m", "decode1m_fp4k") else [0, 17]
 
 
 def _overlap(a, b):
@@ -78,17 +81,19 @@ def _kv_for(qsub_seq, kvrows, N):
 
 
 @pytest.mark.parametrize("name", ["tiny", "encoder64k", "decoder256k", "prefill128k", "decode1m",
-                                  "encoder_group64k", "decoder_group256k"])
+                                  "encoder_group64k", "decoder_group256k", "encoder64k_fp4k", "decode1m_fp4k"])
 def test_workload_parity(name):
     import kv_cache_compression_csa2_amd as K
-    from kv_cache_compression_csa2_amd.pipeline import Step, pack_workload_kv
+    from kv_cache_compression_csa2_amd.pipeline import Step, pack_workload_kv, workload_kidx
     from kv_cache_compression_csa2_amd.workloads import make_workload
     print("case: workload", name, flush=True)
     wl = make_workload(name, device=DEV)
     kv = pack_workload_kv(wl, DEV)
+    kk = workload_kidx(wl)
+    fp4k = wl.kfmt == "fp4"
     step = Step(wl, DEV)
-    step.prepare(wl.k_idx)
-    step.run(wl.k_idx, kv)
+    step.prepare(kk)
+    step.run(kk, kv)
     torch.cuda.synchronize()
     print("  gpu step done", flush=True)
 
@@ -98,12 +103,21 @@ def test_workload_parity(name):
     seqs = sorted(set(q // wl.q_per_seq for q in Qs))
     # oracle view: the sampled queries over the sampled sequences
     qps_sub = len(Qs) if prefill else 1
-    k_sub = u16(wl.k_idx[torch.tensor(seqs, device=DEV, dtype=torch.long)])
+    seq_t = torch.tensor(seqs, device=DEV, dtype=torch.long)
+    k_sub = u16(wl.k_idx[seq_t])
     nv = np_(wl.n_visible[qt]) if wl.n_visible is not None else None
+    kf_sub = None
+    if fp4k:
+        # the oracle packs the sampled sequences' keys itself; the GPU packer
+        # must agree byte for byte
+        kf_sub = O.kidx_fp4_pack(k_sub).reshape(len(seqs), wl.N, O.KIDX_RECORD_BYTES)
+        assert np.array_equal(np_(kk[seq_t]), kf_sub)
+        print("  indexer-K FP4 entries bit-exact", flush=True)
 
     # 1. Full-layer scores
     bs = 8 if wl.hier else 0
-    r = O.index_full(u16(wl.q_idx[0][qt]), np_(wl.w[0][qt]), k_sub, wl.N, qps_sub, n_visible=nv, block_size=bs)
+    r = O.index_full(u16(wl.q_idx[0][qt]), np_(wl.w[0][qt]), k_sub, wl.N, qps_sub, n_visible=nv, block_size=bs,
+                     k_fp4=kf_sub)
     rs, rb = (r if wl.hier else (r, None))
     ok, msg = rel_close(np_(step.scores[qt]), rs)
     assert ok, "scores: " + msg
@@ -138,10 +152,11 @@ def test_workload_parity(name):
         assert all(set(top_o[j].tolist()) <= set(pool[j].tolist()) for j in range(len(Qs)))
         for layer in wl.reindex_layers:
             ps_o = O.index_reindex(u16(wl.q_idx[layer][qt]), np_(wl.w[layer][qt]), k_sub, wl.N, 1, pool,
-                                   n_visible=nv)
+                                   n_visible=nv, k_fp4=kf_sub)
+            kg = kk[seq_t].contiguous()
             ps_g, pid_g = K.csa2_index_reindex(wl.q_idx[layer][qt].contiguous(), wl.w[layer][qt].contiguous(),
-                                               wl.k_idx[torch.tensor(seqs, device=DEV, dtype=torch.long)], wl.N, 1,
-                                               dev_i32(cand_o, DEV))
+                                               None if fp4k else kg, wl.N, 1, dev_i32(cand_o, DEV),
+                                               k_fp4=kg if fp4k else None)
             torch.cuda.synchronize()
             ok, msg = rel_close(np_(ps_g), ps_o)
             assert ok, "reindex %d: %s" % (layer, msg)

@@ -102,6 +102,73 @@ def test_pack_empty():
     torch.cuda.synchronize()
 
 
+# ------------------------------------------------------ FP4 indexer K
+
+def test_kidx_pack_bit_exact():
+    print("case: kidx pack", flush=True)
+    x = _bf16((5000, 128), 11) * torch.exp2(torch.randint(-30, 20, (5000, 1), generator=_g(12), device=DEV)).to(
+        torch.bfloat16)
+    x[0] = 0
+    x[1, :] = -0.0
+    x[2, :64] = 1e-35
+    # exact ties: amax 6 * 2^e so the scale is 2^e, the rest on the grid midpoints
+    rng = np.random.default_rng(13)
+    e = torch.tensor(np.exp2(rng.integers(-20, 20, (100, 1))).astype(np.float32))
+    mids = torch.tensor([0.25, 0.75, 1.25, 1.75, 2.5, 3.5, 5.0, 6.0])
+    v = mids[torch.tensor(rng.integers(0, 8, (100, 128)))] * torch.tensor(
+        rng.choice([-1.0, 1.0], (100, 128)).astype(np.float32)) * e
+    v[:, 0] = 6.0 * e[:, 0]
+    x[100:200] = v.to(torch.bfloat16).to(DEV)
+    x = x.contiguous()
+    rec = K().kidx_fp4_pack(x)
+    torch.cuda.synchronize()
+    assert np.array_equal(np_(rec), O.kidx_fp4_pack(u16(x)))
+    out = torch.empty((0, 68), dtype=torch.uint8, device=DEV)
+    K().kidx_fp4_pack(torch.empty((0, 128), dtype=torch.bfloat16, device=DEV), out=out)  # n == 0
+    torch.cuda.synchronize()
+
+
+@pytest.mark.parametrize("nq,N,qps", [(1, 1024, 1), (3, 1000, 1), (5, 77, 1), (2, 40000, 1), (4, 1, 1),
+                                      (16, 5003, 16), (24, 4096 * 2 + 100, 8)])
+def test_index_full_fp4k_matches_oracle(nq, N, qps):
+    """Scores over FP4 indexer-K entries packed by the oracle; the decode
+    kernel (one sequence per query) and the prefill kernel (8 | q_per_seq)."""
+    print("case: index_full_fp4k", nq, N, qps, flush=True)
+    q, w, k = _idx_inputs(nq, N, nq // qps, 20 + N)
+    kf_host = O.kidx_fp4_pack(u16(k)).reshape(nq // qps, N, 68)
+    kf = torch.tensor(kf_host, device=DEV)
+    rng = np.random.default_rng(N + 1)
+    nv = rng.integers(0, N + 1, nq).astype(np.int32)
+    nv[0] = N
+    s, b = K().csa2_index_full(q, w, None, N, qps, n_visible=dev_i32(nv, DEV), block_size=8, k_fp4=kf)
+    torch.cuda.synchronize()
+    rs, rb = O.index_full(u16(q), np_(w), None, N, qps, n_visible=nv, block_size=8, k_fp4=kf_host)
+    ok, msg = rel_close(np_(s), rs)
+    assert ok, msg
+    ok, msg = rel_close(np_(b), rb)
+    assert ok, msg
+
+
+def test_index_reindex_fp4k_matches_oracle():
+    print("case: reindex fp4k", flush=True)
+    nq, N, nb = 3, 9000, 300
+    q, w, k = _idx_inputs(nq, N, nq, 78)
+    kf_host = O.kidx_fp4_pack(u16(k)).reshape(nq, N, 68)
+    kf = torch.tensor(kf_host, device=DEV)
+    rng = np.random.default_rng(8)
+    blocks = np.sort(np.stack([rng.choice((N + 7) // 8, nb, replace=False) for _ in range(nq)]), 1).astype(np.int32)
+    blocks[1, -5:] = -1
+    nv = np.array([N, 5000, 8999], np.int32)
+    ps, pid = K().csa2_index_reindex(q, w, None, N, 1, dev_i32(blocks, DEV), n_visible=dev_i32(nv, DEV), k_fp4=kf)
+    torch.cuda.synchronize()
+    pool = O.pool_ids(blocks, 8)
+    pool_vis = np.where((pool >= 0) & (pool < nv[:, None]), pool, -1)
+    ref = O.index_reindex(u16(q), np_(w), None, N, 1, pool, n_visible=nv, k_fp4=kf_host)
+    ok, msg = rel_close(np_(ps), ref)
+    assert ok, msg
+    assert np.array_equal(np_(pid), pool_vis)
+
+
 # ------------------------------------------------------------------ indexer
 
 def _idx_inputs(nq, N, nseq, seed):
