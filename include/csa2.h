@@ -195,6 +195,10 @@ int csa2_topk(const float* scores, int32_t rows, int64_t ncols, int64_t ld, cons
  *           buffer; 0 <= swa_len <= 128 and the range must lie inside [0, T).
  *           Both may be NULL (no window keys).
  *   softmax_scale: multiplies q.k before the softmax (1/sqrt(512)).
+ *           The products run in fp16 with fp32 accumulation: decoded FP4 values
+ *           are exact in fp16, and q and swa values must lie below 65504 in
+ *           magnitude (bf16 values of 2^-14 or more convert exactly; smaller
+ *           ones to within 2^-25).
  *   out     [nq][64][512] bf16 out: softmax over all of the query's keys jointly.
  *   lse     [nq][64] fp32 out or NULL: natural-log sum of exp of the scaled logits.
  *           A query with no keys gets out = 0 and lse = -inf.

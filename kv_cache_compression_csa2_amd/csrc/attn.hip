@@ -7,11 +7,14 @@
 // Workgroup = one query (all 64 heads) x a run of 32-key tiles; 4 waves, wave w
 // owns heads 16w..16w+15. Per tile:
 //   1. the workgroup gathers 32 keys (288-byte records, or bf16 window rows),
-//      decodes E2M1 x E4M3 to bf16 (exact) and stores the tile once in LDS,
-//      key-major. The decode uses the gfx950 scaled FP4 conversion with the
-//      scale's power of two, then one multiply by the scale's significand;
-//   2. each wave computes S^T = K . Q^T (16x16x32 bf16 MFMA, its Q slice held
-//      in registers) and runs the online softmax in the exp2 domain;
+//      decodes E2M1 x E4M3 to fp16 (exact: a product of a 2-bit and a 4-bit
+//      significand, between 2^-10 and 2688 in magnitude) and stores the tile
+//      once in LDS, key-major. The decode is the gfx950 scaled FP4->fp16
+//      conversion with the scale's power of two, then one packed fp16 multiply
+//      by the scale's significand; window rows are converted bf16 -> fp16;
+//   2. each wave computes S^T = K . Q^T (16x16x32 fp16 MFMA, its Q slice held
+//      in registers, converted from bf16) and runs the online softmax in the
+//      exp2 domain;
 //   3. O^T += V^T . P^T: V^T comes from the same key-major tile through the LDS
 //      transpose read, P^T straight from the S^T accumulator registers.
 // LDS is double-buffered (one barrier per tile) and the next tile's records are
@@ -26,8 +29,14 @@
 // contraction index: Q is loaded in the same dim order, and O is written back
 // in logical order.
 //
+// fp16 holds every bf16 value of magnitude 2^-14 .. 65504 exactly (smaller
+// ones to within 2^-25), so Q and the window rows must stay below 65504 in
+// magnitude. P is rounded to fp16 (its values are <= 2^8) and the softmax
+// denominator sums the rounded values.
+//
 // The running max is refreshed only when it grows by more than 2^8, so the
-// 128-register O^T rescale is rare; exp2 arguments stay <= 8.
+// 128-register O^T rescale is rare; exp2 arguments stay <= 8. It starts at a
+// finite floor (-2^126), so masked keys (logit -inf) need no special case.
 // Few queries cannot fill the GPU, so a query's tiles may be split across
 // workgroups that write partial (O, max, sum) to the workspace; a second
 // kernel merges them.
@@ -46,39 +55,76 @@ constexpr int kTileB = kTile * kRowB;     // 33,280 bytes
 constexpr int kAttThreads = 256;
 constexpr float kRescaleSlack = 8.0f;     // log2 units
 
-typedef float f32x2 __attribute__((ext_vector_type(2)));
 typedef short i16x4 __attribute__((ext_vector_type(4)));
 typedef __attribute__((address_space(3))) i16x4 lds_i16x4;
+typedef _Float16 f16x2 __attribute__((ext_vector_type(2)));
+typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
+typedef float f32x2 __attribute__((ext_vector_type(2)));
+
+constexpr float kMaxFloor = -8.507059e37f;  // -2^126: running-max floor
 
 CSA2_DEVINL int unit_logical(int u) { return 4 * (u & 15) + (u >> 4); }
 CSA2_DEVINL int perm16(int i) { return ((2 * i) & 15) + (i >> 3); }
+// i with perm16(i) == r
+CSA2_DEVINL int perm16_inv(int r) { return (r >> 1) + 8 * (r & 1); }
 
-// Two FP4 channels (byte SEL of w) times the scale -> packed bf16 pair. The
-// conversion applies only the scale's exponent (a power of two); `mant` is the
-// scale divided by that power of two. Both products are exact.
-template <int SEL>
-CSA2_DEVINL uint32_t deq_pair(uint32_t w, float pow2, float mant) {
-    const f32x2 v = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(w, pow2, SEL);
-    return __builtin_amdgcn_perm(__float_as_uint(v[1] * mant), __float_as_uint(v[0] * mant), 0x07060302u);
+// 16x16x32 fp16 MFMA, same operand layout as the bf16 one.
+CSA2_DEVINL f32x4 mfma16x16x32h(f16x8 a, f16x8 b, f32x4 c) {
+    return __builtin_amdgcn_mfma_f32_16x16x32_f16(a, b, c, 0, 0, 0);
 }
 
-CSA2_DEVINL uint4 deq_unit(uint32_t w, float pow2, float mant) {
+// Two FP4 channels (byte SEL of w) times the scale -> packed fp16 pair. The
+// conversion applies only the scale's exponent (a power of two); `mant` holds
+// the scale divided by that power of two twice. Both products are exact.
+template <int SEL>
+CSA2_DEVINL uint32_t deq_pair(uint32_t w, float pow2, f16x2 mant) {
+    const f16x2 v = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(w, pow2, SEL);
+    return __builtin_bit_cast(uint32_t, v * mant);
+}
+
+CSA2_DEVINL uint4 deq_unit(uint32_t w, float pow2, f16x2 mant) {
     return make_uint4(deq_pair<0>(w, pow2, mant), deq_pair<1>(w, pow2, mant), deq_pair<2>(w, pow2, mant),
                       deq_pair<3>(w, pow2, mant));
 }
 
 template <int SEL>
-CSA2_DEVINL void split_scale(uint32_t sbytes, float& pow2, float& mant) {
+CSA2_DEVINL void split_scale(uint32_t sbytes, float& pow2, f16x2& mant) {
     const float S = __builtin_amdgcn_cvt_f32_fp8((int)sbytes, SEL);  // OCP E4M3 -> f32, exact
     const uint32_t b = __float_as_uint(S);
     pow2 = __uint_as_float(b & 0x7F800000u);
-    mant = (S == 0.0f) ? S : __uint_as_float((b & 0x807FFFFFu) | 0x3F800000u);
+    const _Float16 m = (_Float16)((S == 0.0f) ? S : __uint_as_float((b & 0x807FFFFFu) | 0x3F800000u));
+    mant = f16x2{m, m};
 }
 
-CSA2_DEVINL bf16x8 as_bf16x8_2(i16x4 lo, i16x4 hi) {
+// Two bf16 (one dword) -> two fp16 (one dword), round to nearest even.
+CSA2_DEVINL uint32_t bf16x2_to_f16x2(uint32_t v) {
+    const f32x2 f = {__uint_as_float(v << 16), __uint_as_float(v & 0xFFFF0000u)};
+    return __builtin_bit_cast(uint32_t, __builtin_convertvector(f, f16x2));
+}
+CSA2_DEVINL uint4 bf16x8_to_f16x8(uint4 v) {
+    return make_uint4(bf16x2_to_f16x2(v.x), bf16x2_to_f16x2(v.y), bf16x2_to_f16x2(v.z), bf16x2_to_f16x2(v.w));
+}
+CSA2_DEVINL f16x8 as_f16x8(uint4 v) { return __builtin_bit_cast(f16x8, v); }
+
+CSA2_DEVINL f16x8 as_f16x8_2(i16x4 lo, i16x4 hi) {
     typedef short i16x8 __attribute__((ext_vector_type(8)));
     const i16x8 v = __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
-    return __builtin_bit_cast(bf16x8, v);
+    return __builtin_bit_cast(f16x8, v);
+}
+
+// Max / sum over the four lanes l, l^16, l^32, l^48 (one head's four key
+// groups) with the gfx950 row and half-wave swaps, no LDS round trip.
+CSA2_DEVINL float max_over_groups(float v) {
+    const auto a = __builtin_amdgcn_permlane16_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+    v = fmaxf(__uint_as_float(a[0]), __uint_as_float(a[1]));
+    const auto b = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+    return fmaxf(__uint_as_float(b[0]), __uint_as_float(b[1]));
+}
+CSA2_DEVINL float sum_over_groups(float v) {
+    const auto a = __builtin_amdgcn_permlane16_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+    v = __uint_as_float(a[0]) + __uint_as_float(a[1]);
+    const auto b = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+    return __uint_as_float(b[0]) + __uint_as_float(b[1]);
 }
 
 }  // namespace
@@ -105,16 +151,26 @@ namespace {
 struct RawRec {
     uint4 codes[2];   // 16 code bytes of each of the thread's two rows
     uint32_t sc[2];   // 2 scale bytes of each row
+    int32_t id[2];    // the rows' entry ids (-1: empty slot)
 };
+
+// Tiles of split `s` of `nsplit`: main tiles [M*s/nsplit, M*(s+1)/nsplit) and
+// window tiles [W*s/nsplit, W*(s+1)/nsplit), so window tiles (whose rows are
+// loaded without prefetch) spread over the splits.
+CSA2_DEVINL int part_lo(int n, int s, int nsplit) { return (int)(((int64_t)n * s) / nsplit); }
 
 __global__ __launch_bounds__(kAttThreads, 2) void sparse_attn_kernel(
     const uint16_t* __restrict__ q, const uint8_t* __restrict__ kv, int64_t N, int32_t q_per_seq,
     const int32_t* __restrict__ idx, int32_t k, const uint16_t* __restrict__ swa, int64_t T,
     const int32_t* __restrict__ swa_start, const int32_t* __restrict__ swa_len, float scale_log2,
     uint16_t* __restrict__ out, float* __restrict__ lse, float* __restrict__ part_o, float* __restrict__ part_ml,
-    int32_t nsplit, int32_t tiles_per_split) {
+    int32_t nsplit) {
     __shared__ __attribute__((aligned(16))) uint8_t lds[2 * kTileB];
-    __shared__ uint32_t key_ok[2][kTile];
+    // 0 or -inf per key, stored at perm16_inv(row) (+16 for the second half)
+    // so that a lane's four keys of a half-tile are one 16-byte read
+    __shared__ __attribute__((aligned(16))) float key_bias[2][kTile];
+    // entry ids of this workgroup's main tiles, range-checked (-1: empty)
+    extern __shared__ int32_t sid[];
 
     const int64_t qi = blockIdx.x / nsplit;
     const int split = blockIdx.x % nsplit;
@@ -122,60 +178,64 @@ __global__ __launch_bounds__(kAttThreads, 2) void sparse_attn_kernel(
     const int j = lane & 15, G = lane >> 4;
     const int head = wave * 16 + j;
     const int64_t seq = qi / q_per_seq;
-    const int main_tiles = (k + kTile - 1) / kTile;
+    const int M = N > 0 ? (k + kTile - 1) / kTile : 0;
+    constexpr int W = kMaxWindow / kTile;
     const int slen = (swa && swa_len) ? swa_len[qi] : 0;
     const int sst = (swa && swa_start) ? swa_start[qi] : 0;
-    const int total_tiles = main_tiles + kMaxWindow / kTile;
-    const int t_begin = split * tiles_per_split;
-    int t_end = t_begin + tiles_per_split;
-    t_end = t_end < total_tiles ? t_end : total_tiles;
+    const int m0 = part_lo(M, split, nsplit), nmain = part_lo(M, split + 1, nsplit) - m0;
+    const int w0 = part_lo(W, split, nsplit), w1 = part_lo(W, split + 1, nsplit);
+    // window tiles past the query's window length hold no keys
+    const int wlive = (slen + kTile - 1) / kTile;
+    const int nwin = (w1 < wlive ? w1 : wlive) - w0;
+    const int ntiles = nmain + (nwin > 0 ? nwin : 0);
 
     f32x4 o[32];
 #pragma unroll
     for (int m = 0; m < 32; m++) o[m] = f32x4{0.f, 0.f, 0.f, 0.f};
-    float m_run = -INFINITY, l_run = 0.0f;
+    float m_run = kMaxFloor, l_run = 0.0f;
 
     const uint8_t* kv_seq = kv + seq * N * kRecord;
     const uint16_t* swa_seq = swa ? swa + seq * T * kDim : nullptr;
-    const int32_t* idx_q = idx + qi * (int64_t)k;
+    const int32_t* idx_q = idx + qi * (int64_t)k + (int64_t)m0 * kTile;
+
+    // the workgroup's entry ids, checked once
+    for (int i = tid; i < nmain * kTile; i += kAttThreads) {
+        const int32_t v = (m0 * kTile + i < k) ? idx_q[i] : -1;
+        sid[i] = (v >= 0 && v < N) ? v : -1;
+    }
+    lds_barrier();
 
     // gather role: rows r0 and r0 + 16 of a tile, 32-dim chunk c
     const int r0 = tid >> 4, c = tid & 15;
 
-    auto row_ids = [&](int t, int32_t* id) {
+    // Branch-free loads (an empty slot reads entry 0 and is zeroed at decode),
+    // so nothing between the loads and their use makes the wave wait for them.
+    auto load_raw = [&](int lt, RawRec& rw) {
 #pragma unroll
         for (int h = 0; h < 2; h++) {
-            const int slot = t * kTile + r0 + 16 * h;
-            int32_t v = slot < k ? idx_q[slot] : -1;
-            id[h] = (v >= 0 && v < N) ? v : -1;
+            const int32_t id = sid[lt * kTile + r0 + 16 * h];
+            const uint8_t* rec = kv_seq + (int64_t)(id > 0 ? id : 0) * kRecord;
+            rw.codes[h] = *reinterpret_cast<const uint4*>(rec + 16 * c);
+            rw.sc[h] = *reinterpret_cast<const uint16_t*>(rec + kCodeBytes + 2 * c);
+            rw.id[h] = id;
         }
     };
-    auto load_raw = [&](const int32_t* id, RawRec& rw) {
-#pragma unroll
-        for (int h = 0; h < 2; h++) {
-            if (id[h] >= 0) {
-                const uint8_t* rec = kv_seq + (int64_t)id[h] * kRecord;
-                rw.codes[h] = *reinterpret_cast<const uint4*>(rec + 16 * c);
-                rw.sc[h] = *reinterpret_cast<const uint16_t*>(rec + kCodeBytes + 2 * c);
-            } else {
-                rw.codes[h] = make_uint4(0u, 0u, 0u, 0u);
-                rw.sc[h] = 0u;
-            }
-        }
-    };
-    auto write_main = [&](int buf, const RawRec& rw, const int32_t* id) {
+    auto write_main = [&](int buf, const RawRec& rw) {
         uint8_t* base = lds + buf * kTileB;
 #pragma unroll
         for (int h = 0; h < 2; h++) {
+            const bool ok = rw.id[h] >= 0;
+            const uint4 cd = ok ? rw.codes[h] : make_uint4(0u, 0u, 0u, 0u);
             uint8_t* row = base + (r0 + 16 * h) * kRowB + 16 * c;
-            float p0, m0, p1, m1;
-            split_scale<0>(rw.sc[h], p0, m0);
-            split_scale<1>(rw.sc[h], p1, m1);
-            *reinterpret_cast<uint4*>(row + 0 * 256) = deq_unit(rw.codes[h].x, p0, m0);
-            *reinterpret_cast<uint4*>(row + 1 * 256) = deq_unit(rw.codes[h].y, p0, m0);
-            *reinterpret_cast<uint4*>(row + 2 * 256) = deq_unit(rw.codes[h].z, p1, m1);
-            *reinterpret_cast<uint4*>(row + 3 * 256) = deq_unit(rw.codes[h].w, p1, m1);
-            if (c == 0) key_ok[buf][r0 + 16 * h] = id[h] >= 0 ? 1u : 0u;
+            float p0, p1;
+            f16x2 m0h, m1h;
+            split_scale<0>(rw.sc[h], p0, m0h);
+            split_scale<1>(rw.sc[h], p1, m1h);
+            *reinterpret_cast<uint4*>(row + 0 * 256) = deq_unit(cd.x, p0, m0h);
+            *reinterpret_cast<uint4*>(row + 1 * 256) = deq_unit(cd.y, p0, m0h);
+            *reinterpret_cast<uint4*>(row + 2 * 256) = deq_unit(cd.z, p1, m1h);
+            *reinterpret_cast<uint4*>(row + 3 * 256) = deq_unit(cd.w, p1, m1h);
+            if (c == 0) key_bias[buf][perm16_inv(r0) + 16 * h] = ok ? 0.0f : -INFINITY;
         }
     };
     auto write_window = [&](int buf, int wbase) {
@@ -188,7 +248,7 @@ __global__ __launch_bounds__(kAttThreads, 2) void sparse_attn_kernel(
             if (ok) {
                 const uint4* src = reinterpret_cast<const uint4*>(swa_seq + (int64_t)(sst + r) * kDim) + 4 * c;
 #pragma unroll
-                for (int jj = 0; jj < 4; jj++) u[jj] = src[jj];
+                for (int jj = 0; jj < 4; jj++) u[jj] = bf16x8_to_f16x8(src[jj]);
             } else {
 #pragma unroll
                 for (int jj = 0; jj < 4; jj++) u[jj] = make_uint4(0u, 0u, 0u, 0u);
@@ -196,88 +256,65 @@ __global__ __launch_bounds__(kAttThreads, 2) void sparse_attn_kernel(
             uint8_t* row = base + (r0 + 16 * h) * kRowB + 16 * c;
 #pragma unroll
             for (int jj = 0; jj < 4; jj++) *reinterpret_cast<uint4*>(row + jj * 256) = u[jj];
-            if (c == 0) key_ok[buf][r0 + 16 * h] = ok ? 1u : 0u;
+            if (c == 0) key_bias[buf][perm16_inv(r0) + 16 * h] = ok ? 0.0f : -INFINITY;
         }
     };
 
-    // Records are loaded two tiles ahead of their decode: slot A holds even
-    // tiles (relative to t_begin), slot B odd ones; their ids are read one tile
-    // earlier still.
-    int32_t id_a[2] = {-1, -1}, id_b[2] = {-1, -1}, id_n[2] = {-1, -1};
-    RawRec raw_a, raw_b;
-    auto prefetchable = [&](int t) { return t < t_end && t < main_tiles; };
-    if (prefetchable(t_begin)) {
-        row_ids(t_begin, id_a);
-        load_raw(id_a, raw_a);
-    }
-    if (prefetchable(t_begin + 1)) {
-        row_ids(t_begin + 1, id_b);
-        load_raw(id_b, raw_b);
-    }
-    if (prefetchable(t_begin + 2)) row_ids(t_begin + 2, id_n);
-    // Q after the index and record loads: memory counters retire in order, so
-    // loads issued first are the ones the first decode can wait for alone.
+    // Records are loaded one tile ahead of their decode: they arrive while the
+    // current tile is computed.
+    RawRec raw;
+    if (nmain > 0) load_raw(0, raw);
+    // Q after the record loads: memory counters retire in order, so loads
+    // issued first are the ones the first decode can wait for alone.
     // Q^T operand of k-step s: head `head`, the logical dims of physical unit 4s + G.
-    bf16x8 qf[16];
+    f16x8 qf[16];
     {
         const uint16_t* qh = q + (qi * kHeads + head) * kDim;
 #pragma unroll
         for (int s = 0; s < 16; s++)
-            qf[s] = as_bf16x8(*reinterpret_cast<const uint4*>(qh + 8 * unit_logical(4 * s + G)));
+            qf[s] = as_f16x8(bf16x8_to_f16x8(*reinterpret_cast<const uint4*>(qh + 8 * unit_logical(4 * s + G))));
     }
 
     const int pr_a = perm16(j), pr_t = perm16(4 * G + (j >> 2));
-    auto tile = [&](int t, RawRec& rw, int32_t (&id)[2]) -> bool {
-        const int buf = (t - t_begin) & 1;
-        const bool is_main = t < main_tiles;
-        const int wbase = (t - main_tiles) * kTile;
-        if (!is_main && wbase >= slen) return false;  // no window keys left (uniform)
-
-        // ---- 1. decode this tile into LDS; refill the slot with tile t + 2 ----
-        if (is_main) {
-            write_main(buf, rw, id);
-            if (prefetchable(t + 2)) {
-                id[0] = id_n[0];
-                id[1] = id_n[1];
-                load_raw(id, rw);
-                if (prefetchable(t + 3)) row_ids(t + 3, id_n);
-            }
+    for (int lt = 0; lt < ntiles; lt++) {
+        const int buf = lt & 1;
+        // ---- 1. decode this tile into LDS; load the next main tile's records ----
+        if (lt < nmain) {
+            write_main(buf, raw);
+            if (lt + 1 < nmain) load_raw(lt + 1, raw);
         } else {
-            write_window(buf, wbase);
+            write_window(buf, (w0 + lt - nmain) * kTile);
         }
         lds_barrier();
 
         const uint8_t* base = lds + buf * kTileB;
         // ---- 2. logits S^T[key][head] for this wave's 16 heads ----
         f32x4 s0 = {0.f, 0.f, 0.f, 0.f}, s1 = {0.f, 0.f, 0.f, 0.f};
+        const f32x4 bias0 = *reinterpret_cast<const f32x4*>(&key_bias[buf][4 * G]);
+        const f32x4 bias1 = *reinterpret_cast<const f32x4*>(&key_bias[buf][16 + 4 * G]);
         {
             const uint8_t* ra = base + pr_a * kRowB + 16 * G;
             const uint8_t* rb = ra + 16 * kRowB;
 #pragma unroll
             for (int s = 0; s < 16; s++) {
-                const bf16x8 a0 = as_bf16x8(*reinterpret_cast<const uint4*>(ra + 64 * s));
-                const bf16x8 a1 = as_bf16x8(*reinterpret_cast<const uint4*>(rb + 64 * s));
-                s0 = mfma16x16x32(a0, qf[s], s0);
-                s1 = mfma16x16x32(a1, qf[s], s1);
+                const f16x8 a0 = as_f16x8(*reinterpret_cast<const uint4*>(ra + 64 * s));
+                const f16x8 a1 = as_f16x8(*reinterpret_cast<const uint4*>(rb + 64 * s));
+                s0 = mfma16x16x32h(a0, qf[s], s0);
+                s1 = mfma16x16x32h(a1, qf[s], s1);
             }
         }
         // lane holds logical keys 4G + r of each half-tile, i.e. LDS rows perm16(4G + r)
         float x[8];
 #pragma unroll
         for (int r = 0; r < 4; r++) {
-            const int row = perm16(4 * G + r);
-            x[r] = key_ok[buf][row] ? s0[r] * scale_log2 : -INFINITY;
-            x[4 + r] = key_ok[buf][16 + row] ? s1[r] * scale_log2 : -INFINITY;
+            x[r] = fmaf(s0[r], scale_log2, bias0[r]);
+            x[4 + r] = fmaf(s1[r], scale_log2, bias1[r]);
         }
-        float tmax = x[0];
-#pragma unroll
-        for (int i = 1; i < 8; i++) tmax = fmaxf(tmax, x[i]);
-        tmax = fmaxf(tmax, __shfl_xor(tmax, 16));
-        tmax = fmaxf(tmax, __shfl_xor(tmax, 32));
+        float tmax = fmaxf(fmaxf(fmaxf(x[0], x[1]), fmaxf(x[2], x[3])), fmaxf(fmaxf(x[4], x[5]), fmaxf(x[6], x[7])));
+        tmax = max_over_groups(tmax);
         const float m_new = fmaxf(m_run, tmax);
-        const bool grow = m_new > m_run + kRescaleSlack || (m_run == -INFINITY && m_new != -INFINITY);
-        if (__any(grow)) {
-            const float corr = (m_run == -INFINITY) ? 0.0f : exp2f(m_run - m_new);
+        if (__any(m_new > m_run + kRescaleSlack)) {
+            const float corr = __builtin_amdgcn_exp2f(m_run - m_new);
             l_run *= corr;
 #pragma unroll
             for (int m = 0; m < 32; m++) o[m] *= corr;
@@ -286,14 +323,13 @@ __global__ __launch_bounds__(kAttThreads, 2) void sparse_attn_kernel(
         uint32_t pk[4];
 #pragma unroll
         for (int i = 0; i < 8; i += 2) {
-            const float p0 = (m_run == -INFINITY) ? 0.0f : exp2f(x[i] - m_run);
-            const float p1 = (m_run == -INFINITY) ? 0.0f : exp2f(x[i + 1] - m_run);
-            // round to bf16 (nearest even); the denominator sums the rounded values
-            const uint32_t b = pack_bf16x2(p0, p1);
-            l_run += bf16_bits_to_float(b & 0xFFFFu) + bf16_bits_to_float(b >> 16);
-            pk[i >> 1] = b;
+            const f32x2 p = {__builtin_amdgcn_exp2f(x[i] - m_run), __builtin_amdgcn_exp2f(x[i + 1] - m_run)};
+            // round to fp16 (nearest even); the denominator sums the rounded values
+            const f16x2 h = __builtin_convertvector(p, f16x2);
+            l_run += (float)h[0] + (float)h[1];
+            pk[i >> 1] = __builtin_bit_cast(uint32_t, h);
         }
-        const bf16x8 pf = as_bf16x8(make_uint4(pk[0], pk[1], pk[2], pk[3]));
+        const f16x8 pf = as_f16x8(make_uint4(pk[0], pk[1], pk[2], pk[3]));
 
         // ---- 3. O^T[dim][head] += V^T[dim][keys] . P^T[keys][head] ----
         {
@@ -303,20 +339,13 @@ __global__ __launch_bounds__(kAttThreads, 2) void sparse_attn_kernel(
             for (int mt = 0; mt < 32; mt++) {
                 const i16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(v0 + 32 * mt));
                 const i16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(v1 + 32 * mt));
-                o[mt] = mfma16x16x32(as_bf16x8_2(lo, hi), pf, o[mt]);
+                o[mt] = mfma16x16x32h(as_f16x8_2(lo, hi), pf, o[mt]);
             }
         }
-        return true;
-    };
-    for (int t = t_begin; t < t_end; t += 2) {
-        if (!tile(t, raw_a, id_a)) break;
-        if (t + 1 >= t_end || !tile(t + 1, raw_b, id_b)) break;
     }
 
     // ---- finish: lanes with the same head (G = 0..3) hold different keys' sums ----
-    float l_tot = l_run;
-    l_tot += __shfl_xor(l_tot, 16);
-    l_tot += __shfl_xor(l_tot, 32);
+    const float l_tot = sum_over_groups(l_run);
     // lane holds O^T[physical dim 16mt + 4G + r][head]: logical dims
     // 8*L(2mt + G/2) + 4*(G%2) + r, four consecutive ones per mt
     if (nsplit == 1) {
@@ -380,8 +409,9 @@ int launch_sparse_attn(const uint16_t* q, const uint8_t* kv, int64_t N, int32_t 
                        hipStream_t s) {
     if (nq == 0) return 0;
     const int ns = attn_splits(nq, k);
-    const int tiles = attn_total_tiles(k);
-    const int per = (tiles + ns - 1) / ns;
+    // dynamic LDS: the largest share of main-tile entry ids a split holds
+    const int mt = N > 0 ? (k + kTile - 1) / kTile : 0;
+    const size_t sid_bytes = (size_t)((mt + ns - 1) / ns) * kTile * sizeof(int32_t);
     float* part_o = nullptr;
     float* part_ml = nullptr;
     if (ns > 1) {
@@ -389,8 +419,8 @@ int launch_sparse_attn(const uint16_t* q, const uint8_t* kv, int64_t N, int32_t 
         part_ml = part_o + (size_t)nq * ns * kHeads * kDim;
     }
     const float scale_log2 = softmax_scale * 1.4426950408889634f;
-    hipLaunchKernelGGL(sparse_attn_kernel, dim3((unsigned)((int64_t)nq * ns)), dim3(kAttThreads), 0, s, q, kv, N,
-                       q_per_seq, idx, k, swa, T, swa_start, swa_len, scale_log2, out, lse, part_o, part_ml, ns, per);
+    hipLaunchKernelGGL(sparse_attn_kernel, dim3((unsigned)((int64_t)nq * ns)), dim3(kAttThreads), sid_bytes, s, q,
+                       kv, N, q_per_seq, idx, k, swa, T, swa_start, swa_len, scale_log2, out, lse, part_o, part_ml, ns);
     if (ns > 1)
         hipLaunchKernelGGL(attn_merge_kernel, dim3((unsigned)((int64_t)nq * kHeads)), dim3(128), 0, s, part_o,
                            part_ml, ns, out, lse);

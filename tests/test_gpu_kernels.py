@@ -342,6 +342,43 @@ def test_sparse_attn_degenerate():
     assert torch.all(out2 == 0) and torch.all(torch.isneginf(lse2))
 
 
+def test_sparse_attn_decode_exact():
+    """A query that attends to one entry outputs that entry's value exactly
+    (softmax weight 1): every decoded E2M1 x E4M3 product must equal the
+    oracle's unpacked value bit for bit. 8 records cover all 254 non-NaN scale
+    bytes x 16 codes at every nibble and byte position; a second set of
+    queries attends to one window row only (bf16 values of magnitude >= 2^-14
+    pass through the kernel exactly)."""
+    print("case: attn decode exact", flush=True)
+    scales = [b for b in range(256) if b not in (0x7F, 0xFF)]
+    nrec = 8
+    rec = np.zeros((nrec, 288), np.uint8)
+    for r in range(nrec):
+        for g in range(32):
+            rec[r, 256 + g] = scales[(r * 32 + g) % len(scales)]
+            for i in range(0, 16, 2):
+                lo, hi = (i + r + g) % 16, (i + 1 + r + g) % 16
+                rec[r, 8 * g + i // 2] = lo | (hi << 4)
+    want = O.fp4_unpack(rec)  # exact in bf16; compared as values (the sum of 1 x -0 and +0 is +0)
+    kv = torch.tensor(rec, device=DEV).view(1, nrec, 288)
+    q = _bf16((nrec, 64, 512), 21)
+    idx = torch.arange(nrec, dtype=torch.int32, device=DEV).view(nrec, 1)
+    out, lse = K().csa2_sparse_attn(q, kv.expand(nrec, nrec, 288).contiguous(), nrec, 1, idx)
+    torch.cuda.synchronize()
+    got = bf16_bits_to_f64(u16(out))
+    for r in range(nrec):
+        assert np.array_equal(got[r], np.broadcast_to(want[r], (64, 512))), r
+    # window only: one row per query
+    swa = torch.randn((nrec, 1, 512), generator=_g(22), device=DEV)
+    swa = torch.where(swa.abs() < 2.0 ** -14, torch.zeros_like(swa), swa).to(torch.bfloat16)
+    none = torch.full((nrec, 1), -1, dtype=torch.int32, device=DEV)
+    st = torch.zeros((nrec,), dtype=torch.int32, device=DEV)
+    sl = torch.ones((nrec,), dtype=torch.int32, device=DEV)
+    out2, _ = K().csa2_sparse_attn(q, kv.expand(nrec, nrec, 288).contiguous(), nrec, 1, none, swa, st, sl)
+    torch.cuda.synchronize()
+    assert torch.equal(out2, swa.expand(nrec, 64, 512))
+
+
 def test_sparse_attn_deterministic():
     print("case: attn determinism", flush=True)
     q, kv, idx, swa, st, sl = _attn_case(16, 4000, 512, 1, 11)
