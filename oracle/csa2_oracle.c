@@ -30,6 +30,10 @@
  *   accounting of [TIT] and [EOG] 5.3: 2.5 entries/token x (288 B main KV +
  *   68 B indexer K)): 128 E2M1 codes (64 B) + one binary32 scale (4 B) per
  *   entry, scale = amax / 6 in float, codes by the same nearest-grid rule.
+ *   FP8 window KV ([EOG] 3.4 keeps the SWA KV in FP8; the element type and
+ *   scaling follow the OCP MX standard the same passage names, i.e. MXFP8):
+ *   E4M3 elements, one E8M0 scale per 32 channels, X = 2^(floor(log2 amax) -
+ *   8), elements = nearest E4M3 value of x / X, ties to even, saturating.
  *
  * Precision: bf16 / E4M3 / E2M1 inputs are decoded exactly into double; dot
  * products, weighted sums and the softmax accumulate in double. The scale
@@ -53,6 +57,8 @@
 #define ORC_GROUP 16
 #define ORC_RECORD (ORC_DIM / 2 + ORC_DIM / ORC_GROUP) /* 256 code bytes + 32 scale bytes */
 #define ORC_KREC (ORC_IDX_DIM / 2 + 4)                  /* 64 code bytes + binary32 scale */
+#define ORC_WBLOCK 32                                   /* channels per FP8 window scale */
+#define ORC_WREC (ORC_DIM + ORC_DIM / ORC_WBLOCK)       /* 512 E4M3 codes + 16 E8M0 scales */
 
 int orc_num_threads(void) {
 #ifdef _OPENMP
@@ -64,6 +70,7 @@ int orc_num_threads(void) {
 
 int orc_record_bytes(void) { return ORC_RECORD; }
 int orc_kidx_record_bytes(void) { return ORC_KREC; }
+int orc_swa_record_bytes(void) { return ORC_WREC; }
 
 /* bf16 -> double: the bf16 bits are the high half of an IEEE binary32. */
 static double bf16_value(uint16_t b) {
@@ -230,6 +237,58 @@ void orc_kidx_fp4_unpack(const uint8_t* in, int64_t n, double* out) {
 
 /* Indexer K of entry `row` decoded to double: bf16 (kfmt 0, [.][128] uint16)
  * or the FP4 entry above (kfmt 1, [.][68] bytes). */
+/* [OCP] E8M0 scale: the value 2^(b - 127); b = 255 is NaN. */
+double orc_e8m0_value(uint8_t b) { return b == 255 ? NAN : ldexp(1.0, (int)b - 127); }
+
+/* FP8 window-KV row ([EOG] 3.4: the quantization-sensitive SWA KV stays in
+ * FP8; read here as the OCP MX block format that passage names, with E4M3
+ * elements). Per block of 32 channels: X = 2^(floor(log2 amax) - 8), 8 being
+ * the exponent of the largest power of two E4M3 holds, clamped to the E8M0
+ * range [-127, 127] (amax = 0 gives 2^-127); each element is the nearest E4M3
+ * value of x / X (exact: X is a power of two), ties to the even code, values
+ * past 448 taking 448; a zero magnitude is +0. Layout: bytes 0..511 the codes
+ * in channel order, byte 512 + g the scale of channels 32g .. 32g+31.
+ * Inputs are finite. */
+void orc_swa_fp8_pack(const uint16_t* x, int64_t n, uint8_t* out) {
+#pragma omp parallel for schedule(static)
+    for (int64_t r = 0; r < n; r++) {
+        const uint16_t* row = x + r * ORC_DIM;
+        uint8_t* rec = out + r * ORC_WREC;
+        for (int g = 0; g < ORC_DIM / ORC_WBLOCK; g++) {
+            double amax = 0.0;
+            for (int i = 0; i < ORC_WBLOCK; i++) {
+                double a = fabs(bf16_value(row[g * ORC_WBLOCK + i]));
+                if (a > amax) amax = a;
+            }
+            int xe = -127;
+            if (amax > 0.0) {
+                int e;
+                frexp(amax, &e); /* amax = f * 2^e, 0.5 <= f < 1: floor(log2 amax) = e - 1 */
+                xe = e - 1 - 8;
+                if (xe < -127) xe = -127;
+                if (xe > 127) xe = 127;
+            }
+            rec[ORC_DIM + g] = (uint8_t)(xe + 127);
+            for (int i = 0; i < ORC_WBLOCK; i++) {
+                double v = bf16_value(row[g * ORC_WBLOCK + i]);
+                uint8_t mag = orc_e4m3_encode_nonneg((float)ldexp(fabs(v), -xe));
+                rec[g * ORC_WBLOCK + i] = (uint8_t)(mag | ((v < 0.0 && mag != 0) ? 0x80 : 0x00));
+            }
+        }
+    }
+}
+
+/* Value of channel c of one FP8 window row: E4M3(code) * E8M0(scale). Exact in double. */
+static double swa_fp8_value(const uint8_t* rec, int c) {
+    return orc_e4m3_value(rec[c]) * orc_e8m0_value(rec[ORC_DIM + c / ORC_WBLOCK]);
+}
+
+void orc_swa_fp8_unpack(const uint8_t* in, int64_t n, double* out) {
+#pragma omp parallel for schedule(static)
+    for (int64_t r = 0; r < n; r++)
+        for (int c = 0; c < ORC_DIM; c++) out[r * ORC_DIM + c] = swa_fp8_value(in + r * ORC_WREC, c);
+}
+
 static void load_key(const void* k, int kfmt, int64_t row, double* kd) {
     if (kfmt == 0) {
         const uint16_t* kr = (const uint16_t*)k + row * ORC_IDX_DIM;
@@ -430,9 +489,10 @@ void orc_topk(const float* scores, int32_t rows, int64_t ncols, int64_t ld, cons
  * [start, start+len). One softmax per head over all of them:
  *   l_j = scale * (q_h . k_j); out_h = sum_j softmax(l)_j v_j;
  *   lse_h = log sum_j exp(l_j). No key at all: out = 0, lse = -inf. */
-void orc_sparse_attn(const uint16_t* q, const uint8_t* kv, int64_t N, int32_t nq, int32_t q_per_seq,
-                     const int32_t* idx, int32_t k, const uint16_t* swa, int64_t T, const int32_t* swa_start,
-                     const int32_t* swa_len, double softmax_scale, double* out, double* lse) {
+static void sparse_attn_any(const uint16_t* q, const uint8_t* kv, int64_t N, int32_t nq, int32_t q_per_seq,
+                            const int32_t* idx, int32_t k, const void* swa, int swa_fmt, int64_t T,
+                            const int32_t* swa_start, const int32_t* swa_len, double softmax_scale, double* out,
+                            double* lse) {
 #pragma omp parallel for schedule(dynamic, 1)
     for (int32_t qi = 0; qi < nq; qi++) {
         int64_t seq = qi / q_per_seq;
@@ -450,8 +510,14 @@ void orc_sparse_attn(const uint16_t* q, const uint8_t* kv, int64_t N, int32_t nq
             nk++;
         }
         for (int64_t t = 0; t < slen; t++) {
-            const uint16_t* row = swa + (seq * T + sst + t) * ORC_DIM;
-            for (int c = 0; c < ORC_DIM; c++) keys[nk * ORC_DIM + c] = bf16_value(row[c]);
+            const int64_t r = seq * T + sst + t;
+            if (swa_fmt == 1) {
+                const uint8_t* rec = (const uint8_t*)swa + r * ORC_WREC;
+                for (int c = 0; c < ORC_DIM; c++) keys[nk * ORC_DIM + c] = swa_fp8_value(rec, c);
+            } else {
+                const uint16_t* row = (const uint16_t*)swa + r * ORC_DIM;
+                for (int c = 0; c < ORC_DIM; c++) keys[nk * ORC_DIM + c] = bf16_value(row[c]);
+            }
             nk++;
         }
         for (int h = 0; h < ORC_HEADS; h++) {
@@ -482,4 +548,18 @@ void orc_sparse_attn(const uint16_t* q, const uint8_t* kv, int64_t N, int32_t nq
         free(logit);
         free(keys);
     }
+}
+
+void orc_sparse_attn(const uint16_t* q, const uint8_t* kv, int64_t N, int32_t nq, int32_t q_per_seq,
+                     const int32_t* idx, int32_t k, const uint16_t* swa, int64_t T, const int32_t* swa_start,
+                     const int32_t* swa_len, double softmax_scale, double* out, double* lse) {
+    sparse_attn_any(q, kv, N, nq, q_per_seq, idx, k, swa, 0, T, swa_start, swa_len, softmax_scale, out, lse);
+}
+
+/* The same attention with the window rows as FP8 records (orc_swa_fp8_pack). */
+void orc_sparse_attn_fp8w(const uint16_t* q, const uint8_t* kv, int64_t N, int32_t nq, int32_t q_per_seq,
+                          const int32_t* idx, int32_t k, const uint8_t* swa_fp8, int64_t T,
+                          const int32_t* swa_start, const int32_t* swa_len, double softmax_scale, double* out,
+                          double* lse) {
+    sparse_attn_any(q, kv, N, nq, q_per_seq, idx, k, swa_fp8, 1, T, swa_start, swa_len, softmax_scale, out, lse);
 }

@@ -21,6 +21,7 @@ _lib = None
 
 RECORD_BYTES = 288
 KIDX_RECORD_BYTES = 68  # FP4 indexer-K entry: 64 code bytes + binary32 scale
+SWA_RECORD_BYTES = 528  # FP8 window row: 512 E4M3 codes + 16 E8M0 scales (one per 32 channels)
 IDX_HEADS, IDX_DIM, HEADS, DIM = 32, 128, 64, 512
 
 
@@ -65,6 +66,11 @@ def lib():
         L.orc_index_reindex.argtypes = [vp, vp, vp, i64, i32, i32, vp, vp, i64, vp]
         L.orc_topk.argtypes = [vp, i32, i64, i64, vp, i32, vp, vp]
         L.orc_sparse_attn.argtypes = [vp, vp, i64, i32, i32, vp, i32, vp, i64, vp, vp, f64, vp, vp]
+        L.orc_sparse_attn_fp8w.argtypes = [vp, vp, i64, i32, i32, vp, i32, vp, i64, vp, vp, f64, vp, vp]
+        L.orc_swa_fp8_pack.argtypes = [vp, i64, vp]
+        L.orc_swa_fp8_unpack.argtypes = [vp, i64, vp]
+        L.orc_e8m0_value.restype = f64
+        L.orc_e8m0_value.argtypes = [ctypes.c_uint8]
         L.orc_num_threads.restype = ctypes.c_int
         _lib = L
     return _lib
@@ -186,15 +192,44 @@ def topk(scores, k, row_len=None, id_map=None):
     return out
 
 
-def sparse_attn(q, kv, N, q_per_seq, idx, swa, T, swa_start, swa_len, softmax_scale=1.0 / np.sqrt(512.0)):
-    """Sparse MQA attention; returns (out [nq,64,512] float64, lse [nq,64] float64)."""
+def sparse_attn(q, kv, N, q_per_seq, idx, swa, T, swa_start, swa_len, softmax_scale=1.0 / np.sqrt(512.0),
+                swa_fp8=None):
+    """Sparse MQA attention; returns (out [nq,64,512] float64, lse [nq,64] float64).
+    The window rows are bf16 `swa` [nseq,T,512], or FP8 rows `swa_fp8`
+    [nseq,T,528] when given (then swa is ignored)."""
     qq = _c(q, np.uint16)
     nq = qq.shape[0]
     ii = _c(idx, np.int32)
     k = ii.shape[1]
     out = np.zeros((nq, HEADS, DIM), np.float64)
     lse = np.zeros((nq, HEADS), np.float64)
-    lib().orc_sparse_attn(_p(qq), _p(_c(kv, np.uint8)), N, nq, q_per_seq, _p(ii), k, _p(_c(swa, np.uint16)), T,
-                          _p(_c(swa_start, np.int32)), _p(_c(swa_len, np.int32)), float(softmax_scale), _p(out),
-                          _p(lse))
+    args = (_p(_c(swa_start, np.int32)), _p(_c(swa_len, np.int32)), float(softmax_scale), _p(out), _p(lse))
+    if swa_fp8 is not None:
+        lib().orc_sparse_attn_fp8w(_p(qq), _p(_c(kv, np.uint8)), N, nq, q_per_seq, _p(ii), k,
+                                   _p(_c(swa_fp8, np.uint8)), T, *args)
+    else:
+        lib().orc_sparse_attn(_p(qq), _p(_c(kv, np.uint8)), N, nq, q_per_seq, _p(ii), k, _p(_c(swa, np.uint16)), T,
+                              *args)
     return out, lse
+
+
+def e8m0_value(b):
+    """OCP E8M0 scale byte -> value (2^(b-127); 255 is NaN)."""
+    return lib().orc_e8m0_value(int(b))
+
+
+def swa_fp8_pack(x_bf16):
+    """FP8 window rows [n, 528] uint8 of bf16 rows [n, 512] ([EOG] 3.4 FP8 SWA
+    KV, read as OCP MXFP8: E4M3 elements, one E8M0 scale per 32 channels)."""
+    x = _c(x_bf16, np.uint16).reshape(-1, DIM)
+    out = np.zeros((x.shape[0], SWA_RECORD_BYTES), np.uint8)
+    lib().orc_swa_fp8_pack(_p(x), x.shape[0], _p(out))
+    return out
+
+
+def swa_fp8_unpack(rec):
+    """Exact values of FP8 window rows, float64 [n, 512]."""
+    r = _c(rec, np.uint8).reshape(-1, SWA_RECORD_BYTES)
+    out = np.zeros((r.shape[0], DIM), np.float64)
+    lib().orc_swa_fp8_unpack(_p(r), r.shape[0], _p(out))
+    return out

@@ -604,3 +604,103 @@ def test_index_fp4k_is_the_score_formula_on_decoded_keys():
             i = pool[r, j]
             exp = s[r, i] if i >= 0 else -np.inf
             assert ps[r, j] == exp or (np.isneginf(ps[r, j]) and np.isneginf(exp))
+
+
+# ------------------------------------------------------- FP8 window rows
+
+def _ocp_mx_exp(amax):
+    """OCP MX shared exponent for E4M3 elements: floor(log2 amax) - 8, clamped
+    to the E8M0 range; 2^-127 for an all-zero block."""
+    if amax == 0:
+        return -127
+    m, e = math.frexp(amax)  # amax = m * 2^e, 0.5 <= m < 1
+    return min(max(e - 1 - 8, -127), 127)
+
+
+def _swa_deq_independent(rec):
+    """Dequantize FP8 window rows with torch's E4M3 decode times 2^(b - 127)."""
+    rec = np.asarray(rec, np.uint8).reshape(-1, 528)
+    el = _e4m3_torch(rec[:, :512].reshape(-1)).reshape(rec.shape[0], 512)
+    sb = rec[:, 512:].astype(np.float64)
+    sc = np.where(sb == 255, np.nan, np.exp2(sb - 127))
+    return el * np.repeat(sc, 32, axis=1)
+
+
+def test_swa_fp8_row_layout_and_ocp_scale_rule():
+    x = np.zeros((1, 512), np.float32)
+    x[0, 0:3] = [1.0, 0.5, -0.25]          # amax 1 -> X = 2^-8: codes of 256, 128, -64
+    x[0, 32] = 3.90625                      # amax in [2, 4): X = 2^-7, 500 saturates to 448
+    x[0, 96] = 2.0 ** -130                  # tiny amax: exponent clamps to -127, 2^-3 remains
+    x[0, 128] = 2.0 ** 120                  # X = 2^112, element 256
+    rec = O.swa_fp8_pack(_bf16(x))
+    assert rec.shape == (1, 528) and O.SWA_RECORD_BYTES == 528 == 512 + 512 // 32
+    assert list(rec[0, :3]) == [0x78, 0x70, 0xE8] and not rec[0, 3:32].any()
+    assert rec[0, 32] == 0x7E
+    assert rec[0, 96] == 0x20 and rec[0, 128] == 0x78
+    assert list(rec[0, 512:517]) == [119, 120, 0, 0, 239]  # block 2 is all zero
+    xf = _bf16_to_f64(_bf16(x))[0]
+    for g in range(16):
+        assert rec[0, 512 + g] == _ocp_mx_exp(np.abs(xf[32 * g:32 * g + 32]).max()) + 127
+
+
+def test_swa_fp8_codes_match_torch_rne_and_saturate():
+    rng = np.random.default_rng(31)
+    rows = np.concatenate([rng.normal(0, 1, (24, 512)), rng.normal(0, 1, (16, 512)) * np.exp2(
+        rng.integers(-40, 40, (16, 1))), rng.uniform(-1, 1, (8, 512)) * 3.99]).astype(np.float32)
+    xb = _bf16(rows)
+    xf = _bf16_to_f64(xb)
+    rec = O.swa_fp8_pack(xb)
+    for r in range(rows.shape[0]):
+        for g in range(16):
+            blk = xf[r, 32 * g:32 * g + 32]
+            e = _ocp_mx_exp(np.abs(blk).max())
+            assert rec[r, 512 + g] == e + 127
+            v = blk * 2.0 ** -e
+            codes = rec[r, 32 * g:32 * g + 32]
+            fin = np.abs(v) <= 448.0
+            # in range: torch's round-to-nearest-even cast (sign of a zero result is +)
+            t = torch.tensor(np.abs(v[fin]).astype(np.float32)).to(torch.float8_e4m3fn).view(torch.uint8).numpy()
+            want = np.where((v[fin] < 0) & (t != 0), t | 0x80, t)
+            assert np.array_equal(codes[fin], want), (r, g)
+            # past 448: saturation to +-448
+            assert np.all((codes[~fin] & 0x7F) == 0x7E)
+            assert np.all((codes[~fin] >> 7) == (v[~fin] < 0))
+
+
+def test_swa_fp8_unpack_is_table_times_scale_and_error_bound():
+    rng = np.random.default_rng(32)
+    rec = rng.integers(0, 256, (40, 528)).astype(np.uint8)
+    assert np.array_equal(O.swa_fp8_unpack(rec), _swa_deq_independent(rec), equal_nan=True)
+    # round trip: error <= 2^-4 |x| (normal elements) or half the subnormal step,
+    # except saturated elements, which decode to +-448 X
+    xb = _rand_bf16(rng, (32, 512), 2.0)
+    xf = _bf16_to_f64(xb)
+    rt = O.swa_fp8_unpack(O.swa_fp8_pack(xb))
+    for r in range(32):
+        for g in range(16):
+            blk, got = xf[r, 32 * g:32 * g + 32], rt[r, 32 * g:32 * g + 32]
+            X = 2.0 ** _ocp_mx_exp(np.abs(blk).max())
+            sat = np.abs(blk) > 448 * X
+            assert np.all(got[sat] == np.sign(blk[sat]) * 448 * X)
+            err = np.abs(got[~sat] - blk[~sat])
+            assert np.all(err <= np.maximum(np.abs(blk[~sat]) * 2.0 ** -4, X * 2.0 ** -10))
+
+
+def test_attention_fp8_window_is_attention_on_the_decoded_rows():
+    rng = np.random.default_rng(33)
+    nq, N, k, T = 3, 200, 40, 140
+    q = _rand_bf16(rng, (nq, 64, 512))
+    kv = O.fp4_pack(_rand_bf16(rng, (nq * N, 512))).reshape(nq, N, 288)
+    idx = np.sort(np.stack([rng.choice(N, k, replace=False) for _ in range(nq)]), 1).astype(np.int32)
+    idx[1, -5:] = -1
+    swa = _rand_bf16(rng, (nq, T, 512), 1.5)
+    wrec = O.swa_fp8_pack(swa.reshape(-1, 512)).reshape(nq, T, 528)
+    st = np.array([0, 3, 12], np.int32)
+    sl = np.array([128, 0, 100], np.int32)
+    o8, l8 = O.sparse_attn(q, kv, N, 1, idx, None, T, st, sl, swa_fp8=wrec)
+    # the decoded rows are bf16 values (4 significant bits times a power of two)
+    dec = O.swa_fp8_unpack(wrec.reshape(-1, 528)).reshape(nq, T, 512)
+    db = _bf16(dec)
+    assert np.array_equal(_bf16_to_f64(db), dec)
+    ob, lb = O.sparse_attn(q, kv, N, 1, idx, db, T, st, sl)
+    assert np.array_equal(o8, ob) and np.array_equal(l8, lb)
