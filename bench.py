@@ -14,7 +14,9 @@ A step is one pass of the whole hot path over one batch of synthetic input:
       Reindex layer's and 3 Reuse layers');
   encoder64k_fp4k / decode1m_fp4k : the 64K and 1M steps reading the indexer
       K as FP4 entries (68 B) packed from the same kind of bf16 keys before
-      timing.
+      timing;
+  encoder64k_fp4k_fp8w / decode1m_fp4k_fp8w : the same with the window KV
+      as FP8 rows (528 B) as well: both of the pages' cache precisions.
 The headline is decode queries/s on encoder64k (64 queries, 64K-token context
 at m=2 = 32768 FP4 entries per sequence). Inputs live in HBM before timing and
 two independent input sets alternate between steps, so the 256 MB last-level
@@ -56,10 +58,10 @@ def alg_flops_index_full(wl):
     return 2 * 32 * 128 * n_vis
 
 
-def alg_bytes_attn(nq, k=512, window=128):
-    """Per query-layer: k FP4 records (288 B), the window rows (1 KiB each),
-    the query (64 KiB), the output (64 KiB) and k indices."""
-    return nq * (k * 288 + window * 1024 + 64 * 1024 + 64 * 1024 + k * 4)
+def alg_bytes_attn(nq, k=512, window=128, window_row=1024):
+    """Per query-layer: k FP4 records (288 B), the window rows (1 KiB bf16 or
+    528 B FP8 each), the query (64 KiB), the output (64 KiB) and k indices."""
+    return nq * (k * 288 + window * window_row + 64 * 1024 + 64 * 1024 + k * 4)
 
 
 def alg_flops_attn(nq, k=512, window=128):
@@ -141,7 +143,7 @@ def bench_workload(name, steps, warmup, nsets, torch):
         res["index_full_GBps"] = alg_bytes_index_full(wl) / t_idx / 1e9
         res["index_full_TFLOPs"] = alg_flops_index_full(wl) / t_idx / 1e12
     t_att = calls["attn"][0] * 1e-3
-    res["attn_GBps"] = alg_bytes_attn(wl.nq) / t_att / 1e9
+    res["attn_GBps"] = alg_bytes_attn(wl.nq, window_row=528 if wl.swa_fmt == "fp8" else 1024) / t_att / 1e9
     res["attn_TFLOPs"] = alg_flops_attn(wl.nq) / t_att / 1e12
     res["_alg_bytes_index_full"] = alg_bytes_index_full(wl)
     res["_alg_flops_index_full"] = alg_flops_index_full(wl)
@@ -261,7 +263,7 @@ def main():
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--workloads",
                     default="encoder64k,decoder256k,decode1m,prefill128k,encoder_group64k,decoder_group256k,"
-                            "encoder64k_fp4k,decode1m_fp4k")
+                            "encoder64k_fp4k,decode1m_fp4k,encoder64k_fp4k_fp8w,decode1m_fp4k_fp8w")
     ap.add_argument("--attn-sweep", default="64,256,1024")
     ap.add_argument("--no-cpu", action="store_true")
     ap.add_argument("--calibrate-copy", action="store_true",
@@ -317,7 +319,7 @@ def main():
     line = {
         "metric": METRIC, "value": round(h["queries_per_s"], 1), "unit": "queries/s", "n_gpus": 1,
         "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(h["ms_per_step"], 5),
-        "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "bf16",
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "bf16/fp16",
         "data": "synthetic (seeded; shapes and distributions of the pages' 64K encoder decode)",
         "config": {"workload": "encoder64k: 64 decode queries, 64K-token context at m=2 = 32768 FP4 entries "
                                "per sequence, Full mode, Top-512, 64x512 MQA + 128 SWA",

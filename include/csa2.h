@@ -63,6 +63,7 @@ extern "C" {
 #define CSA2_GROUP 16       /* channels per E4M3 scale */
 #define CSA2_RECORD 288     /* bytes per FP4 main-KV entry: 256 code bytes + 32 scale bytes */
 #define CSA2_KIDX_RECORD 68 /* bytes per FP4 indexer-K entry: 64 code bytes + binary32 scale */
+#define CSA2_SWA_RECORD 528 /* bytes per FP8 window-KV row: 512 E4M3 codes + 16 E8M0 scales */
 #define CSA2_MAX_WINDOW 128 /* sliding-window length limit */
 #define CSA2_MAX_TOPK 4096  /* largest k accepted by csa2_topk */
 
@@ -148,6 +149,21 @@ int csa2_index_reindex(const uint16_t* q_idx, const float* w, const uint16_t* k_
 int kidx_fp4_pack(const uint16_t* x_bf16, int64_t n, uint8_t* out, hipStream_t stream);
 
 /*
+ * swa_fp8_pack -- FP8 window-KV rows (eogee.com report 3.4: the window KV,
+ * sensitive to quantization, stays in FP8; the block scaling is the OCP MX
+ * format the same passage names for the cache: MXFP8 with E4M3 elements).
+ *   x_bf16 [n][512] bf16 row-major.
+ *   out    [n][528] bytes. Bytes 0..511: the E4M3 code of each channel in
+ *          channel order; byte 512+g: the E8M0 scale (value 2^(b-127)) of
+ *          channels 32g..32g+31. Per block X = 2^(floor(log2 amax) - 8),
+ *          clamped to [2^-127, 2^127] (an all-zero block gets 2^-127); each
+ *          channel is the E4M3 value nearest to x / X (ties to even, beyond
+ *          448 -> 448, zero magnitude -> +0). Inputs must be finite. n >= 0.
+ *   value(channel c) = E4M3(code_c) * 2^(scale_byte - 127).
+ */
+int swa_fp8_pack(const uint16_t* x_bf16, int64_t n, uint8_t* out, hipStream_t stream);
+
+/*
  * csa2_index_full_fp4k / csa2_index_reindex_fp4k -- csa2_index_full and
  * csa2_index_reindex over the FP4 indexer-K cache k_fp4 [nseq][N][68] (entries
  * of kidx_fp4_pack) instead of bf16 k_idx; every other argument, output and
@@ -210,6 +226,19 @@ int csa2_sparse_attn(const uint16_t* q, const uint8_t* kv, int64_t N, int32_t nq
                      const int32_t* idx, int32_t k, const uint16_t* swa, int64_t T, const int32_t* swa_start,
                      const int32_t* swa_len, float softmax_scale, uint16_t* out, float* lse, void* workspace,
                      size_t ws_bytes, hipStream_t stream);
+
+/*
+ * csa2_sparse_attn_fp8w -- csa2_sparse_attn with the window KV stored as FP8
+ * rows (eogee.com report 3.4; layout of swa_fp8_pack).
+ *   swa_fp8 [nseq][T][528] FP8 window rows; every other argument, the output
+ *           and the errors as for csa2_sparse_attn. A decoded window value is
+ *           exact in the fp16 products while its 32-channel block maximum
+ *           lies in [2^-7, 2^16) (smaller blocks lose bits below 2^-24).
+ */
+int csa2_sparse_attn_fp8w(const uint16_t* q, const uint8_t* kv, int64_t N, int32_t nq, int32_t q_per_seq,
+                          const int32_t* idx, int32_t k, const uint8_t* swa_fp8, int64_t T, const int32_t* swa_start,
+                          const int32_t* swa_len, float softmax_scale, uint16_t* out, float* lse, void* workspace,
+                          size_t ws_bytes, hipStream_t stream);
 
 #ifdef __cplusplus
 }

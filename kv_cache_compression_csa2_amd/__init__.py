@@ -6,4 +6,4 @@ seeded synthetic workloads and the per-step call sequence.
 """
 from ._lib import (Csa2Error, csa2_index_full, csa2_index_reindex, csa2_sparse_attn,  # noqa: F401
                    csa2_sparse_attn_workspace_bytes, csa2_topk, csa2_topk_workspace_bytes, format_version,
-                   fp4_kv_pack, fp4_kv_unpack, kidx_fp4_pack, load)
+                   fp4_kv_pack, fp4_kv_unpack, kidx_fp4_pack, load, swa_fp8_pack)

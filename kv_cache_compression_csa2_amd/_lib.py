@@ -15,6 +15,7 @@ LIB_PATH = os.path.join(_HERE, "libcsa2.so")
 CSA2_OK, CSA2_EINVAL, CSA2_ELAUNCH, CSA2_EWORKSPACE = 0, -1, -2, -3
 DIM, HEADS, IDX_HEADS, IDX_DIM, RECORD = 512, 64, 32, 128, 288
 KIDX_RECORD = 68  # FP4 indexer-K entry: 64 code bytes + binary32 scale
+SWA_RECORD = 528  # FP8 window-KV row: 512 E4M3 codes + 16 E8M0 scales
 
 _lib = None
 
@@ -44,14 +45,17 @@ def load():
     L.kidx_fp4_pack.argtypes = [vp, i64, vp, vp]
     L.csa2_index_full_fp4k.argtypes = [vp, vp, vp, i64, i32, i32, vp, vp, i32, vp, vp]
     L.csa2_index_reindex_fp4k.argtypes = [vp, vp, vp, i64, i32, i32, vp, vp, i32, i32, vp, vp, vp]
+    L.swa_fp8_pack.argtypes = [vp, i64, vp, vp]
     L.csa2_topk_workspace_bytes.argtypes = [i32, i64, i32]
     L.csa2_topk_workspace_bytes.restype = sz
     L.csa2_topk.argtypes = [vp, i32, i64, i64, vp, i32, vp, vp, vp, sz, vp]
     L.csa2_sparse_attn_workspace_bytes.argtypes = [i32, i32]
     L.csa2_sparse_attn_workspace_bytes.restype = sz
     L.csa2_sparse_attn.argtypes = [vp, vp, i64, i32, i32, vp, i32, vp, i64, vp, vp, f32, vp, vp, vp, sz, vp]
+    L.csa2_sparse_attn_fp8w.argtypes = [vp, vp, i64, i32, i32, vp, i32, vp, i64, vp, vp, f32, vp, vp, vp, sz, vp]
     for name in ["fp4_kv_pack", "fp4_kv_unpack", "csa2_index_full", "csa2_index_reindex", "csa2_topk",
-                 "csa2_sparse_attn", "kidx_fp4_pack", "csa2_index_full_fp4k", "csa2_index_reindex_fp4k"]:
+                 "csa2_sparse_attn", "kidx_fp4_pack", "csa2_index_full_fp4k", "csa2_index_reindex_fp4k",
+                 "swa_fp8_pack", "csa2_sparse_attn_fp8w"]:
         getattr(L, name).restype = ctypes.c_int
     _lib = L
     return L
@@ -59,7 +63,8 @@ def load():
 
 EXPORTS = ["csa2_format_version", "csa2_last_error", "fp4_kv_pack", "fp4_kv_unpack", "csa2_index_full",
            "csa2_index_reindex", "csa2_topk_workspace_bytes", "csa2_topk", "csa2_sparse_attn_workspace_bytes",
-           "csa2_sparse_attn", "kidx_fp4_pack", "csa2_index_full_fp4k", "csa2_index_reindex_fp4k"]
+           "csa2_sparse_attn", "kidx_fp4_pack", "csa2_index_full_fp4k", "csa2_index_reindex_fp4k", "swa_fp8_pack",
+           "csa2_sparse_attn_fp8w"]
 
 
 def _ptr(t):
@@ -137,6 +142,17 @@ def kidx_fp4_pack(x, out=None, stream=None):
     return out
 
 
+def swa_fp8_pack(x, out=None, stream=None):
+    """bf16 [n,512] window rows -> uint8 [n,528] FP8 rows (512 E4M3 codes + 16 E8M0 scales)."""
+    _need(x, torch.bfloat16, "x")
+    n = x.numel() // DIM
+    if out is None:
+        out = torch.empty((n, SWA_RECORD), dtype=torch.uint8, device=x.device)
+    _need(out, torch.uint8, "out")
+    _check(load().swa_fp8_pack(_ptr(x), n, _ptr(out), _stream(stream)), "swa_fp8_pack")
+    return out
+
+
 def csa2_index_full(q_idx, w, k_idx, N, q_per_seq, n_visible=None, block_size=0, scores=None, block_scores=None,
                     stream=None, k_fp4=None):
     """Full-mode indexer scores [nq,N] fp32 (and block maxima [nq,ceil(N/8)] when block_size == 8).
@@ -202,15 +218,20 @@ def csa2_sparse_attn_workspace_bytes(nq, k):
 
 
 def csa2_sparse_attn(q, kv, N, q_per_seq, idx, swa=None, swa_start=None, swa_len=None, softmax_scale=None,
-                     out=None, lse=None, want_lse=True, workspace=None, stream=None):
-    """Sparse MQA attention: bf16 out [nq,64,512] (and lse [nq,64] fp32)."""
+                     out=None, lse=None, want_lse=True, workspace=None, stream=None, swa_fp8=None):
+    """Sparse MQA attention: bf16 out [nq,64,512] (and lse [nq,64] fp32).
+    The window rows are bf16 `swa` [nseq,T,512], or FP8 rows `swa_fp8`
+    [nseq,T,528] (pass swa=None)."""
+    if swa is not None and swa_fp8 is not None:
+        raise ValueError("pass at most one of swa (bf16) and swa_fp8 (uint8 [.., 528])")
     for t, dt, nm in [(q, torch.bfloat16, "q"), (kv, torch.uint8, "kv"), (idx, torch.int32, "idx"),
-                      (swa, torch.bfloat16, "swa"), (swa_start, torch.int32, "swa_start"),
-                      (swa_len, torch.int32, "swa_len")]:
+                      (swa, torch.bfloat16, "swa"), (swa_fp8, torch.uint8, "swa_fp8"),
+                      (swa_start, torch.int32, "swa_start"), (swa_len, torch.int32, "swa_len")]:
         _need(t, dt, nm)
     nq = q.shape[0]
     k = idx.shape[1]
-    T = swa.shape[-2] if swa is not None else 0
+    win = swa if swa_fp8 is None else swa_fp8
+    T = win.shape[-2] if win is not None else 0
     if softmax_scale is None:
         softmax_scale = DIM ** -0.5
     if out is None:
@@ -221,7 +242,8 @@ def csa2_sparse_attn(q, kv, N, q_per_seq, idx, swa=None, swa_start=None, swa_len
     if workspace is None and need:
         workspace = torch.empty((need,), dtype=torch.uint8, device=q.device)
     wsb = workspace.numel() * workspace.element_size() if workspace is not None else 0
-    _check(load().csa2_sparse_attn(_ptr(q), _ptr(kv), N, nq, q_per_seq, _ptr(idx), k, _ptr(swa), T,
-                                   _ptr(swa_start), _ptr(swa_len), float(softmax_scale), _ptr(out), _ptr(lse),
-                                   _ptr(workspace), wsb, _stream(stream)), "csa2_sparse_attn")
+    name = "csa2_sparse_attn" if swa_fp8 is None else "csa2_sparse_attn_fp8w"
+    _check(getattr(load(), name)(_ptr(q), _ptr(kv), N, nq, q_per_seq, _ptr(idx), k, _ptr(win), T, _ptr(swa_start),
+                                 _ptr(swa_len), float(softmax_scale), _ptr(out), _ptr(lse), _ptr(workspace), wsb,
+                                 _stream(stream)), name)
     return out, lse

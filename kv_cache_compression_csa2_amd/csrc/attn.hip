@@ -159,9 +159,16 @@ struct RawRec {
 // loaded without prefetch) spread over the splits.
 CSA2_DEVINL int part_lo(int n, int s, int nsplit) { return (int)(((int64_t)n * s) / nsplit); }
 
+constexpr int kSwaRec = kDim + kDim / 32;  // FP8 window row: 512 E4M3 codes + 16 E8M0 scales
+
+// Window rows are bf16 [T][512] or, with kFp8Win, FP8 rows [T][528] (E4M3
+// elements, one E8M0 scale per 32 channels; each gather thread's 32 channels
+// are exactly one scale block). E4M3 times a power of two is exact in fp16
+// while the block maximum lies in [2^-7, 2^16).
+template <bool kFp8Win>
 __global__ __launch_bounds__(kAttThreads, 2) void sparse_attn_kernel(
     const uint16_t* __restrict__ q, const uint8_t* __restrict__ kv, int64_t N, int32_t q_per_seq,
-    const int32_t* __restrict__ idx, int32_t k, const uint16_t* __restrict__ swa, int64_t T,
+    const int32_t* __restrict__ idx, int32_t k, const void* __restrict__ swa, int64_t T,
     const int32_t* __restrict__ swa_start, const int32_t* __restrict__ swa_len, float scale_log2,
     uint16_t* __restrict__ out, float* __restrict__ lse, float* __restrict__ part_o, float* __restrict__ part_ml,
     int32_t nsplit) {
@@ -186,8 +193,8 @@ __global__ __launch_bounds__(kAttThreads, 2) void sparse_attn_kernel(
     const int w0 = part_lo(W, split, nsplit), w1 = part_lo(W, split + 1, nsplit);
     // window tiles past the query's window length hold no keys
     const int wlive = (slen + kTile - 1) / kTile;
-    const int nwin = (w1 < wlive ? w1 : wlive) - w0;
-    const int ntiles = nmain + (nwin > 0 ? nwin : 0);
+    const int nwin = (w1 < wlive ? w1 : wlive) > w0 ? (w1 < wlive ? w1 : wlive) - w0 : 0;
+    const int ntiles = nmain + nwin;
 
     f32x4 o[32];
 #pragma unroll
@@ -195,7 +202,8 @@ __global__ __launch_bounds__(kAttThreads, 2) void sparse_attn_kernel(
     float m_run = kMaxFloor, l_run = 0.0f;
 
     const uint8_t* kv_seq = kv + seq * N * kRecord;
-    const uint16_t* swa_seq = swa ? swa + seq * T * kDim : nullptr;
+    const uint16_t* swa_seq = (swa && !kFp8Win) ? static_cast<const uint16_t*>(swa) + seq * T * kDim : nullptr;
+    const uint8_t* swa8_seq = (swa && kFp8Win) ? static_cast<const uint8_t*>(swa) + seq * T * kSwaRec : nullptr;
     const int32_t* idx_q = idx + qi * (int64_t)k + (int64_t)m0 * kTile;
 
     // the workgroup's entry ids, checked once
@@ -245,7 +253,23 @@ __global__ __launch_bounds__(kAttThreads, 2) void sparse_attn_kernel(
             const int r = wbase + r0 + 16 * h;
             const bool ok = r < slen && sst + r >= 0 && sst + r < T;
             uint4 u[4];
-            if (ok) {
+            if (ok && kFp8Win) {
+                const uint8_t* rec = swa8_seq + (int64_t)(sst + r) * kSwaRec;
+                const uint4 c0 = reinterpret_cast<const uint4*>(rec + 32 * c)[0];
+                const uint4 c1 = reinterpret_cast<const uint4*>(rec + 32 * c)[1];
+                // the E8M0 byte as the exponent field of a binary32: the
+                // conversion applies that power of two
+                const float X = __uint_as_float((uint32_t)rec[kDim + c] << 23);
+                const uint32_t cw[8] = {c0.x, c0.y, c0.z, c0.w, c1.x, c1.y, c1.z, c1.w};
+                uint32_t h[16];
+#pragma unroll
+                for (int i = 0; i < 8; i++) {
+                    h[2 * i] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(cw[i], X, false));
+                    h[2 * i + 1] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(cw[i], X, true));
+                }
+#pragma unroll
+                for (int jj = 0; jj < 4; jj++) u[jj] = make_uint4(h[4 * jj], h[4 * jj + 1], h[4 * jj + 2], h[4 * jj + 3]);
+            } else if (ok) {
                 const uint4* src = reinterpret_cast<const uint4*>(swa_seq + (int64_t)(sst + r) * kDim) + 4 * c;
 #pragma unroll
                 for (int jj = 0; jj < 4; jj++) u[jj] = bf16x8_to_f16x8(src[jj]);
@@ -404,7 +428,7 @@ size_t attn_workspace_bytes(int32_t nq, int32_t k) {
 }
 
 int launch_sparse_attn(const uint16_t* q, const uint8_t* kv, int64_t N, int32_t nq, int32_t q_per_seq,
-                       const int32_t* idx, int32_t k, const uint16_t* swa, int64_t T, const int32_t* swa_start,
+                       const int32_t* idx, int32_t k, const void* swa, bool swa_fp8, int64_t T, const int32_t* swa_start,
                        const int32_t* swa_len, float softmax_scale, uint16_t* out, float* lse, void* ws,
                        hipStream_t s) {
     if (nq == 0) return 0;
@@ -419,8 +443,13 @@ int launch_sparse_attn(const uint16_t* q, const uint8_t* kv, int64_t N, int32_t 
         part_ml = part_o + (size_t)nq * ns * kHeads * kDim;
     }
     const float scale_log2 = softmax_scale * 1.4426950408889634f;
-    hipLaunchKernelGGL(sparse_attn_kernel, dim3((unsigned)((int64_t)nq * ns)), dim3(kAttThreads), sid_bytes, s, q,
-                       kv, N, q_per_seq, idx, k, swa, T, swa_start, swa_len, scale_log2, out, lse, part_o, part_ml, ns);
+    const dim3 grid((unsigned)((int64_t)nq * ns));
+    if (swa_fp8)
+        hipLaunchKernelGGL(sparse_attn_kernel<true>, grid, dim3(kAttThreads), sid_bytes, s, q, kv, N, q_per_seq, idx,
+                           k, swa, T, swa_start, swa_len, scale_log2, out, lse, part_o, part_ml, ns);
+    else
+        hipLaunchKernelGGL(sparse_attn_kernel<false>, grid, dim3(kAttThreads), sid_bytes, s, q, kv, N, q_per_seq, idx,
+                           k, swa, T, swa_start, swa_len, scale_log2, out, lse, part_o, part_ml, ns);
     if (ns > 1)
         hipLaunchKernelGGL(attn_merge_kernel, dim3((unsigned)((int64_t)nq * kHeads)), dim3(128), 0, s, part_o,
                            part_ml, ns, out, lse);

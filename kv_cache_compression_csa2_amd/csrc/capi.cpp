@@ -152,27 +152,50 @@ size_t csa2_sparse_attn_workspace_bytes(int32_t nq, int32_t k) {
     return csa2::attn_workspace_bytes(nq, k);
 }
 
+static int sparse_attn_impl(const char* fn, const uint16_t* q, const uint8_t* kv, int64_t N, int32_t nq,
+                            int32_t q_per_seq, const int32_t* idx, int32_t k, const void* swa, bool swa_fp8, int64_t T,
+                            const int32_t* swa_start, const int32_t* swa_len, float softmax_scale, uint16_t* out,
+                            float* lse, void* workspace, size_t ws_bytes, hipStream_t stream) {
+    if (nq < 0) return fail(CSA2_EINVAL, "%s: nq < 0", fn);
+    if (N < 1 || N > kMaxN) return fail(CSA2_EINVAL, "%s: N must be in [1, 2^31-1]", fn);
+    if (q_per_seq < 1 || nq % q_per_seq != 0) return fail(CSA2_EINVAL, "%s: q_per_seq must be >= 1 and divide nq", fn);
+    if (k < 0 || k > CSA2_MAX_TOPK) return fail(CSA2_EINVAL, "%s: k must be in [0, %d]", fn, CSA2_MAX_TOPK);
+    if (nq > 0 && (!q || !kv || !out)) return fail(CSA2_EINVAL, "%s: null pointer", fn);
+    if (nq > 0 && k > 0 && !idx) return fail(CSA2_EINVAL, "%s: null idx", fn);
+    if (swa && (T < 1 || !swa_start || !swa_len))
+        return fail(CSA2_EINVAL, "%s: a window needs T >= 1, swa_start and swa_len", fn);
+    if (!(softmax_scale == softmax_scale)) return fail(CSA2_EINVAL, "%s: softmax_scale is NaN", fn);
+    const size_t need = csa2_sparse_attn_workspace_bytes(nq, k);
+    if (nq > 0 && need > 0 && (!workspace || ws_bytes < need))
+        return fail(CSA2_EWORKSPACE, "%s: workspace needs %zu bytes", fn, need);
+    (void)hipGetLastError();
+    csa2::launch_sparse_attn(q, kv, N, nq, q_per_seq, idx, k, swa, swa_fp8, swa ? T : 0, swa ? swa_start : nullptr,
+                             swa ? swa_len : nullptr, softmax_scale, out, lse, workspace, stream);
+    return launched(fn);
+}
+
 int csa2_sparse_attn(const uint16_t* q, const uint8_t* kv, int64_t N, int32_t nq, int32_t q_per_seq,
                      const int32_t* idx, int32_t k, const uint16_t* swa, int64_t T, const int32_t* swa_start,
                      const int32_t* swa_len, float softmax_scale, uint16_t* out, float* lse, void* workspace,
                      size_t ws_bytes, hipStream_t stream) {
-    if (nq < 0) return fail(CSA2_EINVAL, "csa2_sparse_attn: nq < 0");
-    if (N < 1 || N > kMaxN) return fail(CSA2_EINVAL, "csa2_sparse_attn: N must be in [1, 2^31-1]");
-    if (q_per_seq < 1 || nq % q_per_seq != 0)
-        return fail(CSA2_EINVAL, "csa2_sparse_attn: q_per_seq must be >= 1 and divide nq");
-    if (k < 0 || k > CSA2_MAX_TOPK) return fail(CSA2_EINVAL, "csa2_sparse_attn: k must be in [0, %d]", CSA2_MAX_TOPK);
-    if (nq > 0 && (!q || !kv || !out)) return fail(CSA2_EINVAL, "csa2_sparse_attn: null pointer");
-    if (nq > 0 && k > 0 && !idx) return fail(CSA2_EINVAL, "csa2_sparse_attn: null idx");
-    if (swa && (T < 1 || !swa_start || !swa_len))
-        return fail(CSA2_EINVAL, "csa2_sparse_attn: a window needs T >= 1, swa_start and swa_len");
-    if (!(softmax_scale == softmax_scale)) return fail(CSA2_EINVAL, "csa2_sparse_attn: softmax_scale is NaN");
-    const size_t need = csa2_sparse_attn_workspace_bytes(nq, k);
-    if (nq > 0 && need > 0 && (!workspace || ws_bytes < need))
-        return fail(CSA2_EWORKSPACE, "csa2_sparse_attn: workspace needs %zu bytes", need);
+    return sparse_attn_impl("csa2_sparse_attn", q, kv, N, nq, q_per_seq, idx, k, swa, false, T, swa_start, swa_len,
+                            softmax_scale, out, lse, workspace, ws_bytes, stream);
+}
+
+int csa2_sparse_attn_fp8w(const uint16_t* q, const uint8_t* kv, int64_t N, int32_t nq, int32_t q_per_seq,
+                          const int32_t* idx, int32_t k, const uint8_t* swa_fp8, int64_t T, const int32_t* swa_start,
+                          const int32_t* swa_len, float softmax_scale, uint16_t* out, float* lse, void* workspace,
+                          size_t ws_bytes, hipStream_t stream) {
+    return sparse_attn_impl("csa2_sparse_attn_fp8w", q, kv, N, nq, q_per_seq, idx, k, swa_fp8, true, T, swa_start,
+                            swa_len, softmax_scale, out, lse, workspace, ws_bytes, stream);
+}
+
+int swa_fp8_pack(const uint16_t* x, int64_t n, uint8_t* out, hipStream_t stream) {
+    if (n < 0) return fail(CSA2_EINVAL, "swa_fp8_pack: n < 0");
+    if (n > 0 && (!x || !out)) return fail(CSA2_EINVAL, "swa_fp8_pack: null pointer");
     (void)hipGetLastError();
-    csa2::launch_sparse_attn(q, kv, N, nq, q_per_seq, idx, k, swa, swa ? T : 0, swa ? swa_start : nullptr,
-                             swa ? swa_len : nullptr, softmax_scale, out, lse, workspace, stream);
-    return launched("csa2_sparse_attn");
+    csa2::launch_swa_fp8_pack(x, n, out, stream);
+    return launched("swa_fp8_pack");
 }
 
 }  // extern "C"

@@ -115,6 +115,69 @@ __global__ __launch_bounds__(256) void kidx_fp4_pack_kernel(const uint16_t* __re
     if (sl == 0) reinterpret_cast<uint32_t*>(dst)[16] = __float_as_uint(s);
 }
 
+// FP8 window-KV rows: E4M3 elements with one E8M0 scale per 32 channels, the
+// OCP MX block format (eogee.com report 3.4 keeps the window KV in FP8 and
+// names the OCP MX standard for the cache formats). Per block:
+// X = 2^(floor(log2 amax) - 8), 8 being the exponent of E4M3's largest power
+// of two, clamped to E8M0's [-127, 127]; element = nearest E4M3 value of x/X
+// (exact: X is a power of two), ties to even, saturating at 448; a zero
+// magnitude is +0. Row: 512 code bytes in channel order, then 16 scale bytes.
+// Thread = one 32-channel block; 16 threads per row.
+constexpr int kSwaRec = kDim + kDim / 32;  // 528
+
+__global__ __launch_bounds__(256) void swa_fp8_pack_kernel(const uint16_t* __restrict__ x, int64_t n,
+                                                           uint8_t* __restrict__ out) {
+    const int64_t t = blockIdx.x * (int64_t)blockDim.x + threadIdx.x;
+    const int64_t row = t >> 4;
+    const int g = (int)(t & 15);
+    if (row >= n) return;
+    const uint4* src = reinterpret_cast<const uint4*>(x + row * kDim + 32 * g);
+    float xs[32];
+#pragma unroll
+    for (int i = 0; i < 4; i++) {
+        const uint4 v = src[i];
+        const uint32_t wv[4] = {v.x, v.y, v.z, v.w};
+#pragma unroll
+        for (int k = 0; k < 4; k++) {
+            xs[8 * i + 2 * k] = bf16_bits_to_float(wv[k] & 0xFFFFu);
+            xs[8 * i + 2 * k + 1] = bf16_bits_to_float(wv[k] >> 16);
+        }
+    }
+    float amax = 0.0f;
+#pragma unroll
+    for (int i = 0; i < 32; i++) amax = fmaxf(amax, fabsf(xs[i]));
+    int xe = -127;
+    if (amax > 0.0f) {
+        // amax = m * 2^e with 0.5 <= m < 1, so floor(log2 amax) = e - 1
+        xe = __builtin_amdgcn_frexp_expf(amax) - 1 - 8;
+        xe = xe < -127 ? -127 : (xe > 127 ? 127 : xe);
+    }
+    uint32_t codes[8];
+#pragma unroll
+    for (int w = 0; w < 8; w++) {
+        uint32_t word = 0;
+#pragma unroll
+        for (int b = 0; b < 4; b++) {
+            const float v = xs[4 * w + b];
+            uint32_t c = e4m3_encode_rne_sat(ldexpf(fabsf(v), -xe));
+            if (c != 0 && v < 0.0f) c |= 0x80u;
+            word |= c << (8 * b);
+        }
+        codes[w] = word;
+    }
+    uint8_t* dst = out + row * kSwaRec;
+    reinterpret_cast<uint4*>(dst + 32 * g)[0] = make_uint4(codes[0], codes[1], codes[2], codes[3]);
+    reinterpret_cast<uint4*>(dst + 32 * g)[1] = make_uint4(codes[4], codes[5], codes[6], codes[7]);
+    dst[kDim + g] = (uint8_t)(xe + 127);
+}
+
+int launch_swa_fp8_pack(const uint16_t* x, int64_t n, uint8_t* out, hipStream_t s) {
+    if (n == 0) return 0;
+    const int64_t blocks = (n * 16 + 255) / 256;
+    hipLaunchKernelGGL(swa_fp8_pack_kernel, dim3((unsigned)blocks), dim3(256), 0, s, x, n, out);
+    return 0;
+}
+
 int launch_kidx_fp4_pack(const uint16_t* x, int64_t n, uint8_t* out, hipStream_t s) {
     if (n == 0) return 0;
     const int64_t blocks = (n * 16 + 255) / 256;

@@ -40,6 +40,11 @@ class Step:
                               L.csa2_topk_workspace_bytes(nq, (N + 7) // 8, POOL_BLOCKS) if wl.hier else 0,
                               L.csa2_topk_workspace_bytes(nq, pool, TOPK) if wl.hier else 0))
         self.ws_attn = ws(L.csa2_sparse_attn_workspace_bytes(nq, TOPK))
+        # FP8 window rows (the cache format; packed once, outside any timed step)
+        self.swa8 = None
+        if wl.swa_fmt == "fp8":
+            self.swa8 = [L.swa_fp8_pack(s.reshape(-1, L.DIM)).view(s.shape[0], s.shape[1], L.SWA_RECORD)
+                         for s in wl.swa]
 
     @staticmethod
     def _k(k):
@@ -71,8 +76,13 @@ class Step:
 
     def attend(self, layer, kv, idx):
         wl = self.wl
-        L.csa2_sparse_attn(wl.q[layer], kv, wl.N, wl.q_per_seq, idx, wl.swa[layer], wl.swa_start, wl.swa_len,
-                           out=self.out[layer], lse=self.lse[layer], workspace=self.ws_attn)
+        if self.swa8 is not None:
+            L.csa2_sparse_attn(wl.q[layer], kv, wl.N, wl.q_per_seq, idx, None, wl.swa_start, wl.swa_len,
+                               out=self.out[layer], lse=self.lse[layer], workspace=self.ws_attn,
+                               swa_fp8=self.swa8[layer])
+        else:
+            L.csa2_sparse_attn(wl.q[layer], kv, wl.N, wl.q_per_seq, idx, wl.swa[layer], wl.swa_start, wl.swa_len,
+                               out=self.out[layer], lse=self.lse[layer], workspace=self.ws_attn)
 
     def prepare(self, k_idx):
         """Set-up outside a timed step: the decoder group's pool comes from a

@@ -27,6 +27,12 @@ packed from the same bf16 keys on the GPU before timing:
   encoder64k_fp4k    the 64K shapes.
   decode1m_fp4k      the 1M shapes, Full + 3 Reindex + 1 Reuse.
 
+With both of the pages' cache precisions (FP4 indexer K and FP8 window KV,
+528 B per row, packed from the same kind of bf16 rows on the GPU before
+timing):
+
+  encoder64k_fp4k_fp8w, decode1m_fp4k_fp8w.
+
 Layer groups that share one cache (eogee.com report 3.2: an encoder cache
 serves a Full layer and the Reuse layers after it; a decoder cache serves a
 Reindex layer and Reuse layers), timed as layer sequences:
@@ -65,6 +71,10 @@ CONFIGS = {
                             planted=8, prefill=False, kfmt="fp4"),
     "decode1m_fp4k": dict(nq=8, N=1048576, q_per_seq=1, hier=True, seed=8, kv="clustered", kidx="clustered",
                           planted=0, prefill=False, kfmt="fp4"),
+    "encoder64k_fp4k_fp8w": dict(nq=64, N=32768, q_per_seq=1, hier=False, seed=9, kv="random", kidx="normal",
+                                 planted=8, prefill=False, kfmt="fp4", swa_fmt="fp8"),
+    "decode1m_fp4k_fp8w": dict(nq=8, N=1048576, q_per_seq=1, hier=True, seed=10, kv="clustered", kidx="clustered",
+                               planted=0, prefill=False, kfmt="fp4", swa_fmt="fp8"),
 }
 
 # Norm given to a planted main-KV row before packing: about twice the RMS norm
@@ -110,6 +120,7 @@ class Workload:
     swa_T: int
     group: str = None  # None, "encoder" (Full + 5 Reuse) or "decoder" (Reindex + 3 Reuse)
     kfmt: str = "bf16"  # indexer-K cache precision the step reads: "bf16" or "fp4" (68 B entries)
+    swa_fmt: str = "bf16"  # window-KV precision the step reads: "bf16" or "fp8" (528 B rows)
     q_idx: list = field(default_factory=list)  # per indexer layer: bf16 [nq,32,128]
     w: list = field(default_factory=list)  # per indexer layer: f32 [nq,32]
     k_idx: torch.Tensor = None  # bf16 [nseq,N,128]
@@ -181,7 +192,8 @@ def make_workload(name, device="cpu", seed=None, nq=None, N=None):
     q_per_seq = nq if c["prefill"] else c["q_per_seq"]
     nseq = nq // q_per_seq
     swa_T = (nq + WINDOW - 1) if c["prefill"] else WINDOW
-    wl = Workload(name, nq, N, q_per_seq, nseq, c["hier"], swa_T, c.get("group"), c.get("kfmt", "bf16"))
+    wl = Workload(name, nq, N, q_per_seq, nseq, c["hier"], swa_T, c.get("group"), c.get("kfmt", "bf16"),
+                  c.get("swa_fmt", "bf16"))
     s = 0
 
     def nxt():

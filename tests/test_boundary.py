@@ -50,6 +50,8 @@ def _err(rc):
 def test_pack_rejects(args, frag):
     rc, msg = _err(K.load().fp4_kv_pack(*args))
     assert rc == L.CSA2_EINVAL and frag in msg
+    rc, msg = _err(K.load().swa_fp8_pack(*args))
+    assert rc == L.CSA2_EINVAL and frag in msg and msg.startswith("swa_fp8_pack")
 
 
 @pytest.mark.parametrize("kw,frag", [
@@ -153,3 +155,8 @@ def test_attn_rejects(kw, frag, code):
                                              a["T"], a["start"], a["len_"], a["scale"], P, None, a["ws"], a["wsb"],
                                              S))
     assert rc == code and frag in msg, msg
+    # the FP8-window variant checks the same arguments
+    rc, msg = _err(K.load().csa2_sparse_attn_fp8w(P, P, a["N"], a["nq"], a["q_per_seq"], a["idx"], a["k"], a["swa"],
+                                                  a["T"], a["start"], a["len_"], a["scale"], P, None, a["ws"],
+                                                  a["wsb"], S))
+    assert rc == code and frag in msg and msg.startswith("csa2_sparse_attn_fp8w"), msg

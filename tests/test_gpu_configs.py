@@ -13,7 +13,8 @@ Samples: every query of the tiny and 64K workloads, the queries of 2
 sequences at 256K and 1M, 64 strided queries of the prefill chunk. The FP4
 indexer-K workloads also check the GPU's packed entries of the sampled
 sequences against the oracle's packing byte for byte, and score with the
-oracle's own entries.
+oracle's own entries; the FP8 window workloads do the same for every
+attention layer's window rows.
 """
 import math
 
@@ -30,11 +31,11 @@ SCALE = 1.0 / math.sqrt(512.0)
 
 
 def _sample(wl):
-    if wl.name in ("tiny", "encoder64k", "encoder_group64k", "encoder64k_fp4k"):
+    if wl.name in ("tiny", "encoder64k", "encoder_group64k", "encoder64k_fp4k", "encoder64k_fp4k_fp8w"):
         return list(range(wl.nq))
     if wl.name == "prefill128k":
         return list(range(0, wl.nq, wl.nq // 64))
-    return [0, wl.nq - 1] if wl.name in ("decode1m", "decode1m_fp4k") else [0, 17]
+    return [0, wl.nq - 1] if wl.name.startswith("decode1m") else [0, 17]
 
 
 def _overlap(a, b):
@@ -81,7 +82,8 @@ def _kv_for(qsub_seq, kvrows, N):
 
 
 @pytest.mark.parametrize("name", ["tiny", "encoder64k", "decoder256k", "prefill128k", "decode1m",
-                                  "encoder_group64k", "decoder_group256k", "encoder64k_fp4k", "decode1m_fp4k"])
+                                  "encoder_group64k", "decoder_group256k", "encoder64k_fp4k", "decode1m_fp4k",
+                                  "encoder64k_fp4k_fp8w", "decode1m_fp4k_fp8w"])
 def test_workload_parity(name):
     import kv_cache_compression_csa2_amd as K
     from kv_cache_compression_csa2_amd.pipeline import Step, pack_workload_kv, workload_kidx
@@ -186,13 +188,25 @@ def test_workload_parity(name):
     kv_o = _kv_for(seqs, kvrows, wl.N)
     kv_g = kv[torch.tensor(seqs, device=DEV, dtype=torch.long)].contiguous()
     swa_rows = None
+    fp8w = wl.swa_fmt == "fp8"
     for layer, li in enumerate(attn_idx):
         swa_l = wl.swa[layer][torch.tensor(seqs, device=DEV, dtype=torch.long)].contiguous()
         st, sl = np_(wl.swa_start[qt]), np_(wl.swa_len[qt])
-        ro, rl = O.sparse_attn(u16(wl.q[layer][qt]), kv_o, wl.N, qps_sub, li, u16(swa_l), swa_l.shape[1], st, sl,
-                               SCALE)
-        go, gl = K.csa2_sparse_attn(wl.q[layer][qt].contiguous(), kv_g, wl.N, qps_sub, dev_i32(li, DEV), swa_l,
-                                    dev_i32(st, DEV), dev_i32(sl, DEV))
+        if fp8w:
+            # the oracle packs the window rows itself; the pipeline's FP8 rows
+            # must be the same bytes
+            T = swa_l.shape[1]
+            w8o = O.swa_fp8_pack(u16(swa_l).reshape(-1, 512)).reshape(len(seqs), T, 528)
+            w8g = step.swa8[layer][torch.tensor(seqs, device=DEV, dtype=torch.long)].contiguous()
+            assert np.array_equal(np_(w8g), w8o)
+            ro, rl = O.sparse_attn(u16(wl.q[layer][qt]), kv_o, wl.N, qps_sub, li, None, T, st, sl, SCALE, swa_fp8=w8o)
+            go, gl = K.csa2_sparse_attn(wl.q[layer][qt].contiguous(), kv_g, wl.N, qps_sub, dev_i32(li, DEV), None,
+                                        dev_i32(st, DEV), dev_i32(sl, DEV), swa_fp8=w8g)
+        else:
+            ro, rl = O.sparse_attn(u16(wl.q[layer][qt]), kv_o, wl.N, qps_sub, li, u16(swa_l), swa_l.shape[1], st,
+                                   sl, SCALE)
+            go, gl = K.csa2_sparse_attn(wl.q[layer][qt].contiguous(), kv_g, wl.N, qps_sub, dev_i32(li, DEV), swa_l,
+                                        dev_i32(st, DEV), dev_i32(sl, DEV))
         torch.cuda.synchronize()
         err = np.abs(bf16_bits_to_f64(u16(go)) - ro).max()
         assert err <= 1e-2 * np.abs(ro).max(), (layer, err, np.abs(ro).max())

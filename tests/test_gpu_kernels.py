@@ -379,6 +379,75 @@ def test_sparse_attn_decode_exact():
     assert torch.equal(out2, swa.expand(nrec, 64, 512))
 
 
+def _fp8_rows(n, seed):
+    """bf16 window rows spanning several binades, zero blocks and saturating blocks."""
+    g = _g(seed)
+    x = torch.randn((n, 512), generator=g, device=DEV)
+    x = x * torch.exp2(torch.randint(-20, 20, (n, 1), generator=g, device=DEV).float())
+    x[: n // 8, 64:96] = 0.0                      # an all-zero block
+    x[n // 8: n // 4, 0] = 3.99 * x[n // 8: n // 4, 1:32].abs().amax(1)  # block max near 2^(k+1): saturation
+    return x.to(torch.bfloat16)
+
+
+def test_swa_fp8_pack_bit_exact():
+    print("case: swa fp8 pack", flush=True)
+    x = _fp8_rows(777, 41)
+    got = K().swa_fp8_pack(x)
+    torch.cuda.synchronize()
+    assert np.array_equal(np_(got), O.swa_fp8_pack(u16(x)))
+    assert K().swa_fp8_pack(torch.empty((0, 512), dtype=torch.bfloat16, device=DEV)).shape == (0, 528)
+
+
+@pytest.mark.parametrize("nq,N,k,pad,qps", [(3, 2000, 512, 7, 1), (40, 3000, 512, 3, 1), (2, 700, 100, 0, 1),
+                                            (64, 600, 512, 0, 64)])
+def test_sparse_attn_fp8_window_matches_oracle(nq, N, k, pad, qps):
+    print("case: attn fp8 window", nq, N, k, pad, qps, flush=True)
+    T = 128 if qps == 1 else nq + 127
+    q, kv, idx, swa, st, sl = _attn_case(nq, N, k, qps, 300 + nq, T=T, pad=pad)
+    if qps > 1:
+        st = np.arange(nq, dtype=np.int32)
+        sl = np.full(nq, 128, np.int32)
+        sl[:3] = [0, 1, 33]
+    w8 = K().swa_fp8_pack(swa.reshape(-1, 512).contiguous()).view(nq // qps, T, 528)
+    torch.cuda.synchronize()
+    w8o = O.swa_fp8_pack(u16(swa).reshape(-1, 512)).reshape(nq // qps, T, 528)
+    assert np.array_equal(np_(w8), w8o)
+    out, lse = K().csa2_sparse_attn(q, kv, N, qps, dev_i32(idx, DEV), None, dev_i32(st, DEV), dev_i32(sl, DEV),
+                                    swa_fp8=w8)
+    torch.cuda.synchronize()
+    ro, rl = O.sparse_attn(u16(q), np_(kv), N, qps, idx, None, T, st, sl, SCALE, swa_fp8=w8o)
+    got = bf16_bits_to_f64(u16(out))
+    err = np.abs(got - ro).max()
+    assert err <= 1e-2 * np.abs(ro).max(), (err, np.abs(ro).max())
+    glse = np_(lse).astype(np.float64)
+    fin = np.isfinite(rl)
+    assert np.array_equal(fin, np.isfinite(glse))
+    assert np.allclose(glse[fin], rl[fin], rtol=1e-3, atol=2e-3)
+
+
+def test_sparse_attn_fp8_window_decode_exact():
+    """A query attending to one FP8 window row outputs that row's decoded
+    values exactly (block maxima within [2^-7, 2^16))."""
+    print("case: attn fp8 window exact", flush=True)
+    nq = 8
+    x = torch.randn((nq, 512), generator=_g(43), device=DEV)
+    x = (x.view(nq, 16, 32) * torch.exp2(torch.randint(-6, 14, (nq, 16, 1), generator=_g(44), device=DEV).float())
+         ).view(nq, 512).to(torch.bfloat16)
+    w8 = K().swa_fp8_pack(x).view(nq, 1, 528)
+    torch.cuda.synchronize()
+    want = O.swa_fp8_unpack(np_(w8).reshape(nq, 528))
+    q = _bf16((nq, 64, 512), 45)
+    kv = _records(nq * 4, 46).view(nq, 4, 288)
+    none = torch.full((nq, 1), -1, dtype=torch.int32, device=DEV)
+    st = torch.zeros((nq,), dtype=torch.int32, device=DEV)
+    sl = torch.ones((nq,), dtype=torch.int32, device=DEV)
+    out, _ = K().csa2_sparse_attn(q, kv, 4, 1, none, None, st, sl, swa_fp8=w8)
+    torch.cuda.synchronize()
+    got = bf16_bits_to_f64(u16(out))
+    for r in range(nq):
+        assert np.array_equal(got[r], np.broadcast_to(want[r], (64, 512))), r
+
+
 def test_sparse_attn_deterministic():
     print("case: attn determinism", flush=True)
     q, kv, idx, swa, st, sl = _attn_case(16, 4000, 512, 1, 11)
