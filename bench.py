@@ -17,6 +17,10 @@ A step is one pass of the whole hot path over one batch of synthetic input:
       timing;
   encoder64k_fp4k_fp8w / decode1m_fp4k_fp8w : the same with the window KV
       as FP8 rows (528 B) as well: both of the pages' cache precisions.
+In every decode step (one query per sequence) the Full layer's scoring and
+Top-512 run fused (csa2_index_topk: scoring with a per-chunk Top-512 in one
+launch, the chunks' merge in a second; no score row is written); the prefill
+chunk scores and selects in two calls.
 The headline is decode queries/s on encoder64k (64 queries, 64K-token context
 at m=2 = 32768 FP4 entries per sequence). Inputs live in HBM before timing and
 two independent input sets alternate between steps, so the 256 MB last-level
@@ -51,6 +55,26 @@ def alg_bytes_index_full(wl):
     kbytes = (wl.N * row * wl.nseq) if wl.q_per_seq > 1 else n_vis * row
     out = wl.nq * wl.N * 4 + (wl.nq * ((wl.N + 7) // 8) * 4 if wl.hier else 0)
     return kbytes + out + wl.nq * (32 * 128 * 2 + 32 * 4)
+
+
+def fused_chunks(nq, N):
+    """Chunks per query of csa2_index_topk: 8192 entries, or 4096 when 8192
+    would leave fewer than 256 workgroups (the rule in the fused kernel's
+    launcher)."""
+    c = 4096 if nq * ((N + 8191) // 8192) < 256 else 8192
+    return (N + c - 1) // c
+
+
+def alg_bytes_index_topk(wl, k=512):
+    """Fused scoring + per-chunk Top-k (the select launch): K_idx rows read
+    once per query, queries and weights read, each chunk's k candidates
+    written (4 B key + 4 B id; the final ids when a row is one chunk), block
+    maxima written for the hierarchical pool."""
+    n_vis = wl.N * wl.nq if wl.n_visible is None else int(wl.n_visible.sum().item())
+    row = 68 if wl.kfmt == "fp4" else 256
+    c = fused_chunks(wl.nq, wl.N)
+    out = wl.nq * k * (8 * c if c > 1 else 4) + (wl.nq * ((wl.N + 7) // 8) * 4 if wl.hier else 0)
+    return n_vis * row + out + wl.nq * (32 * 128 * 2 + 32 * 4)
 
 
 def alg_flops_index_full(wl):
@@ -142,6 +166,11 @@ def bench_workload(name, steps, warmup, nsets, torch):
         t_idx = calls["index_full"][0] * 1e-3
         res["index_full_GBps"] = alg_bytes_index_full(wl) / t_idx / 1e9
         res["index_full_TFLOPs"] = alg_flops_index_full(wl) / t_idx / 1e12
+    if "index_topk" in calls:
+        t_idx = calls["index_topk"][0] * 1e-3
+        res["index_topk_GBps"] = alg_bytes_index_topk(wl) / t_idx / 1e9
+        res["index_topk_TFLOPs"] = alg_flops_index_full(wl) / t_idx / 1e12
+        res["_alg_bytes_index_topk"] = alg_bytes_index_topk(wl)
     t_att = calls["attn"][0] * 1e-3
     res["attn_GBps"] = alg_bytes_attn(wl.nq, window_row=528 if wl.swa_fmt == "fp8" else 1024) / t_att / 1e9
     res["attn_TFLOPs"] = alg_flops_attn(wl.nq) / t_att / 1e12
@@ -242,7 +271,7 @@ def traffic_from_profiles(kernel_src):
     """HBM bytes per launch of the dominant kernel from the committed rocprofv3
     counter summary (FETCH_SIZE + WRITE_SIZE, calibrated on a 1 GiB copy), if it
     was taken on the current kernel source; else None."""
-    path = os.path.join(ROOT, "profiles", "index_stream_encoder64k_traffic.md")
+    path = os.path.join(ROOT, "profiles", "index_topk_encoder64k_traffic.md")
     if not os.path.exists(path):
         return None
     fields = {}
@@ -296,13 +325,16 @@ def main():
         print("bench: attention gather nq=%d ..." % nq, file=sys.stderr, flush=True)
         sweep[str(nq)] = bench_attn_gather(nq, torch)
     h = res[HEADLINE]
-    t_idx_s = h["calls_ms"]["index_full"] * 1e-3
-    achieved = h["_alg_bytes_index_full"] / t_idx_s / 1e9
+    # dominant kernel: the fused Full-layer scoring + per-chunk Top-512
+    # (index_topk_kernel, the select launch of csa2_index_topk; one launch per
+    # "index_topk" span)
+    t_idx_s = h["calls_ms"]["index_topk"] * 1e-3
+    achieved = h["_alg_bytes_index_topk"] / t_idx_s / 1e9
     src = os.path.join(ROOT, "kv_cache_compression_csa2_amd", "csrc", "index.hip")
-    roofline = {"kernel": "index_stream_kernel<Full> (csa2_index_full)", "bound": "hbm",
-                "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+    roofline = {"kernel": "index_topk_kernel (csa2_index_topk_select: Full scoring + per-chunk Top-512)",
+                "bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
                 "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": traffic_from_profiles(src),
-                "alg_bytes_per_launch": h["_alg_bytes_index_full"]}
+                "alg_bytes_per_launch": h["_alg_bytes_index_topk"]}
     cpu = None
     if not args.no_cpu:
         print("bench: cpu oracle baseline ...", file=sys.stderr, flush=True)

@@ -179,6 +179,47 @@ int csa2_index_reindex_fp4k(const uint16_t* q_idx, const float* w, const uint8_t
                             int32_t block_size, float* pool_scores, int32_t* pool_ids, hipStream_t stream);
 
 /*
+ * csa2_index_topk -- Full-mode scoring fused with the per-query Top-K, for
+ * decode (one query per sequence): the Top-k of csa2_index_full's score row
+ * without writing that row (titansim blog: each Full layer keeps its own
+ * Top-512; eogee.com report 3.5 names a fused Top-K selection kernel).
+ *   q_idx, w, k_idx, N, n_visible: as csa2_index_full with q_per_seq = 1
+ *           (k_idx [nq][N][128], sequence q belongs to query q).
+ *   k       1 .. CSA2_MAX_TOPK; the chunks' candidates must fit two merge
+ *           levels of 16384 (for k = 512: N up to 4,194,304), else EINVAL.
+ *   top_idx [nq][k] int32 out: exactly csa2_topk(scores, k, row_len =
+ *           n_visible) of the row csa2_index_full would produce: ascending
+ *           entry ids, then -1 padding; order of merit score desc, equal
+ *           scores (-0 == +0) by lower entry id.
+ *   block_size 0 or 8; with 8, block_scores [nq][ceil(N/8)] fp32 out as in
+ *           csa2_index_full (the hierarchical pool's input).
+ *   scores  [nq][N] fp32 out or NULL: the score row itself (checking aid).
+ *   workspace / ws_bytes: at least csa2_index_topk_workspace_bytes(nq, N, k)
+ *           bytes (per-chunk candidates); may be NULL when that is 0.
+ *           Contents on entry do not matter.
+ * The call is two launches on `stream`: scoring with a per-chunk Top-k (a
+ * query's row is cut into chunks of 4096 or 8192 entries; with one chunk the
+ * result is final), then the merge of the chunks' candidates. The two halves
+ * are also exported on their own: csa2_index_topk_select (k_is_fp4 selects
+ * the key format) leaves the candidates in the workspace, and
+ * csa2_index_topk_merge, called next on the same stream with the same
+ * (N, nq, k, top_idx, workspace), completes top_idx.
+ */
+size_t csa2_index_topk_workspace_bytes(int32_t nq, int64_t N, int32_t k);
+int csa2_index_topk(const uint16_t* q_idx, const float* w, const uint16_t* k_idx, int64_t N, int32_t nq,
+                    const int32_t* n_visible, int32_t k, int32_t* top_idx, int32_t block_size, float* block_scores,
+                    float* scores, void* workspace, size_t ws_bytes, hipStream_t stream);
+/* csa2_index_topk over FP4 indexer-K entries (k_fp4 [nq][N][68], kidx_fp4_pack). */
+int csa2_index_topk_fp4k(const uint16_t* q_idx, const float* w, const uint8_t* k_fp4, int64_t N, int32_t nq,
+                         const int32_t* n_visible, int32_t k, int32_t* top_idx, int32_t block_size,
+                         float* block_scores, float* scores, void* workspace, size_t ws_bytes, hipStream_t stream);
+int csa2_index_topk_select(const uint16_t* q_idx, const float* w, const void* k, int32_t k_is_fp4, int64_t N,
+                           int32_t nq, const int32_t* n_visible, int32_t topk, int32_t* top_idx, int32_t block_size,
+                           float* block_scores, float* scores, void* workspace, size_t ws_bytes, hipStream_t stream);
+int csa2_index_topk_merge(int64_t N, int32_t nq, int32_t k, int32_t* top_idx, void* workspace, size_t ws_bytes,
+                          hipStream_t stream);
+
+/*
  * csa2_topk -- per-row Top-K selection (titansim blog, CSA2 modes: Top-512;
  * eogee.com report 3.3: Top-2048 blocks).
  *   scores  [rows][ld] fp32, columns [0, ncols) are candidates.

@@ -46,6 +46,12 @@ def load():
     L.csa2_index_full_fp4k.argtypes = [vp, vp, vp, i64, i32, i32, vp, vp, i32, vp, vp]
     L.csa2_index_reindex_fp4k.argtypes = [vp, vp, vp, i64, i32, i32, vp, vp, i32, i32, vp, vp, vp]
     L.swa_fp8_pack.argtypes = [vp, i64, vp, vp]
+    L.csa2_index_topk_workspace_bytes.argtypes = [i32, i64, i32]
+    L.csa2_index_topk_workspace_bytes.restype = sz
+    L.csa2_index_topk.argtypes = [vp, vp, vp, i64, i32, vp, i32, vp, i32, vp, vp, vp, sz, vp]
+    L.csa2_index_topk_fp4k.argtypes = [vp, vp, vp, i64, i32, vp, i32, vp, i32, vp, vp, vp, sz, vp]
+    L.csa2_index_topk_select.argtypes = [vp, vp, vp, i32, i64, i32, vp, i32, vp, i32, vp, vp, vp, sz, vp]
+    L.csa2_index_topk_merge.argtypes = [i64, i32, i32, vp, vp, sz, vp]
     L.csa2_topk_workspace_bytes.argtypes = [i32, i64, i32]
     L.csa2_topk_workspace_bytes.restype = sz
     L.csa2_topk.argtypes = [vp, i32, i64, i64, vp, i32, vp, vp, vp, sz, vp]
@@ -55,7 +61,8 @@ def load():
     L.csa2_sparse_attn_fp8w.argtypes = [vp, vp, i64, i32, i32, vp, i32, vp, i64, vp, vp, f32, vp, vp, vp, sz, vp]
     for name in ["fp4_kv_pack", "fp4_kv_unpack", "csa2_index_full", "csa2_index_reindex", "csa2_topk",
                  "csa2_sparse_attn", "kidx_fp4_pack", "csa2_index_full_fp4k", "csa2_index_reindex_fp4k",
-                 "swa_fp8_pack", "csa2_sparse_attn_fp8w"]:
+                 "swa_fp8_pack", "csa2_sparse_attn_fp8w", "csa2_index_topk", "csa2_index_topk_fp4k",
+                 "csa2_index_topk_select", "csa2_index_topk_merge"]:
         getattr(L, name).restype = ctypes.c_int
     _lib = L
     return L
@@ -64,7 +71,8 @@ def load():
 EXPORTS = ["csa2_format_version", "csa2_last_error", "fp4_kv_pack", "fp4_kv_unpack", "csa2_index_full",
            "csa2_index_reindex", "csa2_topk_workspace_bytes", "csa2_topk", "csa2_sparse_attn_workspace_bytes",
            "csa2_sparse_attn", "kidx_fp4_pack", "csa2_index_full_fp4k", "csa2_index_reindex_fp4k", "swa_fp8_pack",
-           "csa2_sparse_attn_fp8w"]
+           "csa2_sparse_attn_fp8w", "csa2_index_topk_workspace_bytes", "csa2_index_topk", "csa2_index_topk_fp4k",
+           "csa2_index_topk_select", "csa2_index_topk_merge"]
 
 
 def _ptr(t):
@@ -170,6 +178,47 @@ def csa2_index_full(q_idx, w, k_idx, N, q_per_seq, n_visible=None, block_size=0,
     _check(fn(_ptr(q_idx), _ptr(w), kp, N, nq, q_per_seq, _ptr(n_visible), _ptr(scores), block_size,
               _ptr(block_scores) if block_size else None, _stream(stream)), "csa2_index_full" + suffix)
     return (scores, block_scores) if block_size else scores
+
+
+def csa2_index_topk_workspace_bytes(nq, N, k):
+    return load().csa2_index_topk_workspace_bytes(nq, N, k)
+
+
+def csa2_index_topk(q_idx, w, k_idx, N, k, n_visible=None, block_size=0, top=None, block_scores=None,
+                    scores=None, workspace=None, stream=None, k_fp4=None, stage="both"):
+    """Full-mode scores fused with Top-k (decode, one query per sequence):
+    int32 [nq,k] (and block maxima [nq,ceil(N/8)] when block_size == 8).
+    `scores` [nq,N] fp32, when given, also receives the score rows.
+    stage: "both" (complete), "select" (scoring + per-chunk selection, the
+    candidates stay in `workspace`) or "merge" (completes a "select" call
+    with the same top/workspace; the other inputs are ignored)."""
+    for t, dt, nm in [(q_idx, torch.bfloat16, "q_idx"), (w, torch.float32, "w"), (n_visible, torch.int32, "n_visible"),
+                      (scores, torch.float32, "scores")]:
+        _need(t, dt, nm)
+    kp, suffix = _k_args(k_idx, k_fp4)
+    nq = q_idx.shape[0]
+    dev = q_idx.device
+    if top is None:
+        top = torch.empty((nq, k), dtype=torch.int32, device=dev)
+    if block_size and block_scores is None:
+        block_scores = torch.empty((nq, (N + 7) // 8), dtype=torch.float32, device=dev)
+    need = csa2_index_topk_workspace_bytes(nq, N, k)
+    if workspace is None and need:
+        workspace = torch.empty((need,), dtype=torch.uint8, device=dev)
+    wsb = workspace.numel() * workspace.element_size() if workspace is not None else 0
+    if stage == "merge":
+        _check(load().csa2_index_topk_merge(N, nq, k, _ptr(top), _ptr(workspace), wsb, _stream(stream)),
+               "csa2_index_topk_merge")
+        return top
+    args = (N, nq, _ptr(n_visible), k, _ptr(top), block_size, _ptr(block_scores) if block_size else None,
+            _ptr(scores), _ptr(workspace), wsb, _stream(stream))
+    if stage == "select":
+        _check(load().csa2_index_topk_select(_ptr(q_idx), _ptr(w), kp, 1 if suffix else 0, *args),
+               "csa2_index_topk_select")
+    else:
+        fn = getattr(load(), "csa2_index_topk" + suffix)
+        _check(fn(_ptr(q_idx), _ptr(w), kp, *args), "csa2_index_topk" + suffix)
+    return (top, block_scores) if block_size else top
 
 
 def csa2_index_reindex(q_idx, w, k_idx, N, q_per_seq, cand_blocks, n_visible=None, block_size=8, pool_scores=None,

@@ -119,6 +119,72 @@ int csa2_index_reindex_fp4k(const uint16_t* q_idx, const float* w, const uint8_t
                               cand_blocks, nb, block_size, pool_scores, pool_ids, stream);
 }
 
+size_t csa2_index_topk_workspace_bytes(int32_t nq, int64_t N, int32_t k) {
+    if (nq <= 0 || N < 1 || N > kMaxN || k < 1 || k > CSA2_MAX_TOPK) return 0;
+    return csa2::index_topk_workspace_bytes(nq, N, k);
+}
+
+static int index_topk_impl(const char* who, bool merge, const uint16_t* q_idx, const float* w, const void* kc,
+                           bool kfp4, int64_t N, int32_t nq, const int32_t* n_visible, int32_t k, int32_t* top_idx,
+                           int32_t block_size, float* block_scores, float* scores, void* workspace, size_t ws_bytes,
+                           hipStream_t stream) {
+    int rc = check_index_common(who, q_idx, w, kc, N, nq, 1);
+    if (rc) return rc;
+    if (k < 1 || k > CSA2_MAX_TOPK) return fail(CSA2_EINVAL, "%s: k must be in [1, %d]", who, CSA2_MAX_TOPK);
+    if (!csa2::index_topk_fits(nq, N, k))
+        return fail(CSA2_EINVAL, "%s: N too large for this k (use csa2_index_full and csa2_topk)", who);
+    if (nq > 0 && !top_idx) return fail(CSA2_EINVAL, "%s: null top_idx", who);
+    if (block_size != 0 && block_size != 8) return fail(CSA2_EINVAL, "%s: block_size must be 0 or 8", who);
+    if (block_size == 8 && nq > 0 && !block_scores)
+        return fail(CSA2_EINVAL, "%s: block_scores required when block_size == 8", who);
+    const size_t need = csa2_index_topk_workspace_bytes(nq, N, k);
+    if (nq > 0 && need > 0 && (!workspace || ws_bytes < need))
+        return fail(CSA2_EWORKSPACE, "%s: workspace needs %zu bytes", who, need);
+    (void)hipGetLastError();
+    csa2::launch_index_topk(q_idx, w, kc, kfp4, N, nq, n_visible, k, top_idx, block_size ? block_scores : nullptr,
+                            scores, workspace, stream);
+    if (merge) csa2::launch_index_topk_merge(N, nq, k, top_idx, workspace, stream);
+    return launched(who);
+}
+
+int csa2_index_topk(const uint16_t* q_idx, const float* w, const uint16_t* k_idx, int64_t N, int32_t nq,
+                    const int32_t* n_visible, int32_t k, int32_t* top_idx, int32_t block_size, float* block_scores,
+                    float* scores, void* workspace, size_t ws_bytes, hipStream_t stream) {
+    return index_topk_impl("csa2_index_topk", true, q_idx, w, k_idx, false, N, nq, n_visible, k, top_idx,
+                           block_size, block_scores, scores, workspace, ws_bytes, stream);
+}
+
+int csa2_index_topk_fp4k(const uint16_t* q_idx, const float* w, const uint8_t* k_fp4, int64_t N, int32_t nq,
+                         const int32_t* n_visible, int32_t k, int32_t* top_idx, int32_t block_size,
+                         float* block_scores, float* scores, void* workspace, size_t ws_bytes, hipStream_t stream) {
+    return index_topk_impl("csa2_index_topk_fp4k", true, q_idx, w, k_fp4, true, N, nq, n_visible, k, top_idx,
+                           block_size, block_scores, scores, workspace, ws_bytes, stream);
+}
+
+int csa2_index_topk_select(const uint16_t* q_idx, const float* w, const void* k, int32_t k_is_fp4, int64_t N,
+                           int32_t nq, const int32_t* n_visible, int32_t topk, int32_t* top_idx, int32_t block_size,
+                           float* block_scores, float* scores, void* workspace, size_t ws_bytes, hipStream_t stream) {
+    return index_topk_impl("csa2_index_topk_select", false, q_idx, w, k, k_is_fp4 != 0, N, nq, n_visible, topk,
+                           top_idx, block_size, block_scores, scores, workspace, ws_bytes, stream);
+}
+
+int csa2_index_topk_merge(int64_t N, int32_t nq, int32_t k, int32_t* top_idx, void* workspace, size_t ws_bytes,
+                          hipStream_t stream) {
+    if (nq < 0) return fail(CSA2_EINVAL, "csa2_index_topk_merge: nq < 0");
+    if (N < 1 || N > kMaxN) return fail(CSA2_EINVAL, "csa2_index_topk_merge: N must be in [1, 2^31-1]");
+    if (k < 1 || k > CSA2_MAX_TOPK)
+        return fail(CSA2_EINVAL, "csa2_index_topk_merge: k must be in [1, %d]", CSA2_MAX_TOPK);
+    if (!csa2::index_topk_fits(nq, N, k))
+        return fail(CSA2_EINVAL, "csa2_index_topk_merge: N too large for this k");
+    if (nq > 0 && !top_idx) return fail(CSA2_EINVAL, "csa2_index_topk_merge: null top_idx");
+    const size_t need = csa2_index_topk_workspace_bytes(nq, N, k);
+    if (nq > 0 && need > 0 && (!workspace || ws_bytes < need))
+        return fail(CSA2_EWORKSPACE, "csa2_index_topk_merge: workspace needs %zu bytes", need);
+    (void)hipGetLastError();
+    csa2::launch_index_topk_merge(N, nq, k, top_idx, workspace, stream);
+    return launched("csa2_index_topk_merge");
+}
+
 int kidx_fp4_pack(const uint16_t* x_bf16, int64_t n, uint8_t* out, hipStream_t stream) {
     if (n < 0) return fail(CSA2_EINVAL, "kidx_fp4_pack: n < 0");
     if (n > 0 && (!x_bf16 || !out)) return fail(CSA2_EINVAL, "kidx_fp4_pack: null pointer");

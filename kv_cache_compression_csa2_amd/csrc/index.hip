@@ -25,6 +25,7 @@
 
 #include "device_common.h"
 #include "launch.h"
+#include "topk_select.h"
 
 namespace csa2 {
 
@@ -67,6 +68,69 @@ CSA2_DEVINL bf16x8 fp4x8_to_bf16(uint32_t w) {
 // Row of the accumulator held in register r by a lane of half `half` (32x32 layout).
 CSA2_DEVINL int acc_row(int r, int half) { return (r >> 2) * 8 + half * 4 + (r & 3); }
 
+// Per-lane state of the streaming kernels: the query's A operand and head
+// weights. A operand: head = lane % 32; step j covers channels 16j + 8*half
+// .. +8 (bf16 K), or 64*half + 8j .. +8 for FP4 K so that a lane's 8 steps
+// read 32 contiguous code bytes of its entry (the same re-ordering on both
+// operands leaves the dot product unchanged).
+template <bool kFp4>
+struct StreamQuery {
+    bf16x8 a[8];
+    float wr[16];
+    CSA2_DEVINL void load(const uint16_t* q_idx, const float* w, int64_t q, int half, int col_in_tile) {
+        const uint16_t* qrow = q_idx + (q * kIdxHeads + col_in_tile) * kIdxDim;
+#pragma unroll
+        for (int j = 0; j < 8; j++)
+            a[j] = as_bf16x8(reinterpret_cast<const uint4*>(qrow)[kFp4 ? 8 * half + j : 2 * j + half]);
+#pragma unroll
+        for (int r = 0; r < 16; r++) wr[r] = w[q * kIdxHeads + acc_row(r, half)];
+    }
+};
+
+// Loads the K data of entry `ent` of one sequence (kseq: bf16 [N][128] or FP4
+// [N][68]) for this lane's half. Plain (cache-allocating) loads: a tile reads
+// 32 B of each of 32 rows per instruction, and the other 7 instructions of the
+// same wave consume the rest of those lines, so the lines must stay in cache
+// between them. An invalid entry reads entry 0 (its score is discarded).
+template <bool kFp4>
+CSA2_DEVINL void stream_load(const void* kseq, int64_t ent, bool valid, int half, StreamTile<kFp4>& st) {
+    st.ent = ent;
+    st.valid = valid;
+    if constexpr (kFp4) {
+        // 68-byte entries are only 4-byte aligned: dword loads
+        const uint8_t* e = static_cast<const uint8_t*>(kseq) + (valid ? ent : 0) * kKRec;
+        const uint32_t* src = reinterpret_cast<const uint32_t*>(e + 32 * half);
+#pragma unroll
+        for (int j = 0; j < 8; j++) st.code[j] = src[j];
+        st.scale = *reinterpret_cast<const float*>(e + 64);
+    } else {
+        const uint4* src =
+            reinterpret_cast<const uint4*>(static_cast<const uint16_t*>(kseq) + (valid ? ent : 0) * kIdxDim) + half;
+#pragma unroll
+        for (int j = 0; j < 8; j++) st.b[j] = as_bf16x8(src[2 * j]);
+    }
+}
+
+// Score of the tile's entry in lanes 0..31 (lanes 32..63 hold a partial sum):
+// the 32-head contraction, ReLU, weights, head sum; -inf for invalid entries.
+template <bool kFp4>
+CSA2_DEVINL float stream_score(const StreamQuery<kFp4>& Q, const StreamTile<kFp4>& st) {
+    f32x16 acc = {};
+#pragma unroll
+    for (int j = 0; j < 8; j++) {
+        if constexpr (kFp4)
+            acc = mfma32x32x16(Q.a[j], fp4x8_to_bf16(st.code[j]), acc);
+        else
+            acc = mfma32x32x16(Q.a[j], st.b[j], acc);
+    }
+    float s = 0.0f;
+#pragma unroll
+    for (int r = 0; r < 16; r++) s = fmaf(Q.wr[r], relu_bits(acc[r]), s);
+    s += from_upper_half(s);  // lanes 0..31 hold the sum over all 32 heads
+    if constexpr (kFp4) s *= st.scale;
+    return st.valid ? s : -INFINITY;
+}
+
 template <bool kReindex, bool kFp4>
 __global__ __launch_bounds__(kStreamThreads) void index_stream_kernel(
     const uint16_t* __restrict__ q_idx, const float* __restrict__ w, const void* __restrict__ k_idx, int64_t N,
@@ -81,71 +145,27 @@ __global__ __launch_bounds__(kStreamThreads) void index_stream_kernel(
     int64_t nv = n_visible ? (int64_t)n_visible[q] : N;
     nv = nv < N ? nv : N;
 
-    // A operand: head = lane % 32; step j covers channels 16j + 8*half .. +8
-    // (bf16 K), or 64*half + 8j .. +8 for FP4 K so that a lane's 8 steps read
-    // 32 contiguous code bytes of its entry (the same re-ordering on both
-    // operands leaves the dot product unchanged).
-    const uint16_t* qrow = q_idx + (q * kIdxHeads + col_in_tile) * kIdxDim;
-    bf16x8 a[8];
-#pragma unroll
-    for (int j = 0; j < 8; j++)
-        a[j] = as_bf16x8(reinterpret_cast<const uint4*>(qrow)[kFp4 ? 8 * half + j : 2 * j + half]);
-    float wr[16];
-#pragma unroll
-    for (int r = 0; r < 16; r++) wr[r] = w[q * kIdxHeads + acc_row(r, half)];
-
-    const uint16_t* kseq = static_cast<const uint16_t*>(k_idx) + (kFp4 ? 0 : seq * N * kIdxDim);
-    const uint8_t* kfseq = static_cast<const uint8_t*>(k_idx) + (kFp4 ? seq * N * kKRec : 0);
+    StreamQuery<kFp4> Q;
+    Q.load(q_idx, w, q, half, col_in_tile);
+    const void* kseq = kFp4 ? static_cast<const void*>(static_cast<const uint8_t*>(k_idx) + seq * N * kKRec)
+                            : static_cast<const void*>(static_cast<const uint16_t*>(k_idx) + seq * N * kIdxDim);
     const int64_t t_begin = chunk * tiles_per_wg;
     const int64_t t_end = (t_begin + tiles_per_wg < ntiles) ? t_begin + tiles_per_wg : ntiles;
     const int64_t nblk = (N + 7) >> 3;
 
     auto load = [&](int64_t t, StreamTile<kFp4>& st) {
         const int64_t col = t * 32 + col_in_tile;
-        int64_t ent;
-        bool valid;
         if (kReindex) {
             const int32_t blk = (col < ncols) ? cand_blocks[q * nb + (col >> 3)] : -1;
-            ent = (int64_t)blk * 8 + (col & 7);
-            valid = blk >= 0 && ent < nv;
+            const int64_t ent = (int64_t)blk * 8 + (col & 7);
+            stream_load<kFp4>(kseq, ent, blk >= 0 && ent < nv, half, st);
         } else {
-            ent = col;
-            valid = col < nv;
-        }
-        st.ent = ent;
-        st.valid = valid;
-        // Plain (cache-allocating) loads: a tile reads 32 B of each of 32 rows per
-        // instruction, and the other 7 instructions of the same wave consume the
-        // rest of those lines, so the lines must stay in cache between them.
-        if constexpr (kFp4) {
-            // 68-byte entries are only 4-byte aligned: dword loads
-            const uint8_t* e = kfseq + (valid ? ent : 0) * kKRec;
-            const uint32_t* src = reinterpret_cast<const uint32_t*>(e + 32 * half);
-#pragma unroll
-            for (int j = 0; j < 8; j++) st.code[j] = src[j];
-            st.scale = *reinterpret_cast<const float*>(e + 64);
-        } else {
-            const uint4* src = reinterpret_cast<const uint4*>(kseq + (valid ? ent : 0) * kIdxDim) + half;
-#pragma unroll
-            for (int j = 0; j < 8; j++) st.b[j] = as_bf16x8(src[2 * j]);
+            stream_load<kFp4>(kseq, col, col < nv, half, st);
         }
     };
 
     auto finish = [&](int64_t t, const StreamTile<kFp4>& st) {
-        f32x16 acc = {};
-#pragma unroll
-        for (int j = 0; j < 8; j++) {
-            if constexpr (kFp4)
-                acc = mfma32x32x16(a[j], fp4x8_to_bf16(st.code[j]), acc);
-            else
-                acc = mfma32x32x16(a[j], st.b[j], acc);
-        }
-        float s = 0.0f;
-#pragma unroll
-        for (int r = 0; r < 16; r++) s = fmaf(wr[r], relu_bits(acc[r]), s);
-        s += from_upper_half(s);  // lanes 0..31 hold the sum over all 32 heads
-        if constexpr (kFp4) s *= st.scale;
-        if (!st.valid) s = -INFINITY;
+        const float s = stream_score<kFp4>(Q, st);
         const int64_t col = t * 32 + col_in_tile;
         if (half == 0 && col < ncols) scores[q * ncols + col] = s;
         if (kReindex) {
@@ -170,6 +190,110 @@ __global__ __launch_bounds__(kStreamThreads) void index_stream_kernel(
         finish(t1, s1);
         if (t2 >= t_end) break;
         t = t2;
+    }
+}
+
+// Full-mode scoring fused with the per-query Top-K (the selection the pages'
+// DeepSelect kernel makes, eogee.com report 3.5; Top-512 per query, titansim
+// blog): a workgroup scores a chunk of kFtChunk entries of one query exactly
+// as index_stream_kernel does, keeps the scores in LDS instead of writing
+// them out, and selects the chunk's top-k as (key, entry) candidates; the
+// Top-K merge then combines a query's chunks. A query's top-k entry is in its
+// chunk's top-k, so the result equals Top-K over the full score row. With one
+// chunk per query the workgroup writes the final indices itself; otherwise
+// the Top-K merge kernels combine the chunks' candidates (a separate launch:
+// making the last workgroup of a query merge in place needs device-scope
+// fences, whose L2 write-back and invalidate cost the streaming workgroups
+// more than the launch, measured 106 -> 159 us at 64 x 32768).
+// Optional outputs: 8-position block maxima (the hierarchical pool's input)
+// and the scores themselves (a debug path for parity checks).
+constexpr int kFtThreads = 512;
+constexpr int kFtWaves = kFtThreads / 64;
+
+template <bool kFp4, int kFtChunk>
+__global__ __launch_bounds__(kFtThreads) void index_topk_kernel(
+    const uint16_t* __restrict__ q_idx, const float* __restrict__ w, const void* __restrict__ k_idx, int64_t N,
+    const int32_t* __restrict__ n_visible, int32_t k, int32_t nchunks, int32_t* __restrict__ out_idx,
+    uint32_t* __restrict__ cand_key, int32_t* __restrict__ cand_col, float* __restrict__ block_scores,
+    float* __restrict__ scores_dbg) {
+    constexpr int kFtKpt = kFtChunk / kFtThreads;  // keys per thread
+    __shared__ __attribute__((aligned(16))) float sc[kFtChunk];
+    __shared__ tk::RegTk<kFtThreads> sh;
+    const int64_t q = blockIdx.x / nchunks;
+    const int chunk = blockIdx.x % nchunks;
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const int half = lane >> 5, col_in_tile = lane & 31;
+    int64_t nv = n_visible ? (int64_t)n_visible[q] : N;
+    nv = nv < N ? nv : N;
+    const int64_t c0 = (int64_t)chunk * kFtChunk;
+    const int n = (int)((N - c0) < kFtChunk ? (N - c0) : kFtChunk);  // entries of this chunk
+    const int ntile = (n + 31) >> 5;
+    const int64_t nblk = (N + 7) >> 3;
+
+    StreamQuery<kFp4> Q;
+    Q.load(q_idx, w, q, half, col_in_tile);
+    const void* kseq = kFp4 ? static_cast<const void*>(static_cast<const uint8_t*>(k_idx) + q * N * kKRec)
+                            : static_cast<const void*>(static_cast<const uint16_t*>(k_idx) + q * N * kIdxDim);
+    auto load = [&](int t, StreamTile<kFp4>& st) {
+        const int64_t col = c0 + t * 32 + col_in_tile;
+        stream_load<kFp4>(kseq, col, col < nv, half, st);
+    };
+    auto finish = [&](int t, const StreamTile<kFp4>& st) {
+        const float s = stream_score<kFp4>(Q, st);
+        const int p = t * 32 + col_in_tile;
+        if (half == 0) sc[p] = s;
+        if (scores_dbg && half == 0 && p < n) scores_dbg[q * N + c0 + p] = s;
+        if (block_scores) {
+            const float m = max8_lanes(s);
+            if (half == 0 && (lane & 7) == 0 && p < n) block_scores[q * nblk + ((c0 + p) >> 3)] = m;
+        }
+    };
+    int t = wave;
+    if (t < ntile) {
+        StreamTile<kFp4> s0, s1;
+        load(t, s0);
+        while (true) {
+            const int t1 = t + kFtWaves;
+            if (t1 < ntile) load(t1, s1);
+            finish(t, s0);
+            if (t1 >= ntile) break;
+            const int t2 = t1 + kFtWaves;
+            if (t2 < ntile) load(t2, s0);
+            finish(t1, s1);
+            if (t2 >= ntile) break;
+            t = t2;
+        }
+    }
+    __syncthreads();
+
+    // the chunk's keys, kFtKpt consecutive positions per thread
+    uint32_t key[kFtKpt];
+    const int p0 = tid * kFtKpt;
+#pragma unroll
+    for (int u = 0; u < kFtKpt; u += 4) {
+        const float4 f = *reinterpret_cast<const float4*>(&sc[p0 + u]);
+        key[u + 0] = (p0 + u + 0 < n) ? tk::score_key(f.x) : 0u;
+        key[u + 1] = (p0 + u + 1 < n) ? tk::score_key(f.y) : 0u;
+        key[u + 2] = (p0 + u + 2 < n) ? tk::score_key(f.z) : 0u;
+        key[u + 3] = (p0 + u + 3 < n) ? tk::score_key(f.w) : 0u;
+    }
+    if (nchunks == 1) {
+        int32_t* out = out_idx + q * k;
+        const uint32_t emitted = tk::reg_select_emit<kFtThreads, kFtKpt, false>(
+            key, (uint32_t)k, sh, [&](uint32_t slot, int u) { out[slot] = (int32_t)(c0 + p0 + u); });
+        for (int i = (int)emitted + tid; i < k; i += kFtThreads) out[i] = -1;
+    } else {
+        uint32_t* ck = cand_key + (q * nchunks + chunk) * (int64_t)k;
+        int32_t* cc = cand_col + (q * nchunks + chunk) * (int64_t)k;
+        const uint32_t emitted =
+            tk::reg_select_emit<kFtThreads, kFtKpt, false>(key, (uint32_t)k, sh, [&](uint32_t slot, int u) {
+                ck[slot] = key[u];
+                cc[slot] = (int32_t)(c0 + p0 + u);
+            });
+        for (int i = (int)emitted + tid; i < k; i += kFtThreads) {
+            ck[i] = 0u;
+            cc[i] = -1;
+        }
     }
 }
 
@@ -393,6 +517,78 @@ int launch_index_full(const uint16_t* q_idx, const float* w, const void* k, bool
         hipLaunchKernelGGL((index_stream_kernel<false, false>), grid, dim3(kStreamThreads), 0, s, q_idx, w, k, N,
                            q_per_seq, n_visible, (const int32_t*)nullptr, 0, scores, bs, (int32_t*)nullptr, N, ntiles,
                            (int32_t)wgs_per_q, (int32_t)tpw);
+    return 0;
+}
+
+// Entries per fused workgroup: 8192, or 4096 when 8192 would leave fewer than
+// 256 workgroups (one per CU). Measured at 64 x 32768 (256 workgroups of
+// 8192): bf16 keys 106 us with 8192 vs 110 with 4096, FP4 keys 45.7 vs 41.0.
+int64_t index_topk_chunk_len(int32_t nq, int64_t N) { return (int64_t)nq * ((N + 8191) / 8192) < 256 ? 4096 : 8192; }
+int32_t index_topk_chunks(int32_t nq, int64_t N) {
+    const int64_t c = index_topk_chunk_len(nq, N);
+    return (int32_t)((N + c - 1) / c);
+}
+
+// The merge takes at most two levels of <= 16384 candidates per row.
+bool index_topk_fits(int32_t nq, int64_t N, int32_t k) {
+    const int32_t c = index_topk_chunks(nq, N);
+    return c <= 1 || (int64_t)topk_merge_groups(c, k) * k <= 16384;
+}
+
+size_t index_topk_workspace_bytes(int32_t nq, int64_t N, int32_t k) {
+    const int32_t c = index_topk_chunks(nq, N);
+    if (c <= 1) return 0;
+    const int32_t g = topk_merge_groups(c, k);
+    return (size_t)nq * k * ((size_t)c + (g > 1 ? (size_t)g : 0)) * (sizeof(uint32_t) + sizeof(int32_t));
+}
+
+// Workspace layout of the fused call: rows x c x k candidate keys, then their
+// entry ids, then (two-level merge only) rows x g x k of each.
+struct FtWs {
+    uint32_t* ck = nullptr;
+    int32_t* cc = nullptr;
+    uint32_t* ck2 = nullptr;
+    int32_t* cc2 = nullptr;
+    int32_t c = 1;
+};
+FtWs ft_ws(void* ws, int32_t nq, int64_t N, int32_t topk) {
+    FtWs r;
+    r.c = index_topk_chunks(nq, N);
+    if (r.c > 1) {
+        r.ck = reinterpret_cast<uint32_t*>(ws);
+        r.cc = reinterpret_cast<int32_t*>(r.ck + (size_t)nq * r.c * topk);
+        const int32_t g = topk_merge_groups(r.c, topk);
+        if (g > 1) {
+            r.ck2 = reinterpret_cast<uint32_t*>(r.cc + (size_t)nq * r.c * topk);
+            r.cc2 = reinterpret_cast<int32_t*>(r.ck2 + (size_t)nq * g * topk);
+        }
+    }
+    return r;
+}
+
+int launch_index_topk(const uint16_t* q_idx, const float* w, const void* k, bool kfp4, int64_t N, int32_t nq,
+                      const int32_t* n_visible, int32_t topk, int32_t* out_idx, float* block_scores,
+                      float* scores_dbg, void* ws, hipStream_t s) {
+    if (nq == 0) return 0;
+    const FtWs f = ft_ws(ws, nq, N, topk);
+    const bool small = index_topk_chunk_len(nq, N) == 4096;
+    const dim3 grid((unsigned)((int64_t)nq * f.c));
+#define CSA2_FT(FP4, CH)                                                                                           \
+    hipLaunchKernelGGL((index_topk_kernel<FP4, CH>), grid, dim3(kFtThreads), 0, s, q_idx, w, k, N, n_visible, topk, \
+                       f.c, out_idx, f.ck, f.cc, block_scores, scores_dbg)
+    if (kfp4) {
+        if (small) CSA2_FT(true, 4096); else CSA2_FT(true, 8192);
+    } else {
+        if (small) CSA2_FT(false, 4096); else CSA2_FT(false, 8192);
+    }
+#undef CSA2_FT
+    return 0;
+}
+
+int launch_index_topk_merge(int64_t N, int32_t nq, int32_t topk, int32_t* out_idx, void* ws, hipStream_t s) {
+    if (nq == 0) return 0;
+    const FtWs f = ft_ws(ws, nq, N, topk);
+    if (f.c > 1) launch_topk_merge(nq, topk, f.c, f.ck, f.cc, out_idx, f.ck2, f.cc2, s);
     return 0;
 }
 

@@ -23,7 +23,25 @@ int launch_index_reindex(const uint16_t* q_idx, const float* w, const void* k, b
                          int32_t q_per_seq, const int32_t* n_visible, const int32_t* cand_blocks, int32_t nb,
                          float* pool_scores, int32_t* pool_ids, hipStream_t s);
 
+// Full-mode scoring fused with Top-K for decode (one query per sequence), in
+// two launches: scoring + per-chunk selection (writes out_idx itself when the
+// row is one chunk), then the merge of the chunks' candidates held in ws.
+// block_scores and scores_dbg optional.
+size_t index_topk_workspace_bytes(int32_t nq, int64_t N, int32_t k);
+bool index_topk_fits(int32_t nq, int64_t N, int32_t k);
+int launch_index_topk(const uint16_t* q_idx, const float* w, const void* k, bool kfp4, int64_t N, int32_t nq,
+                      const int32_t* n_visible, int32_t topk, int32_t* out_idx, float* block_scores,
+                      float* scores_dbg, void* ws, hipStream_t s);
+int launch_index_topk_merge(int64_t N, int32_t nq, int32_t topk, int32_t* out_idx, void* ws, hipStream_t s);
+
 size_t topk_workspace_bytes(int32_t rows, int64_t ncols, int32_t k);
+// Merge of per-chunk Top-K candidates: rows x nchunks x k (key, column) pairs
+// in column order (unused slots key 0) -> out_idx [rows][k]. Above 16384
+// candidates per row a first level merges groups into ck2/cc2
+// (rows x topk_merge_groups(nchunks, k) x k pairs).
+int32_t topk_merge_groups(int32_t nchunks, int32_t k);
+int launch_topk_merge(int32_t rows, int32_t k, int32_t nchunks, const uint32_t* ck, const int32_t* cc,
+                      int32_t* out_idx, uint32_t* ck2, int32_t* cc2, hipStream_t s);
 int launch_topk(const float* scores, int32_t rows, int64_t ncols, int64_t ld, const int32_t* row_len, int32_t k,
                 const int32_t* id_map, int32_t* out_idx, void* ws, hipStream_t s);
 

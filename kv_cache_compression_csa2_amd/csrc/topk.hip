@@ -26,6 +26,7 @@
 
 #include "device_common.h"
 #include "launch.h"
+#include "topk_select.h"
 
 namespace csa2 {
 
@@ -35,12 +36,7 @@ constexpr int kTkThreads = 512;
 constexpr int kTkWaves = kTkThreads / 64;
 constexpr int kHistBins = 2048;
 
-CSA2_DEVINL uint32_t score_key(float f) {
-    uint32_t u = __float_as_uint(f);
-    if (f != f || u == 0xFF800000u) return 0u;
-    if (u == 0x80000000u) u = 0u;
-    return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
-}
+using tk::score_key;
 
 struct TkShared {
     uint32_t hist[kHistBins];
@@ -273,186 +269,11 @@ __global__ __launch_bounds__(kTkThreads) void topk_merge_kernel(int64_t ld, int3
 
 // ------------------------------------------------------------- register path
 
-constexpr int kRegMaxKpt = 32;        // keys per thread
-constexpr int kRegMaxKeys = 1024 * kRegMaxKpt;  // 32768 per chunk
-constexpr int kRegMaxCand = 16384;    // merge capacity per row
-
-// Histograms of the three radix digits (key bits 31..20, 19..10, 9..0), all
-// cleared once at the start.
-template <int NT>
-struct RegTk {
-    uint32_t h1[4096];
-    uint32_t h2[1024];
-    uint32_t h3[1024];
-    uint32_t wsum[NT / 64];
-    uint32_t sel_bin, sel_above, total;
-};
-
-// Inclusive prefix sum over the 64 lanes with DPP: row_shr 1, 2, 4, 8 within
-// each 16-lane row, then row_bcast15 / row_bcast31 carry row totals forward.
-CSA2_DEVINL uint32_t wave_incl_scan(uint32_t x) {
-    x += (uint32_t)__builtin_amdgcn_update_dpp(0, (int)x, 0x111, 0xF, 0xF, false);
-    x += (uint32_t)__builtin_amdgcn_update_dpp(0, (int)x, 0x112, 0xF, 0xF, false);
-    x += (uint32_t)__builtin_amdgcn_update_dpp(0, (int)x, 0x114, 0xF, 0xF, false);
-    x += (uint32_t)__builtin_amdgcn_update_dpp(0, (int)x, 0x118, 0xF, 0xF, false);
-    x += (uint32_t)__builtin_amdgcn_update_dpp(0, (int)x, 0x142, 0xA, 0xF, false);
-    x += (uint32_t)__builtin_amdgcn_update_dpp(0, (int)x, 0x143, 0xC, 0xF, false);
-    return x;
-}
-
-// Exclusive scan over the block in thread order (one barrier); *total = sum.
-// wsum must not be rewritten until every thread has returned (the callers
-// place a barrier in between).
-template <int NT>
-CSA2_DEVINL uint32_t reg_block_scan(uint32_t v, uint32_t* wsum, uint32_t* total) {
-    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-    const uint32_t x = wave_incl_scan(v);
-    if (lane == 63) wsum[wave] = x;
-    __syncthreads();
-    uint32_t before = 0, tot = 0;
-#pragma unroll
-    for (int i = 0; i < NT / 64; i++) {
-        const uint32_t sw = wsum[i];
-        before += (i < wave) ? sw : 0u;
-        tot += sw;
-    }
-    *total = tot;
-    return before + x - v;
-}
-
-// From histogram h of nbins bins, finds the bin holding the rem-th largest
-// counted key, counting from the top bin: sets sh.sel_bin and sh.sel_above
-// (keys in higher bins). rem == 0 means rem = min(k, all counted keys), which
-// is also stored in sh.total. Two barriers; the results are readable after.
-template <int NT>
-CSA2_DEVINL void reg_pick_bin(const uint32_t* h, RegTk<NT>& sh, int nbins, uint32_t rem, uint32_t k) {
-    constexpr int kMaxPer = 4096 / NT;
-    const int tid = threadIdx.x;
-    const int per = nbins / NT;
-    uint32_t c[kMaxPer], loc = 0;
-#pragma unroll
-    for (int j = 0; j < kMaxPer; j++) {
-        c[j] = (j < per) ? h[nbins - 1 - (tid * per + j)] : 0u;
-        loc += c[j];
-    }
-    uint32_t tot;
-    uint32_t above = reg_block_scan<NT>(loc, sh.wsum, &tot);
-    if (rem == 0) {
-        rem = tot < k ? tot : k;
-        if (tid == 0) sh.total = rem;
-    }
-    if (above < rem && rem <= above + loc) {
-        for (int j = 0; j < per; j++) {
-            if (above + c[j] >= rem) {
-                sh.sel_bin = nbins - 1 - (tid * per + j);
-                sh.sel_above = above;
-                break;
-            }
-            above += c[j];
-        }
-    }
-    __syncthreads();
-}
-
-// Exact selection over the keys held in registers (thread t holds positions
-// t*KPT .. t*KPT+KPT-1 of the segment; key 0 = never selected): a 3-pass MSB
-// radix select (12, 10, 10 bits) over LDS histograms finds the k-th largest
-// key T, then emit(slot, u) is called for every key > T and for the first
-// `need` keys == T, slots ascending with position (one packed block scan of
-// the per-thread counts). Returns the number selected, min(k, #nonzero keys).
-//
-// kNarrow (used for merged candidates, whose values sit in a narrow band at
-// the top of the row): the first digit ends at the highest bit where the
-// largest and smallest key differ -- every key shares the bits above it -- so
-// the first histogram spreads instead of piling into a few bins. The three
-// digits then cover bits [0, s1 + 12); s1 <= 20 always.
-template <int NT, int KPT, bool kNarrow, class Emit>
-CSA2_DEVINL uint32_t reg_select_emit(const uint32_t (&key)[KPT], uint32_t k, RegTk<NT>& sh, Emit emit) {
-    const int tid = threadIdx.x;
-    for (int i = tid; i < 4096; i += NT) sh.h1[i] = 0;
-    for (int i = tid; i < 1024; i += NT) sh.h2[i] = 0;
-    int s1 = 20;        // digit 1 = key bits [s1, s1 + 12)
-    uint32_t high = 0;  // bits >= s1 + 12, shared by every nonzero key
-    if (kNarrow) {
-        uint32_t mx = 0u, mn = 0xFFFFFFFFu;
-#pragma unroll
-        for (int u = 0; u < KPT; u++) {
-            mx = max(mx, key[u]);
-            if (key[u]) mn = min(mn, key[u]);
-        }
-#pragma unroll
-        for (int o = 32; o > 0; o >>= 1) {
-            mx = max(mx, (uint32_t)__shfl_xor((int)mx, o));
-            mn = min(mn, (uint32_t)__shfl_xor((int)mn, o));
-        }
-        if ((tid & 63) == 0) {
-            sh.h3[tid >> 6] = mx;
-            sh.h3[512 + (tid >> 6)] = mn;
-        }
-        __syncthreads();
-        uint32_t bmax = 0u, bmin = 0xFFFFFFFFu;
-#pragma unroll
-        for (int i = 0; i < NT / 64; i++) {
-            bmax = max(bmax, sh.h3[i]);
-            bmin = min(bmin, sh.h3[512 + i]);
-        }
-        if (bmax != 0u) {
-            const int h = bmax > bmin ? 31 - __builtin_clz(bmax ^ bmin) : 0;  // highest differing bit
-            s1 = h >= 31 ? 20 : (h >= 11 ? h - 11 : 0);
-            high = (s1 + 12 < 32) ? (bmax & ~((1u << (s1 + 12)) - 1u)) : 0u;
-        }
-        __syncthreads();  // every thread has read h3 before it is cleared
-    }
-    for (int i = tid; i < 1024; i += NT) sh.h3[i] = 0;
-    const int s2 = s1 >= 10 ? s1 - 10 : 0;  // digit 2 = bits [s2, s1)
-    const int s3 = s2 >= 10 ? s2 - 10 : 0;  // digit 3 = bits [s3, s2); s3 == 0
-    const uint32_t m2 = (1u << (s1 - s2)) - 1u, m3 = (1u << (s2 - s3)) - 1u;
-    __syncthreads();
-#pragma unroll
-    for (int u = 0; u < KPT; u++)
-        if (key[u]) atomicAdd(&sh.h1[(key[u] >> s1) & 4095u], 1u);
-    __syncthreads();
-    reg_pick_bin<NT>(sh.h1, sh, 4096, 0u, k);
-    const uint32_t kk = sh.total;
-    if (kk == 0) return 0;
-    uint32_t prefix = sh.sel_bin, rem = kk - sh.sel_above;  // T's bits [s1, s1 + 12)
-#pragma unroll
-    for (int u = 0; u < KPT; u++)
-        if (key[u] && ((key[u] >> s1) & 4095u) == prefix) atomicAdd(&sh.h2[(key[u] >> s2) & m2], 1u);
-    __syncthreads();
-    reg_pick_bin<NT>(sh.h2, sh, 1024, rem, k);
-    prefix = (prefix << (s1 - s2)) | sh.sel_bin;  // bits [s2, s1 + 12)
-    rem -= sh.sel_above;
-    const uint32_t m12 = (1u << (12 + s1 - s2)) - 1u;
-#pragma unroll
-    for (int u = 0; u < KPT; u++)
-        if (key[u] && ((key[u] >> s2) & m12) == prefix) atomicAdd(&sh.h3[(key[u] >> s3) & m3], 1u);
-    __syncthreads();
-    reg_pick_bin<NT>(sh.h3, sh, 1024, rem, k);
-    const uint32_t T = high | (((prefix << (s2 - s3)) | sh.sel_bin) << s3);
-    const uint32_t need = rem - sh.sel_above;
-
-    uint32_t gt = 0, eq = 0;
-#pragma unroll
-    for (int u = 0; u < KPT; u++) {
-        gt += key[u] > T;
-        eq += key[u] == T;
-    }
-    uint32_t tot;
-    const uint32_t before = reg_block_scan<NT>((gt << 16) | eq, sh.wsum, &tot);
-    const uint32_t gt_before = before >> 16, eq_before = before & 0xFFFFu;
-    uint32_t slot = gt_before + (eq_before < need ? eq_before : need);
-    uint32_t eq_run = eq_before;
-#pragma unroll
-    for (int u = 0; u < KPT; u++) {
-        const bool is_eq = key[u] == T;
-        const bool sel = key[u] > T || (is_eq && eq_run < need);
-        eq_run += is_eq;
-        if (sel && slot < kk) emit(slot, u);  // slot < kk always holds; the check keeps stores in bounds regardless
-        slot += sel;
-    }
-    return kk;
-}
+using tk::RegTk;
+using tk::reg_select_emit;
+using tk::kRegMaxKpt;
+using tk::kRegMaxKeys;
+using tk::kRegMaxCand;
 
 // Loads KPT consecutive scores of this thread (positions tid*KPT..) as keys;
 // positions >= n give key 0.
@@ -567,6 +388,44 @@ __global__ __launch_bounds__(NT) void topk_reg_merge_kernel(int64_t ld, int32_t 
     for (int t = (int)emitted + tid; t < k; t += NT) out[t] = -1;
 }
 
+// One level of a two-level merge: workgroup (row, g) selects the top-k of
+// chunks [g*cpg, min((g+1)*cpg, nchunks)) of the row's nchunks*k candidates
+// and writes them as k candidates of group g (column order kept; unused slots
+// key 0, column -1).
+template <int NT, int KPT>
+__global__ __launch_bounds__(NT) void topk_reg_group_merge_kernel(int32_t k, int32_t nchunks, int32_t cpg,
+                                                                   const uint32_t* __restrict__ cand_key,
+                                                                   const int32_t* __restrict__ cand_col,
+                                                                   uint32_t* __restrict__ out_key,
+                                                                   int32_t* __restrict__ out_col) {
+    __shared__ RegTk<NT> sh;
+    const int tid = threadIdx.x;
+    const int ngroups = (nchunks + cpg - 1) / cpg;
+    const int64_t row = blockIdx.x / ngroups;
+    const int g = blockIdx.x % ngroups;
+    const int c_end = (g + 1) * cpg < nchunks ? (g + 1) * cpg : nchunks;
+    const int n = (c_end - g * cpg) * k;
+    const int64_t base = (row * nchunks + (int64_t)g * cpg) * k;
+    const int p0 = tid * KPT;
+    uint32_t key[KPT];
+    int32_t col[KPT];
+#pragma unroll
+    for (int u = 0; u < KPT; u++) {
+        key[u] = (p0 + u < n) ? cand_key[base + p0 + u] : 0u;
+        col[u] = (p0 + u < n) ? cand_col[base + p0 + u] : -1;
+    }
+    uint32_t* ok = out_key + (row * ngroups + g) * (int64_t)k;
+    int32_t* oc = out_col + (row * ngroups + g) * (int64_t)k;
+    const uint32_t emitted = reg_select_emit<NT, KPT, true>(key, (uint32_t)k, sh, [&](uint32_t slot, int u) {
+        ok[slot] = key[u];
+        oc[slot] = col[u];
+    });
+    for (int t = (int)emitted + tid; t < k; t += NT) {
+        ok[t] = 0u;
+        oc[t] = -1;
+    }
+}
+
 // Chunks per row on the register path; 0 = the shape needs the global-memory path.
 int32_t topk_reg_chunks(int32_t rows, int64_t ncols, int32_t k) {
     // chunks of <= 16384 keys (16 per thread: two workgroups fit a CU) unless
@@ -617,7 +476,66 @@ int32_t topk_chunks(int32_t rows, int64_t ncols, int32_t k) {
     return (int32_t)c;
 }
 
+// Launches the final merge of rows x c x k candidates (the register merge
+// kernel sized for c * k <= kRegMaxCand).
+void launch_reg_merge_any(int32_t rows, int32_t k, int32_t c, const int32_t* id_map, int64_t ld, const uint32_t* ck,
+                          const int32_t* cc, int32_t* out_idx, hipStream_t s) {
+    const dim3 g2((unsigned)rows);
+    const RegShape m = reg_shape((int64_t)c * k);
+#define CSA2_MERGE(NT, KPT) launch_reg_merge<NT, KPT>(g2, s, ld, k, c, id_map, ck, cc, out_idx)
+    if (m.nt == 256) {
+        switch (m.kpt) {
+            case 1: CSA2_MERGE(256, 1); break;
+            case 2: CSA2_MERGE(256, 2); break;
+            case 4: CSA2_MERGE(256, 4); break;
+            default: CSA2_MERGE(256, 8); break;
+        }
+    } else {
+        switch (m.kpt) {
+            case 1: case 2: case 4: CSA2_MERGE(1024, 4); break;
+            case 8: CSA2_MERGE(1024, 8); break;
+            default: CSA2_MERGE(1024, 16); break;
+        }
+    }
+#undef CSA2_MERGE
+}
+
 }  // namespace
+
+// Two-level merges use groups of up to 8192 candidates (half the merge
+// capacity): twice the workgroups of the first level, each with half the
+// keys (measured at 8 x 128 chunks x 512: 35.9 us with 16384-candidate groups).
+constexpr int kGroupCand = kRegMaxCand / 2;
+
+int32_t topk_merge_groups(int32_t nchunks, int32_t k) {
+    if ((int64_t)nchunks * k <= kRegMaxCand) return 1;
+    const int32_t cpg = k <= kGroupCand ? kGroupCand / k : 1;
+    return (nchunks + cpg - 1) / cpg;
+}
+
+int launch_topk_merge(int32_t rows, int32_t k, int32_t nchunks, const uint32_t* ck, const int32_t* cc,
+                      int32_t* out_idx, uint32_t* ck2, int32_t* cc2, hipStream_t s) {
+    if (rows == 0) return 0;
+    const int32_t ng = topk_merge_groups(nchunks, k);
+    if (ng == 1) {
+        launch_reg_merge_any(rows, k, nchunks, nullptr, 0, ck, cc, out_idx, s);
+        return 0;
+    }
+    const int32_t cpg = k <= kGroupCand ? kGroupCand / k : 1;
+    const RegShape m = reg_shape((int64_t)cpg * k);
+    const dim3 g1((unsigned)((int64_t)rows * ng));
+    if (m.nt == 256)
+        hipLaunchKernelGGL((topk_reg_group_merge_kernel<256, 8>), g1, dim3(256), 0, s, k, nchunks, cpg, ck, cc, ck2,
+                           cc2);
+    else if (m.kpt <= 8)
+        hipLaunchKernelGGL((topk_reg_group_merge_kernel<1024, 8>), g1, dim3(1024), 0, s, k, nchunks, cpg, ck, cc, ck2,
+                           cc2);
+    else
+        hipLaunchKernelGGL((topk_reg_group_merge_kernel<1024, 16>), g1, dim3(1024), 0, s, k, nchunks, cpg, ck, cc,
+                           ck2, cc2);
+    launch_reg_merge_any(rows, k, ng, nullptr, 0, ck2, cc2, out_idx, s);
+    return 0;
+}
 
 size_t topk_workspace_bytes(int32_t rows, int64_t ncols, int32_t k) {
     int32_t c = topk_reg_chunks(rows, ncols, k);
@@ -658,26 +576,7 @@ int launch_topk(const float* scores, int32_t rows, int64_t ncols, int64_t ld, co
             }
         }
 #undef CSA2_CHUNK
-        if (c > 1) {
-            const dim3 g2((unsigned)rows);
-            const RegShape m = reg_shape((int64_t)c * k);
-#define CSA2_MERGE(NT, KPT) launch_reg_merge<NT, KPT>(g2, s, ld, k, c, id_map, ck, cc, out_idx)
-            if (m.nt == 256) {
-                switch (m.kpt) {
-                    case 1: CSA2_MERGE(256, 1); break;
-                    case 2: CSA2_MERGE(256, 2); break;
-                    case 4: CSA2_MERGE(256, 4); break;
-                    default: CSA2_MERGE(256, 8); break;
-                }
-            } else {
-                switch (m.kpt) {
-                    case 1: case 2: case 4: CSA2_MERGE(1024, 4); break;
-                    case 8: CSA2_MERGE(1024, 8); break;
-                    default: CSA2_MERGE(1024, 16); break;
-                }
-            }
-#undef CSA2_MERGE
-        }
+        if (c > 1) launch_reg_merge_any(rows, k, c, id_map, ld, ck, cc, out_idx, s);
         return 0;
     }
     hipLaunchKernelGGL(topk_chunk_kernel, dim3((unsigned)((int64_t)rows * c)), dim3(kTkThreads), 0, s, scores, ncols,

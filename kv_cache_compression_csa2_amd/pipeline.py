@@ -8,6 +8,12 @@ Layer modes (titansim blog, CSA2 paragraph; eogee.com report 3.2 and 3.3):
   Reuse    attends with the indices of the previous layer, no scoring.
 Every layer attends with its own Q and its own window KV.
 
+Decode workloads (one query per sequence) run the Full layer's scoring and
+Top-512 fused (csa2_index_topk: no score row is written; its two launches are
+timed separately); the prefill chunk scores with csa2_index_full and selects
+with csa2_topk. `debug_scores` makes the fused call also write the score rows
+(parity checks).
+
 Buffers are allocated once per Step object, so a timed loop allocates nothing.
 """
 import torch
@@ -40,6 +46,9 @@ class Step:
                               L.csa2_topk_workspace_bytes(nq, (N + 7) // 8, POOL_BLOCKS) if wl.hier else 0,
                               L.csa2_topk_workspace_bytes(nq, pool, TOPK) if wl.hier else 0))
         self.ws_attn = ws(L.csa2_sparse_attn_workspace_bytes(nq, TOPK))
+        self.fused = wl.q_per_seq == 1
+        self.ws_ft = ws(L.csa2_index_topk_workspace_bytes(nq, N, TOPK)) if self.fused else None
+        self.debug_scores = False
         # FP8 window rows (the cache format; packed once, outside any timed step)
         self.swa8 = None
         if wl.swa_fmt == "fp8":
@@ -60,6 +69,32 @@ class Step:
                               self.blocks, k_fp4=kf)
         else:
             L.csa2_index_full(wl.q_idx[0], wl.w[0], kb, wl.N, wl.q_per_seq, wl.n_visible, 0, self.scores, k_fp4=kf)
+
+    def index_topk(self, k, stage):
+        wl = self.wl
+        kb, kf = self._k(k)
+        L.csa2_index_topk(wl.q_idx[0], wl.w[0], kb, wl.N, TOPK, n_visible=wl.n_visible, block_size=8 if wl.hier else 0,
+                          top=self.top[0], block_scores=self.blocks, scores=self.scores if self.debug_scores else None,
+                          workspace=self.ws_ft, k_fp4=kf, stage=stage)
+
+    def topk_blocks(self):
+        L.csa2_topk(self.blocks, POOL_BLOCKS, out=self.cand, workspace=self.ws_topk)
+
+    def full_layer(self, k, sp):
+        """The Full layer's scoring and Top-512 (+ the 2048-block pool)."""
+        if self.fused:
+            with sp("index_topk"):
+                self.index_topk(k, "select")
+            with sp("topk_merge"):
+                self.index_topk(k, "merge")
+            if self.wl.hier:
+                with sp("topk_blocks"):
+                    self.topk_blocks()
+        else:
+            with sp("index_full"):
+                self.index_full(k)
+            with sp("topk_full"):
+                self.topk_full()
 
     def topk_full(self):
         wl = self.wl
@@ -88,8 +123,8 @@ class Step:
         """Set-up outside a timed step: the decoder group's pool comes from a
         Full layer of another group."""
         if self.wl.group == "decoder":
-            self.index_full(k_idx)
-            self.topk_full()
+            import contextlib
+            self.full_layer(k_idx, lambda n: contextlib.nullcontext())
 
     def run(self, k_idx, kv, span=None):
         """The whole hot path once, layer by layer: the Full layer (not for the
@@ -100,10 +135,7 @@ class Step:
         sp = span or (lambda n: contextlib.nullcontext())
         wl = self.wl
         if wl.group != "decoder":
-            with sp("index_full"):
-                self.index_full(k_idx)
-            with sp("topk_full"):
-                self.topk_full()
+            self.full_layer(k_idx, sp)
         done = {0} if wl.group != "decoder" else set()
         for layer, src in enumerate(wl.attn_src):
             if src not in done:

@@ -124,6 +124,45 @@ def test_topk_rejects(kw, frag, code):
     assert rc == code and frag in msg, msg
 
 
+@pytest.mark.parametrize("kw,frag,code", [
+    (dict(k=0), "k must be", L.CSA2_EINVAL),
+    (dict(k=4097), "k must be", L.CSA2_EINVAL),
+    (dict(N=0), "N must be", L.CSA2_EINVAL),
+    (dict(N=5_000_000), "too large", L.CSA2_EINVAL),          # 611 chunks of 8192: beyond two merge levels at k=512
+    (dict(N=70000, k=4096), "too large", L.CSA2_EINVAL),
+    (dict(top=None), "null top_idx", L.CSA2_EINVAL),
+    (dict(block_size=4), "block_size", L.CSA2_EINVAL),
+    (dict(block_size=8, block=None), "block_scores", L.CSA2_EINVAL),
+    (dict(ws=None), "workspace", L.CSA2_EWORKSPACE),
+    (dict(wsb=8), "workspace", L.CSA2_EWORKSPACE),
+])
+def test_index_topk_rejects(kw, frag, code):
+    a = dict(N=40000, nq=4, k=512, top=P, block_size=0, block=P, ws=P, wsb=1 << 40)
+    a.update(kw)
+    L_ = K.load()
+    for name, fn in [("csa2_index_topk", L_.csa2_index_topk), ("csa2_index_topk_fp4k", L_.csa2_index_topk_fp4k)]:
+        rc, msg = _err(fn(P, P, P, a["N"], a["nq"], None, a["k"], a["top"], a["block_size"], a["block"], None,
+                          a["ws"], a["wsb"], S))
+        assert rc == code and frag in msg and msg.startswith(name), msg
+    rc, msg = _err(L_.csa2_index_topk_select(P, P, P, 1, a["N"], a["nq"], None, a["k"], a["top"], a["block_size"],
+                                            a["block"], None, a["ws"], a["wsb"], S))
+    assert rc == code and frag in msg, msg
+    if "block" not in frag:
+        rc, msg = _err(L_.csa2_index_topk_merge(a["N"], a["nq"], a["k"], a["top"], a["ws"], a["wsb"], S))
+        assert rc == code and frag in msg, msg
+
+
+def test_index_topk_workspace_sizes():
+    # 64 x 32768: chunks of 8192 (256 workgroups), candidates (key + id) of every chunk
+    assert K.csa2_index_topk_workspace_bytes(64, 32768, 512) == 64 * 4 * 512 * 8
+    # 8 x 2^20: 128 chunks, two merge levels of 16-chunk groups (8 groups)
+    assert K.csa2_index_topk_workspace_bytes(8, 1 << 20, 512) == 8 * 512 * (128 + 8) * 8
+    # one chunk per query: no workspace
+    assert K.csa2_index_topk_workspace_bytes(64, 4096, 512) == 0
+    # few queries: chunks of 4096
+    assert K.csa2_index_topk_workspace_bytes(2, 20000, 512) == 2 * 5 * 512 * 8
+
+
 def test_workspace_sizes():
     assert K.csa2_topk_workspace_bytes(4096, 16384, 512) == 0  # many rows, one 16384-key chunk: one pass per row
     # longer rows: chunks of <= 16384 keys, candidates of every chunk (key + column)

@@ -94,6 +94,7 @@ def test_workload_parity(name):
     kk = workload_kidx(wl)
     fp4k = wl.kfmt == "fp4"
     step = Step(wl, DEV)
+    step.debug_scores = True  # decode steps score and select fused: keep the score rows for step 1
     step.prepare(kk)
     step.run(kk, kv)
     torch.cuda.synchronize()
@@ -134,6 +135,11 @@ def test_workload_parity(name):
                         row_len=None if nv is None else dev_i32(nv, DEV))
     torch.cuda.synchronize()
     assert np.array_equal(np_(top_g), top_o)
+    if step.fused:
+        # the fused selection is exactly Top-K of the row it scored
+        own = K.csa2_topk(step.scores, 512, row_len=wl.n_visible)
+        torch.cuda.synchronize()
+        assert torch.equal(own, step.top[0])
     ov = _overlap(np_(step.top[0][qt]), top_o)
     print("  top-512 overlap mean %.5f min %.5f" % (ov.mean(), ov.min()), flush=True)
     assert ov.mean() >= 0.995

@@ -169,6 +169,67 @@ def test_index_reindex_fp4k_matches_oracle():
     assert np.array_equal(np_(pid), pool_vis)
 
 
+# ------------------------------------------------------ fused scoring + Top-K
+
+def _int_idx_inputs(nq, N, seed):
+    """Small-integer queries and keys and power-of-two weights: every score is
+    an exact fp32 value whatever the summation order, with many ties."""
+    g = _g(seed)
+    q = torch.randint(-2, 3, (nq, 32, 128), generator=g, device=DEV).to(torch.bfloat16)
+    w = torch.exp2(torch.randint(-2, 2, (nq, 32), generator=g, device=DEV).float())
+    k = torch.randint(-2, 3, (nq, N, 128), generator=g, device=DEV).to(torch.bfloat16)
+    return q, w, k
+
+
+@pytest.mark.parametrize("nq,N,k,fp4", [(3, 20000, 512, False), (2, 8192, 512, False), (4, 1000, 512, False),
+                                        (2, 70000, 2048, False), (3, 20000, 100, False), (3, 20000, 512, True),
+                                        (2, 70000, 2048, True)])
+def test_index_topk_bit_exact_on_exact_scores(nq, N, k, fp4):
+    """With exact scores the fused selection must equal the oracle's Top-K of
+    the oracle's score row, ties included (one chunk, several chunks, a
+    ragged tail, the two-level merge at 70000 x 2048, FP4 keys)."""
+    print("case: index_topk exact", nq, N, k, fp4, flush=True)
+    q, w, kb = _int_idx_inputs(nq, N, 500 + N + k)
+    nv = np.array([N, N // 3, 0, 7][:nq], np.int32)
+    nvd = dev_i32(nv, DEV)
+    if fp4:
+        kf_host = O.kidx_fp4_pack(u16(kb)).reshape(nq, N, 68)
+        kf = torch.tensor(kf_host, device=DEV)
+        top, blk = K().csa2_index_topk(q, w, None, N, k, n_visible=nvd, block_size=8, k_fp4=kf)
+        rs, rb = O.index_full(u16(q), np_(w), None, N, 1, n_visible=nv, block_size=8, k_fp4=kf_host)
+    else:
+        top, blk = K().csa2_index_topk(q, w, kb, N, k, n_visible=nvd, block_size=8)
+        rs, rb = O.index_full(u16(q), np_(w), u16(kb), N, 1, n_visible=nv, block_size=8)
+    torch.cuda.synchronize()
+    assert np.array_equal(np_(blk), rb)
+    assert np.array_equal(np_(top), O.topk(rs, k, row_len=nv))
+
+
+def test_index_topk_matches_oracle_and_the_unfused_path():
+    print("case: index_topk random", flush=True)
+    nq, N, k = 4, 33000, 512
+    q, w, kb = _idx_inputs(nq, N, nq, 600)
+    nv = np.array([N, 30000, 513, 20], np.int32)
+    nvd = dev_i32(nv, DEV)
+    sc = torch.empty((nq, N), dtype=torch.float32, device=DEV)
+    top = K().csa2_index_topk(q, w, kb, N, k, n_visible=nvd, scores=sc)
+    s_ref = K().csa2_index_full(q, w, kb, N, 1, n_visible=nvd)
+    t_ref = K().csa2_topk(s_ref, k, row_len=nvd)
+    torch.cuda.synchronize()
+    # the debug scores are the unfused kernel's, and so is the selection
+    assert torch.equal(sc, s_ref)
+    assert torch.equal(top, t_ref)
+    # against the oracle: scores within 1e-3 relative, selections overlap
+    rs = O.index_full(u16(q), np_(w), u16(kb), N, 1, n_visible=nv)
+    ok, msg = rel_close(np_(sc), rs)
+    assert ok, msg
+    to = O.topk(rs, k, row_len=nv)
+    for r in range(nq):
+        a = set(np_(top[r]).tolist()) - {-1}
+        b = set(to[r].tolist()) - {-1}
+        assert len(a & b) >= 0.995 * len(b)
+
+
 # ------------------------------------------------------------------ indexer
 
 def _idx_inputs(nq, N, nseq, seed):
