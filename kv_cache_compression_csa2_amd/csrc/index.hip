@@ -207,15 +207,13 @@ __global__ __launch_bounds__(kStreamThreads) void index_stream_kernel(
 // more than the launch, measured 106 -> 159 us at 64 x 32768).
 // Optional outputs: 8-position block maxima (the hierarchical pool's input)
 // and the scores themselves (a debug path for parity checks).
-constexpr int kFtThreads = 512;
-constexpr int kFtWaves = kFtThreads / 64;
-
-template <bool kFp4, int kFtChunk>
+template <bool kFp4, int kFtThreads, int kFtChunk>
 __global__ __launch_bounds__(kFtThreads) void index_topk_kernel(
     const uint16_t* __restrict__ q_idx, const float* __restrict__ w, const void* __restrict__ k_idx, int64_t N,
     const int32_t* __restrict__ n_visible, int32_t k, int32_t nchunks, int32_t* __restrict__ out_idx,
     uint32_t* __restrict__ cand_key, int32_t* __restrict__ cand_col, float* __restrict__ block_scores,
     float* __restrict__ scores_dbg) {
+    constexpr int kFtWaves = kFtThreads / 64;
     constexpr int kFtKpt = kFtChunk / kFtThreads;  // keys per thread
     __shared__ __attribute__((aligned(16))) float sc[kFtChunk];
     __shared__ tk::RegTk<kFtThreads> sh;
@@ -521,9 +519,12 @@ int launch_index_full(const uint16_t* q_idx, const float* w, const void* k, bool
 }
 
 // Entries per fused workgroup: 8192, or 4096 when 8192 would leave fewer than
-// 256 workgroups (one per CU). Measured at 64 x 32768 (256 workgroups of
-// 8192): bf16 keys 106 us with 8192 vs 110 with 4096, FP4 keys 45.7 vs 41.0.
-int64_t index_topk_chunk_len(int32_t nq, int64_t N) { return (int64_t)nq * ((N + 8191) / 8192) < 256 ? 4096 : 8192; }
+// 512 workgroups; 256 threads for bf16 keys, 512 for FP4 keys (compute-
+// heavier per byte). Measured select + merge (64 x 32K / 32 x 256K / 8 x 1M,
+// us): bf16 with 256 threads 105 / 397 / 404 against 106 / 415 / 423 with
+// 512 threads and 8192 entries; FP4 at 64 x 32K 43 with (512, 4096), 48 with
+// (256, 4096), 47 with (512, 8192).
+int64_t index_topk_chunk_len(int32_t nq, int64_t N) { return (int64_t)nq * ((N + 8191) / 8192) < 512 ? 4096 : 8192; }
 int32_t index_topk_chunks(int32_t nq, int64_t N) {
     const int64_t c = index_topk_chunk_len(nq, N);
     return (int32_t)((N + c - 1) / c);
@@ -573,13 +574,13 @@ int launch_index_topk(const uint16_t* q_idx, const float* w, const void* k, bool
     const FtWs f = ft_ws(ws, nq, N, topk);
     const bool small = index_topk_chunk_len(nq, N) == 4096;
     const dim3 grid((unsigned)((int64_t)nq * f.c));
-#define CSA2_FT(FP4, CH)                                                                                           \
-    hipLaunchKernelGGL((index_topk_kernel<FP4, CH>), grid, dim3(kFtThreads), 0, s, q_idx, w, k, N, n_visible, topk, \
+#define CSA2_FT(FP4, NT, CH)                                                                                    \
+    hipLaunchKernelGGL((index_topk_kernel<FP4, NT, CH>), grid, dim3(NT), 0, s, q_idx, w, k, N, n_visible, topk,   \
                        f.c, out_idx, f.ck, f.cc, block_scores, scores_dbg)
     if (kfp4) {
-        if (small) CSA2_FT(true, 4096); else CSA2_FT(true, 8192);
+        if (small) CSA2_FT(true, 512, 4096); else CSA2_FT(true, 512, 8192);
     } else {
-        if (small) CSA2_FT(false, 4096); else CSA2_FT(false, 8192);
+        if (small) CSA2_FT(false, 256, 4096); else CSA2_FT(false, 256, 8192);
     }
 #undef CSA2_FT
     return 0;

@@ -153,8 +153,8 @@ def test_index_topk_rejects(kw, frag, code):
 
 
 def test_index_topk_workspace_sizes():
-    # 64 x 32768: chunks of 8192 (256 workgroups), candidates (key + id) of every chunk
-    assert K.csa2_index_topk_workspace_bytes(64, 32768, 512) == 64 * 4 * 512 * 8
+    # 64 x 32768: chunks of 4096 (8192 would give only 256 workgroups), candidates (key + id) of every chunk
+    assert K.csa2_index_topk_workspace_bytes(64, 32768, 512) == 64 * 8 * 512 * 8
     # 8 x 2^20: 128 chunks, two merge levels of 16-chunk groups (8 groups)
     assert K.csa2_index_topk_workspace_bytes(8, 1 << 20, 512) == 8 * 512 * (128 + 8) * 8
     # one chunk per query: no workspace
