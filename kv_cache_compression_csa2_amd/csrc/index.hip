@@ -277,14 +277,14 @@ __global__ __launch_bounds__(kFtThreads) void index_topk_kernel(
     }
     if (nchunks == 1) {
         int32_t* out = out_idx + q * k;
-        const uint32_t emitted = tk::reg_select_emit<kFtThreads, kFtKpt, false>(
+        const uint32_t emitted = tk::reg_select_emit<kFtThreads, kFtKpt, true>(
             key, (uint32_t)k, sh, [&](uint32_t slot, int u) { out[slot] = (int32_t)(c0 + p0 + u); });
         for (int i = (int)emitted + tid; i < k; i += kFtThreads) out[i] = -1;
     } else {
         uint32_t* ck = cand_key + (q * nchunks + chunk) * (int64_t)k;
         int32_t* cc = cand_col + (q * nchunks + chunk) * (int64_t)k;
         const uint32_t emitted =
-            tk::reg_select_emit<kFtThreads, kFtKpt, false>(key, (uint32_t)k, sh, [&](uint32_t slot, int u) {
+            tk::reg_select_emit<kFtThreads, kFtKpt, true>(key, (uint32_t)k, sh, [&](uint32_t slot, int u) {
                 ck[slot] = key[u];
                 cc[slot] = (int32_t)(c0 + p0 + u);
             });

@@ -321,7 +321,7 @@ __global__ __launch_bounds__(NT) void topk_reg_chunk_kernel(
     if (nchunks == 1) {
         int32_t* out = out_idx + row * k;
         const int32_t* map = id_map ? id_map + row * ld : nullptr;
-        emitted = reg_select_emit<NT, KPT, false>(key, (uint32_t)k, sh, [&](uint32_t slot, int u) {
+        emitted = reg_select_emit<NT, KPT, true>(key, (uint32_t)k, sh, [&](uint32_t slot, int u) {
             const int64_t col = c0 + p0 + u;
             out[slot] = map ? map[col] : (int32_t)col;
         });
@@ -329,7 +329,7 @@ __global__ __launch_bounds__(NT) void topk_reg_chunk_kernel(
     } else {
         uint32_t* ck = cand_key + (row * nchunks + chunk) * k;
         int32_t* cc = cand_col + (row * nchunks + chunk) * k;
-        emitted = reg_select_emit<NT, KPT, false>(key, (uint32_t)k, sh, [&](uint32_t slot, int u) {
+        emitted = reg_select_emit<NT, KPT, true>(key, (uint32_t)k, sh, [&](uint32_t slot, int u) {
             ck[slot] = key[u];
             cc[slot] = (int32_t)(c0 + p0 + u);
         });
