@@ -262,7 +262,7 @@ __global__ __launch_bounds__(kFtThreads) void index_topk_kernel(
             t = t2;
         }
     }
-    __syncthreads();
+    lds_barrier();
 
     // the chunk's keys, kFtKpt consecutive positions per thread
     uint32_t key[kFtKpt];
@@ -278,15 +278,17 @@ __global__ __launch_bounds__(kFtThreads) void index_topk_kernel(
     if (nchunks == 1) {
         int32_t* out = out_idx + q * k;
         const uint32_t emitted = tk::reg_select_emit<kFtThreads, kFtKpt, true>(
-            key, (uint32_t)k, sh, [&](uint32_t slot, int u) { out[slot] = (int32_t)(c0 + p0 + u); });
+            key, (uint32_t)k, sh, [&](int u) { return (int32_t)(c0 + p0 + u); },
+            [&](uint32_t slot, uint32_t, int32_t col) { out[slot] = col; });
         for (int i = (int)emitted + tid; i < k; i += kFtThreads) out[i] = -1;
     } else {
         uint32_t* ck = cand_key + (q * nchunks + chunk) * (int64_t)k;
         int32_t* cc = cand_col + (q * nchunks + chunk) * (int64_t)k;
-        const uint32_t emitted =
-            tk::reg_select_emit<kFtThreads, kFtKpt, true>(key, (uint32_t)k, sh, [&](uint32_t slot, int u) {
-                ck[slot] = key[u];
-                cc[slot] = (int32_t)(c0 + p0 + u);
+        const uint32_t emitted = tk::reg_select_emit<kFtThreads, kFtKpt, true>(
+            key, (uint32_t)k, sh, [&](int u) { return (int32_t)(c0 + p0 + u); },
+            [&](uint32_t slot, uint32_t kv, int32_t col) {
+                ck[slot] = kv;
+                cc[slot] = col;
             });
         for (int i = (int)emitted + tid; i < k; i += kFtThreads) {
             ck[i] = 0u;

@@ -321,18 +321,19 @@ __global__ __launch_bounds__(NT) void topk_reg_chunk_kernel(
     if (nchunks == 1) {
         int32_t* out = out_idx + row * k;
         const int32_t* map = id_map ? id_map + row * ld : nullptr;
-        emitted = reg_select_emit<NT, KPT, true>(key, (uint32_t)k, sh, [&](uint32_t slot, int u) {
-            const int64_t col = c0 + p0 + u;
-            out[slot] = map ? map[col] : (int32_t)col;
-        });
+        emitted = reg_select_emit<NT, KPT, true>(
+            key, (uint32_t)k, sh, [&](int u) { return (int32_t)(c0 + p0 + u); },
+            [&](uint32_t slot, uint32_t, int32_t col) { out[slot] = map ? map[col] : col; });
         for (int t = (int)emitted + tid; t < k; t += NT) out[t] = -1;
     } else {
         uint32_t* ck = cand_key + (row * nchunks + chunk) * k;
         int32_t* cc = cand_col + (row * nchunks + chunk) * k;
-        emitted = reg_select_emit<NT, KPT, true>(key, (uint32_t)k, sh, [&](uint32_t slot, int u) {
-            ck[slot] = key[u];
-            cc[slot] = (int32_t)(c0 + p0 + u);
-        });
+        emitted = reg_select_emit<NT, KPT, true>(
+            key, (uint32_t)k, sh, [&](int u) { return (int32_t)(c0 + p0 + u); },
+            [&](uint32_t slot, uint32_t kv, int32_t col) {
+                ck[slot] = kv;
+                cc[slot] = col;
+            });
         for (int t = (int)emitted + tid; t < k; t += NT) {
             ck[t] = 0u;
             cc[t] = -1;
@@ -382,9 +383,9 @@ __global__ __launch_bounds__(NT) void topk_reg_merge_kernel(int64_t ld, int32_t 
     }
     int32_t* out = out_idx + row * k;
     const int32_t* map = id_map ? id_map + row * ld : nullptr;
-    const uint32_t emitted = reg_select_emit<NT, KPT, true>(key, (uint32_t)k, sh, [&](uint32_t slot, int u) {
-        out[slot] = map ? map[col[u]] : col[u];
-    });
+    const uint32_t emitted = reg_select_emit<NT, KPT, true>(
+        key, (uint32_t)k, sh, [&](int u) { return col[u]; },
+        [&](uint32_t slot, uint32_t, int32_t c) { out[slot] = map ? map[c] : c; });
     for (int t = (int)emitted + tid; t < k; t += NT) out[t] = -1;
 }
 
@@ -416,10 +417,12 @@ __global__ __launch_bounds__(NT) void topk_reg_group_merge_kernel(int32_t k, int
     }
     uint32_t* ok = out_key + (row * ngroups + g) * (int64_t)k;
     int32_t* oc = out_col + (row * ngroups + g) * (int64_t)k;
-    const uint32_t emitted = reg_select_emit<NT, KPT, true>(key, (uint32_t)k, sh, [&](uint32_t slot, int u) {
-        ok[slot] = key[u];
-        oc[slot] = col[u];
-    });
+    const uint32_t emitted = reg_select_emit<NT, KPT, true>(
+        key, (uint32_t)k, sh, [&](int u) { return col[u]; },
+        [&](uint32_t slot, uint32_t kv, int32_t c) {
+            ok[slot] = kv;
+            oc[slot] = c;
+        });
     for (int t = (int)emitted + tid; t < k; t += NT) {
         ok[t] = 0u;
         oc[t] = -1;
@@ -560,7 +563,11 @@ int launch_topk(const float* scores, int32_t rows, int64_t ncols, int64_t ld, co
         const dim3 g1((unsigned)((int64_t)rows * c));
         const RegShape a = reg_shape(chunk_len);
 #define CSA2_CHUNK(NT, KPT) launch_reg_chunk<NT, KPT>(g1, s, scores, ncols, ld, row_len, k, c, chunk_len, id_map, out_idx, ck, cc)
-        if (a.nt == 256) {
+        if (chunk_len > 8192 && chunk_len <= 16384) {
+            // 512 threads x 32 keys: measured 23% faster than 1024 x 16 for
+            // 4096 rows x 65536 scores (two workgroups of 8 waves per CU)
+            CSA2_CHUNK(512, 32);
+        } else if (a.nt == 256) {
             switch (a.kpt) {
                 case 1: CSA2_CHUNK(256, 1); break;
                 case 2: CSA2_CHUNK(256, 2); break;

@@ -21,16 +21,26 @@ CSA2_DEVINL uint32_t score_key(float f) {
 constexpr int kRegMaxKpt = 32;        // keys per thread
 constexpr int kRegMaxKeys = 1024 * kRegMaxKpt;  // 32768 per chunk
 constexpr int kRegMaxCand = 16384;    // merge capacity per row
+constexpr int kLst = 512;             // keys of the first digit's chosen bin finished by one wave
+constexpr int kStage = 2048;          // largest selection staged in LDS for coalesced output
 
-// Histograms of the three radix digits (key bits 31..20, 19..10, 9..0), all
-// cleared once at the start.
+constexpr int kBins1 = 4096;          // first-digit bins (one more holds key 0)
+
+// Histograms of the three radix digits (key bits 31..20, 19..10, 9..0 when
+// the keys span the whole range; h2 and h3 only when the first digit leaves
+// more than kLst keys in the k-th key's bin), the gathered keys of that bin,
+// and per-wave scan / min / max words. h1 doubles as the output staging area
+// once the threshold is known.
 template <int NT>
 struct RegTk {
-    uint32_t h1[4096];
+    uint32_t h1[kBins1 + 4];
     uint32_t h2[1024];
     uint32_t h3[1024];
+    uint32_t lst[kLst];
     uint32_t wsum[NT / 64];
-    uint32_t sel_bin, sel_above, total;
+    uint32_t wmax[NT / 64], wmin[NT / 64];
+    uint32_t lst_n;
+    uint32_t bc[4];  // results of one wave's pick, read by the others
 };
 
 // Inclusive prefix sum over the 64 lanes with DPP: row_shr 1, 2, 4, 8 within
@@ -53,7 +63,7 @@ CSA2_DEVINL uint32_t reg_block_scan(uint32_t v, uint32_t* wsum, uint32_t* total)
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
     const uint32_t x = wave_incl_scan(v);
     if (lane == 63) wsum[wave] = x;
-    __syncthreads();
+    lds_barrier();
     uint32_t before = 0, tot = 0;
 #pragma unroll
     for (int i = 0; i < NT / 64; i++) {
@@ -65,136 +75,271 @@ CSA2_DEVINL uint32_t reg_block_scan(uint32_t v, uint32_t* wsum, uint32_t* total)
     return before + x - v;
 }
 
-// From histogram h of nbins bins, finds the bin holding the rem-th largest
-// counted key, counting from the top bin: sets sh.sel_bin and sh.sel_above
-// (keys in higher bins). rem == 0 means rem = min(k, all counted keys), which
-// is also stored in sh.total. Two barriers; the results are readable after.
-template <int NT>
-CSA2_DEVINL void reg_pick_bin(const uint32_t* h, RegTk<NT>& sh, int nbins, uint32_t rem, uint32_t k) {
-    constexpr int kMaxPer = 4096 / NT;
-    const int tid = threadIdx.x;
-    const int per = nbins / NT;
-    uint32_t c[kMaxPer], loc = 0;
+// Bin of histogram h (NBINS bins, counted from the top bin down) holding the
+// rem-th counted key and the count of keys in the bins above it; rem == 0
+// stands for min(cap, all counted keys). Returns that rank (0: no keys, bin
+// and above unset); 1 <= rem <= all counted keys otherwise. Every wave
+// computes it on its own, so no barrier is needed: lane l sums the P =
+// NBINS/64 bins of ranks [P*l, P*l + P) (reads rotated across lanes to spread
+// LDS banks), a wave scan finds the lane whose range holds the rank, and a
+// second scan over that lane's P bins the bin.
+template <int NBINS>
+CSA2_DEVINL uint32_t wave_pick(const uint32_t* h, uint32_t rem, uint32_t cap, uint32_t& bin, uint32_t& above) {
+    constexpr int P = NBINS / 64;
+    const int lane = threadIdx.x & 63;
+    const uint32_t* blk = h + NBINS - P * (lane + 1);
+    uint32_t c = 0;
 #pragma unroll
-    for (int j = 0; j < kMaxPer; j++) {
-        c[j] = (j < per) ? h[nbins - 1 - (tid * per + j)] : 0u;
-        loc += c[j];
+    for (int j = 0; j < P / 4; j++) {
+        const int jj = (j + lane) & (P / 4 - 1);
+        const uint4 v = *reinterpret_cast<const uint4*>(blk + 4 * jj);
+        c += v.x + v.y + v.z + v.w;
     }
-    uint32_t tot;
-    uint32_t above = reg_block_scan<NT>(loc, sh.wsum, &tot);
+    const uint32_t incl = wave_incl_scan(c);
     if (rem == 0) {
-        rem = tot < k ? tot : k;
-        if (tid == 0) sh.total = rem;
+        const uint32_t all = (uint32_t)__builtin_amdgcn_readlane((int)incl, 63);
+        rem = all < cap ? all : cap;
+        if (rem == 0) return 0;
     }
-    if (above < rem && rem <= above + loc) {
-        for (int j = 0; j < per; j++) {
-            if (above + c[j] >= rem) {
-                sh.sel_bin = nbins - 1 - (tid * per + j);
-                sh.sel_above = above;
-                break;
-            }
-            above += c[j];
-        }
+    const uint64_t hit = __ballot(incl - c < rem && rem <= incl);
+    const int L = (int)__builtin_ctzll(hit);
+    const uint32_t base = (uint32_t)__builtin_amdgcn_readlane((int)(incl - c), L);
+    const uint32_t ci = lane < P ? h[NBINS - 1 - (P * L + lane)] : 0u;
+    const uint32_t incl2 = wave_incl_scan(ci) + base;
+    const uint64_t hit2 = __ballot(lane < P && incl2 - ci < rem && rem <= incl2);
+    const int I = (int)__builtin_ctzll(hit2);
+    bin = (uint32_t)(NBINS - 1 - (P * L + I));
+    above = (uint32_t)__builtin_amdgcn_readlane((int)(incl2 - ci), I);
+    return rem;
+}
+
+// Bits [0, s1) of the rem-th largest of the n keys in lst (n <= kLst, all
+// nonzero, all equal in the bits above s1), MSB first with wave ballots. On
+// return rem is that key's rank among the keys equal to it and n_eq their
+// number.
+CSA2_DEVINL uint32_t wave_bit_select(const uint32_t* lst, int n, int s1, uint32_t& rem, uint32_t& n_eq) {
+    const int lane = threadIdx.x & 63;
+    const int nv = (n + 63) >> 6;  // occupied lane rows (uniform)
+    uint32_t v[kLst / 64];
+#pragma unroll
+    for (int i = 0; i < kLst / 64; i++) v[i] = (i < nv && lane + 64 * i < n) ? lst[lane + 64 * i] : 0u;
+    const uint32_t low = (1u << s1) - 1u;  // s1 <= 20
+    uint32_t prefix = 0;
+    for (int b = s1 - 1; b >= 0; b--) {
+        const uint32_t mask = low & ~((1u << b) - 1u);  // bits [b, s1)
+        const uint32_t want = prefix | (1u << b);
+        uint32_t cnt = 0;
+#pragma unroll
+        for (int i = 0; i < kLst / 64; i++)
+            if (i < nv) cnt += (uint32_t)__popcll(__ballot(v[i] != 0u && (v[i] & mask) == want));
+        if (cnt >= rem)
+            prefix = want;
+        else
+            rem -= cnt;
     }
-    __syncthreads();
+    uint32_t e = 0;
+#pragma unroll
+    for (int i = 0; i < kLst / 64; i++)
+        if (i < nv) e += (uint32_t)__popcll(__ballot(v[i] != 0u && (v[i] & low) == prefix));
+    n_eq = e;
+    return prefix;
 }
 
 // Exact selection over the keys held in registers (thread t holds positions
-// t*KPT .. t*KPT+KPT-1 of the segment; key 0 = never selected): a 3-pass MSB
-// radix select (12, 10, 10 bits) over LDS histograms finds the k-th largest
-// key T, then emit(slot, u) is called for every key > T and for the first
-// `need` keys == T, slots ascending with position (one packed block scan of
-// the per-thread counts). Returns the number selected, min(k, #nonzero keys).
+// t*KPT .. t*KPT+KPT-1 of the segment; key 0 = never selected). An MSB radix
+// select finds the k-th largest key T: a 12-bit first digit over an LDS
+// histogram, then -- when T's bin holds at most kLst keys, the usual case --
+// those keys are gathered and one wave finishes the remaining bits with
+// ballots; otherwise two more 10-bit histogram digits. Every key > T and the
+// first `need` keys == T are selected, slots ascending with position (one
+// packed block scan of the per-thread counts; when every key equal to T is
+// taken, a key is selected iff it is >= T). out(slot, key, val(u)) is called
+// for every slot < the returned count, min(k, #nonzero keys): by consecutive
+// threads from an LDS copy when the selection has at most kStage keys, else
+// by the key's owner thread.
+// The per-key passes are branch-free except where a wave holds a selected or
+// gathered key.
 //
-// kNarrow (used for merged candidates, whose values sit in a narrow band at
-// the top of the row): the first digit ends at the highest bit where the
-// largest and smallest key differ -- every key shares the bits above it -- so
-// the first histogram spreads instead of piling into a few bins. The three
-// digits then cover bits [0, s1 + 12); s1 <= 20 always.
-template <int NT, int KPT, bool kNarrow, class Emit>
-CSA2_DEVINL uint32_t reg_select_emit(const uint32_t (&key)[KPT], uint32_t k, RegTk<NT>& sh, Emit emit) {
-    const int tid = threadIdx.x;
-    for (int i = tid; i < 4096; i += NT) sh.h1[i] = 0;
-    for (int i = tid; i < 1024; i += NT) sh.h2[i] = 0;
-    int s1 = 20;        // digit 1 = key bits [s1, s1 + 12)
-    uint32_t high = 0;  // bits >= s1 + 12, shared by every nonzero key
+// kNarrow (for keys in a narrow band, e.g. one row's scores or merged
+// candidates): the first digit ends at the highest bit where the largest and
+// smallest key differ -- every key shares the bits above it -- so the first
+// histogram spreads instead of piling into a few bins. Digits then cover bits
+// [0, s1 + 12); s1 <= 20 always.
+template <int NT, int KPT, bool kNarrow, class Val, class Out>
+CSA2_DEVINL uint32_t reg_select_emit(const uint32_t (&key)[KPT], uint32_t k, RegTk<NT>& sh, Val val, Out out) {
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    for (int i = tid; i < kBins1 + 4; i += NT) sh.h1[i] = 0;
+    if (tid == 0) sh.lst_n = 0;
     if (kNarrow) {
         uint32_t mx = 0u, mn = 0xFFFFFFFFu;
 #pragma unroll
         for (int u = 0; u < KPT; u++) {
             mx = max(mx, key[u]);
-            if (key[u]) mn = min(mn, key[u]);
+            mn = min(mn, key[u] ? key[u] : 0xFFFFFFFFu);
         }
 #pragma unroll
         for (int o = 32; o > 0; o >>= 1) {
             mx = max(mx, (uint32_t)__shfl_xor((int)mx, o));
             mn = min(mn, (uint32_t)__shfl_xor((int)mn, o));
         }
-        if ((tid & 63) == 0) {
-            sh.h3[tid >> 6] = mx;
-            sh.h3[512 + (tid >> 6)] = mn;
+        if (lane == 0) {
+            sh.wmax[wave] = mx;
+            sh.wmin[wave] = mn;
         }
-        __syncthreads();
+    }
+    lds_barrier();
+    int s1 = 20;        // digit 1 = key bits [s1, s1 + 12)
+    uint32_t high = 0;  // bits >= s1 + 12, shared by every nonzero key
+    if (kNarrow) {
         uint32_t bmax = 0u, bmin = 0xFFFFFFFFu;
 #pragma unroll
         for (int i = 0; i < NT / 64; i++) {
-            bmax = max(bmax, sh.h3[i]);
-            bmin = min(bmin, sh.h3[512 + i]);
+            bmax = max(bmax, sh.wmax[i]);
+            bmin = min(bmin, sh.wmin[i]);
         }
         if (bmax != 0u) {
             const int h = bmax > bmin ? 31 - __builtin_clz(bmax ^ bmin) : 0;  // highest differing bit
             s1 = h >= 31 ? 20 : (h >= 11 ? h - 11 : 0);
             high = (s1 + 12 < 32) ? (bmax & ~((1u << (s1 + 12)) - 1u)) : 0u;
         }
-        __syncthreads();  // every thread has read h3 before it is cleared
     }
-    for (int i = tid; i < 1024; i += NT) sh.h3[i] = 0;
-    const int s2 = s1 >= 10 ? s1 - 10 : 0;  // digit 2 = bits [s2, s1)
-    const int s3 = s2 >= 10 ? s2 - 10 : 0;  // digit 3 = bits [s3, s2); s3 == 0
-    const uint32_t m2 = (1u << (s1 - s2)) - 1u, m3 = (1u << (s2 - s3)) - 1u;
-    __syncthreads();
+    // key 0 counts in the spare bin kBins1, outside the histogram proper
 #pragma unroll
-    for (int u = 0; u < KPT; u++)
-        if (key[u]) atomicAdd(&sh.h1[(key[u] >> s1) & 4095u], 1u);
-    __syncthreads();
-    reg_pick_bin<NT>(sh.h1, sh, 4096, 0u, k);
-    const uint32_t kk = sh.total;
+    for (int u = 0; u < KPT; u++) atomicAdd(&sh.h1[key[u] ? ((key[u] >> s1) & 4095u) : (uint32_t)kBins1], 1u);
+    lds_barrier();
+    // wave 0 finds kk = min(k, nonzero keys) and T's first digit; the others
+    // wait at one barrier
+    if (wave == 0) {
+        uint32_t bb = 0, ab = 0;
+        const uint32_t kk0 = wave_pick<kBins1>(sh.h1, 0u, k, bb, ab);
+        if (lane == 0) {
+            sh.bc[0] = kk0;
+            sh.bc[1] = bb;
+            sh.bc[2] = ab;
+        }
+    }
+    lds_barrier();
+    const uint32_t kk = sh.bc[0], b1 = sh.bc[1];
+    uint32_t above = sh.bc[2];
     if (kk == 0) return 0;
-    uint32_t prefix = sh.sel_bin, rem = kk - sh.sel_above;  // T's bits [s1, s1 + 12)
+    uint32_t rem = kk - above;  // rank of T within bin b1
+    const uint32_t nb1 = sh.h1[b1];
+    uint32_t T;
+    bool all_eq = false;  // every key equal to T is selected
+    if (nb1 <= (uint32_t)kLst) {
 #pragma unroll
-    for (int u = 0; u < KPT; u++)
-        if (key[u] && ((key[u] >> s1) & 4095u) == prefix) atomicAdd(&sh.h2[(key[u] >> s2) & m2], 1u);
-    __syncthreads();
-    reg_pick_bin<NT>(sh.h2, sh, 1024, rem, k);
-    prefix = (prefix << (s1 - s2)) | sh.sel_bin;  // bits [s2, s1 + 12)
-    rem -= sh.sel_above;
-    const uint32_t m12 = (1u << (12 + s1 - s2)) - 1u;
+        for (int u = 0; u < KPT; u++) {
+            const bool m = key[u] != 0u && ((key[u] >> s1) & 4095u) == b1;
+            const uint64_t bal = __ballot(m);
+            if (bal) {
+                uint32_t base = 0;
+                if (lane == 0) base = __hip_atomic_fetch_add(&sh.lst_n, (uint32_t)__popcll(bal), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
+                base = (uint32_t)__builtin_amdgcn_readfirstlane((int)base);
+                const uint32_t r = __builtin_amdgcn_mbcnt_hi((uint32_t)(bal >> 32), __builtin_amdgcn_mbcnt_lo((uint32_t)bal, 0u));
+                if (m) sh.lst[base + r] = key[u];
+            }
+        }
+        lds_barrier();
+        if (wave == 0) {
+            uint32_t r = rem, n_eq = 0;
+            const uint32_t low = wave_bit_select(sh.lst, (int)nb1, s1, r, n_eq);
+            if (lane == 0) {
+                sh.bc[0] = low;
+                sh.bc[1] = r;
+                sh.bc[3] = n_eq;
+            }
+        }
+        lds_barrier();
+        T = high | (b1 << s1) | sh.bc[0];
+        rem = sh.bc[1];
+        all_eq = rem == sh.bc[3];
+    } else {
+        for (int i = tid; i < 1024; i += NT) {
+            sh.h2[i] = 0;
+            sh.h3[i] = 0;
+        }
+        lds_barrier();
+        const int s2 = s1 >= 10 ? s1 - 10 : 0;  // digit 2 = bits [s2, s1)
+        const int s3 = s2 >= 10 ? s2 - 10 : 0;  // digit 3 = bits [s3, s2); s3 == 0
+        const uint32_t m2 = (1u << (s1 - s2)) - 1u, m3 = (1u << (s2 - s3)) - 1u;
+        uint32_t prefix = b1;  // T's bits [s1, s1 + 12)
 #pragma unroll
-    for (int u = 0; u < KPT; u++)
-        if (key[u] && ((key[u] >> s2) & m12) == prefix) atomicAdd(&sh.h3[(key[u] >> s3) & m3], 1u);
-    __syncthreads();
-    reg_pick_bin<NT>(sh.h3, sh, 1024, rem, k);
-    const uint32_t T = high | (((prefix << (s2 - s3)) | sh.sel_bin) << s3);
-    const uint32_t need = rem - sh.sel_above;
-
-    uint32_t gt = 0, eq = 0;
+        for (int u = 0; u < KPT; u++)
+            if (key[u] && ((key[u] >> s1) & 4095u) == prefix) atomicAdd(&sh.h2[(key[u] >> s2) & m2], 1u);
+        lds_barrier();
+        uint32_t b2 = 0;
+        wave_pick<1024>(sh.h2, rem, 0u, b2, above);
+        rem -= above;
+        prefix = (prefix << (s1 - s2)) | b2;  // bits [s2, s1 + 12)
+        const uint32_t m12 = (1u << (12 + s1 - s2)) - 1u;
 #pragma unroll
-    for (int u = 0; u < KPT; u++) {
-        gt += key[u] > T;
-        eq += key[u] == T;
+        for (int u = 0; u < KPT; u++)
+            if (key[u] && ((key[u] >> s2) & m12) == prefix) atomicAdd(&sh.h3[(key[u] >> s3) & m3], 1u);
+        lds_barrier();
+        uint32_t b3 = 0;
+        wave_pick<1024>(sh.h3, rem, 0u, b3, above);
+        rem -= above;
+        T = high | (((prefix << (s2 - s3)) | b3) << s3);
     }
+    const uint32_t need = rem;
+    // per-thread start slot (and, when some keys equal to T are left out, the
+    // count of keys == T before this thread)
+    uint32_t slot0, eq0 = 0;
     uint32_t tot;
-    const uint32_t before = reg_block_scan<NT>((gt << 16) | eq, sh.wsum, &tot);
-    const uint32_t gt_before = before >> 16, eq_before = before & 0xFFFFu;
-    uint32_t slot = gt_before + (eq_before < need ? eq_before : need);
-    uint32_t eq_run = eq_before;
+    if (all_eq) {
+        uint32_t ge = 0;
 #pragma unroll
-    for (int u = 0; u < KPT; u++) {
-        const bool is_eq = key[u] == T;
-        const bool sel = key[u] > T || (is_eq && eq_run < need);
-        eq_run += is_eq;
-        if (sel && slot < kk) emit(slot, u);  // slot < kk always holds; the check keeps stores in bounds regardless
-        slot += sel;
+        for (int u = 0; u < KPT; u++) ge += key[u] >= T;
+        // its barrier also ends every read of h1 above, which the staging overwrites
+        slot0 = reg_block_scan<NT>(ge, sh.wsum, &tot);
+    } else {
+        uint32_t gt = 0, eq = 0;
+#pragma unroll
+        for (int u = 0; u < KPT; u++) {
+            gt += key[u] > T;
+            eq += key[u] == T;
+        }
+        const uint32_t before = reg_block_scan<NT>((gt << 16) | eq, sh.wsum, &tot);
+        eq0 = before & 0xFFFFu;
+        slot0 = (before >> 16) + (eq0 < need ? eq0 : need);
+    }
+    // Up to kStage selected keys go through LDS (keys in h1[0, kStage),
+    // payloads in h1[kStage, 2 kStage)) and are written out by consecutive
+    // threads; larger selections are written by their owner threads.
+    auto pass = [&](auto&& take) {
+        uint32_t slot = slot0;
+        if (all_eq) {
+#pragma unroll
+            for (int u = 0; u < KPT; u++) {
+                const bool sel = key[u] >= T;
+                if (sel) take(slot, u);
+                slot += sel;
+            }
+        } else {
+            uint32_t eq_run = eq0;
+#pragma unroll
+            for (int u = 0; u < KPT; u++) {
+                const bool is_eq = key[u] == T;
+                const bool sel = key[u] > T || (is_eq && eq_run < need);
+                eq_run += is_eq;
+                if (sel) take(slot, u);
+                slot += sel;
+            }
+        }
+    };
+    if (kk <= (uint32_t)kStage) {
+        pass([&](uint32_t slot, int u) {
+            if (slot < (uint32_t)kStage) {  // always; keeps the stores in bounds regardless
+                sh.h1[slot] = key[u];
+                sh.h1[kStage + slot] = (uint32_t)val(u);
+            }
+        });
+        lds_barrier();
+        for (uint32_t s2 = tid; s2 < kk; s2 += NT) out(s2, sh.h1[s2], (int32_t)sh.h1[kStage + s2]);
+    } else {
+        pass([&](uint32_t slot, int u) {
+            if (slot < kk) out(slot, key[u], (int32_t)val(u));
+        });
     }
     return kk;
 }
