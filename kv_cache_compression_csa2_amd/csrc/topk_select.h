@@ -55,6 +55,28 @@ CSA2_DEVINL uint32_t wave_incl_scan(uint32_t x) {
     return x;
 }
 
+// Max / min over the 64 lanes, in every lane: the same DPP row shifts and row
+// broadcasts as the scan, then lane 63's value. A lane whose source is out of
+// range keeps its own value.
+CSA2_DEVINL uint32_t wave_max_u32(uint32_t x) {
+    x = max(x, (uint32_t)__builtin_amdgcn_update_dpp((int)x, (int)x, 0x111, 0xF, 0xF, false));
+    x = max(x, (uint32_t)__builtin_amdgcn_update_dpp((int)x, (int)x, 0x112, 0xF, 0xF, false));
+    x = max(x, (uint32_t)__builtin_amdgcn_update_dpp((int)x, (int)x, 0x114, 0xF, 0xF, false));
+    x = max(x, (uint32_t)__builtin_amdgcn_update_dpp((int)x, (int)x, 0x118, 0xF, 0xF, false));
+    x = max(x, (uint32_t)__builtin_amdgcn_update_dpp((int)x, (int)x, 0x142, 0xA, 0xF, false));
+    x = max(x, (uint32_t)__builtin_amdgcn_update_dpp((int)x, (int)x, 0x143, 0xC, 0xF, false));
+    return (uint32_t)__builtin_amdgcn_readlane((int)x, 63);
+}
+CSA2_DEVINL uint32_t wave_min_u32(uint32_t x) {
+    x = min(x, (uint32_t)__builtin_amdgcn_update_dpp((int)x, (int)x, 0x111, 0xF, 0xF, false));
+    x = min(x, (uint32_t)__builtin_amdgcn_update_dpp((int)x, (int)x, 0x112, 0xF, 0xF, false));
+    x = min(x, (uint32_t)__builtin_amdgcn_update_dpp((int)x, (int)x, 0x114, 0xF, 0xF, false));
+    x = min(x, (uint32_t)__builtin_amdgcn_update_dpp((int)x, (int)x, 0x118, 0xF, 0xF, false));
+    x = min(x, (uint32_t)__builtin_amdgcn_update_dpp((int)x, (int)x, 0x142, 0xA, 0xF, false));
+    x = min(x, (uint32_t)__builtin_amdgcn_update_dpp((int)x, (int)x, 0x143, 0xC, 0xF, false));
+    return (uint32_t)__builtin_amdgcn_readlane((int)x, 63);
+}
+
 // Exclusive scan over the block in thread order (one barrier); *total = sum.
 // wsum must not be rewritten until every thread has returned (the callers
 // place a barrier in between).
@@ -114,11 +136,28 @@ CSA2_DEVINL uint32_t wave_pick(const uint32_t* h, uint32_t rem, uint32_t cap, ui
 }
 
 // Bits [0, s1) of the rem-th largest of the n keys in lst (n <= kLst, all
-// nonzero, all equal in the bits above s1), MSB first with wave ballots. On
-// return rem is that key's rank among the keys equal to it and n_eq their
-// number.
+// nonzero, all equal in the bits above s1). On return rem is that key's rank
+// among the keys equal to it and n_eq their number. Up to 64 keys: one key
+// per lane, each lane counts the keys above and at its own (a broadcast loop,
+// no serial dependence between steps). More: MSB first with wave ballots.
 CSA2_DEVINL uint32_t wave_bit_select(const uint32_t* lst, int n, int s1, uint32_t& rem, uint32_t& n_eq) {
     const int lane = threadIdx.x & 63;
+    if (n <= 64) {
+        const uint32_t mine = lane < n ? lst[lane] : 0u;
+        uint32_t gt = 0, ge = 0;
+        for (int j = 0; j < n; j++) {
+            const uint32_t kj = (uint32_t)__builtin_amdgcn_readlane((int)mine, j);
+            gt += kj > mine;
+            ge += kj >= mine;
+        }
+        // lanes holding the rem-th largest key (all equal; take the first)
+        const uint64_t hit = __ballot(lane < n && gt < rem && rem <= ge);
+        const int L = (int)__builtin_ctzll(hit);
+        const uint32_t T = (uint32_t)__builtin_amdgcn_readlane((int)mine, L);
+        rem -= (uint32_t)__builtin_amdgcn_readlane((int)gt, L);
+        n_eq = (uint32_t)__builtin_amdgcn_readlane((int)(ge - gt), L);
+        return T & ((1u << s1) - 1u);
+    }
     const int nv = (n + 63) >> 6;  // occupied lane rows (uniform)
     uint32_t v[kLst / 64];
 #pragma unroll
@@ -177,11 +216,8 @@ CSA2_DEVINL uint32_t reg_select_emit(const uint32_t (&key)[KPT], uint32_t k, Reg
             mx = max(mx, key[u]);
             mn = min(mn, key[u] ? key[u] : 0xFFFFFFFFu);
         }
-#pragma unroll
-        for (int o = 32; o > 0; o >>= 1) {
-            mx = max(mx, (uint32_t)__shfl_xor((int)mx, o));
-            mn = min(mn, (uint32_t)__shfl_xor((int)mn, o));
-        }
+        mx = wave_max_u32(mx);
+        mn = wave_min_u32(mn);
         if (lane == 0) {
             sh.wmax[wave] = mx;
             sh.wmin[wave] = mn;
