@@ -134,6 +134,8 @@ CSA2_DEVINL float sum_over_groups(float v) {
 // be computed before launch.
 static inline int attn_total_tiles(int32_t k) { return (k + kTile - 1) / kTile + kMaxWindow / kTile; }
 
+constexpr int kMaxSplits = 16;  // partials per query the merge kernel holds
+
 static inline int attn_splits(int32_t nq, int32_t k) {
     const int tiles = attn_total_tiles(k);
     // Workgroups per query: more splits fill the GPU at small batch but add
@@ -142,6 +144,7 @@ static inline int attn_splits(int32_t nq, int32_t k) {
     // for 8 / 16-32 / 64 / 128 / 256 / 512 queries.
     int want = nq >= 512 ? 1 : nq >= 128 ? 2 : nq >= 64 ? 4 : nq >= 16 ? 7 : 10;
     if (want > tiles) want = tiles;
+    if (want > kMaxSplits) want = kMaxSplits;
     const int per = (tiles + want - 1) / want;
     return (tiles + per - 1) / per;
 }
@@ -394,24 +397,39 @@ __global__ __launch_bounds__(kAttThreads, 2) void sparse_attn_kernel(
     }
 }
 
-// Merge of split partials: one workgroup per (query, head), 128 threads x 4 dims.
+// Merge of split partials: one workgroup per (query, head), 128 threads x 4
+// dims. Every split's (max, sum) pair and O slice are loaded up front, so the
+// merge waits for memory once.
+
 __global__ __launch_bounds__(128) void attn_merge_kernel(const float* __restrict__ part_o,
                                                          const float* __restrict__ part_ml, int32_t nsplit,
                                                          uint16_t* __restrict__ out, float* __restrict__ lse) {
     const int64_t qh = blockIdx.x;  // qi * 64 + head
     const int64_t qi = qh / kHeads, head = qh % kHeads;
+    const int d = threadIdx.x * 4;
+    f32x2 ml[kMaxSplits];
+    f32x4 po[kMaxSplits];
+#pragma unroll
+    for (int s = 0; s < kMaxSplits; s++) {
+        if (s < nsplit) {
+            const int64_t pidx = (qi * nsplit + s) * kHeads + head;
+            ml[s] = *reinterpret_cast<const f32x2*>(part_ml + pidx * 2);
+            po[s] = *reinterpret_cast<const f32x4*>(part_o + pidx * kDim + d);
+        }
+    }
     float M = -INFINITY;
-    for (int s = 0; s < nsplit; s++) M = fmaxf(M, part_ml[((qi * nsplit + s) * kHeads + head) * 2]);
+#pragma unroll
+    for (int s = 0; s < kMaxSplits; s++)
+        if (s < nsplit) M = fmaxf(M, ml[s][0]);
     float L = 0.0f;
     f32x4 acc = {0.f, 0.f, 0.f, 0.f};
-    const int d = threadIdx.x * 4;
-    for (int s = 0; s < nsplit; s++) {
-        const int64_t pidx = (qi * nsplit + s) * kHeads + head;
-        const float ms = part_ml[pidx * 2], ls = part_ml[pidx * 2 + 1];
-        if (ms == -INFINITY) continue;
-        const float f = exp2f(ms - M);
-        L += ls * f;
-        acc += *reinterpret_cast<const f32x4*>(part_o + pidx * kDim + d) * f;
+#pragma unroll
+    for (int s = 0; s < kMaxSplits; s++) {
+        if (s < nsplit && ml[s][0] != -INFINITY) {
+            const float f = exp2f(ml[s][0] - M);
+            L += ml[s][1] * f;
+            acc += po[s] * f;
+        }
     }
     const float inv = L > 0.0f ? 1.0f / L : 0.0f;
     *reinterpret_cast<uint2*>(out + qh * kDim + d) =
