@@ -328,6 +328,24 @@ def test_topk_narrow_band(rows, n, k):
     _topk_check(s, k)
 
 
+@pytest.mark.parametrize("n_tie,n_above", [(40, 500), (300, 300), (700, 100)])
+def test_topk_threshold_bin_sizes(n_tie, n_above):
+    """The k-th key's first-digit bin holding <= 64 keys (one key per lane),
+    65..512 keys (ballot bit select) and > 512 keys (two more histogram
+    digits): n_tie copies of the k-th value, n_above larger values in other
+    bins, background below; ties resolved by lowest position."""
+    print("case: topk bin sizes", n_tie, n_above, flush=True)
+    rng = np.random.default_rng(n_tie + n_above)
+    rows, n, k = 4, 20000, 512
+    s = (1.0 + rng.random((rows, n))).astype(np.float32)  # [1, 2)
+    for r in range(rows):
+        pos = rng.permutation(n)
+        s[r, pos[:n_tie]] = np.float32(10.0)
+        s[r, pos[n_tie:n_tie + n_above]] = (16.0 + 16.0 * rng.random(n_above)).astype(np.float32)
+    _topk_check(s, k)
+    _topk_check(s, 2048)
+
+
 def test_topk_id_map():
     print("case: topk id_map", flush=True)
     rng = np.random.default_rng(2)
