@@ -38,8 +38,8 @@
 // 128-register O^T rescale is rare; exp2 arguments stay <= 8. It starts at a
 // finite floor (-2^126), so masked keys (logit -inf) need no special case.
 // Few queries cannot fill the GPU, so a query's tiles may be split across
-// workgroups that write partial (O, max, sum) to the workspace; a second
-// kernel merges them.
+// workgroups that write partial results (O / sum in bf16, max, sum) to the
+// workspace; a second kernel merges them.
 #include <math.h>
 
 #include "device_common.h"
@@ -52,6 +52,8 @@ namespace {
 constexpr int kTile = 32;                 // keys per tile
 constexpr int kRowB = kDim * 2 + 16;      // bytes per LDS key row (16-byte pad)
 constexpr int kTileB = kTile * kRowB;     // 33,280 bytes
+constexpr int kStgRow = kDim * 2 + 16;    // output staging row: 512 bf16 + pad
+static_assert(4 * 16 * kStgRow <= 2 * kTileB, "output staging must fit the tile buffers");
 constexpr int kAttThreads = 256;
 constexpr float kRescaleSlack = 8.0f;     // log2 units
 
@@ -173,7 +175,7 @@ __global__ __launch_bounds__(kAttThreads, 2) void sparse_attn_kernel(
     const uint16_t* __restrict__ q, const uint8_t* __restrict__ kv, int64_t N, int32_t q_per_seq,
     const int32_t* __restrict__ idx, int32_t k, const void* __restrict__ swa, int64_t T,
     const int32_t* __restrict__ swa_start, const int32_t* __restrict__ swa_len, float scale_log2,
-    uint16_t* __restrict__ out, float* __restrict__ lse, float* __restrict__ part_o, float* __restrict__ part_ml,
+    uint16_t* __restrict__ out, float* __restrict__ lse, uint16_t* __restrict__ part_o, float* __restrict__ part_ml,
     int32_t nsplit) {
     __shared__ __attribute__((aligned(16))) uint8_t lds[2 * kTileB];
     // 0 or -inf per key, stored at perm16_inv(row) (+16 for the second half)
@@ -373,26 +375,35 @@ __global__ __launch_bounds__(kAttThreads, 2) void sparse_attn_kernel(
 
     // ---- finish: lanes with the same head (G = 0..3) hold different keys' sums ----
     const float l_tot = sum_over_groups(l_run);
-    // lane holds O^T[physical dim 16mt + 4G + r][head]: logical dims
-    // 8*L(2mt + G/2) + 4*(G%2) + r, four consecutive ones per mt
-    if (nsplit == 1) {
-        const float inv = l_tot > 0.0f ? 1.0f / l_tot : 0.0f;
-        uint16_t* orow = out + (qi * kHeads + head) * kDim + 4 * (G & 1);
+    const float inv = l_tot > 0.0f ? 1.0f / l_tot : 0.0f;
+    // O / l in bf16 is the output (one split) or the split's partial, which
+    // the merge weights by l * 2^(m - max m). The wave's 16 heads x 512 dims
+    // go through LDS as rows (1040-byte stride: conflict-free writes) and are
+    // stored with 16-byte lanes along each 1 KiB row; straight from the
+    // accumulators every store would scatter 16-byte pieces over 16 rows.
+    // Lane (head j, group G) holds O^T[physical dim 16mt + 4G + r][head j],
+    // logical dims 8*L(2mt + G/2) + 4*(G%2) + r: four consecutive ones per mt.
+    lds_barrier();  // every wave is done with the tile buffers
+    uint8_t* stg = lds + wave * (16 * kStgRow);
+    {
+        uint8_t* row = stg + j * kStgRow + 8 * (G & 1);
 #pragma unroll
         for (int mt = 0; mt < 32; mt++)
-            *reinterpret_cast<uint2*>(orow + 8 * unit_logical(2 * mt + (G >> 1))) =
+            *reinterpret_cast<uint2*>(row + 16 * unit_logical(2 * mt + (G >> 1))) =
                 make_uint2(pack_bf16x2(o[mt][0] * inv, o[mt][1] * inv), pack_bf16x2(o[mt][2] * inv, o[mt][3] * inv));
-        if (lse && G == 0)
-            lse[qi * kHeads + head] = l_tot > 0.0f ? (m_run + log2f(l_tot)) * 0.69314718055994531f : -INFINITY;
-    } else {
-        const int64_t pidx = qi * nsplit + split;
-        float* po = part_o + (pidx * kHeads + head) * kDim + 4 * (G & 1);
+    }
+    lds_barrier();
+    const int64_t prow = nsplit == 1 ? qi * kHeads : (qi * nsplit + split) * kHeads;  // row of head 0
+    uint16_t* dst = (nsplit == 1 ? out : part_o) + (prow + wave * 16) * kDim + 8 * lane;
 #pragma unroll
-        for (int mt = 0; mt < 32; mt++)
-            *reinterpret_cast<f32x4*>(po + 8 * unit_logical(2 * mt + (G >> 1))) = o[mt];
-        if (G == 0) {
-            part_ml[(pidx * kHeads + head) * 2 + 0] = l_tot > 0.0f ? m_run : -INFINITY;
-            part_ml[(pidx * kHeads + head) * 2 + 1] = l_tot;
+    for (int i = 0; i < 16; i++)
+        *reinterpret_cast<uint4*>(dst + (int64_t)i * kDim) = *reinterpret_cast<const uint4*>(stg + i * kStgRow + 16 * lane);
+    if (G == 0) {
+        if (nsplit == 1) {
+            if (lse) lse[qi * kHeads + head] = l_tot > 0.0f ? (m_run + log2f(l_tot)) * 0.69314718055994531f : -INFINITY;
+        } else {
+            part_ml[(prow + head) * 2 + 0] = l_tot > 0.0f ? m_run : -INFINITY;
+            part_ml[(prow + head) * 2 + 1] = l_tot;
         }
     }
 }
@@ -401,20 +412,20 @@ __global__ __launch_bounds__(kAttThreads, 2) void sparse_attn_kernel(
 // dims. Every split's (max, sum) pair and O slice are loaded up front, so the
 // merge waits for memory once.
 
-__global__ __launch_bounds__(128) void attn_merge_kernel(const float* __restrict__ part_o,
+__global__ __launch_bounds__(128) void attn_merge_kernel(const uint16_t* __restrict__ part_o,
                                                          const float* __restrict__ part_ml, int32_t nsplit,
                                                          uint16_t* __restrict__ out, float* __restrict__ lse) {
     const int64_t qh = blockIdx.x;  // qi * 64 + head
     const int64_t qi = qh / kHeads, head = qh % kHeads;
     const int d = threadIdx.x * 4;
     f32x2 ml[kMaxSplits];
-    f32x4 po[kMaxSplits];
+    uint2 po[kMaxSplits];
 #pragma unroll
     for (int s = 0; s < kMaxSplits; s++) {
         if (s < nsplit) {
             const int64_t pidx = (qi * nsplit + s) * kHeads + head;
             ml[s] = *reinterpret_cast<const f32x2*>(part_ml + pidx * 2);
-            po[s] = *reinterpret_cast<const f32x4*>(part_o + pidx * kDim + d);
+            po[s] = *reinterpret_cast<const uint2*>(part_o + pidx * kDim + d);
         }
     }
     float M = -INFINITY;
@@ -426,9 +437,10 @@ __global__ __launch_bounds__(128) void attn_merge_kernel(const float* __restrict
 #pragma unroll
     for (int s = 0; s < kMaxSplits; s++) {
         if (s < nsplit && ml[s][0] != -INFINITY) {
-            const float f = exp2f(ml[s][0] - M);
-            L += ml[s][1] * f;
-            acc += po[s] * f;
+            const float f = ml[s][1] * exp2f(ml[s][0] - M);  // the partial is O / l
+            L += f;
+            acc += f32x4{bf16_bits_to_float(po[s].x & 0xFFFFu), bf16_bits_to_float(po[s].x >> 16),
+                         bf16_bits_to_float(po[s].y & 0xFFFFu), bf16_bits_to_float(po[s].y >> 16)} * f;
         }
     }
     const float inv = L > 0.0f ? 1.0f / L : 0.0f;
@@ -442,7 +454,7 @@ __global__ __launch_bounds__(128) void attn_merge_kernel(const float* __restrict
 size_t attn_workspace_bytes(int32_t nq, int32_t k) {
     const int ns = attn_splits(nq, k);
     if (ns <= 1) return 0;
-    return (size_t)nq * ns * kHeads * (kDim + 2) * sizeof(float);
+    return (size_t)nq * ns * kHeads * (kDim * sizeof(uint16_t) + 2 * sizeof(float));
 }
 
 int launch_sparse_attn(const uint16_t* q, const uint8_t* kv, int64_t N, int32_t nq, int32_t q_per_seq,
@@ -454,11 +466,11 @@ int launch_sparse_attn(const uint16_t* q, const uint8_t* kv, int64_t N, int32_t 
     // dynamic LDS: the largest share of main-tile entry ids a split holds
     const int mt = N > 0 ? (k + kTile - 1) / kTile : 0;
     const size_t sid_bytes = (size_t)((mt + ns - 1) / ns) * kTile * sizeof(int32_t);
-    float* part_o = nullptr;
+    uint16_t* part_o = nullptr;
     float* part_ml = nullptr;
     if (ns > 1) {
-        part_o = reinterpret_cast<float*>(ws);
-        part_ml = part_o + (size_t)nq * ns * kHeads * kDim;
+        part_o = reinterpret_cast<uint16_t*>(ws);
+        part_ml = reinterpret_cast<float*>(part_o + (size_t)nq * ns * kHeads * kDim);
     }
     const float scale_log2 = softmax_scale * 1.4426950408889634f;
     const dim3 grid((unsigned)((int64_t)nq * ns));
