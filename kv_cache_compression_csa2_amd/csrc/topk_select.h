@@ -32,7 +32,7 @@ constexpr int kBins1 = 4096;          // first-digit bins (one more holds key 0)
 // and per-wave scan / min / max words. h1 doubles as the output staging area
 // once the threshold is known.
 template <int NT>
-struct RegTk {
+struct alignas(16) RegTk {
     uint32_t h1[kBins1 + 4];
     uint32_t h2[1024];
     uint32_t h3[1024];
@@ -207,7 +207,8 @@ CSA2_DEVINL uint32_t wave_bit_select(const uint32_t* lst, int n, int s1, uint32_
 template <int NT, int KPT, bool kNarrow, class Val, class Out>
 CSA2_DEVINL uint32_t reg_select_emit(const uint32_t (&key)[KPT], uint32_t k, RegTk<NT>& sh, Val val, Out out) {
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-    for (int i = tid; i < kBins1 + 4; i += NT) sh.h1[i] = 0;
+    constexpr bool kRedundant = NT <= 256;
+    for (int i = tid; i < (kBins1 + 4) / 4; i += NT) reinterpret_cast<uint4*>(sh.h1)[i] = make_uint4(0u, 0u, 0u, 0u);
     if (tid == 0) sh.lst_n = 0;
     if (kNarrow) {
         uint32_t mx = 0u, mn = 0xFFFFFFFFu;
@@ -243,20 +244,28 @@ CSA2_DEVINL uint32_t reg_select_emit(const uint32_t (&key)[KPT], uint32_t k, Reg
 #pragma unroll
     for (int u = 0; u < KPT; u++) atomicAdd(&sh.h1[key[u] ? ((key[u] >> s1) & 4095u) : (uint32_t)kBins1], 1u);
     lds_barrier();
-    // wave 0 finds kk = min(k, nonzero keys) and T's first digit; the others
-    // wait at one barrier
-    if (wave == 0) {
-        uint32_t bb = 0, ab = 0;
-        const uint32_t kk0 = wave_pick<kBins1>(sh.h1, 0u, k, bb, ab);
-        if (lane == 0) {
-            sh.bc[0] = kk0;
-            sh.bc[1] = bb;
-            sh.bc[2] = ab;
+    // kk = min(k, nonzero keys) and T's first digit: with at most four waves
+    // every wave finds them itself; else wave 0 does and the others wait at
+    // one barrier
+    uint32_t kk, b1, above;
+    if (kRedundant) {
+        b1 = above = 0;
+        kk = wave_pick<kBins1>(sh.h1, 0u, k, b1, above);
+    } else {
+        if (wave == 0) {
+            uint32_t bb = 0, ab = 0;
+            const uint32_t kk0 = wave_pick<kBins1>(sh.h1, 0u, k, bb, ab);
+            if (lane == 0) {
+                sh.bc[0] = kk0;
+                sh.bc[1] = bb;
+                sh.bc[2] = ab;
+            }
         }
+        lds_barrier();
+        kk = sh.bc[0];
+        b1 = sh.bc[1];
+        above = sh.bc[2];
     }
-    lds_barrier();
-    const uint32_t kk = sh.bc[0], b1 = sh.bc[1];
-    uint32_t above = sh.bc[2];
     if (kk == 0) return 0;
     uint32_t rem = kk - above;  // rank of T within bin b1
     const uint32_t nb1 = sh.h1[b1];
@@ -276,19 +285,26 @@ CSA2_DEVINL uint32_t reg_select_emit(const uint32_t (&key)[KPT], uint32_t k, Reg
             }
         }
         lds_barrier();
-        if (wave == 0) {
-            uint32_t r = rem, n_eq = 0;
-            const uint32_t low = wave_bit_select(sh.lst, (int)nb1, s1, r, n_eq);
-            if (lane == 0) {
-                sh.bc[0] = low;
-                sh.bc[1] = r;
-                sh.bc[3] = n_eq;
+        if (kRedundant) {
+            uint32_t n_eq = 0;
+            const uint32_t low = wave_bit_select(sh.lst, (int)nb1, s1, rem, n_eq);
+            T = high | (b1 << s1) | low;
+            all_eq = rem == n_eq;
+        } else {
+            if (wave == 0) {
+                uint32_t r = rem, n_eq = 0;
+                const uint32_t low = wave_bit_select(sh.lst, (int)nb1, s1, r, n_eq);
+                if (lane == 0) {
+                    sh.bc[0] = low;
+                    sh.bc[1] = r;
+                    sh.bc[3] = n_eq;
+                }
             }
+            lds_barrier();
+            T = high | (b1 << s1) | sh.bc[0];
+            rem = sh.bc[1];
+            all_eq = rem == sh.bc[3];
         }
-        lds_barrier();
-        T = high | (b1 << s1) | sh.bc[0];
-        rem = sh.bc[1];
-        all_eq = rem == sh.bc[3];
     } else {
         for (int i = tid; i < 1024; i += NT) {
             sh.h2[i] = 0;
