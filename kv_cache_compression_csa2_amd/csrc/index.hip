@@ -316,7 +316,7 @@ struct PfPre<true> {
     float scale;
 };
 
-template <bool kFp4>
+template <bool kFp4, bool kBlk>
 __global__ __launch_bounds__(256, 2) void index_prefill_kernel(
     const uint16_t* __restrict__ q_idx, const float* __restrict__ w, const void* __restrict__ k_idx, int64_t N,
     int32_t q_per_seq, const int32_t* __restrict__ n_visible, float* __restrict__ scores,
@@ -422,7 +422,7 @@ __global__ __launch_bounds__(256, 2) void index_prefill_kernel(
     auto store = [&](float s, float m, int64_t q, int64_t col) {
         if (half == 0 && col < N) {
             scores[q * N + col] = s;
-            if (block_scores && (lane & 7) == 0) block_scores[q * nblk + (col >> 3)] = m;
+            if (kBlk && (lane & 7) == 0) block_scores[q * nblk + (col >> 3)] = m;
         }
     };
     // One group = 32 entries (rows h2*32.. of an LDS tile) for both queries:
@@ -446,8 +446,8 @@ __global__ __launch_bounds__(256, 2) void index_prefill_kernel(
         }
         out[0] = head_sum(pa, wa, nva, pcol, pesc);
         out[1] = head_sum(pb, wb, nvb, pcol, pesc);
-        out[2] = max8_lanes(out[0]);
-        out[3] = max8_lanes(out[1]);
+        out[2] = kBlk ? max8_lanes(out[0]) : 0.0f;  // block maxima only when asked for
+        out[3] = kBlk ? max8_lanes(out[1]) : 0.0f;
         __builtin_amdgcn_sched_group_barrier(0x100, kFp4 ? 9 : 8, 0);  // fragment reads first
         __builtin_amdgcn_sched_group_barrier(0x002, 8, 0);
 #pragma unroll
@@ -494,12 +494,15 @@ int launch_index_full(const uint16_t* q_idx, const float* w, const void* k, bool
     if (q_per_seq % kPfQueries == 0) {
         const int32_t nchunks = (int32_t)((N + kPfChunk - 1) / kPfChunk);
         const int64_t grid = (int64_t)(nq / kPfQueries) * nchunks;
-        if (kfp4)
-            hipLaunchKernelGGL(index_prefill_kernel<true>, dim3((unsigned)grid), dim3(256), 0, s, q_idx, w, k, N,
-                               q_per_seq, n_visible, scores, bs, nchunks);
-        else
-            hipLaunchKernelGGL(index_prefill_kernel<false>, dim3((unsigned)grid), dim3(256), 0, s, q_idx, w, k, N,
-                               q_per_seq, n_visible, scores, bs, nchunks);
+#define CSA2_PF(FP4, BLK)                                                                                  \
+    hipLaunchKernelGGL((index_prefill_kernel<FP4, BLK>), dim3((unsigned)grid), dim3(256), 0, s, q_idx, w, k, N, \
+                       q_per_seq, n_visible, scores, bs, nchunks)
+        if (kfp4) {
+            if (bs) CSA2_PF(true, true); else CSA2_PF(true, false);
+        } else {
+            if (bs) CSA2_PF(false, true); else CSA2_PF(false, false);
+        }
+#undef CSA2_PF
         return 0;
     }
     const int64_t ntiles = (N + 31) / 32;

@@ -147,6 +147,10 @@ def test_index_full_fp4k_matches_oracle(nq, N, qps):
     assert ok, msg
     ok, msg = rel_close(np_(b), rb)
     assert ok, msg
+    s2 = K().csa2_index_full(q, w, None, N, qps, n_visible=dev_i32(nv, DEV), k_fp4=kf)  # no blocks
+    torch.cuda.synchronize()
+    ok, msg = rel_close(np_(s2), rs)
+    assert ok, msg
 
 
 def test_index_reindex_fp4k_matches_oracle():
