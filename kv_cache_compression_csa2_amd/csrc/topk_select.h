@@ -272,9 +272,11 @@ CSA2_DEVINL uint32_t reg_select_emit(const uint32_t (&key)[KPT], uint32_t k, Reg
     uint32_t T;
     bool all_eq = false;  // every key equal to T is selected
     if (nb1 <= (uint32_t)kLst) {
+        // keys of bin b1: every nonzero key shares the bits above the digit
+        const uint32_t lo = high | (b1 << s1), width = 1u << s1;
 #pragma unroll
         for (int u = 0; u < KPT; u++) {
-            const bool m = key[u] != 0u && ((key[u] >> s1) & 4095u) == b1;
+            const bool m = key[u] != 0u && key[u] - lo < width;
             const uint64_t bal = __ballot(m);
             if (bal) {
                 uint32_t base = 0;
@@ -317,16 +319,15 @@ CSA2_DEVINL uint32_t reg_select_emit(const uint32_t (&key)[KPT], uint32_t k, Reg
         uint32_t prefix = b1;  // T's bits [s1, s1 + 12)
 #pragma unroll
         for (int u = 0; u < KPT; u++)
-            if (key[u] && ((key[u] >> s1) & 4095u) == prefix) atomicAdd(&sh.h2[(key[u] >> s2) & m2], 1u);
+            if (key[u] && key[u] - (high | (prefix << s1)) < (1u << s1)) atomicAdd(&sh.h2[(key[u] >> s2) & m2], 1u);
         lds_barrier();
         uint32_t b2 = 0;
         wave_pick<1024>(sh.h2, rem, 0u, b2, above);
         rem -= above;
         prefix = (prefix << (s1 - s2)) | b2;  // bits [s2, s1 + 12)
-        const uint32_t m12 = (1u << (12 + s1 - s2)) - 1u;
 #pragma unroll
         for (int u = 0; u < KPT; u++)
-            if (key[u] && ((key[u] >> s2) & m12) == prefix) atomicAdd(&sh.h3[(key[u] >> s3) & m3], 1u);
+            if (key[u] && key[u] - (high | (prefix << s2)) < (1u << s2)) atomicAdd(&sh.h3[(key[u] >> s3) & m3], 1u);
         lds_barrier();
         uint32_t b3 = 0;
         wave_pick<1024>(sh.h3, rem, 0u, b3, above);
