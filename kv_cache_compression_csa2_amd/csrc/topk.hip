@@ -296,6 +296,53 @@ CSA2_DEVINL void load_keys(const float* src, int n, uint32_t (&key)[KPT]) {
     }
 }
 
+// The same keys with coalesced loads: thread t loads float4 number j*NT + t
+// (positions 4(j*NT + t) .. +3, 16-byte lanes along the row) and the keys go
+// through LDS in two halves to come back as each thread's run of KPT
+// consecutive positions. stage holds NT*KPT/2 words; a barrier follows.
+template <int NT, int KPT>
+CSA2_DEVINL void load_keys_coalesced(const float* src, int n, uint32_t (&key)[KPT], uint32_t* stage) {
+    static_assert(KPT % 8 == 0, "two halves of whole float4 loads per thread");
+    constexpr int kJ = KPT / 4;            // float4 loads per thread
+    constexpr int kHalf = NT * KPT / 2;    // positions per half
+    const int tid = threadIdx.x;
+    const bool vec = (reinterpret_cast<uintptr_t>(src) & 15u) == 0;
+    uint4 v[kJ];
+#pragma unroll
+    for (int j = 0; j < kJ; j++) {
+        const int p = 4 * (j * NT + tid);
+        float4 f;
+        if (vec && p + 4 <= n) {
+            f = *reinterpret_cast<const float4*>(src + p);
+        } else {
+            f.x = p + 0 < n ? src[p + 0] : -INFINITY;
+            f.y = p + 1 < n ? src[p + 1] : -INFINITY;
+            f.z = p + 2 < n ? src[p + 2] : -INFINITY;
+            f.w = p + 3 < n ? src[p + 3] : -INFINITY;
+        }
+        v[j] = make_uint4(score_key(f.x), score_key(f.y), score_key(f.z), score_key(f.w));
+    }
+#pragma unroll
+    for (int h = 0; h < 2; h++) {
+#pragma unroll
+        for (int j = h * kJ / 2; j < (h + 1) * kJ / 2; j++)
+            *reinterpret_cast<uint4*>(stage + 4 * (j * NT + tid) - h * kHalf) = v[j];
+        lds_barrier();
+        if (tid / (NT / 2) == h) {
+            const uint32_t* run = stage + (tid - h * (NT / 2)) * KPT;
+#pragma unroll
+            for (int u = 0; u < KPT; u += 4) {
+                const uint4 w = *reinterpret_cast<const uint4*>(run + u);
+                key[u] = w.x;
+                key[u + 1] = w.y;
+                key[u + 2] = w.z;
+                key[u + 3] = w.w;
+            }
+        }
+        lds_barrier();
+    }
+}
+
 // Stage 1 (or the only stage): one NT-thread workgroup per (row, chunk), the
 // chunk's keys in registers.
 template <int NT, int KPT>
@@ -303,7 +350,10 @@ __global__ __launch_bounds__(NT) void topk_reg_chunk_kernel(
     const float* __restrict__ scores, int64_t ncols, int64_t ld, const int32_t* __restrict__ row_len, int32_t k,
     int32_t nchunks, int64_t chunk_len, const int32_t* __restrict__ id_map, int32_t* __restrict__ out_idx,
     uint32_t* __restrict__ cand_key, int32_t* __restrict__ cand_col) {
-    __shared__ RegTk<NT> sh;
+    // the selection's LDS, which first stages half of the chunk's keys
+    constexpr size_t kStageB = (size_t)NT * KPT / 2 * sizeof(uint32_t);
+    __shared__ __attribute__((aligned(16))) uint8_t smem[sizeof(RegTk<NT>) > kStageB ? sizeof(RegTk<NT>) : kStageB];
+    RegTk<NT>& sh = *reinterpret_cast<RegTk<NT>*>(smem);
     const int tid = threadIdx.x;
     const int64_t row = blockIdx.x / nchunks;
     const int64_t chunk = blockIdx.x % nchunks;
@@ -315,7 +365,10 @@ __global__ __launch_bounds__(NT) void topk_reg_chunk_kernel(
     nn = nn < chunk_len ? nn : chunk_len;
     const int n = nn > 0 ? (int)nn : 0;
     uint32_t key[KPT];
-    load_keys<KPT>(scores + row * ld + c0, n, key);
+    if constexpr (KPT % 8 == 0)
+        load_keys_coalesced<NT, KPT>(scores + row * ld + c0, n, key, reinterpret_cast<uint32_t*>(smem));
+    else
+        load_keys<KPT>(scores + row * ld + c0, n, key);
     const int p0 = tid * KPT;
     uint32_t emitted;
     if (nchunks == 1) {
