@@ -220,6 +220,36 @@ int csa2_index_topk_merge(int64_t N, int32_t nq, int32_t k, int32_t* top_idx, vo
                           hipStream_t stream);
 
 /*
+ * csa2_index_reindex_topk -- Reindex-mode scoring fused with the layer's
+ * Top-K (eogee.com report 3.3: a Reindex layer scores only the candidate pool
+ * with its own indexer query and keeps its own Top-K; report 3.5 names the
+ * fused selection kernel; titansim blog: Top-512). One launch scores chunks
+ * of the pool and selects each chunk's top-k; a second merges the chunks when
+ * a row has more than one.
+ *   q_idx, w, k_idx, N, nq, q_per_seq, n_visible, cand_blocks, nb: as
+ *           csa2_index_reindex (block_size 8).
+ *   k       1 .. CSA2_MAX_TOPK; the chunks' candidates must fit two merge
+ *           levels of 16384, else EINVAL (k = 512 always fits).
+ *   top_idx [nq][k] int32 out: csa2_topk(pool_scores, k, id_map = pool_ids)
+ *           of csa2_index_reindex's outputs -- entry ids in pool-position
+ *           order (ascending when cand_blocks is ascending), then -1 padding;
+ *           equal scores by lower pool position.
+ *   pool_scores [nq][nb*8] fp32 out or NULL: the pool row itself (checking aid).
+ *   workspace / ws_bytes: at least csa2_index_reindex_topk_workspace_bytes(nq,
+ *           nb, k) bytes (per-chunk candidates); may be NULL when that is 0.
+ * _fp4k: the same over the FP4 indexer-K cache (k_fp4 [nseq][N][68]).
+ */
+size_t csa2_index_reindex_topk_workspace_bytes(int32_t nq, int32_t nb, int32_t k);
+int csa2_index_reindex_topk(const uint16_t* q_idx, const float* w, const uint16_t* k_idx, int64_t N, int32_t nq,
+                            int32_t q_per_seq, const int32_t* n_visible, const int32_t* cand_blocks, int32_t nb,
+                            int32_t k, int32_t* top_idx, float* pool_scores, void* workspace, size_t ws_bytes,
+                            hipStream_t stream);
+int csa2_index_reindex_topk_fp4k(const uint16_t* q_idx, const float* w, const uint8_t* k_fp4, int64_t N, int32_t nq,
+                                 int32_t q_per_seq, const int32_t* n_visible, const int32_t* cand_blocks, int32_t nb,
+                                 int32_t k, int32_t* top_idx, float* pool_scores, void* workspace, size_t ws_bytes,
+                                 hipStream_t stream);
+
+/*
  * csa2_topk -- per-row Top-K selection (titansim blog, CSA2 modes: Top-512;
  * eogee.com report 3.3: Top-2048 blocks).
  *   scores  [rows][ld] fp32, columns [0, ncols) are candidates.

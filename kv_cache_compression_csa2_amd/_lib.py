@@ -52,6 +52,10 @@ def load():
     L.csa2_index_topk_fp4k.argtypes = [vp, vp, vp, i64, i32, vp, i32, vp, i32, vp, vp, vp, sz, vp]
     L.csa2_index_topk_select.argtypes = [vp, vp, vp, i32, i64, i32, vp, i32, vp, i32, vp, vp, vp, sz, vp]
     L.csa2_index_topk_merge.argtypes = [i64, i32, i32, vp, vp, sz, vp]
+    L.csa2_index_reindex_topk_workspace_bytes.argtypes = [i32, i32, i32]
+    L.csa2_index_reindex_topk_workspace_bytes.restype = sz
+    L.csa2_index_reindex_topk.argtypes = [vp, vp, vp, i64, i32, i32, vp, vp, i32, i32, vp, vp, vp, sz, vp]
+    L.csa2_index_reindex_topk_fp4k.argtypes = [vp, vp, vp, i64, i32, i32, vp, vp, i32, i32, vp, vp, vp, sz, vp]
     L.csa2_topk_workspace_bytes.argtypes = [i32, i64, i32]
     L.csa2_topk_workspace_bytes.restype = sz
     L.csa2_topk.argtypes = [vp, i32, i64, i64, vp, i32, vp, vp, vp, sz, vp]
@@ -62,7 +66,8 @@ def load():
     for name in ["fp4_kv_pack", "fp4_kv_unpack", "csa2_index_full", "csa2_index_reindex", "csa2_topk",
                  "csa2_sparse_attn", "kidx_fp4_pack", "csa2_index_full_fp4k", "csa2_index_reindex_fp4k",
                  "swa_fp8_pack", "csa2_sparse_attn_fp8w", "csa2_index_topk", "csa2_index_topk_fp4k",
-                 "csa2_index_topk_select", "csa2_index_topk_merge"]:
+                 "csa2_index_topk_select", "csa2_index_topk_merge", "csa2_index_reindex_topk",
+                 "csa2_index_reindex_topk_fp4k"]:
         getattr(L, name).restype = ctypes.c_int
     _lib = L
     return L
@@ -72,7 +77,8 @@ EXPORTS = ["csa2_format_version", "csa2_last_error", "fp4_kv_pack", "fp4_kv_unpa
            "csa2_index_reindex", "csa2_topk_workspace_bytes", "csa2_topk", "csa2_sparse_attn_workspace_bytes",
            "csa2_sparse_attn", "kidx_fp4_pack", "csa2_index_full_fp4k", "csa2_index_reindex_fp4k", "swa_fp8_pack",
            "csa2_sparse_attn_fp8w", "csa2_index_topk_workspace_bytes", "csa2_index_topk", "csa2_index_topk_fp4k",
-           "csa2_index_topk_select", "csa2_index_topk_merge"]
+           "csa2_index_topk_select", "csa2_index_topk_merge", "csa2_index_reindex_topk_workspace_bytes",
+           "csa2_index_reindex_topk", "csa2_index_reindex_topk_fp4k"]
 
 
 def _ptr(t):
@@ -239,6 +245,34 @@ def csa2_index_reindex(q_idx, w, k_idx, N, q_per_seq, cand_blocks, n_visible=Non
     _check(fn(_ptr(q_idx), _ptr(w), kp, N, nq, q_per_seq, _ptr(n_visible), _ptr(cand_blocks), nb, block_size,
               _ptr(pool_scores), _ptr(pool_ids), _stream(stream)), "csa2_index_reindex" + suffix)
     return pool_scores, pool_ids
+
+
+def csa2_index_reindex_topk_workspace_bytes(nq, nb, k):
+    return load().csa2_index_reindex_topk_workspace_bytes(nq, nb, k)
+
+
+def csa2_index_reindex_topk(q_idx, w, k_idx, N, q_per_seq, cand_blocks, k, n_visible=None, top=None,
+                            pool_scores=None, workspace=None, stream=None, k_fp4=None):
+    """Reindex-mode scores over the pool fused with the Top-k: int32 [nq, k]
+    entry ids (csa2_topk of csa2_index_reindex's pool row through its ids).
+    `pool_scores` [nq, nb*8] fp32, when given, also receives the pool row."""
+    for t, dt, nm in [(q_idx, torch.bfloat16, "q_idx"), (w, torch.float32, "w"),
+                      (cand_blocks, torch.int32, "cand_blocks"), (n_visible, torch.int32, "n_visible"),
+                      (pool_scores, torch.float32, "pool_scores")]:
+        _need(t, dt, nm)
+    kp, suffix = _k_args(k_idx, k_fp4)
+    nq, nb = cand_blocks.shape
+    dev = q_idx.device
+    if top is None:
+        top = torch.empty((nq, k), dtype=torch.int32, device=dev)
+    need = csa2_index_reindex_topk_workspace_bytes(nq, nb, k)
+    if workspace is None and need:
+        workspace = torch.empty((need,), dtype=torch.uint8, device=dev)
+    wsb = workspace.numel() * workspace.element_size() if workspace is not None else 0
+    fn = getattr(load(), "csa2_index_reindex_topk" + suffix)
+    _check(fn(_ptr(q_idx), _ptr(w), kp, N, nq, q_per_seq, _ptr(n_visible), _ptr(cand_blocks), nb, k, _ptr(top),
+              _ptr(pool_scores), _ptr(workspace), wsb, _stream(stream)), "csa2_index_reindex_topk" + suffix)
+    return top
 
 
 def csa2_topk_workspace_bytes(rows, ncols, k):

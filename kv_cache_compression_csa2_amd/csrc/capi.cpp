@@ -185,6 +185,46 @@ int csa2_index_topk_merge(int64_t N, int32_t nq, int32_t k, int32_t* top_idx, vo
     return launched("csa2_index_topk_merge");
 }
 
+size_t csa2_index_reindex_topk_workspace_bytes(int32_t nq, int32_t nb, int32_t k) {
+    if (nq <= 0 || nb < 1 || nb > 65536 || k < 1 || k > CSA2_MAX_TOPK) return 0;
+    return csa2::reindex_topk_workspace_bytes(nq, nb, k);
+}
+
+static int reindex_topk_impl(const char* who, const uint16_t* q_idx, const float* w, const void* kc, bool kfp4,
+                             int64_t N, int32_t nq, int32_t q_per_seq, const int32_t* n_visible,
+                             const int32_t* cand_blocks, int32_t nb, int32_t k, int32_t* top_idx, float* pool_scores,
+                             void* workspace, size_t ws_bytes, hipStream_t stream) {
+    int rc = check_index_common(who, q_idx, w, kc, N, nq, q_per_seq);
+    if (rc) return rc;
+    if (nb < 1 || nb > 65536) return fail(CSA2_EINVAL, "%s: nb must be in [1, 65536]", who);
+    if (k < 1 || k > CSA2_MAX_TOPK) return fail(CSA2_EINVAL, "%s: k must be in [1, %d]", who, CSA2_MAX_TOPK);
+    if (!csa2::reindex_topk_fits(nq, nb, k)) return fail(CSA2_EINVAL, "%s: pool too large for this k", who);
+    if (nq > 0 && (!cand_blocks || !top_idx)) return fail(CSA2_EINVAL, "%s: null pointer", who);
+    const size_t need = csa2_index_reindex_topk_workspace_bytes(nq, nb, k);
+    if (nq > 0 && need > 0 && (!workspace || ws_bytes < need))
+        return fail(CSA2_EWORKSPACE, "%s: workspace needs %zu bytes", who, need);
+    (void)hipGetLastError();
+    csa2::launch_index_reindex_topk(q_idx, w, kc, kfp4, N, nq, q_per_seq, n_visible, cand_blocks, nb, k, top_idx,
+                                    pool_scores, workspace, stream);
+    return launched(who);
+}
+
+int csa2_index_reindex_topk(const uint16_t* q_idx, const float* w, const uint16_t* k_idx, int64_t N, int32_t nq,
+                            int32_t q_per_seq, const int32_t* n_visible, const int32_t* cand_blocks, int32_t nb,
+                            int32_t k, int32_t* top_idx, float* pool_scores, void* workspace, size_t ws_bytes,
+                            hipStream_t stream) {
+    return reindex_topk_impl("csa2_index_reindex_topk", q_idx, w, k_idx, false, N, nq, q_per_seq, n_visible,
+                             cand_blocks, nb, k, top_idx, pool_scores, workspace, ws_bytes, stream);
+}
+
+int csa2_index_reindex_topk_fp4k(const uint16_t* q_idx, const float* w, const uint8_t* k_fp4, int64_t N, int32_t nq,
+                                 int32_t q_per_seq, const int32_t* n_visible, const int32_t* cand_blocks, int32_t nb,
+                                 int32_t k, int32_t* top_idx, float* pool_scores, void* workspace, size_t ws_bytes,
+                                 hipStream_t stream) {
+    return reindex_topk_impl("csa2_index_reindex_topk_fp4k", q_idx, w, k_fp4, true, N, nq, q_per_seq, n_visible,
+                             cand_blocks, nb, k, top_idx, pool_scores, workspace, ws_bytes, stream);
+}
+
 int kidx_fp4_pack(const uint16_t* x_bf16, int64_t n, uint8_t* out, hipStream_t stream) {
     if (n < 0) return fail(CSA2_EINVAL, "kidx_fp4_pack: n < 0");
     if (n > 0 && (!x_bf16 || !out)) return fail(CSA2_EINVAL, "kidx_fp4_pack: null pointer");

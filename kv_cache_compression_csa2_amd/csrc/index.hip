@@ -207,41 +207,68 @@ __global__ __launch_bounds__(kStreamThreads) void index_stream_kernel(
 // more than the launch, measured 106 -> 159 us at 64 x 32768).
 // Optional outputs: 8-position block maxima (the hierarchical pool's input)
 // and the scores themselves (a debug path for parity checks).
-template <bool kFp4, int kFtThreads, int kFtChunk>
+//
+// kRe: the same for a Reindex layer (eogee.com report 3.3: scoring restricted
+// to the candidate pool) -- the row is the pool, position j*8 + t holding
+// entry cand_blocks[q][j]*8 + t of sequence q / q_per_seq, and the candidates
+// carry entry ids; with ascending cand_blocks the result is the Top-K of
+// csa2_index_reindex's pool row mapped through its pool ids.
+template <bool kFp4, bool kRe, int kFtThreads, int kFtChunk>
 __global__ __launch_bounds__(kFtThreads) void index_topk_kernel(
     const uint16_t* __restrict__ q_idx, const float* __restrict__ w, const void* __restrict__ k_idx, int64_t N,
-    const int32_t* __restrict__ n_visible, int32_t k, int32_t nchunks, int32_t* __restrict__ out_idx,
-    uint32_t* __restrict__ cand_key, int32_t* __restrict__ cand_col, float* __restrict__ block_scores,
-    float* __restrict__ scores_dbg) {
+    int32_t q_per_seq, const int32_t* __restrict__ n_visible, const int32_t* __restrict__ cand_blocks, int32_t nb,
+    int32_t k, int32_t nchunks, int32_t* __restrict__ out_idx, uint32_t* __restrict__ cand_key,
+    int32_t* __restrict__ cand_col, float* __restrict__ block_scores, float* __restrict__ scores_dbg) {
     constexpr int kFtWaves = kFtThreads / 64;
     constexpr int kFtKpt = kFtChunk / kFtThreads;  // keys per thread
+    static_assert(kFtKpt >= 4 && kFtKpt % 4 == 0, "keys are read from LDS as float4");
     __shared__ __attribute__((aligned(16))) float sc[kFtChunk];
     __shared__ tk::RegTk<kFtThreads> sh;
+    // Reindex: the chunk's pool block ids (-1 past the pool)
+    __shared__ int32_t cblk[kRe ? kFtChunk / 8 : 1];
     const int64_t q = blockIdx.x / nchunks;
     const int chunk = blockIdx.x % nchunks;
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const int half = lane >> 5, col_in_tile = lane & 31;
     int64_t nv = n_visible ? (int64_t)n_visible[q] : N;
     nv = nv < N ? nv : N;
+    const int64_t ncols = kRe ? (int64_t)nb * 8 : N;  // row length: entries or pool positions
     const int64_t c0 = (int64_t)chunk * kFtChunk;
-    const int n = (int)((N - c0) < kFtChunk ? (N - c0) : kFtChunk);  // entries of this chunk
+    const int n = (int)((ncols - c0) < kFtChunk ? (ncols - c0) : kFtChunk);  // positions of this chunk
     const int ntile = (n + 31) >> 5;
     const int64_t nblk = (N + 7) >> 3;
+    if constexpr (kRe) {
+        for (int i = tid; i < kFtChunk / 8; i += kFtThreads) {
+            const int64_t b = c0 / 8 + i;
+            cblk[i] = b < nb ? cand_blocks[q * nb + b] : -1;
+        }
+        lds_barrier();
+    }
 
     StreamQuery<kFp4> Q;
     Q.load(q_idx, w, q, half, col_in_tile);
-    const void* kseq = kFp4 ? static_cast<const void*>(static_cast<const uint8_t*>(k_idx) + q * N * kKRec)
-                            : static_cast<const void*>(static_cast<const uint16_t*>(k_idx) + q * N * kIdxDim);
+    const int64_t seq = kRe ? q / q_per_seq : q;
+    const void* kseq = kFp4 ? static_cast<const void*>(static_cast<const uint8_t*>(k_idx) + seq * N * kKRec)
+                            : static_cast<const void*>(static_cast<const uint16_t*>(k_idx) + seq * N * kIdxDim);
+    // entry id at position p of the chunk (Reindex), p < n
+    auto pool_entry = [&](int p) { return (int64_t)cblk[p >> 3] * 8 + (p & 7); };
     auto load = [&](int t, StreamTile<kFp4>& st) {
-        const int64_t col = c0 + t * 32 + col_in_tile;
-        stream_load<kFp4>(kseq, col, col < nv, half, st);
+        const int p = t * 32 + col_in_tile;
+        if constexpr (kRe) {
+            const int32_t blk = p < n ? cblk[p >> 3] : -1;
+            const int64_t ent = (int64_t)blk * 8 + (p & 7);
+            stream_load<kFp4>(kseq, ent, blk >= 0 && ent < nv, half, st);
+        } else {
+            const int64_t col = c0 + p;
+            stream_load<kFp4>(kseq, col, col < nv, half, st);
+        }
     };
     auto finish = [&](int t, const StreamTile<kFp4>& st) {
         const float s = stream_score<kFp4>(Q, st);
         const int p = t * 32 + col_in_tile;
         if (half == 0) sc[p] = s;
-        if (scores_dbg && half == 0 && p < n) scores_dbg[q * N + c0 + p] = s;
-        if (block_scores) {
+        if (scores_dbg && half == 0 && p < n) scores_dbg[q * ncols + c0 + p] = s;
+        if (!kRe && block_scores) {
             const float m = max8_lanes(s);
             if (half == 0 && (lane & 7) == 0 && p < n) block_scores[q * nblk + ((c0 + p) >> 3)] = m;
         }
@@ -275,17 +302,18 @@ __global__ __launch_bounds__(kFtThreads) void index_topk_kernel(
         key[u + 2] = (p0 + u + 2 < n) ? tk::score_key(f.z) : 0u;
         key[u + 3] = (p0 + u + 3 < n) ? tk::score_key(f.w) : 0u;
     }
+    // a selected key's payload: its entry id
+    auto ent_of = [&](int u) { return (int32_t)(kRe ? pool_entry(p0 + u) : c0 + p0 + u); };
     if (nchunks == 1) {
         int32_t* out = out_idx + q * k;
         const uint32_t emitted = tk::reg_select_emit<kFtThreads, kFtKpt, true>(
-            key, (uint32_t)k, sh, [&](int u) { return (int32_t)(c0 + p0 + u); },
-            [&](uint32_t slot, uint32_t, int32_t col) { out[slot] = col; });
+            key, (uint32_t)k, sh, ent_of, [&](uint32_t slot, uint32_t, int32_t col) { out[slot] = col; });
         for (int i = (int)emitted + tid; i < k; i += kFtThreads) out[i] = -1;
     } else {
         uint32_t* ck = cand_key + (q * nchunks + chunk) * (int64_t)k;
         int32_t* cc = cand_col + (q * nchunks + chunk) * (int64_t)k;
         const uint32_t emitted = tk::reg_select_emit<kFtThreads, kFtKpt, true>(
-            key, (uint32_t)k, sh, [&](int u) { return (int32_t)(c0 + p0 + u); },
+            key, (uint32_t)k, sh, ent_of,
             [&](uint32_t slot, uint32_t kv, int32_t col) {
                 ck[slot] = kv;
                 cc[slot] = col;
@@ -536,16 +564,36 @@ int32_t index_topk_chunks(int32_t nq, int64_t N) {
 }
 
 // The merge takes at most two levels of <= 16384 candidates per row.
-bool index_topk_fits(int32_t nq, int64_t N, int32_t k) {
-    const int32_t c = index_topk_chunks(nq, N);
-    return c <= 1 || (int64_t)topk_merge_groups(c, k) * k <= 16384;
-}
+static bool chunks_fit(int32_t c, int32_t k) { return c <= 1 || (int64_t)topk_merge_groups(c, k) * k <= 16384; }
 
-size_t index_topk_workspace_bytes(int32_t nq, int64_t N, int32_t k) {
-    const int32_t c = index_topk_chunks(nq, N);
+// Reindex rows are short (nb * 8 pool positions, 16384 for the pages' 2048
+// blocks) and few: the smallest chunk of 1024 .. 8192 positions holding at
+// least 2k of them that keeps the grid within 512 workgroups (small batches
+// still spread over the GPU) and the candidates within the merge.
+int64_t reindex_topk_chunk_len(int32_t nq, int64_t ncols, int32_t k) {
+    int64_t len = 1024;
+    while (len < 8192 && len < 2 * (int64_t)k) len *= 2;
+    while (len < 8192 && (int64_t)nq * ((ncols + len - 1) / len) > 512) len *= 2;
+    while (len < 8192 && !chunks_fit((int32_t)((ncols + len - 1) / len), k)) len *= 2;
+    return len;
+}
+int32_t reindex_topk_chunks(int32_t nq, int32_t nb, int32_t k) {
+    const int64_t nc = (int64_t)nb * 8;
+    const int64_t len = reindex_topk_chunk_len(nq, nc, k);
+    return (int32_t)((nc + len - 1) / len);
+}
+static size_t chunks_workspace_bytes(int32_t nq, int32_t c, int32_t k) {
     if (c <= 1) return 0;
     const int32_t g = topk_merge_groups(c, k);
     return (size_t)nq * k * ((size_t)c + (g > 1 ? (size_t)g : 0)) * (sizeof(uint32_t) + sizeof(int32_t));
+}
+bool index_topk_fits(int32_t nq, int64_t N, int32_t k) { return chunks_fit(index_topk_chunks(nq, N), k); }
+size_t index_topk_workspace_bytes(int32_t nq, int64_t N, int32_t k) {
+    return chunks_workspace_bytes(nq, index_topk_chunks(nq, N), k);
+}
+bool reindex_topk_fits(int32_t nq, int32_t nb, int32_t k) { return chunks_fit(reindex_topk_chunks(nq, nb, k), k); }
+size_t reindex_topk_workspace_bytes(int32_t nq, int32_t nb, int32_t k) {
+    return chunks_workspace_bytes(nq, reindex_topk_chunks(nq, nb, k), k);
 }
 
 // Workspace layout of the fused call: rows x c x k candidate keys, then their
@@ -557,9 +605,9 @@ struct FtWs {
     int32_t* cc2 = nullptr;
     int32_t c = 1;
 };
-FtWs ft_ws(void* ws, int32_t nq, int64_t N, int32_t topk) {
+FtWs ft_ws_chunks(void* ws, int32_t nq, int32_t c, int32_t topk) {
     FtWs r;
-    r.c = index_topk_chunks(nq, N);
+    r.c = c;
     if (r.c > 1) {
         r.ck = reinterpret_cast<uint32_t*>(ws);
         r.cc = reinterpret_cast<int32_t*>(r.ck + (size_t)nq * r.c * topk);
@@ -571,6 +619,7 @@ FtWs ft_ws(void* ws, int32_t nq, int64_t N, int32_t topk) {
     }
     return r;
 }
+FtWs ft_ws(void* ws, int32_t nq, int64_t N, int32_t topk) { return ft_ws_chunks(ws, nq, index_topk_chunks(nq, N), topk); }
 
 int launch_index_topk(const uint16_t* q_idx, const float* w, const void* k, bool kfp4, int64_t N, int32_t nq,
                       const int32_t* n_visible, int32_t topk, int32_t* out_idx, float* block_scores,
@@ -579,9 +628,9 @@ int launch_index_topk(const uint16_t* q_idx, const float* w, const void* k, bool
     const FtWs f = ft_ws(ws, nq, N, topk);
     const bool small = index_topk_chunk_len(nq, N) == 4096;
     const dim3 grid((unsigned)((int64_t)nq * f.c));
-#define CSA2_FT(FP4, NT, CH)                                                                                    \
-    hipLaunchKernelGGL((index_topk_kernel<FP4, NT, CH>), grid, dim3(NT), 0, s, q_idx, w, k, N, n_visible, topk,   \
-                       f.c, out_idx, f.ck, f.cc, block_scores, scores_dbg)
+#define CSA2_FT(FP4, NT, CH)                                                                                   \
+    hipLaunchKernelGGL((index_topk_kernel<FP4, false, NT, CH>), grid, dim3(NT), 0, s, q_idx, w, k, N, 1, n_visible, \
+                       nullptr, 0, topk, f.c, out_idx, f.ck, f.cc, block_scores, scores_dbg)
     if (kfp4) {
         if (small) CSA2_FT(true, 512, 4096); else CSA2_FT(true, 512, 8192);
     } else {
@@ -594,6 +643,37 @@ int launch_index_topk(const uint16_t* q_idx, const float* w, const void* k, bool
 int launch_index_topk_merge(int64_t N, int32_t nq, int32_t topk, int32_t* out_idx, void* ws, hipStream_t s) {
     if (nq == 0) return 0;
     const FtWs f = ft_ws(ws, nq, N, topk);
+    if (f.c > 1) launch_topk_merge(nq, topk, f.c, f.ck, f.cc, out_idx, f.ck2, f.cc2, s);
+    return 0;
+}
+
+// Reindex scoring fused with the Top-K: the chunk kernel in Reindex mode
+// (256 threads for either key format), then the merge of the chunks'
+// candidates when a row has more than one chunk.
+int launch_index_reindex_topk(const uint16_t* q_idx, const float* w, const void* k, bool kfp4, int64_t N, int32_t nq,
+                              int32_t q_per_seq, const int32_t* n_visible, const int32_t* cand_blocks, int32_t nb,
+                              int32_t topk, int32_t* out_idx, float* pool_scores, void* ws, hipStream_t s) {
+    if (nq == 0) return 0;
+    const FtWs f = ft_ws_chunks(ws, nq, reindex_topk_chunks(nq, nb, topk), topk);
+    const int64_t len = reindex_topk_chunk_len(nq, (int64_t)nb * 8, topk);
+    const dim3 grid((unsigned)((int64_t)nq * f.c));
+#define CSA2_RT(FP4, CH)                                                                                         \
+    hipLaunchKernelGGL((index_topk_kernel<FP4, true, 256, CH>), grid, dim3(256), 0, s, q_idx, w, k, N, q_per_seq, \
+                       n_visible, cand_blocks, nb, topk, f.c, out_idx, f.ck, f.cc, nullptr, pool_scores)
+#define CSA2_RT_LEN(FP4)                   \
+    switch (len) {                         \
+        case 1024: CSA2_RT(FP4, 1024); break; \
+        case 2048: CSA2_RT(FP4, 2048); break; \
+        case 4096: CSA2_RT(FP4, 4096); break; \
+        default: CSA2_RT(FP4, 8192); break;   \
+    }
+    if (kfp4) {
+        CSA2_RT_LEN(true)
+    } else {
+        CSA2_RT_LEN(false)
+    }
+#undef CSA2_RT_LEN
+#undef CSA2_RT
     if (f.c > 1) launch_topk_merge(nq, topk, f.c, f.ck, f.cc, out_idx, f.ck2, f.cc2, s);
     return 0;
 }

@@ -33,6 +33,11 @@ int launch_index_topk(const uint16_t* q_idx, const float* w, const void* k, bool
                       const int32_t* n_visible, int32_t topk, int32_t* out_idx, float* block_scores,
                       float* scores_dbg, void* ws, hipStream_t s);
 int launch_index_topk_merge(int64_t N, int32_t nq, int32_t topk, int32_t* out_idx, void* ws, hipStream_t s);
+bool reindex_topk_fits(int32_t nq, int32_t nb, int32_t k);
+size_t reindex_topk_workspace_bytes(int32_t nq, int32_t nb, int32_t k);
+int launch_index_reindex_topk(const uint16_t* q_idx, const float* w, const void* k, bool kfp4, int64_t N, int32_t nq,
+                              int32_t q_per_seq, const int32_t* n_visible, const int32_t* cand_blocks, int32_t nb,
+                              int32_t topk, int32_t* out_idx, float* pool_scores, void* ws, hipStream_t s);
 
 size_t topk_workspace_bytes(int32_t rows, int64_t ncols, int32_t k);
 // Merge of per-chunk Top-K candidates: rows x nchunks x k (key, column) pairs

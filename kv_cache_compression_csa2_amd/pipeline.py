@@ -11,8 +11,10 @@ Every layer attends with its own Q and its own window KV.
 Decode workloads (one query per sequence) run the Full layer's scoring and
 Top-512 fused (csa2_index_topk: no score row is written; its two launches are
 timed separately); the prefill chunk scores with csa2_index_full and selects
-with csa2_topk. `debug_scores` makes the fused call also write the score rows
-(parity checks).
+with csa2_topk. Reindex layers score the pool and select in one call
+(csa2_index_reindex_topk); `fused_reindex = False` switches them to
+csa2_index_reindex + csa2_topk. `debug_scores` makes the fused calls also
+write the score rows (parity checks).
 
 Buffers are allocated once per Step object, so a timed loop allocates nothing.
 """
@@ -49,6 +51,8 @@ class Step:
         self.fused = wl.q_per_seq == 1
         self.ws_ft = ws(L.csa2_index_topk_workspace_bytes(nq, N, TOPK)) if self.fused else None
         self.debug_scores = False
+        self.fused_reindex = True
+        self.ws_rt = ws(L.csa2_index_reindex_topk_workspace_bytes(nq, POOL_BLOCKS, TOPK)) if wl.hier else None
         # FP8 window rows (the cache format; packed once, outside any timed step)
         self.swa8 = None
         if wl.swa_fmt == "fp8":
@@ -105,6 +109,12 @@ class Step:
     def reindex(self, layer, k):
         wl = self.wl
         kb, kf = self._k(k)
+        if self.fused_reindex:
+            L.csa2_index_reindex_topk(wl.q_idx[layer], wl.w[layer], kb, wl.N, wl.q_per_seq, self.cand, TOPK,
+                                      n_visible=wl.n_visible, top=self.top[layer],
+                                      pool_scores=self.pool_scores if self.debug_scores else None,
+                                      workspace=self.ws_rt, k_fp4=kf)
+            return
         L.csa2_index_reindex(wl.q_idx[layer], wl.w[layer], kb, wl.N, wl.q_per_seq, self.cand, wl.n_visible,
                              pool_scores=self.pool_scores, pool_ids=self.pool_ids, k_fp4=kf)
         L.csa2_topk(self.pool_scores, TOPK, id_map=self.pool_ids, out=self.top[layer], workspace=self.ws_topk)

@@ -152,6 +152,40 @@ def test_index_topk_rejects(kw, frag, code):
         assert rc == code and frag in msg, msg
 
 
+@pytest.mark.parametrize("kw,frag,code", [
+    (dict(k=0), "k must be", L.CSA2_EINVAL),
+    (dict(k=4097), "k must be", L.CSA2_EINVAL),
+    (dict(N=0), "N must be", L.CSA2_EINVAL),
+    (dict(nb=0), "nb must be", L.CSA2_EINVAL),
+    (dict(nb=65537), "nb must be", L.CSA2_EINVAL),
+    (dict(nq=3, qps=2), "q_per_seq", L.CSA2_EINVAL),
+    (dict(nb=65536, k=4096), "too large", L.CSA2_EINVAL),   # 64 chunks of 8192 x 4096 slots: beyond the merge
+    (dict(top=None), "null pointer", L.CSA2_EINVAL),
+    (dict(blocks=None), "null pointer", L.CSA2_EINVAL),
+    (dict(ws=None), "workspace", L.CSA2_EWORKSPACE),
+    (dict(wsb=8), "workspace", L.CSA2_EWORKSPACE),
+])
+def test_index_reindex_topk_rejects(kw, frag, code):
+    a = dict(N=40000, nq=4, qps=1, nb=2048, k=512, blocks=P, top=P, ws=P, wsb=1 << 40)
+    a.update(kw)
+    L_ = K.load()
+    for name in ("csa2_index_reindex_topk", "csa2_index_reindex_topk_fp4k"):
+        rc, msg = _err(getattr(L_, name)(P, P, P, a["N"], a["nq"], a["qps"], None, a["blocks"], a["nb"], a["k"],
+                                         a["top"], None, a["ws"], a["wsb"], S))
+        assert rc == code and frag in msg and msg.startswith(name), msg
+
+
+def test_index_reindex_topk_workspace_sizes():
+    # 32 x 2048 blocks (16384 positions): chunks of 1024 (512 workgroups), 16 x 512 candidates per row
+    assert K.csa2_index_reindex_topk_workspace_bytes(32, 2048, 512) == 32 * 16 * 512 * 8
+    # 64 queries: chunks of 2048 keep the grid at 512 workgroups
+    assert K.csa2_index_reindex_topk_workspace_bytes(64, 2048, 512) == 64 * 8 * 512 * 8
+    # k = 2048: chunks of at least 4096 positions
+    assert K.csa2_index_reindex_topk_workspace_bytes(8, 2048, 2048) == 8 * 4 * 2048 * 8
+    # a pool of one chunk: no workspace
+    assert K.csa2_index_reindex_topk_workspace_bytes(4, 100, 512) == 0
+
+
 def test_index_topk_workspace_sizes():
     # 64 x 32768: chunks of 4096 (8192 would give only 256 workgroups), candidates (key + id) of every chunk
     assert K.csa2_index_topk_workspace_bytes(64, 32768, 512) == 64 * 8 * 512 * 8

@@ -158,6 +158,16 @@ def test_workload_parity(name):
         assert ovc.mean() >= 0.995
         pool = O.pool_ids(cand_o, 8)
         assert all(set(top_o[j].tolist()) <= set(pool[j].tolist()) for j in range(len(Qs)))
+        if step.fused_reindex and wl.reindex_layers:
+            # the fused Reindex selection (last layer) is csa2_topk of its own pool row
+            lr = wl.reindex_layers[-1]
+            ps_u, pid_u = K.csa2_index_reindex(wl.q_idx[lr], wl.w[lr], None if fp4k else kk, wl.N, wl.q_per_seq,
+                                               step.cand, n_visible=wl.n_visible, k_fp4=kk if fp4k else None)
+            t_u = K.csa2_topk(ps_u, 512, id_map=pid_u)
+            torch.cuda.synchronize()
+            assert torch.equal(ps_u, step.pool_scores)
+            assert torch.equal(t_u, step.top[lr])
+            print("  fused reindex + Top-K equals the unfused calls", flush=True)
         for layer in wl.reindex_layers:
             ps_o = O.index_reindex(u16(wl.q_idx[layer][qt]), np_(wl.w[layer][qt]), k_sub, wl.N, 1, pool,
                                    n_visible=nv, k_fp4=kf_sub)

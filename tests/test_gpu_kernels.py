@@ -175,13 +175,13 @@ def test_index_reindex_fp4k_matches_oracle():
 
 # ------------------------------------------------------ fused scoring + Top-K
 
-def _int_idx_inputs(nq, N, seed):
+def _int_idx_inputs(nq, N, seed, nseq=None):
     """Small-integer queries and keys and power-of-two weights: every score is
     an exact fp32 value whatever the summation order, with many ties."""
     g = _g(seed)
     q = torch.randint(-2, 3, (nq, 32, 128), generator=g, device=DEV).to(torch.bfloat16)
     w = torch.exp2(torch.randint(-2, 2, (nq, 32), generator=g, device=DEV).float())
-    k = torch.randint(-2, 3, (nq, N, 128), generator=g, device=DEV).to(torch.bfloat16)
+    k = torch.randint(-2, 3, (nq if nseq is None else nseq, N, 128), generator=g, device=DEV).to(torch.bfloat16)
     return q, w, k
 
 
@@ -280,6 +280,63 @@ def test_index_reindex_matches_oracle():
     ok, msg = rel_close(np_(ps), ref)
     assert ok, msg
     assert np.array_equal(np_(pid), pool_vis)
+
+
+def _pool_blocks(nq, N, nb, seed):
+    """Ascending distinct block ids per query, the last rows' tails padded with -1."""
+    rng = np.random.default_rng(seed)
+    nblk = (N + 7) // 8
+    b = np.sort(np.stack([rng.choice(nblk, min(nb, nblk), replace=False) for _ in range(nq)]), 1).astype(np.int32)
+    if b.shape[1] < nb:
+        b = np.concatenate([b, np.full((nq, nb - b.shape[1]), -1, np.int32)], 1)
+    if nq > 1:
+        b[1, -5:] = -1
+    return b
+
+
+@pytest.mark.parametrize("nq,N,nb,k,qps,fp4", [(3, 9000, 300, 512, 1, False), (2, 70000, 2048, 512, 1, False),
+                                               (4, 70000, 2048, 512, 2, False), (2, 70000, 2048, 2048, 1, False),
+                                               (3, 20000, 2048, 512, 1, True), (40, 40000, 2048, 512, 1, False),
+                                               (2, 5000, 10, 512, 1, False), (3, 9000, 300, 100, 3, True)])
+def test_index_reindex_topk_bit_exact_on_exact_scores(nq, N, nb, k, qps, fp4):
+    """With exact scores the fused Reindex selection must equal the oracle's
+    Top-K of the oracle's pool row through the pool ids, ties included (one
+    and several chunks of each length, queries sharing a sequence, padding
+    blocks, a pool smaller than k, FP4 keys)."""
+    print("case: reindex_topk exact", nq, N, nb, k, qps, fp4, flush=True)
+    q, w, kb = _int_idx_inputs(nq, N, 900 + N + nb + k, nseq=nq // qps)
+    blocks = _pool_blocks(nq, N, nb, N + nb)
+    nv = np.array([N, N // 2, 3 * N // 4, 9, N, N // 3] * 8, np.int32)[:nq]
+    pool = O.pool_ids(blocks, 8)
+    if fp4:
+        kf_host = O.kidx_fp4_pack(u16(kb)).reshape(nq // qps, N, 68)
+        kf = torch.tensor(kf_host, device=DEV)
+        top = K().csa2_index_reindex_topk(q, w, None, N, qps, dev_i32(blocks, DEV), k, n_visible=dev_i32(nv, DEV),
+                                          k_fp4=kf)
+        ref = O.index_reindex(u16(q), np_(w), None, N, qps, pool, n_visible=nv, k_fp4=kf_host)
+    else:
+        top = K().csa2_index_reindex_topk(q, w, kb, N, qps, dev_i32(blocks, DEV), k, n_visible=dev_i32(nv, DEV))
+        ref = O.index_reindex(u16(q), np_(w), u16(kb), N, qps, pool, n_visible=nv)
+    torch.cuda.synchronize()
+    assert np.array_equal(np_(top), O.topk(ref, k, id_map=pool))
+
+
+def test_index_reindex_topk_matches_the_unfused_path():
+    """Random inputs at the pages' pool size (2048 blocks): the fused call's
+    debug pool row is csa2_index_reindex's, and its selection is csa2_topk of
+    that row through the pool ids."""
+    print("case: reindex_topk random", flush=True)
+    nq, N, nb = 8, 100000, 2048
+    q, w, kb = _idx_inputs(nq, N, nq, 910)
+    blocks = dev_i32(_pool_blocks(nq, N, nb, 911), DEV)
+    nv = dev_i32(np.array([N, 90000, 513, 20, N, 70000, 99999, 50000], np.int32), DEV)
+    ps = torch.empty((nq, nb * 8), dtype=torch.float32, device=DEV)
+    top = K().csa2_index_reindex_topk(q, w, kb, N, 1, blocks, 512, n_visible=nv, pool_scores=ps)
+    ps_ref, pid = K().csa2_index_reindex(q, w, kb, N, 1, blocks, n_visible=nv)
+    t_ref = K().csa2_topk(ps_ref, 512, id_map=pid)
+    torch.cuda.synchronize()
+    assert torch.equal(ps, ps_ref)
+    assert torch.equal(top, t_ref)
 
 
 # ------------------------------------------------------------------ Top-K
