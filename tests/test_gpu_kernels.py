@@ -482,6 +482,25 @@ def test_sparse_attn_degenerate():
     assert torch.all(out2 == 0) and torch.all(torch.isneginf(lse2))
 
 
+def test_zero_queries():
+    """Every call accepts an empty batch and launches nothing."""
+    print("case: zero queries", flush=True)
+    e = lambda *shape, dt=torch.bfloat16: torch.empty(shape, dtype=dt, device=DEV)
+    N = 4096
+    q, w = e(0, 32, 128), e(0, 32, dt=torch.float32)
+    kb = _bf16((1, N, 128), 31)
+    blocks = e(0, 2048, dt=torch.int32)
+    s = K().csa2_index_full(q, w, kb, N, 1)
+    top = K().csa2_index_topk(q, w, kb, N, 512)
+    ps, pid = K().csa2_index_reindex(q, w, kb, N, 1, blocks)
+    rt = K().csa2_index_reindex_topk(q, w, kb, N, 1, blocks, 512)
+    t = K().csa2_topk(e(0, N, dt=torch.float32), 512)
+    out, lse = K().csa2_sparse_attn(e(0, 64, 512), _records(N, 32).view(1, N, 288), N, 1, e(0, 512, dt=torch.int32))
+    torch.cuda.synchronize()
+    for x in (s, top, ps, pid, rt, t, out, lse):
+        assert x.shape[0] == 0
+
+
 def test_sparse_attn_decode_exact():
     """A query that attends to one entry outputs that entry's value exactly
     (softmax weight 1): every decoded E2M1 x E4M3 product must equal the
