@@ -4,23 +4,26 @@
 //
 // Scores map to order-preserving 32-bit keys (larger key = larger score, -0
 // folded onto +0, -inf and NaN to key 0 = never chosen). A workgroup finds the
-// exact k-th largest key T with a 3-pass MSB radix select (12, 10, 10 bits)
-// over LDS histograms, then emits every key > T plus the lowest-column ties
-// == T, in column order -- so the output is already ascending.
+// exact k-th largest key T with an MSB radix select over LDS histograms (a
+// 12-bit first digit; the few keys of T's bin are then resolved by one wave,
+// or by two more digits when the bin is crowded), then emits every key > T
+// plus the lowest-column ties == T, in column order -- so the output is
+// already ascending.
 //
 // Long rows are split: stage 1 selects the top-k of each chunk as (key,
 // column) candidates; stage 2 selects the row's top-k among the candidates.
 // A row's top-k entry is in its chunk's top-k (fewer than k chunk entries can
 // beat it), so the two stages give the same set as one pass.
 //
-// Main path: each thread of a 256- or 1024-thread workgroup holds a
+// Main path: each thread of a 256- to 1024-thread workgroup holds a
 // contiguous run of up to 32 keys (chunks <= 32768 keys, merges <= 16384
-// candidates) in registers, so the radix passes read no memory; wave scans use
-// DPP, and the ordered emission is one packed block scan of per-thread
-// (> T, == T) counts followed by in-order writes. The merge stage starts its
-// first digit at the highest bit where its candidates differ, since they sit
-// in a narrow band at the top of the row. Shapes beyond those capacities take
-// the global-memory path (512 threads, every pass re-reads the scores through
+// candidates) in registers, so the radix passes read no memory; the chunk
+// keys arrive with coalesced loads through LDS. Wave scans use DPP, and the
+// ordered emission is one packed block scan of per-thread counts followed by
+// an LDS-staged, coalesced write. Every select's first digit starts at the
+// highest bit where the segment's keys differ, since score rows and merged
+// candidates sit in narrow bands. Shapes beyond those capacities take the
+// global-memory path (512 threads, every pass re-reads the scores through
 // the caches).
 #include <math.h>
 
