@@ -13,11 +13,14 @@
 // byte accounting). FP4 codes decode exactly to bf16 and feed the same MFMA;
 // s multiplies the entry's head sum once (ReLU(s x) = s ReLU(x), s >= 0).
 //
-// Two kernels:
+// Three kernels:
 //  * index_stream_kernel -- one query per workgroup slice; each wave streams
 //    32-entry tiles of the indexer K straight from HBM into MFMA operand
 //    registers (2 tiles in flight). Bound by HBM (256 B per entry per query).
 //    Serves decode (a sequence per query) and the Reindex pool gather.
+//  * index_topk_kernel -- the same streaming score for a chunk of a row, kept
+//    in LDS and reduced to the chunk's top-k candidates (decode Full layers,
+//    and Reindex layers over their pool); a merge finishes the row.
 //  * index_prefill_kernel -- many queries over one sequence: a workgroup holds
 //    8 queries' operands in registers and stages 64-entry K tiles in LDS, so
 //    each K byte read from L2 feeds 8 queries. Bound by MFMA.
