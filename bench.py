@@ -270,10 +270,21 @@ def cpu_baseline(torch, target_s=15.0):
                       "%.1f s of CPU time" % (reps, n, total)}
 
 
-def traffic_from_profiles(kernel_src):
+# sources the fused scoring + Top-K kernel is compiled from
+KERNEL_SOURCES = ["index.hip", "topk_select.h", "device_common.h"]
+
+
+def kernel_source_hash():
+    h = hashlib.sha256()
+    for f in KERNEL_SOURCES:
+        h.update(open(os.path.join(ROOT, "kv_cache_compression_csa2_amd", "csrc", f), "rb").read())
+    return h.hexdigest()[:16]
+
+
+def traffic_from_profiles():
     """HBM bytes per launch of the dominant kernel from the committed rocprofv3
     counter summary (FETCH_SIZE + WRITE_SIZE, calibrated on a 1 GiB copy), if it
-    was taken on the current kernel source; else None."""
+    was taken on the current kernel sources; else None."""
     path = os.path.join(ROOT, "profiles", "index_topk_encoder64k_traffic.md")
     if not os.path.exists(path):
         return None
@@ -282,8 +293,7 @@ def traffic_from_profiles(kernel_src):
         if ":" in line and not line.startswith(("|", "#", "`", "rocprof")):
             k, v = line.split(":", 1)
             fields[k.strip()] = v.strip()
-    h = hashlib.sha256(open(kernel_src, "rb").read()).hexdigest()[:16]
-    if fields.get("kernel_source_sha256_16") != h or "hbm_bytes_per_launch" not in fields:
+    if fields.get("kernel_source_sha256_16") != kernel_source_hash() or "hbm_bytes_per_launch" not in fields:
         return None
     return int(fields["hbm_bytes_per_launch"])
 
@@ -333,10 +343,9 @@ def main():
     # "index_topk" span)
     t_idx_s = h["_calls_mean_ms"]["index_topk"] * 1e-3  # mean launch duration
     achieved = h["_alg_bytes_index_topk"] / t_idx_s / 1e9
-    src = os.path.join(ROOT, "kv_cache_compression_csa2_amd", "csrc", "index.hip")
     roofline = {"kernel": "index_topk_kernel (csa2_index_topk_select: Full scoring + per-chunk Top-512)",
                 "bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": traffic_from_profiles(src),
+                "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": traffic_from_profiles(),
                 "alg_bytes_per_launch": h["_alg_bytes_index_topk"]}
     cpu = None
     if not args.no_cpu:
