@@ -352,7 +352,8 @@ def _topk_check(scores_np, k, row_len=None, id_map=None):
 
 @pytest.mark.parametrize("rows,n,k", [(1, 1024, 512), (3, 1000, 512), (64, 32768, 512), (8, 131072, 2048),
                                       (4, 300001, 512), (2, 1 << 20, 512), (300, 5000, 512), (2, 100, 4096),
-                                      (2, 32769, 512), (3, 65536, 2048), (2, 300000, 4096), (1, 40000, 3)])
+                                      (2, 32769, 512), (3, 65536, 2048), (2, 300000, 4096), (1, 40000, 3),
+                                      (2, 40000, 4096)])
 def test_topk_bit_exact_on_oracle_scores(rows, n, k):
     print("case: topk", rows, n, k, flush=True)
     rng = np.random.default_rng(rows * 7 + n)
