@@ -188,8 +188,11 @@ CSA2_DEVINL uint32_t wave_bit_select(const uint32_t* lst, int n, int s1, uint32_
 // t*KPT .. t*KPT+KPT-1 of the segment; key 0 = never selected). An MSB radix
 // select finds the k-th largest key T: a 12-bit first digit over an LDS
 // histogram, then -- when T's bin holds at most kLst keys, the usual case --
-// those keys are gathered and one wave finishes the remaining bits with
-// ballots; otherwise two more 10-bit histogram digits. Every key > T and the
+// those keys are gathered and one wave resolves T among them (every wave, in
+// workgroups of at most four waves, so no barrier is needed): a rank count
+// with one key per lane up to 64 keys, else the remaining bits MSB-first with
+// ballots; a crowded bin takes two more 10-bit histogram digits. The bin and
+// the threshold are found the same way. Every key > T and the
 // first `need` keys == T are selected, slots ascending with position (one
 // packed block scan of the per-thread counts; when every key equal to T is
 // taken, a key is selected iff it is >= T). out(slot, key, val(u)) is called
