@@ -442,18 +442,28 @@ __global__ __launch_bounds__(256, 2) void index_prefill_kernel(
     };
     // ReLU-weighted head sum of one query's 32 x 32 block (times the entry's
     // scale for FP4 K); valid in lanes 0..31.
-    auto head_sum = [&](const f32x16& acc, const float (&wr)[16], int64_t nv, int64_t col, float esc) {
-        float s = 0.0f;
+    // ReLU-weighted head sums of both queries' 32 x 32 blocks, one query per
+    // half-wave: each lane sums its 16 heads of each query, and one half-wave
+    // swap hands lanes 0..31 both halves of query a and lanes 32..63 both
+    // halves of query b (times the entry's scale for FP4 K).
+    const int64_t nv_mine = half ? nvb : nva;
+    auto head_sums = [&](const f32x16& acca, const f32x16& accb, int64_t col, float esc) {
+        float sa = 0.0f, sb = 0.0f;
 #pragma unroll
-        for (int r = 0; r < 16; r++) s = fmaf(wr[r], relu_bits(acc[r]), s);
-        s += from_upper_half(s);
+        for (int r = 0; r < 16; r++) {
+            sa = fmaf(wa[r], relu_bits(acca[r]), sa);
+            sb = fmaf(wb[r], relu_bits(accb[r]), sb);
+        }
+        const auto x = __builtin_amdgcn_permlane32_swap(__float_as_uint(sa), __float_as_uint(sb), false, false);
+        float s = __uint_as_float(x[0]) + __uint_as_float(x[1]);
         if constexpr (kFp4) s *= esc;
-        return col < nv ? s : -INFINITY;
+        return col < nv_mine ? s : -INFINITY;
     };
-    auto store = [&](float s, float m, int64_t q, int64_t col) {
-        if (half == 0 && col < N) {
-            scores[q * N + col] = s;
-            if (kBlk && (lane & 7) == 0) block_scores[q * nblk + (col >> 3)] = m;
+    const int64_t q_mine = half ? qb : qa;
+    auto store = [&](float s, float m, int64_t col) {
+        if (col < N) {
+            scores[q_mine * N + col] = s;
+            if (kBlk && (lane & 7) == 0) block_scores[q_mine * nblk + (col >> 3)] = m;
         }
     };
     // One group = 32 entries (rows h2*32.. of an LDS tile) for both queries:
@@ -462,7 +472,7 @@ __global__ __launch_bounds__(256, 2) void index_prefill_kernel(
     // the shadow of these MFMAs. The group's entry scale (FP4 K) is read here,
     // while its tile is still in LDS, and travels with the accumulators.
     auto group = [&](int buf, int h2, f32x16& acca, f32x16& accb, float& esc, const f32x16& pa, const f32x16& pb,
-                     float pesc, int64_t pcol, float (&out)[4]) {
+                     float pesc, int64_t pcol, float (&out)[2]) {
         const uint8_t* rowp = lds[buf] + (h2 * 32 + col_in_tile) * kPfRow + half * 16;
         bf16x8 bj[8];
 #pragma unroll
@@ -475,10 +485,8 @@ __global__ __launch_bounds__(256, 2) void index_prefill_kernel(
             acca = mfma32x32x16(aa[j], bj[j], acca);
             accb = mfma32x32x16(ab[j], bj[j], accb);
         }
-        out[0] = head_sum(pa, wa, nva, pcol, pesc);
-        out[1] = head_sum(pb, wb, nvb, pcol, pesc);
-        out[2] = kBlk ? max8_lanes(out[0]) : 0.0f;  // block maxima only when asked for
-        out[3] = kBlk ? max8_lanes(out[1]) : 0.0f;
+        out[0] = head_sums(pa, pb, pcol, pesc);
+        out[1] = kBlk ? max8_lanes(out[0]) : 0.0f;  // block maxima only when asked for
         __builtin_amdgcn_sched_group_barrier(0x100, kFp4 ? 9 : 8, 0);  // fragment reads first
         __builtin_amdgcn_sched_group_barrier(0x002, 8, 0);
 #pragma unroll
@@ -493,7 +501,7 @@ __global__ __launch_bounds__(256, 2) void index_prefill_kernel(
     lds_barrier();
     f32x16 pa, pb, ca, cb;
     float pesc = 1.0f, cesc = 1.0f;
-    float out[4];
+    float out[2];
     {
         const f32x16 z = {};
         group(0, 0, pa, pb, pesc, z, z, 1.0f, N, out);  // no previous group: its results are discarded
@@ -504,14 +512,12 @@ __global__ __launch_bounds__(256, 2) void index_prefill_kernel(
         const Pre nxt = gload(more ? st + 1 : 0);
         const int64_t col0 = tile_base + (int64_t)st * kPfSub + col_in_tile;
         group(st & 1, 1, ca, cb, cesc, pa, pb, pesc, col0, out);
-        store(out[0], out[2], qa, col0);
-        store(out[1], out[3], qb, col0);
+        store(out[0], out[1], col0);
         if (more) lstore((st + 1) & 1, nxt);
         lds_barrier();
         // After the last tile this reads the stale buffer; those results are never stored.
         group((st + 1) & 1, 0, pa, pb, pesc, ca, cb, cesc, col0 + 32, out);
-        store(out[0], out[2], qa, col0 + 32);
-        store(out[1], out[3], qb, col0 + 32);
+        store(out[0], out[1], col0 + 32);
     }
 }
 
