@@ -312,7 +312,7 @@ def main():
                     help="only run a 1 GiB device copy (counter calibration for rocprofv3 --pmc)")
     args = ap.parse_args()
     if args.gpus != 1:
-        print("bench.py: this build runs on one GPU only; --gpus %d is not supported" % args.gpus, file=sys.stderr)
+        print("bench.py: the benchmark runs on one GPU only; --gpus %d is not supported" % args.gpus, file=sys.stderr)
         sys.exit(2)
     import torch
     import kv_cache_compression_csa2_amd as K
