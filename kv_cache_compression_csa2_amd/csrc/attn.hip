@@ -395,9 +395,20 @@ __global__ __launch_bounds__(kAttThreads, 2) void sparse_attn_kernel(
     lds_barrier();
     const int64_t prow = nsplit == 1 ? qi * kHeads : (qi * nsplit + split) * kHeads;  // row of head 0
     uint16_t* dst = (nsplit == 1 ? out : part_o) + (prow + wave * 16) * kDim + 8 * lane;
+    // Split partials go out with non-temporal stores: written once and read by
+    // the merge, they would otherwise sit in L2 as dirty lines, whose later
+    // write-back measurably slowed the kernel after the step's attention. The
+    // unsplit (large-batch) output keeps ordinary stores, which measured faster.
+    if (nsplit > 1) {
 #pragma unroll
-    for (int i = 0; i < 16; i++)
-        *reinterpret_cast<uint4*>(dst + (int64_t)i * kDim) = *reinterpret_cast<const uint4*>(stg + i * kStgRow + 16 * lane);
+        for (int i = 0; i < 16; i++)
+            __builtin_nontemporal_store(*reinterpret_cast<const u32x4*>(stg + i * kStgRow + 16 * lane),
+                                        reinterpret_cast<u32x4*>(dst + (int64_t)i * kDim));
+    } else {
+#pragma unroll
+        for (int i = 0; i < 16; i++)
+            *reinterpret_cast<uint4*>(dst + (int64_t)i * kDim) = *reinterpret_cast<const uint4*>(stg + i * kStgRow + 16 * lane);
+    }
     if (G == 0) {
         if (nsplit == 1) {
             if (lse) lse[qi * kHeads + head] = l_tot > 0.0f ? (m_run + log2f(l_tot)) * 0.69314718055994531f : -INFINITY;
@@ -444,8 +455,9 @@ __global__ __launch_bounds__(128) void attn_merge_kernel(const uint16_t* __restr
         }
     }
     const float inv = L > 0.0f ? 1.0f / L : 0.0f;
-    *reinterpret_cast<uint2*>(out + qh * kDim + d) =
-        make_uint2(pack_bf16x2(acc[0] * inv, acc[1] * inv), pack_bf16x2(acc[2] * inv, acc[3] * inv));
+    uint32_t* o32 = reinterpret_cast<uint32_t*>(out + qh * kDim + d);  // non-temporal, as the split partials
+    __builtin_nontemporal_store(pack_bf16x2(acc[0] * inv, acc[1] * inv), o32);
+    __builtin_nontemporal_store(pack_bf16x2(acc[2] * inv, acc[3] * inv), o32 + 1);
     if (lse && threadIdx.x == 0) lse[qh] = L > 0.0f ? (M + log2f(L)) * 0.69314718055994531f : -INFINITY;
 }
 
