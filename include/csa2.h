@@ -38,6 +38,10 @@
  *     calling thread's last failure.
  *   - Geometry is fixed: 512-channel main entries in 288-byte records, 32 x 128
  *     indexer heads, 64 x 512 attention heads, sliding windows of at most 128.
+ *   - Query, key, record, window, output and workspace arrays are accessed
+ *     with 16-byte vector loads and stores: their base pointers must be
+ *     16-byte aligned (hipMalloc and torch allocations are). csa2_topk's score
+ *     rows may start at any 4-byte boundary (unaligned rows take scalar loads).
  */
 #ifndef CSA2_H
 #define CSA2_H
