@@ -564,14 +564,21 @@ void launch_reg_merge_any(int32_t rows, int32_t k, int32_t c, const int32_t* id_
 
 }  // namespace
 
-// Two-level merges use groups of up to 8192 candidates (half the merge
-// capacity): twice the workgroups of the first level, each with half the
-// keys (measured at 8 x 128 chunks x 512: 35.9 us with 16384-candidate groups).
-constexpr int kGroupCand = kRegMaxCand / 2;
+// Two-level merges: first-level groups of 2048 candidates where the second
+// level still fits the merge capacity (more, smaller workgroups: 20.7 against
+// 23.0 us with 8192-candidate groups, and 35.9 us with 16384, at 8 rows x 128
+// chunks x 512), else groups of up to 8192 candidates.
+static int32_t merge_chunks_per_group(int32_t nchunks, int32_t k) {
+    for (const int32_t cand : {2048, kRegMaxCand / 2}) {
+        const int32_t cpg = k <= cand ? cand / k : 1;
+        if ((int64_t)((nchunks + cpg - 1) / cpg) * k <= kRegMaxCand) return cpg;
+    }
+    return k <= kRegMaxCand / 2 ? (kRegMaxCand / 2) / k : 1;
+}
 
 int32_t topk_merge_groups(int32_t nchunks, int32_t k) {
     if ((int64_t)nchunks * k <= kRegMaxCand) return 1;
-    const int32_t cpg = k <= kGroupCand ? kGroupCand / k : 1;
+    const int32_t cpg = merge_chunks_per_group(nchunks, k);
     return (nchunks + cpg - 1) / cpg;
 }
 
@@ -583,7 +590,7 @@ int launch_topk_merge(int32_t rows, int32_t k, int32_t nchunks, const uint32_t* 
         launch_reg_merge_any(rows, k, nchunks, nullptr, 0, ck, cc, out_idx, s);
         return 0;
     }
-    const int32_t cpg = k <= kGroupCand ? kGroupCand / k : 1;
+    const int32_t cpg = merge_chunks_per_group(nchunks, k);
     const RegShape m = reg_shape((int64_t)cpg * k);
     const dim3 g1((unsigned)((int64_t)rows * ng));
     if (m.nt == 256)

@@ -189,8 +189,11 @@ def test_index_reindex_topk_workspace_sizes():
 def test_index_topk_workspace_sizes():
     # 64 x 32768: chunks of 4096 (8192 would give only 256 workgroups), candidates (key + id) of every chunk
     assert K.csa2_index_topk_workspace_bytes(64, 32768, 512) == 64 * 8 * 512 * 8
-    # 8 x 2^20: 128 chunks, two merge levels of 16-chunk groups (8 groups)
-    assert K.csa2_index_topk_workspace_bytes(8, 1 << 20, 512) == 8 * 512 * (128 + 8) * 8
+    # 8 x 2^20: 128 chunks, two merge levels of 4-chunk groups (32 groups of 2048 candidates)
+    assert K.csa2_index_topk_workspace_bytes(8, 1 << 20, 512) == 8 * 512 * (128 + 32) * 8
+    # k = 1024 at 2^20: 2048-candidate groups would leave 64 x 1024 for the second level;
+    # 8-chunk groups of 8192 candidates keep it at 16 x 1024
+    assert K.csa2_index_topk_workspace_bytes(8, 1 << 20, 1024) == 8 * 1024 * (128 + 16) * 8
     # one chunk per query: no workspace
     assert K.csa2_index_topk_workspace_bytes(64, 4096, 512) == 0
     # few queries: chunks of 4096
