@@ -629,9 +629,11 @@ int launch_topk(const float* scores, int32_t rows, int64_t ncols, int64_t ld, co
         const dim3 g1((unsigned)((int64_t)rows * c));
         const RegShape a = reg_shape(chunk_len);
 #define CSA2_CHUNK(NT, KPT) launch_reg_chunk<NT, KPT>(g1, s, scores, ncols, ld, row_len, k, c, chunk_len, id_map, out_idx, ck, cc)
-        if (chunk_len > 8192 && chunk_len <= 16384) {
+        if (chunk_len > 8192 && chunk_len <= 16384 && (int64_t)rows * c >= 256) {
             // 512 threads x 32 keys: measured 23% faster than 1024 x 16 for
-            // 4096 rows x 65536 scores (two workgroups of 8 waves per CU)
+            // 4096 rows x 65536 scores (two workgroups of 8 waves per CU);
+            // with fewer workgroups than CUs, 1024 x 16 is faster (8 rows x
+            // 131072 block scores, k = 2048: 26.5 against 28.6 us)
             CSA2_CHUNK(512, 32);
         } else if (a.nt == 256) {
             switch (a.kpt) {
