@@ -19,7 +19,8 @@
  *          and 3.3 (index_n_heads 32, index_head_dim 128, index_topk 512,
  *          candidate_topk_blocks 2048, candidate_block_size 8).
  *   [OCP]  OCP Microscaling Formats (MX) v1.0, the "OCP standard" [EOG] 3.4
- *          names: E2M1 and E4M3 element encodings.
+ *          names: E2M1 and E4M3 element encodings, E8M0 shared scales and
+ *          the rule that picks a block's shared scale.
  *
  * Readings where the pages are silent (each is listed in the design notes):
  *   indexer score = sum_h w_h * max(q_h . k, 0); block score = max of its 8
@@ -28,8 +29,11 @@
  *   elements rounded to the nearest E2M1 grid value, ties to the even code.
  *   FP4 indexer K (the pages' storage precision, implied by the 890 B/token
  *   accounting of [TIT] and [EOG] 5.3: 2.5 entries/token x (288 B main KV +
- *   68 B indexer K)): 128 E2M1 codes (64 B) + one binary32 scale (4 B) per
- *   entry, scale = amax / 6 in float, codes by the same nearest-grid rule.
+ *   68 B indexer K); [EOG] 3.4 says the predecessor already ran FP4 on the
+ *   indexer Q/K and names the OCP MXFP4 standard for the cache): read as OCP
+ *   MXFP4 proper, 128 E2M1 codes (64 B) + one E8M0 scale per 32 channels
+ *   (4 B), X = 2^(floor(log2 amax) - 2), elements = nearest E2M1 value of
+ *   x / X, ties to even, saturating at 6.
  *   FP8 window KV ([EOG] 3.4 keeps the SWA KV in FP8; the element type and
  *   scaling follow the OCP MX standard the same passage names, i.e. MXFP8):
  *   E4M3 elements, one E8M0 scale per 32 channels, X = 2^(floor(log2 amax) -
@@ -56,7 +60,8 @@
 #define ORC_DIM 512
 #define ORC_GROUP 16
 #define ORC_RECORD (ORC_DIM / 2 + ORC_DIM / ORC_GROUP) /* 256 code bytes + 32 scale bytes */
-#define ORC_KREC (ORC_IDX_DIM / 2 + 4)                  /* 64 code bytes + binary32 scale */
+#define ORC_KBLOCK 32                                   /* channels per indexer-K E8M0 scale */
+#define ORC_KREC (ORC_IDX_DIM / 2 + ORC_IDX_DIM / ORC_KBLOCK) /* 64 code bytes + 4 E8M0 scales */
 #define ORC_WBLOCK 32                                   /* channels per FP8 window scale */
 #define ORC_WREC (ORC_DIM + ORC_DIM / ORC_WBLOCK)       /* 512 E4M3 codes + 16 E8M0 scales */
 
@@ -188,45 +193,61 @@ void orc_fp4_unpack(const uint8_t* in, int64_t n, double* out) {
         for (int c = 0; c < ORC_DIM; c++) out[r * ORC_DIM + c] = record_value(in + r * ORC_RECORD, c);
 }
 
-/* FP4 indexer-K entry (reading of the pages' byte accounting: 128-dim FP4 +
- * a 4-byte scale = 68 B): bytes [0,64) hold channel 2j in the low nibble and
- * 2j+1 in the high nibble of byte j; bytes [64,68) hold the scale as an IEEE
- * binary32, least significant byte first. Scale = amax / 6 computed in float;
- * each channel takes the nearest E2M1 grid value times the scale, ties to the
- * even code, as for the main KV. */
+/* [OCP] E8M0 scale: the value 2^(b - 127); b = 255 is NaN. */
+double orc_e8m0_value(uint8_t b) { return b == 255 ? NAN : ldexp(1.0, (int)b - 127); }
+
+/* OCP MX shared-scale exponent of a block whose largest magnitude is amax, for
+ * elements whose largest power of two is 2^emax: floor(log2 amax) - emax,
+ * clamped to the E8M0 range [-127, 127]; an all-zero block takes -127. */
+static int mx_scale_exp(double amax, int emax) {
+    int e, xe = -127;
+    if (amax > 0.0) {
+        frexp(amax, &e); /* amax = f * 2^e, 0.5 <= f < 1: floor(log2 amax) = e - 1 */
+        xe = e - 1 - emax;
+        if (xe < -127) xe = -127;
+        if (xe > 127) xe = 127;
+    }
+    return xe;
+}
+
+/* FP4 indexer-K entry, read as OCP MXFP4 ([EOG] 3.4 names the OCP MXFP4
+ * standard and says the indexer Q/K already ran in FP4; the 68 B size comes
+ * from the 890 B/token accounting). Per block of 32 channels: X =
+ * 2^(floor(log2 amax) - 2), 2 being the exponent of E2M1's largest power of
+ * two (4); each element is the E2M1 value nearest to x / X (exact: X is a
+ * power of two), ties to the even code, magnitudes past 6 taking 6, zero
+ * magnitude +0. Layout: bytes [0,64) hold channel 2j in the low nibble and
+ * 2j+1 in the high nibble of byte j; byte 64+g holds the E8M0 scale of
+ * channels 32g..32g+31. */
 void orc_kidx_fp4_pack(const uint16_t* x, int64_t n, uint8_t* out) {
 #pragma omp parallel for schedule(static)
     for (int64_t r = 0; r < n; r++) {
         const uint16_t* xr = x + r * ORC_IDX_DIM;
         uint8_t* o = out + r * ORC_KREC;
         memset(o, 0, ORC_KREC);
-        float amax = 0.0f;
-        for (int c = 0; c < ORC_IDX_DIM; c++) {
-            float a = fabsf((float)bf16_value(xr[c]));
-            if (a > amax) amax = a;
-        }
-        float s = amax / 6.0f;
-        uint32_t sb;
-        memcpy(&sb, &s, 4);
-        for (int b = 0; b < 4; b++) o[ORC_IDX_DIM / 2 + b] = (uint8_t)(sb >> (8 * b));
-        for (int c = 0; c < ORC_IDX_DIM; c++) {
-            uint8_t code = (s == 0.0f) ? 0 : orc_e2m1_encode(bf16_value(xr[c]), (double)s);
-            o[c / 2] |= (uint8_t)(code << (4 * (c & 1)));
+        for (int g = 0; g < ORC_IDX_DIM / ORC_KBLOCK; g++) {
+            double amax = 0.0;
+            for (int c = 0; c < ORC_KBLOCK; c++) {
+                double a = fabs(bf16_value(xr[g * ORC_KBLOCK + c]));
+                if (a > amax) amax = a;
+            }
+            int xe = mx_scale_exp(amax, 2);
+            o[ORC_IDX_DIM / 2 + g] = (uint8_t)(xe + 127);
+            for (int c = 0; c < ORC_KBLOCK; c++) {
+                int ch = g * ORC_KBLOCK + c;
+                /* nearest grid value v * X of x: the same rule as the main KV
+                 * with the power-of-two scale X */
+                uint8_t code = orc_e2m1_encode(bf16_value(xr[ch]), ldexp(1.0, xe));
+                o[ch / 2] |= (uint8_t)(code << (4 * (ch & 1)));
+            }
         }
     }
 }
 
-static double kidx_fp4_scale(const uint8_t* rec) {
-    uint32_t sb = 0;
-    for (int b = 0; b < 4; b++) sb |= (uint32_t)rec[ORC_IDX_DIM / 2 + b] << (8 * b);
-    float s;
-    memcpy(&s, &sb, 4);
-    return (double)s;
-}
-
-/* Channel c of an FP4 indexer-K entry: E2M1(code) * scale, exact in double. */
+/* Channel c of an FP4 indexer-K entry: E2M1(code) * E8M0(scale of its block),
+ * exact in double. */
 static double kidx_fp4_value(const uint8_t* rec, int c) {
-    return orc_e2m1_value((rec[c / 2] >> (4 * (c & 1))) & 15) * kidx_fp4_scale(rec);
+    return orc_e2m1_value((rec[c / 2] >> (4 * (c & 1))) & 15) * orc_e8m0_value(rec[ORC_IDX_DIM / 2 + c / ORC_KBLOCK]);
 }
 
 void orc_kidx_fp4_unpack(const uint8_t* in, int64_t n, double* out) {
@@ -235,10 +256,6 @@ void orc_kidx_fp4_unpack(const uint8_t* in, int64_t n, double* out) {
         for (int c = 0; c < ORC_IDX_DIM; c++) out[r * ORC_IDX_DIM + c] = kidx_fp4_value(in + r * ORC_KREC, c);
 }
 
-/* Indexer K of entry `row` decoded to double: bf16 (kfmt 0, [.][128] uint16)
- * or the FP4 entry above (kfmt 1, [.][68] bytes). */
-/* [OCP] E8M0 scale: the value 2^(b - 127); b = 255 is NaN. */
-double orc_e8m0_value(uint8_t b) { return b == 255 ? NAN : ldexp(1.0, (int)b - 127); }
 
 /* FP8 window-KV row ([EOG] 3.4: the quantization-sensitive SWA KV stays in
  * FP8; read here as the OCP MX block format that passage names, with E4M3
@@ -260,14 +277,7 @@ void orc_swa_fp8_pack(const uint16_t* x, int64_t n, uint8_t* out) {
                 double a = fabs(bf16_value(row[g * ORC_WBLOCK + i]));
                 if (a > amax) amax = a;
             }
-            int xe = -127;
-            if (amax > 0.0) {
-                int e;
-                frexp(amax, &e); /* amax = f * 2^e, 0.5 <= f < 1: floor(log2 amax) = e - 1 */
-                xe = e - 1 - 8;
-                if (xe < -127) xe = -127;
-                if (xe > 127) xe = 127;
-            }
+            int xe = mx_scale_exp(amax, 8);
             rec[ORC_DIM + g] = (uint8_t)(xe + 127);
             for (int i = 0; i < ORC_WBLOCK; i++) {
                 double v = bf16_value(row[g * ORC_WBLOCK + i]);
@@ -289,6 +299,8 @@ void orc_swa_fp8_unpack(const uint8_t* in, int64_t n, double* out) {
         for (int c = 0; c < ORC_DIM; c++) out[r * ORC_DIM + c] = swa_fp8_value(in + r * ORC_WREC, c);
 }
 
+/* Indexer K of entry `row` decoded to double: bf16 (kfmt 0, [.][128] uint16)
+ * or the FP4 entry above (kfmt 1, [.][68] bytes). */
 static void load_key(const void* k, int kfmt, int64_t row, double* kd) {
     if (kfmt == 0) {
         const uint16_t* kr = (const uint16_t*)k + row * ORC_IDX_DIM;

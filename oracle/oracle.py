@@ -20,7 +20,7 @@ _LIB_PATH = os.path.join(_HERE, "libcsa2_oracle.so")
 _lib = None
 
 RECORD_BYTES = 288
-KIDX_RECORD_BYTES = 68  # FP4 indexer-K entry: 64 code bytes + binary32 scale
+KIDX_RECORD_BYTES = 68  # FP4 indexer-K entry (OCP MXFP4): 64 code bytes + 4 E8M0 scales (one per 32 channels)
 SWA_RECORD_BYTES = 528  # FP8 window row: 512 E4M3 codes + 16 E8M0 scales (one per 32 channels)
 IDX_HEADS, IDX_DIM, HEADS, DIM = 32, 128, 64, 512
 
@@ -121,8 +121,10 @@ def fp4_unpack(rec):
 
 
 def kidx_fp4_pack(x_bf16):
-    """FP4 indexer-K entry of each 128-channel bf16 row [n, 68] uint8 (the
-    pages' byte accounting: 128-dim FP4 + a 4-byte scale)."""
+    """FP4 indexer-K entry of each 128-channel bf16 row [n, 68] uint8, read as
+    OCP MXFP4 (eogee.com report 3.4 names the standard; the 68 B size comes
+    from the 890 B/token accounting): 64 code bytes + one E8M0 scale per 32
+    channels."""
     x = _c(x_bf16, np.uint16).reshape(-1, IDX_DIM)
     out = np.zeros((x.shape[0], KIDX_RECORD_BYTES), np.uint8)
     lib().orc_kidx_fp4_pack(_p(x), x.shape[0], _p(out))

@@ -230,8 +230,10 @@ def test_workload_parity(name):
         # the pipeline's own output where its selection equals the oracle's
         src = wl.attn_src[layer]
         same = [j for j, q in enumerate(Qs) if set(np_(step.top[src][q]).tolist()) == set(li[j].tolist())]
-        if same:
-            pe = np.abs(bf16_bits_to_f64(u16(step.out[layer][qt][same])) - ro[same]).max()
-            assert pe <= 1e-2 * np.abs(ro[same]).max()
+        # most sampled queries select exactly the oracle's set (overlap >= 99.5%
+        # above), so this check of the pipeline's own launch always runs
+        assert len(same) >= (len(Qs) + 1) // 2, (layer, len(same), len(Qs))
+        pe = np.abs(bf16_bits_to_f64(u16(step.out[layer][qt][same])) - ro[same]).max()
+        assert pe <= 1e-2 * np.abs(ro[same]).max()
         print("  attention layer %d ok (max err %.3g of %.3g)" % (layer, err, np.abs(ro).max()), flush=True)
     del swa_rows

@@ -494,19 +494,31 @@ def test_planted_entries_are_recalled():
 
 # ------------------------------------------------------ FP4 indexer K (NEXT row)
 
+def _mx_exp(amax, emax):
+    """OCP MX shared exponent of a block: floor(log2 amax) - emax, emax being
+    the exponent of the element type's largest power of two (2 for E2M1, 8 for
+    E4M3), clamped to the E8M0 range; -127 for an all-zero block."""
+    if amax == 0:
+        return -127
+    m, e = math.frexp(amax)  # amax = m * 2^e, 0.5 <= m < 1
+    return min(max(e - 1 - emax, -127), 127)
+
+
 def _kidx_deq_independent(rec):
-    """Decode FP4 indexer-K entries with the OCP E2M1 table and numpy's view of
-    the little-endian binary32 scale."""
+    """Decode FP4 indexer-K entries (OCP MXFP4) with the OCP E2M1 table and
+    the E8M0 scale 2^(b - 127) of each 32-channel block."""
     rec = np.asarray(rec, np.uint8).reshape(-1, 68)
     codes = rec[:, :64]
     nib = np.stack([codes & 15, codes >> 4], -1).reshape(rec.shape[0], 128)
-    sc = np.ascontiguousarray(rec[:, 64:68]).view("<f4").astype(np.float64)  # [n, 1]
-    return _e2m1_table()[nib] * sc
+    sb = rec[:, 64:68].astype(np.float64)
+    sc = np.where(sb == 255, np.nan, np.exp2(sb - 127))
+    return _e2m1_table()[nib] * np.repeat(sc, 32, axis=1)
 
 
 def _nearest_grid_code(x, s):
     """Brute force over the 8 magnitudes: nearest v*s to |x| (exact in float64
-    for a binary32 s), ties to the even code, +0 for magnitude 0."""
+    for a power-of-two s), ties to the even code, +0 for magnitude 0; past 6s
+    the nearest is 6s, i.e. saturation."""
     mags = np.array([0, 0.5, 1, 1.5, 2, 3, 4, 6], np.float64) * s
     d = np.abs(np.abs(x) - mags)
     best = 0
@@ -518,43 +530,54 @@ def _nearest_grid_code(x, s):
     return best
 
 
+def _nibbles(rec_row):
+    return np.stack([rec_row[:64] & 15, rec_row[:64] >> 4], -1).reshape(128)
+
+
 def test_kidx_fp4_entry_layout_matches_68_byte_accounting():
     g = _golden("byte_accounting.txt")
-    assert O.KIDX_RECORD_BYTES == int(g["indexer_key_bytes_read"]) == 128 // 2 + 4
+    assert O.KIDX_RECORD_BYTES == int(g["indexer_key_bytes_read"]) == 128 // 2 + 128 // 32
     x = np.zeros((2, 128), np.float32)
-    x[0, :6] = [6, -6, 3, 0.5, 0, -1.25]  # amax 6 -> scale 1; -1.25 is a tie -> 1 (even code 2)
-    x[1, 127] = -0.75 * 2.0 ** -20        # the amax: scale = it / 6, code 7 (6s) with the sign bit
+    x[0, :6] = [6, -6, 3, 0.5, 0, -1.25]  # block 0: amax 6 -> X = 2^(2-2) = 1; -1.25 is a tie -> 1 (even code 2)
+    x[0, 32:36] = [7, 5, 3.5, -0.25]      # block 1: amax 7 -> X = 1; 7 saturates to 6, ties 5 -> 4, 3.5 -> 4, -0.25 -> +0
+    x[1, 127] = -0.75 * 2.0 ** -20        # block 3: X = 2^(-21-2); the value is -6 X
     rec = O.kidx_fp4_pack(_bf16(x))
     assert rec.shape == (2, 68)
-    assert list(rec[0, :3]) == [0xF7, 0x15, 0xA0] and not rec[0, 3:64].any()
-    assert rec[0, 64:].tobytes() == np.float32(1.0).tobytes()  # little-endian binary32
-    s1 = np.float32(np.float32(0.75 * 2.0 ** -20) / np.float32(6.0))
-    assert rec[1, 64:].tobytes() == s1.tobytes()
+    assert list(rec[0, :3]) == [0xF7, 0x15, 0xA0] and not rec[0, 3:16].any()
+    assert list(rec[0, 16:18]) == [0x67, 0x06] and not rec[0, 18:64].any()
+    assert list(rec[0, 64:]) == [127, 127, 0, 0]  # all-zero blocks take 2^-127
     assert rec[1, 63] == (0x8 | 7) << 4 and not rec[1, :63].any()
+    assert list(rec[1, 64:]) == [0, 0, 0, 104]
 
 
-def test_kidx_fp4_codes_brute_force_and_scale_definition():
+def test_kidx_fp4_codes_brute_force_and_scale_rule():
     rng = np.random.default_rng(21)
     rows = np.concatenate([rng.normal(0, 1, (40, 128)), rng.normal(0, 1, (20, 128)) * np.exp2(
-        rng.integers(-30, 30, (20, 1))), rng.uniform(-6, 6, (10, 128))]).astype(np.float32)
+        rng.integers(-30, 30, (20, 1))), rng.uniform(-8, 8, (10, 128)),
+        rng.normal(0, 1, (10, 128)) * np.exp2(rng.integers(-40, 40, (10, 128)))]).astype(np.float32)
+    rows[-1, :32] = 0.0          # an all-zero block
+    rows[-2, 32:64] = 1e-38      # a tiny block: the exponent clamps at -127
     xb = _bf16(rows)
     xf = _bf16_to_f64(xb)
     rec = O.kidx_fp4_pack(xb)
     for r in range(rows.shape[0]):
-        amax = np.float32(np.abs(xf[r]).max())
-        s = np.float32(amax / np.float32(6.0))
-        assert rec[r, 64:].tobytes() == s.tobytes()
-        nib = np.stack([rec[r, :64] & 15, rec[r, :64] >> 4], -1).reshape(128)
-        want = [_nearest_grid_code(xf[r, c], float(s)) for c in range(128)]
-        assert list(nib) == want, r
+        nib = _nibbles(rec[r])
+        for g in range(4):
+            blk = xf[r, 32 * g:32 * g + 32]
+            e = _mx_exp(np.abs(blk).max(), 2)
+            assert rec[r, 64 + g] == e + 127, (r, g)
+            want = [_nearest_grid_code(v, 2.0 ** e) for v in blk]
+            assert list(nib[32 * g:32 * g + 32]) == want, (r, g)
 
 
 def test_kidx_fp4_unpack_is_table_times_scale_and_ties_go_even():
     rng = np.random.default_rng(22)
+    rec = rng.integers(0, 256, (40, 68)).astype(np.uint8)
+    assert np.array_equal(O.kidx_fp4_unpack(rec), _kidx_deq_independent(rec), equal_nan=True)
     xb = _rand_bf16(rng, (64, 128), 3.0)
     rec = O.kidx_fp4_pack(xb)
     assert np.array_equal(O.kidx_fp4_unpack(rec), _kidx_deq_independent(rec))
-    # every midpoint between neighbours of the grid, times scale 1 (amax 6)
+    # every midpoint between neighbours of the grid, times scale 1 (block amax 6)
     mids = np.array([0.25, 0.75, 1.25, 1.75, 2.5, 3.5, 5.0])
     even = np.array([0, 2, 2, 4, 4, 6, 6])  # the even neighbour's code
     x = np.zeros((1, 128), np.float32)
@@ -562,11 +585,27 @@ def test_kidx_fp4_unpack_is_table_times_scale_and_ties_go_even():
     x[0, 1:8] = mids
     x[0, 8:15] = -mids
     rec = O.kidx_fp4_pack(_bf16(x))
-    nib = np.stack([rec[0, :64] & 15, rec[0, :64] >> 4], -1).reshape(128)
+    nib = _nibbles(rec[0])
     assert list(nib[1:8]) == list(even)
     assert list(nib[8:15]) == [c | 8 if c else 0 for c in even]
-    # an all-zero row: zero scale, zero codes
+    # an all-zero row: zero codes, every block scale 2^-127 (byte 0)
     assert not O.kidx_fp4_pack(np.zeros((1, 128), np.uint16)).any()
+
+
+def test_kidx_fp4_round_trip_error_bound_and_saturation():
+    rng = np.random.default_rng(25)
+    xb = _rand_bf16(rng, (48, 128), 2.0)
+    xf = _bf16_to_f64(xb)
+    rt = O.kidx_fp4_unpack(O.kidx_fp4_pack(xb))
+    for r in range(48):
+        for g in range(4):
+            blk, got = xf[r, 32 * g:32 * g + 32], rt[r, 32 * g:32 * g + 32]
+            X = 2.0 ** _mx_exp(np.abs(blk).max(), 2)
+            sat = np.abs(blk) > 6 * X
+            assert np.all(got[sat] == np.sign(blk[sat]) * 6 * X)
+            err = np.abs(got[~sat] - blk[~sat])
+            # half the grid spacing: X/4 below 2X, |x|/4 above
+            assert np.all(err <= np.maximum(np.abs(blk[~sat]) / 4, X / 4))
 
 
 def test_kidx_fp4_pack_is_scale_equivariant():
@@ -576,7 +615,7 @@ def test_kidx_fp4_pack_is_scale_equivariant():
     for m in (-7, 5):
         rec2 = O.kidx_fp4_pack(_bf16(_bf16_to_f64(xb) * 2.0 ** m))
         assert np.array_equal(rec2[:, :64], rec[:, :64])
-        assert np.array_equal(rec2[:, 64:].copy().view("<f4"), rec[:, 64:].copy().view("<f4") * np.float32(2.0 ** m))
+        assert np.array_equal(rec2[:, 64:].astype(int), rec[:, 64:].astype(int) + m)
 
 
 def test_index_fp4k_is_the_score_formula_on_decoded_keys():
@@ -609,12 +648,8 @@ def test_index_fp4k_is_the_score_formula_on_decoded_keys():
 # ------------------------------------------------------- FP8 window rows
 
 def _ocp_mx_exp(amax):
-    """OCP MX shared exponent for E4M3 elements: floor(log2 amax) - 8, clamped
-    to the E8M0 range; 2^-127 for an all-zero block."""
-    if amax == 0:
-        return -127
-    m, e = math.frexp(amax)  # amax = m * 2^e, 0.5 <= m < 1
-    return min(max(e - 1 - 8, -127), 127)
+    """OCP MX shared exponent for E4M3 elements (largest power of two 2^8)."""
+    return _mx_exp(amax, 8)
 
 
 def _swa_deq_independent(rec):
