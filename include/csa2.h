@@ -66,7 +66,7 @@ extern "C" {
 #define CSA2_IDX_DIM 128    /* indexer head dim */
 #define CSA2_GROUP 16       /* channels per E4M3 scale */
 #define CSA2_RECORD 288     /* bytes per FP4 main-KV entry: 256 code bytes + 32 scale bytes */
-#define CSA2_KIDX_RECORD 68 /* bytes per FP4 indexer-K entry: 64 code bytes + binary32 scale */
+#define CSA2_KIDX_RECORD 68 /* bytes per FP4 indexer-K entry: 64 code bytes + 4 E8M0 scales */
 #define CSA2_SWA_RECORD 528 /* bytes per FP8 window-KV row: 512 E4M3 codes + 16 E8M0 scales */
 #define CSA2_MAX_WINDOW 128 /* sliding-window length limit */
 #define CSA2_MAX_TOPK 4096  /* largest k accepted by csa2_topk */
@@ -138,17 +138,19 @@ int csa2_index_reindex(const uint16_t* q_idx, const float* w, const uint16_t* k_
 /*
  * kidx_fp4_pack -- FP4 indexer-K entries, the storage precision the pages'
  * byte accounting implies (890 B/token = 2.5 entries x (288 B main KV + 68 B
- * indexer K): titansim blog, eogee.com report 5.3; eogee.com 3.4 notes FP4
- * indexer Q/K in the predecessor).
+ * indexer K): titansim blog, eogee.com report 5.3), in the OCP MXFP4 format
+ * eogee.com report 3.4 names (that passage also notes FP4 indexer Q/K in the
+ * predecessor).
  *   x_bf16 [n][128] bf16 row-major.
  *   out    [n][68] bytes. Entry: byte j (0..63) holds channel 2j in bits 3:0
- *          and channel 2j+1 in bits 7:4 as E2M1 codes (bit 3 sign); bytes
- *          64..67 hold the scale s as an IEEE binary32, least significant byte
- *          first. s = amax / 6 (fp32, round to nearest); each channel takes the
- *          E2M1 code whose value times s is nearest to x (ties to the even
- *          code, beyond 6s -> 6s, zero magnitude -> +0); s == 0 gives zero
- *          codes. Inputs must be finite. n >= 0; entries are independent.
- *   value(channel c) = E2M1(code_c) * s.
+ *          and channel 2j+1 in bits 7:4 as E2M1 codes (bit 3 sign); byte 64+g
+ *          (g = 0..3) holds the E8M0 scale (value 2^(b-127)) of channels
+ *          32g..32g+31. Per block X = 2^(floor(log2 amax) - 2), clamped to
+ *          [2^-127, 2^127] (an all-zero block gets 2^-127); each channel takes
+ *          the E2M1 code nearest to x / X (ties to the even code, beyond 6 ->
+ *          6, zero magnitude -> +0). Inputs must be finite. n >= 0; entries
+ *          are independent.
+ *   value(channel c) = E2M1(code_c) * 2^(scale_byte(c/32) - 127).
  */
 int kidx_fp4_pack(const uint16_t* x_bf16, int64_t n, uint8_t* out, hipStream_t stream);
 
@@ -171,9 +173,10 @@ int swa_fp8_pack(const uint16_t* x_bf16, int64_t n, uint8_t* out, hipStream_t st
  * csa2_index_full_fp4k / csa2_index_reindex_fp4k -- csa2_index_full and
  * csa2_index_reindex over the FP4 indexer-K cache k_fp4 [nseq][N][68] (entries
  * of kidx_fp4_pack) instead of bf16 k_idx; every other argument, output and
- * error rule is the same. The score uses the decoded key E2M1(code) * s; the
- * kernels apply s once per entry after the head sum, since ReLU(s x) = s ReLU(x)
- * for s >= 0.
+ * error rule is the same. The score uses the decoded key E2M1(code) * 2^(b-127),
+ * which enters the bf16 products exactly for scale bytes b in [2, 252] (the
+ * packer writes 0..252; blocks with a byte below 2 have all magnitudes under
+ * 2^-123 and decode to subnormal numbers, which the products may flush to 0).
  */
 int csa2_index_full_fp4k(const uint16_t* q_idx, const float* w, const uint8_t* k_fp4, int64_t N, int32_t nq,
                          int32_t q_per_seq, const int32_t* n_visible, float* scores, int32_t block_size,

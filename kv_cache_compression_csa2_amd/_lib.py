@@ -14,7 +14,7 @@ LIB_PATH = os.path.join(_HERE, "libcsa2.so")
 
 CSA2_OK, CSA2_EINVAL, CSA2_ELAUNCH, CSA2_EWORKSPACE = 0, -1, -2, -3
 DIM, HEADS, IDX_HEADS, IDX_DIM, RECORD = 512, 64, 32, 128, 288
-KIDX_RECORD = 68  # FP4 indexer-K entry: 64 code bytes + binary32 scale
+KIDX_RECORD = 68  # FP4 indexer-K entry (OCP MXFP4): 64 code bytes + 4 E8M0 block scales
 SWA_RECORD = 528  # FP8 window-KV row: 512 E4M3 codes + 16 E8M0 scales
 
 _lib = None
@@ -146,7 +146,8 @@ def _k_args(k_idx, k_fp4):
 
 
 def kidx_fp4_pack(x, out=None, stream=None):
-    """bf16 [n,128] indexer keys -> uint8 [n,68] FP4 entries (64 code bytes + binary32 scale)."""
+    """bf16 [n,128] indexer keys -> uint8 [n,68] FP4 entries (OCP MXFP4: 64 code bytes + one E8M0
+    scale per 32 channels)."""
     _need(x, torch.bfloat16, "x")
     n = x.numel() // IDX_DIM
     if out is None:

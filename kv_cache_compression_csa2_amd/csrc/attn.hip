@@ -38,8 +38,10 @@
 // 128-register O^T rescale is rare; exp2 arguments stay <= 8. It starts at a
 // finite floor (-2^126), so masked keys (logit -inf) need no special case.
 // Few queries cannot fill the GPU, so a query's tiles may be split across
-// workgroups that write partial results (O / sum in bf16, max, sum) to the
-// workspace; a second kernel merges them.
+// workgroups that write partial results (O / sum in fp16, max, sum) to the
+// workspace; a second kernel merges them. O / sum is a convex combination of
+// value rows, all below 65504 in magnitude, so fp16 holds it with 8 times the
+// resolution of bf16 in the same bytes.
 #include <math.h>
 
 #include "device_common.h"
@@ -107,6 +109,12 @@ CSA2_DEVINL uint4 bf16x8_to_f16x8(uint4 v) {
     return make_uint4(bf16x2_to_f16x2(v.x), bf16x2_to_f16x2(v.y), bf16x2_to_f16x2(v.z), bf16x2_to_f16x2(v.w));
 }
 CSA2_DEVINL f16x8 as_f16x8(uint4 v) { return __builtin_bit_cast(f16x8, v); }
+
+// Two floats -> packed fp16 pair (lo in bits 0..15), round to nearest even.
+CSA2_DEVINL uint32_t pack_f16x2(float lo, float hi) {
+    return __builtin_bit_cast(uint32_t, __builtin_convertvector(f32x2{lo, hi}, f16x2));
+}
+CSA2_DEVINL float f16_bits_to_float(uint32_t b) { return (float)__builtin_bit_cast(_Float16, (uint16_t)b); }
 
 CSA2_DEVINL f16x8 as_f16x8_2(i16x4 lo, i16x4 hi) {
     typedef short i16x8 __attribute__((ext_vector_type(8)));
@@ -376,8 +384,8 @@ __global__ __launch_bounds__(kAttThreads, 2) void sparse_attn_kernel(
     // ---- finish: lanes with the same head (G = 0..3) hold different keys' sums ----
     const float l_tot = sum_over_groups(l_run);
     const float inv = l_tot > 0.0f ? 1.0f / l_tot : 0.0f;
-    // O / l in bf16 is the output (one split) or the split's partial, which
-    // the merge weights by l * 2^(m - max m). The wave's 16 heads x 512 dims
+    // O / l is the output in bf16 (one split) or the split's partial in fp16,
+    // which the merge weights by l * 2^(m - max m). The wave's 16 heads x 512 dims
     // go through LDS as rows (1040-byte stride: conflict-free writes) and are
     // stored with 16-byte lanes along each 1 KiB row; straight from the
     // accumulators every store would scatter 16-byte pieces over 16 rows.
@@ -387,10 +395,17 @@ __global__ __launch_bounds__(kAttThreads, 2) void sparse_attn_kernel(
     uint8_t* stg = lds + wave * (16 * kStgRow);
     {
         uint8_t* row = stg + j * kStgRow + 8 * (G & 1);
+        if (nsplit > 1) {
 #pragma unroll
-        for (int mt = 0; mt < 32; mt++)
-            *reinterpret_cast<uint2*>(row + 16 * unit_logical(2 * mt + (G >> 1))) =
-                make_uint2(pack_bf16x2(o[mt][0] * inv, o[mt][1] * inv), pack_bf16x2(o[mt][2] * inv, o[mt][3] * inv));
+            for (int mt = 0; mt < 32; mt++)
+                *reinterpret_cast<uint2*>(row + 16 * unit_logical(2 * mt + (G >> 1))) =
+                    make_uint2(pack_f16x2(o[mt][0] * inv, o[mt][1] * inv), pack_f16x2(o[mt][2] * inv, o[mt][3] * inv));
+        } else {
+#pragma unroll
+            for (int mt = 0; mt < 32; mt++)
+                *reinterpret_cast<uint2*>(row + 16 * unit_logical(2 * mt + (G >> 1))) =
+                    make_uint2(pack_bf16x2(o[mt][0] * inv, o[mt][1] * inv), pack_bf16x2(o[mt][2] * inv, o[mt][3] * inv));
+        }
     }
     lds_barrier();
     const int64_t prow = nsplit == 1 ? qi * kHeads : (qi * nsplit + split) * kHeads;  // row of head 0
@@ -450,8 +465,8 @@ __global__ __launch_bounds__(128) void attn_merge_kernel(const uint16_t* __restr
         if (s < nsplit && ml[s][0] != -INFINITY) {
             const float f = ml[s][1] * exp2f(ml[s][0] - M);  // the partial is O / l
             L += f;
-            acc += f32x4{bf16_bits_to_float(po[s].x & 0xFFFFu), bf16_bits_to_float(po[s].x >> 16),
-                         bf16_bits_to_float(po[s].y & 0xFFFFu), bf16_bits_to_float(po[s].y >> 16)} * f;
+            acc += f32x4{f16_bits_to_float(po[s].x & 0xFFFFu), f16_bits_to_float(po[s].x >> 16),
+                         f16_bits_to_float(po[s].y & 0xFFFFu), f16_bits_to_float(po[s].y >> 16)} * f;
         }
     }
     const float inv = L > 0.0f ? 1.0f / L : 0.0f;

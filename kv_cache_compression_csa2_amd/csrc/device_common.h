@@ -16,6 +16,8 @@ constexpr int kGroup = 16;     // channels per E4M3 scale
 constexpr int kCodeBytes = kDim / 2;
 constexpr int kRecord = kCodeBytes + kDim / kGroup;  // 288
 constexpr int kMaxWindow = 128;
+constexpr int kKidxBlock = 32;                            // channels per E8M0 scale of an FP4 indexer-K entry
+constexpr int kKidxRecord = kIdxDim / 2 + kIdxDim / kKidxBlock;  // 68
 
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef float f32x16 __attribute__((ext_vector_type(16)));

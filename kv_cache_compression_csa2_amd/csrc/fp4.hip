@@ -69,13 +69,18 @@ __global__ __launch_bounds__(256) void fp4_unpack_kernel(const uint8_t* __restri
     dst[1] = make_uint4(o[4], o[5], o[6], o[7]);
 }
 
-// FP4 indexer-K entries (68 bytes: 64 code bytes, binary32 scale), the
-// storage precision implied by the pages' 890 B/token accounting (titansim
-// blog; eogee.com report 5.3). 16 threads per 128-channel row, 8 channels
-// each; the row's 16 threads are 16 aligned lanes of one wave. The scale is
-// amax / 6 rounded to nearest; the midpoints of the E2M1 grid times that
-// binary32 scale are exact in double, so the nearest-code decision (ties to
-// the even code) is made there.
+// FP4 indexer-K entries in the OCP MXFP4 format (68 bytes: 64 code bytes, then
+// one E8M0 scale per 32 channels), the storage precision implied by the pages'
+// 890 B/token accounting (titansim blog; eogee.com report 5.3) in the standard
+// eogee.com report 3.4 names. Per block: X = 2^(floor(log2 amax) - 2), 2 being
+// the exponent of E2M1's largest power of two, clamped to E8M0's [-127, 127];
+// element = nearest E2M1 value of x/X (exact: X is a power of two), ties to the
+// even code, past 6 saturating to 6; zero magnitude is +0.
+// 16 threads per 128-channel row, 8 channels each: threads 4g..4g+3 of a row
+// (aligned lanes of one wave) hold block g. The block maximum is taken on the
+// bf16 bit patterns (|x| orders like its 15 low bits), and floor(log2 amax)
+// is the exponent field minus 127 for normal values; bf16 subnormals and
+// zero blocks fall below the clamp, so the rule needs no float log.
 __global__ __launch_bounds__(256) void kidx_fp4_pack_kernel(const uint16_t* __restrict__ x, int64_t n,
                                                             uint8_t* __restrict__ out) {
     const int64_t t = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
@@ -84,35 +89,30 @@ __global__ __launch_bounds__(256) void kidx_fp4_pack_kernel(const uint16_t* __re
     const bool ok = row < n;
     const uint4 v = ok ? reinterpret_cast<const uint4*>(x + row * kIdxDim)[sl] : make_uint4(0u, 0u, 0u, 0u);
     const uint32_t wv[4] = {v.x, v.y, v.z, v.w};
-    float xs[8];
-    float amax = 0.0f;
+    uint32_t amax_bits = 0;
 #pragma unroll
-    for (int i = 0; i < 4; i++) {
-        xs[2 * i] = bf16_bits_to_float(wv[i] & 0xFFFFu);
-        xs[2 * i + 1] = bf16_bits_to_float(wv[i] >> 16);
-    }
-#pragma unroll
-    for (int i = 0; i < 8; i++) amax = fmaxf(amax, fabsf(xs[i]));
-#pragma unroll
-    for (int o = 1; o < 16; o <<= 1) amax = fmaxf(amax, __shfl_xor(amax, o));
+    for (int i = 0; i < 4; i++) amax_bits = max(amax_bits, max(wv[i] & 0x7FFFu, (wv[i] >> 16) & 0x7FFFu));
+    amax_bits = max(amax_bits, (uint32_t)__shfl_xor((int)amax_bits, 1));
+    amax_bits = max(amax_bits, (uint32_t)__shfl_xor((int)amax_bits, 2));
     if (!ok) return;
-    const float s = __fdiv_rn(amax, 6.0f);
-    const double sd = (double)s;
-    const double mid[7] = {0.25 * sd, 0.75 * sd, 1.25 * sd, 1.75 * sd, 2.5 * sd, 3.5 * sd, 5.0 * sd};
+    int xe = (int)(amax_bits >> 7) - 127 - 2;
+    xe = xe < -127 ? -127 : xe;  // the largest bf16 exponent keeps xe <= 125
+    const float inv_x = __uint_as_float((uint32_t)(127 - xe) << 23);  // 2^-xe, a normal float
     uint32_t codes = 0;
 #pragma unroll
     for (int i = 0; i < 8; i++) {
-        const double a = fabs((double)xs[i]);
-        uint32_t c = 0;
-#pragma unroll
-        for (int m = 0; m < 7; m++) c += (uint32_t)(a > mid[m]);
-        if (c < 7 && (c & 1u) && a == mid[c]) c++;  // exact tie: the even neighbour
-        if (c != 0 && xs[i] < 0.0f) c |= 8u;
+        const float xv = bf16_bits_to_float((wv[i >> 1] >> (16 * (i & 1))) & 0xFFFFu);
+        const float a = fabsf(xv) * inv_x;  // exact, or below 2^-126 where the code is 0 anyway
+        // nearest grid value; ties go to the even code (>= where the upper
+        // neighbour is even: 0.75, 1.75, 3.5)
+        uint32_t c = (uint32_t)(a > 0.25f) + (uint32_t)(a >= 0.75f) + (uint32_t)(a > 1.25f) +
+                     (uint32_t)(a >= 1.75f) + (uint32_t)(a > 2.5f) + (uint32_t)(a >= 3.5f) + (uint32_t)(a > 5.0f);
+        if (c != 0 && xv < 0.0f) c |= 8u;
         codes |= c << (4 * i);
     }
-    uint8_t* dst = out + row * 68;
+    uint8_t* dst = out + row * kKidxRecord;
     reinterpret_cast<uint32_t*>(dst)[sl] = codes;
-    if (sl == 0) reinterpret_cast<uint32_t*>(dst)[16] = __float_as_uint(s);
+    if ((sl & 3) == 0) dst[kIdxDim / 2 + (sl >> 2)] = (uint8_t)(xe + 127);
 }
 
 // FP8 window-KV rows: E4M3 elements with one E8M0 scale per 32 channels, the

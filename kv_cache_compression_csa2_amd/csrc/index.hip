@@ -8,10 +8,12 @@
 // holds 16 heads of one entry; the ReLU-weighted head sum runs in fp32 on the
 // lane, then one cross-half exchange adds the other 16 heads.
 //
-// The indexer K is either bf16 [N][128] or FP4 entries [N][68] (128 E2M1
-// codes + one binary32 scale s, the storage precision implied by the pages'
-// byte accounting). FP4 codes decode exactly to bf16 and feed the same MFMA;
-// s multiplies the entry's head sum once (ReLU(s x) = s ReLU(x), s >= 0).
+// The indexer K is either bf16 [N][128] or FP4 entries [N][68] in the OCP
+// MXFP4 format (128 E2M1 codes + one E8M0 scale per 32 channels, the storage
+// precision implied by the pages' byte accounting). The gfx950 scaled
+// FP4 -> bf16 conversion applies a block's power-of-two scale itself, so the
+// decoded key E2M1 * 2^(b-127) is exact in bf16 (for scale bytes 2..252, the
+// range whose decoded values are normal numbers) and feeds the same MFMA.
 //
 // Three kernels:
 //  * index_stream_kernel -- one query per workgroup slice; each wave streams
@@ -48,25 +50,30 @@ struct StreamTile<false> {
 template <>
 struct StreamTile<true> {
     uint32_t code[8];  // 64 channels of the entry, 8 per dword
-    float scale;
+    uint32_t scales;   // the entry's 4 E8M0 block scales
     int64_t ent;
     bool valid;
 };
 
-constexpr int kKRec = 68;  // bytes per FP4 indexer-K entry
+constexpr int kKRec = kKidxRecord;  // bytes per FP4 indexer-K entry
 
 typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
 
-// Eight E2M1 codes (channel 2b in bits 8b..8b+3, 2b+1 above) -> their exact
-// bf16 values, in channel order.
-CSA2_DEVINL bf16x8 fp4x8_to_bf16(uint32_t w) {
-    const bf16x2 p0 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(w, 1.0f, 0);
-    const bf16x2 p1 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(w, 1.0f, 1);
-    const bf16x2 p2 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(w, 1.0f, 2);
-    const bf16x2 p3 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(w, 1.0f, 3);
+// Eight E2M1 codes (channel 2b in bits 8b..8b+3, 2b+1 above) times the power
+// of two `x` -> their bf16 values, in channel order (exact while they are
+// normal bf16 numbers).
+CSA2_DEVINL bf16x8 fp4x8_to_bf16(uint32_t w, float x) {
+    const bf16x2 p0 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(w, x, 0);
+    const bf16x2 p1 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(w, x, 1);
+    const bf16x2 p2 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(w, x, 2);
+    const bf16x2 p3 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(w, x, 3);
     return as_bf16x8(make_uint4(__builtin_bit_cast(uint32_t, p0), __builtin_bit_cast(uint32_t, p1),
                                 __builtin_bit_cast(uint32_t, p2), __builtin_bit_cast(uint32_t, p3)));
 }
+
+// E8M0 byte `sel` of four packed scale bytes -> its value 2^(b-127) as a float
+// (the byte becomes the binary32 exponent field).
+CSA2_DEVINL float e8m0_byte(uint32_t four, int sel) { return __uint_as_float(((four >> (8 * sel)) & 0xFFu) << 23); }
 
 // Row of the accumulator held in register r by a lane of half `half` (32x32 layout).
 CSA2_DEVINL int acc_row(int r, int half) { return (r >> 2) * 8 + half * 4 + (r & 3); }
@@ -105,7 +112,7 @@ CSA2_DEVINL void stream_load(const void* kseq, int64_t ent, bool valid, int half
         const uint32_t* src = reinterpret_cast<const uint32_t*>(e + 32 * half);
 #pragma unroll
         for (int j = 0; j < 8; j++) st.code[j] = src[j];
-        st.scale = *reinterpret_cast<const float*>(e + 64);
+        st.scales = *reinterpret_cast<const uint32_t*>(e + kIdxDim / 2);
     } else {
         const uint4* src =
             reinterpret_cast<const uint4*>(static_cast<const uint16_t*>(kseq) + (valid ? ent : 0) * kIdxDim) + half;
@@ -117,12 +124,17 @@ CSA2_DEVINL void stream_load(const void* kseq, int64_t ent, bool valid, int half
 // Score of the tile's entry in lanes 0..31 (lanes 32..63 hold a partial sum):
 // the 32-head contraction, ReLU, weights, head sum; -inf for invalid entries.
 template <bool kFp4>
-CSA2_DEVINL float stream_score(const StreamQuery<kFp4>& Q, const StreamTile<kFp4>& st) {
+CSA2_DEVINL float stream_score(const StreamQuery<kFp4>& Q, const StreamTile<kFp4>& st, int half) {
     f32x16 acc = {};
+    float x0 = 1.0f, x1 = 1.0f;  // FP4: scales of the lane's blocks 2*half and 2*half+1
+    if constexpr (kFp4) {
+        x0 = e8m0_byte(st.scales, 2 * half);
+        x1 = e8m0_byte(st.scales, 2 * half + 1);
+    }
 #pragma unroll
     for (int j = 0; j < 8; j++) {
         if constexpr (kFp4)
-            acc = mfma32x32x16(Q.a[j], fp4x8_to_bf16(st.code[j]), acc);
+            acc = mfma32x32x16(Q.a[j], fp4x8_to_bf16(st.code[j], j < 4 ? x0 : x1), acc);
         else
             acc = mfma32x32x16(Q.a[j], st.b[j], acc);
     }
@@ -130,7 +142,6 @@ CSA2_DEVINL float stream_score(const StreamQuery<kFp4>& Q, const StreamTile<kFp4
 #pragma unroll
     for (int r = 0; r < 16; r++) s = fmaf(Q.wr[r], relu_bits(acc[r]), s);
     s += from_upper_half(s);  // lanes 0..31 hold the sum over all 32 heads
-    if constexpr (kFp4) s *= st.scale;
     return st.valid ? s : -INFINITY;
 }
 
@@ -168,7 +179,7 @@ __global__ __launch_bounds__(kStreamThreads) void index_stream_kernel(
     };
 
     auto finish = [&](int64_t t, const StreamTile<kFp4>& st) {
-        const float s = stream_score<kFp4>(Q, st);
+        const float s = stream_score<kFp4>(Q, st, half);
         const int64_t col = t * 32 + col_in_tile;
         if (half == 0 && col < ncols) scores[q * ncols + col] = s;
         if (kReindex) {
@@ -267,7 +278,7 @@ __global__ __launch_bounds__(kFtThreads) void index_topk_kernel(
         }
     };
     auto finish = [&](int t, const StreamTile<kFp4>& st) {
-        const float s = stream_score<kFp4>(Q, st);
+        const float s = stream_score<kFp4>(Q, st, half);
         const int p = t * 32 + col_in_tile;
         if (half == 0) sc[p] = s;
         if (scores_dbg && half == 0 && p < n) scores_dbg[q * ncols + c0 + p] = s;
@@ -334,7 +345,7 @@ constexpr int kPfRow = 256 + 16;       // padded LDS row bytes
 constexpr int kPfChunk = 4096;         // entries per workgroup
 
 // Registers of one prefill tile load: bf16 K 4 units of 16 bytes per thread;
-// FP4 K 16 code bytes and the entry scale per thread.
+// FP4 K 16 code bytes (one 32-channel block) and that block's scale per thread.
 template <bool kFp4>
 struct PfPre;
 template <>
@@ -344,7 +355,7 @@ struct PfPre<false> {
 template <>
 struct PfPre<true> {
     uint4 v;
-    float scale;
+    float x;  // the block's E8M0 scale as a float
 };
 
 template <bool kFp4, bool kBlk>
@@ -353,7 +364,6 @@ __global__ __launch_bounds__(256, 2) void index_prefill_kernel(
     int32_t q_per_seq, const int32_t* __restrict__ n_visible, float* __restrict__ scores,
     float* __restrict__ block_scores, int32_t nchunks) {
     __shared__ __attribute__((aligned(16))) uint8_t lds[2][kPfSub * kPfRow];
-    __shared__ float kscale[2][kPfSub];  // FP4 K: the entries' scales
     const int b = blockIdx.x;
     int chunk, qg;
     if ((nchunks & 7) == 0) {
@@ -400,7 +410,7 @@ __global__ __launch_bounds__(256, 2) void index_prefill_kernel(
 
     // Tile loads into registers. bf16 K: 4 16-byte units per thread of the
     // 64 x 256 B tile. FP4 K: thread (entry tid/4, quarter tid%4) takes 16 code
-    // bytes (32 channels) and the entry's scale.
+    // bytes (32 channels, one scale block) and that block's scale.
     using Pre = PfPre<kFp4>;
     auto gload = [&](int st) {
         Pre p;
@@ -410,7 +420,7 @@ __global__ __launch_bounds__(256, 2) void index_prefill_kernel(
             e = e < N ? e : 0;
             const uint32_t* src = reinterpret_cast<const uint32_t*>(kfseq + e * kKRec) + 4 * qq;
             p.v = make_uint4(src[0], src[1], src[2], src[3]);
-            p.scale = *reinterpret_cast<const float*>(kfseq + e * kKRec + 64);
+            p.x = __uint_as_float((uint32_t)kfseq[e * kKRec + kIdxDim / 2 + qq] << 23);
         } else {
 #pragma unroll
             for (int i = 0; i < 4; i++) {
@@ -429,8 +439,7 @@ __global__ __launch_bounds__(256, 2) void index_prefill_kernel(
             uint8_t* dst = &lds[buf][row * kPfRow + qq * 64];
             const uint32_t c[4] = {p.v.x, p.v.y, p.v.z, p.v.w};
 #pragma unroll
-            for (int i = 0; i < 4; i++) *reinterpret_cast<bf16x8*>(dst + 16 * i) = fp4x8_to_bf16(c[i]);
-            if (qq == 0) kscale[buf][row] = p.scale;
+            for (int i = 0; i < 4; i++) *reinterpret_cast<bf16x8*>(dst + 16 * i) = fp4x8_to_bf16(c[i], p.x);
         } else {
 #pragma unroll
             for (int i = 0; i < 4; i++) {
@@ -440,14 +449,12 @@ __global__ __launch_bounds__(256, 2) void index_prefill_kernel(
             }
         }
     };
-    // ReLU-weighted head sum of one query's 32 x 32 block (times the entry's
-    // scale for FP4 K); valid in lanes 0..31.
     // ReLU-weighted head sums of both queries' 32 x 32 blocks, one query per
     // half-wave: each lane sums its 16 heads of each query, and one half-wave
     // swap hands lanes 0..31 both halves of query a and lanes 32..63 both
-    // halves of query b (times the entry's scale for FP4 K).
+    // halves of query b.
     const int64_t nv_mine = half ? nvb : nva;
-    auto head_sums = [&](const f32x16& acca, const f32x16& accb, int64_t col, float esc) {
+    auto head_sums = [&](const f32x16& acca, const f32x16& accb, int64_t col) {
         float sa = 0.0f, sb = 0.0f;
 #pragma unroll
         for (int r = 0; r < 16; r++) {
@@ -455,8 +462,7 @@ __global__ __launch_bounds__(256, 2) void index_prefill_kernel(
             sb = fmaf(wb[r], relu_bits(accb[r]), sb);
         }
         const auto x = __builtin_amdgcn_permlane32_swap(__float_as_uint(sa), __float_as_uint(sb), false, false);
-        float s = __uint_as_float(x[0]) + __uint_as_float(x[1]);
-        if constexpr (kFp4) s *= esc;
+        const float s = __uint_as_float(x[0]) + __uint_as_float(x[1]);
         return col < nv_mine ? s : -INFINITY;
     };
     const int64_t q_mine = half ? qb : qa;
@@ -469,15 +475,13 @@ __global__ __launch_bounds__(256, 2) void index_prefill_kernel(
     // One group = 32 entries (rows h2*32.. of an LDS tile) for both queries:
     // 8 fragment reads, 16 MFMAs. The epilogue of the previous group runs in
     // the same straight-line block so the scheduler can put its VALU work in
-    // the shadow of these MFMAs. The group's entry scale (FP4 K) is read here,
-    // while its tile is still in LDS, and travels with the accumulators.
-    auto group = [&](int buf, int h2, f32x16& acca, f32x16& accb, float& esc, const f32x16& pa, const f32x16& pb,
-                     float pesc, int64_t pcol, float (&out)[2]) {
+    // the shadow of these MFMAs.
+    auto group = [&](int buf, int h2, f32x16& acca, f32x16& accb, const f32x16& pa, const f32x16& pb, int64_t pcol,
+                     float (&out)[2]) {
         const uint8_t* rowp = lds[buf] + (h2 * 32 + col_in_tile) * kPfRow + half * 16;
         bf16x8 bj[8];
 #pragma unroll
         for (int j = 0; j < 8; j++) bj[j] = as_bf16x8(*reinterpret_cast<const uint4*>(rowp + j * 32));
-        if constexpr (kFp4) esc = kscale[buf][h2 * 32 + col_in_tile];
         acca = f32x16{};
         accb = f32x16{};
 #pragma unroll
@@ -485,9 +489,9 @@ __global__ __launch_bounds__(256, 2) void index_prefill_kernel(
             acca = mfma32x32x16(aa[j], bj[j], acca);
             accb = mfma32x32x16(ab[j], bj[j], accb);
         }
-        out[0] = head_sums(pa, pb, pcol, pesc);
+        out[0] = head_sums(pa, pb, pcol);
         out[1] = kBlk ? max8_lanes(out[0]) : 0.0f;  // block maxima only when asked for
-        __builtin_amdgcn_sched_group_barrier(0x100, kFp4 ? 9 : 8, 0);  // fragment reads first
+        __builtin_amdgcn_sched_group_barrier(0x100, 8, 0);  // fragment reads first
         __builtin_amdgcn_sched_group_barrier(0x002, 8, 0);
 #pragma unroll
         for (int i = 0; i < 16; i++) {
@@ -500,23 +504,22 @@ __global__ __launch_bounds__(256, 2) void index_prefill_kernel(
     lstore(0, gload(0));
     lds_barrier();
     f32x16 pa, pb, ca, cb;
-    float pesc = 1.0f, cesc = 1.0f;
     float out[2];
     {
         const f32x16 z = {};
-        group(0, 0, pa, pb, pesc, z, z, 1.0f, N, out);  // no previous group: its results are discarded
+        group(0, 0, pa, pb, z, z, N, out);  // no previous group: its results are discarded
     }
     for (int st = 0; st < nsub; st++) {
         const bool more = st + 1 < nsub;
         // the last iteration re-reads tile 0 (in bounds) and discards it
         const Pre nxt = gload(more ? st + 1 : 0);
         const int64_t col0 = tile_base + (int64_t)st * kPfSub + col_in_tile;
-        group(st & 1, 1, ca, cb, cesc, pa, pb, pesc, col0, out);
+        group(st & 1, 1, ca, cb, pa, pb, col0, out);
         store(out[0], out[1], col0);
         if (more) lstore((st + 1) & 1, nxt);
         lds_barrier();
         // After the last tile this reads the stale buffer; those results are never stored.
-        group((st + 1) & 1, 0, pa, pb, pesc, ca, cb, cesc, col0 + 32, out);
+        group((st + 1) & 1, 0, pa, pb, ca, cb, col0 + 32, out);
         store(out[0], out[1], col0 + 32);
     }
 }

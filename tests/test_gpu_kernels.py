@@ -111,6 +111,9 @@ def test_kidx_pack_bit_exact():
     x[0] = 0
     x[1, :] = -0.0
     x[2, :64] = 1e-35
+    x[3, :32] = 1e-39  # a block of bf16 subnormals (scale byte 0, codes up to 2)
+    x[3, 32:64] = -3e-39
+    x[4, 96:] = 3e38   # the largest binades
     # exact ties: amax 6 * 2^e so the scale is 2^e, the rest on the grid midpoints
     rng = np.random.default_rng(13)
     e = torch.tensor(np.exp2(rng.integers(-20, 20, (100, 1))).astype(np.float32))
@@ -151,6 +154,44 @@ def test_index_full_fp4k_matches_oracle(nq, N, qps):
     torch.cuda.synchronize()
     ok, msg = rel_close(np_(s2), rs)
     assert ok, msg
+
+
+@pytest.mark.parametrize("qps", [1, 8])
+def test_index_fp4k_decodes_every_code_and_scale_exactly(qps):
+    """Every E2M1 code under every E8M0 scale byte 2..252 (the bytes whose
+    decoded values are normal numbers; the packer never writes more than 252),
+    in every channel position: entry i holds one nonzero code in channel
+    i % 128 and scale byte b in all four blocks. Head 0 of the query is all
+    ones and head 1 all minus ones, so with w = (1, 1) the score is |v| and
+    with w = (1, 0) it is max(v, 0): the decoded value v = E2M1 * 2^(b-127)
+    must come out bit-exact. qps 1: the decode kernel; 8: the prefill kernel."""
+    print("case: fp4k exhaustive decode", qps, flush=True)
+    bs = np.arange(2, 253)
+    codes = np.arange(16)
+    n = len(bs) * len(codes)
+    ent = np.zeros((n, 68), np.uint8)
+    i = np.arange(n)
+    b, c = bs[i // 16], codes[i % 16]
+    ch = i % 128
+    ent[i, ch // 2] = (c << (4 * (ch % 2))).astype(np.uint8)
+    ent[:, 64:] = b[:, None].astype(np.uint8)
+    nq = 2 if qps == 1 else 8
+    nseq = nq // qps
+    kf_host = np.ascontiguousarray(np.broadcast_to(ent, (nseq, n, 68)))
+    q = torch.zeros((nq, 32, 128), dtype=torch.bfloat16)
+    q[:, 0] = 1.0
+    q[:, 1] = -1.0
+    w = torch.zeros((nq, 32), dtype=torch.float32)
+    w[:, 0] = 1.0
+    w[0::2, 1] = 1.0
+    q, w = q.to(DEV), w.to(DEV)
+    s = K().csa2_index_full(q, w, None, n, qps, k_fp4=torch.tensor(kf_host, device=DEV))
+    torch.cuda.synchronize()
+    ref = O.index_full(u16(q), np_(w), None, n, qps, k_fp4=kf_host)
+    assert np.array_equal(np_(s), ref)
+    v = O.kidx_fp4_unpack(ent)[i, ch]
+    assert np.array_equal(ref[0], np.abs(v).astype(np.float32))
+    assert np.array_equal(ref[1], np.maximum(v, 0).astype(np.float32))
 
 
 def test_index_reindex_fp4k_matches_oracle():
