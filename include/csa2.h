@@ -227,6 +227,31 @@ int csa2_index_topk_merge(int64_t N, int32_t nq, int32_t k, int32_t* top_idx, vo
                           hipStream_t stream);
 
 /*
+ * csa2_index_topk_noalloc -- csa2_index_topk with no workspace argument and no
+ * allocation, for callers that cannot allocate device memory (code under HIP
+ * graph capture, tight serving loops, harnesses that forbid hipMalloc).
+ *   Arguments, outputs and errors as csa2_index_topk (k_is_fp4 != 0: `k` holds
+ *   FP4 entries [nq][N][68], else bf16 keys [nq][N][128]), except:
+ *   - the per-chunk candidates go to a static device array of
+ *     csa2_index_topk_noalloc_scratch_bytes() bytes (16 MiB) that each GPU
+ *     the library runs on holds until the process ends; a call whose
+ *     csa2_index_topk_workspace_bytes(nq, N, topk) exceeds it returns
+ *     CSA2_EINVAL (Top-512 fits up to 128 queries x 262144 entries or 16 x
+ *     1048576);
+ *   - the scratch of the calling thread's current device is used, so the
+ *     stream must belong to that device;
+ *   - every call on one GPU shares that scratch: calls that overlap in time on
+ *     one GPU (different streams, or different host threads) race and give
+ *     undefined results. Calls in order on one stream are safe.
+ *   The first call on a device looks up the scratch address (CSA2_ELAUNCH if
+ *   that fails). No hipMalloc, hipFree or memset is made.
+ */
+size_t csa2_index_topk_noalloc_scratch_bytes(void);
+int csa2_index_topk_noalloc(const uint16_t* q_idx, const float* w, const void* k, int32_t k_is_fp4, int64_t N,
+                            int32_t nq, const int32_t* n_visible, int32_t topk, int32_t* top_idx, int32_t block_size,
+                            float* block_scores, float* scores, hipStream_t stream);
+
+/*
  * csa2_index_reindex_topk -- Reindex-mode scoring fused with the layer's
  * Top-K (eogee.com report 3.3: a Reindex layer scores only the candidate pool
  * with its own indexer query and keeps its own Top-K; report 3.5 names the

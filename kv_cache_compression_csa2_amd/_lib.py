@@ -52,6 +52,9 @@ def load():
     L.csa2_index_topk_fp4k.argtypes = [vp, vp, vp, i64, i32, vp, i32, vp, i32, vp, vp, vp, sz, vp]
     L.csa2_index_topk_select.argtypes = [vp, vp, vp, i32, i64, i32, vp, i32, vp, i32, vp, vp, vp, sz, vp]
     L.csa2_index_topk_merge.argtypes = [i64, i32, i32, vp, vp, sz, vp]
+    L.csa2_index_topk_noalloc_scratch_bytes.argtypes = []
+    L.csa2_index_topk_noalloc_scratch_bytes.restype = sz
+    L.csa2_index_topk_noalloc.argtypes = [vp, vp, vp, i32, i64, i32, vp, i32, vp, i32, vp, vp, vp]
     L.csa2_index_reindex_topk_workspace_bytes.argtypes = [i32, i32, i32]
     L.csa2_index_reindex_topk_workspace_bytes.restype = sz
     L.csa2_index_reindex_topk.argtypes = [vp, vp, vp, i64, i32, i32, vp, vp, i32, i32, vp, vp, vp, sz, vp]
@@ -67,7 +70,7 @@ def load():
                  "csa2_sparse_attn", "kidx_fp4_pack", "csa2_index_full_fp4k", "csa2_index_reindex_fp4k",
                  "swa_fp8_pack", "csa2_sparse_attn_fp8w", "csa2_index_topk", "csa2_index_topk_fp4k",
                  "csa2_index_topk_select", "csa2_index_topk_merge", "csa2_index_reindex_topk",
-                 "csa2_index_reindex_topk_fp4k"]:
+                 "csa2_index_reindex_topk_fp4k", "csa2_index_topk_noalloc"]:
         getattr(L, name).restype = ctypes.c_int
     _lib = L
     return L
@@ -78,7 +81,8 @@ EXPORTS = ["csa2_format_version", "csa2_last_error", "fp4_kv_pack", "fp4_kv_unpa
            "csa2_sparse_attn", "kidx_fp4_pack", "csa2_index_full_fp4k", "csa2_index_reindex_fp4k", "swa_fp8_pack",
            "csa2_sparse_attn_fp8w", "csa2_index_topk_workspace_bytes", "csa2_index_topk", "csa2_index_topk_fp4k",
            "csa2_index_topk_select", "csa2_index_topk_merge", "csa2_index_reindex_topk_workspace_bytes",
-           "csa2_index_reindex_topk", "csa2_index_reindex_topk_fp4k"]
+           "csa2_index_reindex_topk", "csa2_index_reindex_topk_fp4k", "csa2_index_topk_noalloc_scratch_bytes",
+           "csa2_index_topk_noalloc"]
 
 
 def _ptr(t):
@@ -225,6 +229,33 @@ def csa2_index_topk(q_idx, w, k_idx, N, k, n_visible=None, block_size=0, top=Non
     else:
         fn = getattr(load(), "csa2_index_topk" + suffix)
         _check(fn(_ptr(q_idx), _ptr(w), kp, *args), "csa2_index_topk" + suffix)
+    return (top, block_scores) if block_size else top
+
+
+def csa2_index_topk_noalloc_scratch_bytes():
+    return load().csa2_index_topk_noalloc_scratch_bytes()
+
+
+def csa2_index_topk_noalloc(q_idx, w, k_idx, N, k, n_visible=None, block_size=0, top=None, block_scores=None,
+                            scores=None, stream=None, k_fp4=None):
+    """csa2_index_topk without a workspace: the library's static device scratch
+    holds the candidates (calls overlapping on one GPU race). Outputs must be
+    passed in (`top`, and `block_scores` when block_size == 8) for a call that
+    allocates nothing; missing ones are allocated here, outside the call."""
+    for t, dt, nm in [(q_idx, torch.bfloat16, "q_idx"), (w, torch.float32, "w"), (n_visible, torch.int32, "n_visible"),
+                      (scores, torch.float32, "scores"), (top, torch.int32, "top"),
+                      (block_scores, torch.float32, "block_scores")]:
+        _need(t, dt, nm)
+    kp, suffix = _k_args(k_idx, k_fp4)
+    nq = q_idx.shape[0]
+    dev = q_idx.device
+    if top is None:
+        top = torch.empty((nq, k), dtype=torch.int32, device=dev)
+    if block_size and block_scores is None:
+        block_scores = torch.empty((nq, (N + 7) // 8), dtype=torch.float32, device=dev)
+    _check(load().csa2_index_topk_noalloc(_ptr(q_idx), _ptr(w), kp, 1 if suffix else 0, N, nq, _ptr(n_visible), k,
+                                          _ptr(top), block_size, _ptr(block_scores) if block_size else None,
+                                          _ptr(scores), _stream(stream)), "csa2_index_topk_noalloc")
     return (top, block_scores) if block_size else top
 
 

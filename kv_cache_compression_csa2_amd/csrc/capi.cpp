@@ -124,10 +124,9 @@ size_t csa2_index_topk_workspace_bytes(int32_t nq, int64_t N, int32_t k) {
     return csa2::index_topk_workspace_bytes(nq, N, k);
 }
 
-static int index_topk_impl(const char* who, bool merge, const uint16_t* q_idx, const float* w, const void* kc,
-                           bool kfp4, int64_t N, int32_t nq, const int32_t* n_visible, int32_t k, int32_t* top_idx,
-                           int32_t block_size, float* block_scores, float* scores, void* workspace, size_t ws_bytes,
-                           hipStream_t stream) {
+// Argument checks of the fused scoring + Top-K calls (everything but the workspace).
+static int index_topk_args(const char* who, const uint16_t* q_idx, const float* w, const void* kc, int64_t N,
+                           int32_t nq, int32_t k, int32_t* top_idx, int32_t block_size, float* block_scores) {
     int rc = check_index_common(who, q_idx, w, kc, N, nq, 1);
     if (rc) return rc;
     if (k < 1 || k > CSA2_MAX_TOPK) return fail(CSA2_EINVAL, "%s: k must be in [1, %d]", who, CSA2_MAX_TOPK);
@@ -137,6 +136,15 @@ static int index_topk_impl(const char* who, bool merge, const uint16_t* q_idx, c
     if (block_size != 0 && block_size != 8) return fail(CSA2_EINVAL, "%s: block_size must be 0 or 8", who);
     if (block_size == 8 && nq > 0 && !block_scores)
         return fail(CSA2_EINVAL, "%s: block_scores required when block_size == 8", who);
+    return CSA2_OK;
+}
+
+static int index_topk_impl(const char* who, bool merge, const uint16_t* q_idx, const float* w, const void* kc,
+                           bool kfp4, int64_t N, int32_t nq, const int32_t* n_visible, int32_t k, int32_t* top_idx,
+                           int32_t block_size, float* block_scores, float* scores, void* workspace, size_t ws_bytes,
+                           hipStream_t stream) {
+    const int rc = index_topk_args(who, q_idx, w, kc, N, nq, k, top_idx, block_size, block_scores);
+    if (rc) return rc;
     const size_t need = csa2_index_topk_workspace_bytes(nq, N, k);
     if (nq > 0 && need > 0 && (!workspace || ws_bytes < need))
         return fail(CSA2_EWORKSPACE, "%s: workspace needs %zu bytes", who, need);
@@ -166,6 +174,32 @@ int csa2_index_topk_select(const uint16_t* q_idx, const float* w, const void* k,
                            float* block_scores, float* scores, void* workspace, size_t ws_bytes, hipStream_t stream) {
     return index_topk_impl("csa2_index_topk_select", false, q_idx, w, k, k_is_fp4 != 0, N, nq, n_visible, topk,
                            top_idx, block_size, block_scores, scores, workspace, ws_bytes, stream);
+}
+
+size_t csa2_index_topk_noalloc_scratch_bytes(void) { return csa2::index_topk_noalloc_capacity(); }
+
+int csa2_index_topk_noalloc(const uint16_t* q_idx, const float* w, const void* k, int32_t k_is_fp4, int64_t N,
+                            int32_t nq, const int32_t* n_visible, int32_t topk, int32_t* top_idx, int32_t block_size,
+                            float* block_scores, float* scores, hipStream_t stream) {
+    const char* who = "csa2_index_topk_noalloc";
+    const int rc = index_topk_args(who, q_idx, w, k, N, nq, topk, top_idx, block_size, block_scores);
+    if (rc) return rc;
+    const size_t need = csa2_index_topk_workspace_bytes(nq, N, topk);
+    const size_t cap = csa2::index_topk_noalloc_capacity();
+    if (need > cap)
+        return fail(CSA2_EINVAL, "%s: this call needs %zu bytes of scratch; the static scratch holds %zu", who, need,
+                    cap);
+    void* ws = nullptr;
+    if (nq > 0 && need > 0) {
+        hipError_t e = hipSuccess;
+        ws = csa2::index_topk_noalloc_scratch(&e);
+        if (!ws) return fail(CSA2_ELAUNCH, "%s: scratch address lookup failed: %s", who, hipGetErrorString(e));
+    }
+    (void)hipGetLastError();
+    csa2::launch_index_topk(q_idx, w, k, k_is_fp4 != 0, N, nq, n_visible, topk, top_idx,
+                            block_size ? block_scores : nullptr, scores, ws, stream);
+    csa2::launch_index_topk_merge(N, nq, topk, top_idx, ws, stream);
+    return launched(who);
 }
 
 int csa2_index_topk_merge(int64_t N, int32_t nq, int32_t k, int32_t* top_idx, void* workspace, size_t ws_bytes,

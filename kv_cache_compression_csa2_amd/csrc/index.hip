@@ -28,6 +28,8 @@
 //    each K byte read from L2 feeds 8 queries. Bound by MFMA.
 #include <math.h>
 
+#include <mutex>
+
 #include "device_common.h"
 #include "launch.h"
 #include "topk_select.h"
@@ -650,6 +652,43 @@ int launch_index_topk(const uint16_t* q_idx, const float* w, const void* k, bool
     }
 #undef CSA2_FT
     return 0;
+}
+
+// Scratch of csa2_index_topk_noalloc, for callers that cannot allocate: the
+// per-chunk candidates of one call live in this file-scope device array, of
+// which every GPU the library runs on holds its own copy until the process
+// ends. Every selection slot is rewritten by each call, so nothing needs
+// clearing; calls that overlap on one GPU share the array and race.
+constexpr size_t kNoAllocScratchBytes = size_t(16) << 20;
+static __device__ __align__(256) uint8_t scratch[kNoAllocScratchBytes];
+
+size_t index_topk_noalloc_capacity() { return kNoAllocScratchBytes; }
+
+// Device address of the current device's copy of `scratch`. In host code the
+// array's name is only a stand-in, so the address is looked up once per
+// device (with that device current) and kept.
+void* index_topk_noalloc_scratch(hipError_t* err) {
+    constexpr int kMaxDevices = 64;
+    static std::mutex mu;
+    static void* addr[kMaxDevices] = {};
+    int dev = -1;
+    hipError_t e = hipGetDevice(&dev);
+    if (e != hipSuccess || dev < 0 || dev >= kMaxDevices) {
+        *err = e != hipSuccess ? e : hipErrorInvalidDevice;
+        return nullptr;
+    }
+    std::lock_guard<std::mutex> lock(mu);
+    if (!addr[dev]) {
+        void* p = nullptr;
+        e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+        if (e != hipSuccess || !p) {
+            *err = e != hipSuccess ? e : hipErrorInvalidSymbol;
+            return nullptr;
+        }
+        addr[dev] = p;
+    }
+    *err = hipSuccess;
+    return addr[dev];
 }
 
 int launch_index_topk_merge(int64_t N, int32_t nq, int32_t topk, int32_t* out_idx, void* ws, hipStream_t s) {

@@ -33,6 +33,10 @@ int launch_index_topk(const uint16_t* q_idx, const float* w, const void* k, bool
                       const int32_t* n_visible, int32_t topk, int32_t* out_idx, float* block_scores,
                       float* scores_dbg, void* ws, hipStream_t s);
 int launch_index_topk_merge(int64_t N, int32_t nq, int32_t topk, int32_t* out_idx, void* ws, hipStream_t s);
+// Static device scratch of csa2_index_topk_noalloc: its size, and its address
+// on the current device (nullptr and *err set when the lookup fails).
+size_t index_topk_noalloc_capacity();
+void* index_topk_noalloc_scratch(hipError_t* err);
 bool reindex_topk_fits(int32_t nq, int32_t nb, int32_t k);
 size_t reindex_topk_workspace_bytes(int32_t nq, int32_t nb, int32_t k);
 int launch_index_reindex_topk(const uint16_t* q_idx, const float* w, const void* k, bool kfp4, int64_t N, int32_t nq,

@@ -236,3 +236,19 @@ def test_attn_rejects(kw, frag, code):
                                                   a["T"], a["start"], a["len_"], a["scale"], P, None, a["ws"],
                                                   a["wsb"], S))
     assert rc == code and frag in msg and msg.startswith("csa2_sparse_attn_fp8w"), msg
+
+
+def test_index_topk_noalloc_rejects_calls_beyond_its_scratch():
+    """The no-allocation call refuses (before touching the device) any call
+    whose candidates would not fit the static scratch."""
+    import kv_cache_compression_csa2_amd._lib as L
+    lib = L.load()
+    cap = lib.csa2_index_topk_noalloc_scratch_bytes()
+    assert cap == 16 << 20
+    assert lib.csa2_index_topk_workspace_bytes(64, 1 << 20, 512) > cap
+    rc = lib.csa2_index_topk_noalloc(1, 1, 1, 0, 1 << 20, 64, None, 512, 1, 0, None, None, None)
+    assert rc == L.CSA2_EINVAL
+    assert b"static scratch holds" in lib.csa2_last_error()
+    # the usual argument checks come first
+    rc = lib.csa2_index_topk_noalloc(1, 1, 1, 0, 1024, 4, None, 0, 1, 0, None, None, None)
+    assert rc == L.CSA2_EINVAL and b"k must be in" in lib.csa2_last_error()
