@@ -252,6 +252,34 @@ int csa2_index_topk_noalloc(const uint16_t* q_idx, const float* w, const void* k
                             float* block_scores, float* scores, hipStream_t stream);
 
 /*
+ * csa2_index_prefill_topk -- Full-mode scoring fused with the per-query Top-K
+ * for a prefill chunk (many queries over one sequence): the Top-k of
+ * csa2_index_full's score row without writing that row (eogee.com report 3.5
+ * names the fused Top-K selection kernel; titansim blog: Top-512 per query).
+ *   q_idx, w, k_idx, N, nq, q_per_seq, n_visible: as csa2_index_full;
+ *           q_per_seq must be a multiple of 8 (the kernel scores 8 queries of
+ *           one sequence together).
+ *   k       1 .. 512.
+ *   top_idx [nq][k] int32 out: exactly csa2_topk(scores, k, row_len =
+ *           n_visible) of the row csa2_index_full would produce (ascending
+ *           entry ids, then -1 padding; equal scores by lower entry id).
+ *   scores  [nq][N] fp32 out or NULL: the score row itself (checking aid).
+ *   workspace / ws_bytes: at least csa2_index_prefill_topk_workspace_bytes(nq,
+ *           N, k) bytes (0 when a row is scored by one workgroup; then the
+ *           call is one launch). Contents on entry do not matter.
+ *   EINVAL also when the chunks' candidates would not fit two merge levels of
+ *   16384 (the workspace-size call then returns 0).
+ * _fp4k: the same over FP4 indexer-K entries (k_fp4 [nseq][N][68]).
+ */
+size_t csa2_index_prefill_topk_workspace_bytes(int32_t nq, int64_t N, int32_t k);
+int csa2_index_prefill_topk(const uint16_t* q_idx, const float* w, const uint16_t* k_idx, int64_t N, int32_t nq,
+                            int32_t q_per_seq, const int32_t* n_visible, int32_t k, int32_t* top_idx, float* scores,
+                            void* workspace, size_t ws_bytes, hipStream_t stream);
+int csa2_index_prefill_topk_fp4k(const uint16_t* q_idx, const float* w, const uint8_t* k_fp4, int64_t N, int32_t nq,
+                                 int32_t q_per_seq, const int32_t* n_visible, int32_t k, int32_t* top_idx,
+                                 float* scores, void* workspace, size_t ws_bytes, hipStream_t stream);
+
+/*
  * csa2_index_reindex_topk -- Reindex-mode scoring fused with the layer's
  * Top-K (eogee.com report 3.3: a Reindex layer scores only the candidate pool
  * with its own indexer query and keeps its own Top-K; report 3.5 names the

@@ -55,6 +55,10 @@ def load():
     L.csa2_index_topk_noalloc_scratch_bytes.argtypes = []
     L.csa2_index_topk_noalloc_scratch_bytes.restype = sz
     L.csa2_index_topk_noalloc.argtypes = [vp, vp, vp, i32, i64, i32, vp, i32, vp, i32, vp, vp, vp]
+    L.csa2_index_prefill_topk_workspace_bytes.argtypes = [i32, i64, i32]
+    L.csa2_index_prefill_topk_workspace_bytes.restype = sz
+    L.csa2_index_prefill_topk.argtypes = [vp, vp, vp, i64, i32, i32, vp, i32, vp, vp, vp, sz, vp]
+    L.csa2_index_prefill_topk_fp4k.argtypes = [vp, vp, vp, i64, i32, i32, vp, i32, vp, vp, vp, sz, vp]
     L.csa2_index_reindex_topk_workspace_bytes.argtypes = [i32, i32, i32]
     L.csa2_index_reindex_topk_workspace_bytes.restype = sz
     L.csa2_index_reindex_topk.argtypes = [vp, vp, vp, i64, i32, i32, vp, vp, i32, i32, vp, vp, vp, sz, vp]
@@ -70,7 +74,8 @@ def load():
                  "csa2_sparse_attn", "kidx_fp4_pack", "csa2_index_full_fp4k", "csa2_index_reindex_fp4k",
                  "swa_fp8_pack", "csa2_sparse_attn_fp8w", "csa2_index_topk", "csa2_index_topk_fp4k",
                  "csa2_index_topk_select", "csa2_index_topk_merge", "csa2_index_reindex_topk",
-                 "csa2_index_reindex_topk_fp4k", "csa2_index_topk_noalloc"]:
+                 "csa2_index_reindex_topk_fp4k", "csa2_index_topk_noalloc", "csa2_index_prefill_topk",
+                 "csa2_index_prefill_topk_fp4k"]:
         getattr(L, name).restype = ctypes.c_int
     _lib = L
     return L
@@ -82,7 +87,8 @@ EXPORTS = ["csa2_format_version", "csa2_last_error", "fp4_kv_pack", "fp4_kv_unpa
            "csa2_sparse_attn_fp8w", "csa2_index_topk_workspace_bytes", "csa2_index_topk", "csa2_index_topk_fp4k",
            "csa2_index_topk_select", "csa2_index_topk_merge", "csa2_index_reindex_topk_workspace_bytes",
            "csa2_index_reindex_topk", "csa2_index_reindex_topk_fp4k", "csa2_index_topk_noalloc_scratch_bytes",
-           "csa2_index_topk_noalloc"]
+           "csa2_index_topk_noalloc", "csa2_index_prefill_topk_workspace_bytes", "csa2_index_prefill_topk",
+           "csa2_index_prefill_topk_fp4k"]
 
 
 def _ptr(t):
@@ -230,6 +236,33 @@ def csa2_index_topk(q_idx, w, k_idx, N, k, n_visible=None, block_size=0, top=Non
         fn = getattr(load(), "csa2_index_topk" + suffix)
         _check(fn(_ptr(q_idx), _ptr(w), kp, *args), "csa2_index_topk" + suffix)
     return (top, block_scores) if block_size else top
+
+
+def csa2_index_prefill_topk_workspace_bytes(nq, N, k):
+    return load().csa2_index_prefill_topk_workspace_bytes(nq, N, k)
+
+
+def csa2_index_prefill_topk(q_idx, w, k_idx, N, q_per_seq, k, n_visible=None, top=None, scores=None, workspace=None,
+                            stream=None, k_fp4=None):
+    """Prefill-chunk scores fused with Top-k (q_per_seq a multiple of 8,
+    k <= 512): int32 [nq,k]. `scores` [nq,N] fp32, when given, also receives
+    the score rows."""
+    for t, dt, nm in [(q_idx, torch.bfloat16, "q_idx"), (w, torch.float32, "w"), (n_visible, torch.int32, "n_visible"),
+                      (scores, torch.float32, "scores"), (top, torch.int32, "top")]:
+        _need(t, dt, nm)
+    kp, suffix = _k_args(k_idx, k_fp4)
+    nq = q_idx.shape[0]
+    dev = q_idx.device
+    if top is None:
+        top = torch.empty((nq, k), dtype=torch.int32, device=dev)
+    need = csa2_index_prefill_topk_workspace_bytes(nq, N, k)
+    if workspace is None and need:
+        workspace = torch.empty((need,), dtype=torch.uint8, device=dev)
+    wsb = workspace.numel() * workspace.element_size() if workspace is not None else 0
+    fn = getattr(load(), "csa2_index_prefill_topk" + suffix)
+    _check(fn(_ptr(q_idx), _ptr(w), kp, N, nq, q_per_seq, _ptr(n_visible), k, _ptr(top), _ptr(scores),
+              _ptr(workspace), wsb, _stream(stream)), "csa2_index_prefill_topk" + suffix)
+    return top
 
 
 def csa2_index_topk_noalloc_scratch_bytes():

@@ -219,6 +219,45 @@ int csa2_index_topk_merge(int64_t N, int32_t nq, int32_t k, int32_t* top_idx, vo
     return launched("csa2_index_topk_merge");
 }
 
+size_t csa2_index_prefill_topk_workspace_bytes(int32_t nq, int64_t N, int32_t k) {
+    if (nq <= 0 || N < 1 || N > kMaxN || k < 1 || k > CSA2_MAX_TOPK) return 0;
+    if (!csa2::prefill_topk_fits(nq, N, k)) return 0;
+    return csa2::prefill_topk_workspace_bytes(nq, N, k);
+}
+
+static int prefill_topk_impl(const char* who, const uint16_t* q_idx, const float* w, const void* kc, bool kfp4,
+                             int64_t N, int32_t nq, int32_t q_per_seq, const int32_t* n_visible, int32_t k,
+                             int32_t* top_idx, float* scores, void* workspace, size_t ws_bytes, hipStream_t stream) {
+    int rc = check_index_common(who, q_idx, w, kc, N, nq, q_per_seq);
+    if (rc) return rc;
+    if (q_per_seq % 8 != 0) return fail(CSA2_EINVAL, "%s: q_per_seq must be a multiple of 8", who);
+    if (k < 1 || k > 512) return fail(CSA2_EINVAL, "%s: k must be in [1, 512]", who);
+    if (!csa2::prefill_topk_fits(nq, N, k))
+        return fail(CSA2_EINVAL, "%s: N too large for this k (use csa2_index_full and csa2_topk)", who);
+    if (nq > 0 && !top_idx) return fail(CSA2_EINVAL, "%s: null top_idx", who);
+    const size_t need = csa2_index_prefill_topk_workspace_bytes(nq, N, k);
+    if (nq > 0 && need > 0 && (!workspace || ws_bytes < need))
+        return fail(CSA2_EWORKSPACE, "%s: workspace needs %zu bytes", who, need);
+    (void)hipGetLastError();
+    csa2::launch_index_prefill_topk(q_idx, w, kc, kfp4, N, nq, q_per_seq, n_visible, k, top_idx, scores, workspace,
+                                    stream);
+    return launched(who);
+}
+
+int csa2_index_prefill_topk(const uint16_t* q_idx, const float* w, const uint16_t* k_idx, int64_t N, int32_t nq,
+                            int32_t q_per_seq, const int32_t* n_visible, int32_t k, int32_t* top_idx, float* scores,
+                            void* workspace, size_t ws_bytes, hipStream_t stream) {
+    return prefill_topk_impl("csa2_index_prefill_topk", q_idx, w, k_idx, false, N, nq, q_per_seq, n_visible, k, top_idx,
+                             scores, workspace, ws_bytes, stream);
+}
+
+int csa2_index_prefill_topk_fp4k(const uint16_t* q_idx, const float* w, const uint8_t* k_fp4, int64_t N, int32_t nq,
+                                 int32_t q_per_seq, const int32_t* n_visible, int32_t k, int32_t* top_idx,
+                                 float* scores, void* workspace, size_t ws_bytes, hipStream_t stream) {
+    return prefill_topk_impl("csa2_index_prefill_topk_fp4k", q_idx, w, k_fp4, true, N, nq, q_per_seq, n_visible, k,
+                             top_idx, scores, workspace, ws_bytes, stream);
+}
+
 size_t csa2_index_reindex_topk_workspace_bytes(int32_t nq, int32_t nb, int32_t k) {
     if (nq <= 0 || nb < 1 || nb > 65536 || k < 1 || k > CSA2_MAX_TOPK) return 0;
     return csa2::reindex_topk_workspace_bytes(nq, nb, k);

@@ -28,6 +28,7 @@
 //    each K byte read from L2 feeds 8 queries. Bound by MFMA.
 #include <math.h>
 
+#include <algorithm>
 #include <mutex>
 
 #include "device_common.h"
@@ -344,7 +345,12 @@ __global__ __launch_bounds__(kFtThreads) void index_topk_kernel(
 constexpr int kPfQueries = 8;          // queries per workgroup (2 per wave)
 constexpr int kPfSub = 64;             // entries per LDS tile
 constexpr int kPfRow = 256 + 16;       // padded LDS row bytes
-constexpr int kPfChunk = 4096;         // entries per workgroup
+constexpr int kPfChunk = 4096;         // entries per workgroup (scores written out)
+constexpr int kPfSelK = 512;           // largest k of the fused prefill selection
+constexpr int kPfBuf = 960;            // candidate slots per query (a multiple of 64; 2 workgroups fit a CU)
+constexpr int kPfHigh = kPfBuf - 64;   // compact before a tile's 64 entries could overflow
+constexpr int kPfLow = kPfSelK + 128;  // buffers at or below this are left alone in a round
+constexpr int64_t kPfMaxChunk = 65536; // entry offsets within a chunk fit 16 bits
 
 // Registers of one prefill tile load: bf16 K 4 units of 16 bytes per thread;
 // FP4 K 16 code bytes (one 32-channel block) and that block's scale per thread.
@@ -360,15 +366,35 @@ struct PfPre<true> {
     float x;  // the block's E8M0 scale as a float
 };
 
-template <bool kFp4, bool kBlk>
+// kSel: scoring fused with the per-query Top-k (k <= kPfSelK; the DeepSelect
+// selection eogee.com report 3.5 names, for the prefill chunk): no score row
+// is written. Each wave owns its 2 queries' candidate buffers in LDS (keys and
+// 16-bit entry offsets within the chunk) and sees their entries in ascending
+// order, so an entry can only enter a query's Top-k if its score beats the
+// k-th best so far (T): an equal score arrives after every buffered one and
+// ranks below them. Passing entries are appended; the buffers are compacted to
+// their k best (tk::wave_keep_topk, T becomes the k-th key) only at tile
+// boundaries, all waves in the same round: the waves meet at every tile's
+// barrier, so one wave compacting alone would stall the other three. A random
+// row of n entries appends about k (1 + ln(n / k)) entries, so rounds are few.
+// At the end each query's k best go out in entry order: final indices when the
+// row is one chunk, else (key, entry) candidates that the Top-K merge combines.
+// `scores`, when given, still receives the score row (a checking aid).
+template <bool kFp4, bool kBlk, bool kSel>
 __global__ __launch_bounds__(256, 2) void index_prefill_kernel(
     const uint16_t* __restrict__ q_idx, const float* __restrict__ w, const void* __restrict__ k_idx, int64_t N,
     int32_t q_per_seq, const int32_t* __restrict__ n_visible, float* __restrict__ scores,
-    float* __restrict__ block_scores, int32_t nchunks) {
+    float* __restrict__ block_scores, int32_t nchunks, int64_t chunk_len, int32_t k, int32_t* __restrict__ out_idx,
+    uint32_t* __restrict__ cand_key, int32_t* __restrict__ cand_col) {
     __shared__ __attribute__((aligned(16))) uint8_t lds[2][kPfSub * kPfRow];
+    // kSel: candidate keys and entry offsets of the workgroup's 8 queries, and
+    // each wave's "a buffer is nearly full" flag per tile parity
+    __shared__ uint32_t bkey[kSel ? kPfQueries : 1][kSel ? kPfBuf : 1];
+    __shared__ uint16_t bid[kSel ? kPfQueries : 1][kSel ? kPfBuf : 1];
+    __shared__ __attribute__((aligned(16))) uint32_t full_flag[2][4];
     const int b = blockIdx.x;
     int chunk, qg;
-    if ((nchunks & 7) == 0) {
+    if (!kSel && (nchunks & 7) == 0) {
         // Consecutive workgroups land on different XCDs (round-robin); give each
         // XCD a fixed slice of entry chunks so its L2 keeps serving the same K.
         const int per = nchunks >> 3;
@@ -405,9 +431,17 @@ __global__ __launch_bounds__(256, 2) void index_prefill_kernel(
 
     const uint16_t* kseq = static_cast<const uint16_t*>(k_idx) + (kFp4 ? 0 : seq * N * kIdxDim);
     const uint8_t* kfseq = static_cast<const uint8_t*>(k_idx) + (kFp4 ? seq * N * kKRec : 0);
-    const int64_t e_begin = (int64_t)chunk * kPfChunk;
-    const int64_t e_end = (e_begin + kPfChunk < N) ? e_begin + kPfChunk : N;
-    const int nsub = (int)((e_end - e_begin + kPfSub - 1) / kPfSub);
+    const int64_t e_begin = (int64_t)chunk * chunk_len;
+    int64_t e_end = (e_begin + chunk_len < N) ? e_begin + chunk_len : N;
+    if (kSel && !scores) {
+        // entries no query of the workgroup sees need no scoring (unless the
+        // score row, -inf there, is asked for)
+        int64_t nvmax = 0;
+        for (int i = 0; i < kPfQueries; i++)
+            nvmax = max(nvmax, n_visible ? (int64_t)n_visible[(int64_t)qg * kPfQueries + i] : N);
+        e_end = e_end < nvmax ? e_end : nvmax;
+    }
+    const int nsub = e_end > e_begin ? (int)((e_end - e_begin + kPfSub - 1) / kPfSub) : 0;
     const int64_t nblk = (N + 7) >> 3;
 
     // Tile loads into registers. bf16 K: 4 16-byte units per thread of the
@@ -468,8 +502,31 @@ __global__ __launch_bounds__(256, 2) void index_prefill_kernel(
         return col < nv_mine ? s : -INFINITY;
     };
     const int64_t q_mine = half ? qb : qa;
+    // kSel state of the wave's two queries (wave-uniform): buffered candidates
+    // and the score an entry must beat, as a float (-inf: any valid score).
+    // key(s) > key(t) <=> s > t for every score s (NaN and -inf never pass),
+    // so the common case -- no lane passes once the threshold has settled --
+    // costs one compare and one branch per 32 entries.
+    uint32_t na = 0, nb = 0;
+    float ta = -INFINITY, tb = -INFINITY;
+    const int slot_a = 2 * wave, slot_b = 2 * wave + 1;
     auto store = [&](float s, float m, int64_t col) {
-        if (col < N) {
+        if constexpr (kSel) {
+            if (scores && col < N) scores[q_mine * N + col] = s;
+            const bool pass = s > (half ? tb : ta);
+            const uint64_t bal = __ballot(pass);
+            if (bal == 0) return;
+            const uint32_t ml = (uint32_t)bal, mh = (uint32_t)(bal >> 32);
+            // rank among the passing lanes of this half-wave (lanes 0..31: query a)
+            const uint32_t rank = __builtin_amdgcn_mbcnt_hi(half ? mh : 0u, __builtin_amdgcn_mbcnt_lo(half ? 0u : ml, 0u));
+            if (pass) {
+                const uint32_t pos = (half ? nb : na) + rank;
+                bkey[half ? slot_b : slot_a][pos] = tk::score_key(s);
+                bid[half ? slot_b : slot_a][pos] = (uint16_t)(col - e_begin);
+            }
+            na += (uint32_t)__builtin_popcount(ml);
+            nb += (uint32_t)__builtin_popcount(mh);
+        } else if (col < N) {
             scores[q_mine * N + col] = s;
             if (kBlk && (lane & 7) == 0) block_scores[q_mine * nblk + (col >> 3)] = m;
         }
@@ -519,10 +576,51 @@ __global__ __launch_bounds__(256, 2) void index_prefill_kernel(
         group(st & 1, 1, ca, cb, pa, pb, col0, out);
         store(out[0], out[1], col0);
         if (more) lstore((st + 1) & 1, nxt);
+        if constexpr (kSel) {
+            // 64 more entries per query arrive before the next barrier
+            if (lane == 0) full_flag[st & 1][wave] = (uint32_t)(max(na, nb) > (uint32_t)kPfHigh);
+        }
         lds_barrier();
         // After the last tile this reads the stale buffer; those results are never stored.
         group((st + 1) & 1, 0, pa, pb, ca, cb, col0 + 32, out);
+        if constexpr (kSel) {
+            // read after the group's fragment reads are issued, so the wait is theirs
+            const uint4 f = *reinterpret_cast<const uint4*>(full_flag[st & 1]);
+            if (f.x | f.y | f.z | f.w) {
+                // a compaction round: every wave compacts its fuller buffers
+                if (na > (uint32_t)kPfLow) {
+                    ta = tk::key_score(tk::wave_keep_topk<kPfBuf>(bkey[slot_a], bid[slot_a], na, (uint32_t)k));
+                    na = (uint32_t)k;
+                }
+                if (nb > (uint32_t)kPfLow) {
+                    tb = tk::key_score(tk::wave_keep_topk<kPfBuf>(bkey[slot_b], bid[slot_b], nb, (uint32_t)k));
+                    nb = (uint32_t)k;
+                }
+            }
+        }
         store(out[0], out[1], col0 + 32);
+    }
+    if constexpr (kSel) {
+        // each query's k best, in entry order
+#pragma unroll
+        for (int h = 0; h < 2; h++) {
+            const int slot = h ? slot_b : slot_a;
+            uint32_t n = h ? nb : na;
+            if (n > (uint32_t)k) {
+                tk::wave_keep_topk<kPfBuf>(bkey[slot], bid[slot], n, (uint32_t)k);
+                n = (uint32_t)k;
+            }
+            const int64_t q = h ? qb : qa;
+            if (nchunks == 1) {
+                for (int i = lane; i < k; i += 64) out_idx[q * k + i] = i < (int)n ? (int32_t)(e_begin + bid[slot][i]) : -1;
+            } else {
+                const int64_t base = (q * nchunks + chunk) * (int64_t)k;
+                for (int i = lane; i < k; i += 64) {
+                    cand_key[base + i] = i < (int)n ? bkey[slot][i] : 0u;
+                    cand_col[base + i] = i < (int)n ? (int32_t)(e_begin + bid[slot][i]) : -1;
+                }
+            }
+        }
     }
 }
 
@@ -536,9 +634,10 @@ int launch_index_full(const uint16_t* q_idx, const float* w, const void* k, bool
     if (q_per_seq % kPfQueries == 0) {
         const int32_t nchunks = (int32_t)((N + kPfChunk - 1) / kPfChunk);
         const int64_t grid = (int64_t)(nq / kPfQueries) * nchunks;
-#define CSA2_PF(FP4, BLK)                                                                                  \
-    hipLaunchKernelGGL((index_prefill_kernel<FP4, BLK>), dim3((unsigned)grid), dim3(256), 0, s, q_idx, w, k, N, \
-                       q_per_seq, n_visible, scores, bs, nchunks)
+#define CSA2_PF(FP4, BLK)                                                                                     \
+    hipLaunchKernelGGL((index_prefill_kernel<FP4, BLK, false>), dim3((unsigned)grid), dim3(256), 0, s, q_idx, w, k, \
+                       N, q_per_seq, n_visible, scores, bs, nchunks, (int64_t)kPfChunk, 0, (int32_t*)nullptr,       \
+                       (uint32_t*)nullptr, (int32_t*)nullptr)
         if (kfp4) {
             if (bs) CSA2_PF(true, true); else CSA2_PF(true, false);
         } else {
@@ -725,6 +824,46 @@ int launch_index_reindex_topk(const uint16_t* q_idx, const float* w, const void*
     }
 #undef CSA2_RT_LEN
 #undef CSA2_RT
+    if (f.c > 1) launch_topk_merge(nq, topk, f.c, f.ck, f.cc, out_idx, f.ck2, f.cc2, s);
+    return 0;
+}
+
+// Fused prefill scoring + Top-K: whole rows of up to 65536 entries per
+// workgroup (fewest candidates, fewest compactions), cut into more chunks
+// only when the batch would leave fewer than 512 workgroups (chunks of at
+// least 4096 entries, multiples of the 64-entry tile).
+int64_t prefill_topk_chunk_len(int32_t nq, int64_t N) {
+    const int64_t groups = nq / kPfQueries > 0 ? nq / kPfQueries : 1;
+    int64_t nch = (N + kPfMaxChunk - 1) / kPfMaxChunk;
+    const int64_t want = std::min((512 + groups - 1) / groups, (N + 4095) / 4096);
+    nch = nch > want ? nch : want;
+    const int64_t len = (N + nch - 1) / nch;
+    return (len + kPfSub - 1) / kPfSub * kPfSub;
+}
+int32_t prefill_topk_chunks(int32_t nq, int64_t N) {
+    const int64_t len = prefill_topk_chunk_len(nq, N);
+    return (int32_t)((N + len - 1) / len);
+}
+bool prefill_topk_fits(int32_t nq, int64_t N, int32_t k) {
+    return k >= 1 && k <= kPfSelK && chunks_fit(prefill_topk_chunks(nq, N), k);
+}
+size_t prefill_topk_workspace_bytes(int32_t nq, int64_t N, int32_t k) {
+    return chunks_workspace_bytes(nq, prefill_topk_chunks(nq, N), k);
+}
+
+int launch_index_prefill_topk(const uint16_t* q_idx, const float* w, const void* k, bool kfp4, int64_t N, int32_t nq,
+                              int32_t q_per_seq, const int32_t* n_visible, int32_t topk, int32_t* out_idx,
+                              float* scores_dbg, void* ws, hipStream_t s) {
+    if (nq == 0) return 0;
+    const FtWs f = ft_ws_chunks(ws, nq, prefill_topk_chunks(nq, N), topk);
+    const int64_t len = prefill_topk_chunk_len(nq, N);
+    const dim3 grid((unsigned)((int64_t)(nq / kPfQueries) * f.c));
+    if (kfp4)
+        hipLaunchKernelGGL((index_prefill_kernel<true, false, true>), grid, dim3(256), 0, s, q_idx, w, k, N,
+                           q_per_seq, n_visible, scores_dbg, (float*)nullptr, f.c, len, topk, out_idx, f.ck, f.cc);
+    else
+        hipLaunchKernelGGL((index_prefill_kernel<false, false, true>), grid, dim3(256), 0, s, q_idx, w, k, N,
+                           q_per_seq, n_visible, scores_dbg, (float*)nullptr, f.c, len, topk, out_idx, f.ck, f.cc);
     if (f.c > 1) launch_topk_merge(nq, topk, f.c, f.ck, f.cc, out_idx, f.ck2, f.cc2, s);
     return 0;
 }

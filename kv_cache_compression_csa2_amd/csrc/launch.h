@@ -43,6 +43,15 @@ int launch_index_reindex_topk(const uint16_t* q_idx, const float* w, const void*
                               int32_t q_per_seq, const int32_t* n_visible, const int32_t* cand_blocks, int32_t nb,
                               int32_t topk, int32_t* out_idx, float* pool_scores, void* ws, hipStream_t s);
 
+// Prefill scoring (q_per_seq a multiple of 8) fused with the per-query Top-k
+// (k <= 512): one launch scores and selects per chunk of the row (final
+// indices when a row is one chunk), a second merges chunks' candidates.
+bool prefill_topk_fits(int32_t nq, int64_t N, int32_t k);
+size_t prefill_topk_workspace_bytes(int32_t nq, int64_t N, int32_t k);
+int launch_index_prefill_topk(const uint16_t* q_idx, const float* w, const void* k, bool kfp4, int64_t N, int32_t nq,
+                              int32_t q_per_seq, const int32_t* n_visible, int32_t topk, int32_t* out_idx,
+                              float* scores_dbg, void* ws, hipStream_t s);
+
 size_t topk_workspace_bytes(int32_t rows, int64_t ncols, int32_t k);
 // Merge of per-chunk Top-K candidates: rows x nchunks x k (key, column) pairs
 // in column order (unused slots key 0) -> out_idx [rows][k]. Above 16384

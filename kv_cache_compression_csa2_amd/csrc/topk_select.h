@@ -18,6 +18,13 @@ CSA2_DEVINL uint32_t score_key(float f) {
     return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
 }
 
+// The score whose key is k (the inverse of score_key on keys >= 1); key 0
+// (no score) maps to -inf, which no score exceeds.
+CSA2_DEVINL float key_score(uint32_t k) {
+    if (k == 0u) return -__builtin_inff();
+    return __uint_as_float((k & 0x80000000u) ? (k & 0x7FFFFFFFu) : ~k);
+}
+
 constexpr int kRegMaxKpt = 32;        // keys per thread
 constexpr int kRegMaxKeys = 1024 * kRegMaxKpt;  // 32768 per chunk
 constexpr int kRegMaxCand = 16384;    // merge capacity per row
@@ -398,6 +405,76 @@ CSA2_DEVINL uint32_t reg_select_emit(const uint32_t (&key)[KPT], uint32_t k, Reg
         });
     }
     return kk;
+}
+
+// One wave keeps the k best of n > k keys held in LDS at key[0, n) (payloads
+// id[0, n)), positions in arrival order: larger key first, equal keys by lower
+// position. The kept ones move to key[0, k) / id[0, k) in position order, and
+// the k-th largest key is returned. Lane l holds positions [P*l, P*l + P)
+// (contiguous runs, so lane order is position order); every load is done
+// before the first store, so the compaction can run in place. The k-th key is
+// built bit by bit from the top (the largest t with at least k keys >= t,
+// counted with one ballot per key slot), starting below the highest bit where
+// the largest and smallest keys differ; keys above it are kept, then equal
+// ones in position order until k are. Must be called by all 64 lanes of the
+// wave (wave-uniform n and k); key 0 marks no key and never appears among
+// valid positions.
+template <int C, typename Id>
+CSA2_DEVINL uint32_t wave_keep_topk(uint32_t* key, Id* id, uint32_t n, uint32_t k) {
+    constexpr int P = C / 64;
+    static_assert(P * 64 == C, "buffer size must be a multiple of 64");
+    const uint32_t lane = threadIdx.x & 63;
+    uint32_t kv[P];
+    Id iv[P];
+    uint32_t lmax = 0u, lmin = 0xFFFFFFFFu;
+#pragma unroll
+    for (int j = 0; j < P; j++) {
+        const uint32_t p = lane * P + j;
+        kv[j] = p < n ? key[p] : 0u;
+        iv[j] = id[p];
+        lmax = max(lmax, kv[j]);
+        lmin = p < n ? min(lmin, kv[j]) : lmin;
+    }
+    const uint32_t hi = wave_max_u32(lmax), lo = wave_min_u32(lmin);
+    uint32_t t = hi;
+    if (hi != lo) {
+        const int top = 31 - __builtin_clz(hi ^ lo);
+        t = top == 31 ? 0u : hi & ~((2u << top) - 1u);  // the bits every key shares
+        for (int b = top; b >= 0; b--) {
+            const uint32_t c = t | (1u << b);
+            uint32_t cnt = 0;
+#pragma unroll
+            for (int j = 0; j < P; j++) cnt += (uint32_t)__builtin_popcountll(__ballot(kv[j] >= c));
+            if (cnt >= k) t = c;
+        }
+    }
+    uint32_t gt = 0, eq = 0;
+#pragma unroll
+    for (int j = 0; j < P; j++) {
+        gt += (uint32_t)(kv[j] > t);
+        eq += (uint32_t)(kv[j] == t);
+    }
+    const uint32_t igt = wave_incl_scan(gt), ieq = wave_incl_scan(eq);
+    const uint32_t need = k - (uint32_t)__builtin_amdgcn_readlane((int)igt, 63);  // equal keys to keep, >= 1
+    uint32_t e = ieq - eq;  // equal keys at lower positions
+    // A stable partition of [0, n): kept keys to [0, k) and the others to
+    // [k, n), both in position order, so every store is unconditional (no
+    // divergent branch per key); positions past n are rewritten in place.
+    uint32_t o = (igt - gt) + min(e, need);                 // kept keys at lower positions
+    uint32_t d = k + min(lane * P, n) - o;                  // discarded keys at lower positions, offset by k
+#pragma unroll
+    for (int j = 0; j < P; j++) {
+        const uint32_t p = lane * P + j;
+        const bool iseq = kv[j] == t;
+        const bool keep = kv[j] > t || (iseq && e < need);
+        e += (uint32_t)iseq;
+        const uint32_t dst = p >= n ? p : (keep ? o : d);
+        o += (uint32_t)(keep && p < n);
+        d += (uint32_t)(!keep && p < n);
+        key[dst] = kv[j];
+        id[dst] = iv[j];
+    }
+    return t;
 }
 
 }  // namespace tk

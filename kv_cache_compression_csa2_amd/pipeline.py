@@ -10,8 +10,8 @@ Every layer attends with its own Q and its own window KV.
 
 Decode workloads (one query per sequence) run the Full layer's scoring and
 Top-512 fused (csa2_index_topk: no score row is written; its two launches are
-timed separately); the prefill chunk scores with csa2_index_full and selects
-with csa2_topk. Reindex layers score the pool and select in one call
+timed separately); so does the prefill chunk (csa2_index_prefill_topk, one
+launch when each row is one chunk). Reindex layers score the pool and select in one call
 (csa2_index_reindex_topk); `fused_reindex = False` switches them to
 csa2_index_reindex + csa2_topk. `debug_scores` makes the fused calls also
 write the score rows (parity checks).
@@ -50,6 +50,9 @@ class Step:
         self.ws_attn = ws(L.csa2_sparse_attn_workspace_bytes(nq, TOPK))
         self.fused = wl.q_per_seq == 1
         self.ws_ft = ws(L.csa2_index_topk_workspace_bytes(nq, N, TOPK)) if self.fused else None
+        # prefill chunk: scoring fused with the Top-512 (8 queries of a sequence per workgroup)
+        self.prefill_fused = not self.fused and wl.q_per_seq % 8 == 0 and not wl.hier
+        self.ws_pf = ws(L.csa2_index_prefill_topk_workspace_bytes(nq, N, TOPK)) if self.prefill_fused else None
         self.debug_scores = False
         self.fused_reindex = True
         self.ws_rt = ws(L.csa2_index_reindex_topk_workspace_bytes(nq, POOL_BLOCKS, TOPK)) if wl.hier else None
@@ -81,6 +84,13 @@ class Step:
                           top=self.top[0], block_scores=self.blocks, scores=self.scores if self.debug_scores else None,
                           workspace=self.ws_ft, k_fp4=kf, stage=stage)
 
+    def index_prefill_topk(self, k):
+        wl = self.wl
+        kb, kf = self._k(k)
+        L.csa2_index_prefill_topk(wl.q_idx[0], wl.w[0], kb, wl.N, wl.q_per_seq, TOPK, n_visible=wl.n_visible,
+                                  top=self.top[0], scores=self.scores if self.debug_scores else None,
+                                  workspace=self.ws_pf, k_fp4=kf)
+
     def topk_blocks(self):
         L.csa2_topk(self.blocks, POOL_BLOCKS, out=self.cand, workspace=self.ws_topk)
 
@@ -94,6 +104,9 @@ class Step:
             if self.wl.hier:
                 with sp("topk_blocks"):
                     self.topk_blocks()
+        elif self.prefill_fused:
+            with sp("index_topk"):
+                self.index_prefill_topk(k)
         else:
             with sp("index_full"):
                 self.index_full(k)

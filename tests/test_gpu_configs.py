@@ -135,7 +135,7 @@ def test_workload_parity(name):
                         row_len=None if nv is None else dev_i32(nv, DEV))
     torch.cuda.synchronize()
     assert np.array_equal(np_(top_g), top_o)
-    if step.fused:
+    if step.fused or step.prefill_fused:
         # the fused selection is exactly Top-K of the row it scored
         own = K.csa2_topk(step.scores, 512, row_len=wl.n_visible)
         torch.cuda.synchronize()

@@ -362,6 +362,76 @@ def test_index_reindex_topk_bit_exact_on_exact_scores(nq, N, nb, k, qps, fp4):
     assert np.array_equal(np_(top), O.topk(ref, k, id_map=pool))
 
 
+@pytest.mark.parametrize("nq,qps,N,k,fp4", [(16, 16, 5003, 512, False), (8, 8, 70000, 512, False),
+                                            (64, 32, 20000, 100, False), (256, 256, 16384, 512, False),
+                                            (24, 8, 9000, 512, True), (8, 8, 600, 512, False),
+                                            (8, 8, 4096, 512, False), (16, 8, 4000, 300, True)])
+def test_index_prefill_topk_bit_exact_on_exact_scores(nq, qps, N, k, fp4):
+    """Prefill scoring fused with Top-k, on exact-score inputs (small-integer Q
+    and K, power-of-two w, many ties): the selection must equal the oracle's
+    Top-K of the oracle's score row with causal row lengths (one chunk per
+    row, several chunks, a ragged tail, rows with fewer visible entries than
+    k or none, FP4 keys)."""
+    print("case: prefill_topk exact", nq, qps, N, k, fp4, flush=True)
+    q, w, kb = _int_idx_inputs(nq, N, 1300 + N + k + nq, nseq=nq // qps)
+    rng = np.random.default_rng(N + nq)
+    nv = rng.integers(N // 2, N + 1, nq).astype(np.int32)
+    nv[0], nv[-1] = N, min(k // 2, N)
+    if nq > 2:
+        nv[1] = 0
+    nvd = dev_i32(nv, DEV)
+    if fp4:
+        kf_host = O.kidx_fp4_pack(u16(kb)).reshape(nq // qps, N, 68)
+        kf = torch.tensor(kf_host, device=DEV)
+        top = K().csa2_index_prefill_topk(q, w, None, N, qps, k, n_visible=nvd, k_fp4=kf)
+        rs = O.index_full(u16(q), np_(w), None, N, qps, n_visible=nv, k_fp4=kf_host)
+    else:
+        top = K().csa2_index_prefill_topk(q, w, kb, N, qps, k, n_visible=nvd)
+        rs = O.index_full(u16(q), np_(w), u16(kb), N, qps, n_visible=nv)
+    torch.cuda.synchronize()
+    assert np.array_equal(np_(top), O.topk(rs, k, row_len=nv))
+
+
+def test_index_prefill_topk_matches_the_unfused_path():
+    """Random inputs at the prefill chunk's row length: the fused call's debug
+    score rows equal csa2_index_full's bit for bit, and its selection is
+    csa2_topk of that row with the causal row lengths."""
+    print("case: prefill_topk random", flush=True)
+    nq, N, k = 64, 65536, 512
+    q, w, kb = _idx_inputs(nq, N, 1, 1400)
+    nv = dev_i32(np.arange(N - nq + 1, N + 1) // 1, DEV)
+    sc = torch.empty((nq, N), dtype=torch.float32, device=DEV)
+    top = K().csa2_index_prefill_topk(q, w, kb, N, nq, k, n_visible=nv, scores=sc)
+    ref_sc = K().csa2_index_full(q, w, kb, N, nq, n_visible=nv)
+    ref_top = K().csa2_topk(ref_sc, k, row_len=nv)
+    torch.cuda.synchronize()
+    assert torch.equal(sc, ref_sc)
+    assert torch.equal(top, ref_top)
+
+
+def test_index_prefill_topk_rising_scores_compact_often():
+    """Scores that never fall along the row (every entry beats the current
+    k-th best, so the candidate buffers fill and are compacted every few
+    tiles), with long runs of equal scores: still the oracle's Top-K."""
+    print("case: prefill_topk rising", flush=True)
+    nq, N, k = 8, 30000, 512
+    q = torch.zeros((nq, 32, 128), dtype=torch.bfloat16, device=DEV)
+    q[:, 0, 0] = 1.0
+    q[:, 1, 1] = 1.0
+    w = torch.zeros((nq, 32), dtype=torch.float32, device=DEV)
+    w[:, 0] = 1.0
+    w[1::2, 1] = 0.5
+    kb = torch.zeros((1, N, 128), dtype=torch.float32, device=DEV)
+    kb[0, :, 0] = torch.arange(N, device=DEV, dtype=torch.float32) / 7.0  # bf16 rounding makes runs of ties
+    kb[0, :, 1] = torch.arange(N, device=DEV, dtype=torch.float32) % 13
+    kb = kb.to(torch.bfloat16)
+    nv = dev_i32(np.array([N, N - 1, 20000, 513, 512, 100, N, 7], np.int32), DEV)
+    top = K().csa2_index_prefill_topk(q, w, kb, N, nq, k, n_visible=nv)
+    torch.cuda.synchronize()
+    rs = O.index_full(u16(q), np_(w), u16(kb), N, nq, n_visible=np_(nv))
+    assert np.array_equal(np_(top), O.topk(rs, k, row_len=np_(nv)))
+
+
 def test_index_reindex_topk_matches_the_unfused_path():
     """Random inputs at the pages' pool size (2048 blocks): the fused call's
     debug pool row is csa2_index_reindex's, and its selection is csa2_topk of
