@@ -71,6 +71,18 @@ extern "C" {
 #define CSA2_MAX_WINDOW 128 /* sliding-window length limit */
 #define CSA2_MAX_TOPK 4096  /* largest k accepted by csa2_topk */
 
+/* Status bits the attention calls OR into the first 4 bytes of their
+ * workspace for inputs outside the documented domain (device data the host
+ * cannot check without synchronizing). The library never clears the word:
+ * the caller zeroes it, runs one or more calls, synchronizes and reads it. The
+ * outputs of a query that set a bit are unspecified. */
+#define CSA2_STATUS_IDX 1u        /* a selected id outside [-1, N) (the slot is skipped) */
+#define CSA2_STATUS_WIN_LEN 2u    /* swa_len outside [0, 128] (at most 128 rows are used) */
+#define CSA2_STATUS_WIN_RANGE 4u  /* window rows outside [0, T) (those rows are skipped) */
+#define CSA2_STATUS_NONFINITE 8u  /* a non-finite output element: a window value fp16 cannot hold (magnitude
+                                   * >= 65536; FP8 rows: a block scale byte above 134), a NaN E4M3 scale byte,
+                                   * or another non-finite input */
+
 /* Layout version of the 288-byte record (below); bumps if the layout changes. */
 int csa2_format_version(void);
 
@@ -108,7 +120,8 @@ int fp4_kv_unpack(const uint8_t* in, int64_t n, uint16_t* y_bf16, hipStream_t st
  *   q_per_seq queries per sequence; query q reads sequence q / q_per_seq
  *             (decode: 1, prefill chunk on one sequence: nq). Must divide nq.
  *   n_visible [nq] int32 or NULL (= N): entries [0, n_visible[q]) are visible
- *             (0 <= n_visible <= N); the rest score -inf.
+ *             and the rest score -inf; values above N act as N, negative
+ *             values as 0.
  *   scores    [nq][N] fp32 out: sum_h w[q][h] * max(q_idx[q][h] . k, 0).
  *   block_size 0 (no block scores) or 8.
  *   block_scores [nq][ceil(N/8)] fp32 out (when block_size == 8): max of the
@@ -313,7 +326,8 @@ int csa2_index_reindex_topk_fp4k(const uint16_t* q_idx, const float* w, const ui
  * csa2_topk -- per-row Top-K selection (titansim blog, CSA2 modes: Top-512;
  * eogee.com report 3.3: Top-2048 blocks).
  *   scores  [rows][ld] fp32, columns [0, ncols) are candidates.
- *   row_len [rows] int32 or NULL: only columns [0, row_len[r]) of row r compete.
+ *   row_len [rows] int32 or NULL: only columns [0, row_len[r]) of row r compete
+ *           (values above ncols act as ncols, negative values as 0).
  *   k       1 .. CSA2_MAX_TOPK.
  *   id_map  [rows][ld] int32 or NULL: output column c of row r as id_map[r][c]
  *           (used to turn pool positions into entry ids).
@@ -339,18 +353,25 @@ int csa2_topk(const float* scores, int32_t rows, int64_t ncols, int64_t ld, cons
  *   swa     [nseq][T][512] bf16: the layer's window KV rows (key = value).
  *   swa_start, swa_len [nq] int32: query q also attends to rows
  *           [swa_start[q], swa_start[q]+swa_len[q]) of its sequence's window
- *           buffer; 0 <= swa_len <= 128 and the range must lie inside [0, T).
- *           Both may be NULL (no window keys).
+ *           buffer; 0 <= swa_len <= 128 and the range must lie inside [0, T)
+ *           (else CSA2_STATUS_WIN_LEN / _WIN_RANGE). Both may be NULL (no
+ *           window keys).
  *   softmax_scale: multiplies q.k before the softmax (1/sqrt(512)).
  *           The products run in fp16 with fp32 accumulation: decoded FP4 values
- *           are exact in fp16, and q and swa values must lie below 65504 in
- *           magnitude (bf16 values of 2^-14 or more convert exactly; smaller
- *           ones to within 2^-25).
+ *           are exact in fp16; each head's q is scaled by a power of two (undone
+ *           in its logits) so every finite bf16 q converts exactly, except
+ *           elements below 2^-28 of the head's largest, which round; window
+ *           values must lie below 65504 in magnitude (else the output is not
+ *           finite and CSA2_STATUS_NONFINITE is set; bf16 values of 2^-14 or
+ *           more convert exactly, smaller ones to within 2^-25).
  *   out     [nq][64][512] bf16 out: softmax over all of the query's keys jointly.
  *   lse     [nq][64] fp32 out or NULL: natural-log sum of exp of the scaled logits.
  *           A query with no keys gets out = 0 and lse = -inf.
  *   workspace / ws_bytes: at least csa2_sparse_attn_workspace_bytes(nq, k) bytes
- *           (partial results when a query's keys are split across workgroups).
+ *           (>= 256: the status word, then partial results when a query's keys
+ *           are split across workgroups). Bytes [0, 4) hold the status word
+ *           (CSA2_STATUS_* bits, ORed in, never cleared); the rest need no
+ *           initialization.
  */
 size_t csa2_sparse_attn_workspace_bytes(int32_t nq, int32_t k);
 int csa2_sparse_attn(const uint16_t* q, const uint8_t* kv, int64_t N, int32_t nq, int32_t q_per_seq,

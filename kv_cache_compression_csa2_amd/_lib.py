@@ -361,6 +361,15 @@ def csa2_topk(scores, k, row_len=None, id_map=None, out=None, workspace=None, st
     return out
 
 
+STATUS_IDX, STATUS_WIN_LEN, STATUS_WIN_RANGE, STATUS_NONFINITE = 1, 2, 4, 8
+
+
+def attn_status(workspace):
+    """The status word of an attention workspace (CSA2_STATUS_* bits; the
+    caller zeroes it before the calls it covers and reads it after them)."""
+    return int(workspace[:4].view(torch.int32)[0].item())
+
+
 def csa2_sparse_attn_workspace_bytes(nq, k):
     return load().csa2_sparse_attn_workspace_bytes(nq, k)
 

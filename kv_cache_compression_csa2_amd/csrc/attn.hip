@@ -30,9 +30,13 @@
 // in logical order.
 //
 // fp16 holds every bf16 value of magnitude 2^-14 .. 65504 exactly (smaller
-// ones to within 2^-25), so Q and the window rows must stay below 65504 in
-// magnitude. P is rounded to fp16 (its values are <= 2^8) and the softmax
-// denominator sums the rounded values.
+// ones to within 2^-25). Each head's Q is scaled by a power of two that puts
+// its largest magnitude in [2^14, 2^15) before the conversion, and the head's
+// logit scale carries the inverse, so any finite bf16 Q converts exactly
+// (elements below 2^-28 of the head's largest lose bits). Window rows must
+// stay below 65504 in magnitude (a status bit reports rows that do not). P is
+// rounded to fp16 (its values are <= 2^8) and the softmax denominator sums
+// the rounded values.
 //
 // The running max is refreshed only when it grows by more than 2^8, so the
 // 128-register O^T rescale is rare; exp2 arguments stay <= 8. It starts at a
@@ -110,6 +114,30 @@ CSA2_DEVINL uint4 bf16x8_to_f16x8(uint4 v) {
 }
 CSA2_DEVINL f16x8 as_f16x8(uint4 v) { return __builtin_bit_cast(f16x8, v); }
 
+// Eight bf16 times the power of two `up` -> fp16 (round to nearest even).
+CSA2_DEVINL uint32_t bf16x2_to_f16x2_scaled(uint32_t v, float up) {
+    const f32x2 f = {__uint_as_float(v << 16) * up, __uint_as_float(v & 0xFFFF0000u) * up};
+    return __builtin_bit_cast(uint32_t, __builtin_convertvector(f, f16x2));
+}
+CSA2_DEVINL uint4 bf16x8_to_f16x8_scaled(uint4 v, float up) {
+    return make_uint4(bf16x2_to_f16x2_scaled(v.x, up), bf16x2_to_f16x2_scaled(v.y, up),
+                      bf16x2_to_f16x2_scaled(v.z, up), bf16x2_to_f16x2_scaled(v.w, up));
+}
+typedef unsigned short u16x2 __attribute__((ext_vector_type(2)));
+// Running maximum of bf16 magnitude bits (|x| orders like them), two lanes of
+// 16 bits at a time (packed u16 max).
+CSA2_DEVINL u16x2 bf16x8_max_mag2(uint4 v, u16x2 m) {
+    const uint32_t w[4] = {v.x, v.y, v.z, v.w};
+#pragma unroll
+    for (int i = 0; i < 4; i++) m = __builtin_elementwise_max(m, __builtin_bit_cast(u16x2, w[i] & 0x7FFF7FFFu));
+    return m;
+}
+// Largest magnitude of eight bf16 as magnitude bits.
+CSA2_DEVINL uint32_t bf16x8_max_mag(uint4 v) {
+    const u16x2 m = bf16x8_max_mag2(v, u16x2{0, 0});
+    return max((uint32_t)m[0], (uint32_t)m[1]);
+}
+
 // Two floats -> packed fp16 pair (lo in bits 0..15), round to nearest even.
 CSA2_DEVINL uint32_t pack_f16x2(float lo, float hi) {
     return __builtin_bit_cast(uint32_t, __builtin_convertvector(f32x2{lo, hi}, f16x2));
@@ -129,6 +157,12 @@ CSA2_DEVINL float max_over_groups(float v) {
     v = fmaxf(__uint_as_float(a[0]), __uint_as_float(a[1]));
     const auto b = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
     return fmaxf(__uint_as_float(b[0]), __uint_as_float(b[1]));
+}
+CSA2_DEVINL uint32_t max_over_groups_u(uint32_t v) {
+    const auto a = __builtin_amdgcn_permlane16_swap(v, v, false, false);
+    v = max(a[0], a[1]);
+    const auto b = __builtin_amdgcn_permlane32_swap(v, v, false, false);
+    return max(b[0], b[1]);
 }
 CSA2_DEVINL float sum_over_groups(float v) {
     const auto a = __builtin_amdgcn_permlane16_swap(__float_as_uint(v), __float_as_uint(v), false, false);
@@ -184,11 +218,13 @@ __global__ __launch_bounds__(kAttThreads, 2) void sparse_attn_kernel(
     const int32_t* __restrict__ idx, int32_t k, const void* __restrict__ swa, int64_t T,
     const int32_t* __restrict__ swa_start, const int32_t* __restrict__ swa_len, float scale_log2,
     uint16_t* __restrict__ out, float* __restrict__ lse, uint16_t* __restrict__ part_o, float* __restrict__ part_ml,
-    int32_t nsplit) {
+    int32_t nsplit, uint32_t* __restrict__ status) {
     __shared__ __attribute__((aligned(16))) uint8_t lds[2 * kTileB];
     // 0 or -inf per key, stored at perm16_inv(row) (+16 for the second half)
     // so that a lane's four keys of a half-tile are one 16-byte read
     __shared__ __attribute__((aligned(16))) float key_bias[2][kTile];
+    // status bits seen by the workgroup (written only when an input is out of domain)
+    __shared__ uint32_t bad_sh;
     // entry ids of this workgroup's main tiles, range-checked (-1: empty)
     extern __shared__ int32_t sid[];
 
@@ -219,12 +255,22 @@ __global__ __launch_bounds__(kAttThreads, 2) void sparse_attn_kernel(
     const uint8_t* swa8_seq = (swa && kFp8Win) ? static_cast<const uint8_t*>(swa) + seq * T * kSwaRec : nullptr;
     const int32_t* idx_q = idx + qi * (int64_t)k + (int64_t)m0 * kTile;
 
-    // the workgroup's entry ids, checked once
+    // the workgroup's entry ids, checked once (ids outside [-1, N) are
+    // skipped and reported); the status bits gather in bad_sh, cleared here
+    // with no dependence on any load and set only after the barrier below
+    if (tid == 0) bad_sh = 0u;
+    uint32_t bad = 0;
     for (int i = tid; i < nmain * kTile; i += kAttThreads) {
         const int32_t v = (m0 * kTile + i < k) ? idx_q[i] : -1;
         sid[i] = (v >= 0 && v < N) ? v : -1;
+        bad |= (v < -1 || v >= N) ? kStatusIdx : 0u;
+    }
+    if (split == 0 && tid == 0 && swa) {
+        bad |= (slen < 0 || slen > kMaxWindow) ? kStatusWinLen : 0u;
+        bad |= (slen > 0 && (sst < 0 || (int64_t)sst + slen > T)) ? kStatusWinRange : 0u;
     }
     lds_barrier();
+    if (bad) atomicOr(&bad_sh, bad);
 
     // gather role: rows r0 and r0 + 16 of a tile, 32-dim chunk c
     const int r0 = tid >> 4, c = tid & 15;
@@ -270,6 +316,10 @@ __global__ __launch_bounds__(kAttThreads, 2) void sparse_attn_kernel(
                 const uint8_t* rec = swa8_seq + (int64_t)(sst + r) * kSwaRec;
                 const uint4 c0 = reinterpret_cast<const uint4*>(rec + 32 * c)[0];
                 const uint4 c1 = reinterpret_cast<const uint4*>(rec + 32 * c)[1];
+                // 448 * 2^(b-127) < 65504 only for scale bytes up to 134; past
+                // that the conversion's result is out of fp16's range (a plain
+                // store: every writer stores the same bit)
+                if (rec[kDim + c] > 134) bad_sh = kStatusNonFinite;
                 // the E8M0 byte as the exponent field of a binary32: the
                 // conversion applies that power of two
                 const float X = __uint_as_float((uint32_t)rec[kDim + c] << 23);
@@ -305,11 +355,25 @@ __global__ __launch_bounds__(kAttThreads, 2) void sparse_attn_kernel(
     // issued first are the ones the first decode can wait for alone.
     // Q^T operand of k-step s: head `head`, the logical dims of physical unit 4s + G.
     f16x8 qf[16];
+    float sl2;  // this head's logit scale (log2 units), times 2^-sh
     {
         const uint16_t* qh = q + (qi * kHeads + head) * kDim;
+        uint4 qr[16];
+        uint32_t amax = 0;  // largest |q| of the head as bf16 magnitude bits
 #pragma unroll
-        for (int s = 0; s < 16; s++)
-            qf[s] = as_f16x8(bf16x8_to_f16x8(*reinterpret_cast<const uint4*>(qh + 8 * unit_logical(4 * s + G))));
+        for (int s = 0; s < 16; s++) {
+            qr[s] = *reinterpret_cast<const uint4*>(qh + 8 * unit_logical(4 * s + G));
+            amax = max(amax, bf16x8_max_mag(qr[s]));
+        }
+        amax = (uint32_t)max_over_groups_u(amax);
+        // 2^sh puts the head's largest magnitude in [2^14, 2^15): exponent
+        // field e -> floor(log2 amax) = e - 127 (bf16 subnormals and zero heads
+        // take the clamp)
+        const int sh = min(max(14 - ((int)(amax >> 7) - 127), -126), 126);
+        const float up = __uint_as_float((uint32_t)(127 + sh) << 23);
+#pragma unroll
+        for (int s = 0; s < 16; s++) qf[s] = as_f16x8(bf16x8_to_f16x8_scaled(qr[s], up));
+        sl2 = scale_log2 * __uint_as_float((uint32_t)(127 - sh) << 23);
     }
 
     const int pr_a = perm16(j), pr_t = perm16(4 * G + (j >> 2));
@@ -344,8 +408,8 @@ __global__ __launch_bounds__(kAttThreads, 2) void sparse_attn_kernel(
         float x[8];
 #pragma unroll
         for (int r = 0; r < 4; r++) {
-            x[r] = fmaf(s0[r], scale_log2, bias0[r]);
-            x[4 + r] = fmaf(s1[r], scale_log2, bias1[r]);
+            x[r] = fmaf(s0[r], sl2, bias0[r]);
+            x[4 + r] = fmaf(s1[r], sl2, bias1[r]);
         }
         float tmax = fmaxf(fmaxf(fmaxf(x[0], x[1]), fmaxf(x[2], x[3])), fmaxf(fmaxf(x[4], x[5]), fmaxf(x[6], x[7])));
         tmax = max_over_groups(tmax);
@@ -393,21 +457,41 @@ __global__ __launch_bounds__(kAttThreads, 2) void sparse_attn_kernel(
     // logical dims 8*L(2mt + G/2) + 4*(G%2) + r: four consecutive ones per mt.
     lds_barrier();  // every wave is done with the tile buffers
     uint8_t* stg = lds + wave * (16 * kStgRow);
+    // Out-of-domain inputs (a window value fp16 cannot hold, a NaN scale,
+    // another non-finite input) always leave non-finite values in the output:
+    // the packed words' exponent fields are checked once here instead of
+    // every input value in the tile loop.
+    uint32_t emax = 0;
     {
         uint8_t* row = stg + j * kStgRow + 8 * (G & 1);
         if (nsplit > 1) {
+            u16x2 mm = {0, 0};
 #pragma unroll
-            for (int mt = 0; mt < 32; mt++)
-                *reinterpret_cast<uint2*>(row + 16 * unit_logical(2 * mt + (G >> 1))) =
+            for (int mt = 0; mt < 32; mt++) {
+                const uint2 w2 =
                     make_uint2(pack_f16x2(o[mt][0] * inv, o[mt][1] * inv), pack_f16x2(o[mt][2] * inv, o[mt][3] * inv));
+                *reinterpret_cast<uint2*>(row + 16 * unit_logical(2 * mt + (G >> 1))) = w2;
+                mm = __builtin_elementwise_max(mm, __builtin_bit_cast(u16x2, w2.x & 0x7C007C00u));
+                mm = __builtin_elementwise_max(mm, __builtin_bit_cast(u16x2, w2.y & 0x7C007C00u));
+            }
+            emax = max(mm[0], mm[1]) == 0x7C00 ? 1u : 0u;
         } else {
+            u16x2 mm = {0, 0};
 #pragma unroll
-            for (int mt = 0; mt < 32; mt++)
-                *reinterpret_cast<uint2*>(row + 16 * unit_logical(2 * mt + (G >> 1))) =
-                    make_uint2(pack_bf16x2(o[mt][0] * inv, o[mt][1] * inv), pack_bf16x2(o[mt][2] * inv, o[mt][3] * inv));
+            for (int mt = 0; mt < 32; mt++) {
+                const uint2 w2 = make_uint2(pack_bf16x2(o[mt][0] * inv, o[mt][1] * inv),
+                                            pack_bf16x2(o[mt][2] * inv, o[mt][3] * inv));
+                *reinterpret_cast<uint2*>(row + 16 * unit_logical(2 * mt + (G >> 1))) = w2;
+                mm = __builtin_elementwise_max(mm, __builtin_bit_cast(u16x2, w2.x & 0x7F807F80u));
+                mm = __builtin_elementwise_max(mm, __builtin_bit_cast(u16x2, w2.y & 0x7F807F80u));
+            }
+            emax = max(mm[0], mm[1]) == 0x7F80 ? 1u : 0u;
         }
+        emax |= (l_tot == l_tot && l_tot != INFINITY) ? 0u : 1u;
     }
+    if (__any(emax) && lane == 0) atomicOr(&bad_sh, kStatusNonFinite);
     lds_barrier();
+    if (tid == 0 && status && bad_sh) atomicOr(status, bad_sh);
     const int64_t prow = nsplit == 1 ? qi * kHeads : (qi * nsplit + split) * kHeads;  // row of head 0
     uint16_t* dst = (nsplit == 1 ? out : part_o) + (prow + wave * 16) * kDim + 8 * lane;
     // Split partials go out with non-temporal stores: written once and read by
@@ -425,11 +509,14 @@ __global__ __launch_bounds__(kAttThreads, 2) void sparse_attn_kernel(
             *reinterpret_cast<uint4*>(dst + (int64_t)i * kDim) = *reinterpret_cast<const uint4*>(stg + i * kStgRow + 16 * lane);
     }
     if (G == 0) {
+        // the head index from the hardware lane id: recomputed here rather
+        // than kept live (in a register or a spill slot) through the tile loop
+        const int head_e = wave * 16 + (int)(__builtin_amdgcn_mbcnt_hi(~0u, __builtin_amdgcn_mbcnt_lo(~0u, 0u)) & 15);
         if (nsplit == 1) {
-            if (lse) lse[qi * kHeads + head] = l_tot > 0.0f ? (m_run + log2f(l_tot)) * 0.69314718055994531f : -INFINITY;
+            if (lse) lse[qi * kHeads + head_e] = l_tot > 0.0f ? (m_run + log2f(l_tot)) * 0.69314718055994531f : -INFINITY;
         } else {
-            part_ml[(prow + head) * 2 + 0] = l_tot > 0.0f ? m_run : -INFINITY;
-            part_ml[(prow + head) * 2 + 1] = l_tot;
+            part_ml[(prow + head_e) * 2 + 0] = l_tot > 0.0f ? m_run : -INFINITY;
+            part_ml[(prow + head_e) * 2 + 1] = l_tot;
         }
     }
 }
@@ -478,10 +565,12 @@ __global__ __launch_bounds__(128) void attn_merge_kernel(const uint16_t* __restr
 
 }  // namespace
 
+// Workspace: the status word (kStatusBytes, so the partials stay aligned),
+// then the split partials when a query's tiles are split.
 size_t attn_workspace_bytes(int32_t nq, int32_t k) {
     const int ns = attn_splits(nq, k);
-    if (ns <= 1) return 0;
-    return (size_t)nq * ns * kHeads * (kDim * sizeof(uint16_t) + 2 * sizeof(float));
+    if (ns <= 1) return kStatusBytes;
+    return kStatusBytes + (size_t)nq * ns * kHeads * (kDim * sizeof(uint16_t) + 2 * sizeof(float));
 }
 
 int launch_sparse_attn(const uint16_t* q, const uint8_t* kv, int64_t N, int32_t nq, int32_t q_per_seq,
@@ -495,18 +584,19 @@ int launch_sparse_attn(const uint16_t* q, const uint8_t* kv, int64_t N, int32_t 
     const size_t sid_bytes = (size_t)((mt + ns - 1) / ns) * kTile * sizeof(int32_t);
     uint16_t* part_o = nullptr;
     float* part_ml = nullptr;
+    uint32_t* status = reinterpret_cast<uint32_t*>(ws);
     if (ns > 1) {
-        part_o = reinterpret_cast<uint16_t*>(ws);
+        part_o = reinterpret_cast<uint16_t*>(static_cast<uint8_t*>(ws) + kStatusBytes);
         part_ml = reinterpret_cast<float*>(part_o + (size_t)nq * ns * kHeads * kDim);
     }
     const float scale_log2 = softmax_scale * 1.4426950408889634f;
     const dim3 grid((unsigned)((int64_t)nq * ns));
     if (swa_fp8)
         hipLaunchKernelGGL(sparse_attn_kernel<true>, grid, dim3(kAttThreads), sid_bytes, s, q, kv, N, q_per_seq, idx,
-                           k, swa, T, swa_start, swa_len, scale_log2, out, lse, part_o, part_ml, ns);
+                           k, swa, T, swa_start, swa_len, scale_log2, out, lse, part_o, part_ml, ns, status);
     else
         hipLaunchKernelGGL(sparse_attn_kernel<false>, grid, dim3(kAttThreads), sid_bytes, s, q, kv, N, q_per_seq, idx,
-                           k, swa, T, swa_start, swa_len, scale_log2, out, lse, part_o, part_ml, ns);
+                           k, swa, T, swa_start, swa_len, scale_log2, out, lse, part_o, part_ml, ns, status);
     if (ns > 1)
         hipLaunchKernelGGL(attn_merge_kernel, dim3((unsigned)((int64_t)nq * kHeads)), dim3(128), 0, s, part_o,
                            part_ml, ns, out, lse);

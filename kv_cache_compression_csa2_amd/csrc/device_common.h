@@ -19,6 +19,13 @@ constexpr int kMaxWindow = 128;
 constexpr int kKidxBlock = 32;                            // channels per E8M0 scale of an FP4 indexer-K entry
 constexpr int kKidxRecord = kIdxDim / 2 + kIdxDim / kKidxBlock;  // 68
 
+// Attention status bits (the first word of its workspace; ORed, never cleared).
+constexpr uint32_t kStatusIdx = 1u;       // a selected id outside [-1, N)
+constexpr uint32_t kStatusWinLen = 2u;    // swa_len outside [0, 128]
+constexpr uint32_t kStatusWinRange = 4u;  // window rows outside [0, T)
+constexpr uint32_t kStatusNonFinite = 8u; // a non-finite output (a window value fp16 cannot hold, a NaN scale, ...)
+constexpr size_t kStatusBytes = 256;      // the status word's share of the workspace
+
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef float f32x16 __attribute__((ext_vector_type(16)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));

@@ -576,6 +576,123 @@ def test_sparse_attn_no_split_many_queries():
     _attn_check(q, kv, idx, swa, st, sl, N, nq, nq + 127)
 
 
+def test_sparse_attn_split_path():
+    """129..511 queries: each query's tiles split over workgroups and merged."""
+    print("case: attn split path", flush=True)
+    nq, N = 200, 800
+    q, kv, idx, swa, st, sl = _attn_case(nq, N, 512, 1, 6, pad=5)
+    sl[:6] = [0, 1, 31, 33, 64, 127]
+    _attn_check(q, kv, idx, swa, st, sl, N, 1, 128)
+
+
+@pytest.mark.parametrize("nq,k", [(12, 512), (12, 80)])
+def test_sparse_attn_window_lengths(nq, k):
+    """Window lengths at and around tile boundaries, window starts inside the
+    buffer, and fewer selected entries than one tile per wave."""
+    print("case: attn window lengths", nq, k, flush=True)
+    N, T = 900, 300
+    q, kv, idx, swa, st, sl = _attn_case(nq, N, k, 1, 7 + k, T=T, pad=3)
+    sl = np.array([0, 1, 31, 32, 33, 63, 64, 65, 97, 127, 128, 5], np.int32)[:nq]
+    st = np.random.default_rng(8).integers(0, T - 128, nq).astype(np.int32)
+    _attn_check(q, kv, idx, swa, st, sl, N, 1, T)
+
+
+def test_sparse_attn_q_of_any_magnitude():
+    """Every finite bf16 Q enters the fp16 products exactly: heads scaled far
+    above fp16's range (2^20 .. 2^100), far below it (2^-20 .. 2^-100) and an
+    all-zero head still match the oracle (hard-max and uniform softmaxes
+    included)."""
+    print("case: attn q magnitudes", flush=True)
+    nq, N, k = 3, 2000, 512
+    q, kv, idx, swa, st, sl = _attn_case(nq, N, k, 1, 501)
+    ex = torch.tensor([0, 20, 100, -100, -20, 60, -60, 10] * 8, dtype=torch.float32, device=DEV)
+    qs = (q.float() * torch.exp2(ex).view(1, 64, 1)).to(torch.bfloat16)
+    qs[1, 5] = 0
+    assert torch.isfinite(qs.float()).all()
+    _attn_check(qs.contiguous(), kv, idx, swa, st, sl, N, 1, 128)
+
+
+def _attn_status_of(q, kv, idx, swa, st, sl, N, swa_fp8=None):
+    import kv_cache_compression_csa2_amd._lib as L
+    nq, k = q.shape[0], idx.shape[1]
+    ws = torch.empty((L.csa2_sparse_attn_workspace_bytes(nq, k),), dtype=torch.uint8, device=DEV)
+    ws[:4].zero_()
+    K().csa2_sparse_attn(q, kv, N, 1, dev_i32(idx, DEV), swa, dev_i32(st, DEV), dev_i32(sl, DEV), workspace=ws,
+                         swa_fp8=swa_fp8)
+    torch.cuda.synchronize()
+    return L.attn_status(ws)
+
+
+@pytest.mark.parametrize("nq", [6, 600])
+def test_sparse_attn_status_reports_out_of_domain_inputs(nq):
+    """Inputs outside the documented domain set their status bit (ids outside
+    [-1, N), swa_len above 128, window rows past the buffer, window values fp16
+    cannot hold, which leave a non-finite output); in-domain calls leave the
+    word at 0. Both the split (6 queries) and the unsplit (600) launch."""
+    import kv_cache_compression_csa2_amd._lib as L
+    print("case: attn status", nq, flush=True)
+    N, k, T = 1000, 64, 200
+    q, kv, idx, swa, st, sl = _attn_case(nq, N, k, 1, 600 + nq, T=T)
+    assert _attn_status_of(q, kv, idx, swa, st, sl, N) == 0
+    bad = idx.copy()
+    bad[1, 3] = N
+    assert _attn_status_of(q, kv, bad, swa, st, sl, N) == L.STATUS_IDX
+    bad[1, 3] = -7
+    assert _attn_status_of(q, kv, bad, swa, st, sl, N) == L.STATUS_IDX
+    sl2 = sl.copy()
+    sl2[2] = 130
+    assert _attn_status_of(q, kv, idx, swa, st, sl2, N) == L.STATUS_WIN_LEN
+    st2 = st.copy()
+    st2[3] = T - 10
+    assert _attn_status_of(q, kv, idx, swa, st2, sl, N) == L.STATUS_WIN_RANGE
+    swa2 = swa.clone()
+    swa2[4, 5, 100] = 70000.0
+    assert _attn_status_of(q, kv, idx, swa2, st, sl, N) == L.STATUS_NONFINITE
+    swa2[4, 5, 100] = 65280.0  # the largest bf16 below 65504 is in range
+    assert _attn_status_of(q, kv, idx, swa2, st, sl, N) == 0
+    # FP8 rows: a block scale that lifts its values past 65504
+    w8 = K().swa_fp8_pack(swa.reshape(-1, 512).contiguous()).view(swa.shape[0], T, 528)
+    assert _attn_status_of(q, kv, idx, None, st, sl, N, swa_fp8=w8) == 0
+    w8b = w8.clone()
+    w8b[0, 7, 512 + 3] = 135
+    assert _attn_status_of(q, kv, idx, None, st, sl, N, swa_fp8=w8b) == L.STATUS_NONFINITE
+
+
+def test_visible_lengths_are_clamped_like_the_oracle():
+    """n_visible above N acts as N and below 0 as 0 in every scoring call (and
+    row_len likewise in csa2_topk), exactly as in the oracle."""
+    print("case: visibility clamps", flush=True)
+    nq, N = 8, 3000
+    q, w, kb = _idx_inputs(nq, N, nq, 700)
+    nv = np.array([N + 5, -3, 100, 2 ** 31 - 1, 0, N, 1, -2 ** 31], np.int32)
+    nvd = dev_i32(nv, DEV)
+    s = K().csa2_index_full(q, w, kb, N, 1, n_visible=nvd)
+    top = K().csa2_index_topk(q, w, kb, N, 512, n_visible=nvd)
+    torch.cuda.synchronize()
+    rs = O.index_full(u16(q), np_(w), u16(kb), N, 1, n_visible=nv)
+    ok, msg = rel_close(np_(s), rs)
+    assert ok, msg
+    assert np.array_equal(np_(top), O.topk(rs, 512, row_len=nv))
+    assert np.array_equal(np_(K().csa2_topk(s, 512, row_len=nvd)), O.topk(np_(s), 512, row_len=nv))
+    # prefill: 8 queries of one sequence
+    q1, w1, k1 = _idx_inputs(8, N, 1, 710)
+    s1 = K().csa2_index_full(q1, w1, k1, N, 8, n_visible=nvd)
+    t1 = K().csa2_index_prefill_topk(q1, w1, k1, N, 8, 512, n_visible=nvd)
+    torch.cuda.synchronize()
+    r1 = O.index_full(u16(q1), np_(w1), u16(k1), N, 8, n_visible=nv)
+    ok, msg = rel_close(np_(s1), r1)
+    assert ok, msg
+    assert np.array_equal(np_(t1), O.topk(np_(s1), 512, row_len=nv))
+    # reindex: pool positions past the clamped length score -inf
+    blocks = np.tile(np.arange(0, 300, 2, dtype=np.int32), (nq, 1))
+    ps, pid = K().csa2_index_reindex(q, w, kb, N, 1, dev_i32(blocks, DEV), n_visible=nvd)
+    torch.cuda.synchronize()
+    pool = O.pool_ids(blocks, 8)
+    ref = O.index_reindex(u16(q), np_(w), u16(kb), N, 1, pool, n_visible=nv)
+    ok, msg = rel_close(np_(ps), ref)
+    assert ok, msg
+
+
 def test_sparse_attn_degenerate():
     print("case: attn degenerate", flush=True)
     nq, N = 4, 300
