@@ -240,6 +240,28 @@ int csa2_index_topk_merge(int64_t N, int32_t nq, int32_t k, int32_t* top_idx, vo
                           hipStream_t stream);
 
 /*
+ * csa2_index_topk_merge_pool -- the rest of a hierarchical Full layer after
+ * csa2_index_topk_select with block_size 8: completes the layer's Top-k (as
+ * csa2_index_topk_merge) and selects the candidate pool's best blocks from the
+ * block maxima (as csa2_topk(block_scores, pool_k); eogee.com report 3.3: the
+ * Full layer keeps the 2048 best 8-position blocks for the Reindex layers).
+ * The two selections do not depend on each other and share launches.
+ *   N, nq, k, top_idx: as the csa2_index_topk_select call before it, on the
+ *           same stream.
+ *   block_scores [nq][ceil(N/8)] fp32 in: the block maxima that call wrote.
+ *   pool_k  1 .. CSA2_MAX_TOPK.
+ *   cand_blocks [nq][pool_k] int32 out: exactly csa2_topk(block_scores,
+ *           pool_k): ascending block ids, then -1 padding.
+ *   workspace / ws_bytes: at least csa2_index_topk_pool_workspace_bytes(nq, N,
+ *           k, pool_k) bytes, the same buffer the select call wrote its
+ *           candidates to (the pool's selection uses the bytes after them).
+ */
+size_t csa2_index_topk_pool_workspace_bytes(int32_t nq, int64_t N, int32_t k, int32_t pool_k);
+int csa2_index_topk_merge_pool(int64_t N, int32_t nq, int32_t k, int32_t* top_idx, const float* block_scores,
+                               int32_t pool_k, int32_t* cand_blocks, void* workspace, size_t ws_bytes,
+                               hipStream_t stream);
+
+/*
  * csa2_index_topk_noalloc -- csa2_index_topk with no workspace argument and no
  * allocation, for callers that cannot allocate device memory (code under HIP
  * graph capture, tight serving loops, harnesses that forbid hipMalloc).

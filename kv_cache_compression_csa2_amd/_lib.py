@@ -52,6 +52,9 @@ def load():
     L.csa2_index_topk_fp4k.argtypes = [vp, vp, vp, i64, i32, vp, i32, vp, i32, vp, vp, vp, sz, vp]
     L.csa2_index_topk_select.argtypes = [vp, vp, vp, i32, i64, i32, vp, i32, vp, i32, vp, vp, vp, sz, vp]
     L.csa2_index_topk_merge.argtypes = [i64, i32, i32, vp, vp, sz, vp]
+    L.csa2_index_topk_pool_workspace_bytes.argtypes = [i32, i64, i32, i32]
+    L.csa2_index_topk_pool_workspace_bytes.restype = sz
+    L.csa2_index_topk_merge_pool.argtypes = [i64, i32, i32, vp, vp, i32, vp, vp, sz, vp]
     L.csa2_index_topk_noalloc_scratch_bytes.argtypes = []
     L.csa2_index_topk_noalloc_scratch_bytes.restype = sz
     L.csa2_index_topk_noalloc.argtypes = [vp, vp, vp, i32, i64, i32, vp, i32, vp, i32, vp, vp, vp]
@@ -73,8 +76,8 @@ def load():
     for name in ["fp4_kv_pack", "fp4_kv_unpack", "csa2_index_full", "csa2_index_reindex", "csa2_topk",
                  "csa2_sparse_attn", "kidx_fp4_pack", "csa2_index_full_fp4k", "csa2_index_reindex_fp4k",
                  "swa_fp8_pack", "csa2_sparse_attn_fp8w", "csa2_index_topk", "csa2_index_topk_fp4k",
-                 "csa2_index_topk_select", "csa2_index_topk_merge", "csa2_index_reindex_topk",
-                 "csa2_index_reindex_topk_fp4k", "csa2_index_topk_noalloc", "csa2_index_prefill_topk",
+                 "csa2_index_topk_select", "csa2_index_topk_merge", "csa2_index_topk_merge_pool",
+                 "csa2_index_reindex_topk", "csa2_index_reindex_topk_fp4k", "csa2_index_topk_noalloc", "csa2_index_prefill_topk",
                  "csa2_index_prefill_topk_fp4k"]:
         getattr(L, name).restype = ctypes.c_int
     _lib = L
@@ -85,7 +88,8 @@ EXPORTS = ["csa2_format_version", "csa2_last_error", "fp4_kv_pack", "fp4_kv_unpa
            "csa2_index_reindex", "csa2_topk_workspace_bytes", "csa2_topk", "csa2_sparse_attn_workspace_bytes",
            "csa2_sparse_attn", "kidx_fp4_pack", "csa2_index_full_fp4k", "csa2_index_reindex_fp4k", "swa_fp8_pack",
            "csa2_sparse_attn_fp8w", "csa2_index_topk_workspace_bytes", "csa2_index_topk", "csa2_index_topk_fp4k",
-           "csa2_index_topk_select", "csa2_index_topk_merge", "csa2_index_reindex_topk_workspace_bytes",
+           "csa2_index_topk_select", "csa2_index_topk_merge", "csa2_index_topk_pool_workspace_bytes",
+           "csa2_index_topk_merge_pool", "csa2_index_reindex_topk_workspace_bytes",
            "csa2_index_reindex_topk", "csa2_index_reindex_topk_fp4k", "csa2_index_topk_noalloc_scratch_bytes",
            "csa2_index_topk_noalloc", "csa2_index_prefill_topk_workspace_bytes", "csa2_index_prefill_topk",
            "csa2_index_prefill_topk_fp4k"]
@@ -236,6 +240,27 @@ def csa2_index_topk(q_idx, w, k_idx, N, k, n_visible=None, block_size=0, top=Non
         fn = getattr(load(), "csa2_index_topk" + suffix)
         _check(fn(_ptr(q_idx), _ptr(w), kp, *args), "csa2_index_topk" + suffix)
     return (top, block_scores) if block_size else top
+
+
+def csa2_index_topk_pool_workspace_bytes(nq, N, k, pool_k):
+    return load().csa2_index_topk_pool_workspace_bytes(nq, N, k, pool_k)
+
+
+def csa2_index_topk_merge_pool(N, k, top, block_scores, pool_k, cand_blocks=None, workspace=None, stream=None):
+    """Completes a csa2_index_topk(stage="select", block_size=8) call: its
+    Top-k into `top` and the pool's Top-pool_k blocks of `block_scores` into
+    `cand_blocks` (int32 [nq,pool_k]). `workspace` is the select call's, of at
+    least csa2_index_topk_pool_workspace_bytes(nq, N, k, pool_k) bytes."""
+    for t, dt, nm in [(top, torch.int32, "top"), (block_scores, torch.float32, "block_scores"),
+                      (cand_blocks, torch.int32, "cand_blocks")]:
+        _need(t, dt, nm)
+    nq = top.shape[0]
+    if cand_blocks is None:
+        cand_blocks = torch.empty((nq, pool_k), dtype=torch.int32, device=top.device)
+    wsb = workspace.numel() * workspace.element_size() if workspace is not None else 0
+    _check(load().csa2_index_topk_merge_pool(N, nq, k, _ptr(top), _ptr(block_scores), pool_k, _ptr(cand_blocks),
+                                             _ptr(workspace), wsb, _stream(stream)), "csa2_index_topk_merge_pool")
+    return top, cand_blocks
 
 
 def csa2_index_prefill_topk_workspace_bytes(nq, N, k):

@@ -219,6 +219,31 @@ int csa2_index_topk_merge(int64_t N, int32_t nq, int32_t k, int32_t* top_idx, vo
     return launched("csa2_index_topk_merge");
 }
 
+size_t csa2_index_topk_pool_workspace_bytes(int32_t nq, int64_t N, int32_t k, int32_t pool_k) {
+    if (nq <= 0 || N < 1 || N > kMaxN || k < 1 || k > CSA2_MAX_TOPK || pool_k < 1 || pool_k > CSA2_MAX_TOPK) return 0;
+    if (!csa2::index_topk_fits(nq, N, k)) return 0;
+    return csa2::index_topk_pool_workspace_bytes(nq, N, k, pool_k);
+}
+
+int csa2_index_topk_merge_pool(int64_t N, int32_t nq, int32_t k, int32_t* top_idx, const float* block_scores,
+                               int32_t pool_k, int32_t* cand_blocks, void* workspace, size_t ws_bytes,
+                               hipStream_t stream) {
+    const char* who = "csa2_index_topk_merge_pool";
+    if (nq < 0) return fail(CSA2_EINVAL, "%s: nq < 0", who);
+    if (N < 1 || N > kMaxN) return fail(CSA2_EINVAL, "%s: N must be in [1, 2^31-1]", who);
+    if (k < 1 || k > CSA2_MAX_TOPK) return fail(CSA2_EINVAL, "%s: k must be in [1, %d]", who, CSA2_MAX_TOPK);
+    if (pool_k < 1 || pool_k > CSA2_MAX_TOPK)
+        return fail(CSA2_EINVAL, "%s: pool_k must be in [1, %d]", who, CSA2_MAX_TOPK);
+    if (!csa2::index_topk_fits(nq, N, k)) return fail(CSA2_EINVAL, "%s: N too large for this k", who);
+    if (nq > 0 && (!top_idx || !block_scores || !cand_blocks)) return fail(CSA2_EINVAL, "%s: null pointer", who);
+    const size_t need = csa2_index_topk_pool_workspace_bytes(nq, N, k, pool_k);
+    if (nq > 0 && need > 0 && (!workspace || ws_bytes < need))
+        return fail(CSA2_EWORKSPACE, "%s: workspace needs %zu bytes", who, need);
+    (void)hipGetLastError();
+    csa2::launch_index_topk_merge_pool(N, nq, k, top_idx, block_scores, pool_k, cand_blocks, workspace, stream);
+    return launched(who);
+}
+
 size_t csa2_index_prefill_topk_workspace_bytes(int32_t nq, int64_t N, int32_t k) {
     if (nq <= 0 || N < 1 || N > kMaxN || k < 1 || k > CSA2_MAX_TOPK) return 0;
     if (!csa2::prefill_topk_fits(nq, N, k)) return 0;

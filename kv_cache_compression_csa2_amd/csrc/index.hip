@@ -797,6 +797,29 @@ int launch_index_topk_merge(int64_t N, int32_t nq, int32_t topk, int32_t* out_id
     return 0;
 }
 
+// The hierarchical Full layer's two selections after the scoring launch: the
+// Top-k merge of the chunks' candidates and the pool's Top-pool_k blocks over
+// the block maxima do not depend on each other, so each level of the two runs
+// in one launch (two launches instead of four at 8 x 1M entries).
+static size_t align256(size_t b) { return (b + 255) & ~size_t(255); }
+size_t index_topk_pool_workspace_bytes(int32_t nq, int64_t N, int32_t k, int32_t pool_k) {
+    return align256(index_topk_workspace_bytes(nq, N, k)) + topk_workspace_bytes(nq, (N + 7) / 8, pool_k);
+}
+int launch_index_topk_merge_pool(int64_t N, int32_t nq, int32_t topk, int32_t* out_idx, const float* block_scores,
+                                 int32_t pool_k, int32_t* cand_blocks, void* ws, hipStream_t s) {
+    if (nq == 0) return 0;
+    const FtWs f = ft_ws(ws, nq, N, topk);
+    void* ws_b = ws ? static_cast<void*>(static_cast<uint8_t*>(ws) + align256(index_topk_workspace_bytes(nq, N, topk)))
+                    : nullptr;
+    const int64_t nblk = (N + 7) / 8;
+    if (!launch_topk_merge_select(nq, topk, f.c, f.ck, f.cc, out_idx, f.ck2, f.cc2, block_scores, nq, nblk, pool_k,
+                                  cand_blocks, ws_b, s)) {
+        launch_index_topk_merge(N, nq, topk, out_idx, ws, s);
+        launch_topk(block_scores, nq, nblk, nblk, nullptr, pool_k, nullptr, cand_blocks, ws_b, s);
+    }
+    return 0;
+}
+
 // Reindex scoring fused with the Top-K: the chunk kernel in Reindex mode
 // (256 threads for either key format), then the merge of the chunks'
 // candidates when a row has more than one chunk.

@@ -33,6 +33,12 @@ int launch_index_topk(const uint16_t* q_idx, const float* w, const void* k, bool
                       const int32_t* n_visible, int32_t topk, int32_t* out_idx, float* block_scores,
                       float* scores_dbg, void* ws, hipStream_t s);
 int launch_index_topk_merge(int64_t N, int32_t nq, int32_t topk, int32_t* out_idx, void* ws, hipStream_t s);
+// The merge above and the pool's Top-pool_k blocks over the block maxima
+// (rows of ceil(N / 8)), sharing launches; ws holds the merge's candidates
+// first (as for launch_index_topk), then the block selection's.
+size_t index_topk_pool_workspace_bytes(int32_t nq, int64_t N, int32_t k, int32_t pool_k);
+int launch_index_topk_merge_pool(int64_t N, int32_t nq, int32_t topk, int32_t* out_idx, const float* block_scores,
+                                 int32_t pool_k, int32_t* cand_blocks, void* ws, hipStream_t s);
 // Static device scratch of csa2_index_topk_noalloc: its size, and its address
 // on the current device (nullptr and *err set when the lookup fails).
 size_t index_topk_noalloc_capacity();
@@ -60,6 +66,13 @@ size_t topk_workspace_bytes(int32_t rows, int64_t ncols, int32_t k);
 int32_t topk_merge_groups(int32_t nchunks, int32_t k);
 int launch_topk_merge(int32_t rows, int32_t k, int32_t nchunks, const uint32_t* ck, const int32_t* cc,
                       int32_t* out_idx, uint32_t* ck2, int32_t* cc2, hipStream_t s);
+// That merge together with an independent Top-k_b over rows_b x ncols_b
+// scores (as launch_topk, no row_len or id_map; its chunks' candidates in
+// ws_b), each level of the two in one launch. Returns false, launching
+// nothing, when the second selection needs the global-memory path.
+bool launch_topk_merge_select(int32_t rows_a, int32_t k_a, int32_t nchunks_a, const uint32_t* ck, const int32_t* cc,
+                              int32_t* out_a, uint32_t* ck2, int32_t* cc2, const float* scores_b, int32_t rows_b,
+                              int64_t ncols_b, int32_t k_b, int32_t* out_b, void* ws_b, hipStream_t s);
 int launch_topk(const float* scores, int32_t rows, int64_t ncols, int64_t ld, const int32_t* row_len, int32_t k,
                 const int32_t* id_map, int32_t* out_idx, void* ws, hipStream_t s);
 

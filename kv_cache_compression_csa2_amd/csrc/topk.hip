@@ -346,44 +346,72 @@ CSA2_DEVINL void load_keys_coalesced(const float* src, int n, uint32_t (&key)[KP
     }
 }
 
-// Stage 1 (or the only stage): one NT-thread workgroup per (row, chunk), the
-// chunk's keys in registers.
+// One selection of a register-path launch, as plain values: the kernels below
+// take it by value, and the paired kernel takes two and tells them apart by
+// workgroup index.
+enum : int32_t {
+    kJobChunk = 0,  // Top-k of each (row, chunk) of a float score matrix
+    kJobMerge = 1,  // Top-k of each row's nchunks x k candidates -> final ids
+    kJobGroup = 2,  // Top-k of each group of cpg chunks' candidates -> candidates
+};
+struct TkJob {
+    int32_t mode = kJobChunk;
+    int32_t nblocks = 0;              // workgroups of the job
+    const float* scores = nullptr;    // kJobChunk: rows x ld scores
+    int64_t ncols = 0, ld = 0;
+    const int32_t* row_len = nullptr;
+    int64_t chunk_len = 0;
+    const int32_t* id_map = nullptr;  // final ids are mapped through id_map[row * ld + col]
+    const uint32_t* ck_in = nullptr;  // merges: candidate keys and columns in
+    const int32_t* cc_in = nullptr;
+    int32_t nchunks = 1;              // chunks per row (of the scores, or of the input candidates)
+    int32_t cpg = 1;                  // kJobGroup: input chunks per group
+    int32_t k = 0;
+    int32_t* out_idx = nullptr;       // final ids [rows][k]
+    uint32_t* ck_out = nullptr;       // candidates out (kJobChunk with nchunks > 1, kJobGroup)
+    int32_t* cc_out = nullptr;
+};
+
+// LDS of a register-path workgroup: the selection's state, which first stages
+// half of a chunk's keys when they are loaded coalesced.
 template <int NT, int KPT>
-__global__ __launch_bounds__(NT) void topk_reg_chunk_kernel(
-    const float* __restrict__ scores, int64_t ncols, int64_t ld, const int32_t* __restrict__ row_len, int32_t k,
-    int32_t nchunks, int64_t chunk_len, const int32_t* __restrict__ id_map, int32_t* __restrict__ out_idx,
-    uint32_t* __restrict__ cand_key, int32_t* __restrict__ cand_col) {
-    // the selection's LDS, which first stages half of the chunk's keys
-    constexpr size_t kStageB = (size_t)NT * KPT / 2 * sizeof(uint32_t);
-    __shared__ __attribute__((aligned(16))) uint8_t smem[sizeof(RegTk<NT>) > kStageB ? sizeof(RegTk<NT>) : kStageB];
+constexpr size_t reg_smem_bytes() {
+    constexpr size_t stage = (KPT % 8 == 0) ? (size_t)NT * KPT / 2 * sizeof(uint32_t) : 0;
+    return sizeof(RegTk<NT>) > stage ? sizeof(RegTk<NT>) : stage;
+}
+
+// kJobChunk, workgroup `bid` = (row, chunk): the chunk's keys in registers.
+template <int NT, int KPT>
+CSA2_DEVINL void reg_chunk_body(const TkJob& j, int64_t bid, uint8_t* smem) {
     RegTk<NT>& sh = *reinterpret_cast<RegTk<NT>*>(smem);
     const int tid = threadIdx.x;
-    const int64_t row = blockIdx.x / nchunks;
-    const int64_t chunk = blockIdx.x % nchunks;
-    int64_t len = row_len ? (int64_t)row_len[row] : ncols;
-    len = len < ncols ? len : ncols;
+    const int64_t row = bid / j.nchunks;
+    const int64_t chunk = bid % j.nchunks;
+    int64_t len = j.row_len ? (int64_t)j.row_len[row] : j.ncols;
+    len = len < j.ncols ? len : j.ncols;
     len = len > 0 ? len : 0;
-    const int64_t c0 = chunk * chunk_len;
+    const int64_t c0 = chunk * j.chunk_len;
     int64_t nn = len - c0;
-    nn = nn < chunk_len ? nn : chunk_len;
+    nn = nn < j.chunk_len ? nn : j.chunk_len;
     const int n = nn > 0 ? (int)nn : 0;
+    const int32_t k = j.k;
     uint32_t key[KPT];
     if constexpr (KPT % 8 == 0)
-        load_keys_coalesced<NT, KPT>(scores + row * ld + c0, n, key, reinterpret_cast<uint32_t*>(smem));
+        load_keys_coalesced<NT, KPT>(j.scores + row * j.ld + c0, n, key, reinterpret_cast<uint32_t*>(smem));
     else
-        load_keys<KPT>(scores + row * ld + c0, n, key);
+        load_keys<KPT>(j.scores + row * j.ld + c0, n, key);
     const int p0 = tid * KPT;
     uint32_t emitted;
-    if (nchunks == 1) {
-        int32_t* out = out_idx + row * k;
-        const int32_t* map = id_map ? id_map + row * ld : nullptr;
+    if (j.nchunks == 1) {
+        int32_t* out = j.out_idx + row * k;
+        const int32_t* map = j.id_map ? j.id_map + row * j.ld : nullptr;
         emitted = reg_select_emit<NT, KPT, true>(
             key, (uint32_t)k, sh, [&](int u) { return (int32_t)(c0 + p0 + u); },
             [&](uint32_t slot, uint32_t, int32_t col) { out[slot] = map ? map[col] : col; });
         for (int t = (int)emitted + tid; t < k; t += NT) out[t] = -1;
     } else {
-        uint32_t* ck = cand_key + (row * nchunks + chunk) * k;
-        int32_t* cc = cand_col + (row * nchunks + chunk) * k;
+        uint32_t* ck = j.ck_out + (row * j.nchunks + chunk) * k;
+        int32_t* cc = j.cc_out + (row * j.nchunks + chunk) * k;
         emitted = reg_select_emit<NT, KPT, true>(
             key, (uint32_t)k, sh, [&](int u) { return (int32_t)(c0 + p0 + u); },
             [&](uint32_t slot, uint32_t kv, int32_t col) {
@@ -397,24 +425,12 @@ __global__ __launch_bounds__(NT) void topk_reg_chunk_kernel(
     }
 }
 
-// Stage 2: one workgroup per row over its nchunks * k candidates, which are
-// in column order (chunk by chunk, each chunk's selection ascending; unused
-// slots hold key 0).
-template <int NT, int KPT>
-__global__ __launch_bounds__(NT) void topk_reg_merge_kernel(int64_t ld, int32_t k, int32_t nchunks,
-                                                             const int32_t* __restrict__ id_map,
-                                                             const uint32_t* __restrict__ cand_key,
-                                                             const int32_t* __restrict__ cand_col,
-                                                             int32_t* __restrict__ out_idx) {
-    __shared__ RegTk<NT> sh;
-    const int tid = threadIdx.x;
-    const int64_t row = blockIdx.x;
-    const int n = nchunks * k;
-    const uint32_t* ckr = cand_key + row * (int64_t)n;
-    const int32_t* ccr = cand_col + row * (int64_t)n;
-    const int p0 = tid * KPT;
-    uint32_t key[KPT];
-    int32_t col[KPT];
+// Loads candidates [base, base + n) as this thread's KPT consecutive (key,
+// column) pairs; positions >= n give key 0.
+template <int KPT>
+CSA2_DEVINL void load_cands(const uint32_t* ckr, const int32_t* ccr, int n, uint32_t (&key)[KPT],
+                            int32_t (&col)[KPT]) {
+    const int p0 = threadIdx.x * KPT;
     const bool aligned = ((reinterpret_cast<uintptr_t>(ckr) | reinterpret_cast<uintptr_t>(ccr)) & 15u) == 0;
     if ((KPT % 4) == 0 && aligned && p0 + KPT <= n) {
 #pragma unroll
@@ -437,42 +453,48 @@ __global__ __launch_bounds__(NT) void topk_reg_merge_kernel(int64_t ld, int32_t 
             col[u] = (p0 + u < n) ? ccr[p0 + u] : -1;
         }
     }
-    int32_t* out = out_idx + row * k;
-    const int32_t* map = id_map ? id_map + row * ld : nullptr;
+}
+
+// kJobMerge, workgroup `bid` = row: the row's nchunks * k candidates, which
+// are in column order (chunk by chunk, each chunk's selection ascending;
+// unused slots hold key 0).
+template <int NT, int KPT>
+CSA2_DEVINL void reg_merge_body(const TkJob& j, int64_t bid, uint8_t* smem) {
+    RegTk<NT>& sh = *reinterpret_cast<RegTk<NT>*>(smem);
+    const int tid = threadIdx.x;
+    const int64_t row = bid;
+    const int32_t k = j.k;
+    const int n = j.nchunks * k;
+    uint32_t key[KPT];
+    int32_t col[KPT];
+    load_cands<KPT>(j.ck_in + row * (int64_t)n, j.cc_in + row * (int64_t)n, n, key, col);
+    int32_t* out = j.out_idx + row * k;
+    const int32_t* map = j.id_map ? j.id_map + row * j.ld : nullptr;
     const uint32_t emitted = reg_select_emit<NT, KPT, true>(
         key, (uint32_t)k, sh, [&](int u) { return col[u]; },
         [&](uint32_t slot, uint32_t, int32_t c) { out[slot] = map ? map[c] : c; });
     for (int t = (int)emitted + tid; t < k; t += NT) out[t] = -1;
 }
 
-// One level of a two-level merge: workgroup (row, g) selects the top-k of
-// chunks [g*cpg, min((g+1)*cpg, nchunks)) of the row's nchunks*k candidates
-// and writes them as k candidates of group g (column order kept; unused slots
-// key 0, column -1).
+// kJobGroup, workgroup `bid` = (row, g): the top-k of chunks [g*cpg,
+// min((g+1)*cpg, nchunks)) of the row's candidates, written as k candidates
+// of group g (column order kept; unused slots key 0, column -1).
 template <int NT, int KPT>
-__global__ __launch_bounds__(NT) void topk_reg_group_merge_kernel(int32_t k, int32_t nchunks, int32_t cpg,
-                                                                   const uint32_t* __restrict__ cand_key,
-                                                                   const int32_t* __restrict__ cand_col,
-                                                                   uint32_t* __restrict__ out_key,
-                                                                   int32_t* __restrict__ out_col) {
-    __shared__ RegTk<NT> sh;
+CSA2_DEVINL void reg_group_body(const TkJob& j, int64_t bid, uint8_t* smem) {
+    RegTk<NT>& sh = *reinterpret_cast<RegTk<NT>*>(smem);
     const int tid = threadIdx.x;
-    const int ngroups = (nchunks + cpg - 1) / cpg;
-    const int64_t row = blockIdx.x / ngroups;
-    const int g = blockIdx.x % ngroups;
-    const int c_end = (g + 1) * cpg < nchunks ? (g + 1) * cpg : nchunks;
-    const int n = (c_end - g * cpg) * k;
-    const int64_t base = (row * nchunks + (int64_t)g * cpg) * k;
-    const int p0 = tid * KPT;
+    const int32_t k = j.k;
+    const int ngroups = (j.nchunks + j.cpg - 1) / j.cpg;
+    const int64_t row = bid / ngroups;
+    const int g = (int)(bid % ngroups);
+    const int c_end = (g + 1) * j.cpg < j.nchunks ? (g + 1) * j.cpg : j.nchunks;
+    const int n = (c_end - g * j.cpg) * k;
+    const int64_t base = (row * j.nchunks + (int64_t)g * j.cpg) * k;
     uint32_t key[KPT];
     int32_t col[KPT];
-#pragma unroll
-    for (int u = 0; u < KPT; u++) {
-        key[u] = (p0 + u < n) ? cand_key[base + p0 + u] : 0u;
-        col[u] = (p0 + u < n) ? cand_col[base + p0 + u] : -1;
-    }
-    uint32_t* ok = out_key + (row * ngroups + g) * (int64_t)k;
-    int32_t* oc = out_col + (row * ngroups + g) * (int64_t)k;
+    load_cands<KPT>(j.ck_in + base, j.cc_in + base, n, key, col);
+    uint32_t* ok = j.ck_out + (row * ngroups + g) * (int64_t)k;
+    int32_t* oc = j.cc_out + (row * ngroups + g) * (int64_t)k;
     const uint32_t emitted = reg_select_emit<NT, KPT, true>(
         key, (uint32_t)k, sh, [&](int u) { return col[u]; },
         [&](uint32_t slot, uint32_t kv, int32_t c) {
@@ -483,6 +505,106 @@ __global__ __launch_bounds__(NT) void topk_reg_group_merge_kernel(int32_t k, int
         ok[t] = 0u;
         oc[t] = -1;
     }
+}
+
+template <int NT, int KPT>
+__global__ __launch_bounds__(NT) void topk_reg_chunk_kernel(TkJob j) {
+    __shared__ __attribute__((aligned(16))) uint8_t smem[reg_smem_bytes<NT, KPT>()];
+    reg_chunk_body<NT, KPT>(j, blockIdx.x, smem);
+}
+template <int NT, int KPT>
+__global__ __launch_bounds__(NT) void topk_reg_merge_kernel(TkJob j) {
+    __shared__ __attribute__((aligned(16))) uint8_t smem[sizeof(RegTk<NT>)];
+    reg_merge_body<NT, KPT>(j, blockIdx.x, smem);
+}
+template <int NT, int KPT>
+__global__ __launch_bounds__(NT) void topk_reg_group_merge_kernel(TkJob j) {
+    __shared__ __attribute__((aligned(16))) uint8_t smem[sizeof(RegTk<NT>)];
+    reg_group_body<NT, KPT>(j, blockIdx.x, smem);
+}
+
+// Any job on 1024 threads with one inlined selection: the mode only decides
+// where the keys come from and where the selected ones go, so the select code
+// (the bulk of a kernel's instructions) is not repeated per mode.
+template <int KPT>
+CSA2_DEVINL void reg_any_body(const TkJob& j, int64_t bid, uint8_t* smem) {
+    constexpr int NT = 1024;
+    RegTk<NT>& sh = *reinterpret_cast<RegTk<NT>*>(smem);
+    const int tid = threadIdx.x;
+    const int32_t k = j.k;
+    uint32_t key[KPT];
+    int32_t col[KPT];
+    int32_t* out = nullptr;         // final ids (else candidates to ok / oc)
+    const int32_t* map = nullptr;
+    uint32_t* ok = nullptr;
+    int32_t* oc = nullptr;
+    if (j.mode == kJobChunk) {
+        const int64_t row = bid / j.nchunks, chunk = bid % j.nchunks;
+        int64_t len = j.row_len ? (int64_t)j.row_len[row] : j.ncols;
+        len = len < j.ncols ? len : j.ncols;
+        len = len > 0 ? len : 0;
+        const int64_t c0 = chunk * j.chunk_len;
+        int64_t nn = len - c0;
+        nn = nn < j.chunk_len ? nn : j.chunk_len;
+        const int n = nn > 0 ? (int)nn : 0;
+        if constexpr (KPT % 8 == 0)
+            load_keys_coalesced<NT, KPT>(j.scores + row * j.ld + c0, n, key, reinterpret_cast<uint32_t*>(smem));
+        else
+            load_keys<KPT>(j.scores + row * j.ld + c0, n, key);
+#pragma unroll
+        for (int u = 0; u < KPT; u++) col[u] = (int32_t)(c0 + tid * KPT + u);
+        if (j.nchunks == 1) {
+            out = j.out_idx + row * k;
+            map = j.id_map ? j.id_map + row * j.ld : nullptr;
+        } else {
+            ok = j.ck_out + (row * j.nchunks + chunk) * k;
+            oc = j.cc_out + (row * j.nchunks + chunk) * k;
+        }
+    } else if (j.mode == kJobMerge) {
+        const int n = j.nchunks * k;
+        load_cands<KPT>(j.ck_in + bid * (int64_t)n, j.cc_in + bid * (int64_t)n, n, key, col);
+        out = j.out_idx + bid * k;
+        map = j.id_map ? j.id_map + bid * j.ld : nullptr;
+    } else {
+        const int ngroups = (j.nchunks + j.cpg - 1) / j.cpg;
+        const int64_t row = bid / ngroups;
+        const int g = (int)(bid % ngroups);
+        const int c_end = (g + 1) * j.cpg < j.nchunks ? (g + 1) * j.cpg : j.nchunks;
+        const int64_t base = (row * j.nchunks + (int64_t)g * j.cpg) * k;
+        load_cands<KPT>(j.ck_in + base, j.cc_in + base, (c_end - g * j.cpg) * k, key, col);
+        ok = j.ck_out + (row * ngroups + g) * (int64_t)k;
+        oc = j.cc_out + (row * ngroups + g) * (int64_t)k;
+    }
+    const uint32_t emitted = reg_select_emit<NT, KPT, true>(
+        key, (uint32_t)k, sh, [&](int u) { return col[u]; },
+        [&](uint32_t slot, uint32_t kv, int32_t c) {
+            if (out) {
+                out[slot] = map ? map[c] : c;
+            } else {
+                ok[slot] = kv;
+                oc[slot] = c;
+            }
+        });
+    for (int t = (int)emitted + tid; t < k; t += NT) {
+        if (out) {
+            out[t] = -1;
+        } else {
+            ok[t] = 0u;
+            oc[t] = -1;
+        }
+    }
+}
+
+// Two independent selections in one launch of 1024-thread workgroups:
+// workgroups [0, a.nblocks) run job a, the rest job b (each with up to KPT
+// keys per thread). Small selections cost little more than a launch, so two
+// that do not depend on each other share one.
+template <int KPT>
+__global__ __launch_bounds__(1024) void topk_pair_kernel(TkJob a, TkJob b) {
+    __shared__ __attribute__((aligned(16))) uint8_t smem[reg_smem_bytes<1024, KPT>()];
+    const bool first = (int)blockIdx.x < a.nblocks;
+    const TkJob j = first ? a : b;
+    reg_any_body<KPT>(j, first ? (int64_t)blockIdx.x : (int64_t)blockIdx.x - a.nblocks, smem);
 }
 
 // Chunks per row on the register path; 0 = the shape needs the global-memory path.
@@ -516,18 +638,110 @@ RegShape reg_shape(int64_t n) {
     return {1024, kpt};
 }
 
-template <int NT, int KPT>
-void launch_reg_chunk(dim3 grid, hipStream_t s, const float* scores, int64_t ncols, int64_t ld, const int32_t* row_len,
-                      int32_t k, int32_t c, int64_t chunk_len, const int32_t* id_map, int32_t* out_idx, uint32_t* ck,
-                      int32_t* cc) {
-    hipLaunchKernelGGL((topk_reg_chunk_kernel<NT, KPT>), grid, dim3(NT), 0, s, scores, ncols, ld, row_len, k, c,
-                       chunk_len, id_map, out_idx, ck, cc);
+// Threads and keys per thread of a job: from its segment size (the chunk
+// length, nchunks * k merged candidates, or cpg * k grouped ones), as each
+// kernel below is instantiated.
+RegShape job_shape(const TkJob& j) {
+    if (j.mode == kJobChunk) {
+        // 512 threads x 32 keys: measured 23% faster than 1024 x 16 for 4096
+        // rows x 65536 scores (two workgroups of 8 waves per CU); with fewer
+        // workgroups than CUs, 1024 x 16 is faster (8 rows x 131072 block
+        // scores, k = 2048: 26.5 against 28.6 us)
+        if (j.chunk_len > 8192 && j.chunk_len <= 16384 && j.nblocks >= 256) return {512, 32};
+        RegShape a = reg_shape(j.chunk_len);
+        if (a.nt == 1024) a.kpt = a.kpt < 4 ? 4 : a.kpt > 32 ? 32 : a.kpt;
+        return a;
+    }
+    if (j.mode == kJobMerge) {
+        RegShape m = reg_shape((int64_t)j.nchunks * j.k);
+        if (m.nt == 1024) m.kpt = m.kpt < 4 ? 4 : m.kpt > 16 ? 16 : m.kpt;
+        return m;
+    }
+    const RegShape m = reg_shape((int64_t)j.cpg * j.k);
+    if (m.nt == 256) return {256, 8};
+    return {1024, m.kpt <= 8 ? 8 : 16};
 }
 
-template <int NT, int KPT>
-void launch_reg_merge(dim3 grid, hipStream_t s, int64_t ld, int32_t k, int32_t c, const int32_t* id_map,
-                      const uint32_t* ck, const int32_t* cc, int32_t* out_idx) {
-    hipLaunchKernelGGL((topk_reg_merge_kernel<NT, KPT>), grid, dim3(NT), 0, s, ld, k, c, id_map, ck, cc, out_idx);
+void launch_chunk_job(const TkJob& j, RegShape a, hipStream_t s) {
+    const dim3 g((unsigned)j.nblocks);
+#define CSA2_CHUNK(NT, KPT) hipLaunchKernelGGL((topk_reg_chunk_kernel<NT, KPT>), g, dim3(NT), 0, s, j)
+    if (a.nt == 512) {
+        CSA2_CHUNK(512, 32);
+    } else if (a.nt == 256) {
+        switch (a.kpt) {
+            case 1: CSA2_CHUNK(256, 1); break;
+            case 2: CSA2_CHUNK(256, 2); break;
+            case 4: CSA2_CHUNK(256, 4); break;
+            default: CSA2_CHUNK(256, 8); break;
+        }
+    } else {
+        switch (a.kpt) {
+            case 4: CSA2_CHUNK(1024, 4); break;
+            case 8: CSA2_CHUNK(1024, 8); break;
+            case 16: CSA2_CHUNK(1024, 16); break;
+            default: CSA2_CHUNK(1024, 32); break;
+        }
+    }
+#undef CSA2_CHUNK
+}
+
+void launch_merge_job(const TkJob& j, RegShape m, hipStream_t s) {
+    const dim3 g((unsigned)j.nblocks);
+#define CSA2_MERGE(NT, KPT) hipLaunchKernelGGL((topk_reg_merge_kernel<NT, KPT>), g, dim3(NT), 0, s, j)
+    if (m.nt == 256) {
+        switch (m.kpt) {
+            case 1: CSA2_MERGE(256, 1); break;
+            case 2: CSA2_MERGE(256, 2); break;
+            case 4: CSA2_MERGE(256, 4); break;
+            default: CSA2_MERGE(256, 8); break;
+        }
+    } else {
+        switch (m.kpt) {
+            case 4: CSA2_MERGE(1024, 4); break;
+            case 8: CSA2_MERGE(1024, 8); break;
+            default: CSA2_MERGE(1024, 16); break;
+        }
+    }
+#undef CSA2_MERGE
+}
+
+void launch_group_job(const TkJob& j, RegShape m, hipStream_t s) {
+    const dim3 g((unsigned)j.nblocks);
+    if (m.nt == 256)
+        hipLaunchKernelGGL((topk_reg_group_merge_kernel<256, 8>), g, dim3(256), 0, s, j);
+    else if (m.kpt == 8)
+        hipLaunchKernelGGL((topk_reg_group_merge_kernel<1024, 8>), g, dim3(1024), 0, s, j);
+    else
+        hipLaunchKernelGGL((topk_reg_group_merge_kernel<1024, 16>), g, dim3(1024), 0, s, j);
+}
+
+void launch_job(const TkJob& j, hipStream_t s) {
+    if (j.nblocks == 0) return;
+    const RegShape sh = job_shape(j);
+    switch (j.mode) {
+        case kJobChunk: launch_chunk_job(j, sh, s); break;
+        case kJobMerge: launch_merge_job(j, sh, s); break;
+        default: launch_group_job(j, sh, s); break;
+    }
+}
+
+// Two independent jobs: one launch when both take the same 1024-thread shape
+// (run with another shape, a selection measured up to 3.6 times slower: a
+// 2048-candidate group merge took 22 us at 1024 x 16 against 6 us at
+// 256 x 8), else one launch each.
+void launch_pair(const TkJob& a, const TkJob& b, hipStream_t s) {
+    const RegShape sa = job_shape(a), sb = job_shape(b);
+    if (a.nblocks == 0 || b.nblocks == 0 || sa.nt != 1024 || sb.nt != 1024 || sa.kpt != sb.kpt || sa.kpt > 16) {
+        launch_job(a, s);
+        launch_job(b, s);
+        return;
+    }
+    const dim3 g((unsigned)(a.nblocks + b.nblocks));
+    switch (sa.kpt) {
+        case 4: hipLaunchKernelGGL(topk_pair_kernel<4>, g, dim3(1024), 0, s, a, b); break;
+        case 8: hipLaunchKernelGGL(topk_pair_kernel<8>, g, dim3(1024), 0, s, a, b); break;
+        default: hipLaunchKernelGGL(topk_pair_kernel<16>, g, dim3(1024), 0, s, a, b); break;
+    }
 }
 
 int32_t topk_chunks(int32_t rows, int64_t ncols, int32_t k) {
@@ -538,29 +752,26 @@ int32_t topk_chunks(int32_t rows, int64_t ncols, int32_t k) {
     return (int32_t)c;
 }
 
-// Launches the final merge of rows x c x k candidates (the register merge
-// kernel sized for c * k <= kRegMaxCand).
-void launch_reg_merge_any(int32_t rows, int32_t k, int32_t c, const int32_t* id_map, int64_t ld, const uint32_t* ck,
-                          const int32_t* cc, int32_t* out_idx, hipStream_t s) {
-    const dim3 g2((unsigned)rows);
-    const RegShape m = reg_shape((int64_t)c * k);
-#define CSA2_MERGE(NT, KPT) launch_reg_merge<NT, KPT>(g2, s, ld, k, c, id_map, ck, cc, out_idx)
-    if (m.nt == 256) {
-        switch (m.kpt) {
-            case 1: CSA2_MERGE(256, 1); break;
-            case 2: CSA2_MERGE(256, 2); break;
-            case 4: CSA2_MERGE(256, 4); break;
-            default: CSA2_MERGE(256, 8); break;
-        }
-    } else {
-        switch (m.kpt) {
-            case 1: case 2: case 4: CSA2_MERGE(1024, 4); break;
-            case 8: CSA2_MERGE(1024, 8); break;
-            default: CSA2_MERGE(1024, 16); break;
-        }
-    }
-#undef CSA2_MERGE
+TkJob merge_job(int32_t rows, int32_t k, int32_t c, const int32_t* id_map, int64_t ld, const uint32_t* ck,
+                const int32_t* cc, int32_t* out_idx) {
+    TkJob j;
+    j.mode = kJobMerge;
+    j.nblocks = rows;
+    j.k = k;
+    j.nchunks = c;
+    j.id_map = id_map;
+    j.ld = ld;
+    j.ck_in = ck;
+    j.cc_in = cc;
+    j.out_idx = out_idx;
+    return j;
 }
+
+// The launches of one register-path selection: one or two levels of jobs.
+struct TkPlan {
+    int n = 0;
+    TkJob lv[2];
+};
 
 }  // namespace
 
@@ -582,28 +793,97 @@ int32_t topk_merge_groups(int32_t nchunks, int32_t k) {
     return (nchunks + cpg - 1) / cpg;
 }
 
-int launch_topk_merge(int32_t rows, int32_t k, int32_t nchunks, const uint32_t* ck, const int32_t* cc,
-                      int32_t* out_idx, uint32_t* ck2, int32_t* cc2, hipStream_t s) {
-    if (rows == 0) return 0;
+// The merge of rows x nchunks x k candidates (nothing when nchunks <= 1).
+static TkPlan plan_merge(int32_t rows, int32_t k, int32_t nchunks, const uint32_t* ck, const int32_t* cc,
+                         int32_t* out_idx, uint32_t* ck2, int32_t* cc2) {
+    TkPlan p;
+    if (rows == 0 || nchunks <= 1) return p;
     const int32_t ng = topk_merge_groups(nchunks, k);
     if (ng == 1) {
-        launch_reg_merge_any(rows, k, nchunks, nullptr, 0, ck, cc, out_idx, s);
-        return 0;
+        p.lv[p.n++] = merge_job(rows, k, nchunks, nullptr, 0, ck, cc, out_idx);
+        return p;
     }
-    const int32_t cpg = merge_chunks_per_group(nchunks, k);
-    const RegShape m = reg_shape((int64_t)cpg * k);
-    const dim3 g1((unsigned)((int64_t)rows * ng));
-    if (m.nt == 256)
-        hipLaunchKernelGGL((topk_reg_group_merge_kernel<256, 8>), g1, dim3(256), 0, s, k, nchunks, cpg, ck, cc, ck2,
-                           cc2);
-    else if (m.kpt <= 8)
-        hipLaunchKernelGGL((topk_reg_group_merge_kernel<1024, 8>), g1, dim3(1024), 0, s, k, nchunks, cpg, ck, cc, ck2,
-                           cc2);
-    else
-        hipLaunchKernelGGL((topk_reg_group_merge_kernel<1024, 16>), g1, dim3(1024), 0, s, k, nchunks, cpg, ck, cc,
-                           ck2, cc2);
-    launch_reg_merge_any(rows, k, ng, nullptr, 0, ck2, cc2, out_idx, s);
+    TkJob g;
+    g.mode = kJobGroup;
+    g.nblocks = rows * ng;
+    g.k = k;
+    g.nchunks = nchunks;
+    g.cpg = merge_chunks_per_group(nchunks, k);
+    g.ck_in = ck;
+    g.cc_in = cc;
+    g.ck_out = ck2;
+    g.cc_out = cc2;
+    p.lv[p.n++] = g;
+    p.lv[p.n++] = merge_job(rows, k, ng, nullptr, 0, ck2, cc2, out_idx);
+    return p;
+}
+
+// Top-k over rows x ncols scores on the register path (n = 0: the shape needs
+// the global-memory path). ws holds the chunks' candidates.
+// c_force > 0 takes that many chunks instead of topk_reg_chunks' count (the
+// caller checks the merge capacity and the workspace).
+static TkPlan plan_select(const float* scores, int32_t rows, int64_t ncols, int64_t ld, const int32_t* row_len,
+                          int32_t k, const int32_t* id_map, int32_t* out_idx, void* ws, int32_t c_force = 0) {
+    TkPlan p;
+    const int32_t c = c_force > 0 ? c_force : topk_reg_chunks(rows, ncols, k);
+    if (c == 0 || rows == 0) return p;
+    TkJob j;
+    j.mode = kJobChunk;
+    j.nblocks = rows * c;
+    j.scores = scores;
+    j.ncols = ncols;
+    j.ld = ld;
+    j.row_len = row_len;
+    j.chunk_len = (ncols + c - 1) / c;
+    j.id_map = id_map;
+    j.nchunks = c;
+    j.k = k;
+    j.out_idx = out_idx;
+    if (c > 1) {
+        j.ck_out = reinterpret_cast<uint32_t*>(ws);
+        j.cc_out = reinterpret_cast<int32_t*>(j.ck_out + (size_t)rows * c * k);
+    }
+    p.lv[p.n++] = j;
+    if (c > 1) p.lv[p.n++] = merge_job(rows, k, c, id_map, ld, j.ck_out, j.cc_out, out_idx);
+    return p;
+}
+
+int launch_topk_merge(int32_t rows, int32_t k, int32_t nchunks, const uint32_t* ck, const int32_t* cc,
+                      int32_t* out_idx, uint32_t* ck2, int32_t* cc2, hipStream_t s) {
+    const TkPlan p = plan_merge(rows, k, nchunks, ck, cc, out_idx, ck2, cc2);
+    for (int i = 0; i < p.n; i++) launch_job(p.lv[i], s);
     return 0;
+}
+
+bool launch_topk_merge_select(int32_t rows_a, int32_t k_a, int32_t nchunks_a, const uint32_t* ck, const int32_t* cc,
+                              int32_t* out_a, uint32_t* ck2, int32_t* cc2, const float* scores_b, int32_t rows_b,
+                              int64_t ncols_b, int32_t k_b, int32_t* out_b, void* ws_b, hipStream_t s) {
+    TkPlan b = plan_select(scores_b, rows_b, ncols_b, ncols_b, nullptr, k_b, nullptr, out_b, ws_b);
+    if (rows_b > 0 && b.n == 0) return false;
+    const TkPlan a = plan_merge(rows_a, k_a, nchunks_a, ck, cc, out_a, ck2, cc2);
+    if (a.n > 0 && b.n > 0) {
+        // Fewer, longer chunks of the second selection where that gives its
+        // first level the shape of the merge's first level, so the two share
+        // a launch (32 x 32768 block maxima, k = 2048: 2 chunks of 16384 beside
+        // a 16384-candidate merge). Fewer chunks need no more workspace.
+        const RegShape sa = job_shape(a.lv[0]), sb = job_shape(b.lv[0]);
+        const int64_t len = (int64_t)1024 * sa.kpt;
+        const int32_t c = (int32_t)((ncols_b + len - 1) / len);
+        if (sa.nt == 1024 && (sa.nt != sb.nt || sa.kpt != sb.kpt) && c < b.lv[0].nchunks &&
+            (c == 1 || (int64_t)c * k_b <= kRegMaxCand)) {
+            const TkPlan b2 = plan_select(scores_b, rows_b, ncols_b, ncols_b, nullptr, k_b, nullptr, out_b, ws_b, c);
+            const RegShape s2 = job_shape(b2.lv[0]);
+            if (s2.nt == sa.nt && s2.kpt == sa.kpt) b = b2;
+        }
+    }
+    const int levels = a.n > b.n ? a.n : b.n;
+    for (int i = 0; i < levels; i++) {
+        if (i < a.n && i < b.n)
+            launch_pair(a.lv[i], b.lv[i], s);
+        else
+            launch_job(i < a.n ? a.lv[i] : b.lv[i], s);
+    }
+    return true;
 }
 
 size_t topk_workspace_bytes(int32_t rows, int64_t ncols, int32_t k) {
@@ -616,43 +896,18 @@ size_t topk_workspace_bytes(int32_t rows, int64_t ncols, int32_t k) {
 int launch_topk(const float* scores, int32_t rows, int64_t ncols, int64_t ld, const int32_t* row_len, int32_t k,
                 const int32_t* id_map, int32_t* out_idx, void* ws, hipStream_t s) {
     if (rows == 0) return 0;
-    const int32_t cl = topk_reg_chunks(rows, ncols, k);
-    const int32_t c = cl ? cl : topk_chunks(rows, ncols, k);
+    const TkPlan p = plan_select(scores, rows, ncols, ld, row_len, k, id_map, out_idx, ws);
+    if (p.n > 0) {
+        for (int i = 0; i < p.n; i++) launch_job(p.lv[i], s);
+        return 0;
+    }
+    const int32_t c = topk_chunks(rows, ncols, k);
     const int64_t chunk_len = (ncols + c - 1) / c;
     uint32_t* ck = nullptr;
     int32_t* cc = nullptr;
     if (c > 1) {
         ck = reinterpret_cast<uint32_t*>(ws);
         cc = reinterpret_cast<int32_t*>(ck + (size_t)rows * c * k);
-    }
-    if (cl) {
-        const dim3 g1((unsigned)((int64_t)rows * c));
-        const RegShape a = reg_shape(chunk_len);
-#define CSA2_CHUNK(NT, KPT) launch_reg_chunk<NT, KPT>(g1, s, scores, ncols, ld, row_len, k, c, chunk_len, id_map, out_idx, ck, cc)
-        if (chunk_len > 8192 && chunk_len <= 16384 && (int64_t)rows * c >= 256) {
-            // 512 threads x 32 keys: measured 23% faster than 1024 x 16 for
-            // 4096 rows x 65536 scores (two workgroups of 8 waves per CU);
-            // with fewer workgroups than CUs, 1024 x 16 is faster (8 rows x
-            // 131072 block scores, k = 2048: 26.5 against 28.6 us)
-            CSA2_CHUNK(512, 32);
-        } else if (a.nt == 256) {
-            switch (a.kpt) {
-                case 1: CSA2_CHUNK(256, 1); break;
-                case 2: CSA2_CHUNK(256, 2); break;
-                case 4: CSA2_CHUNK(256, 4); break;
-                default: CSA2_CHUNK(256, 8); break;
-            }
-        } else {
-            switch (a.kpt) {
-                case 1: case 2: case 4: CSA2_CHUNK(1024, 4); break;
-                case 8: CSA2_CHUNK(1024, 8); break;
-                case 16: CSA2_CHUNK(1024, 16); break;
-                default: CSA2_CHUNK(1024, 32); break;
-            }
-        }
-#undef CSA2_CHUNK
-        if (c > 1) launch_reg_merge_any(rows, k, c, id_map, ld, ck, cc, out_idx, s);
-        return 0;
     }
     hipLaunchKernelGGL(topk_chunk_kernel, dim3((unsigned)((int64_t)rows * c)), dim3(kTkThreads), 0, s, scores, ncols,
                        ld, row_len, k, c, chunk_len, id_map, out_idx, ck, cc);

@@ -10,7 +10,9 @@ Every layer attends with its own Q and its own window KV.
 
 Decode workloads (one query per sequence) run the Full layer's scoring and
 Top-512 fused (csa2_index_topk: no score row is written; its two launches are
-timed separately); so does the prefill chunk (csa2_index_prefill_topk, one
+timed separately; the hierarchical layer completes the Top-512 and selects
+its 2048-block pool together, csa2_index_topk_merge_pool); so does the
+prefill chunk (csa2_index_prefill_topk, one
 launch when each row is one chunk). Reindex layers score the pool and select in one call
 (csa2_index_reindex_topk); `fused_reindex = False` switches them to
 csa2_index_reindex + csa2_topk. `debug_scores` makes the fused calls also
@@ -49,7 +51,11 @@ class Step:
                               L.csa2_topk_workspace_bytes(nq, pool, TOPK) if wl.hier else 0))
         self.ws_attn = ws(L.csa2_sparse_attn_workspace_bytes(nq, TOPK))
         self.fused = wl.q_per_seq == 1
-        self.ws_ft = ws(L.csa2_index_topk_workspace_bytes(nq, N, TOPK)) if self.fused else None
+        self.ws_ft = None
+        if self.fused:
+            # the hierarchical layer's pool selection runs beside the merge (csa2_index_topk_merge_pool)
+            self.ws_ft = ws(L.csa2_index_topk_pool_workspace_bytes(nq, N, TOPK, POOL_BLOCKS) if wl.hier
+                            else L.csa2_index_topk_workspace_bytes(nq, N, TOPK))
         # prefill chunk: scoring fused with the Top-512 (8 queries of a sequence per workgroup)
         self.prefill_fused = not self.fused and wl.q_per_seq % 8 == 0 and not wl.hier
         self.ws_pf = ws(L.csa2_index_prefill_topk_workspace_bytes(nq, N, TOPK)) if self.prefill_fused else None
@@ -91,19 +97,19 @@ class Step:
                                   top=self.top[0], scores=self.scores if self.debug_scores else None,
                                   workspace=self.ws_pf, k_fp4=kf)
 
-    def topk_blocks(self):
-        L.csa2_topk(self.blocks, POOL_BLOCKS, out=self.cand, workspace=self.ws_topk)
-
     def full_layer(self, k, sp):
         """The Full layer's scoring and Top-512 (+ the 2048-block pool)."""
         if self.fused:
             with sp("index_topk"):
                 self.index_topk(k, "select")
-            with sp("topk_merge"):
-                self.index_topk(k, "merge")
             if self.wl.hier:
-                with sp("topk_blocks"):
-                    self.topk_blocks()
+                # Top-512 merge and the 2048-block pool, sharing launches
+                with sp("topk_merge+pool"):
+                    L.csa2_index_topk_merge_pool(self.wl.N, TOPK, self.top[0], self.blocks, POOL_BLOCKS,
+                                                 cand_blocks=self.cand, workspace=self.ws_ft)
+            else:
+                with sp("topk_merge"):
+                    self.index_topk(k, "merge")
         elif self.prefill_fused:
             with sp("index_topk"):
                 self.index_prefill_topk(k)

@@ -155,6 +155,39 @@ def test_index_topk_rejects(kw, frag, code):
 @pytest.mark.parametrize("kw,frag,code", [
     (dict(k=0), "k must be", L.CSA2_EINVAL),
     (dict(k=4097), "k must be", L.CSA2_EINVAL),
+    (dict(pool_k=0), "pool_k must be", L.CSA2_EINVAL),
+    (dict(pool_k=4097), "pool_k must be", L.CSA2_EINVAL),
+    (dict(N=0), "N must be", L.CSA2_EINVAL),
+    (dict(nq=-1), "nq < 0", L.CSA2_EINVAL),
+    (dict(N=5_000_000), "too large", L.CSA2_EINVAL),
+    (dict(top=None), "null pointer", L.CSA2_EINVAL),
+    (dict(block=None), "null pointer", L.CSA2_EINVAL),
+    (dict(cand=None), "null pointer", L.CSA2_EINVAL),
+    (dict(ws=None), "workspace", L.CSA2_EWORKSPACE),
+    (dict(wsb=8), "workspace", L.CSA2_EWORKSPACE),
+])
+def test_index_topk_merge_pool_rejects(kw, frag, code):
+    a = dict(N=1 << 20, nq=8, k=512, pool_k=2048, top=P, block=P, cand=P, ws=P, wsb=1 << 40)
+    a.update(kw)
+    rc, msg = _err(K.load().csa2_index_topk_merge_pool(a["N"], a["nq"], a["k"], a["top"], a["block"], a["pool_k"],
+                                                       a["cand"], a["ws"], a["wsb"], S))
+    assert rc == code and frag in msg and msg.startswith("csa2_index_topk_merge_pool"), msg
+
+
+def test_index_topk_pool_workspace_covers_both_selections():
+    L_ = K.load()
+    for nq, N, k, pk in [(8, 1 << 20, 512, 2048), (32, 262144, 512, 2048), (3, 20000, 100, 3000), (2, 4096, 512, 2048)]:
+        a = L_.csa2_index_topk_workspace_bytes(nq, N, k)
+        b = L_.csa2_topk_workspace_bytes(nq, (N + 7) // 8, pk)
+        got = L_.csa2_index_topk_pool_workspace_bytes(nq, N, k, pk)
+        assert got == ((a + 255) // 256) * 256 + b, (nq, N, k, pk, got, a, b)
+    assert L_.csa2_index_topk_pool_workspace_bytes(8, 1 << 20, 512, 0) == 0
+    assert L_.csa2_index_topk_pool_workspace_bytes(8, 5_000_000, 512, 2048) == 0
+
+
+@pytest.mark.parametrize("kw,frag,code", [
+    (dict(k=0), "k must be", L.CSA2_EINVAL),
+    (dict(k=4097), "k must be", L.CSA2_EINVAL),
     (dict(N=0), "N must be", L.CSA2_EINVAL),
     (dict(nb=0), "nb must be", L.CSA2_EINVAL),
     (dict(nb=65537), "nb must be", L.CSA2_EINVAL),

@@ -275,6 +275,64 @@ def test_index_topk_matches_oracle_and_the_unfused_path():
         assert len(a & b) >= 0.995 * len(b)
 
 
+def _merge_pool(q, w, kb, kf, N, k, pool_k, nvd):
+    """select (block maxima on) + csa2_index_topk_merge_pool, one workspace."""
+    nq = q.shape[0]
+    ws = torch.empty((max(K().csa2_index_topk_pool_workspace_bytes(nq, N, k, pool_k), 1),), dtype=torch.uint8,
+                     device=DEV)
+    top = torch.empty((nq, k), dtype=torch.int32, device=DEV)
+    blk = torch.empty((nq, (N + 7) // 8), dtype=torch.float32, device=DEV)
+    K().csa2_index_topk(q, w, kb, N, k, n_visible=nvd, block_size=8, top=top, block_scores=blk, workspace=ws,
+                        k_fp4=kf, stage="select")
+    _, cand = K().csa2_index_topk_merge_pool(N, k, top, blk, pool_k, workspace=ws)
+    return top, blk, cand
+
+
+@pytest.mark.parametrize("nq,N,k,pool_k,fp4", [(3, 20000, 512, 2048, False), (2, 70000, 512, 2048, False),
+                                               (4, 1000, 512, 200, False), (2, 70000, 2048, 512, True),
+                                               (3, 40000, 100, 3000, False)])
+def test_index_topk_merge_pool_bit_exact_on_exact_scores(nq, N, k, pool_k, fp4):
+    """The Top-k merge and the pool's block selection sharing launches give
+    exactly the oracle's Top-k of the oracle's score row and its Top-pool_k of
+    the oracle's block maxima (ties included; one chunk, two-level merges,
+    pools wider than the block row)."""
+    print("case: index_topk_merge_pool exact", nq, N, k, pool_k, fp4, flush=True)
+    q, w, kb = _int_idx_inputs(nq, N, 900 + N + k)
+    nv = np.array([N, N // 3, 0, 7][:nq], np.int32)
+    kf_host = O.kidx_fp4_pack(u16(kb)).reshape(nq, N, 68) if fp4 else None
+    top, blk, cand = _merge_pool(q, w, None if fp4 else kb, torch.tensor(kf_host, device=DEV) if fp4 else None, N, k,
+                                 pool_k, dev_i32(nv, DEV))
+    torch.cuda.synchronize()
+    rs, rb = O.index_full(u16(q), np_(w), None if fp4 else u16(kb), N, 1, n_visible=nv, block_size=8, k_fp4=kf_host)
+    assert np.array_equal(np_(blk), rb)
+    assert np.array_equal(np_(top), O.topk(rs, k, row_len=nv))
+    assert np.array_equal(np_(cand), O.topk(rb, pool_k))
+
+
+@pytest.mark.parametrize("nq,N,pool_k", [(8, 1 << 20, 2048), (32, 262144, 2048), (1, 1 << 21, 4096),
+                                         (2, 4096, 2048)])
+def test_index_topk_merge_pool_matches_the_separate_calls(nq, N, pool_k):
+    """At the decode shapes (8 x 1M: both selections two levels; 32 x 256K:
+    one merge level against two block levels), a pool that needs the
+    global-memory Top-K (1 x 2M, 4096 blocks: the calls run apart) and a row
+    of one chunk: the same ids as csa2_index_topk + csa2_topk of its block
+    maxima."""
+    print("case: index_topk_merge_pool vs separate", nq, N, pool_k, flush=True)
+    k = 512
+    q, w, kb = _idx_inputs(nq, N, nq, 950 + nq)
+    nv = np.full(nq, N, np.int32)
+    nv[-1] = N - 12345 if N > 20000 else N
+    nvd = dev_i32(nv, DEV)
+    top, blk, cand = _merge_pool(q, w, kb, None, N, k, pool_k, nvd)
+    t_ref, b_ref = K().csa2_index_topk(q, w, kb, N, k, n_visible=nvd, block_size=8)
+    c_ref = K().csa2_topk(b_ref, pool_k)
+    torch.cuda.synchronize()
+    assert torch.equal(blk, b_ref)
+    assert torch.equal(top, t_ref)
+    assert torch.equal(cand, c_ref)
+    del kb
+
+
 # ------------------------------------------------------------------ indexer
 
 def _idx_inputs(nq, N, nseq, seed):
