@@ -455,23 +455,26 @@ __global__ __launch_bounds__(256, 2) void index_prefill_kernel(
     // 64 x 256 B tile. FP4 K: thread (entry tid/4, quarter tid%4) takes 16 code
     // bytes (32 channels, one scale block) and that block's scale.
     using Pre = PfPre<kFp4>;
+    // The tile's first entry is uniform: a scalar base plus 32-bit lane offsets,
+    // and rows past the sequence re-read its last entry (their scores are
+    // never kept).
     auto gload = [&](int st) {
         Pre p;
+        const int64_t t0 = e_begin + (int64_t)st * kPfSub;
+        const int lim = (int)(N - 1 - t0 < kPfSub - 1 ? N - 1 - t0 : kPfSub - 1);
         if constexpr (kFp4) {
             const int row = tid >> 2, qq = tid & 3;
-            int64_t e = e_begin + (int64_t)st * kPfSub + row;
-            e = e < N ? e : 0;
-            const uint32_t* src = reinterpret_cast<const uint32_t*>(kfseq + e * kKRec) + 4 * qq;
+            const uint8_t* e = kfseq + t0 * kKRec + (uint32_t)((row < lim ? row : lim) * kKRec);
+            const uint32_t* src = reinterpret_cast<const uint32_t*>(e) + 4 * qq;
             p.v = make_uint4(src[0], src[1], src[2], src[3]);
-            p.x = __uint_as_float((uint32_t)kfseq[e * kKRec + kIdxDim / 2 + qq] << 23);
+            p.x = __uint_as_float((uint32_t)e[kIdxDim / 2 + qq] << 23);
         } else {
+            const uint4* tb = reinterpret_cast<const uint4*>(kseq + t0 * kIdxDim);
 #pragma unroll
             for (int i = 0; i < 4; i++) {
                 const int u = i * 256 + tid;  // 16-byte unit within the 64 x 256 B tile
                 const int row = u >> 4, c16 = u & 15;
-                int64_t e = e_begin + (int64_t)st * kPfSub + row;
-                e = e < N ? e : 0;
-                p.v[i] = reinterpret_cast<const uint4*>(kseq + e * kIdxDim)[c16];
+                p.v[i] = tb[(uint32_t)((row < lim ? row : lim) * 16 + c16)];
             }
         }
         return p;
@@ -496,8 +499,10 @@ __global__ __launch_bounds__(256, 2) void index_prefill_kernel(
     // half-wave: each lane sums its 16 heads of each query, and one half-wave
     // swap hands lanes 0..31 both halves of query a and lanes 32..63 both
     // halves of query b.
-    const int64_t nv_mine = half ? nvb : nva;
-    auto head_sums = [&](const f32x16& acca, const f32x16& accb, int64_t col) {
+    // entry positions fit 32 bits (N < 2^31)
+    const int32_t nv_mine = (int32_t)(half ? nvb : nva);
+    const int32_t n32 = (int32_t)N;
+    auto head_sums = [&](const f32x16& acca, const f32x16& accb, int32_t col) {
         float sa = 0.0f, sb = 0.0f;
 #pragma unroll
         for (int r = 0; r < 16; r++) {
@@ -509,6 +514,8 @@ __global__ __launch_bounds__(256, 2) void index_prefill_kernel(
         return col < nv_mine ? s : -INFINITY;
     };
     const int64_t q_mine = half ? qb : qa;
+    float* srow = scores ? scores + q_mine * N : nullptr;  // this half-wave's score row
+    float* brow = kBlk ? block_scores + q_mine * nblk : nullptr;
     // kSel state of the wave's two queries (wave-uniform): buffered candidates
     // and the score an entry must beat, as a float (-inf: any valid score).
     // key(s) > key(t) <=> s > t for every score s (NaN and -inf never pass),
@@ -517,9 +524,9 @@ __global__ __launch_bounds__(256, 2) void index_prefill_kernel(
     uint32_t na = 0, nb = 0;
     float ta = -INFINITY, tb = -INFINITY;
     const int slot_a = 2 * wave, slot_b = 2 * wave + 1;
-    auto store = [&](float s, float m, int64_t col) {
+    auto store = [&](float s, float m, int32_t col) {
         if constexpr (kSel) {
-            if (scores && col < N) scores[q_mine * N + col] = s;
+            if (srow && col < n32) srow[(uint32_t)col] = s;
             const bool pass = s > (half ? tb : ta);
             const uint64_t bal = __ballot(pass);
             if (bal == 0) return;
@@ -529,20 +536,20 @@ __global__ __launch_bounds__(256, 2) void index_prefill_kernel(
             if (pass) {
                 const uint32_t pos = (half ? nb : na) + rank;
                 bkey[half ? slot_b : slot_a][pos] = tk::score_key(s);
-                bid[half ? slot_b : slot_a][pos] = (uint16_t)(col - e_begin);
+                bid[half ? slot_b : slot_a][pos] = (uint16_t)(col - (int32_t)e_begin);
             }
             na += (uint32_t)__builtin_popcount(ml);
             nb += (uint32_t)__builtin_popcount(mh);
-        } else if (col < N) {
-            scores[q_mine * N + col] = s;
-            if (kBlk && (lane & 7) == 0) block_scores[q_mine * nblk + (col >> 3)] = m;
+        } else if (col < n32) {
+            srow[(uint32_t)col] = s;
+            if (kBlk && (lane & 7) == 0) brow[(uint32_t)col >> 3] = m;
         }
     };
     // One group = 32 entries (rows h2*32.. of an LDS tile) for both queries:
     // 8 fragment reads, 16 MFMAs. The epilogue of the previous group runs in
     // the same straight-line block so the scheduler can put its VALU work in
     // the shadow of these MFMAs.
-    auto group = [&](int buf, int h2, f32x16& acca, f32x16& accb, const f32x16& pa, const f32x16& pb, int64_t pcol,
+    auto group = [&](int buf, int h2, f32x16& acca, f32x16& accb, const f32x16& pa, const f32x16& pb, int32_t pcol,
                      float (&out)[2]) {
         const uint8_t* rowp = lds[buf] + (h2 * 32 + col_in_tile) * kPfRow + half * 16;
         bf16x8 bj[8];
@@ -573,13 +580,13 @@ __global__ __launch_bounds__(256, 2) void index_prefill_kernel(
     float out[2];
     {
         const f32x16 z = {};
-        group(0, 0, pa, pb, z, z, N, out);  // no previous group: its results are discarded
+        group(0, 0, pa, pb, z, z, n32, out);  // no previous group: its results are discarded
     }
     for (int st = 0; st < nsub; st++) {
         const bool more = st + 1 < nsub;
         // the last iteration re-reads tile 0 (in bounds) and discards it
         const Pre nxt = gload(more ? st + 1 : 0);
-        const int64_t col0 = tile_base + (int64_t)st * kPfSub + col_in_tile;
+        const int32_t col0 = (int32_t)tile_base + st * kPfSub + col_in_tile;
         group(st & 1, 1, ca, cb, pa, pb, col0, out);
         store(out[0], out[1], col0);
         if (more) lstore((st + 1) & 1, nxt);
