@@ -93,6 +93,21 @@ def alg_bytes_attn(nq, k=512, window=128, window_row=1024):
     return nq * (k * 288 + window * window_row + 64 * 1024 + 64 * 1024 + k * 4)
 
 
+def alg_bytes_step_unfused(wl, k=512, pool_blocks=2048):
+    """Algorithmic bytes of one decode step counted as the unfused calls move
+    them (the accounting the step targets are stated in): Full scoring with its
+    score row (and block maxima) written, both read back by the Top-K, each
+    Reindex layer's pool keys read and its pool scores and ids written, and
+    every attention layer."""
+    blk = ((wl.N + 7) // 8) * 4 if wl.hier else 0
+    index = alg_bytes_index_full(wl)
+    topk = wl.nq * (wl.N * 4 + blk)
+    n_re = wl.n_index_layers - 1
+    pool = pool_blocks * 8
+    reindex = n_re * wl.nq * pool * (256 + 4 + 4)
+    return index + topk + reindex + wl.n_attn_layers * alg_bytes_attn(wl.nq)
+
+
 def alg_flops_attn(nq, k=512, window=128):
     return nq * 2 * 2 * 64 * (k + window) * 512
 
@@ -183,6 +198,7 @@ def bench_workload(name, steps, warmup, nsets, torch):
     res["attn_GBps"] = alg_bytes_attn(wl.nq, window_row=528 if wl.swa_fmt == "fp8" else 1024) / t_att / 1e9
     res["attn_TFLOPs"] = alg_flops_attn(wl.nq) / t_att / 1e12
     res["_alg_bytes_index_full"] = alg_bytes_index_full(wl)
+    res["_alg_bytes_step"] = alg_bytes_step_unfused(wl)
     res["_alg_flops_index_full"] = alg_flops_index_full(wl)
     if wl.q_per_seq > 1:
         # the same scoring alone, score row written (csa2_index_full), outside the step
@@ -289,32 +305,74 @@ def cpu_baseline(torch, target_s=15.0):
                       "%.1f s of CPU time" % (reps, n, total)}
 
 
-# sources the fused scoring + Top-K kernel is compiled from
+# sources the scoring kernels (fused decode scoring + Top-K, prefill scoring) are compiled from
 KERNEL_SOURCES = ["index.hip", "topk_select.h", "device_common.h"]
+# sources of the sparse attention kernels
+ATTN_SOURCES = ["attn.hip", "device_common.h"]
 
 
-def kernel_source_hash():
+def kernel_source_hash(files=KERNEL_SOURCES):
     h = hashlib.sha256()
-    for f in KERNEL_SOURCES:
+    for f in files:
         h.update(open(os.path.join(ROOT, "kv_cache_compression_csa2_amd", "csrc", f), "rb").read())
     return h.hexdigest()[:16]
+
+
+def profile_fields(name, files):
+    """The machine-read 'key: value' lines of a committed rocprofv3 summary
+    under profiles/, if it was taken on the current sources of its kernel
+    (its kernel_source_sha256_16 line); else {}."""
+    path = os.path.join(ROOT, "profiles", name)
+    if not os.path.exists(path):
+        return {}
+    fields = {}
+    for line in open(path):
+        if ":" in line and not line.startswith(("|", "#", "`", "rocprof")):
+            k, v = line.split(":", 1)
+            fields[k.strip()] = v.strip()
+    return fields if fields.get("kernel_source_sha256_16") == kernel_source_hash(files) else {}
 
 
 def traffic_from_profiles():
     """HBM bytes per launch of the dominant kernel from the committed rocprofv3
     counter summary (FETCH_SIZE + WRITE_SIZE, calibrated on a 1 GiB copy), if it
     was taken on the current kernel sources; else None."""
-    path = os.path.join(ROOT, "profiles", "index_topk_encoder64k_traffic.md")
-    if not os.path.exists(path):
-        return None
-    fields = {}
-    for line in open(path):
-        if ":" in line and not line.startswith(("|", "#", "`", "rocprof")):
-            k, v = line.split(":", 1)
-            fields[k.strip()] = v.strip()
-    if fields.get("kernel_source_sha256_16") != kernel_source_hash() or "hbm_bytes_per_launch" not in fields:
-        return None
-    return int(fields["hbm_bytes_per_launch"])
+    f = profile_fields("index_topk_encoder64k_traffic.md", KERNEL_SOURCES)
+    return int(f["hbm_bytes_per_launch"]) if "hbm_bytes_per_launch" in f else None
+
+
+def target_rooflines(res, sweep):
+    """The three step targets, each against its roofline: the FP4 main-KV
+    gather at 1024 query-layers (>= 60% of HBM), the prefill indexer (>= 50%
+    of bf16 MFMA) and the 1M decode step (>= 60% of HBM, step bytes counted as
+    the unfused calls move them). Counter figures come from the committed
+    summaries while they match the current kernel sources (else null)."""
+    t = {}
+    if "1024" in sweep:
+        g = sweep["1024"]
+        f = profile_fields("sparse_attn_gather_traffic.md", ATTN_SOURCES)
+        t["fp4_gather_1024_queries"] = {
+            "bound": "hbm", "achieved": round(g["GBps"], 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+            "frac": round(g["GBps"] / HBM_PEAK_GBS, 4), "target_frac": 0.60,
+            "alg_bytes_per_launch": alg_bytes_attn(1024),
+            "traffic": int(f["hbm_bytes_per_launch_1024q"]) if "hbm_bytes_per_launch_1024q" in f else None}
+    if "prefill128k" in res:
+        p = res["prefill128k"]
+        f = profile_fields("index_prefill_prefill128k_mfma.md", KERNEL_SOURCES)
+        t["prefill_indexer"] = {
+            "bound": "mfma", "achieved": round(p["scoring_only_TFLOPs"], 1), "peak": BF16_PEAK_TFLOPS,
+            "unit": "TFLOP/s", "frac": round(p["scoring_only_TFLOPs"] / BF16_PEAK_TFLOPS, 4), "target_frac": 0.50,
+            "call": "csa2_index_full", "ms": round(p["scoring_only_ms"], 4),
+            "mfma_busy": float(f["mfma_busy_scoring_only"]) if "mfma_busy_scoring_only" in f else None,
+            "clock_ghz": float(f["clock_ghz_scoring_only"]) if "clock_ghz_scoring_only" in f else None}
+    if "decode1m" in res:
+        d = res["decode1m"]
+        gbs = d["_alg_bytes_step"] / (d["ms_per_step"] * 1e-3) / 1e9
+        t["decode1m_step"] = {
+            "bound": "hbm", "achieved": round(gbs, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+            "frac": round(gbs / HBM_PEAK_GBS, 4), "target_frac": 0.60, "alg_bytes_per_step": d["_alg_bytes_step"],
+            "queries_per_s": round(d["queries_per_s"], 1)}
+    return t
 
 
 def main():
@@ -387,6 +445,7 @@ def main():
             e["fused_indexer_TFLOPs"] = round(p["index_topk_TFLOPs"], 2)
             e["fused_indexer_frac_of_bf16_peak"] = round(p["index_topk_TFLOPs"] / BF16_PEAK_TFLOPS, 4)
     extra["attn_gather_sweep"] = {k: {kk: round(vv, 4) for kk, vv in v.items()} for k, v in sweep.items()}
+    extra["targets"] = target_rooflines(res, sweep)
     line = {
         "metric": METRIC, "value": round(h["queries_per_s"], 1), "unit": "queries/s", "n_gpus": 1,
         "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(h["ms_per_step"], 5),
