@@ -24,7 +24,10 @@
 // highest bit where the segment's keys differ, since score rows and merged
 // candidates sit in narrow bands. Shapes beyond those capacities take the
 // global-memory path (512 threads, every pass re-reads the scores through
-// the caches).
+// the caches). Each register-path launch is described by a job (chunk
+// select, final merge, group merge); two independent selections whose jobs
+// take the same shape share one launch (the hierarchical Full layer's Top-K
+// merge and its pool's block selection).
 #include <math.h>
 
 #include "device_common.h"
