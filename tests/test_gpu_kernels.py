@@ -309,6 +309,21 @@ def test_index_topk_merge_pool_bit_exact_on_exact_scores(nq, N, k, pool_k, fp4):
     assert np.array_equal(np_(cand), O.topk(rb, pool_k))
 
 
+@pytest.mark.parametrize("nq,N,k,pool_k", [(2, 7, 512, 3), (3, 13, 5, 1), (1, 8, 1, 1), (4, 4100, 512, 4096)])
+def test_index_topk_merge_pool_degenerate_shapes(nq, N, k, pool_k):
+    """Rows shorter than one block, k above the row length, pools wider than
+    the block row, single entries: the oracle's Top-k and Top-pool_k, -1 padded."""
+    print("case: index_topk_merge_pool degenerate", nq, N, k, pool_k, flush=True)
+    q, w, kb = _int_idx_inputs(nq, N, 1300 + N)
+    nv = np.array([N, max(N // 3, 1), 0, 1][:nq], np.int32)
+    top, blk, cand = _merge_pool(q, w, kb, None, N, k, pool_k, dev_i32(nv, DEV))
+    torch.cuda.synchronize()
+    rs, rb = O.index_full(u16(q), np_(w), u16(kb), N, 1, n_visible=nv, block_size=8)
+    assert np.array_equal(np_(blk), rb)
+    assert np.array_equal(np_(top), O.topk(rs, k, row_len=nv))
+    assert np.array_equal(np_(cand), O.topk(rb, pool_k))
+
+
 @pytest.mark.parametrize("nq,N,pool_k", [(8, 1 << 20, 2048), (32, 262144, 2048), (1, 1 << 21, 4096),
                                          (2, 4096, 2048)])
 def test_index_topk_merge_pool_matches_the_separate_calls(nq, N, pool_k):
