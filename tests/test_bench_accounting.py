@@ -57,3 +57,13 @@ def test_committed_counter_summaries_are_machine_readable():
         fields = {k.strip(): v.strip() for k, v in fields.items()}
         assert len(fields.get("kernel_source_sha256_16", "")) == 16, name
         float(fields[key])
+
+
+def test_bench_refuses_more_than_one_gpu():
+    """The benchmark measures one GPU; asking for more ends with a message and
+    a non-zero status before any GPU work."""
+    import subprocess
+    r = subprocess.run([sys.executable, os.path.join(ROOT, "bench.py"), "--gpus", "2"], capture_output=True,
+                       text=True, timeout=300, cwd=ROOT)
+    assert r.returncode != 0
+    assert "one GPU" in (r.stdout + r.stderr)
