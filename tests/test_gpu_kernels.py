@@ -658,6 +658,21 @@ def test_sparse_attn_split_path():
     _attn_check(q, kv, idx, swa, st, sl, N, 1, 128)
 
 
+@pytest.mark.parametrize("nq", [15, 16, 63, 64, 127, 128, 511, 512])
+def test_sparse_attn_split_table_boundaries(nq):
+    """Batches on both sides of each step of the split table (7 / 4 / 2 / 1
+    workgroups per query from 16 / 64 / 128 / 512 queries), so every split
+    count and the unsplit path run against the oracle, with empty slots and
+    mixed window lengths."""
+    print("case: attn split boundary", nq, flush=True)
+    N, T = 1500, 300
+    q, kv, idx, swa, st, sl = _attn_case(nq, N, 512, 1, 40 + nq, T=T, pad=5)
+    rng = np.random.default_rng(41 + nq)
+    sl = rng.choice(np.array([0, 1, 32, 33, 96, 128], np.int32), nq).astype(np.int32)
+    st = rng.integers(0, T - 128, nq).astype(np.int32)
+    _attn_check(q, kv, idx, swa, st, sl, N, 1, T)
+
+
 @pytest.mark.parametrize("nq,k", [(12, 512), (12, 80)])
 def test_sparse_attn_window_lengths(nq, k):
     """Window lengths at and around tile boundaries, window starts inside the
