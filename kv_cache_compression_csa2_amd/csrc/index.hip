@@ -357,6 +357,8 @@ constexpr int kPfSelK = 512;           // largest k of the fused prefill selecti
 constexpr int kPfBuf = 960;            // candidate slots per query (a multiple of 64; 2 workgroups fit a CU)
 constexpr int kPfHigh = kPfBuf - 64;   // compact before a tile's 64 entries could overflow
 constexpr int kPfLow = kPfSelK + 128;  // buffers at or below this are left alone in a round
+constexpr int kPfSlack = 64;           // a round's compaction may keep up to k + kPfSlack (<= kPfLow)
+static_assert(kPfSelK + kPfSlack <= kPfLow, "a compacted buffer must stay out of the next round");
 constexpr int64_t kPfMaxChunk = 65536; // entry offsets within a chunk fit 16 bits
 
 // Registers of one prefill tile load: bf16 K 4 units of 16 bytes per thread;
@@ -377,16 +379,20 @@ struct PfPre<true> {
 // selection eogee.com report 3.5 names, for the prefill chunk): no score row
 // is written. Each wave owns its 2 queries' candidate buffers in LDS (keys and
 // 16-bit entry offsets within the chunk) and sees their entries in ascending
-// order, so an entry can only enter a query's Top-k if its score beats the
-// k-th best so far (T): an equal score arrives after every buffered one and
-// ranks below them. Passing entries are appended; the buffers are compacted to
-// their k best (tk::wave_keep_topk, T becomes the k-th key) only at tile
-// boundaries, all waves in the same round: the waves meet at every tile's
-// barrier, so one wave compacting alone would stall the other three. A random
-// row of n entries appends about k (1 + ln(n / k)) entries, so rounds are few.
-// At the end each query's k best go out in entry order: final indices when the
-// row is one chunk, else (key, entry) candidates that the Top-K merge combines.
-// `scores`, when given, still receives the score row (a checking aid).
+// order. A query's threshold T is a score that at least k buffered entries
+// reach; an entry can only enter the query's Top-k if its score beats T (an
+// equal or lower score arrives after k buffered ones that rank above it).
+// Passing entries are appended; the buffers are compacted (tk::wave_keep_topk)
+// only at tile boundaries, all waves in the same round (the waves meet at
+// every tile's barrier, so one wave compacting alone would stall the other
+// three). A round's compaction keeps every entry at or above a new T that
+// between k and k + kPfSlack of them reach: the radix search stops there
+// instead of resolving the exact k-th key. A random row of n entries appends
+// about k (1 + ln(n / k)) entries, so rounds are few. At the end an exact
+// compaction leaves each query's k best, which go out in entry order: final
+// indices when the row is one chunk, else (key, entry) candidates that the
+// Top-K merge combines. `scores`, when given, still receives the score row (a
+// checking aid).
 template <bool kFp4, bool kBlk, bool kSel>
 __global__ __launch_bounds__(256, 2) void index_prefill_kernel(
     const uint16_t* __restrict__ q_idx, const float* __restrict__ w, const void* __restrict__ k_idx, int64_t N,
@@ -604,14 +610,12 @@ __global__ __launch_bounds__(256, 2) void index_prefill_kernel(
             const uint4 f = *reinterpret_cast<const uint4*>(full_flag[st & 1]);
             if (f.x | f.y | f.z | f.w) {
                 // a compaction round: every wave compacts its fuller buffers
-                if (na > (uint32_t)kPfLow) {
-                    ta = tk::key_score(tk::wave_keep_topk<kPfBuf>(bkey[slot_a], bid[slot_a], na, (uint32_t)k));
-                    na = (uint32_t)k;
-                }
-                if (nb > (uint32_t)kPfLow) {
-                    tb = tk::key_score(tk::wave_keep_topk<kPfBuf>(bkey[slot_b], bid[slot_b], nb, (uint32_t)k));
-                    nb = (uint32_t)k;
-                }
+                if (na > (uint32_t)kPfLow)
+                    ta = tk::key_score(
+                        tk::wave_keep_topk<kPfBuf>(bkey[slot_a], bid[slot_a], na, (uint32_t)k, (uint32_t)kPfSlack, na));
+                if (nb > (uint32_t)kPfLow)
+                    tb = tk::key_score(
+                        tk::wave_keep_topk<kPfBuf>(bkey[slot_b], bid[slot_b], nb, (uint32_t)k, (uint32_t)kPfSlack, nb));
             }
         }
         store(out[0], out[1], col0 + 32);
@@ -622,10 +626,7 @@ __global__ __launch_bounds__(256, 2) void index_prefill_kernel(
         for (int h = 0; h < 2; h++) {
             const int slot = h ? slot_b : slot_a;
             uint32_t n = h ? nb : na;
-            if (n > (uint32_t)k) {
-                tk::wave_keep_topk<kPfBuf>(bkey[slot], bid[slot], n, (uint32_t)k);
-                n = (uint32_t)k;
-            }
+            if (n > (uint32_t)k) tk::wave_keep_topk<kPfBuf>(bkey[slot], bid[slot], n, (uint32_t)k, 0u, n);  // exact: n = k
             const int64_t q = h ? qb : qa;
             if (nchunks == 1) {
                 for (int i = lane; i < k; i += 64) out_idx[q * k + i] = i < (int)n ? (int32_t)(e_begin + bid[slot][i]) : -1;

@@ -409,18 +409,23 @@ CSA2_DEVINL uint32_t reg_select_emit(const uint32_t (&key)[KPT], uint32_t k, Reg
 
 // One wave keeps the k best of n > k keys held in LDS at key[0, n) (payloads
 // id[0, n)), positions in arrival order: larger key first, equal keys by lower
-// position. The kept ones move to key[0, k) / id[0, k) in position order, and
-// the k-th largest key is returned. Lane l holds positions [P*l, P*l + P)
-// (contiguous runs, so lane order is position order); every load is done
-// before the first store, so the compaction can run in place. The k-th key is
-// built bit by bit from the top (the largest t with at least k keys >= t,
-// counted with one ballot per key slot), starting below the highest bit where
-// the largest and smallest keys differ; keys above it are kept, then equal
-// ones in position order until k are. Must be called by all 64 lanes of the
-// wave (wave-uniform n and k); key 0 marks no key and never appears among
-// valid positions.
+// position. The kept ones move to the front, key[0, kept) / id[0, kept), in
+// position order. Lane l holds positions [P*l, P*l + P) (contiguous runs, so
+// lane order is position order); every load is done before the first store,
+// so the compaction can run in place. The threshold t is built bit by bit from
+// the top (the largest t with at least k keys >= t, counted with one ballot per
+// key slot), starting below the highest bit where the largest and smallest
+// keys differ. Exact (slack 0, or when the search runs to the last bit): keys
+// above the k-th largest are kept, then equal ones in position order until k
+// are; that key is returned. With slack > 0 the search stops as soon as at
+// most k + slack keys are >= t: all of them are kept (k <= kept <= k + slack)
+// and t is returned -- a lower bound of the k-th largest key that need not be
+// a key itself (0 when it would map to no finite score). Every dropped key
+// then has at least k larger ones, so no key of the top k is lost. Must be
+// called by all 64 lanes of the wave (wave-uniform n, k and slack); key 0
+// marks no key and never appears among valid positions.
 template <int C, typename Id>
-CSA2_DEVINL uint32_t wave_keep_topk(uint32_t* key, Id* id, uint32_t n, uint32_t k) {
+CSA2_DEVINL uint32_t wave_keep_topk(uint32_t* key, Id* id, uint32_t n, uint32_t k, uint32_t slack, uint32_t& kept) {
     constexpr int P = C / 64;
     static_assert(P * 64 == C, "buffer size must be a multiple of 64");
     const uint32_t lane = threadIdx.x & 63;
@@ -437,44 +442,55 @@ CSA2_DEVINL uint32_t wave_keep_topk(uint32_t* key, Id* id, uint32_t n, uint32_t 
     }
     const uint32_t hi = wave_max_u32(lmax), lo = wave_min_u32(lmin);
     uint32_t t = hi;
+    uint32_t cnt_t = n;  // keys >= t (every valid key shares t's bits so far)
     if (hi != lo) {
         const int top = 31 - __builtin_clz(hi ^ lo);
         t = top == 31 ? 0u : hi & ~((2u << top) - 1u);  // the bits every key shares
-        for (int b = top; b >= 0; b--) {
+        for (int b = top; b >= 0 && cnt_t > k + slack; b--) {
             const uint32_t c = t | (1u << b);
             uint32_t cnt = 0;
 #pragma unroll
             for (int j = 0; j < P; j++) cnt += (uint32_t)__builtin_popcountll(__ballot(kv[j] >= c));
-            if (cnt >= k) t = c;
+            if (cnt >= k) {
+                t = c;
+                cnt_t = cnt;
+            }
         }
     }
+    // keep every key >= t when they are few enough, else the exact k
+    const bool all_ge = cnt_t <= k + slack;
     uint32_t gt = 0, eq = 0;
 #pragma unroll
     for (int j = 0; j < P; j++) {
-        gt += (uint32_t)(kv[j] > t);
-        eq += (uint32_t)(kv[j] == t);
+        const bool v = lane * P + j < n;
+        gt += (uint32_t)(v && kv[j] > t);
+        eq += (uint32_t)(v && kv[j] == t);
     }
     const uint32_t igt = wave_incl_scan(gt), ieq = wave_incl_scan(eq);
-    const uint32_t need = k - (uint32_t)__builtin_amdgcn_readlane((int)igt, 63);  // equal keys to keep, >= 1
+    const uint32_t ngt = (uint32_t)__builtin_amdgcn_readlane((int)igt, 63);
+    const uint32_t need = all_ge ? (uint32_t)__builtin_amdgcn_readlane((int)ieq, 63) : k - ngt;  // equal keys to keep
+    const uint32_t nkeep = ngt + need;
     uint32_t e = ieq - eq;  // equal keys at lower positions
-    // A stable partition of [0, n): kept keys to [0, k) and the others to
-    // [k, n), both in position order, so every store is unconditional (no
+    // A stable partition of [0, n): kept keys to [0, nkeep) and the others to
+    // [nkeep, n), both in position order, so every store is unconditional (no
     // divergent branch per key); positions past n are rewritten in place.
     uint32_t o = (igt - gt) + min(e, need);                 // kept keys at lower positions
-    uint32_t d = k + min(lane * P, n) - o;                  // discarded keys at lower positions, offset by k
+    uint32_t d = nkeep + min(lane * P, n) - o;              // discarded keys at lower positions, offset by nkeep
 #pragma unroll
     for (int j = 0; j < P; j++) {
         const uint32_t p = lane * P + j;
-        const bool iseq = kv[j] == t;
-        const bool keep = kv[j] > t || (iseq && e < need);
+        const bool iseq = p < n && kv[j] == t;
+        const bool keep = p < n && (kv[j] > t || (iseq && e < need));
         e += (uint32_t)iseq;
         const uint32_t dst = p >= n ? p : (keep ? o : d);
-        o += (uint32_t)(keep && p < n);
+        o += (uint32_t)keep;
         d += (uint32_t)(!keep && p < n);
         key[dst] = kv[j];
         id[dst] = iv[j];
     }
-    return t;
+    kept = nkeep;
+    // valid keys are at least key(-FLT_MAX) = 2^23: a smaller t admits every score
+    return t < 0x00800000u ? 0u : t;
 }
 
 }  // namespace tk
