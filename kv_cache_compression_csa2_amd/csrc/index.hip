@@ -148,6 +148,67 @@ CSA2_DEVINL float stream_score(const StreamQuery<kFp4>& Q, const StreamTile<kFp4
     return st.valid ? s : -INFINITY;
 }
 
+// bf16 Full rows, line-ordered: a wave's 32-entry tile is 8 KiB of
+// consecutive entries. Instruction j reads line j >> 2 (bytes 128 (j >> 2) ..
+// +128) of entries 8 (j & 3) .. +8, one whole 128-byte line per 8 lanes, with
+// non-temporal loads: each line is read once, by one instruction, so nothing
+// has to stay cached for a later one (a plain streaming read reaches less
+// bandwidth than a non-temporal one on this part).
+// Buffer resource word 3 for the gfx9-family raw loads (32-bit data format),
+// and the cache-policy operand that marks a load non-temporal (the nt bit).
+constexpr int kRsrcFlags = 0x00020000;
+constexpr int kCpolNt = 2;
+struct LineTile {
+    u32x4 v[8];
+};
+// rs: buffer resource over the chunk's valid entries (reads past them return
+// zeros; their scores are discarded); off0: the tile's byte offset in it.
+CSA2_DEVINL void line_load(__amdgpu_buffer_rsrc_t rs, int off0, int lane, LineTile& lt) {
+    const int lo = (lane >> 3) * (kIdxDim * 2) + 16 * (lane & 7);
+#pragma unroll
+    for (int j = 0; j < 8; j++)
+        lt.v[j] = __builtin_bit_cast(
+            u32x4, __builtin_amdgcn_raw_buffer_load_b128(rs, lo + 128 * (j >> 2), off0 + 2048 * (j & 3), kCpolNt));
+}
+// The tile's operands in MFMA layout (lane (n, half) takes 16-byte unit
+// 2j + half of entry n at step j), through a wave-private 4 KiB LDS stage, one
+// line of the 32 entries at a time. Stage slot of 16-byte unit u (0..7) of
+// entry e: row e >> 1, group 8 (e & 1) + (u ^ ((e >> 1) & 7)) of 16 -- writes
+// (16 lanes: 2 entries x 8 units) and reads (16 lanes: 16 entries, one unit)
+// both touch 16 distinct groups, so neither has bank conflicts. LDS
+// operations of one wave complete in order, so the stage needs no barrier:
+// the wave barriers only keep the compiler from moving accesses across.
+CSA2_DEVINL void line_operands(const LineTile& lt, uint8_t* stage, int lane, bf16x8 (&b)[8]) {
+    const int e_in = lane >> 3, u = lane & 7, n = lane & 31, half = lane >> 5;
+#pragma unroll
+    for (int r = 0; r < 2; r++) {
+#pragma unroll
+        for (int jj = 0; jj < 4; jj++) {
+            const int e = 8 * jj + e_in;
+            *reinterpret_cast<u32x4*>(stage + 256 * (e >> 1) + 16 * (8 * (e & 1) + (u ^ ((e >> 1) & 7)))) =
+                lt.v[4 * r + jj];
+        }
+        __builtin_amdgcn_wave_barrier();
+#pragma unroll
+        for (int s2 = 0; s2 < 4; s2++) {
+            const int uu = 2 * s2 + half;
+            b[4 * r + s2] = as_bf16x8(
+                *reinterpret_cast<const u32x4*>(stage + 256 * (n >> 1) + 16 * (8 * (n & 1) + (uu ^ ((n >> 1) & 7)))));
+        }
+        __builtin_amdgcn_wave_barrier();
+    }
+}
+CSA2_DEVINL float line_score(const StreamQuery<false>& Q, const bf16x8 (&b)[8], bool valid) {
+    f32x16 acc = {};
+#pragma unroll
+    for (int j = 0; j < 8; j++) acc = mfma32x32x16(Q.a[j], b[j], acc);
+    float s = 0.0f;
+#pragma unroll
+    for (int r = 0; r < 16; r++) s = fmaf(Q.wr[r], relu_bits(acc[r]), s);
+    s += from_upper_half(s);
+    return valid ? s : -INFINITY;
+}
+
 template <bool kReindex, bool kFp4>
 __global__ __launch_bounds__(kStreamThreads) void index_stream_kernel(
     const uint16_t* __restrict__ q_idx, const float* __restrict__ w, const void* __restrict__ k_idx, int64_t N,
@@ -231,7 +292,7 @@ __global__ __launch_bounds__(kStreamThreads) void index_stream_kernel(
 // carry entry ids; with ascending cand_blocks the result is the Top-K of
 // csa2_index_reindex's pool row mapped through its pool ids.
 template <bool kFp4, bool kRe, int kFtThreads, int kFtChunk>
-__global__ __launch_bounds__(kFtThreads) void index_topk_kernel(
+__global__ __launch_bounds__(kFtThreads, kFtThreads == 256 ? 3 : 1) void index_topk_kernel(
     const uint16_t* __restrict__ q_idx, const float* __restrict__ w, const void* __restrict__ k_idx, int64_t N,
     int32_t q_per_seq, const int32_t* __restrict__ n_visible, const int32_t* __restrict__ cand_blocks, int32_t nb,
     int32_t k, int32_t nchunks, int32_t* __restrict__ out_idx, uint32_t* __restrict__ cand_key,
@@ -249,6 +310,9 @@ __global__ __launch_bounds__(kFtThreads) void index_topk_kernel(
     tk::RegTk<kFtThreads>& sh = *reinterpret_cast<tk::RegTk<kFtThreads>*>(smem);
     // Reindex: the chunk's pool block ids (-1 past the pool)
     __shared__ int32_t cblk[kRe ? kFtChunk / 8 : 1];
+    // bf16 Full rows: each wave's line-ordered tile stage
+    constexpr bool kLine = !kFp4 && !kRe;
+    __shared__ __attribute__((aligned(16))) uint8_t stage[kLine ? kFtWaves : 1][kLine ? 4096 : 16];
     const int64_t q = blockIdx.x / nchunks;
     const int chunk = blockIdx.x % nchunks;
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
@@ -297,7 +361,40 @@ __global__ __launch_bounds__(kFtThreads) void index_topk_kernel(
         }
     };
     int t = wave;
-    if (t < ntile) {
+    if constexpr (kLine) {
+        // the chunk's entries below nv
+        const int64_t nvalid = nv - c0 < 0 ? 0 : (nv - c0 < kFtChunk ? nv - c0 : kFtChunk);
+        const __amdgpu_buffer_rsrc_t rs = __builtin_amdgcn_make_buffer_rsrc(
+            const_cast<uint16_t*>(static_cast<const uint16_t*>(kseq) + c0 * kIdxDim), (short)0,
+            (int)(nvalid * kIdxDim * 2), kRsrcFlags);
+        auto lfinish = [&](int tt, const LineTile& lt) {
+            bf16x8 b[8];
+            line_operands(lt, stage[wave], lane, b);
+            const int p = tt * 32 + col_in_tile;
+            const float s = line_score(Q, b, c0 + p < nv);
+            if (half == 0) sc[p] = s;
+            if (scores_dbg && half == 0 && p < n) scores_dbg[q * ncols + c0 + p] = s;
+            if (block_scores) {
+                const float m = max8_lanes(s);
+                if (half == 0 && (lane & 7) == 0 && p < n) block_scores[q * nblk + ((c0 + p) >> 3)] = m;
+            }
+        };
+        if (t < ntile) {
+            LineTile l0, l1;
+            line_load(rs, t * 8192, lane, l0);
+            while (true) {
+                const int t1 = t + kFtWaves;
+                if (t1 < ntile) line_load(rs, t1 * 8192, lane, l1);
+                lfinish(t, l0);
+                if (t1 >= ntile) break;
+                const int t2 = t1 + kFtWaves;
+                if (t2 < ntile) line_load(rs, t2 * 8192, lane, l0);
+                lfinish(t1, l1);
+                if (t2 >= ntile) break;
+                t = t2;
+            }
+        }
+    } else if (t < ntile) {
         StreamTile<kFp4> s0, s1;
         load(t, s0);
         while (true) {
