@@ -209,6 +209,35 @@ CSA2_DEVINL float line_score(const StreamQuery<false>& Q, const bf16x8 (&b)[8], 
     return valid ? s : -INFINITY;
 }
 
+// FP4 Full rows, line-ordered: a 32-entry tile is 2176 consecutive bytes (17
+// lines, line-aligned when the sequence length is a multiple of 32), read as
+// 136 16-byte units by 3 non-temporal instructions (the third on 8 lanes; the
+// other lanes' offsets lie past the resource and read nothing).
+struct LineTile4 {
+    u32x4 v[3];
+};
+CSA2_DEVINL void line_load4(__amdgpu_buffer_rsrc_t rs, int off0, int lane, LineTile4& lt) {
+#pragma unroll
+    for (int i = 0; i < 3; i++) {
+        const int vo = (i < 2 || lane < 8) ? 16 * (lane + 64 * i) : 0x40000000;
+        lt.v[i] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(rs, vo, off0, kCpolNt));
+    }
+}
+// The tile through a wave-private 3 KiB LDS stage into the per-entry layout
+// of stream_load: lane (n, half) takes code dwords 8 half .. +8 and the scale
+// dword of entry n (4-byte aligned reads at 68-byte strides).
+CSA2_DEVINL void line_operands4(const LineTile4& lt, uint8_t* stage, int lane, StreamTile<true>& st) {
+#pragma unroll
+    for (int i = 0; i < 3; i++) *reinterpret_cast<u32x4*>(stage + 16 * (lane + 64 * i)) = lt.v[i];
+    __builtin_amdgcn_wave_barrier();
+    const uint8_t* e = stage + kKRec * (lane & 31);
+    const uint32_t* c = reinterpret_cast<const uint32_t*>(e + 32 * (lane >> 5));
+#pragma unroll
+    for (int j = 0; j < 8; j++) st.code[j] = c[j];
+    st.scales = *reinterpret_cast<const uint32_t*>(e + kIdxDim / 2);
+    __builtin_amdgcn_wave_barrier();
+}
+
 template <bool kReindex, bool kFp4>
 __global__ __launch_bounds__(kStreamThreads) void index_stream_kernel(
     const uint16_t* __restrict__ q_idx, const float* __restrict__ w, const void* __restrict__ k_idx, int64_t N,
@@ -311,8 +340,8 @@ __global__ __launch_bounds__(kFtThreads, kFtThreads == 256 ? 3 : 1) void index_t
     // Reindex: the chunk's pool block ids (-1 past the pool)
     __shared__ int32_t cblk[kRe ? kFtChunk / 8 : 1];
     // bf16 Full rows: each wave's line-ordered tile stage
-    constexpr bool kLine = !kFp4 && !kRe;
-    __shared__ __attribute__((aligned(16))) uint8_t stage[kLine ? kFtWaves : 1][kLine ? 4096 : 16];
+    constexpr bool kLine = !kRe;
+    __shared__ __attribute__((aligned(16))) uint8_t stage[kLine ? kFtWaves : 1][kLine ? (kFp4 ? 3072 : 4096) : 16];
     const int64_t q = blockIdx.x / nchunks;
     const int chunk = blockIdx.x % nchunks;
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
@@ -361,7 +390,44 @@ __global__ __launch_bounds__(kFtThreads, kFtThreads == 256 ? 3 : 1) void index_t
         }
     };
     int t = wave;
-    if constexpr (kLine) {
+    if constexpr (kLine && kFp4) {
+        if ((N & 31) == 0) {
+            // whole 32-entry tiles (the row is a multiple of 32): the chunk's
+            // entries as one buffer resource, every tile read in whole lines
+            const __amdgpu_buffer_rsrc_t rs = __builtin_amdgcn_make_buffer_rsrc(
+                const_cast<uint8_t*>(static_cast<const uint8_t*>(kseq) + c0 * kKRec), (short)0, n * kKRec, kRsrcFlags);
+            auto lfinish = [&](int tt, const LineTile4& lt) {
+                StreamTile<true> st;
+                line_operands4(lt, stage[wave], lane, st);
+                const int p = tt * 32 + col_in_tile;
+                st.valid = c0 + p < nv;
+                const float s = stream_score<true>(Q, st, half);
+                if (half == 0) sc[p] = s;
+                if (scores_dbg && half == 0 && p < n) scores_dbg[q * ncols + c0 + p] = s;
+                if (block_scores) {
+                    const float m = max8_lanes(s);
+                    if (half == 0 && (lane & 7) == 0 && p < n) block_scores[q * nblk + ((c0 + p) >> 3)] = m;
+                }
+            };
+            if (t < ntile) {
+                LineTile4 l0, l1;
+                line_load4(rs, t * 32 * kKRec, lane, l0);
+                while (true) {
+                    const int t1 = t + kFtWaves;
+                    if (t1 < ntile) line_load4(rs, t1 * 32 * kKRec, lane, l1);
+                    lfinish(t, l0);
+                    if (t1 >= ntile) break;
+                    const int t2 = t1 + kFtWaves;
+                    if (t2 < ntile) line_load4(rs, t2 * 32 * kKRec, lane, l0);
+                    lfinish(t1, l1);
+                    if (t2 >= ntile) break;
+                    t = t2;
+                }
+            }
+            t = ntile;  // done: the per-entry path below runs no tile
+        }
+    }
+    if constexpr (kLine && !kFp4) {
         // the chunk's entries below nv
         const int64_t nvalid = nv - c0 < 0 ? 0 : (nv - c0 < kFtChunk ? nv - c0 : kFtChunk);
         const __amdgpu_buffer_rsrc_t rs = __builtin_amdgcn_make_buffer_rsrc(
