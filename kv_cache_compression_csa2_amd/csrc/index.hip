@@ -170,6 +170,21 @@ CSA2_DEVINL void line_load(__amdgpu_buffer_rsrc_t rs, int off0, int lane, LineTi
         lt.v[j] = __builtin_bit_cast(
             u32x4, __builtin_amdgcn_raw_buffer_load_b128(rs, lo + 128 * (j >> 2), off0 + 2048 * (j & 3), kCpolNt));
 }
+// Reindex rows: the tile's 32 pool positions are 4 blocks of 8 consecutive
+// entries (cb: their block ids, -1 for an empty slot); instruction j reads
+// line j >> 2 of block j & 3's 8 entries, so every line is again read whole
+// by one instruction. rs covers the sequence; an empty slot's offset lies past
+// it and reads zeros.
+CSA2_DEVINL void line_load_blocks(__amdgpu_buffer_rsrc_t rs, const int32_t* cb, int lane, LineTile& lt) {
+    const int lo = (lane >> 3) * (kIdxDim * 2) + 16 * (lane & 7);
+#pragma unroll
+    for (int j = 0; j < 8; j++) {
+        const int blk = __builtin_amdgcn_readfirstlane(cb[j & 3]);
+        const int so = blk >= 0 ? blk * (8 * kIdxDim * 2) : 0x7FFFF000;
+        lt.v[j] = __builtin_bit_cast(
+            u32x4, __builtin_amdgcn_raw_buffer_load_b128(rs, lo + 128 * (j >> 2), so, kCpolNt));
+    }
+}
 // The tile's operands in MFMA layout (lane (n, half) takes 16-byte unit
 // 2j + half of entry n at step j), through a wave-private 4 KiB LDS stage, one
 // line of the 32 entries at a time. Stage slot of 16-byte unit u (0..7) of
@@ -321,7 +336,7 @@ __global__ __launch_bounds__(kStreamThreads) void index_stream_kernel(
 // carry entry ids; with ascending cand_blocks the result is the Top-K of
 // csa2_index_reindex's pool row mapped through its pool ids.
 template <bool kFp4, bool kRe, int kFtThreads, int kFtChunk>
-__global__ __launch_bounds__(kFtThreads, kFtThreads == 256 ? 3 : 1) void index_topk_kernel(
+__global__ __launch_bounds__(kFtThreads, kFtThreads == 256 && !kRe ? 3 : 1) void index_topk_kernel(
     const uint16_t* __restrict__ q_idx, const float* __restrict__ w, const void* __restrict__ k_idx, int64_t N,
     int32_t q_per_seq, const int32_t* __restrict__ n_visible, const int32_t* __restrict__ cand_blocks, int32_t nb,
     int32_t k, int32_t nchunks, int32_t* __restrict__ out_idx, uint32_t* __restrict__ cand_key,
@@ -339,8 +354,8 @@ __global__ __launch_bounds__(kFtThreads, kFtThreads == 256 ? 3 : 1) void index_t
     tk::RegTk<kFtThreads>& sh = *reinterpret_cast<tk::RegTk<kFtThreads>*>(smem);
     // Reindex: the chunk's pool block ids (-1 past the pool)
     __shared__ int32_t cblk[kRe ? kFtChunk / 8 : 1];
-    // bf16 Full rows: each wave's line-ordered tile stage
-    constexpr bool kLine = !kRe;
+    // line-ordered tiles (bf16 rows, FP4 Full rows): each wave's LDS stage
+    constexpr bool kLine = !(kRe && kFp4);
     __shared__ __attribute__((aligned(16))) uint8_t stage[kLine ? kFtWaves : 1][kLine ? (kFp4 ? 3072 : 4096) : 16];
     const int64_t q = blockIdx.x / nchunks;
     const int chunk = blockIdx.x % nchunks;
@@ -428,39 +443,57 @@ __global__ __launch_bounds__(kFtThreads, kFtThreads == 256 ? 3 : 1) void index_t
         }
     }
     if constexpr (kLine && !kFp4) {
-        // the chunk's entries below nv
-        const int64_t nvalid = nv - c0 < 0 ? 0 : (nv - c0 < kFtChunk ? nv - c0 : kFtChunk);
-        const __amdgpu_buffer_rsrc_t rs = __builtin_amdgcn_make_buffer_rsrc(
-            const_cast<uint16_t*>(static_cast<const uint16_t*>(kseq) + c0 * kIdxDim), (short)0,
-            (int)(nvalid * kIdxDim * 2), kRsrcFlags);
-        auto lfinish = [&](int tt, const LineTile& lt) {
-            bf16x8 b[8];
-            line_operands(lt, stage[wave], lane, b);
-            const int p = tt * 32 + col_in_tile;
-            const float s = line_score(Q, b, c0 + p < nv);
-            if (half == 0) sc[p] = s;
-            if (scores_dbg && half == 0 && p < n) scores_dbg[q * ncols + c0 + p] = s;
-            if (block_scores) {
-                const float m = max8_lanes(s);
-                if (half == 0 && (lane & 7) == 0 && p < n) block_scores[q * nblk + ((c0 + p) >> 3)] = m;
+        // Full: the chunk's entries below nv; Reindex: the whole sequence (its
+        // byte offsets must fit an int: N < 2^23, else the per-entry path runs)
+        if (!kRe || N < (int64_t(1) << 23)) {
+            const int64_t nvalid = nv - c0 < 0 ? 0 : (nv - c0 < kFtChunk ? nv - c0 : kFtChunk);
+            const __amdgpu_buffer_rsrc_t rs = __builtin_amdgcn_make_buffer_rsrc(
+                const_cast<uint16_t*>(static_cast<const uint16_t*>(kseq) + (kRe ? 0 : c0) * kIdxDim), (short)0,
+                (int)((kRe ? N : nvalid) * kIdxDim * 2), kRsrcFlags);
+            auto lload = [&](int tt, LineTile& lt) {
+                if constexpr (kRe)
+                    line_load_blocks(rs, &cblk[tt * 4], lane, lt);
+                else
+                    line_load(rs, tt * 8192, lane, lt);
+            };
+            auto lfinish = [&](int tt, const LineTile& lt) {
+                bf16x8 b[8];
+                line_operands(lt, stage[wave], lane, b);
+                const int p = tt * 32 + col_in_tile;
+                bool valid;
+                if constexpr (kRe) {
+                    const int32_t blk = p < n ? cblk[p >> 3] : -1;
+                    valid = blk >= 0 && (int64_t)blk * 8 + (p & 7) < nv;
+                } else {
+                    valid = c0 + p < nv;
+                }
+                const float s = line_score(Q, b, valid);
+                if (half == 0) sc[p] = s;
+                if (scores_dbg && half == 0 && p < n) scores_dbg[q * ncols + c0 + p] = s;
+                if (!kRe && block_scores) {
+                    const float m = max8_lanes(s);
+                    if (half == 0 && (lane & 7) == 0 && p < n) block_scores[q * nblk + ((c0 + p) >> 3)] = m;
+                }
+            };
+            if (t < ntile) {
+                LineTile l0, l1;
+                lload(t, l0);
+                while (true) {
+                    const int t1 = t + kFtWaves;
+                    if (t1 < ntile) lload(t1, l1);
+                    lfinish(t, l0);
+                    if (t1 >= ntile) break;
+                    const int t2 = t1 + kFtWaves;
+                    if (t2 < ntile) lload(t2, l0);
+                    lfinish(t1, l1);
+                    if (t2 >= ntile) break;
+                    t = t2;
+                }
             }
-        };
-        if (t < ntile) {
-            LineTile l0, l1;
-            line_load(rs, t * 8192, lane, l0);
-            while (true) {
-                const int t1 = t + kFtWaves;
-                if (t1 < ntile) line_load(rs, t1 * 8192, lane, l1);
-                lfinish(t, l0);
-                if (t1 >= ntile) break;
-                const int t2 = t1 + kFtWaves;
-                if (t2 < ntile) line_load(rs, t2 * 8192, lane, l0);
-                lfinish(t1, l1);
-                if (t2 >= ntile) break;
-                t = t2;
-            }
+            t = ntile;  // done: the per-entry path below runs no tile
         }
-    } else if (t < ntile) {
+    }
+    if (t < ntile) {
         StreamTile<kFp4> s0, s1;
         load(t, s0);
         while (true) {
