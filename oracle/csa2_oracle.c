@@ -325,8 +325,19 @@ static double index_score(const double* qd /*[32][128]*/, const float* w /*[32]*
     return s;
 }
 
-static void decode_query(const uint16_t* q, double* qd) {
-    for (int t = 0; t < ORC_IDX_HEADS * ORC_IDX_DIM; t++) qd[t] = bf16_value(q[t]);
+/* The 32 x 128 indexer query of query q decoded to double: bf16 (qfmt 0,
+ * [.][32][128] uint16) or, for the indexer Q in FP4 ([EOG] 3.4: the
+ * predecessor already trained the indexer Q and K in FP4), one MXFP4 entry per
+ * head in the indexer-K entry format above (qfmt 1, [.][32][68] bytes). */
+static void decode_query(const void* q_all, int qfmt, int64_t q, double* qd) {
+    if (qfmt == 0) {
+        const uint16_t* qq = (const uint16_t*)q_all + q * ORC_IDX_HEADS * ORC_IDX_DIM;
+        for (int t = 0; t < ORC_IDX_HEADS * ORC_IDX_DIM; t++) qd[t] = bf16_value(qq[t]);
+    } else {
+        const uint8_t* qq = (const uint8_t*)q_all + q * ORC_IDX_HEADS * ORC_KREC;
+        for (int h = 0; h < ORC_IDX_HEADS; h++)
+            for (int c = 0; c < ORC_IDX_DIM; c++) qd[h * ORC_IDX_DIM + c] = kidx_fp4_value(qq + h * ORC_KREC, c);
+    }
 }
 
 /* Full-mode scoring ([TIT] CSA2 Full mode; [EOG] 3.3 first indexer scans every
@@ -334,14 +345,13 @@ static void decode_query(const uint16_t* q, double* qd) {
  * n_visible[q] (or N when n_visible is NULL) score -inf. Scores are stored as
  * float. When block_size > 0, block j's score is the max over its positions
  * [j*bs, j*bs+bs) ([EOG] 3.3: each block takes its highest index score). */
-static void index_full_any(const uint16_t* q_idx, const float* w, const void* k_idx, int kfmt, int64_t N,
+static void index_full_any(const void* q_idx, int qfmt, const float* w, const void* k_idx, int kfmt, int64_t N,
                            int32_t nq, int32_t q_per_seq, const int32_t* n_visible, float* scores,
                            int32_t block_size, float* block_scores) {
     const int64_t CH = 4096; /* entries per parallel work item */
     int64_t nch = (N + CH - 1) / CH;
     double* qd = (double*)malloc(sizeof(double) * (size_t)(nq > 0 ? nq : 1) * ORC_IDX_HEADS * ORC_IDX_DIM);
-    for (int32_t q = 0; q < nq; q++)
-        decode_query(q_idx + (int64_t)q * ORC_IDX_HEADS * ORC_IDX_DIM, qd + (int64_t)q * ORC_IDX_HEADS * ORC_IDX_DIM);
+    for (int32_t q = 0; q < nq; q++) decode_query(q_idx, qfmt, q, qd + (int64_t)q * ORC_IDX_HEADS * ORC_IDX_DIM);
 #pragma omp parallel for schedule(dynamic, 1)
     for (int64_t item = 0; item < (int64_t)nq * nch; item++) {
         int32_t q = (int32_t)(item / nch);
@@ -379,14 +389,25 @@ static void index_full_any(const uint16_t* q_idx, const float* w, const void* k_
 void orc_index_full(const uint16_t* q_idx, const float* w, const uint16_t* k_idx, int64_t N, int32_t nq,
                     int32_t q_per_seq, const int32_t* n_visible, float* scores, int32_t block_size,
                     float* block_scores) {
-    index_full_any(q_idx, w, k_idx, 0, N, nq, q_per_seq, n_visible, scores, block_size, block_scores);
+    index_full_any(q_idx, 0, w, k_idx, 0, N, nq, q_per_seq, n_visible, scores, block_size, block_scores);
 }
 
 /* Full-mode scoring over the FP4 indexer-K cache ([N][68] entries). */
 void orc_index_full_fp4k(const uint16_t* q_idx, const float* w, const uint8_t* k_fp4, int64_t N, int32_t nq,
                          int32_t q_per_seq, const int32_t* n_visible, float* scores, int32_t block_size,
                          float* block_scores) {
-    index_full_any(q_idx, w, k_fp4, 1, N, nq, q_per_seq, n_visible, scores, block_size, block_scores);
+    index_full_any(q_idx, 0, w, k_fp4, 1, N, nq, q_per_seq, n_visible, scores, block_size, block_scores);
+}
+
+/* Full-mode scoring with both the indexer Q and the indexer K as MXFP4 entries
+ * ([EOG] 3.4: the indexer Q/K already ran in FP4 in the predecessor; entry
+ * format of orc_kidx_fp4_pack, one entry per query head): q_fp4 [nq][32][68],
+ * k_fp4 [nseq][N][68]. The score is the same formula over the decoded values,
+ * accumulated in double and stored as float. */
+void orc_index_full_fp4qk(const uint8_t* q_fp4, const float* w, const uint8_t* k_fp4, int64_t N, int32_t nq,
+                          int32_t q_per_seq, const int32_t* n_visible, float* scores, int32_t block_size,
+                          float* block_scores) {
+    index_full_any(q_fp4, 1, w, k_fp4, 1, N, nq, q_per_seq, n_visible, scores, block_size, block_scores);
 }
 
 /* Candidate pool ([EOG] 3.3): the chosen blocks' positions, in block order.
@@ -412,7 +433,7 @@ static void index_reindex_any(const uint16_t* q_idx, const float* w, const void*
         int64_t seq = q / q_per_seq;
         int64_t nv = n_visible ? n_visible[q] : N;
         if (nv > N) nv = N;
-        decode_query(q_idx + (int64_t)q * ORC_IDX_HEADS * ORC_IDX_DIM, qd);
+        decode_query(q_idx, 0, q, qd);
         const float* ww = w + (int64_t)q * ORC_IDX_HEADS;
         double kd[ORC_IDX_DIM];
         for (int64_t p = 0; p < pool_len; p++) {

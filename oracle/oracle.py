@@ -59,6 +59,7 @@ def lib():
         L.orc_fp4_unpack.argtypes = [vp, i64, vp]
         L.orc_index_full.argtypes = [vp, vp, vp, i64, i32, i32, vp, vp, i32, vp]
         L.orc_index_full_fp4k.argtypes = [vp, vp, vp, i64, i32, i32, vp, vp, i32, vp]
+        L.orc_index_full_fp4qk.argtypes = [vp, vp, vp, i64, i32, i32, vp, vp, i32, vp]
         L.orc_kidx_fp4_pack.argtypes = [vp, i64, vp]
         L.orc_kidx_fp4_unpack.argtypes = [vp, i64, vp]
         L.orc_index_reindex_fp4k.argtypes = [vp, vp, vp, i64, i32, i32, vp, vp, i64, vp]
@@ -139,10 +140,23 @@ def kidx_fp4_unpack(rec):
     return out
 
 
-def index_full(q_idx, w, k_idx, N, q_per_seq, n_visible=None, block_size=0, k_fp4=None):
+def index_full(q_idx, w, k_idx, N, q_per_seq, n_visible=None, block_size=0, k_fp4=None, q_fp4=None):
     """Full-mode indexer scores [nq, N] float32 (+ block maxima when block_size>0).
     The indexer K is bf16 `k_idx` [nseq, N, 128], or FP4 entries `k_fp4`
-    [nseq, N, 68] when given (then k_idx is ignored)."""
+    [nseq, N, 68] when given (then k_idx is ignored). With `q_fp4` [nq, 32, 68]
+    (MXFP4 indexer Q, one entry per head; eogee.com report 3.4: the indexer Q/K
+    ran in FP4) the query is read from those entries (q_idx is ignored) and the
+    K must be FP4 entries too."""
+    if q_fp4 is not None:
+        qq = _c(q_fp4, np.uint8).reshape(-1, IDX_HEADS * KIDX_RECORD_BYTES)
+        nq = qq.shape[0]
+        assert k_fp4 is not None, "the MXFP4-Q scoring reads FP4 K entries"
+        scores = np.zeros((nq, N), np.float32)
+        nb = (N + block_size - 1) // block_size if block_size > 0 else 0
+        blocks = np.zeros((nq, nb), np.float32) if block_size > 0 else None
+        lib().orc_index_full_fp4qk(_p(qq), _p(_c(w, np.float32)), _p(_c(k_fp4, np.uint8)), N, nq, q_per_seq,
+                                   _p(_c(n_visible, np.int32)), _p(scores), block_size, _p(blocks))
+        return (scores, blocks) if block_size > 0 else scores
     q = _c(q_idx, np.uint16)
     nq = q.shape[0]
     ww = _c(w, np.float32)

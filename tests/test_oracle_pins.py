@@ -645,6 +645,35 @@ def test_index_fp4k_is_the_score_formula_on_decoded_keys():
             assert ps[r, j] == exp or (np.isneginf(ps[r, j]) and np.isneginf(exp))
 
 
+def test_index_fp4qk_is_the_score_formula_on_decoded_query_and_keys():
+    """MXFP4 indexer Q and K (eogee.com report 3.4: the indexer Q/K ran in FP4):
+    the score is the formula on the decoded values of both, each decoded here
+    with the OCP table independently of the oracle."""
+    rng = np.random.default_rng(25)
+    nq, N = 4, 133
+    qf = O.kidx_fp4_pack(_rand_bf16(rng, (nq * 32, 128))).reshape(nq, 32, 68)
+    w = rng.uniform(0, 1, (nq, 32)).astype(np.float32)
+    w[1, 3] = -0.5  # a negative weight: w * ReLU, not ReLU(w * .)
+    kf = O.kidx_fp4_pack(_rand_bf16(rng, (2 * N, 128))).reshape(2, N, 68)
+    nv = np.array([133, 70, 0, 9], np.int32)
+    s, b = O.index_full(None, w, None, N, 2, n_visible=nv, block_size=8, k_fp4=kf, q_fp4=qf)
+    qd = _kidx_deq_independent(qf.reshape(-1, 68)).reshape(nq, 32, 128)
+    kd = _kidx_deq_independent(kf.reshape(-1, 68)).reshape(2, N, 128)
+    d = np.einsum("qhc,qnc->qhn", qd, kd[np.arange(nq) // 2])  # query q reads sequence q // 2
+    ref = np.einsum("qh,qhn->qn", w.astype(np.float64), np.maximum(d, 0.0))
+    for r in range(nq):
+        assert np.allclose(s[r, :nv[r]], ref[r, :nv[r]], rtol=1e-6, atol=1e-6)
+        assert np.all(np.isneginf(s[r, nv[r]:]))
+    pad = np.concatenate([s[0], np.full(136 - N, -np.inf, np.float32)])
+    assert np.array_equal(b[0], pad.reshape(17, 8).max(1))
+    # a query already on the MXFP4 grid packs losslessly, so its FP4 entries
+    # score exactly like the bf16 query through the bf16-Q scorer
+    qg = _bf16(qd.reshape(nq, 32, 128))
+    assert np.array_equal(O.kidx_fp4_pack(qg.reshape(-1, 128)), qf.reshape(-1, 68))
+    s_bf = O.index_full(qg, w, None, N, 2, n_visible=nv, k_fp4=kf)
+    assert np.array_equal(O.index_full(None, w, None, N, 2, n_visible=nv, k_fp4=kf, q_fp4=qf), s_bf)
+
+
 # ------------------------------------------------------- FP8 window rows
 
 def _ocp_mx_exp(amax):
