@@ -62,6 +62,8 @@ def load():
     L.csa2_index_prefill_topk_workspace_bytes.restype = sz
     L.csa2_index_prefill_topk.argtypes = [vp, vp, vp, i64, i32, i32, vp, i32, vp, vp, vp, sz, vp]
     L.csa2_index_prefill_topk_fp4k.argtypes = [vp, vp, vp, i64, i32, i32, vp, i32, vp, vp, vp, sz, vp]
+    L.csa2_index_full_fp4qk.argtypes = [vp, vp, vp, i64, i32, i32, vp, vp, i32, vp, vp]
+    L.csa2_index_prefill_topk_fp4qk.argtypes = [vp, vp, vp, i64, i32, i32, vp, i32, vp, vp, vp, sz, vp]
     L.csa2_index_reindex_topk_workspace_bytes.argtypes = [i32, i32, i32]
     L.csa2_index_reindex_topk_workspace_bytes.restype = sz
     L.csa2_index_reindex_topk.argtypes = [vp, vp, vp, i64, i32, i32, vp, vp, i32, i32, vp, vp, vp, sz, vp]
@@ -78,7 +80,7 @@ def load():
                  "swa_fp8_pack", "csa2_sparse_attn_fp8w", "csa2_index_topk", "csa2_index_topk_fp4k",
                  "csa2_index_topk_select", "csa2_index_topk_merge", "csa2_index_topk_merge_pool",
                  "csa2_index_reindex_topk", "csa2_index_reindex_topk_fp4k", "csa2_index_topk_noalloc", "csa2_index_prefill_topk",
-                 "csa2_index_prefill_topk_fp4k"]:
+                 "csa2_index_prefill_topk_fp4k", "csa2_index_full_fp4qk", "csa2_index_prefill_topk_fp4qk"]:
         getattr(L, name).restype = ctypes.c_int
     _lib = L
     return L
@@ -92,7 +94,7 @@ EXPORTS = ["csa2_format_version", "csa2_last_error", "fp4_kv_pack", "fp4_kv_unpa
            "csa2_index_topk_merge_pool", "csa2_index_reindex_topk_workspace_bytes",
            "csa2_index_reindex_topk", "csa2_index_reindex_topk_fp4k", "csa2_index_topk_noalloc_scratch_bytes",
            "csa2_index_topk_noalloc", "csa2_index_prefill_topk_workspace_bytes", "csa2_index_prefill_topk",
-           "csa2_index_prefill_topk_fp4k"]
+           "csa2_index_prefill_topk_fp4k", "csa2_index_full_fp4qk", "csa2_index_prefill_topk_fp4qk"]
 
 
 def _ptr(t):
@@ -159,6 +161,20 @@ def _k_args(k_idx, k_fp4):
     return _ptr(k_idx), ""
 
 
+def _q_args(q_idx, q_fp4, suffix):
+    """(pointer, query count, call suffix) of the indexer-Q operand: bf16 q_idx
+    [nq,32,128], or MXFP4 entries q_fp4 [nq,32,68] (then the K must be FP4 too)."""
+    if (q_idx is None) == (q_fp4 is None):
+        raise ValueError("pass exactly one of q_idx (bf16) and q_fp4 (uint8 [nq, 32, 68])")
+    if q_fp4 is None:
+        _need(q_idx, torch.bfloat16, "q_idx")
+        return _ptr(q_idx), q_idx.shape[0], suffix
+    _need(q_fp4, torch.uint8, "q_fp4")
+    if suffix != "_fp4k":
+        raise ValueError("an MXFP4 indexer Q pairs with FP4 indexer-K entries (k_fp4)")
+    return _ptr(q_fp4), q_fp4.numel() // (IDX_HEADS * KIDX_RECORD), "_fp4qk"
+
+
 def kidx_fp4_pack(x, out=None, stream=None):
     """bf16 [n,128] indexer keys -> uint8 [n,68] FP4 entries (OCP MXFP4: 64 code bytes + one E8M0
     scale per 32 channels)."""
@@ -183,20 +199,22 @@ def swa_fp8_pack(x, out=None, stream=None):
 
 
 def csa2_index_full(q_idx, w, k_idx, N, q_per_seq, n_visible=None, block_size=0, scores=None, block_scores=None,
-                    stream=None, k_fp4=None):
+                    stream=None, k_fp4=None, q_fp4=None):
     """Full-mode indexer scores [nq,N] fp32 (and block maxima [nq,ceil(N/8)] when block_size == 8).
-    The indexer K is bf16 `k_idx` [nseq,N,128], or FP4 entries `k_fp4` [nseq,N,68] (pass k_idx=None)."""
-    for t, dt, nm in [(q_idx, torch.bfloat16, "q_idx"), (w, torch.float32, "w"), (n_visible, torch.int32, "n_visible")]:
+    The indexer K is bf16 `k_idx` [nseq,N,128], or FP4 entries `k_fp4` [nseq,N,68] (pass k_idx=None);
+    with `q_fp4` [nq,32,68] (MXFP4 query entries, q_idx=None, k_fp4 required) the call is
+    csa2_index_full_fp4qk (prefill chunks: q_per_seq a multiple of 8)."""
+    for t, dt, nm in [(w, torch.float32, "w"), (n_visible, torch.int32, "n_visible")]:
         _need(t, dt, nm)
     kp, suffix = _k_args(k_idx, k_fp4)
-    nq = q_idx.shape[0]
-    dev = q_idx.device
+    qp, nq, suffix = _q_args(q_idx, q_fp4, suffix)
+    dev = w.device
     if scores is None:
         scores = torch.empty((nq, N), dtype=torch.float32, device=dev)
     if block_size and block_scores is None:
         block_scores = torch.empty((nq, (N + 7) // 8), dtype=torch.float32, device=dev)
     fn = getattr(load(), "csa2_index_full" + suffix)
-    _check(fn(_ptr(q_idx), _ptr(w), kp, N, nq, q_per_seq, _ptr(n_visible), _ptr(scores), block_size,
+    _check(fn(qp, _ptr(w), kp, N, nq, q_per_seq, _ptr(n_visible), _ptr(scores), block_size,
               _ptr(block_scores) if block_size else None, _stream(stream)), "csa2_index_full" + suffix)
     return (scores, block_scores) if block_size else scores
 
@@ -268,16 +286,16 @@ def csa2_index_prefill_topk_workspace_bytes(nq, N, k):
 
 
 def csa2_index_prefill_topk(q_idx, w, k_idx, N, q_per_seq, k, n_visible=None, top=None, scores=None, workspace=None,
-                            stream=None, k_fp4=None):
+                            stream=None, k_fp4=None, q_fp4=None):
     """Prefill-chunk scores fused with Top-k (q_per_seq a multiple of 8,
     k <= 512): int32 [nq,k]. `scores` [nq,N] fp32, when given, also receives
-    the score rows."""
-    for t, dt, nm in [(q_idx, torch.bfloat16, "q_idx"), (w, torch.float32, "w"), (n_visible, torch.int32, "n_visible"),
+    the score rows. `q_fp4` [nq,32,68] (with k_fp4) selects the MXFP4-Q call."""
+    for t, dt, nm in [(w, torch.float32, "w"), (n_visible, torch.int32, "n_visible"),
                       (scores, torch.float32, "scores"), (top, torch.int32, "top")]:
         _need(t, dt, nm)
     kp, suffix = _k_args(k_idx, k_fp4)
-    nq = q_idx.shape[0]
-    dev = q_idx.device
+    qp, nq, suffix = _q_args(q_idx, q_fp4, suffix)
+    dev = w.device
     if top is None:
         top = torch.empty((nq, k), dtype=torch.int32, device=dev)
     need = csa2_index_prefill_topk_workspace_bytes(nq, N, k)
@@ -285,7 +303,7 @@ def csa2_index_prefill_topk(q_idx, w, k_idx, N, q_per_seq, k, n_visible=None, to
         workspace = torch.empty((need,), dtype=torch.uint8, device=dev)
     wsb = workspace.numel() * workspace.element_size() if workspace is not None else 0
     fn = getattr(load(), "csa2_index_prefill_topk" + suffix)
-    _check(fn(_ptr(q_idx), _ptr(w), kp, N, nq, q_per_seq, _ptr(n_visible), k, _ptr(top), _ptr(scores),
+    _check(fn(qp, _ptr(w), kp, N, nq, q_per_seq, _ptr(n_visible), k, _ptr(top), _ptr(scores),
               _ptr(workspace), wsb, _stream(stream)), "csa2_index_prefill_topk" + suffix)
     return top
 

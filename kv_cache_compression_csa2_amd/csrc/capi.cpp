@@ -283,6 +283,43 @@ int csa2_index_prefill_topk_fp4k(const uint16_t* q_idx, const float* w, const ui
                              top_idx, scores, workspace, ws_bytes, stream);
 }
 
+int csa2_index_full_fp4qk(const uint8_t* q_fp4, const float* w, const uint8_t* k_fp4, int64_t N, int32_t nq,
+                          int32_t q_per_seq, const int32_t* n_visible, float* scores, int32_t block_size,
+                          float* block_scores, hipStream_t stream) {
+    const char* who = "csa2_index_full_fp4qk";
+    int rc = check_index_common(who, reinterpret_cast<const uint16_t*>(q_fp4), w, k_fp4, N, nq, q_per_seq);
+    if (rc) return rc;
+    if (q_per_seq % 8 != 0) return fail(CSA2_EINVAL, "%s: q_per_seq must be a multiple of 8", who);
+    if (nq > 0 && !scores) return fail(CSA2_EINVAL, "%s: null scores", who);
+    if (block_size != 0 && block_size != 8) return fail(CSA2_EINVAL, "%s: block_size must be 0 or 8", who);
+    if (block_size == 8 && nq > 0 && !block_scores)
+        return fail(CSA2_EINVAL, "%s: block_scores required when block_size == 8", who);
+    (void)hipGetLastError();
+    csa2::launch_index_full_fp4qk(q_fp4, w, k_fp4, N, nq, q_per_seq, n_visible, scores, block_size, block_scores,
+                                  stream);
+    return launched(who);
+}
+
+int csa2_index_prefill_topk_fp4qk(const uint8_t* q_fp4, const float* w, const uint8_t* k_fp4, int64_t N, int32_t nq,
+                                  int32_t q_per_seq, const int32_t* n_visible, int32_t k, int32_t* top_idx,
+                                  float* scores, void* workspace, size_t ws_bytes, hipStream_t stream) {
+    const char* who = "csa2_index_prefill_topk_fp4qk";
+    int rc = check_index_common(who, reinterpret_cast<const uint16_t*>(q_fp4), w, k_fp4, N, nq, q_per_seq);
+    if (rc) return rc;
+    if (q_per_seq % 8 != 0) return fail(CSA2_EINVAL, "%s: q_per_seq must be a multiple of 8", who);
+    if (k < 1 || k > 512) return fail(CSA2_EINVAL, "%s: k must be in [1, 512]", who);
+    if (!csa2::prefill_topk_fits(nq, N, k))
+        return fail(CSA2_EINVAL, "%s: N too large for this k (use csa2_index_full_fp4qk and csa2_topk)", who);
+    if (nq > 0 && !top_idx) return fail(CSA2_EINVAL, "%s: null top_idx", who);
+    const size_t need = csa2_index_prefill_topk_workspace_bytes(nq, N, k);
+    if (nq > 0 && need > 0 && (!workspace || ws_bytes < need))
+        return fail(CSA2_EWORKSPACE, "%s: workspace needs %zu bytes", who, need);
+    (void)hipGetLastError();
+    csa2::launch_index_prefill_topk_fp4qk(q_fp4, w, k_fp4, N, nq, q_per_seq, n_visible, k, top_idx, scores, workspace,
+                                          stream);
+    return launched(who);
+}
+
 size_t csa2_index_reindex_topk_workspace_bytes(int32_t nq, int32_t nb, int32_t k) {
     if (nq <= 0 || nb < 1 || nb > 65536 || k < 1 || k > CSA2_MAX_TOPK) return 0;
     return csa2::reindex_topk_workspace_bytes(nq, nb, k);

@@ -33,6 +33,7 @@
 #include <math.h>
 
 #include <algorithm>
+#include <type_traits>
 #include <mutex>
 
 #include "device_common.h"
@@ -575,6 +576,26 @@ struct PfPre<true> {
     float x;  // the block's E8M0 scale as a float
 };
 
+// kQ4 (MXFP4 Q and K): thread (entry tid/4, block tid%4) copies the block's 16
+// code bytes and its scale byte unchanged; nothing is decoded.
+struct PfPreQ4 {
+    uint4 v;
+    uint32_t sb;  // the block's E8M0 scale byte
+};
+constexpr int kPfRowQ4 = 80;  // LDS row of a raw MXFP4 entry: 64 code bytes, 4 scales, 12 pad
+
+typedef int i32x8 __attribute__((ext_vector_type(8)));
+
+// 32x32x64 MXFP4 x MXFP4 MFMA (gfx950 scaled f8f6f4, both operands E2M1): lane
+// l holds row / column l % 32 and 32 consecutive channels of one scale block,
+// whose E8M0 byte `sa` / `sb` it supplies; the result layout is that of the
+// 32x32 bf16 MFMA. Each product is exact and accumulates in fp32.
+CSA2_DEVINL f32x16 mfma32x32x64_fp4(uint4 a, uint4 b, uint32_t sa, uint32_t sb, f32x16 c) {
+    const i32x8 av = {(int)a.x, (int)a.y, (int)a.z, (int)a.w, 0, 0, 0, 0};
+    const i32x8 bv = {(int)b.x, (int)b.y, (int)b.z, (int)b.w, 0, 0, 0, 0};
+    return __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(av, bv, c, 4, 4, 0, (int)sa, 0, (int)sb);
+}
+
 // kSel: scoring fused with the per-query Top-k (k <= kPfSelK; the DeepSelect
 // selection eogee.com report 3.5 names, for the prefill chunk): no score row
 // is written. Each wave owns its 2 queries' candidate buffers in LDS (keys and
@@ -593,7 +614,12 @@ struct PfPre<true> {
 // indices when the row is one chunk, else (key, entry) candidates that the
 // Top-K merge combines. `scores`, when given, still receives the score row (a
 // checking aid).
-template <bool kFp4, bool kBlk, bool kSel>
+// kQ4: the indexer Q is MXFP4 too (one 68-byte entry per head, the K entry
+// format; eogee.com report 3.4: the indexer Q/K already ran in FP4), and the
+// contraction runs on the scaled FP4 MFMA straight from the stored codes:
+// 4 MFMAs of 32x32x64 per 32-entry group where bf16 operands take 16 of
+// 32x32x16, and the K tile is copied to LDS undecoded (80-byte rows).
+template <bool kFp4, bool kBlk, bool kSel, bool kQ4 = false>
 __global__ __launch_bounds__(256, 2) void index_prefill_kernel(
     const uint16_t* __restrict__ q_idx, const float* __restrict__ w, const void* __restrict__ k_idx, int64_t N,
     int32_t q_per_seq, const int32_t* __restrict__ n_visible, float* __restrict__ scores,
@@ -625,8 +651,29 @@ __global__ __launch_bounds__(256, 2) void index_prefill_kernel(
     nva = nva < N ? nva : N;
     nvb = nvb < N ? nvb : N;
 
+    static_assert(!kQ4 || kFp4, "MXFP4 Q pairs with MXFP4 K");
     bf16x8 aa[8], ab[8];
-    {
+    // kQ4: K-step s uses scale block 2s + half of head col_in_tile: 16 code
+    // bytes (dword loads: entries are 4-byte aligned) and the block's scale
+    uint4 qa4[2], qb4[2];
+    uint32_t qas[2], qbs[2];
+    if constexpr (kQ4) {
+        const uint8_t* q8 = reinterpret_cast<const uint8_t*>(q_idx);
+        const uint8_t* ea = q8 + (qa * kIdxHeads + col_in_tile) * kKRec;
+        const uint8_t* eb = q8 + (qb * kIdxHeads + col_in_tile) * kKRec;
+        const uint32_t sca = *reinterpret_cast<const uint32_t*>(ea + kIdxDim / 2);
+        const uint32_t scb = *reinterpret_cast<const uint32_t*>(eb + kIdxDim / 2);
+#pragma unroll
+        for (int st = 0; st < 2; st++) {
+            const int blk = 2 * st + half;
+            const uint32_t* ca = reinterpret_cast<const uint32_t*>(ea + 16 * blk);
+            const uint32_t* cb = reinterpret_cast<const uint32_t*>(eb + 16 * blk);
+            qa4[st] = make_uint4(ca[0], ca[1], ca[2], ca[3]);
+            qb4[st] = make_uint4(cb[0], cb[1], cb[2], cb[3]);
+            qas[st] = (sca >> (8 * blk)) & 0xFFu;
+            qbs[st] = (scb >> (8 * blk)) & 0xFFu;
+        }
+    } else {
         const uint4* sa = reinterpret_cast<const uint4*>(q_idx + (qa * kIdxHeads + col_in_tile) * kIdxDim) + half;
         const uint4* sb = reinterpret_cast<const uint4*>(q_idx + (qb * kIdxHeads + col_in_tile) * kIdxDim) + half;
 #pragma unroll
@@ -660,7 +707,7 @@ __global__ __launch_bounds__(256, 2) void index_prefill_kernel(
     // Tile loads into registers. bf16 K: 4 16-byte units per thread of the
     // 64 x 256 B tile. FP4 K: thread (entry tid/4, quarter tid%4) takes 16 code
     // bytes (32 channels, one scale block) and that block's scale.
-    using Pre = PfPre<kFp4>;
+    using Pre = std::conditional_t<kQ4, PfPreQ4, PfPre<kFp4>>;
     // The tile's first entry is uniform: a scalar base plus 32-bit lane offsets,
     // and rows past the sequence re-read its last entry (their scores are
     // never kept).
@@ -668,7 +715,13 @@ __global__ __launch_bounds__(256, 2) void index_prefill_kernel(
         Pre p;
         const int64_t t0 = e_begin + (int64_t)st * kPfSub;
         const int lim = (int)(N - 1 - t0 < kPfSub - 1 ? N - 1 - t0 : kPfSub - 1);
-        if constexpr (kFp4) {
+        if constexpr (kQ4) {
+            const int row = tid >> 2, qq = tid & 3;
+            const uint8_t* e = kfseq + t0 * kKRec + (uint32_t)((row < lim ? row : lim) * kKRec);
+            const uint32_t* src = reinterpret_cast<const uint32_t*>(e) + 4 * qq;
+            p.v = make_uint4(src[0], src[1], src[2], src[3]);
+            p.sb = e[kIdxDim / 2 + qq];
+        } else if constexpr (kFp4) {
             const int row = tid >> 2, qq = tid & 3;
             const uint8_t* e = kfseq + t0 * kKRec + (uint32_t)((row < lim ? row : lim) * kKRec);
             const uint32_t* src = reinterpret_cast<const uint32_t*>(e) + 4 * qq;
@@ -686,7 +739,11 @@ __global__ __launch_bounds__(256, 2) void index_prefill_kernel(
         return p;
     };
     auto lstore = [&](int buf, const Pre& p) {
-        if constexpr (kFp4) {
+        if constexpr (kQ4) {
+            const int row = tid >> 2, qq = tid & 3;
+            *reinterpret_cast<uint4*>(&lds[buf][row * kPfRowQ4 + 16 * qq]) = p.v;
+            lds[buf][row * kPfRowQ4 + kIdxDim / 2 + qq] = (uint8_t)p.sb;
+        } else if constexpr (kFp4) {
             const int row = tid >> 2, qq = tid & 3;
             uint8_t* dst = &lds[buf][row * kPfRow + qq * 64];
             const uint32_t c[4] = {p.v.x, p.v.y, p.v.z, p.v.w};
@@ -759,6 +816,27 @@ __global__ __launch_bounds__(256, 2) void index_prefill_kernel(
     // the shadow of these MFMAs.
     auto group = [&](int buf, int h2, f32x16& acca, f32x16& accb, const f32x16& pa, const f32x16& pb, int32_t pcol,
                      float (&out)[2]) {
+        if constexpr (kQ4) {
+            // entry h2*32 + col_in_tile: scale blocks 2s + half for K-steps s = 0, 1
+            const uint8_t* rowp = lds[buf] + (h2 * 32 + col_in_tile) * kPfRowQ4;
+            const uint4 b0 = *reinterpret_cast<const uint4*>(rowp + 16 * half);
+            const uint4 b1 = *reinterpret_cast<const uint4*>(rowp + 16 * (2 + half));
+            const uint32_t sc = *reinterpret_cast<const uint32_t*>(rowp + kIdxDim / 2);
+            const uint32_t s0 = (sc >> (8 * half)) & 0xFFu, s1 = (sc >> (8 * (2 + half))) & 0xFFu;
+            acca = mfma32x32x64_fp4(qa4[0], b0, qas[0], s0, f32x16{});
+            accb = mfma32x32x64_fp4(qb4[0], b0, qbs[0], s0, f32x16{});
+            acca = mfma32x32x64_fp4(qa4[1], b1, qas[1], s1, acca);
+            accb = mfma32x32x64_fp4(qb4[1], b1, qbs[1], s1, accb);
+            out[0] = head_sums(pa, pb, pcol);
+            out[1] = kBlk ? max8_lanes(out[0]) : 0.0f;
+            __builtin_amdgcn_sched_group_barrier(0x100, 3, 0);  // fragment reads first
+#pragma unroll
+            for (int i = 0; i < 4; i++) {
+                __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+                __builtin_amdgcn_sched_group_barrier(0x002, 16, 0);
+            }
+            return;
+        }
         const uint8_t* rowp = lds[buf] + (h2 * 32 + col_in_tile) * kPfRow + half * 16;
         bf16x8 bj[8];
 #pragma unroll
@@ -1104,6 +1182,39 @@ int launch_index_prefill_topk(const uint16_t* q_idx, const float* w, const void*
     else
         hipLaunchKernelGGL((index_prefill_kernel<false, false, true>), grid, dim3(256), 0, s, q_idx, w, k, N,
                            q_per_seq, n_visible, scores_dbg, (float*)nullptr, f.c, len, topk, out_idx, f.ck, f.cc);
+    if (f.c > 1) launch_topk_merge(nq, topk, f.c, f.ck, f.cc, out_idx, f.ck2, f.cc2, s);
+    return 0;
+}
+
+int launch_index_full_fp4qk(const uint8_t* q_fp4, const float* w, const uint8_t* k_fp4, int64_t N, int32_t nq,
+                            int32_t q_per_seq, const int32_t* n_visible, float* scores, int32_t block_size,
+                            float* block_scores, hipStream_t s) {
+    if (nq == 0) return 0;
+    float* bs = block_size > 0 ? block_scores : nullptr;
+    const int32_t nchunks = (int32_t)((N + kPfChunk - 1) / kPfChunk);
+    const dim3 grid((unsigned)((int64_t)(nq / kPfQueries) * nchunks));
+    const uint16_t* q = reinterpret_cast<const uint16_t*>(q_fp4);  // the kernel reads it as bytes
+    if (bs)
+        hipLaunchKernelGGL((index_prefill_kernel<true, true, false, true>), grid, dim3(256), 0, s, q, w, k_fp4, N,
+                           q_per_seq, n_visible, scores, bs, nchunks, (int64_t)kPfChunk, 0, (int32_t*)nullptr,
+                           (uint32_t*)nullptr, (int32_t*)nullptr);
+    else
+        hipLaunchKernelGGL((index_prefill_kernel<true, false, false, true>), grid, dim3(256), 0, s, q, w, k_fp4, N,
+                           q_per_seq, n_visible, scores, bs, nchunks, (int64_t)kPfChunk, 0, (int32_t*)nullptr,
+                           (uint32_t*)nullptr, (int32_t*)nullptr);
+    return 0;
+}
+
+int launch_index_prefill_topk_fp4qk(const uint8_t* q_fp4, const float* w, const uint8_t* k_fp4, int64_t N,
+                                    int32_t nq, int32_t q_per_seq, const int32_t* n_visible, int32_t topk,
+                                    int32_t* out_idx, float* scores_dbg, void* ws, hipStream_t s) {
+    if (nq == 0) return 0;
+    const FtWs f = ft_ws_chunks(ws, nq, prefill_topk_chunks(nq, N), topk);
+    const int64_t len = prefill_topk_chunk_len(nq, N);
+    const dim3 grid((unsigned)((int64_t)(nq / kPfQueries) * f.c));
+    hipLaunchKernelGGL((index_prefill_kernel<true, false, true, true>), grid, dim3(256), 0, s,
+                       reinterpret_cast<const uint16_t*>(q_fp4), w, k_fp4, N, q_per_seq, n_visible, scores_dbg,
+                       (float*)nullptr, f.c, len, topk, out_idx, f.ck, f.cc);
     if (f.c > 1) launch_topk_merge(nq, topk, f.c, f.ck, f.cc, out_idx, f.ck2, f.cc2, s);
     return 0;
 }

@@ -58,6 +58,16 @@ int launch_index_prefill_topk(const uint16_t* q_idx, const float* w, const void*
                               int32_t q_per_seq, const int32_t* n_visible, int32_t topk, int32_t* out_idx,
                               float* scores_dbg, void* ws, hipStream_t s);
 
+// MXFP4 indexer Q [nq][32][68] with MXFP4 K [nseq][N][68] on the scaled FP4
+// MFMA, for prefill chunks (q_per_seq a multiple of 8): scoring alone, and
+// scoring fused with the per-query Top-k (workspace as launch_index_prefill_topk).
+int launch_index_full_fp4qk(const uint8_t* q_fp4, const float* w, const uint8_t* k_fp4, int64_t N, int32_t nq,
+                            int32_t q_per_seq, const int32_t* n_visible, float* scores, int32_t block_size,
+                            float* block_scores, hipStream_t s);
+int launch_index_prefill_topk_fp4qk(const uint8_t* q_fp4, const float* w, const uint8_t* k_fp4, int64_t N,
+                                    int32_t nq, int32_t q_per_seq, const int32_t* n_visible, int32_t topk,
+                                    int32_t* out_idx, float* scores_dbg, void* ws, hipStream_t s);
+
 size_t topk_workspace_bytes(int32_t rows, int64_t ncols, int32_t k);
 // Merge of per-chunk Top-K candidates: rows x nchunks x k (key, column) pairs
 // in column order (unused slots key 0) -> out_idx [rows][k]. Above 16384

@@ -94,6 +94,31 @@ def test_index_fp4k_rejects(kw, frag):
 
 
 @pytest.mark.parametrize("kw,frag", [
+    (dict(N=0), "N must be"),
+    (dict(q_per_seq=1), "multiple of 8"),
+    (dict(nq=24, q_per_seq=12), "multiple of 8"),
+    (dict(q_per_seq=3), "divide"),
+    (dict(block_size=8, block=None), "block_scores"),
+    (dict(scores=None), "null scores"),
+    (dict(k=None), "null pointer"),
+    (dict(q=None), "null pointer"),
+])
+def test_index_fp4qk_rejects(kw, frag):
+    a = dict(q=P, w=P, k=P, N=100, nq=8, q_per_seq=8, scores=P, block_size=0, block=P)
+    a.update(kw)
+    L_ = K.load()
+    rc, msg = _err(L_.csa2_index_full_fp4qk(a["q"], a["w"], a["k"], a["N"], a["nq"], a["q_per_seq"], None,
+                                           a["scores"], a["block_size"], a["block"], S))
+    assert rc == L.CSA2_EINVAL and frag in msg and "fp4qk" in msg, msg
+    if "scores" not in kw and "block_size" not in kw:
+        rc, msg = _err(L_.csa2_index_prefill_topk_fp4qk(a["q"], a["w"], a["k"], a["N"], a["nq"], a["q_per_seq"], None,
+                                                       512, P, None, P, 1 << 30, S))
+        assert rc == L.CSA2_EINVAL and frag in msg and "fp4qk" in msg, msg
+    rc, msg = _err(L_.csa2_index_prefill_topk_fp4qk(P, P, P, 100, 8, 8, None, 513, P, None, P, 1 << 30, S))
+    assert rc == L.CSA2_EINVAL and "k must be" in msg
+
+
+@pytest.mark.parametrize("kw,frag", [
     (dict(block_size=16), "block_size"),
     (dict(nb=0), "nb must be"),
     (dict(nb=70000), "nb must be"),

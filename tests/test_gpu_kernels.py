@@ -194,6 +194,128 @@ def test_index_fp4k_decodes_every_code_and_scale_exactly(qps):
     assert np.array_equal(ref[1], np.maximum(v, 0).astype(np.float32))
 
 
+# ------------------------------------------- MXFP4 indexer Q and K
+
+
+def _fp4qk_inputs(nq, N, nseq, seed):
+    """bf16 queries and keys packed by the oracle's own packer into MXFP4
+    entries (one per query head / per key), and the GPU packer's query entries,
+    which must be the same bytes."""
+    q, w, k = _idx_inputs(nq, N, nseq, seed)
+    qf_host = O.kidx_fp4_pack(u16(q).reshape(-1, 128)).reshape(nq, 32, 68)
+    kf_host = O.kidx_fp4_pack(u16(k).reshape(-1, 128)).reshape(nseq, N, 68)
+    qf = K().kidx_fp4_pack(q.reshape(-1, 128)).reshape(nq, 32, 68)
+    torch.cuda.synchronize()
+    assert np.array_equal(np_(qf), qf_host)
+    return qf, qf_host, w, torch.tensor(kf_host, device=DEV), kf_host
+
+
+@pytest.mark.parametrize("nq,N,qps", [(8, 1000, 8), (16, 5003, 16), (24, 4096 * 2 + 100, 8), (8, 1, 8),
+                                      (8, 64, 8), (32, 4097, 32)])
+def test_index_full_fp4qk_matches_oracle(nq, N, qps):
+    """MXFP4 query and key entries on the scaled FP4 matrix instruction: scores
+    and block maxima within the score tolerance of the oracle (exact products,
+    fp32 sums), with causal-like visible lengths and ragged tails."""
+    print("case: index_full_fp4qk", nq, N, qps, flush=True)
+    qf, qf_host, w, kf, kf_host = _fp4qk_inputs(nq, N, nq // qps, 30 + N + nq)
+    rng = np.random.default_rng(N + 7)
+    nv = rng.integers(0, N + 1, nq).astype(np.int32)
+    nv[0] = N
+    s, b = K().csa2_index_full(None, w, None, N, qps, n_visible=dev_i32(nv, DEV), block_size=8, k_fp4=kf, q_fp4=qf)
+    s2 = K().csa2_index_full(None, w, None, N, qps, k_fp4=kf, q_fp4=qf)  # every entry visible, no blocks
+    torch.cuda.synchronize()
+    rs, rb = O.index_full(None, np_(w), None, N, qps, n_visible=nv, block_size=8, k_fp4=kf_host, q_fp4=qf_host)
+    ok, msg = rel_close(np_(s), rs)
+    assert ok, msg
+    ok, msg = rel_close(np_(b), rb)
+    assert ok, msg
+    ok, msg = rel_close(np_(s2), O.index_full(None, np_(w), None, N, qps, k_fp4=kf_host, q_fp4=qf_host))
+    assert ok, msg
+
+
+def test_index_fp4qk_products_exact_for_every_code_and_scale():
+    """Every E2M1 key code under every E8M0 scale byte 2..252 in every channel
+    position (as the FP4-K exhaustive test), against queries whose four blocks
+    carry different scales: head 0 is +1 in every channel with block scales
+    1, 2, 1/2, 4, head 1 is -1 everywhere. The score with w = (1, 1) is
+    v*m if v > 0 else -v, and with w = (1, 0) max(v*m, 0), for the decoded key
+    value v and the channel's block multiplier m: bit-exact."""
+    print("case: fp4qk exhaustive products", flush=True)
+    bs = np.arange(2, 253)
+    n = len(bs) * 16
+    i = np.arange(n)
+    b, c, ch = bs[i // 16], i % 16, i % 128
+    ent = np.zeros((n, 68), np.uint8)
+    ent[i, ch // 2] = (c << (4 * (ch % 2))).astype(np.uint8)
+    ent[:, 64:] = b[:, None].astype(np.uint8)
+    nq = 8
+    qent = np.zeros((nq, 32, 68), np.uint8)
+    qent[:, 0, :64] = 0x22          # code 2 = +1.0 in both nibbles
+    qent[:, 0, 64:] = [127, 128, 126, 129]
+    qent[:, 1, :64] = 0xAA          # code 10 = -1.0
+    qent[:, 1, 64:] = 127
+    qent[:, 2:, 64:] = 127          # zero codes elsewhere
+    w = torch.zeros((nq, 32), dtype=torch.float32)
+    w[:, 0] = 1.0
+    w[0::2, 1] = 1.0
+    s = K().csa2_index_full(None, w.to(DEV), None, n, nq, k_fp4=torch.tensor(ent[None], device=DEV),
+                            q_fp4=torch.tensor(qent, device=DEV))
+    torch.cuda.synchronize()
+    ref = O.index_full(None, np_(w), None, n, nq, k_fp4=ent[None], q_fp4=qent)
+    assert np.array_equal(np_(s), ref)
+    v = O.kidx_fp4_unpack(ent)[i, ch]
+    m = np.array([1.0, 2.0, 0.5, 4.0])[ch // 32]
+    assert np.array_equal(ref[0], np.where(v > 0, v * m, -v).astype(np.float32))
+    assert np.array_equal(ref[1], np.maximum(v * m, 0).astype(np.float32))
+
+
+def _fp4qk_exact_entries(n, rng):
+    """Random MXFP4 entries with scale bytes 126..127: every product of a
+    query and a key value is a multiple of 1/16 below 36 in magnitude, so with
+    power-of-two weights of at most 1 every score is exact in fp32."""
+    e = rng.integers(0, 256, (n, 68)).astype(np.uint8)
+    e[:, 64:] = rng.integers(126, 128, (n, 4))
+    return e
+
+
+@pytest.mark.parametrize("nq,qps,N,k", [(8, 8, 5003, 512), (16, 8, 70000, 512), (24, 24, 20000, 100),
+                                        (8, 8, 600, 512), (64, 64, 4096, 512)])
+def test_index_prefill_topk_fp4qk_bit_exact_on_exact_scores(nq, qps, N, k):
+    """Prefill scoring with MXFP4 Q and K fused with Top-k, on exact-score
+    entries: the selection equals the oracle's Top-K of the oracle's score row
+    (one chunk, several chunks, rows with fewer visible entries than k or none)."""
+    print("case: prefill_topk fp4qk exact", nq, qps, N, k, flush=True)
+    rng = np.random.default_rng(1500 + N + nq)
+    qf_host = _fp4qk_exact_entries(nq * 32, rng).reshape(nq, 32, 68)
+    kf_host = _fp4qk_exact_entries((nq // qps) * N, rng).reshape(nq // qps, N, 68)
+    w_host = np.exp2(rng.integers(-2, 1, (nq, 32))).astype(np.float32)
+    nv = rng.integers(N // 2, N + 1, nq).astype(np.int32)
+    nv[0], nv[-1], nv[1] = N, min(k // 2, N), 0
+    top = K().csa2_index_prefill_topk(None, torch.tensor(w_host, device=DEV), None, N, qps, k,
+                                      n_visible=dev_i32(nv, DEV), k_fp4=torch.tensor(kf_host, device=DEV),
+                                      q_fp4=torch.tensor(qf_host, device=DEV))
+    torch.cuda.synchronize()
+    rs = O.index_full(None, w_host, None, N, qps, n_visible=nv, k_fp4=kf_host, q_fp4=qf_host)
+    assert np.array_equal(np_(top), O.topk(rs, k, row_len=nv))
+
+
+def test_index_prefill_topk_fp4qk_matches_the_unfused_path():
+    """Random MXFP4 entries at the prefill chunk's row length: the fused call's
+    debug score rows equal csa2_index_full_fp4qk's bit for bit, and its
+    selection is csa2_topk of that row with the causal row lengths."""
+    print("case: prefill_topk fp4qk random", flush=True)
+    nq, N, k = 64, 65536, 512
+    qf, _, w, kf, _ = _fp4qk_inputs(nq, N, 1, 1600)
+    nv = dev_i32(np.arange(N - nq + 1, N + 1), DEV)
+    sc = torch.empty((nq, N), dtype=torch.float32, device=DEV)
+    top = K().csa2_index_prefill_topk(None, w, None, N, nq, k, n_visible=nv, scores=sc, k_fp4=kf, q_fp4=qf)
+    ref_sc = K().csa2_index_full(None, w, None, N, nq, n_visible=nv, k_fp4=kf, q_fp4=qf)
+    ref_top = K().csa2_topk(ref_sc, k, row_len=nv)
+    torch.cuda.synchronize()
+    assert torch.equal(sc, ref_sc)
+    assert torch.equal(top, ref_top)
+
+
 def test_index_reindex_fp4k_matches_oracle():
     print("case: reindex fp4k", flush=True)
     nq, N, nb = 3, 9000, 300
