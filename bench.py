@@ -16,7 +16,11 @@ A step is one pass of the whole hot path over one batch of synthetic input:
       K as FP4 entries (68 B) packed from the same kind of bf16 keys before
       timing;
   encoder64k_fp4k_fp8w / decode1m_fp4k_fp8w : the same with the window KV
-      as FP8 rows (528 B) as well: both of the pages' cache precisions.
+      as FP8 rows (528 B) as well: both of the pages' cache precisions;
+  prefill128k_fp4k : the prefill step over FP4 indexer-K entries;
+  prefill128k_fp4qk : the same with the indexer Q in MXFP4 too (the step
+      packs the bf16 query into one entry per head, then scores on the
+      scaled FP4 matrix instruction).
 In every decode step (one query per sequence) the Full layer's scoring and
 Top-512 run fused (csa2_index_topk: scoring with a per-chunk Top-512 in one
 launch, the chunks' merge in a second; no score row is written); the prefill
@@ -45,8 +49,14 @@ sys.path.insert(0, ROOT)
 
 HBM_PEAK_GBS = 8000.0       # MI355X HBM3E
 BF16_PEAK_TFLOPS = 2500.0   # MI355X dense bf16 MFMA
+FP4_PEAK_TFLOPS = 10100.0   # MI355X dense fp4 MFMA
 METRIC = "CSA2 decode queries/s + HBM GB/s at 64K/1M ctx; prefill indexer TFLOP/s"
 HEADLINE = "encoder64k"
+
+
+def query_bytes(wl):
+    """One query's indexer Q: 32 x 128 bf16, or 32 MXFP4 entries of 68 B."""
+    return 32 * 68 if wl.qfmt == "fp4" else 32 * 128 * 2
 
 
 def alg_bytes_index_full(wl):
@@ -57,7 +67,7 @@ def alg_bytes_index_full(wl):
     row = 68 if wl.kfmt == "fp4" else 256
     kbytes = (wl.N * row * wl.nseq) if wl.q_per_seq > 1 else n_vis * row
     out = wl.nq * wl.N * 4 + (wl.nq * ((wl.N + 7) // 8) * 4 if wl.hier else 0)
-    return kbytes + out + wl.nq * (32 * 128 * 2 + 32 * 4)
+    return kbytes + out + wl.nq * (query_bytes(wl) + 32 * 4)
 
 
 def fused_chunks(nq, N):
@@ -76,10 +86,10 @@ def alg_bytes_index_topk(wl, k=512):
     n_vis = wl.N * wl.nq if wl.n_visible is None else int(wl.n_visible.sum().item())
     row = 68 if wl.kfmt == "fp4" else 256
     if wl.q_per_seq > 1:  # prefill: one chunk per row at the benchmark's shapes
-        return wl.N * row * wl.nseq + wl.nq * k * 4 + wl.nq * (32 * 128 * 2 + 32 * 4)
+        return wl.N * row * wl.nseq + wl.nq * k * 4 + wl.nq * (query_bytes(wl) + 32 * 4)
     c = fused_chunks(wl.nq, wl.N)
     out = wl.nq * k * (8 * c if c > 1 else 4) + (wl.nq * ((wl.N + 7) // 8) * 4 if wl.hier else 0)
-    return n_vis * row + out + wl.nq * (32 * 128 * 2 + 32 * 4)
+    return n_vis * row + out + wl.nq * (query_bytes(wl) + 32 * 4)
 
 
 def alg_flops_index_full(wl):
@@ -208,12 +218,17 @@ def bench_workload(name, steps, warmup, nsets, torch):
         t = Timer(torch)
         for i in range(warmup + steps):
             with t.span("index_full" if i >= warmup else "warm"):
-                L.csa2_index_full(wl0.q_idx[0], wl0.w[0], kb, wl0.N, wl0.q_per_seq, wl0.n_visible, 0, st.scores,
-                                  k_fp4=kf)
+                if st.qf is not None:  # the MXFP4 query the step packed
+                    L.csa2_index_full(None, wl0.w[0], kb, wl0.N, wl0.q_per_seq, wl0.n_visible, 0, st.scores,
+                                      k_fp4=kf, q_fp4=st.qf)
+                else:
+                    L.csa2_index_full(wl0.q_idx[0], wl0.w[0], kb, wl0.N, wl0.q_per_seq, wl0.n_visible, 0, st.scores,
+                                      k_fp4=kf)
         torch.cuda.synchronize()
         t_sc = t.summary()["index_full"][2] * 1e-3
         res["scoring_only_ms"] = t_sc * 1e3
         res["scoring_only_TFLOPs"] = alg_flops_index_full(wl) / t_sc / 1e12
+        res["_mfma_dtype"] = "fp4" if wl.qfmt == "fp4" else "bf16"
     del sets
     torch.cuda.empty_cache()
     return res
@@ -365,6 +380,17 @@ def target_rooflines(res, sweep):
             "call": "csa2_index_full", "ms": round(p["scoring_only_ms"], 4),
             "mfma_busy": float(f["mfma_busy_scoring_only"]) if "mfma_busy_scoring_only" in f else None,
             "clock_ghz": float(f["clock_ghz_scoring_only"]) if "clock_ghz_scoring_only" in f else None}
+    for pn, dt in [("prefill128k_fp4k", "bf16"), ("prefill128k_fp4qk", "fp4")]:
+        # the same indexer figure at the pages' FP4 indexer-K precision (bf16
+        # products), and with the indexer Q in MXFP4 too (fp4 products)
+        if pn in res:
+            p = res[pn]
+            peak = FP4_PEAK_TFLOPS if dt == "fp4" else BF16_PEAK_TFLOPS
+            t["prefill_indexer_" + pn.split("_", 1)[1]] = {
+                "bound": "mfma", "achieved": round(p["scoring_only_TFLOPs"], 1), "peak": peak, "unit": "TFLOP/s",
+                "frac": round(p["scoring_only_TFLOPs"] / peak, 4), "target_frac": 0.50, "mfma_dtype": dt,
+                "call": "csa2_index_full" + ("_fp4qk" if dt == "fp4" else "_fp4k"),
+                "ms": round(p["scoring_only_ms"], 4)}
     if "decode1m" in res:
         d = res["decode1m"]
         gbs = d["_alg_bytes_step"] / (d["ms_per_step"] * 1e-3) / 1e9
@@ -382,7 +408,8 @@ def main():
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--workloads",
                     default="encoder64k,decoder256k,decode1m,prefill128k,encoder_group64k,decoder_group256k,"
-                            "encoder64k_fp4k,decode1m_fp4k,encoder64k_fp4k_fp8w,decode1m_fp4k_fp8w")
+                            "encoder64k_fp4k,decode1m_fp4k,encoder64k_fp4k_fp8w,decode1m_fp4k_fp8w,"
+                            "prefill128k_fp4k,prefill128k_fp4qk")
     ap.add_argument("--attn-sweep", default="64,256,1024")
     ap.add_argument("--no-cpu", action="store_true")
     ap.add_argument("--calibrate-copy", action="store_true",
@@ -408,7 +435,7 @@ def main():
     res = {}
     for n in names:
         print("bench: %s ..." % n, file=sys.stderr, flush=True)
-        res[n] = bench_workload(n, args.steps, args.warmup, 1 if n in ("prefill128k", "tiny") else 4, torch)
+        res[n] = bench_workload(n, args.steps, args.warmup, 1 if n.startswith("prefill") or n == "tiny" else 4, torch)
         print("bench: %s %.4f ms/step" % (n, res[n]["ms_per_step"]), file=sys.stderr, flush=True)
     sweep = {}
     for nq in [int(x) for x in args.attn_sweep.split(",") if x]:
@@ -432,18 +459,22 @@ def main():
     for n, r in res.items():
         e = {k: (round(v, 4) if isinstance(v, float) else v) for k, v in r.items() if not k.startswith("_")}
         extra[n] = e
-    if "prefill128k" in res:
+    for pn in [n for n in res if n.startswith("prefill")]:
         # the prefill indexer figure: the chunk's scoring flops over the time of
         # csa2_index_full (scoring alone, score row written); the step runs the
-        # fused scoring + Top-512 call, reported beside it
-        p = res["prefill128k"]
-        e = extra["prefill128k"]
+        # fused scoring + Top-512 call, reported beside it. The peak is that of
+        # the matrix instruction's own operand type (bf16, or fp4 for MXFP4 Q x K).
+        p = res[pn]
+        e = extra[pn]
+        dt = p["_mfma_dtype"]
+        peak = FP4_PEAK_TFLOPS if dt == "fp4" else BF16_PEAK_TFLOPS
         tf = p["scoring_only_TFLOPs"]
         e["indexer_TFLOPs"] = round(tf, 2)
-        e["indexer_frac_of_bf16_peak"] = round(tf / BF16_PEAK_TFLOPS, 4)
+        e["indexer_mfma_dtype"] = dt
+        e["indexer_frac_of_%s_peak" % dt] = round(tf / peak, 4)
         if "index_topk_TFLOPs" in p:
             e["fused_indexer_TFLOPs"] = round(p["index_topk_TFLOPs"], 2)
-            e["fused_indexer_frac_of_bf16_peak"] = round(p["index_topk_TFLOPs"] / BF16_PEAK_TFLOPS, 4)
+            e["fused_indexer_frac_of_%s_peak" % dt] = round(p["index_topk_TFLOPs"] / peak, 4)
     extra["attn_gather_sweep"] = {k: {kk: round(vv, 4) for kk, vv in v.items()} for k, v in sweep.items()}
     extra["targets"] = target_rooflines(res, sweep)
     line = {

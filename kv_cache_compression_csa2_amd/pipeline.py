@@ -59,6 +59,12 @@ class Step:
         # prefill chunk: scoring fused with the Top-512 (8 queries of a sequence per workgroup)
         self.prefill_fused = not self.fused and wl.q_per_seq % 8 == 0 and not wl.hier
         self.ws_pf = ws(L.csa2_index_prefill_topk_workspace_bytes(nq, N, TOPK)) if self.prefill_fused else None
+        # MXFP4 indexer Q (prefill chunks with FP4 K): packed inside the step from the bf16 query
+        self.qf = None
+        if wl.qfmt == "fp4":
+            if not (self.prefill_fused and wl.kfmt == "fp4"):
+                raise ValueError("an MXFP4 indexer Q is scored by the prefill-chunk call over FP4 K entries")
+            self.qf = torch.empty((nq, L.IDX_HEADS, L.KIDX_RECORD), dtype=torch.uint8, device=device)
         self.debug_scores = False
         self.fused_reindex = True
         self.ws_rt = ws(L.csa2_index_reindex_topk_workspace_bytes(nq, POOL_BLOCKS, TOPK)) if wl.hier else None
@@ -93,9 +99,14 @@ class Step:
     def index_prefill_topk(self, k):
         wl = self.wl
         kb, kf = self._k(k)
-        L.csa2_index_prefill_topk(wl.q_idx[0], wl.w[0], kb, wl.N, wl.q_per_seq, TOPK, n_visible=wl.n_visible,
+        qb, qf = (None, self.qf) if self.qf is not None else (wl.q_idx[0], None)
+        L.csa2_index_prefill_topk(qb, wl.w[0], kb, wl.N, wl.q_per_seq, TOPK, n_visible=wl.n_visible,
                                   top=self.top[0], scores=self.scores if self.debug_scores else None,
-                                  workspace=self.ws_pf, k_fp4=kf)
+                                  workspace=self.ws_pf, k_fp4=kf, q_fp4=qf)
+
+    def pack_query(self):
+        """The Full layer's bf16 indexer query -> one MXFP4 entry per head."""
+        L.kidx_fp4_pack(self.wl.q_idx[0].reshape(-1, L.IDX_DIM), out=self.qf.view(-1, L.KIDX_RECORD))
 
     def full_layer(self, k, sp):
         """The Full layer's scoring and Top-512 (+ the 2048-block pool)."""
@@ -111,6 +122,9 @@ class Step:
                 with sp("topk_merge"):
                     self.index_topk(k, "merge")
         elif self.prefill_fused:
+            if self.qf is not None:
+                with sp("q_pack"):
+                    self.pack_query()
             with sp("index_topk"):
                 self.index_prefill_topk(k)
         else:

@@ -33,6 +33,11 @@ timing):
 
   encoder64k_fp4k_fp8w, decode1m_fp4k_fp8w.
 
+The prefill chunk with the indexer K in FP4 (prefill128k_fp4k), and with the
+indexer Q in FP4 as well (prefill128k_fp4qk; eogee.com report 3.4: the
+predecessor already trained the indexer Q/K in FP4): the step itself packs
+the Full layer's bf16 query into one MXFP4 entry per head before scoring.
+
 Layer groups that share one cache (eogee.com report 3.2: an encoder cache
 serves a Full layer and the Reuse layers after it; a decoder cache serves a
 Reindex layer and Reuse layers), timed as layer sequences:
@@ -75,6 +80,10 @@ CONFIGS = {
                                  planted=8, prefill=False, kfmt="fp4", swa_fmt="fp8"),
     "decode1m_fp4k_fp8w": dict(nq=8, N=1048576, q_per_seq=1, hier=True, seed=10, kv="clustered", kidx="clustered",
                                planted=0, prefill=False, kfmt="fp4", swa_fmt="fp8"),
+    "prefill128k_fp4k": dict(nq=4096, N=65536, q_per_seq=4096, hier=False, seed=11, kv="random", kidx="normal",
+                             planted=0, prefill=True, kfmt="fp4"),
+    "prefill128k_fp4qk": dict(nq=4096, N=65536, q_per_seq=4096, hier=False, seed=12, kv="random", kidx="normal",
+                              planted=0, prefill=True, kfmt="fp4", qfmt="fp4"),
 }
 
 # Norm given to a planted main-KV row before packing: about twice the RMS norm
@@ -121,6 +130,7 @@ class Workload:
     group: str = None  # None, "encoder" (Full + 5 Reuse) or "decoder" (Reindex + 3 Reuse)
     kfmt: str = "bf16"  # indexer-K cache precision the step reads: "bf16" or "fp4" (68 B entries)
     swa_fmt: str = "bf16"  # window-KV precision the step reads: "bf16" or "fp8" (528 B rows)
+    qfmt: str = "bf16"  # Full-layer indexer-Q precision: "bf16", or "fp4" (the step packs MXFP4 entries per head)
     q_idx: list = field(default_factory=list)  # per indexer layer: bf16 [nq,32,128]
     w: list = field(default_factory=list)  # per indexer layer: f32 [nq,32]
     k_idx: torch.Tensor = None  # bf16 [nseq,N,128]
@@ -193,7 +203,7 @@ def make_workload(name, device="cpu", seed=None, nq=None, N=None):
     nseq = nq // q_per_seq
     swa_T = (nq + WINDOW - 1) if c["prefill"] else WINDOW
     wl = Workload(name, nq, N, q_per_seq, nseq, c["hier"], swa_T, c.get("group"), c.get("kfmt", "bf16"),
-                  c.get("swa_fmt", "bf16"))
+                  c.get("swa_fmt", "bf16"), c.get("qfmt", "bf16"))
     s = 0
 
     def nxt():

@@ -15,8 +15,8 @@ import bench  # noqa: E402
 class _Wl:
     """The shape fields bench's accounting reads from a workload."""
 
-    def __init__(self, nq, N, hier, n_index_layers, n_attn_layers, kfmt="bf16", q_per_seq=1):
-        self.nq, self.N, self.hier, self.kfmt, self.q_per_seq = nq, N, hier, kfmt, q_per_seq
+    def __init__(self, nq, N, hier, n_index_layers, n_attn_layers, kfmt="bf16", q_per_seq=1, qfmt="bf16"):
+        self.nq, self.N, self.hier, self.kfmt, self.q_per_seq, self.qfmt = nq, N, hier, kfmt, q_per_seq, qfmt
         self.nseq = nq // q_per_seq
         self.n_visible = None
         self.n_index_layers, self.n_attn_layers = n_index_layers, n_attn_layers
@@ -30,6 +30,15 @@ def test_attention_bytes_and_flops_per_query_layer():
     assert bench.alg_bytes_attn(1024) == 1024 * 411648
     # FP8 window rows: 128 x 528 B
     assert bench.alg_bytes_attn(1, window_row=528) == 512 * 288 + 128 * 528 + 2 * 65536 + 2048
+
+
+def test_prefill_fused_scoring_bytes_with_mxfp4_query():
+    # one sequence of 65536 FP4 key entries read once, 4096 x 512 ids written,
+    # per query 32 MXFP4 entries (68 B) of indexer Q and 32 fp32 weights
+    wl = _Wl(4096, 65536, False, 1, 1, kfmt="fp4", q_per_seq=4096, qfmt="fp4")
+    assert bench.alg_bytes_index_topk(wl) == 65536 * 68 + 4096 * 512 * 4 + 4096 * (32 * 68 + 128)
+    wl.qfmt = "bf16"
+    assert bench.alg_bytes_index_topk(wl) == 65536 * 68 + 4096 * 512 * 4 + 4096 * (8192 + 128)
 
 
 def test_headline_fused_scoring_bytes_per_launch():

@@ -10,10 +10,11 @@ Protocol per workload:
   4. attention of every layer: GPU attention on the oracle's indices within
      1e-2 * max|ref| of the oracle's.
 Samples: every query of the tiny and 64K workloads, the queries of 2
-sequences at 256K and 1M, 64 strided queries of the prefill chunk. The FP4
+sequences at 256K and 1M, 64 strided queries of the prefill chunks. The FP4
 indexer-K workloads also check the GPU's packed entries of the sampled
 sequences against the oracle's packing byte for byte, and score with the
-oracle's own entries; the FP8 window workloads do the same for every
+oracle's own entries; the MXFP4 indexer-Q workload does the same for the
+sampled queries' entries; the FP8 window workloads do the same for every
 attention layer's window rows.
 """
 import math
@@ -33,7 +34,7 @@ SCALE = 1.0 / math.sqrt(512.0)
 def _sample(wl):
     if wl.name in ("tiny", "encoder64k", "encoder_group64k", "encoder64k_fp4k", "encoder64k_fp4k_fp8w"):
         return list(range(wl.nq))
-    if wl.name == "prefill128k":
+    if wl.name.startswith("prefill"):
         return list(range(0, wl.nq, wl.nq // 64))
     return [0, wl.nq - 1] if wl.name.startswith("decode1m") else [0, 17]
 
@@ -83,7 +84,8 @@ def _kv_for(qsub_seq, kvrows, N):
 
 @pytest.mark.parametrize("name", ["tiny", "encoder64k", "decoder256k", "prefill128k", "decode1m",
                                   "encoder_group64k", "decoder_group256k", "encoder64k_fp4k", "decode1m_fp4k",
-                                  "encoder64k_fp4k_fp8w", "decode1m_fp4k_fp8w"])
+                                  "encoder64k_fp4k_fp8w", "decode1m_fp4k_fp8w", "prefill128k_fp4k",
+                                  "prefill128k_fp4qk"])
 def test_workload_parity(name):
     import kv_cache_compression_csa2_amd as K
     from kv_cache_compression_csa2_amd.pipeline import Step, pack_workload_kv, workload_kidx
@@ -117,10 +119,18 @@ def test_workload_parity(name):
         assert np.array_equal(np_(kk[seq_t]), kf_sub)
         print("  indexer-K FP4 entries bit-exact", flush=True)
 
+    qf_sub = None
+    if wl.qfmt == "fp4":
+        # the oracle packs the sampled queries' indexer Q itself; the step's
+        # MXFP4 query entries must be the same bytes
+        qf_sub = O.kidx_fp4_pack(u16(wl.q_idx[0][qt]).reshape(-1, 128)).reshape(len(Qs), 32, O.KIDX_RECORD_BYTES)
+        assert np.array_equal(np_(step.qf[qt]), qf_sub)
+        print("  indexer-Q MXFP4 entries bit-exact", flush=True)
+
     # 1. Full-layer scores
     bs = 8 if wl.hier else 0
-    r = O.index_full(u16(wl.q_idx[0][qt]), np_(wl.w[0][qt]), k_sub, wl.N, qps_sub, n_visible=nv, block_size=bs,
-                     k_fp4=kf_sub)
+    r = O.index_full(None if qf_sub is not None else u16(wl.q_idx[0][qt]), np_(wl.w[0][qt]), k_sub, wl.N, qps_sub,
+                     n_visible=nv, block_size=bs, k_fp4=kf_sub, q_fp4=qf_sub)
     rs, rb = (r if wl.hier else (r, None))
     ok, msg = rel_close(np_(step.scores[qt]), rs)
     assert ok, "scores: " + msg
