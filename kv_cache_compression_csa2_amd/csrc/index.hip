@@ -556,10 +556,11 @@ constexpr int kPfRow = 256 + 16;       // padded LDS row bytes
 constexpr int kPfChunk = 4096;         // entries per workgroup (scores written out)
 constexpr int kPfSelK = 512;           // largest k of the fused prefill selection
 constexpr int kPfBuf = 960;            // candidate slots per query (a multiple of 64; 2 workgroups fit a CU)
-constexpr int kPfHigh = kPfBuf - 64;   // compact before a tile's 64 entries could overflow
+constexpr int kPfBufQ4 = 896;          // the same for the MXFP4 Q x K variant (3 workgroups fit a CU)
 constexpr int kPfLow = kPfSelK + 128;  // buffers at or below this are left alone in a round
 constexpr int kPfSlack = 64;           // a round's compaction may keep up to k + kPfSlack (<= kPfLow)
 static_assert(kPfSelK + kPfSlack <= kPfLow, "a compacted buffer must stay out of the next round");
+static_assert(kPfBufQ4 - 64 > kPfLow && kPfBufQ4 % 64 == 0, "room for a tile after a compaction");
 constexpr int64_t kPfMaxChunk = 65536; // entry offsets within a chunk fit 16 bits
 
 // Registers of one prefill tile load: bf16 K 4 units of 16 bytes per thread;
@@ -625,11 +626,15 @@ __global__ __launch_bounds__(256, 2) void index_prefill_kernel(
     int32_t q_per_seq, const int32_t* __restrict__ n_visible, float* __restrict__ scores,
     float* __restrict__ block_scores, int32_t nchunks, int64_t chunk_len, int32_t k, int32_t* __restrict__ out_idx,
     uint32_t* __restrict__ cand_key, int32_t* __restrict__ cand_col) {
-    __shared__ __attribute__((aligned(16))) uint8_t lds[2][kPfSub * kPfRow];
+    // candidate slots per query: the MXFP4 variant's smaller tiles and buffers
+    // (53 KB with the selection) leave room for a third workgroup per CU
+    constexpr int kBuf = kQ4 ? kPfBufQ4 : kPfBuf;
+    constexpr int kHigh = kBuf - 64;  // compact before a tile's 64 entries could overflow
+    __shared__ __attribute__((aligned(16))) uint8_t lds[2][kPfSub * (kQ4 ? kPfRowQ4 : kPfRow)];
     // kSel: candidate keys and entry offsets of the workgroup's 8 queries, and
     // each wave's "a buffer is nearly full" flag per tile parity
-    __shared__ uint32_t bkey[kSel ? kPfQueries : 1][kSel ? kPfBuf : 1];
-    __shared__ uint16_t bid[kSel ? kPfQueries : 1][kSel ? kPfBuf : 1];
+    __shared__ uint32_t bkey[kSel ? kPfQueries : 1][kSel ? kBuf : 1];
+    __shared__ uint16_t bid[kSel ? kPfQueries : 1][kSel ? kBuf : 1];
     __shared__ __attribute__((aligned(16))) uint32_t full_flag[2][4];
     const int b = blockIdx.x;
     int chunk, qg;
@@ -878,7 +883,7 @@ __global__ __launch_bounds__(256, 2) void index_prefill_kernel(
         if (more) lstore((st + 1) & 1, nxt);
         if constexpr (kSel) {
             // 64 more entries per query arrive before the next barrier
-            if (lane == 0) full_flag[st & 1][wave] = (uint32_t)(max(na, nb) > (uint32_t)kPfHigh);
+            if (lane == 0) full_flag[st & 1][wave] = (uint32_t)(max(na, nb) > (uint32_t)kHigh);
         }
         lds_barrier();
         // After the last tile this reads the stale buffer; those results are never stored.
@@ -890,10 +895,10 @@ __global__ __launch_bounds__(256, 2) void index_prefill_kernel(
                 // a compaction round: every wave compacts its fuller buffers
                 if (na > (uint32_t)kPfLow)
                     ta = tk::key_score(
-                        tk::wave_keep_topk<kPfBuf>(bkey[slot_a], bid[slot_a], na, (uint32_t)k, (uint32_t)kPfSlack, na));
+                        tk::wave_keep_topk<kBuf>(bkey[slot_a], bid[slot_a], na, (uint32_t)k, (uint32_t)kPfSlack, na));
                 if (nb > (uint32_t)kPfLow)
                     tb = tk::key_score(
-                        tk::wave_keep_topk<kPfBuf>(bkey[slot_b], bid[slot_b], nb, (uint32_t)k, (uint32_t)kPfSlack, nb));
+                        tk::wave_keep_topk<kBuf>(bkey[slot_b], bid[slot_b], nb, (uint32_t)k, (uint32_t)kPfSlack, nb));
             }
         }
         store(out[0], out[1], col0 + 32);
@@ -904,7 +909,7 @@ __global__ __launch_bounds__(256, 2) void index_prefill_kernel(
         for (int h = 0; h < 2; h++) {
             const int slot = h ? slot_b : slot_a;
             uint32_t n = h ? nb : na;
-            if (n > (uint32_t)k) tk::wave_keep_topk<kPfBuf>(bkey[slot], bid[slot], n, (uint32_t)k, 0u, n);  // exact: n = k
+            if (n > (uint32_t)k) tk::wave_keep_topk<kBuf>(bkey[slot], bid[slot], n, (uint32_t)k, 0u, n);  // exact: n = k
             const int64_t q = h ? qb : qa;
             if (nchunks == 1) {
                 for (int i = lane; i < k; i += 64) out_idx[q * k + i] = i < (int)n ? (int32_t)(e_begin + bid[slot][i]) : -1;
@@ -1150,31 +1155,37 @@ int launch_index_reindex_topk(const uint16_t* q_idx, const float* w, const void*
 // workgroup (fewest candidates, fewest compactions), cut into more chunks
 // only when the batch would leave fewer than 512 workgroups (chunks of at
 // least 4096 entries, multiples of the 64-entry tile).
-int64_t prefill_topk_chunk_len(int32_t nq, int64_t N) {
+int64_t prefill_topk_chunk_len(int32_t nq, int64_t N, bool q4) {
     const int64_t groups = nq / kPfQueries > 0 ? nq / kPfQueries : 1;
     int64_t nch = (N + kPfMaxChunk - 1) / kPfMaxChunk;
-    const int64_t want = std::min((512 + groups - 1) / groups, (N + 4095) / 4096);
+    // workgroups wanted: 512 (two per CU) for bf16 products; the MXFP4 variant
+    // holds three per CU and wants two full rounds of them
+    const int64_t wgs = q4 ? 1536 : 512;
+    const int64_t want = std::min((wgs + groups - 1) / groups, (N + 4095) / 4096);
     nch = nch > want ? nch : want;
     const int64_t len = (N + nch - 1) / nch;
     return (len + kPfSub - 1) / kPfSub * kPfSub;
 }
-int32_t prefill_topk_chunks(int32_t nq, int64_t N) {
-    const int64_t len = prefill_topk_chunk_len(nq, N);
+int32_t prefill_topk_chunks(int32_t nq, int64_t N, bool q4) {
+    const int64_t len = prefill_topk_chunk_len(nq, N, q4);
     return (int32_t)((N + len - 1) / len);
 }
 bool prefill_topk_fits(int32_t nq, int64_t N, int32_t k) {
-    return k >= 1 && k <= kPfSelK && chunks_fit(prefill_topk_chunks(nq, N), k);
+    return k >= 1 && k <= kPfSelK && chunks_fit(prefill_topk_chunks(nq, N, false), k) &&
+           chunks_fit(prefill_topk_chunks(nq, N, true), k);
 }
+// one workspace size serves both variants
 size_t prefill_topk_workspace_bytes(int32_t nq, int64_t N, int32_t k) {
-    return chunks_workspace_bytes(nq, prefill_topk_chunks(nq, N), k);
+    return std::max(chunks_workspace_bytes(nq, prefill_topk_chunks(nq, N, false), k),
+                    chunks_workspace_bytes(nq, prefill_topk_chunks(nq, N, true), k));
 }
 
 int launch_index_prefill_topk(const uint16_t* q_idx, const float* w, const void* k, bool kfp4, int64_t N, int32_t nq,
                               int32_t q_per_seq, const int32_t* n_visible, int32_t topk, int32_t* out_idx,
                               float* scores_dbg, void* ws, hipStream_t s) {
     if (nq == 0) return 0;
-    const FtWs f = ft_ws_chunks(ws, nq, prefill_topk_chunks(nq, N), topk);
-    const int64_t len = prefill_topk_chunk_len(nq, N);
+    const FtWs f = ft_ws_chunks(ws, nq, prefill_topk_chunks(nq, N, false), topk);
+    const int64_t len = prefill_topk_chunk_len(nq, N, false);
     const dim3 grid((unsigned)((int64_t)(nq / kPfQueries) * f.c));
     if (kfp4)
         hipLaunchKernelGGL((index_prefill_kernel<true, false, true>), grid, dim3(256), 0, s, q_idx, w, k, N,
@@ -1209,8 +1220,8 @@ int launch_index_prefill_topk_fp4qk(const uint8_t* q_fp4, const float* w, const 
                                     int32_t nq, int32_t q_per_seq, const int32_t* n_visible, int32_t topk,
                                     int32_t* out_idx, float* scores_dbg, void* ws, hipStream_t s) {
     if (nq == 0) return 0;
-    const FtWs f = ft_ws_chunks(ws, nq, prefill_topk_chunks(nq, N), topk);
-    const int64_t len = prefill_topk_chunk_len(nq, N);
+    const FtWs f = ft_ws_chunks(ws, nq, prefill_topk_chunks(nq, N, true), topk);
+    const int64_t len = prefill_topk_chunk_len(nq, N, true);
     const dim3 grid((unsigned)((int64_t)(nq / kPfQueries) * f.c));
     hipLaunchKernelGGL((index_prefill_kernel<true, false, true, true>), grid, dim3(256), 0, s,
                        reinterpret_cast<const uint16_t*>(q_fp4), w, k_fp4, N, q_per_seq, n_visible, scores_dbg,
