@@ -391,6 +391,11 @@ def target_rooflines(res, sweep):
                 "frac": round(p["scoring_only_TFLOPs"] / peak, 4), "target_frac": 0.50, "mfma_dtype": dt,
                 "call": "csa2_index_full" + ("_fp4qk" if dt == "fp4" else "_fp4k"),
                 "ms": round(p["scoring_only_ms"], 4)}
+            if dt == "fp4":
+                f = profile_fields("index_prefill_prefill128k_mfma.md", KERNEL_SOURCES)
+                e = t["prefill_indexer_" + pn.split("_", 1)[1]]
+                e["mfma_busy"] = float(f["mfma_busy_fp4qk_scoring_only"]) if "mfma_busy_fp4qk_scoring_only" in f else None
+                e["clock_ghz"] = float(f["clock_ghz_fp4qk_scoring_only"]) if "clock_ghz_fp4qk_scoring_only" in f else None
     if "decode1m" in res:
         d = res["decode1m"]
         gbs = d["_alg_bytes_step"] / (d["ms_per_step"] * 1e-3) / 1e9
