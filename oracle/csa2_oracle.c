@@ -424,7 +424,7 @@ void orc_pool_ids(const int32_t* blocks, int32_t nq, int32_t nb, int32_t block_s
 /* Reindex-mode scoring ([TIT] Reindex mode; [EOG] 3.3 later indexers score only
  * inside the pool): the layer's own (Q_idx, w) over the shared indexer K, for
  * the pool positions only. Positions whose id is -1 or not visible score -inf. */
-static void index_reindex_any(const uint16_t* q_idx, const float* w, const void* k_idx, int kfmt, int64_t N,
+static void index_reindex_any(const void* q_idx, int qfmt, const float* w, const void* k_idx, int kfmt, int64_t N,
                               int32_t nq, int32_t q_per_seq, const int32_t* n_visible, const int32_t* pool,
                               int64_t pool_len, float* pool_scores) {
 #pragma omp parallel for schedule(dynamic, 1)
@@ -433,7 +433,7 @@ static void index_reindex_any(const uint16_t* q_idx, const float* w, const void*
         int64_t seq = q / q_per_seq;
         int64_t nv = n_visible ? n_visible[q] : N;
         if (nv > N) nv = N;
-        decode_query(q_idx, 0, q, qd);
+        decode_query(q_idx, qfmt, q, qd);
         const float* ww = w + (int64_t)q * ORC_IDX_HEADS;
         double kd[ORC_IDX_DIM];
         for (int64_t p = 0; p < pool_len; p++) {
@@ -451,14 +451,22 @@ static void index_reindex_any(const uint16_t* q_idx, const float* w, const void*
 void orc_index_reindex(const uint16_t* q_idx, const float* w, const uint16_t* k_idx, int64_t N, int32_t nq,
                        int32_t q_per_seq, const int32_t* n_visible, const int32_t* pool, int64_t pool_len,
                        float* pool_scores) {
-    index_reindex_any(q_idx, w, k_idx, 0, N, nq, q_per_seq, n_visible, pool, pool_len, pool_scores);
+    index_reindex_any(q_idx, 0, w, k_idx, 0, N, nq, q_per_seq, n_visible, pool, pool_len, pool_scores);
 }
 
 /* Reindex-mode scoring over the FP4 indexer-K cache. */
 void orc_index_reindex_fp4k(const uint16_t* q_idx, const float* w, const uint8_t* k_fp4, int64_t N, int32_t nq,
                             int32_t q_per_seq, const int32_t* n_visible, const int32_t* pool, int64_t pool_len,
                             float* pool_scores) {
-    index_reindex_any(q_idx, w, k_fp4, 1, N, nq, q_per_seq, n_visible, pool, pool_len, pool_scores);
+    index_reindex_any(q_idx, 0, w, k_fp4, 1, N, nq, q_per_seq, n_visible, pool, pool_len, pool_scores);
+}
+
+/* Reindex-mode scoring with the indexer Q and K both as MXFP4 entries
+ * (q_fp4 [nq][32][68], as orc_index_full_fp4qk). */
+void orc_index_reindex_fp4qk(const uint8_t* q_fp4, const float* w, const uint8_t* k_fp4, int64_t N, int32_t nq,
+                             int32_t q_per_seq, const int32_t* n_visible, const int32_t* pool, int64_t pool_len,
+                             float* pool_scores) {
+    index_reindex_any(q_fp4, 1, w, k_fp4, 1, N, nq, q_per_seq, n_visible, pool, pool_len, pool_scores);
 }
 
 typedef struct {

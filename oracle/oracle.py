@@ -60,6 +60,7 @@ def lib():
         L.orc_index_full.argtypes = [vp, vp, vp, i64, i32, i32, vp, vp, i32, vp]
         L.orc_index_full_fp4k.argtypes = [vp, vp, vp, i64, i32, i32, vp, vp, i32, vp]
         L.orc_index_full_fp4qk.argtypes = [vp, vp, vp, i64, i32, i32, vp, vp, i32, vp]
+        L.orc_index_reindex_fp4qk.argtypes = [vp, vp, vp, i64, i32, i32, vp, vp, i64, vp]
         L.orc_kidx_fp4_pack.argtypes = [vp, i64, vp]
         L.orc_kidx_fp4_unpack.argtypes = [vp, i64, vp]
         L.orc_index_reindex_fp4k.argtypes = [vp, vp, vp, i64, i32, i32, vp, vp, i64, vp]
@@ -183,13 +184,20 @@ def pool_ids(blocks, block_size):
     return out
 
 
-def index_reindex(q_idx, w, k_idx, N, q_per_seq, pool, n_visible=None, k_fp4=None):
+def index_reindex(q_idx, w, k_idx, N, q_per_seq, pool, n_visible=None, k_fp4=None, q_fp4=None):
     """Reindex-mode scores over pool positions [nq, pool_len] float32 (FP4
-    indexer K from `k_fp4` when given)."""
-    q = _c(q_idx, np.uint16)
-    nq = q.shape[0]
+    indexer K from `k_fp4` when given; MXFP4 indexer Q from `q_fp4`
+    [nq, 32, 68] when given, which needs the FP4 K)."""
     pl = _c(pool, np.int32)
     out = np.zeros(pl.shape, np.float32)
+    if q_fp4 is not None:
+        assert k_fp4 is not None, "the MXFP4-Q scoring reads FP4 K entries"
+        qq = _c(q_fp4, np.uint8).reshape(-1, IDX_HEADS * KIDX_RECORD_BYTES)
+        lib().orc_index_reindex_fp4qk(_p(qq), _p(_c(w, np.float32)), _p(_c(k_fp4, np.uint8)), N, qq.shape[0],
+                                      q_per_seq, _p(_c(n_visible, np.int32)), _p(pl), pl.shape[1], _p(out))
+        return out
+    q = _c(q_idx, np.uint16)
+    nq = q.shape[0]
     if k_fp4 is not None:
         lib().orc_index_reindex_fp4k(_p(q), _p(_c(w, np.float32)), _p(_c(k_fp4, np.uint8)), N, nq, q_per_seq,
                                      _p(_c(n_visible, np.int32)), _p(pl), pl.shape[1], _p(out))

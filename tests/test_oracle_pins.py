@@ -672,6 +672,18 @@ def test_index_fp4qk_is_the_score_formula_on_decoded_query_and_keys():
     assert np.array_equal(O.kidx_fp4_pack(qg.reshape(-1, 128)), qf.reshape(-1, 68))
     s_bf = O.index_full(qg, w, None, N, 2, n_visible=nv, k_fp4=kf)
     assert np.array_equal(O.index_full(None, w, None, N, 2, n_visible=nv, k_fp4=kf, q_fp4=qf), s_bf)
+    # Reindex with the MXFP4 query: the independent numpy scores at the pool's
+    # positions (-inf for padding and invisible ones), queries of sequence q // 2
+    pool = np.stack([(np.arange(0, 160) * 7 + 3 * r) % N for r in range(nq)]).astype(np.int32)
+    pool[2, 4] = -1
+    ps = O.index_reindex(None, w, None, N, 2, pool, n_visible=nv, k_fp4=kf, q_fp4=qf)
+    for r in range(nq):
+        for j in range(pool.shape[1]):
+            i = pool[r, j]
+            if i < 0 or i >= nv[r]:
+                assert np.isneginf(ps[r, j])
+            else:
+                assert abs(ps[r, j] - ref[r, i]) <= 1e-6 * max(1.0, abs(ref[r, i]))
 
 
 # ------------------------------------------------------- FP8 window rows
