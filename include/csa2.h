@@ -315,22 +315,42 @@ int csa2_index_prefill_topk_fp4k(const uint16_t* q_idx, const float* w, const ui
                                  float* scores, void* workspace, size_t ws_bytes, hipStream_t stream);
 
 /*
- * csa2_index_full_fp4qk / csa2_index_prefill_topk_fp4qk -- csa2_index_full and
- * csa2_index_prefill_topk for a prefill chunk with the indexer Q in FP4 as
- * well (eogee.com report 3.4: the predecessor model already trained the
- * indexer Q and K in FP4): q_fp4 [nq][32][68] holds one MXFP4 entry per query
- * head, in the indexer-K entry format (kidx_fp4_pack of the [nq * 32][128]
- * bf16 query), and k_fp4 [nseq][N][68] the FP4 indexer K. The score is
- * sum_h w[q][h] * max(q_h . k, 0) over the decoded values of both entries:
- * E2M1 products times their two blocks' 2^(b - 127), exact, accumulated in
- * fp32 on the gfx950 scaled FP4 matrix instruction. q_per_seq must be a
- * multiple of 8 (EINVAL otherwise); every other argument, output, workspace
- * and error rule is that of the bf16-Q call. Caller-owned device buffers;
- * nothing is allocated.
+ * The *_fp4qk calls -- every indexer call with the indexer Q in FP4 as well
+ * (eogee.com report 3.4: the predecessor model already trained the indexer Q
+ * and K in FP4): q_fp4 [nq][32][68] holds one MXFP4 entry per query head, in
+ * the indexer-K entry format (kidx_fp4_pack of the [nq * 32][128] bf16
+ * query), in place of the bf16 q_idx, and the indexer K is the FP4 cache
+ * k_fp4 [nseq][N][68]. The score is sum_h w[q][h] * max(q_h . k, 0) over the
+ * decoded values of both entries: E2M1 products times their two blocks'
+ * 2^(b - 127), exact, accumulated in fp32 on the gfx950 scaled FP4 matrix
+ * instruction (no decode step). Every other argument, output, workspace and
+ * error rule is that of the matching _fp4k call:
+ *   csa2_index_full_fp4qk          csa2_index_full_fp4k
+ *   csa2_index_reindex_fp4qk       csa2_index_reindex_fp4k
+ *   csa2_index_topk_fp4qk          csa2_index_topk_fp4k (decode, fused Top-K)
+ *   csa2_index_topk_select_fp4qk   its first launch alone (as csa2_index_topk_select;
+ *                                  csa2_index_topk_merge finishes it)
+ *   csa2_index_reindex_topk_fp4qk  csa2_index_reindex_topk_fp4k
+ *   csa2_index_prefill_topk_fp4qk  csa2_index_prefill_topk_fp4k (q_per_seq a multiple of 8)
+ * Caller-owned device buffers; nothing is allocated.
  */
 int csa2_index_full_fp4qk(const uint8_t* q_fp4, const float* w, const uint8_t* k_fp4, int64_t N, int32_t nq,
                           int32_t q_per_seq, const int32_t* n_visible, float* scores, int32_t block_size,
                           float* block_scores, hipStream_t stream);
+int csa2_index_reindex_fp4qk(const uint8_t* q_fp4, const float* w, const uint8_t* k_fp4, int64_t N, int32_t nq,
+                             int32_t q_per_seq, const int32_t* n_visible, const int32_t* cand_blocks, int32_t nb,
+                             int32_t block_size, float* pool_scores, int32_t* pool_ids, hipStream_t stream);
+int csa2_index_topk_fp4qk(const uint8_t* q_fp4, const float* w, const uint8_t* k_fp4, int64_t N, int32_t nq,
+                          const int32_t* n_visible, int32_t k, int32_t* top_idx, int32_t block_size,
+                          float* block_scores, float* scores, void* workspace, size_t ws_bytes, hipStream_t stream);
+int csa2_index_topk_select_fp4qk(const uint8_t* q_fp4, const float* w, const uint8_t* k_fp4, int64_t N, int32_t nq,
+                                 const int32_t* n_visible, int32_t k, int32_t* top_idx, int32_t block_size,
+                                 float* block_scores, float* scores, void* workspace, size_t ws_bytes,
+                                 hipStream_t stream);
+int csa2_index_reindex_topk_fp4qk(const uint8_t* q_fp4, const float* w, const uint8_t* k_fp4, int64_t N, int32_t nq,
+                                  int32_t q_per_seq, const int32_t* n_visible, const int32_t* cand_blocks, int32_t nb,
+                                  int32_t k, int32_t* top_idx, float* pool_scores, void* workspace, size_t ws_bytes,
+                                  hipStream_t stream);
 int csa2_index_prefill_topk_fp4qk(const uint8_t* q_fp4, const float* w, const uint8_t* k_fp4, int64_t N, int32_t nq,
                                   int32_t q_per_seq, const int32_t* n_visible, int32_t k, int32_t* top_idx,
                                   float* scores, void* workspace, size_t ws_bytes, hipStream_t stream);

@@ -63,6 +63,10 @@ def load():
     L.csa2_index_prefill_topk.argtypes = [vp, vp, vp, i64, i32, i32, vp, i32, vp, vp, vp, sz, vp]
     L.csa2_index_prefill_topk_fp4k.argtypes = [vp, vp, vp, i64, i32, i32, vp, i32, vp, vp, vp, sz, vp]
     L.csa2_index_full_fp4qk.argtypes = [vp, vp, vp, i64, i32, i32, vp, vp, i32, vp, vp]
+    L.csa2_index_reindex_fp4qk.argtypes = [vp, vp, vp, i64, i32, i32, vp, vp, i32, i32, vp, vp, vp]
+    L.csa2_index_topk_fp4qk.argtypes = [vp, vp, vp, i64, i32, vp, i32, vp, i32, vp, vp, vp, sz, vp]
+    L.csa2_index_topk_select_fp4qk.argtypes = [vp, vp, vp, i64, i32, vp, i32, vp, i32, vp, vp, vp, sz, vp]
+    L.csa2_index_reindex_topk_fp4qk.argtypes = [vp, vp, vp, i64, i32, i32, vp, vp, i32, i32, vp, vp, vp, sz, vp]
     L.csa2_index_prefill_topk_fp4qk.argtypes = [vp, vp, vp, i64, i32, i32, vp, i32, vp, vp, vp, sz, vp]
     L.csa2_index_reindex_topk_workspace_bytes.argtypes = [i32, i32, i32]
     L.csa2_index_reindex_topk_workspace_bytes.restype = sz
@@ -80,7 +84,9 @@ def load():
                  "swa_fp8_pack", "csa2_sparse_attn_fp8w", "csa2_index_topk", "csa2_index_topk_fp4k",
                  "csa2_index_topk_select", "csa2_index_topk_merge", "csa2_index_topk_merge_pool",
                  "csa2_index_reindex_topk", "csa2_index_reindex_topk_fp4k", "csa2_index_topk_noalloc", "csa2_index_prefill_topk",
-                 "csa2_index_prefill_topk_fp4k", "csa2_index_full_fp4qk", "csa2_index_prefill_topk_fp4qk"]:
+                 "csa2_index_prefill_topk_fp4k", "csa2_index_full_fp4qk", "csa2_index_prefill_topk_fp4qk",
+                 "csa2_index_reindex_fp4qk", "csa2_index_topk_fp4qk", "csa2_index_topk_select_fp4qk",
+                 "csa2_index_reindex_topk_fp4qk"]:
         getattr(L, name).restype = ctypes.c_int
     _lib = L
     return L
@@ -94,7 +100,9 @@ EXPORTS = ["csa2_format_version", "csa2_last_error", "fp4_kv_pack", "fp4_kv_unpa
            "csa2_index_topk_merge_pool", "csa2_index_reindex_topk_workspace_bytes",
            "csa2_index_reindex_topk", "csa2_index_reindex_topk_fp4k", "csa2_index_topk_noalloc_scratch_bytes",
            "csa2_index_topk_noalloc", "csa2_index_prefill_topk_workspace_bytes", "csa2_index_prefill_topk",
-           "csa2_index_prefill_topk_fp4k", "csa2_index_full_fp4qk", "csa2_index_prefill_topk_fp4qk"]
+           "csa2_index_prefill_topk_fp4k", "csa2_index_full_fp4qk", "csa2_index_prefill_topk_fp4qk",
+           "csa2_index_reindex_fp4qk", "csa2_index_topk_fp4qk", "csa2_index_topk_select_fp4qk",
+           "csa2_index_reindex_topk_fp4qk"]
 
 
 def _ptr(t):
@@ -203,7 +211,7 @@ def csa2_index_full(q_idx, w, k_idx, N, q_per_seq, n_visible=None, block_size=0,
     """Full-mode indexer scores [nq,N] fp32 (and block maxima [nq,ceil(N/8)] when block_size == 8).
     The indexer K is bf16 `k_idx` [nseq,N,128], or FP4 entries `k_fp4` [nseq,N,68] (pass k_idx=None);
     with `q_fp4` [nq,32,68] (MXFP4 query entries, q_idx=None, k_fp4 required) the call is
-    csa2_index_full_fp4qk (prefill chunks: q_per_seq a multiple of 8)."""
+    csa2_index_full_fp4qk."""
     for t, dt, nm in [(w, torch.float32, "w"), (n_visible, torch.int32, "n_visible")]:
         _need(t, dt, nm)
     kp, suffix = _k_args(k_idx, k_fp4)
@@ -224,19 +232,19 @@ def csa2_index_topk_workspace_bytes(nq, N, k):
 
 
 def csa2_index_topk(q_idx, w, k_idx, N, k, n_visible=None, block_size=0, top=None, block_scores=None,
-                    scores=None, workspace=None, stream=None, k_fp4=None, stage="both"):
+                    scores=None, workspace=None, stream=None, k_fp4=None, stage="both", q_fp4=None):
     """Full-mode scores fused with Top-k (decode, one query per sequence):
     int32 [nq,k] (and block maxima [nq,ceil(N/8)] when block_size == 8).
     `scores` [nq,N] fp32, when given, also receives the score rows.
     stage: "both" (complete), "select" (scoring + per-chunk selection, the
     candidates stay in `workspace`) or "merge" (completes a "select" call
-    with the same top/workspace; the other inputs are ignored)."""
-    for t, dt, nm in [(q_idx, torch.bfloat16, "q_idx"), (w, torch.float32, "w"), (n_visible, torch.int32, "n_visible"),
-                      (scores, torch.float32, "scores")]:
+    with the same top/workspace; the other inputs are ignored). `q_fp4`
+    [nq,32,68] (with k_fp4, q_idx=None) selects the MXFP4-Q calls."""
+    for t, dt, nm in [(w, torch.float32, "w"), (n_visible, torch.int32, "n_visible"), (scores, torch.float32, "scores")]:
         _need(t, dt, nm)
     kp, suffix = _k_args(k_idx, k_fp4)
-    nq = q_idx.shape[0]
-    dev = q_idx.device
+    qp, nq, suffix = _q_args(q_idx, q_fp4, suffix)
+    dev = w.device
     if top is None:
         top = torch.empty((nq, k), dtype=torch.int32, device=dev)
     if block_size and block_scores is None:
@@ -251,12 +259,13 @@ def csa2_index_topk(q_idx, w, k_idx, N, k, n_visible=None, block_size=0, top=Non
         return top
     args = (N, nq, _ptr(n_visible), k, _ptr(top), block_size, _ptr(block_scores) if block_size else None,
             _ptr(scores), _ptr(workspace), wsb, _stream(stream))
-    if stage == "select":
-        _check(load().csa2_index_topk_select(_ptr(q_idx), _ptr(w), kp, 1 if suffix else 0, *args),
-               "csa2_index_topk_select")
+    if stage == "select" and suffix == "_fp4qk":
+        _check(load().csa2_index_topk_select_fp4qk(qp, _ptr(w), kp, *args), "csa2_index_topk_select_fp4qk")
+    elif stage == "select":
+        _check(load().csa2_index_topk_select(qp, _ptr(w), kp, 1 if suffix else 0, *args), "csa2_index_topk_select")
     else:
         fn = getattr(load(), "csa2_index_topk" + suffix)
-        _check(fn(_ptr(q_idx), _ptr(w), kp, *args), "csa2_index_topk" + suffix)
+        _check(fn(qp, _ptr(w), kp, *args), "csa2_index_topk" + suffix)
     return (top, block_scores) if block_size else top
 
 
@@ -336,21 +345,23 @@ def csa2_index_topk_noalloc(q_idx, w, k_idx, N, k, n_visible=None, block_size=0,
 
 
 def csa2_index_reindex(q_idx, w, k_idx, N, q_per_seq, cand_blocks, n_visible=None, block_size=8, pool_scores=None,
-                       pool_ids=None, want_ids=True, stream=None, k_fp4=None):
+                       pool_ids=None, want_ids=True, stream=None, k_fp4=None, q_fp4=None):
     """Reindex-mode scores over the pool [nq, nb*8] fp32 (+ entry ids [nq, nb*8] int32).
-    The indexer K is bf16 `k_idx`, or FP4 entries `k_fp4` (pass k_idx=None)."""
-    for t, dt, nm in [(q_idx, torch.bfloat16, "q_idx"), (w, torch.float32, "w"),
-                      (cand_blocks, torch.int32, "cand_blocks"), (n_visible, torch.int32, "n_visible")]:
+    The indexer K is bf16 `k_idx`, or FP4 entries `k_fp4` (pass k_idx=None); `q_fp4`
+    [nq,32,68] (with k_fp4, q_idx=None) selects csa2_index_reindex_fp4qk."""
+    for t, dt, nm in [(w, torch.float32, "w"), (cand_blocks, torch.int32, "cand_blocks"),
+                      (n_visible, torch.int32, "n_visible")]:
         _need(t, dt, nm)
     kp, suffix = _k_args(k_idx, k_fp4)
+    qp, _, suffix = _q_args(q_idx, q_fp4, suffix)
     nq, nb = cand_blocks.shape
-    dev = q_idx.device
+    dev = w.device
     if pool_scores is None:
         pool_scores = torch.empty((nq, nb * block_size), dtype=torch.float32, device=dev)
     if want_ids and pool_ids is None:
         pool_ids = torch.empty((nq, nb * block_size), dtype=torch.int32, device=dev)
     fn = getattr(load(), "csa2_index_reindex" + suffix)
-    _check(fn(_ptr(q_idx), _ptr(w), kp, N, nq, q_per_seq, _ptr(n_visible), _ptr(cand_blocks), nb, block_size,
+    _check(fn(qp, _ptr(w), kp, N, nq, q_per_seq, _ptr(n_visible), _ptr(cand_blocks), nb, block_size,
               _ptr(pool_scores), _ptr(pool_ids), _stream(stream)), "csa2_index_reindex" + suffix)
     return pool_scores, pool_ids
 
@@ -360,17 +371,18 @@ def csa2_index_reindex_topk_workspace_bytes(nq, nb, k):
 
 
 def csa2_index_reindex_topk(q_idx, w, k_idx, N, q_per_seq, cand_blocks, k, n_visible=None, top=None,
-                            pool_scores=None, workspace=None, stream=None, k_fp4=None):
+                            pool_scores=None, workspace=None, stream=None, k_fp4=None, q_fp4=None):
     """Reindex-mode scores over the pool fused with the Top-k: int32 [nq, k]
     entry ids (csa2_topk of csa2_index_reindex's pool row through its ids).
-    `pool_scores` [nq, nb*8] fp32, when given, also receives the pool row."""
-    for t, dt, nm in [(q_idx, torch.bfloat16, "q_idx"), (w, torch.float32, "w"),
-                      (cand_blocks, torch.int32, "cand_blocks"), (n_visible, torch.int32, "n_visible"),
-                      (pool_scores, torch.float32, "pool_scores")]:
+    `pool_scores` [nq, nb*8] fp32, when given, also receives the pool row.
+    `q_fp4` [nq,32,68] (with k_fp4, q_idx=None) selects the MXFP4-Q call."""
+    for t, dt, nm in [(w, torch.float32, "w"), (cand_blocks, torch.int32, "cand_blocks"),
+                      (n_visible, torch.int32, "n_visible"), (pool_scores, torch.float32, "pool_scores")]:
         _need(t, dt, nm)
     kp, suffix = _k_args(k_idx, k_fp4)
+    qp, _, suffix = _q_args(q_idx, q_fp4, suffix)
     nq, nb = cand_blocks.shape
-    dev = q_idx.device
+    dev = w.device
     if top is None:
         top = torch.empty((nq, k), dtype=torch.int32, device=dev)
     need = csa2_index_reindex_topk_workspace_bytes(nq, nb, k)
@@ -378,7 +390,7 @@ def csa2_index_reindex_topk(q_idx, w, k_idx, N, q_per_seq, cand_blocks, k, n_vis
         workspace = torch.empty((need,), dtype=torch.uint8, device=dev)
     wsb = workspace.numel() * workspace.element_size() if workspace is not None else 0
     fn = getattr(load(), "csa2_index_reindex_topk" + suffix)
-    _check(fn(_ptr(q_idx), _ptr(w), kp, N, nq, q_per_seq, _ptr(n_visible), _ptr(cand_blocks), nb, k, _ptr(top),
+    _check(fn(qp, _ptr(w), kp, N, nq, q_per_seq, _ptr(n_visible), _ptr(cand_blocks), nb, k, _ptr(top),
               _ptr(pool_scores), _ptr(workspace), wsb, _stream(stream)), "csa2_index_reindex_topk" + suffix)
     return top
 

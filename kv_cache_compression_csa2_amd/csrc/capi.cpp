@@ -64,7 +64,7 @@ static int check_index_common(const char* who, const uint16_t* q_idx, const floa
 // Full scoring over bf16 (kfp4 == false) or FP4 (kfp4 == true) indexer K.
 static int index_full_impl(const char* who, const uint16_t* q_idx, const float* w, const void* k, bool kfp4,
                            int64_t N, int32_t nq, int32_t q_per_seq, const int32_t* n_visible, float* scores,
-                           int32_t block_size, float* block_scores, hipStream_t stream) {
+                           int32_t block_size, float* block_scores, hipStream_t stream, bool qfp4 = false) {
     int rc = check_index_common(who, q_idx, w, k, N, nq, q_per_seq);
     if (rc) return rc;
     if (nq > 0 && !scores) return fail(CSA2_EINVAL, "%s: null scores", who);
@@ -72,14 +72,15 @@ static int index_full_impl(const char* who, const uint16_t* q_idx, const float* 
     if (block_size == 8 && nq > 0 && !block_scores)
         return fail(CSA2_EINVAL, "%s: block_scores required when block_size == 8", who);
     (void)hipGetLastError();
-    csa2::launch_index_full(q_idx, w, k, kfp4, N, nq, q_per_seq, n_visible, scores, block_size, block_scores, stream);
+    csa2::launch_index_full(q_idx, w, k, kfp4, N, nq, q_per_seq, n_visible, scores, block_size, block_scores, stream,
+                            qfp4);
     return launched(who);
 }
 
 static int index_reindex_impl(const char* who, const uint16_t* q_idx, const float* w, const void* k, bool kfp4,
                               int64_t N, int32_t nq, int32_t q_per_seq, const int32_t* n_visible,
                               const int32_t* cand_blocks, int32_t nb, int32_t block_size, float* pool_scores,
-                              int32_t* pool_ids, hipStream_t stream) {
+                              int32_t* pool_ids, hipStream_t stream, bool qfp4 = false) {
     int rc = check_index_common(who, q_idx, w, k, N, nq, q_per_seq);
     if (rc) return rc;
     if (block_size != 8) return fail(CSA2_EINVAL, "%s: block_size must be 8", who);
@@ -87,7 +88,7 @@ static int index_reindex_impl(const char* who, const uint16_t* q_idx, const floa
     if (nq > 0 && (!cand_blocks || !pool_scores)) return fail(CSA2_EINVAL, "%s: null pointer", who);
     (void)hipGetLastError();
     csa2::launch_index_reindex(q_idx, w, k, kfp4, N, nq, q_per_seq, n_visible, cand_blocks, nb, pool_scores, pool_ids,
-                               stream);
+                               stream, qfp4);
     return launched(who);
 }
 
@@ -142,7 +143,7 @@ static int index_topk_args(const char* who, const uint16_t* q_idx, const float* 
 static int index_topk_impl(const char* who, bool merge, const uint16_t* q_idx, const float* w, const void* kc,
                            bool kfp4, int64_t N, int32_t nq, const int32_t* n_visible, int32_t k, int32_t* top_idx,
                            int32_t block_size, float* block_scores, float* scores, void* workspace, size_t ws_bytes,
-                           hipStream_t stream) {
+                           hipStream_t stream, bool qfp4 = false) {
     const int rc = index_topk_args(who, q_idx, w, kc, N, nq, k, top_idx, block_size, block_scores);
     if (rc) return rc;
     const size_t need = csa2_index_topk_workspace_bytes(nq, N, k);
@@ -150,7 +151,7 @@ static int index_topk_impl(const char* who, bool merge, const uint16_t* q_idx, c
         return fail(CSA2_EWORKSPACE, "%s: workspace needs %zu bytes", who, need);
     (void)hipGetLastError();
     csa2::launch_index_topk(q_idx, w, kc, kfp4, N, nq, n_visible, k, top_idx, block_size ? block_scores : nullptr,
-                            scores, workspace, stream);
+                            scores, workspace, stream, qfp4);
     if (merge) csa2::launch_index_topk_merge(N, nq, k, top_idx, workspace, stream);
     return launched(who);
 }
@@ -286,18 +287,33 @@ int csa2_index_prefill_topk_fp4k(const uint16_t* q_idx, const float* w, const ui
 int csa2_index_full_fp4qk(const uint8_t* q_fp4, const float* w, const uint8_t* k_fp4, int64_t N, int32_t nq,
                           int32_t q_per_seq, const int32_t* n_visible, float* scores, int32_t block_size,
                           float* block_scores, hipStream_t stream) {
-    const char* who = "csa2_index_full_fp4qk";
-    int rc = check_index_common(who, reinterpret_cast<const uint16_t*>(q_fp4), w, k_fp4, N, nq, q_per_seq);
-    if (rc) return rc;
-    if (q_per_seq % 8 != 0) return fail(CSA2_EINVAL, "%s: q_per_seq must be a multiple of 8", who);
-    if (nq > 0 && !scores) return fail(CSA2_EINVAL, "%s: null scores", who);
-    if (block_size != 0 && block_size != 8) return fail(CSA2_EINVAL, "%s: block_size must be 0 or 8", who);
-    if (block_size == 8 && nq > 0 && !block_scores)
-        return fail(CSA2_EINVAL, "%s: block_scores required when block_size == 8", who);
-    (void)hipGetLastError();
-    csa2::launch_index_full_fp4qk(q_fp4, w, k_fp4, N, nq, q_per_seq, n_visible, scores, block_size, block_scores,
-                                  stream);
-    return launched(who);
+    return index_full_impl("csa2_index_full_fp4qk", reinterpret_cast<const uint16_t*>(q_fp4), w, k_fp4, true, N, nq,
+                           q_per_seq, n_visible, scores, block_size, block_scores, stream, true);
+}
+
+int csa2_index_reindex_fp4qk(const uint8_t* q_fp4, const float* w, const uint8_t* k_fp4, int64_t N, int32_t nq,
+                             int32_t q_per_seq, const int32_t* n_visible, const int32_t* cand_blocks, int32_t nb,
+                             int32_t block_size, float* pool_scores, int32_t* pool_ids, hipStream_t stream) {
+    return index_reindex_impl("csa2_index_reindex_fp4qk", reinterpret_cast<const uint16_t*>(q_fp4), w, k_fp4, true, N,
+                              nq, q_per_seq, n_visible, cand_blocks, nb, block_size, pool_scores, pool_ids, stream,
+                              true);
+}
+
+int csa2_index_topk_fp4qk(const uint8_t* q_fp4, const float* w, const uint8_t* k_fp4, int64_t N, int32_t nq,
+                          const int32_t* n_visible, int32_t k, int32_t* top_idx, int32_t block_size,
+                          float* block_scores, float* scores, void* workspace, size_t ws_bytes, hipStream_t stream) {
+    return index_topk_impl("csa2_index_topk_fp4qk", true, reinterpret_cast<const uint16_t*>(q_fp4), w, k_fp4, true, N,
+                           nq, n_visible, k, top_idx, block_size, block_scores, scores, workspace, ws_bytes, stream,
+                           true);
+}
+
+int csa2_index_topk_select_fp4qk(const uint8_t* q_fp4, const float* w, const uint8_t* k_fp4, int64_t N, int32_t nq,
+                                 const int32_t* n_visible, int32_t k, int32_t* top_idx, int32_t block_size,
+                                 float* block_scores, float* scores, void* workspace, size_t ws_bytes,
+                                 hipStream_t stream) {
+    return index_topk_impl("csa2_index_topk_select_fp4qk", false, reinterpret_cast<const uint16_t*>(q_fp4), w, k_fp4,
+                           true, N, nq, n_visible, k, top_idx, block_size, block_scores, scores, workspace, ws_bytes,
+                           stream, true);
 }
 
 int csa2_index_prefill_topk_fp4qk(const uint8_t* q_fp4, const float* w, const uint8_t* k_fp4, int64_t N, int32_t nq,
@@ -328,7 +344,7 @@ size_t csa2_index_reindex_topk_workspace_bytes(int32_t nq, int32_t nb, int32_t k
 static int reindex_topk_impl(const char* who, const uint16_t* q_idx, const float* w, const void* kc, bool kfp4,
                              int64_t N, int32_t nq, int32_t q_per_seq, const int32_t* n_visible,
                              const int32_t* cand_blocks, int32_t nb, int32_t k, int32_t* top_idx, float* pool_scores,
-                             void* workspace, size_t ws_bytes, hipStream_t stream) {
+                             void* workspace, size_t ws_bytes, hipStream_t stream, bool qfp4 = false) {
     int rc = check_index_common(who, q_idx, w, kc, N, nq, q_per_seq);
     if (rc) return rc;
     if (nb < 1 || nb > 65536) return fail(CSA2_EINVAL, "%s: nb must be in [1, 65536]", who);
@@ -340,7 +356,7 @@ static int reindex_topk_impl(const char* who, const uint16_t* q_idx, const float
         return fail(CSA2_EWORKSPACE, "%s: workspace needs %zu bytes", who, need);
     (void)hipGetLastError();
     csa2::launch_index_reindex_topk(q_idx, w, kc, kfp4, N, nq, q_per_seq, n_visible, cand_blocks, nb, k, top_idx,
-                                    pool_scores, workspace, stream);
+                                    pool_scores, workspace, stream, qfp4);
     return launched(who);
 }
 
@@ -358,6 +374,15 @@ int csa2_index_reindex_topk_fp4k(const uint16_t* q_idx, const float* w, const ui
                                  hipStream_t stream) {
     return reindex_topk_impl("csa2_index_reindex_topk_fp4k", q_idx, w, k_fp4, true, N, nq, q_per_seq, n_visible,
                              cand_blocks, nb, k, top_idx, pool_scores, workspace, ws_bytes, stream);
+}
+
+int csa2_index_reindex_topk_fp4qk(const uint8_t* q_fp4, const float* w, const uint8_t* k_fp4, int64_t N, int32_t nq,
+                                  int32_t q_per_seq, const int32_t* n_visible, const int32_t* cand_blocks, int32_t nb,
+                                  int32_t k, int32_t* top_idx, float* pool_scores, void* workspace, size_t ws_bytes,
+                                  hipStream_t stream) {
+    return reindex_topk_impl("csa2_index_reindex_topk_fp4qk", reinterpret_cast<const uint16_t*>(q_fp4), w, k_fp4,
+                             true, N, nq, q_per_seq, n_visible, cand_blocks, nb, k, top_idx, pool_scores, workspace,
+                             ws_bytes, stream, true);
 }
 
 int kidx_fp4_pack(const uint16_t* x_bf16, int64_t n, uint8_t* out, hipStream_t stream) {

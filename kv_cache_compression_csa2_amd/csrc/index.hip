@@ -86,6 +86,18 @@ CSA2_DEVINL float e8m0_byte(uint32_t four, int sel) { return __uint_as_float(((f
 // Row of the accumulator held in register r by a lane of half `half` (32x32 layout).
 CSA2_DEVINL int acc_row(int r, int half) { return (r >> 2) * 8 + half * 4 + (r & 3); }
 
+typedef int i32x8 __attribute__((ext_vector_type(8)));
+
+// 32x32x64 MXFP4 x MXFP4 MFMA (gfx950 scaled f8f6f4, both operands E2M1): lane
+// l holds row / column l % 32 and 32 consecutive channels of one scale block,
+// whose E8M0 byte `sa` / `sb` it supplies; the result layout is that of the
+// 32x32 bf16 MFMA. Each product is exact and accumulates in fp32.
+CSA2_DEVINL f32x16 mfma32x32x64_fp4(uint4 a, uint4 b, uint32_t sa, uint32_t sb, f32x16 c) {
+    const i32x8 av = {(int)a.x, (int)a.y, (int)a.z, (int)a.w, 0, 0, 0, 0};
+    const i32x8 bv = {(int)b.x, (int)b.y, (int)b.z, (int)b.w, 0, 0, 0, 0};
+    return __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(av, bv, c, 4, 4, 0, (int)sa, 0, (int)sb);
+}
+
 // Per-lane state of the streaming kernels: the query's A operand and head
 // weights. A operand: head = lane % 32; step j covers channels 16j + 8*half
 // .. +8 (bf16 K), or 64*half + 8j .. +8 for FP4 K so that a lane's 8 steps
@@ -151,6 +163,50 @@ CSA2_DEVINL float stream_score(const StreamQuery<kFp4>& Q, const StreamTile<kFp4
     for (int r = 0; r < 16; r++) s = fmaf(Q.wr[r], relu_bits(acc[r]), s);
     s += from_upper_half(s);  // lanes 0..31 hold the sum over all 32 heads
     return st.valid ? s : -INFINITY;
+}
+
+// MXFP4 indexer Q (one 68-byte entry per head, the K entry format) with FP4 K:
+// K-step s of lane (head / entry lane % 32, half) contracts scale block
+// 2*half + s, i.e. the code dwords 4s .. 4s+3 of the 8 a K lane already holds
+// (stream_load, line_operands4) against the same block of the query head, on
+// the scaled FP4 MFMA: two 32x32x64 instructions, no decode.
+struct StreamQuery4 {
+    uint4 a4[2];
+    uint32_t s4[2];
+    float wr[16];
+    CSA2_DEVINL void load(const uint16_t* q_idx, const float* w, int64_t q, int half, int col_in_tile) {
+        const uint8_t* e = reinterpret_cast<const uint8_t*>(q_idx) + (q * kIdxHeads + col_in_tile) * kKRec;
+        const uint32_t sc = *reinterpret_cast<const uint32_t*>(e + kIdxDim / 2);
+#pragma unroll
+        for (int st = 0; st < 2; st++) {
+            const uint32_t* c = reinterpret_cast<const uint32_t*>(e + 16 * (2 * half + st));
+            a4[st] = make_uint4(c[0], c[1], c[2], c[3]);
+            s4[st] = (sc >> (8 * (2 * half + st))) & 0xFFu;
+        }
+#pragma unroll
+        for (int r = 0; r < 16; r++) wr[r] = w[q * kIdxHeads + acc_row(r, half)];
+    }
+};
+CSA2_DEVINL float stream_score4(const StreamQuery4& Q, const StreamTile<true>& st, int half) {
+    f32x16 acc = mfma32x32x64_fp4(Q.a4[0], make_uint4(st.code[0], st.code[1], st.code[2], st.code[3]), Q.s4[0],
+                                  (st.scales >> (16 * half)) & 0xFFu, f32x16{});
+    acc = mfma32x32x64_fp4(Q.a4[1], make_uint4(st.code[4], st.code[5], st.code[6], st.code[7]), Q.s4[1],
+                           (st.scales >> (16 * half + 8)) & 0xFFu, acc);
+    float s = 0.0f;
+#pragma unroll
+    for (int r = 0; r < 16; r++) s = fmaf(Q.wr[r], relu_bits(acc[r]), s);
+    s += from_upper_half(s);
+    return st.valid ? s : -INFINITY;
+}
+// The query state and score of the decode kernels for each operand format.
+template <bool kFp4, bool kQ4>
+using StreamQ = std::conditional_t<kQ4, StreamQuery4, StreamQuery<kFp4>>;
+template <bool kFp4, bool kQ4>
+CSA2_DEVINL float score_tile(const StreamQ<kFp4, kQ4>& Q, const StreamTile<kFp4>& st, int half) {
+    if constexpr (kQ4)
+        return stream_score4(Q, st, half);
+    else
+        return stream_score<kFp4>(Q, st, half);
 }
 
 // bf16 Full rows, line-ordered: a wave's 32-entry tile is 8 KiB of
@@ -258,7 +314,7 @@ CSA2_DEVINL void line_operands4(const LineTile4& lt, uint8_t* stage, int lane, S
     __builtin_amdgcn_wave_barrier();
 }
 
-template <bool kReindex, bool kFp4>
+template <bool kReindex, bool kFp4, bool kQ4 = false>
 __global__ __launch_bounds__(kStreamThreads) void index_stream_kernel(
     const uint16_t* __restrict__ q_idx, const float* __restrict__ w, const void* __restrict__ k_idx, int64_t N,
     int32_t q_per_seq, const int32_t* __restrict__ n_visible, const int32_t* __restrict__ cand_blocks, int32_t nb,
@@ -272,7 +328,7 @@ __global__ __launch_bounds__(kStreamThreads) void index_stream_kernel(
     int64_t nv = n_visible ? (int64_t)n_visible[q] : N;
     nv = nv < N ? nv : N;
 
-    StreamQuery<kFp4> Q;
+    StreamQ<kFp4, kQ4> Q;
     Q.load(q_idx, w, q, half, col_in_tile);
     const void* kseq = kFp4 ? static_cast<const void*>(static_cast<const uint8_t*>(k_idx) + seq * N * kKRec)
                             : static_cast<const void*>(static_cast<const uint16_t*>(k_idx) + seq * N * kIdxDim);
@@ -292,7 +348,7 @@ __global__ __launch_bounds__(kStreamThreads) void index_stream_kernel(
     };
 
     auto finish = [&](int64_t t, const StreamTile<kFp4>& st) {
-        const float s = stream_score<kFp4>(Q, st, half);
+        const float s = score_tile<kFp4, kQ4>(Q, st, half);
         const int64_t col = t * 32 + col_in_tile;
         if (half == 0 && col < ncols) scores[q * ncols + col] = s;
         if (kReindex) {
@@ -340,7 +396,7 @@ __global__ __launch_bounds__(kStreamThreads) void index_stream_kernel(
 // entry cand_blocks[q][j]*8 + t of sequence q / q_per_seq, and the candidates
 // carry entry ids; with ascending cand_blocks the result is the Top-K of
 // csa2_index_reindex's pool row mapped through its pool ids.
-template <bool kFp4, bool kRe, int kFtThreads, int kFtChunk>
+template <bool kFp4, bool kRe, int kFtThreads, int kFtChunk, bool kQ4 = false>
 __global__ __launch_bounds__(kFtThreads, kFtThreads == 256 && !kRe ? 3 : 1) void index_topk_kernel(
     const uint16_t* __restrict__ q_idx, const float* __restrict__ w, const void* __restrict__ k_idx, int64_t N,
     int32_t q_per_seq, const int32_t* __restrict__ n_visible, const int32_t* __restrict__ cand_blocks, int32_t nb,
@@ -381,7 +437,8 @@ __global__ __launch_bounds__(kFtThreads, kFtThreads == 256 && !kRe ? 3 : 1) void
         lds_barrier();
     }
 
-    StreamQuery<kFp4> Q;
+    static_assert(!kQ4 || kFp4, "MXFP4 Q pairs with MXFP4 K");
+    StreamQ<kFp4, kQ4> Q;
     Q.load(q_idx, w, q, half, col_in_tile);
     const int64_t seq = kRe ? q / q_per_seq : q;
     const void* kseq = kFp4 ? static_cast<const void*>(static_cast<const uint8_t*>(k_idx) + seq * N * kKRec)
@@ -400,7 +457,7 @@ __global__ __launch_bounds__(kFtThreads, kFtThreads == 256 && !kRe ? 3 : 1) void
         }
     };
     auto finish = [&](int t, const StreamTile<kFp4>& st) {
-        const float s = stream_score<kFp4>(Q, st, half);
+        const float s = score_tile<kFp4, kQ4>(Q, st, half);
         const int p = t * 32 + col_in_tile;
         if (half == 0) sc[p] = s;
         if (scores_dbg && half == 0 && p < n) scores_dbg[q * ncols + c0 + p] = s;
@@ -421,7 +478,7 @@ __global__ __launch_bounds__(kFtThreads, kFtThreads == 256 && !kRe ? 3 : 1) void
                 line_operands4(lt, stage[wave], lane, st);
                 const int p = tt * 32 + col_in_tile;
                 st.valid = c0 + p < nv;
-                const float s = stream_score<true>(Q, st, half);
+                const float s = score_tile<true, kQ4>(Q, st, half);
                 if (half == 0) sc[p] = s;
                 if (scores_dbg && half == 0 && p < n) scores_dbg[q * ncols + c0 + p] = s;
                 if (block_scores) {
@@ -584,18 +641,6 @@ struct PfPreQ4 {
     uint32_t sb;  // the block's E8M0 scale byte
 };
 constexpr int kPfRowQ4 = 80;  // LDS row of a raw MXFP4 entry: 64 code bytes, 4 scales, 12 pad
-
-typedef int i32x8 __attribute__((ext_vector_type(8)));
-
-// 32x32x64 MXFP4 x MXFP4 MFMA (gfx950 scaled f8f6f4, both operands E2M1): lane
-// l holds row / column l % 32 and 32 consecutive channels of one scale block,
-// whose E8M0 byte `sa` / `sb` it supplies; the result layout is that of the
-// 32x32 bf16 MFMA. Each product is exact and accumulates in fp32.
-CSA2_DEVINL f32x16 mfma32x32x64_fp4(uint4 a, uint4 b, uint32_t sa, uint32_t sb, f32x16 c) {
-    const i32x8 av = {(int)a.x, (int)a.y, (int)a.z, (int)a.w, 0, 0, 0, 0};
-    const i32x8 bv = {(int)b.x, (int)b.y, (int)b.z, (int)b.w, 0, 0, 0, 0};
-    return __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(av, bv, c, 4, 4, 0, (int)sa, 0, (int)sb);
-}
 
 // kSel: scoring fused with the per-query Top-k (k <= kPfSelK; the DeepSelect
 // selection eogee.com report 3.5 names, for the prefill chunk): no score row
@@ -928,9 +973,12 @@ __global__ __launch_bounds__(256, 2) void index_prefill_kernel(
 
 int launch_index_full(const uint16_t* q_idx, const float* w, const void* k, bool kfp4, int64_t N, int32_t nq,
                       int32_t q_per_seq, const int32_t* n_visible, float* scores, int32_t block_size,
-                      float* block_scores, hipStream_t s) {
+                      float* block_scores, hipStream_t s, bool qfp4) {
     if (nq == 0) return 0;
     float* bs = block_size > 0 ? block_scores : nullptr;
+    if (qfp4 && q_per_seq % kPfQueries == 0)
+        return launch_index_full_fp4qk(reinterpret_cast<const uint8_t*>(q_idx), w, static_cast<const uint8_t*>(k), N,
+                                       nq, q_per_seq, n_visible, scores, block_size, block_scores, s);
     if (q_per_seq % kPfQueries == 0) {
         const int32_t nchunks = (int32_t)((N + kPfChunk - 1) / kPfChunk);
         const int64_t grid = (int64_t)(nq / kPfQueries) * nchunks;
@@ -953,7 +1001,11 @@ int launch_index_full(const uint16_t* q_idx, const float* w, const void* k, bool
     if (tpw < kStreamWaves) tpw = kStreamWaves;
     const int64_t wgs_per_q = (ntiles + tpw - 1) / tpw;
     const dim3 grid((unsigned)(wgs_per_q * nq));
-    if (kfp4)
+    if (qfp4)
+        hipLaunchKernelGGL((index_stream_kernel<false, true, true>), grid, dim3(kStreamThreads), 0, s, q_idx, w, k, N,
+                           q_per_seq, n_visible, (const int32_t*)nullptr, 0, scores, bs, (int32_t*)nullptr, N, ntiles,
+                           (int32_t)wgs_per_q, (int32_t)tpw);
+    else if (kfp4)
         hipLaunchKernelGGL((index_stream_kernel<false, true>), grid, dim3(kStreamThreads), 0, s, q_idx, w, k, N,
                            q_per_seq, n_visible, (const int32_t*)nullptr, 0, scores, bs, (int32_t*)nullptr, N, ntiles,
                            (int32_t)wgs_per_q, (int32_t)tpw);
@@ -1036,18 +1088,20 @@ FtWs ft_ws(void* ws, int32_t nq, int64_t N, int32_t topk) { return ft_ws_chunks(
 
 int launch_index_topk(const uint16_t* q_idx, const float* w, const void* k, bool kfp4, int64_t N, int32_t nq,
                       const int32_t* n_visible, int32_t topk, int32_t* out_idx, float* block_scores,
-                      float* scores_dbg, void* ws, hipStream_t s) {
+                      float* scores_dbg, void* ws, hipStream_t s, bool qfp4) {
     if (nq == 0) return 0;
     const FtWs f = ft_ws(ws, nq, N, topk);
     const bool small = index_topk_chunk_len(nq, N) == 4096;
     const dim3 grid((unsigned)((int64_t)nq * f.c));
-#define CSA2_FT(FP4, NT, CH)                                                                                   \
-    hipLaunchKernelGGL((index_topk_kernel<FP4, false, NT, CH>), grid, dim3(NT), 0, s, q_idx, w, k, N, 1, n_visible, \
-                       nullptr, 0, topk, f.c, out_idx, f.ck, f.cc, block_scores, scores_dbg)
-    if (kfp4) {
-        if (small) CSA2_FT(true, 512, 4096); else CSA2_FT(true, 512, 8192);
+#define CSA2_FT(FP4, NT, CH, Q4)                                                                               \
+    hipLaunchKernelGGL((index_topk_kernel<FP4, false, NT, CH, Q4>), grid, dim3(NT), 0, s, q_idx, w, k, N, 1,       \
+                       n_visible, nullptr, 0, topk, f.c, out_idx, f.ck, f.cc, block_scores, scores_dbg)
+    if (qfp4) {
+        if (small) CSA2_FT(true, 512, 4096, true); else CSA2_FT(true, 512, 8192, true);
+    } else if (kfp4) {
+        if (small) CSA2_FT(true, 512, 4096, false); else CSA2_FT(true, 512, 8192, false);
     } else {
-        if (small) CSA2_FT(false, 256, 4096); else CSA2_FT(false, 256, 8192);
+        if (small) CSA2_FT(false, 256, 4096, false); else CSA2_FT(false, 256, 8192, false);
     }
 #undef CSA2_FT
     return 0;
@@ -1125,25 +1179,27 @@ int launch_index_topk_merge_pool(int64_t N, int32_t nq, int32_t topk, int32_t* o
 // candidates when a row has more than one chunk.
 int launch_index_reindex_topk(const uint16_t* q_idx, const float* w, const void* k, bool kfp4, int64_t N, int32_t nq,
                               int32_t q_per_seq, const int32_t* n_visible, const int32_t* cand_blocks, int32_t nb,
-                              int32_t topk, int32_t* out_idx, float* pool_scores, void* ws, hipStream_t s) {
+                              int32_t topk, int32_t* out_idx, float* pool_scores, void* ws, hipStream_t s, bool qfp4) {
     if (nq == 0) return 0;
     const FtWs f = ft_ws_chunks(ws, nq, reindex_topk_chunks(nq, nb, topk), topk);
     const int64_t len = reindex_topk_chunk_len(nq, (int64_t)nb * 8, topk);
     const dim3 grid((unsigned)((int64_t)nq * f.c));
-#define CSA2_RT(FP4, CH)                                                                                         \
-    hipLaunchKernelGGL((index_topk_kernel<FP4, true, 256, CH>), grid, dim3(256), 0, s, q_idx, w, k, N, q_per_seq, \
-                       n_visible, cand_blocks, nb, topk, f.c, out_idx, f.ck, f.cc, nullptr, pool_scores)
-#define CSA2_RT_LEN(FP4)                   \
-    switch (len) {                         \
-        case 1024: CSA2_RT(FP4, 1024); break; \
-        case 2048: CSA2_RT(FP4, 2048); break; \
-        case 4096: CSA2_RT(FP4, 4096); break; \
-        default: CSA2_RT(FP4, 8192); break;   \
+#define CSA2_RT(FP4, CH, Q4)                                                                                    \
+    hipLaunchKernelGGL((index_topk_kernel<FP4, true, 256, CH, Q4>), grid, dim3(256), 0, s, q_idx, w, k, N,       \
+                       q_per_seq, n_visible, cand_blocks, nb, topk, f.c, out_idx, f.ck, f.cc, nullptr, pool_scores)
+#define CSA2_RT_LEN(FP4, Q4)                   \
+    switch (len) {                             \
+        case 1024: CSA2_RT(FP4, 1024, Q4); break; \
+        case 2048: CSA2_RT(FP4, 2048, Q4); break; \
+        case 4096: CSA2_RT(FP4, 4096, Q4); break; \
+        default: CSA2_RT(FP4, 8192, Q4); break;   \
     }
-    if (kfp4) {
-        CSA2_RT_LEN(true)
+    if (qfp4) {
+        CSA2_RT_LEN(true, true)
+    } else if (kfp4) {
+        CSA2_RT_LEN(true, false)
     } else {
-        CSA2_RT_LEN(false)
+        CSA2_RT_LEN(false, false)
     }
 #undef CSA2_RT_LEN
 #undef CSA2_RT
@@ -1232,7 +1288,7 @@ int launch_index_prefill_topk_fp4qk(const uint8_t* q_fp4, const float* w, const 
 
 int launch_index_reindex(const uint16_t* q_idx, const float* w, const void* k, bool kfp4, int64_t N, int32_t nq,
                          int32_t q_per_seq, const int32_t* n_visible, const int32_t* cand_blocks, int32_t nb,
-                         float* pool_scores, int32_t* pool_ids, hipStream_t s) {
+                         float* pool_scores, int32_t* pool_ids, hipStream_t s, bool qfp4) {
     if (nq == 0) return 0;
     const int64_t ncols = (int64_t)nb * 8;
     const int64_t ntiles = (ncols + 31) / 32;
@@ -1242,7 +1298,11 @@ int launch_index_reindex(const uint16_t* q_idx, const float* w, const void* k, b
     if (tpw < kStreamWaves) tpw = kStreamWaves;
     const int64_t wgs_per_q = (ntiles + tpw - 1) / tpw;
     const dim3 grid((unsigned)(wgs_per_q * nq));
-    if (kfp4)
+    if (qfp4)
+        hipLaunchKernelGGL((index_stream_kernel<true, true, true>), grid, dim3(kStreamThreads), 0, s, q_idx, w, k, N,
+                           q_per_seq, n_visible, cand_blocks, nb, pool_scores, (float*)nullptr, pool_ids, ncols,
+                           ntiles, (int32_t)wgs_per_q, (int32_t)tpw);
+    else if (kfp4)
         hipLaunchKernelGGL((index_stream_kernel<true, true>), grid, dim3(kStreamThreads), 0, s, q_idx, w, k, N,
                            q_per_seq, n_visible, cand_blocks, nb, pool_scores, (float*)nullptr, pool_ids, ncols,
                            ntiles, (int32_t)wgs_per_q, (int32_t)tpw);

@@ -15,13 +15,14 @@ int launch_kidx_fp4_pack(const uint16_t* x, int64_t n, uint8_t* out, hipStream_t
 int launch_swa_fp8_pack(const uint16_t* x, int64_t n, uint8_t* out, hipStream_t s);
 
 // Indexer scoring; k is bf16 [nseq][N][128] (kfp4 false) or FP4 entries
-// [nseq][N][68] (kfp4 true).
+// [nseq][N][68] (kfp4 true). qfp4 (with kfp4): q_idx points to MXFP4 query
+// entries [nq][32][68] instead of bf16 [nq][32][128] (every scoring launcher).
 int launch_index_full(const uint16_t* q_idx, const float* w, const void* k, bool kfp4, int64_t N, int32_t nq,
                       int32_t q_per_seq, const int32_t* n_visible, float* scores, int32_t block_size,
-                      float* block_scores, hipStream_t s);
+                      float* block_scores, hipStream_t s, bool qfp4 = false);
 int launch_index_reindex(const uint16_t* q_idx, const float* w, const void* k, bool kfp4, int64_t N, int32_t nq,
                          int32_t q_per_seq, const int32_t* n_visible, const int32_t* cand_blocks, int32_t nb,
-                         float* pool_scores, int32_t* pool_ids, hipStream_t s);
+                         float* pool_scores, int32_t* pool_ids, hipStream_t s, bool qfp4 = false);
 
 // Full-mode scoring fused with Top-K for decode (one query per sequence), in
 // two launches: scoring + per-chunk selection (writes out_idx itself when the
@@ -31,7 +32,7 @@ size_t index_topk_workspace_bytes(int32_t nq, int64_t N, int32_t k);
 bool index_topk_fits(int32_t nq, int64_t N, int32_t k);
 int launch_index_topk(const uint16_t* q_idx, const float* w, const void* k, bool kfp4, int64_t N, int32_t nq,
                       const int32_t* n_visible, int32_t topk, int32_t* out_idx, float* block_scores,
-                      float* scores_dbg, void* ws, hipStream_t s);
+                      float* scores_dbg, void* ws, hipStream_t s, bool qfp4 = false);
 int launch_index_topk_merge(int64_t N, int32_t nq, int32_t topk, int32_t* out_idx, void* ws, hipStream_t s);
 // The merge above and the pool's Top-pool_k blocks over the block maxima
 // (rows of ceil(N / 8)), sharing launches; ws holds the merge's candidates
@@ -47,7 +48,8 @@ bool reindex_topk_fits(int32_t nq, int32_t nb, int32_t k);
 size_t reindex_topk_workspace_bytes(int32_t nq, int32_t nb, int32_t k);
 int launch_index_reindex_topk(const uint16_t* q_idx, const float* w, const void* k, bool kfp4, int64_t N, int32_t nq,
                               int32_t q_per_seq, const int32_t* n_visible, const int32_t* cand_blocks, int32_t nb,
-                              int32_t topk, int32_t* out_idx, float* pool_scores, void* ws, hipStream_t s);
+                              int32_t topk, int32_t* out_idx, float* pool_scores, void* ws, hipStream_t s,
+                              bool qfp4 = false);
 
 // Prefill scoring (q_per_seq a multiple of 8) fused with the per-query Top-k
 // (k <= 512): one launch scores and selects per chunk of the row (final

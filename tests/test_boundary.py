@@ -107,15 +107,25 @@ def test_index_fp4qk_rejects(kw, frag):
     a = dict(q=P, w=P, k=P, N=100, nq=8, q_per_seq=8, scores=P, block_size=0, block=P)
     a.update(kw)
     L_ = K.load()
-    rc, msg = _err(L_.csa2_index_full_fp4qk(a["q"], a["w"], a["k"], a["N"], a["nq"], a["q_per_seq"], None,
-                                           a["scores"], a["block_size"], a["block"], S))
-    assert rc == L.CSA2_EINVAL and frag in msg and "fp4qk" in msg, msg
+    if frag != "multiple of 8":  # only the prefill-chunk call scores 8 queries of a sequence together
+        rc, msg = _err(L_.csa2_index_full_fp4qk(a["q"], a["w"], a["k"], a["N"], a["nq"], a["q_per_seq"], None,
+                                               a["scores"], a["block_size"], a["block"], S))
+        assert rc == L.CSA2_EINVAL and frag in msg and "fp4qk" in msg, msg
     if "scores" not in kw and "block_size" not in kw:
         rc, msg = _err(L_.csa2_index_prefill_topk_fp4qk(a["q"], a["w"], a["k"], a["N"], a["nq"], a["q_per_seq"], None,
                                                        512, P, None, P, 1 << 30, S))
         assert rc == L.CSA2_EINVAL and frag in msg and "fp4qk" in msg, msg
     rc, msg = _err(L_.csa2_index_prefill_topk_fp4qk(P, P, P, 100, 8, 8, None, 513, P, None, P, 1 << 30, S))
     assert rc == L.CSA2_EINVAL and "k must be" in msg
+    # the decode and Reindex MXFP4-Q calls check as their FP4-K siblings
+    rc, msg = _err(L_.csa2_index_topk_fp4qk(P, P, P, 100, 2, None, 0, P, 0, None, None, P, 1 << 30, S))
+    assert rc == L.CSA2_EINVAL and "k must be" in msg and "fp4qk" in msg, msg
+    rc, msg = _err(L_.csa2_index_topk_select_fp4qk(None, P, P, 100, 2, None, 512, P, 0, None, None, P, 1 << 30, S))
+    assert rc == L.CSA2_EINVAL and "null pointer" in msg, msg
+    rc, msg = _err(L_.csa2_index_reindex_fp4qk(P, P, P, 100, 2, 1, None, P, 0, 8, P, None, S))
+    assert rc == L.CSA2_EINVAL and "nb must be" in msg and "fp4qk" in msg, msg
+    rc, msg = _err(L_.csa2_index_reindex_topk_fp4qk(P, P, P, 100, 2, 1, None, P, 4, 0, P, None, P, 1 << 30, S))
+    assert rc == L.CSA2_EINVAL and "k must be" in msg and "fp4qk" in msg, msg
 
 
 @pytest.mark.parametrize("kw,frag", [

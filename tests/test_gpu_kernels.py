@@ -211,11 +211,13 @@ def _fp4qk_inputs(nq, N, nseq, seed):
 
 
 @pytest.mark.parametrize("nq,N,qps", [(8, 1000, 8), (16, 5003, 16), (24, 4096 * 2 + 100, 8), (8, 1, 8),
-                                      (8, 64, 8), (32, 4097, 32)])
+                                      (8, 64, 8), (32, 4097, 32), (1, 1024, 1), (3, 1000, 1), (5, 77, 1),
+                                      (2, 40000, 1), (4, 1, 1), (12, 3000, 3)])
 def test_index_full_fp4qk_matches_oracle(nq, N, qps):
     """MXFP4 query and key entries on the scaled FP4 matrix instruction: scores
     and block maxima within the score tolerance of the oracle (exact products,
-    fp32 sums), with causal-like visible lengths and ragged tails."""
+    fp32 sums), with causal-like visible lengths and ragged tails; the prefill
+    kernel (8 | q_per_seq) and the streaming kernel (the rest)."""
     print("case: index_full_fp4qk", nq, N, qps, flush=True)
     qf, qf_host, w, kf, kf_host = _fp4qk_inputs(nq, N, nq // qps, 30 + N + nq)
     rng = np.random.default_rng(N + 7)
@@ -233,14 +235,15 @@ def test_index_full_fp4qk_matches_oracle(nq, N, qps):
     assert ok, msg
 
 
-def test_index_fp4qk_products_exact_for_every_code_and_scale():
+@pytest.mark.parametrize("qps", [1, 8])
+def test_index_fp4qk_products_exact_for_every_code_and_scale(qps):
     """Every E2M1 key code under every E8M0 scale byte 2..252 in every channel
     position (as the FP4-K exhaustive test), against queries whose four blocks
     carry different scales: head 0 is +1 in every channel with block scales
     1, 2, 1/2, 4, head 1 is -1 everywhere. The score with w = (1, 1) is
     v*m if v > 0 else -v, and with w = (1, 0) max(v*m, 0), for the decoded key
     value v and the channel's block multiplier m: bit-exact."""
-    print("case: fp4qk exhaustive products", flush=True)
+    print("case: fp4qk exhaustive products", qps, flush=True)
     bs = np.arange(2, 253)
     n = len(bs) * 16
     i = np.arange(n)
@@ -258,10 +261,11 @@ def test_index_fp4qk_products_exact_for_every_code_and_scale():
     w = torch.zeros((nq, 32), dtype=torch.float32)
     w[:, 0] = 1.0
     w[0::2, 1] = 1.0
-    s = K().csa2_index_full(None, w.to(DEV), None, n, nq, k_fp4=torch.tensor(ent[None], device=DEV),
+    kent = np.ascontiguousarray(np.broadcast_to(ent, (nq // qps, n, 68)))
+    s = K().csa2_index_full(None, w.to(DEV), None, n, qps, k_fp4=torch.tensor(kent, device=DEV),
                             q_fp4=torch.tensor(qent, device=DEV))
     torch.cuda.synchronize()
-    ref = O.index_full(None, np_(w), None, n, nq, k_fp4=ent[None], q_fp4=qent)
+    ref = O.index_full(None, np_(w), None, n, qps, k_fp4=kent, q_fp4=qent)
     assert np.array_equal(np_(s), ref)
     v = O.kidx_fp4_unpack(ent)[i, ch]
     m = np.array([1.0, 2.0, 0.5, 4.0])[ch // 32]
@@ -297,6 +301,72 @@ def test_index_prefill_topk_fp4qk_bit_exact_on_exact_scores(nq, qps, N, k):
     torch.cuda.synchronize()
     rs = O.index_full(None, w_host, None, N, qps, n_visible=nv, k_fp4=kf_host, q_fp4=qf_host)
     assert np.array_equal(np_(top), O.topk(rs, k, row_len=nv))
+
+
+@pytest.mark.parametrize("nq,N,k", [(3, 20000, 512), (2, 8192, 512), (4, 1000, 512), (2, 70000, 2048),
+                                    (3, 20000, 100), (8, 65536, 512)])
+def test_index_topk_fp4qk_bit_exact_on_exact_scores(nq, N, k):
+    """Decode Full scoring with MXFP4 Q and K fused with Top-k, on exact-score
+    entries: the oracle's Top-K of the oracle's score row (one chunk, several,
+    a ragged tail, the two-level merge, rows with fewer visible entries than k
+    or none), with the block maxima, and the select + merge launches apart."""
+    print("case: index_topk fp4qk exact", nq, N, k, flush=True)
+    rng = np.random.default_rng(1700 + N + k + nq)
+    qf_host = _fp4qk_exact_entries(nq * 32, rng).reshape(nq, 32, 68)
+    kf_host = _fp4qk_exact_entries(nq * N, rng).reshape(nq, N, 68)
+    w_host = np.exp2(rng.integers(-2, 1, (nq, 32))).astype(np.float32)
+    nv = rng.integers(N // 2, N + 1, nq).astype(np.int32)
+    nv[0], nv[1] = N, 0
+    if nq > 2:
+        nv[2] = min(k // 2, N)
+    qf, kf, w, nvd = (torch.tensor(qf_host, device=DEV), torch.tensor(kf_host, device=DEV),
+                      torch.tensor(w_host, device=DEV), dev_i32(nv, DEV))
+    top, blk = K().csa2_index_topk(None, w, None, N, k, n_visible=nvd, block_size=8, k_fp4=kf, q_fp4=qf)
+    ws = torch.empty((max(K().csa2_index_topk_workspace_bytes(nq, N, k), 1),), dtype=torch.uint8, device=DEV)
+    top2 = torch.empty_like(top)
+    K().csa2_index_topk(None, w, None, N, k, n_visible=nvd, top=top2, workspace=ws, k_fp4=kf, q_fp4=qf,
+                        stage="select")
+    K().csa2_index_topk(None, w, None, N, k, top=top2, workspace=ws, k_fp4=kf, q_fp4=qf, stage="merge")
+    torch.cuda.synchronize()
+    rs, rb = O.index_full(None, w_host, None, N, 1, n_visible=nv, block_size=8, k_fp4=kf_host, q_fp4=qf_host)
+    top_o = O.topk(rs, k, row_len=nv)
+    assert np.array_equal(np_(top), top_o)
+    assert np.array_equal(np_(top2), top_o)
+    assert np.array_equal(np_(blk), rb)
+
+
+@pytest.mark.parametrize("nq,N,nb,k,qps", [(2, 1 << 20, 2048, 512, 1), (3, 9000, 300, 512, 1),
+                                           (16, 40000, 1000, 100, 8)])
+def test_index_reindex_fp4qk_matches_oracle_and_topk_is_exact(nq, N, nb, k, qps):
+    """Reindex with MXFP4 Q and K: pool scores within the score tolerance of
+    the oracle on random entries (pool ids exact), and on exact-score entries
+    the fused Reindex + Top-k equals the oracle's Top-K through the pool ids
+    (padding blocks, blocks shared by sequences of several queries)."""
+    print("case: reindex fp4qk", nq, N, nb, k, qps, flush=True)
+    rng = np.random.default_rng(1800 + N + nb)
+    blocks = np.sort(np.stack([rng.choice((N + 7) // 8, nb, replace=False) for _ in range(nq)]), 1).astype(np.int32)
+    blocks[0, -3:] = -1
+    nv = rng.integers(N // 2, N + 1, nq).astype(np.int32)
+    pool = O.pool_ids(blocks, 8)
+    # random entries: scores
+    qf, qf_host, w, kf, kf_host = _fp4qk_inputs(nq, N, nq // qps, 1900 + nb)
+    ps, pid = K().csa2_index_reindex(None, w, None, N, qps, dev_i32(blocks, DEV), n_visible=dev_i32(nv, DEV),
+                                     k_fp4=kf, q_fp4=qf)
+    torch.cuda.synchronize()
+    ref = O.index_reindex(None, np_(w), None, N, qps, pool, n_visible=nv, k_fp4=kf_host, q_fp4=qf_host)
+    ok, msg = rel_close(np_(ps), ref)
+    assert ok, msg
+    assert np.array_equal(np_(pid), np.where((pool >= 0) & (pool < nv[:, None]), pool, -1))
+    # exact-score entries: the fused selection
+    qx = _fp4qk_exact_entries(nq * 32, rng).reshape(nq, 32, 68)
+    kx = _fp4qk_exact_entries((nq // qps) * N, rng).reshape(nq // qps, N, 68)
+    wx = np.exp2(rng.integers(-2, 1, (nq, 32))).astype(np.float32)
+    top = K().csa2_index_reindex_topk(None, torch.tensor(wx, device=DEV), None, N, qps, dev_i32(blocks, DEV), k,
+                                      n_visible=dev_i32(nv, DEV), k_fp4=torch.tensor(kx, device=DEV),
+                                      q_fp4=torch.tensor(qx, device=DEV))
+    torch.cuda.synchronize()
+    rx = O.index_reindex(None, wx, None, N, qps, pool, n_visible=nv, k_fp4=kx, q_fp4=qx)
+    assert np.array_equal(np_(top), O.topk(rx, k, id_map=pool))
 
 
 def test_index_prefill_topk_fp4qk_matches_the_unfused_path():
