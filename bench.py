@@ -20,7 +20,10 @@ A step is one pass of the whole hot path over one batch of synthetic input:
   prefill128k_fp4k : the prefill step over FP4 indexer-K entries;
   prefill128k_fp4qk : the same with the indexer Q in MXFP4 too (the step
       packs the bf16 query into one entry per head, then scores on the
-      scaled FP4 matrix instruction).
+      scaled FP4 matrix instruction);
+  encoder64k_fp4qk_fp8w / decode1m_fp4qk_fp8w : the 64K and 1M steps with
+      MXFP4 indexer Q and K and FP8 window KV (each scoring layer's query
+      packed inside the step).
 In every decode step (one query per sequence) the Full layer's scoring and
 Top-512 run fused (csa2_index_topk: scoring with a per-chunk Top-512 in one
 launch, the chunks' merge in a second; no score row is written); the prefill
@@ -414,7 +417,7 @@ def main():
     ap.add_argument("--workloads",
                     default="encoder64k,decoder256k,decode1m,prefill128k,encoder_group64k,decoder_group256k,"
                             "encoder64k_fp4k,decode1m_fp4k,encoder64k_fp4k_fp8w,decode1m_fp4k_fp8w,"
-                            "prefill128k_fp4k,prefill128k_fp4qk")
+                            "prefill128k_fp4k,prefill128k_fp4qk,encoder64k_fp4qk_fp8w,decode1m_fp4qk_fp8w")
     ap.add_argument("--attn-sweep", default="64,256,1024")
     ap.add_argument("--no-cpu", action="store_true")
     ap.add_argument("--calibrate-copy", action="store_true",

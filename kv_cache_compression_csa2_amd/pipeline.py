@@ -59,12 +59,14 @@ class Step:
         # prefill chunk: scoring fused with the Top-512 (8 queries of a sequence per workgroup)
         self.prefill_fused = not self.fused and wl.q_per_seq % 8 == 0 and not wl.hier
         self.ws_pf = ws(L.csa2_index_prefill_topk_workspace_bytes(nq, N, TOPK)) if self.prefill_fused else None
-        # MXFP4 indexer Q (prefill chunks with FP4 K): packed inside the step from the bf16 query
-        self.qf = None
+        # MXFP4 indexer Q of every scoring layer (with FP4 K): packed inside the step from the bf16 query
+        self.qfl = None
         if wl.qfmt == "fp4":
-            if not (self.prefill_fused and wl.kfmt == "fp4"):
-                raise ValueError("an MXFP4 indexer Q is scored by the prefill-chunk call over FP4 K entries")
-            self.qf = torch.empty((nq, L.IDX_HEADS, L.KIDX_RECORD), dtype=torch.uint8, device=device)
+            if wl.kfmt != "fp4":
+                raise ValueError("an MXFP4 indexer Q is scored against FP4 K entries")
+            self.qfl = [torch.empty((nq, L.IDX_HEADS, L.KIDX_RECORD), dtype=torch.uint8, device=device)
+                        for _ in range(wl.n_index_layers)]
+        self.qf = self.qfl[0] if self.qfl else None
         self.debug_scores = False
         self.fused_reindex = True
         self.ws_rt = ws(L.csa2_index_reindex_topk_workspace_bytes(nq, POOL_BLOCKS, TOPK)) if wl.hier else None
@@ -89,27 +91,35 @@ class Step:
         else:
             L.csa2_index_full(wl.q_idx[0], wl.w[0], kb, wl.N, wl.q_per_seq, wl.n_visible, 0, self.scores, k_fp4=kf)
 
+    def _q(self, layer):
+        """(q_idx, q_fp4) keyword pair of a scoring layer's indexer query."""
+        return (None, self.qfl[layer]) if self.qfl else (self.wl.q_idx[layer], None)
+
     def index_topk(self, k, stage):
         wl = self.wl
         kb, kf = self._k(k)
-        L.csa2_index_topk(wl.q_idx[0], wl.w[0], kb, wl.N, TOPK, n_visible=wl.n_visible, block_size=8 if wl.hier else 0,
+        qb, qf = self._q(0)
+        L.csa2_index_topk(qb, wl.w[0], kb, wl.N, TOPK, n_visible=wl.n_visible, block_size=8 if wl.hier else 0,
                           top=self.top[0], block_scores=self.blocks, scores=self.scores if self.debug_scores else None,
-                          workspace=self.ws_ft, k_fp4=kf, stage=stage)
+                          workspace=self.ws_ft, k_fp4=kf, stage=stage, q_fp4=qf)
 
     def index_prefill_topk(self, k):
         wl = self.wl
         kb, kf = self._k(k)
-        qb, qf = (None, self.qf) if self.qf is not None else (wl.q_idx[0], None)
+        qb, qf = self._q(0)
         L.csa2_index_prefill_topk(qb, wl.w[0], kb, wl.N, wl.q_per_seq, TOPK, n_visible=wl.n_visible,
                                   top=self.top[0], scores=self.scores if self.debug_scores else None,
                                   workspace=self.ws_pf, k_fp4=kf, q_fp4=qf)
 
-    def pack_query(self):
-        """The Full layer's bf16 indexer query -> one MXFP4 entry per head."""
-        L.kidx_fp4_pack(self.wl.q_idx[0].reshape(-1, L.IDX_DIM), out=self.qf.view(-1, L.KIDX_RECORD))
+    def pack_query(self, layer=0):
+        """A scoring layer's bf16 indexer query -> one MXFP4 entry per head."""
+        L.kidx_fp4_pack(self.wl.q_idx[layer].reshape(-1, L.IDX_DIM), out=self.qfl[layer].view(-1, L.KIDX_RECORD))
 
     def full_layer(self, k, sp):
         """The Full layer's scoring and Top-512 (+ the 2048-block pool)."""
+        if self.qfl is not None:
+            with sp("q_pack"):
+                self.pack_query(0)
         if self.fused:
             with sp("index_topk"):
                 self.index_topk(k, "select")
@@ -122,12 +132,11 @@ class Step:
                 with sp("topk_merge"):
                     self.index_topk(k, "merge")
         elif self.prefill_fused:
-            if self.qf is not None:
-                with sp("q_pack"):
-                    self.pack_query()
             with sp("index_topk"):
                 self.index_prefill_topk(k)
         else:
+            if self.qfl is not None:
+                raise ValueError("the MXFP4-Q steps score with the fused calls")
             with sp("index_full"):
                 self.index_full(k)
             with sp("topk_full"):
@@ -142,14 +151,15 @@ class Step:
     def reindex(self, layer, k):
         wl = self.wl
         kb, kf = self._k(k)
+        qb, qf = self._q(layer)
         if self.fused_reindex:
-            L.csa2_index_reindex_topk(wl.q_idx[layer], wl.w[layer], kb, wl.N, wl.q_per_seq, self.cand, TOPK,
+            L.csa2_index_reindex_topk(qb, wl.w[layer], kb, wl.N, wl.q_per_seq, self.cand, TOPK,
                                       n_visible=wl.n_visible, top=self.top[layer],
                                       pool_scores=self.pool_scores if self.debug_scores else None,
-                                      workspace=self.ws_rt, k_fp4=kf)
+                                      workspace=self.ws_rt, k_fp4=kf, q_fp4=qf)
             return
-        L.csa2_index_reindex(wl.q_idx[layer], wl.w[layer], kb, wl.N, wl.q_per_seq, self.cand, wl.n_visible,
-                             pool_scores=self.pool_scores, pool_ids=self.pool_ids, k_fp4=kf)
+        L.csa2_index_reindex(qb, wl.w[layer], kb, wl.N, wl.q_per_seq, self.cand, wl.n_visible,
+                             pool_scores=self.pool_scores, pool_ids=self.pool_ids, k_fp4=kf, q_fp4=qf)
         L.csa2_topk(self.pool_scores, TOPK, id_map=self.pool_ids, out=self.top[layer], workspace=self.ws_topk)
 
     def attend(self, layer, kv, idx):
@@ -182,6 +192,9 @@ class Step:
         done = {0} if wl.group != "decoder" else set()
         for layer, src in enumerate(wl.attn_src):
             if src not in done:
+                if self.qfl is not None:
+                    with sp("q_pack"):
+                        self.pack_query(src)
                 with sp("reindex+topk"):
                     self.reindex(src, k_idx)
                 done.add(src)

@@ -37,6 +37,10 @@ The prefill chunk with the indexer K in FP4 (prefill128k_fp4k), and with the
 indexer Q in FP4 as well (prefill128k_fp4qk; eogee.com report 3.4: the
 predecessor already trained the indexer Q/K in FP4): the step itself packs
 the Full layer's bf16 query into one MXFP4 entry per head before scoring.
+The 64K and 1M decode steps at all of these precisions (MXFP4 indexer Q and K,
+FP8 window KV; each scoring layer's query packed inside the step):
+
+  encoder64k_fp4qk_fp8w, decode1m_fp4qk_fp8w.
 
 Layer groups that share one cache (eogee.com report 3.2: an encoder cache
 serves a Full layer and the Reuse layers after it; a decoder cache serves a
@@ -80,6 +84,10 @@ CONFIGS = {
                                  planted=8, prefill=False, kfmt="fp4", swa_fmt="fp8"),
     "decode1m_fp4k_fp8w": dict(nq=8, N=1048576, q_per_seq=1, hier=True, seed=10, kv="clustered", kidx="clustered",
                                planted=0, prefill=False, kfmt="fp4", swa_fmt="fp8"),
+    "encoder64k_fp4qk_fp8w": dict(nq=64, N=32768, q_per_seq=1, hier=False, seed=13, kv="random", kidx="normal",
+                                  planted=8, prefill=False, kfmt="fp4", swa_fmt="fp8", qfmt="fp4"),
+    "decode1m_fp4qk_fp8w": dict(nq=8, N=1048576, q_per_seq=1, hier=True, seed=14, kv="clustered", kidx="clustered",
+                                planted=0, prefill=False, kfmt="fp4", swa_fmt="fp8", qfmt="fp4"),
     "prefill128k_fp4k": dict(nq=4096, N=65536, q_per_seq=4096, hier=False, seed=11, kv="random", kidx="normal",
                              planted=0, prefill=True, kfmt="fp4"),
     "prefill128k_fp4qk": dict(nq=4096, N=65536, q_per_seq=4096, hier=False, seed=12, kv="random", kidx="normal",
@@ -130,7 +138,7 @@ class Workload:
     group: str = None  # None, "encoder" (Full + 5 Reuse) or "decoder" (Reindex + 3 Reuse)
     kfmt: str = "bf16"  # indexer-K cache precision the step reads: "bf16" or "fp4" (68 B entries)
     swa_fmt: str = "bf16"  # window-KV precision the step reads: "bf16" or "fp8" (528 B rows)
-    qfmt: str = "bf16"  # Full-layer indexer-Q precision: "bf16", or "fp4" (the step packs MXFP4 entries per head)
+    qfmt: str = "bf16"  # indexer-Q precision: "bf16", or "fp4" (the step packs each layer's MXFP4 entries per head)
     q_idx: list = field(default_factory=list)  # per indexer layer: bf16 [nq,32,128]
     w: list = field(default_factory=list)  # per indexer layer: f32 [nq,32]
     k_idx: torch.Tensor = None  # bf16 [nseq,N,128]

@@ -13,8 +13,8 @@ Samples: every query of the tiny and 64K workloads, the queries of 2
 sequences at 256K and 1M, 64 strided queries of the prefill chunks. The FP4
 indexer-K workloads also check the GPU's packed entries of the sampled
 sequences against the oracle's packing byte for byte, and score with the
-oracle's own entries; the MXFP4 indexer-Q workload does the same for the
-sampled queries' entries; the FP8 window workloads do the same for every
+oracle's own entries; the MXFP4 indexer-Q workloads do the same for the
+sampled queries' entries of every scoring layer; the FP8 window workloads do the same for every
 attention layer's window rows.
 """
 import math
@@ -32,7 +32,8 @@ SCALE = 1.0 / math.sqrt(512.0)
 
 
 def _sample(wl):
-    if wl.name in ("tiny", "encoder64k", "encoder_group64k", "encoder64k_fp4k", "encoder64k_fp4k_fp8w"):
+    if wl.name in ("tiny", "encoder64k", "encoder_group64k", "encoder64k_fp4k", "encoder64k_fp4k_fp8w",
+                   "encoder64k_fp4qk_fp8w"):
         return list(range(wl.nq))
     if wl.name.startswith("prefill"):
         return list(range(0, wl.nq, wl.nq // 64))
@@ -85,7 +86,7 @@ def _kv_for(qsub_seq, kvrows, N):
 @pytest.mark.parametrize("name", ["tiny", "encoder64k", "decoder256k", "prefill128k", "decode1m",
                                   "encoder_group64k", "decoder_group256k", "encoder64k_fp4k", "decode1m_fp4k",
                                   "encoder64k_fp4k_fp8w", "decode1m_fp4k_fp8w", "prefill128k_fp4k",
-                                  "prefill128k_fp4qk"])
+                                  "prefill128k_fp4qk", "encoder64k_fp4qk_fp8w", "decode1m_fp4qk_fp8w"])
 def test_workload_parity(name):
     import kv_cache_compression_csa2_amd as K
     from kv_cache_compression_csa2_amd.pipeline import Step, pack_workload_kv, workload_kidx
@@ -119,18 +120,24 @@ def test_workload_parity(name):
         assert np.array_equal(np_(kk[seq_t]), kf_sub)
         print("  indexer-K FP4 entries bit-exact", flush=True)
 
-    qf_sub = None
-    if wl.qfmt == "fp4":
-        # the oracle packs the sampled queries' indexer Q itself; the step's
-        # MXFP4 query entries must be the same bytes
-        qf_sub = O.kidx_fp4_pack(u16(wl.q_idx[0][qt]).reshape(-1, 128)).reshape(len(Qs), 32, O.KIDX_RECORD_BYTES)
-        assert np.array_equal(np_(step.qf[qt]), qf_sub)
+    def q_sub(layer):
+        """The sampled queries' indexer Q of a scoring layer for the oracle: bf16
+        bits, or (MXFP4-Q workloads) the oracle's own packing, which the step's
+        entries must equal byte for byte."""
+        if wl.qfmt != "fp4":
+            return u16(wl.q_idx[layer][qt]), None
+        qf = O.kidx_fp4_pack(u16(wl.q_idx[layer][qt]).reshape(-1, 128)).reshape(len(Qs), 32, O.KIDX_RECORD_BYTES)
+        assert np.array_equal(np_(step.qfl[layer][qt]), qf)
+        return None, qf
+
+    qb_sub, qf_sub = q_sub(0)
+    if qf_sub is not None:
         print("  indexer-Q MXFP4 entries bit-exact", flush=True)
 
     # 1. Full-layer scores
     bs = 8 if wl.hier else 0
-    r = O.index_full(None if qf_sub is not None else u16(wl.q_idx[0][qt]), np_(wl.w[0][qt]), k_sub, wl.N, qps_sub,
-                     n_visible=nv, block_size=bs, k_fp4=kf_sub, q_fp4=qf_sub)
+    r = O.index_full(qb_sub, np_(wl.w[0][qt]), k_sub, wl.N, qps_sub, n_visible=nv, block_size=bs, k_fp4=kf_sub,
+                     q_fp4=qf_sub)
     rs, rb = (r if wl.hier else (r, None))
     ok, msg = rel_close(np_(step.scores[qt]), rs)
     assert ok, "scores: " + msg
@@ -171,20 +178,24 @@ def test_workload_parity(name):
         if step.fused_reindex and wl.reindex_layers:
             # the fused Reindex selection (last layer) is csa2_topk of its own pool row
             lr = wl.reindex_layers[-1]
-            ps_u, pid_u = K.csa2_index_reindex(wl.q_idx[lr], wl.w[lr], None if fp4k else kk, wl.N, wl.q_per_seq,
-                                               step.cand, n_visible=wl.n_visible, k_fp4=kk if fp4k else None)
+            qb_l, qf_l = step._q(lr)
+            ps_u, pid_u = K.csa2_index_reindex(qb_l, wl.w[lr], None if fp4k else kk, wl.N, wl.q_per_seq,
+                                               step.cand, n_visible=wl.n_visible, k_fp4=kk if fp4k else None, q_fp4=qf_l)
             t_u = K.csa2_topk(ps_u, 512, id_map=pid_u)
             torch.cuda.synchronize()
             assert torch.equal(ps_u, step.pool_scores)
             assert torch.equal(t_u, step.top[lr])
             print("  fused reindex + Top-K equals the unfused calls", flush=True)
         for layer in wl.reindex_layers:
-            ps_o = O.index_reindex(u16(wl.q_idx[layer][qt]), np_(wl.w[layer][qt]), k_sub, wl.N, 1, pool,
-                                   n_visible=nv, k_fp4=kf_sub)
+            qb_o, qf_o = q_sub(layer)
+            ps_o = O.index_reindex(qb_o, np_(wl.w[layer][qt]), k_sub, wl.N, 1, pool, n_visible=nv, k_fp4=kf_sub,
+                                   q_fp4=qf_o)
             kg = kk[seq_t].contiguous()
-            ps_g, pid_g = K.csa2_index_reindex(wl.q_idx[layer][qt].contiguous(), wl.w[layer][qt].contiguous(),
-                                               None if fp4k else kg, wl.N, 1, dev_i32(cand_o, DEV),
-                                               k_fp4=kg if fp4k else None)
+            qb_g, qf_g = step._q(layer)
+            ps_g, pid_g = K.csa2_index_reindex(None if qb_g is None else qb_g[qt].contiguous(),
+                                               wl.w[layer][qt].contiguous(), None if fp4k else kg, wl.N, 1,
+                                               dev_i32(cand_o, DEV), k_fp4=kg if fp4k else None,
+                                               q_fp4=None if qf_g is None else qf_g[qt].contiguous())
             torch.cuda.synchronize()
             ok, msg = rel_close(np_(ps_g), ps_o)
             assert ok, "reindex %d: %s" % (layer, msg)
