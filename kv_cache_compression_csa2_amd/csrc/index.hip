@@ -867,6 +867,7 @@ __global__ __launch_bounds__(256, 2) void index_prefill_kernel(
     auto group = [&](int buf, int h2, f32x16& acca, f32x16& accb, const f32x16& pa, const f32x16& pb, int32_t pcol,
                      float (&out)[2]) {
         if constexpr (kQ4) {
+            __builtin_amdgcn_s_setprio(1);
             // entry h2*32 + col_in_tile: scale blocks 2s + half for K-steps s = 0, 1
             const uint8_t* rowp = lds[buf] + (h2 * 32 + col_in_tile) * kPfRowQ4;
             const uint4 b0 = *reinterpret_cast<const uint4*>(rowp + 16 * half);
@@ -885,8 +886,11 @@ __global__ __launch_bounds__(256, 2) void index_prefill_kernel(
                 __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
                 __builtin_amdgcn_sched_group_barrier(0x002, 16, 0);
             }
+            __builtin_amdgcn_s_setprio(0);
             return;
         }
+        // the wave issuing its MFMAs goes first on the SIMD
+        __builtin_amdgcn_s_setprio(1);
         const uint8_t* rowp = lds[buf] + (h2 * 32 + col_in_tile) * kPfRow + half * 16;
         bf16x8 bj[8];
 #pragma unroll
@@ -907,6 +911,7 @@ __global__ __launch_bounds__(256, 2) void index_prefill_kernel(
             __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
             __builtin_amdgcn_sched_group_barrier(0x002, 5, 0);
         }
+        __builtin_amdgcn_s_setprio(0);
     };
 
     const int64_t tile_base = e_begin;
