@@ -743,15 +743,23 @@ __global__ __launch_bounds__(256, 2) void index_prefill_kernel(
     const uint8_t* kfseq = static_cast<const uint8_t*>(k_idx) + (kFp4 ? seq * N * kKRec : 0);
     const int64_t e_begin = (int64_t)chunk * chunk_len;
     int64_t e_end = (e_begin + chunk_len < N) ? e_begin + chunk_len : N;
-    if (kSel && !scores) {
-        // entries no query of the workgroup sees need no scoring (unless the
-        // score row, -inf there, is asked for)
+    // Entries no query of the workgroup sees need no products: the selection
+    // skips them; a written score row gets -inf there from plain stores after
+    // the tile loop (whole tiles past the largest visible length).
+    int64_t e_fill = e_end;  // first entry of the -inf fill
+    if (kSel || scores) {
         int64_t nvmax = 0;
         for (int i = 0; i < kPfQueries; i++)
             nvmax = max(nvmax, n_visible ? (int64_t)n_visible[(int64_t)qg * kPfQueries + i] : N);
-        e_end = e_end < nvmax ? e_end : nvmax;
+        if (kSel && !scores) {
+            e_end = e_end < nvmax ? e_end : nvmax;
+        } else if (!kSel) {
+            const int64_t t_end = e_begin + (nvmax > e_begin ? (nvmax - e_begin + kPfSub - 1) / kPfSub * kPfSub : 0);
+            e_fill = t_end < e_end ? t_end : e_end;
+        }
     }
-    const int nsub = e_end > e_begin ? (int)((e_end - e_begin + kPfSub - 1) / kPfSub) : 0;
+    const int64_t e_tiles = kSel ? e_end : e_fill;  // entries the tile loop scores
+    const int nsub = e_tiles > e_begin ? (int)((e_tiles - e_begin + kPfSub - 1) / kPfSub) : 0;
     const int64_t nblk = (N + 7) >> 3;
 
     // Tile loads into registers. bf16 K: 4 16-byte units per thread of the
@@ -952,6 +960,18 @@ __global__ __launch_bounds__(256, 2) void index_prefill_kernel(
             }
         }
         store(out[0], out[1], col0 + 32);
+    }
+    if (!kSel && e_fill < e_end) {
+        // -inf past the tiles scored (every entry there is invisible to all
+        // of the workgroup's queries), and their blocks' maxima; e_fill is
+        // then a multiple of the tile, so no block straddles it
+        for (int i = 0; i < kPfQueries; i++) {
+            const int64_t q = (int64_t)qg * kPfQueries + i;
+            for (int64_t c = e_fill + tid; c < e_end; c += 256) __builtin_nontemporal_store(-INFINITY, scores + q * N + c);
+            if constexpr (kBlk)
+                for (int64_t b = (e_fill >> 3) + tid; b < ((e_end + 7) >> 3); b += 256)
+                    __builtin_nontemporal_store(-INFINITY, block_scores + q * nblk + b);
+        }
     }
     if constexpr (kSel) {
         // each query's k best, in entry order
